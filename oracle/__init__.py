@@ -1,0 +1,26 @@
+"""CPU oracle for the sparse MoE layer (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import or call this package. It shares no code with the HIP
+library and never imports it.
+"""
+from .moe import (  # noqa: F401
+    backward,
+    build,
+    exp_c,
+    expert_backward,
+    expert_forward,
+    forward,
+    gate_logits,
+    gelu_erf,
+    loss_fp64,
+    permutation,
+    route,
+    router_backward_dlogits,
+    routing_weights,
+    select_topk,
+    selection_key,
+    sigmoid_c,
+    sigmoid_c_sweep,
+    silu,
+)

@@ -1,0 +1,458 @@
+"""CPU oracle for one sparse MoE layer: forward (Route, Dispatch, Expert
+computation, Combine) and backward.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import or call anything under
+``oracle/``. The HIP library never links, loads or calls it, and this module
+never imports the HIP package: the two share no code. Inputs come from the
+seeded generators (``workloads``) as numpy arrays.
+
+Precision: the router runs in fp32 with a fixed summation order ("Scalable
+Training of Mixture-of-Experts Models with Megatron Core", section 5.1 keeps
+the router in FP32; the order itself is spelled out in ``gate.c``). Every
+other floating-point step runs in fp64, so the oracle is the exact result of
+the definitions up to fp64 rounding.
+
+Definitions followed (page titles are the pages' own):
+
+* Router, "Scalable Training ... with Megatron Core", section 2.2: logits
+  l = W_r^T x; softmax scores p_i = e^{l_i} / sum_j e^{l_j} or sigmoid scores;
+  top-k selection. "emerging-techniques-moe-training", Quick Start and the
+  Mixtral block: softmax over all experts, torch.topk, then division by the
+  sum of the k selected scores.
+* Selection ties, silent on the pages: the total order is (key descending,
+  expert index ascending); -0 and +0 are equal; a NaN key ranks as -inf.
+* Sigmoid scoring (DeepSeek-V3, section 2.2): the printed normaliser sums over
+  all experts; the workload normalises over the selected experts, which is
+  the reading taken. The aux-loss-free bias (same section) enters only the
+  selection key sigma(l) + bias, never the weights.
+* Dispatch, section 2.1 stage 2: tokens regrouped into expert-contiguous
+  order. Within an expert the order is ascending token index (the pages give
+  none; ascending is the plainest reading of "restore the original order" in
+  stage 4).
+* Expert computation, section 2.1 stage 3. GELU expert: Linear + GELU(erf) +
+  Linear with biases ("emerging-techniques-moe-training", Quick Start).
+  SwiGLU expert without bias: three matrices, gate and up then down ("Mixture
+  -of-Experts from Architecture to Large-Scale Training", section 2.5; the
+  formula itself is lost in the extracted page, the standard
+  silu(x W_g^T) * (x W_u^T) W_d^T is used).
+* Combine, section 2.1 stage 4 and section 1.1's MoE(x) = sum_{i in TopK}
+  p_i E_i(x): out[t] = sum_j w[t,j] y_{e_j}(x_t), plus the shared expert's
+  output with weight 1 (the shared expert is named in the handbook page's
+  introduction; its weight is not given, 1 is taken).
+
+Parity status: every function here is pinned by tests/test_oracle_*.py
+against closed forms, invariants, brute force and finite differences; the
+absolute output values of the four model-shaped workloads rest on those pins
+(the pages print no worked example).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_gate.so")
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile gate.c into liboracle_gate.so with gcc (no GPU toolchain)."""
+    src = os.path.join(_HERE, "gate.c")
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math",
+           "-fopenmp", "-fPIC", "-shared", "-o", tmp, src, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+            fp = ctypes.POINTER(ctypes.c_float)
+            lib.oracle_gate_logits.argtypes = [fp, fp, fp, ctypes.c_long, ctypes.c_long,
+                                               ctypes.c_long, fp]
+            lib.oracle_gate_logits.restype = None
+            lib.oracle_exp_c.argtypes = [ctypes.c_double]
+            lib.oracle_exp_c.restype = ctypes.c_double
+            lib.oracle_sigmoid_c.argtypes = [ctypes.c_float]
+            lib.oracle_sigmoid_c.restype = ctypes.c_float
+            lib.oracle_sigmoid_c_array.argtypes = [fp, ctypes.c_long, fp]
+            lib.oracle_sigmoid_c_array.restype = None
+            lib.oracle_sigmoid_c_sweep.argtypes = [
+                ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_double),
+                ctypes.POINTER(ctypes.c_long), ctypes.POINTER(ctypes.c_long)]
+            lib.oracle_sigmoid_c_sweep.restype = None
+            _lib = lib
+    return _lib
+
+
+def _fptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+# --------------------------------------------------------------------- router
+
+def gate_logits(x: np.ndarray, w_gate: np.ndarray, b_gate=None) -> np.ndarray:
+    """fp32 router logits in gate order G (see gate.c). x[T,h], w_gate[E,h]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w_gate, dtype=np.float32)
+    T, h = x.shape
+    E = w.shape[0]
+    assert w.shape[1] == h
+    out = np.empty((T, E), dtype=np.float32)
+    b = None
+    if b_gate is not None:
+        b = np.ascontiguousarray(b_gate, dtype=np.float32)
+    _load().oracle_gate_logits(_fptr(x), _fptr(w), _fptr(b) if b is not None else None,
+                               T, h, E, _fptr(out))
+    return out
+
+
+def exp_c(y: float) -> float:
+    """The fp64 exponential used inside sigma_c (gate.c)."""
+    return float(_load().oracle_exp_c(float(y)))
+
+
+def sigmoid_c(l: np.ndarray) -> np.ndarray:
+    """Canonical fp32 sigmoid (gate.c), elementwise."""
+    l = np.ascontiguousarray(l, dtype=np.float32)
+    out = np.empty_like(l)
+    _load().oracle_sigmoid_c_array(_fptr(l), l.size, _fptr(out))
+    return out
+
+
+def sigmoid_c_sweep(lo: float, hi: float):
+    mu = ctypes.c_double()
+    nd = ctypes.c_long()
+    nc = ctypes.c_long()
+    _load().oracle_sigmoid_c_sweep(lo, hi, ctypes.byref(mu), ctypes.byref(nd), ctypes.byref(nc))
+    return mu.value, nd.value, nc.value
+
+
+def selection_key(logits: np.ndarray, score: str, sel_bias=None) -> np.ndarray:
+    """fp32 key the top-k ranks on.
+
+    Softmax: the logit itself. Softmax is strictly increasing in each logit, so
+    ranking logits ranks the probabilities the pages select on, and equal
+    logits give equal probabilities. Sigmoid: sigma_c(l) + bias (fp32 add).
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    if score == "softmax":
+        key = logits.copy()
+    elif score == "sigmoid":
+        key = sigmoid_c(logits)
+        if sel_bias is not None:
+            key = (key + np.asarray(sel_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    else:
+        raise ValueError(score)
+    key = np.where(np.isnan(key), np.float32(-np.inf), key).astype(np.float32)
+    key = key + np.float32(0.0)   # -0 -> +0
+    return key
+
+
+def select_topk(key: np.ndarray, k: int) -> np.ndarray:
+    """First k experts of each row in the order (key desc, index asc)."""
+    T, E = key.shape
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((idx, -key.astype(np.float64)), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def routing_weights(logits_sel: np.ndarray, logits_all: np.ndarray, score: str) -> np.ndarray:
+    """fp64 weights of the k selected experts (rows of logits_sel).
+
+    softmax: p = softmax over all E logits, then p_sel / sum(p_sel).
+    sigmoid: s = sigma(l) of the selected logits, then s / sum(s).
+    """
+    ls = logits_sel.astype(np.float64)
+    if score == "softmax":
+        la = logits_all.astype(np.float64)
+        m = la.max(axis=1, keepdims=True)
+        z = np.exp(la - m).sum(axis=1, keepdims=True)
+        p_sel = np.exp(ls - m) / z
+        return p_sel / p_sel.sum(axis=1, keepdims=True)
+    s = 1.0 / (1.0 + np.exp(-ls))
+    return s / s.sum(axis=1, keepdims=True)
+
+
+def route(x, w_gate, k: int, score: str = "softmax", b_gate=None, sel_bias=None,
+          logits=None):
+    """Router stage. Returns logits (fp32), key (fp32), topk_idx [T,k] int32,
+    topk_w [T,k] fp64, routing_map [T,E] uint8, counts [E] int64."""
+    if logits is None:
+        logits = gate_logits(x, w_gate, b_gate)
+    T, E = logits.shape
+    key = selection_key(logits, score, sel_bias)
+    topk_idx = select_topk(key, k)
+    sel_logits = np.take_along_axis(logits, topk_idx.astype(np.int64), axis=1)
+    topk_w = routing_weights(sel_logits, logits, score)
+    routing_map = np.zeros((T, E), dtype=np.uint8)
+    np.put_along_axis(routing_map, topk_idx.astype(np.int64), 1, axis=1)
+    counts = routing_map.sum(axis=0).astype(np.int64)
+    return dict(logits=logits, key=key, topk_idx=topk_idx, topk_w=topk_w,
+                routing_map=routing_map, counts=counts)
+
+
+# ------------------------------------------------------------------ dispatch
+
+def permutation(topk_idx: np.ndarray, E: int):
+    """Expert-contiguous order of the (token, expert) pairs.
+
+    Pairs are listed expert by expert; inside an expert, tokens ascend. Returns
+    offsets [E+1] (exclusive prefix of the counts), sorted_token [T*k] (the
+    token of each permuted row) and row_of [T,k] (the permuted row of pair
+    (t, topk_idx[t,j])).
+    """
+    T, k = topk_idx.shape
+    routing_map = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(routing_map, topk_idx.astype(np.int64), True, axis=1)
+    e_of_row, t_of_row = np.nonzero(routing_map.T)     # row-major over (e, t)
+    counts = routing_map.sum(axis=0)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    row_index = np.full((E, T), -1, dtype=np.int64)
+    row_index[e_of_row, t_of_row] = np.arange(e_of_row.size)
+    row_of = row_index[topk_idx.astype(np.int64), np.arange(T)[:, None]]
+    return dict(offsets=offsets, sorted_token=t_of_row.astype(np.int64),
+                row_of=row_of, counts=counts.astype(np.int64))
+
+
+# ------------------------------------------------------------------- experts
+
+def silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def gelu_erf(a):
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
+
+
+def expert_forward(xe, w1e, w2e, act: str, b1e=None, b2e=None):
+    """One expert on the rows xe [m,h] in fp64. w1e [n1*F,h] (SwiGLU: gate rows
+    then up rows), w2e [h,F]. Returns y [m,h] and the cached pre-activations."""
+    xe = np.asarray(xe, dtype=np.float64)
+    w1e = np.asarray(w1e, dtype=np.float64)
+    w2e = np.asarray(w2e, dtype=np.float64)
+    F = w2e.shape[1]
+    a = xe @ w1e.T
+    if b1e is not None:
+        a = a + np.asarray(b1e, dtype=np.float64)[None, :]
+    if act == "swiglu":
+        g, u = a[:, :F], a[:, F:]
+        hid = silu(g) * u
+    elif act == "gelu":
+        hid = gelu_erf(a)
+    else:
+        raise ValueError(act)
+    y = hid @ w2e.T
+    if b2e is not None:
+        y = y + np.asarray(b2e, dtype=np.float64)[None, :]
+    return y, dict(a=a, hid=hid)
+
+
+def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bias=None,
+            b1=None, b2=None, w1_sh=None, w2_sh=None, tokens=None, routing=None):
+    """Whole layer in fp64 (router fp32). All arrays numpy; x [T,h].
+
+    ``tokens`` restricts the evaluation to those token indices (routing is
+    per-token, so this equals the full computation on those rows). Returns
+    the route dict plus out [n,h] fp64, y_pair [n,k,h] (expert outputs per
+    selected pair) and y_shared [n,h] or None.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        x = x[tokens]
+    if routing is None:
+        routing = route(x, w_gate, k, score, b_gate, sel_bias)
+    topk_idx = routing["topk_idx"]
+    topk_w = routing["topk_w"]
+    n, h = x.shape
+    E = w1.shape[0]
+    out = np.zeros((n, h), dtype=np.float64)
+    y_pair = np.zeros((n, k, h), dtype=np.float64)
+    # Per expert, as in the pages' loop over experts: gather the tokens that
+    # chose it, run the expert, weight and add back.
+    for e in range(E):
+        tok, slot = np.nonzero(topk_idx == e)
+        if tok.size == 0:
+            continue
+        y, _ = expert_forward(x[tok], w1[e], w2[e], act,
+                              None if b1 is None else b1[e], None if b2 is None else b2[e])
+        y_pair[tok, slot] = y
+    for j in range(k):
+        out += topk_w[:, j:j + 1] * y_pair[:, j]
+    y_sh = None
+    if w1_sh is not None:
+        y_sh, _ = expert_forward(x, w1_sh, w2_sh, act)
+        out += y_sh
+    res = dict(routing)
+    res.update(out=out, y_pair=y_pair, y_shared=y_sh)
+    return res
+
+
+# ------------------------------------------------------------------ backward
+
+def _dsilu(g):
+    s = 1.0 / (1.0 + np.exp(-g))
+    return s * (1.0 + g * (1.0 - s))
+
+
+def _dgelu(a):
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    cdf = 0.5 * (1.0 + erf(a / math.sqrt(2.0)))
+    pdf = np.exp(-0.5 * a * a) / math.sqrt(2.0 * math.pi)
+    return cdf + a * pdf
+
+
+def expert_backward(xe, w1e, w2e, act, dy, b1e=None, b2e=None):
+    """Gradients of sum(dy * expert(xe)) w.r.t. xe, w1e, w2e, b1e, b2e (fp64)."""
+    xe = np.asarray(xe, dtype=np.float64)
+    w1e = np.asarray(w1e, dtype=np.float64)
+    w2e = np.asarray(w2e, dtype=np.float64)
+    F = w2e.shape[1]
+    _, c = expert_forward(xe, w1e, w2e, act, b1e, b2e)
+    a, hid = c["a"], c["hid"]
+    dw2 = dy.T @ hid                      # [h,F]
+    dhid = dy @ w2e                       # [m,F]
+    if act == "swiglu":
+        g, u = a[:, :F], a[:, F:]
+        da = np.concatenate([dhid * u * _dsilu(g), dhid * silu(g)], axis=1)
+    else:
+        da = dhid * _dgelu(a)
+    dw1 = da.T @ xe                       # [n1F,h]
+    dx = da @ w1e                         # [m,h]
+    db1 = da.sum(axis=0) if b1e is not None else None
+    db2 = dy.sum(axis=0) if b2e is not None else None
+    return dict(dx=dx, dw1=dw1, dw2=dw2, db1=db1, db2=db2, dgu=da, hid=hid)
+
+
+def router_backward_dlogits(topk_w, d_topk_w, score, logits_sel=None):
+    """d L / d logit of each selected expert (fp64), [T,k].
+
+    softmax renormalised over the selection: w_j = e^{l_j} / sum_sel e^{l_i},
+    so dl_j = w_j (g_j - sum_i w_i g_i). Unselected logits do not reach the
+    output and get 0. sigmoid normalised over the selection: w_j = s_j / S with
+    s = sigma(l), so dl_j = s_j (1 - s_j) / S * (g_j - sum_i w_i g_i).
+    """
+    w = np.asarray(topk_w, dtype=np.float64)
+    g = np.asarray(d_topk_w, dtype=np.float64)
+    centred = g - (w * g).sum(axis=1, keepdims=True)
+    if score == "softmax":
+        return w * centred
+    s = 1.0 / (1.0 + np.exp(-np.asarray(logits_sel, dtype=np.float64)))
+    S = s.sum(axis=1, keepdims=True)
+    return s * (1.0 - s) / S * centred
+
+
+def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
+             b1=None, b2=None, routing=None, experts=None):
+    """Gradients of L = sum(grad_out * out) for the routed layer (no shared
+    expert). Top-k indices carry no gradient.
+
+    Returns dx [T,h], d_topk_w [T,k], d_logits_sel [T,k], dw_gate [E,h],
+    db_gate [E], and dicts dw1/dw2/db1/db2 keyed by expert (all experts, or
+    those listed in ``experts``; an expert with no tokens gets exact zeros).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    T, h = x.shape
+    E = w1.shape[0]
+    if routing is None:
+        routing = route(x, w_gate, k, score, b_gate, sel_bias)
+    topk_idx = routing["topk_idx"]
+    topk_w = routing["topk_w"]
+    G = np.asarray(grad_out, dtype=np.float64)
+    x64 = x.astype(np.float64)
+    want = set(range(E)) if experts is None else set(int(e) for e in experts)
+    dx = np.zeros((T, h), dtype=np.float64)
+    d_topk_w = np.zeros((T, k), dtype=np.float64)
+    dw1, dw2, db1, db2 = {}, {}, {}, {}
+    for e in range(E):
+        tok, slot = np.nonzero(topk_idx == e)
+        n1F = w1.shape[1]
+        if tok.size == 0:
+            if e in want:
+                dw1[e] = np.zeros((n1F, h))
+                dw2[e] = np.zeros((h, w2.shape[2]))
+                if b1 is not None:
+                    db1[e] = np.zeros(n1F)
+                    db2[e] = np.zeros(h)
+            continue
+        b1e = None if b1 is None else b1[e]
+        b2e = None if b2 is None else b2[e]
+        y, _ = expert_forward(x64[tok], w1[e], w2[e], act, b1e, b2e)
+        d_topk_w[tok, slot] = (G[tok] * y).sum(axis=1)
+        dy = topk_w[tok, slot][:, None] * G[tok]
+        gb = expert_backward(x64[tok], w1[e], w2[e], act, dy, b1e, b2e)
+        np.add.at(dx, tok, gb["dx"])
+        if e in want:
+            dw1[e] = gb["dw1"]
+            dw2[e] = gb["dw2"]
+            if b1 is not None:
+                db1[e] = gb["db1"]
+                db2[e] = gb["db2"]
+    logits_sel = np.take_along_axis(routing["logits"], topk_idx.astype(np.int64), axis=1)
+    dl = router_backward_dlogits(topk_w, d_topk_w, score, logits_sel)
+    dlogits = np.zeros((T, E), dtype=np.float64)
+    np.put_along_axis(dlogits, topk_idx.astype(np.int64), dl, axis=1)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    dw_gate = dlogits.T @ x64
+    db_gate = dlogits.sum(axis=0)
+    dx += dlogits @ wg
+    return dict(dx=dx, d_topk_w=d_topk_w, d_logits_sel=dl, d_logits=dlogits,
+                dw_gate=dw_gate, db_gate=db_gate, dw1=dw1, dw2=dw2, db1=db1, db2=db2)
+
+
+# ----------------------------------------------------- fp64 forward for FD
+
+def loss_fp64(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
+              b1=None, b2=None, expect_idx=None):
+    """L = sum(grad_out * out) with every step, logits included, in fp64.
+
+    Used only to check the backward by finite differences: the fp32 gate order
+    would quantise small perturbations of the router weights. Selection uses
+    the fp64 logits; ``expect_idx`` asserts that a perturbation left it
+    unchanged (top-k is piecewise constant, so the derivative exists only
+    there).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    logits = x @ np.asarray(w_gate, dtype=np.float64).T
+    if b_gate is not None:
+        logits = logits + np.asarray(b_gate, dtype=np.float64)[None, :]
+    if score == "softmax":
+        key = logits
+    else:
+        key = 1.0 / (1.0 + np.exp(-logits))
+        if sel_bias is not None:
+            key = key + np.asarray(sel_bias, dtype=np.float64)[None, :]
+    T, E = logits.shape
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -key), axis=-1)
+    topk_idx = order[:, :k]
+    if expect_idx is not None and not np.array_equal(topk_idx, expect_idx):
+        raise RuntimeError("selection changed under the perturbation")
+    sel = np.take_along_axis(logits, topk_idx, axis=1)
+    w = routing_weights(sel, logits, score)
+    out = np.zeros_like(x)
+    for e in range(w1.shape[0]):
+        tok, slot = np.nonzero(topk_idx == e)
+        if tok.size == 0:
+            continue
+        y, _ = expert_forward(x[tok], w1[e], w2[e], act,
+                              None if b1 is None else b1[e], None if b2 is None else b2[e])
+        np.add.at(out, tok, w[tok, slot][:, None] * y)
+    return float((np.asarray(grad_out, dtype=np.float64) * out).sum()), topk_idx, logits, w

@@ -1,0 +1,237 @@
+"""Benchmark of the sparse MoE layer on one MI355X.
+
+One step = one pass of the whole forward hot path over one batch of synthetic
+input: Route -> Permute -> Grouped FFN (two grouped GEMMs with the fused
+SwiGLU) -> Unpermute, all through libmoe.so's C ABI on one stream. The
+default workload is the Mixtral-8x7B-shaped layer (T=4096 tokens, h=4096,
+E=8, top-2, SwiGLU 14336, bf16 with fp32 accumulation).
+
+Prints one JSON line: active TFLOP/s (router GEMM plus every routed
+token's expert FLOPs, no padding credited) and tokens/s, per-stage times with
+their roofline fractions (stages timed separately with HIP events after an
+eviction of the 256 MB last-level cache), the roofline of the dominant stage,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer active TFLOP/s + tokens/s at 1 MI355X; % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--stage-reps", type=int, default=10)
+    p.add_argument("--cpu-tokens", type=int, default=256,
+                   help="tokens of the workload the CPU oracle is timed on")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-stages", action="store_true")
+    return p.parse_args()
+
+
+def stage_bytes(cfg, P, es):
+    """Algorithmic HBM bytes of the memory-bound stages (index traffic included)."""
+    T, h, k, E = cfg.T, cfg.h, cfg.k, cfg.E
+    route = T * h * es + E * h * es + T * k * 8 + E * 4
+    permute = T * h * es + P * h * es + T * k * 4 * 3 + P * 4
+    unpermute = P * h * es + T * h * es + T * k * 8 + (T * h * es if cfg.n_shared else 0)
+    return dict(route=route, permute=permute, unpermute=unpermute)
+
+
+def ffn_flops(cfg):
+    nmat = 3 if cfg.act == "swiglu" else 2
+    return (cfg.P + cfg.n_shared * cfg.T) * nmat * 2.0 * cfg.h * cfg.F
+
+
+def ffn_weight_bytes(cfg, es):
+    n1 = 2 if cfg.act == "swiglu" else 1
+    return (cfg.E + cfg.n_shared) * (n1 + 1) * cfg.h * cfg.F * es
+
+
+def cpu_baseline(cfg, inp, n_tok):
+    """The oracle as it stands, on the first n_tok tokens of the workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    class Lazy:
+        def __init__(self, t):
+            self.t = t
+            self.shape = tuple(t.shape)
+
+        def __getitem__(self, e):
+            return self.t[e].float().cpu().numpy()
+
+    x = inp["x"][:n_tok].float().cpu().numpy()
+    wg = inp["w_gate"].float().cpu().numpy()
+    sel = None if inp.get("sel_bias") is None else inp["sel_bias"].cpu().numpy()
+    bg = None if inp.get("b_gate") is None else inp["b_gate"].cpu().numpy()
+    w1, w2 = Lazy(inp["w1"]), Lazy(inp["w2"])
+    # stage the needed experts' weights on the host outside the timed region
+    r = oracle.route(x, wg, cfg.k, cfg.score, bg, sel)
+    used = sorted(set(int(e) for e in np.unique(r["topk_idx"])))
+    W1 = {e: w1[e] for e in used}
+    W2 = {e: w2[e] for e in used}
+
+    class Dict:
+        def __init__(self, d, shape):
+            self.d = d
+            self.shape = shape
+
+        def __getitem__(self, e):
+            return self.d[e]
+
+    W1o, W2o = Dict(W1, w1.shape), Dict(W2, w2.shape)
+    w1s = None if inp.get("w1_sh") is None else inp["w1_sh"].float().cpu().numpy()
+    w2s = None if inp.get("w2_sh") is None else inp["w2_sh"].float().cpu().numpy()
+    t0 = time.perf_counter()
+    ref = oracle.forward(x, wg, W1o, W2o, cfg.k, cfg.score, cfg.act, b_gate=bg, sel_bias=sel,
+                         w1_sh=w1s, w2_sh=w2s)
+    dt = time.perf_counter() - t0
+    sub = cfg.with_shape(T=n_tok)
+    flops = sub.active_flops_forward()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [os.cpu_count() or 1])
+    del ref
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "tokens_per_s": n_tok / dt,
+            "seconds": dt, "cores": int(threads), "kind": "oracle",
+            "sample": "oracle forward (fp32 router, fp64 experts) on the first %d of %d tokens "
+                      "of the same seeded workload; expert weights staged on the host beforehand"
+                      % (n_tok, cfg.T)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
+              "(no collectives or sharding in this build); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_experts_layer_06_amd import binding as B
+    from mixture_experts_layer_06_amd import layer
+    from mixture_experts_layer_06_amd import workloads as wl
+
+    B.load()
+    cfg = wl.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.make_inputs(cfg, device=dev, with_grad_out=False)
+    es = 2 if cfg.dtype == "bf16" else 4
+    flops = cfg.active_flops_forward()
+
+    def step():
+        return layer.forward(inp, cfg.k, cfg.score, cfg.act)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    counts = res["counts"].cpu().numpy()
+
+    out = {
+        "metric": METRIC,
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.h, "experts": cfg.E,
+                   "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
+                   "shared_experts": cfg.n_shared},
+        "tokens_per_s": cfg.T / dt,
+        "frac_of_bf16_peak": flops / dt / 1e12 / PEAK_BF16_TFLOPS,
+        "active_gflop_per_step": flops / 1e9,
+        "expert_load": {"min": int(counts.min()), "max": int(counts.max())},
+    }
+
+    if not args.no_stages:
+        stream = torch.cuda.current_stream(dev)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        E = cfg.E
+        r = B.moe_route(inp["x"], inp["w_gate"], cfg.k, cfg.score, b_gate=inp.get("b_gate"),
+                        sel_bias=inp.get("sel_bias"))
+        p = B.moe_permute(inp["x"], r["topk_idx"], E)
+        has_sh = inp.get("w1_sh") is not None
+        f = B.moe_grouped_ffn(p["x_perm"], p["offsets"], inp["w1"], inp["w2"], cfg.act,
+                              b1=inp.get("b1"), b2=inp.get("b2"), x_sh=inp["x"] if has_sh else None,
+                              w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"))
+        calls = {
+            "route": lambda: B.moe_route(inp["x"], inp["w_gate"], cfg.k, cfg.score,
+                                         b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias")),
+            "permute": lambda: B.moe_permute(inp["x"], r["topk_idx"], E),
+            "grouped_ffn": lambda: B.moe_grouped_ffn(
+                p["x_perm"], p["offsets"], inp["w1"], inp["w2"], cfg.act, b1=inp.get("b1"),
+                b2=inp.get("b2"), x_sh=inp["x"] if has_sh else None, w1_sh=inp.get("w1_sh"),
+                w2_sh=inp.get("w2_sh")),
+            "unpermute": lambda: B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"]),
+        }
+        stages = {}
+        for name, fn in calls.items():
+            fn()
+            ts = []
+            for _ in range(args.stage_reps):
+                flush.fill_(1)     # evict the last-level cache
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            stages[name] = {"s_median": float(np.median(ts)), "s_min": float(np.min(ts))}
+        sb = stage_bytes(cfg, cfg.P, es)
+        for name in ("route", "permute", "unpermute"):
+            t = stages[name]["s_median"]
+            stages[name]["gb_per_s"] = sb[name] / t / 1e9
+            stages[name]["hbm_frac"] = sb[name] / t / 1e9 / PEAK_HBM_GBS
+            stages[name]["algorithmic_bytes"] = sb[name]
+        t = stages["grouped_ffn"]["s_median"]
+        ff = ffn_flops(cfg)
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+        stages["grouped_ffn"]["tflops"] = ff / t / 1e12
+        stages["grouped_ffn"]["mfma_frac"] = ff / t / 1e12 / peak
+        stages["grouped_ffn"]["weight_gb_per_s"] = ffn_weight_bytes(cfg, es) / t / 1e9
+        out["stages"] = stages
+        out["roofline"] = {
+            "kernel": "grouped_ffn: grouped_gemm_bf16 SwiGLU + plain launches",
+            "bound": "mfma", "achieved": ff / t / 1e12, "peak": peak, "unit": "TFLOP/s",
+            "frac": ff / t / 1e12 / peak, "traffic": None,
+            "flops_per_launch": ff,
+        }
+        del flush
+
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.T))
+        except Exception as exc:   # report, never hide, a failing baseline
+            out["cpu_baseline"] = {"error": repr(exc)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

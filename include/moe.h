@@ -1,0 +1,225 @@
+/*
+ * moe.h - C ABI of libmoe.so, the MI355X (gfx950) sparse Mixture-of-Experts
+ * layer: Route -> Dispatch (permute) -> Expert computation (one grouped FFN
+ * over all experts) -> Combine (weighted un-permute), and the backward of each
+ * stage. The four stages and the router's two outputs (routing weights and a
+ * boolean token-expert map) are those of "Scalable Training of
+ * Mixture-of-Experts Models with Megatron Core", section 2.1; the router
+ * (gate linear, softmax or sigmoid score, top-k) is section 2.2 of that page;
+ * top-k renormalisation is in "emerging-techniques-moe-training" (Quick Start,
+ * Top-2 routing, Mixtral block).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer into memory the caller owns
+ *   (hipMalloc or a framework allocator), except where stated. The library
+ *   allocates nothing and keeps no state between calls; all entry points are
+ *   reentrant.
+ * - Every call is asynchronous: it enqueues kernels on `stream` (a
+ *   hipStream_t; NULL = the default stream) and returns. It never
+ *   synchronises with the host, so expert token counts stay on the device.
+ * - Tensors are dense, row-major, with the shapes given in brackets. Base
+ *   pointers must be 16-byte aligned.
+ * - dtype is MOE_DTYPE_BF16 (activations and weights in bfloat16, fp32
+ *   accumulation) or MOE_DTYPE_F32. Routing quantities (logits, weights,
+ *   routing-weight gradients) are always fp32; weight gradients are fp32.
+ * - Arguments are validated on the host before anything is enqueued. A call
+ *   that returns an error has enqueued nothing and left every output
+ *   untouched. MOE_ERR_HIP reports a failed kernel launch; the message is in
+ *   moe_last_error() (thread-local). No C++ exception crosses this ABI.
+ * - Index inputs produced by one stage and consumed by the next (topk_idx,
+ *   offsets, row_of, sorted_token) must be those the producing entry point
+ *   wrote (or satisfy the same invariants). Kernels never read or write out of
+ *   bounds for any index values, but results are unspecified for indices that
+ *   break the invariants.
+ * - Results are deterministic: identical inputs give bitwise identical
+ *   outputs (no floating-point atomics).
+ *
+ * Supported sizes (MOE_ERR_UNSUPPORTED otherwise): h % 64 == 0, F % 64 == 0,
+ * 1 <= k <= E <= 256, k <= 8, T*k < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad enum      */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid but outside the supported sizes      */
+    MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    MOE_ERR_HIP = 4           /* a HIP launch failed; see moe_last_error()  */
+} moe_status;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+/* Static text for a moe_status value. */
+const char *moe_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* ------------------------------------------------------------------ Route
+ * Router stage ("Scalable Training ... with Megatron Core", section 2.2:
+ * gating l = W_r^T x, then a softmax or sigmoid score, then top-k; section
+ * 5.1: the router stays in fp32).
+ *
+ *   x        [T,h] dtype       token hidden states
+ *   w_gate   [E,h] dtype       router weight (row e = expert e)
+ *   b_gate   [E]   fp32|NULL   router bias
+ *   sel_bias [E]   fp32|NULL   aux-loss-free selection bias (sigmoid only;
+ *                              enters the selection key, not the weights)
+ * Outputs:
+ *   logits      [T,E] fp32|NULL  gate logits
+ *   topk_idx    [T,k] int32      selected experts, best first
+ *   topk_w      [T,k] fp32       routing weights, summing to 1 per token
+ *   routing_map [T,E] uint8|NULL 1 where expert e is selected for token t
+ *   counts      [E]   int32      tokens per expert (overwritten)
+ *
+ * Logit of (t,e): fp32, summed in a fixed order: 64 partial sums by residue
+ * i mod 64, each an fma chain over ascending i, then a halving tree
+ * (s = 32..1: part[j] += part[j+s]), then + b_gate[e]. The key is the logit
+ * (softmax; softmax is increasing in each logit) or sigma_c(l) + sel_bias[e]
+ * (sigmoid; sigma_c rounds a fixed fp64 evaluation of 1/(1+e^-l), argument
+ * clamped to [-80,80], to fp32). Top-k order: key descending, then expert
+ * index ascending; -0 equals +0; a NaN key ranks as -inf. Weights: softmax
+ * renormalised over the k selected (= softmax of the selected logits);
+ * sigmoid: sigma(l_j) / sum of the selected sigma(l_i).
+ */
+int moe_route(const void *x, int dtype, int64_t T, int64_t h, const void *w_gate,
+              const float *b_gate, int E, int k, int score, const float *sel_bias,
+              float *logits, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
+              int32_t *counts, void *stream);
+
+/* ---------------------------------------------------------------- Permute
+ * Dispatch stage ("Scalable Training ... with Megatron Core", section 2.1
+ * stage 2: tokens regrouped by expert before expert computation; no
+ * all-to-all: every expert is local).
+ *
+ *   x        [T,h] dtype   token hidden states
+ *   topk_idx [T,k] int32   from moe_route (or any per-token-distinct indices
+ *                          in [0,E), e.g. replayed routing)
+ * Outputs:
+ *   offsets      [E+1] int32   start row of each expert's segment; offsets[E]
+ *                              = T*k
+ *   sorted_token [T*k] int32   token of each permuted row
+ *   row_of       [T,k] int32   permuted row of pair (t, topk_idx[t,j])
+ *   x_perm       [T*k,h] dtype|NULL  x[sorted_token[r]] in row r (NULL:
+ *                              indices only)
+ * Order inside a segment: ascending token index (stable).
+ * Workspace: moe_permute_workspace_size(T,E,k) bytes of device memory.
+ */
+size_t moe_permute_workspace_size(int64_t T, int E, int k);
+int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
+                const int32_t *topk_idx, int32_t *offsets, int32_t *sorted_token,
+                int32_t *row_of, void *x_perm, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* ------------------------------------------------------------ Grouped FFN
+ * Expert computation as one grouped GEMM over all experts ("Scalable
+ * Training ... with Megatron Core", section 2.1 stage 3, TEGroupedMLP), each
+ * expert a SwiGLU FFN without bias ("Mixture-of-Experts from Architecture to
+ * Large-Scale Training", section 2.5: three weight matrices) or
+ * Linear + GELU(erf) + Linear with biases ("emerging-techniques-moe-training",
+ * Quick Start). Segment e is rows [offsets[e], offsets[e+1]) of x_perm and
+ * uses expert e's weights; segment sizes are read on the device.
+ *
+ *   x_perm  [P,h] dtype       permuted tokens (P = T*k)
+ *   offsets [E+1] int32       segment starts, offsets[E] = P
+ *   w1      [E,n1*F,h] dtype  first projection; SwiGLU (n1 = 2): rows 0..F-1
+ *                             gate, rows F..2F-1 up; GELU: n1 = 1
+ *   b1      [E,n1*F] dtype|NULL, w2 [E,h,F] dtype, b2 [E,h] dtype|NULL
+ *   x_sh    [T_sh,h] dtype|NULL  shared-expert input (the unpermuted x);
+ *   w1_sh   [n1*F,h], w2_sh [h,F]  shared-expert weights (no bias)
+ * Outputs:
+ *   act  [P+T_sh,F] dtype     activation silu(g)*u or GELU(a) (input of the
+ *                             second GEMM; rows P.. are the shared expert's)
+ *   gu   [P+T_sh,n1*F] dtype|NULL  pre-activations (kept for the backward)
+ *   y    [P,h] dtype          expert outputs in permuted order
+ *   y_sh [T_sh,h] dtype|NULL  shared-expert output
+ * Arithmetic: fp32 accumulation on MFMA; act, gu and y are rounded to dtype.
+ */
+int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t h, int64_t F, int E,
+                    const int32_t *offsets, int act_kind, const void *w1, const void *b1,
+                    const void *w2, const void *b2, const void *x_sh, int64_t T_sh,
+                    const void *w1_sh, const void *w2_sh, void *act, void *gu, void *y,
+                    void *y_sh, void *stream);
+
+/* -------------------------------------------------------------- Unpermute
+ * Combine stage ("Scalable Training ... with Megatron Core", section 2.1
+ * stage 4 and section 1.1's MoE(x) = sum over the top-k of p_i E_i(x)):
+ *   out[t] = sum_{j<k, ascending} topk_w[t,j] * y[row_of[t,j]]  (+ y_sh[t])
+ * accumulated in fp32, rounded once to dtype.
+ *   y [P,h] dtype, row_of [T,k], topk_w [T,k] fp32, y_sh [T,h] dtype|NULL
+ *   out [T,h] dtype (output)
+ */
+int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int k,
+                  const int32_t *row_of, const float *topk_w, const void *y_sh, void *out,
+                  void *stream);
+
+/* =============================== backward ===============================
+ * Gradients of L = sum(grad_out * out) (grad_out = dL/dout). Top-k indices
+ * carry no gradient. Order of use: moe_unpermute_bwd, moe_grouped_ffn_bwd,
+ * moe_route_bwd, moe_permute_bwd.
+ */
+
+/* Combine backward: grad_y[row_of[t,j]] = topk_w[t,j] * grad_out[t] (dtype)
+ * and grad_topk_w[t,j] = <grad_out[t], y[row_of[t,j]]> (fp32). */
+int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype, int64_t T, int64_t h,
+                      int k, const int32_t *row_of, const float *topk_w, void *grad_y,
+                      float *grad_topk_w, void *stream);
+
+/* Grouped FFN backward (SwiGLU, no bias). Per segment e with rows X_e of
+ * x_perm, saved pre-activations (g,u) = gu rows and act = silu(g)*u:
+ *   dact = grad_y W2[e];  dg = dact * u * silu'(g);  du = dact * silu(g)
+ *   grad_w2[e] = grad_y_e^T act_e          [h,F]  fp32
+ *   grad_w1[e] = [dg du]_e^T X_e           [2F,h] fp32 (zeros for an empty e)
+ *   grad_x_perm = [dg du] W1[e]            [P,h]  dtype
+ * grad_gu [P,2F] dtype is caller-provided scratch that receives [dg du]. */
+int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const void *act,
+                        const void *gu, int dtype, int64_t P, int64_t h, int64_t F, int E,
+                        const int32_t *offsets, int act_kind, const void *w1, const void *w2,
+                        void *grad_gu, void *grad_x_perm, float *grad_w1, float *grad_w2,
+                        void *stream);
+
+/* Router backward. grad_logits_sel[t,j] = dL/dl for the selected expert
+ * topk_idx[t,j] (unselected logits get 0):
+ *   softmax:  w_j (g_j - sum_i w_i g_i)
+ *   sigmoid:  s_j (1 - s_j) / S (g_j - sum_i w_i g_i), s = sigma(l), S = sum s
+ * with g = grad_topk_w. Then, segment by segment of the permutation,
+ *   grad_w_gate[e] = sum over rows r of e (ascending) of dl(r) x[sorted_token[r]]
+ *   grad_b_gate[e] = sum of the same dl(r)
+ * (grad_w_gate [E,h] fp32, grad_b_gate [E] fp32 or NULL). logits [T,E] fp32 is
+ * read for sigmoid only (may be NULL for softmax). Workspace:
+ * moe_route_bwd_workspace_size(T,h,E,k) bytes of device memory. */
+size_t moe_route_bwd_workspace_size(int64_t T, int64_t h, int E, int k);
+int moe_route_bwd(const void *x, int dtype, int64_t T, int64_t h, int E, int k, int score,
+                  const float *logits, const int32_t *topk_idx, const float *topk_w,
+                  const float *grad_topk_w, const int32_t *offsets,
+                  const int32_t *sorted_token, float *grad_logits_sel, float *grad_w_gate,
+                  float *grad_b_gate, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Dispatch backward plus the router's input gradient, one rounding:
+ *   grad_x[t] = sum_j grad_x_perm[row_of[t,j]]
+ *             + sum_j grad_logits_sel[t,j] * w_gate[topk_idx[t,j]]
+ * (the second sum is skipped when grad_logits_sel is NULL). */
+int moe_permute_bwd(const void *grad_x_perm, int dtype, int64_t T, int64_t h, int k,
+                    const int32_t *row_of, const float *grad_logits_sel,
+                    const int32_t *topk_idx, const void *w_gate, int E, void *grad_x,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,308 @@
+"""ctypes binding of libmoe.so: the C entry points under the same names.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch on the input's device, and the
+call goes to the C ABI on torch's current stream. Every step of the layer
+runs in the library's HIP kernels; there is no fallback. If the library is
+not built, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+_lib = None
+_lock = threading.Lock()
+
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+SCORE = {"softmax": 0, "sigmoid": 1}
+ACT = {"gelu": 0, "swiglu": 1}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "moe_abi_version": ([], _int),
+    "moe_status_string": ([_int], ctypes.c_char_p),
+    "moe_last_error": ([], ctypes.c_char_p),
+    "moe_route": ([_vp, _int, _i64, _i64, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                   _vp], _int),
+    "moe_permute_workspace_size": ([_i64, _int, _int], _sz),
+    "moe_permute": ([_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_grouped_ffn": ([_vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp, _i64,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp], _int),
+    "moe_unpermute": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp], _int),
+    "moe_unpermute_bwd": ([_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp], _int),
+    "moe_grouped_ffn_bwd": ([_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _vp], _int),
+    "moe_route_bwd_workspace_size": ([_i64, _i64, _int, _int], _sz),
+    "moe_route_bwd": ([_vp, _int, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                       _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_permute_bwd": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _int, _vp, _vp], _int),
+}
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def load(path: Optional[str] = None):
+    """Load libmoe.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise MoeError("libmoe.so is not built (%s); run "
+                           "`python -m mixture_experts_layer_06_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+        return lib
+
+
+def lib():
+    return _lib if _lib is not None else load()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        L = lib()
+        raise MoeError("%s: %s: %s" % (name, L.moe_status_string(rc).decode(),
+                                       L.moe_last_error().decode()))
+
+
+def _req(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if t is None:
+        raise MoeError("%s is required" % name)
+    if not t.is_cuda:
+        raise MoeError("%s must be a device tensor" % name)
+    if device is not None and t.device != device:
+        raise MoeError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise MoeError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoeError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t
+
+
+def _opt(t, name, **kw):
+    return None if t is None else _req(t, name, **kw)
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+# ----------------------------------------------------------------- forward
+
+def moe_route(x, w_gate, k: int, score: str = "softmax", b_gate=None, sel_bias=None,
+              want_logits: bool = False, want_map: bool = False):
+    _req(x, "x")
+    dev = x.device
+    T, h = x.shape
+    E = w_gate.shape[0]
+    _req(w_gate, "w_gate", dtype=x.dtype, shape=(E, h), device=dev)
+    _opt(b_gate, "b_gate", dtype=torch.float32, shape=(E,), device=dev)
+    _opt(sel_bias, "sel_bias", dtype=torch.float32, shape=(E,), device=dev)
+    out = dict(
+        topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        counts=torch.empty((E,), dtype=torch.int32, device=dev),
+        logits=torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None,
+        routing_map=torch.empty((T, E), dtype=torch.uint8, device=dev) if want_map else None,
+    )
+    rc = lib().moe_route(_ptr(x), DTYPE[x.dtype], T, h, _ptr(w_gate), _ptr(b_gate), E, k,
+                         SCORE[score], _ptr(sel_bias), _ptr(out["logits"]), _ptr(out["topk_idx"]),
+                         _ptr(out["topk_w"]), _ptr(out["routing_map"]), _ptr(out["counts"]),
+                         _stream(x))
+    _check(rc, "moe_route")
+    return out
+
+
+def moe_permute(x, topk_idx, E: int, with_x_perm: bool = True):
+    _req(x, "x")
+    dev = x.device
+    T, h = x.shape
+    k = topk_idx.shape[1]
+    _req(topk_idx, "topk_idx", dtype=torch.int32, shape=(T, k), device=dev)
+    P = T * k
+    ws_bytes = lib().moe_permute_workspace_size(T, E, k)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    out = dict(
+        offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+        sorted_token=torch.empty((P,), dtype=torch.int32, device=dev),
+        row_of=torch.empty((T, k), dtype=torch.int32, device=dev),
+        x_perm=torch.empty((P, h), dtype=x.dtype, device=dev) if with_x_perm else None,
+    )
+    rc = lib().moe_permute(_ptr(x), DTYPE[x.dtype], T, h, E, k, _ptr(topk_idx), _ptr(out["offsets"]),
+                           _ptr(out["sorted_token"]), _ptr(out["row_of"]), _ptr(out["x_perm"]),
+                           _ptr(ws), ws.numel(), _stream(x))
+    _check(rc, "moe_permute")
+    return out
+
+
+def moe_grouped_ffn(x_perm, offsets, w1, w2, act: str = "swiglu", b1=None, b2=None, x_sh=None,
+                    w1_sh=None, w2_sh=None, keep_gu: bool = False):
+    _req(x_perm, "x_perm")
+    dev = x_perm.device
+    dt = x_perm.dtype
+    P, h = x_perm.shape
+    E = w1.shape[0]
+    n1 = 2 if act == "swiglu" else 1
+    F = w2.shape[2]
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(w1, "w1", dtype=dt, shape=(E, n1 * F, h), device=dev)
+    _req(w2, "w2", dtype=dt, shape=(E, h, F), device=dev)
+    _opt(b1, "b1", dtype=dt, shape=(E, n1 * F), device=dev)
+    _opt(b2, "b2", dtype=dt, shape=(E, h), device=dev)
+    T_sh = 0
+    if x_sh is not None:
+        T_sh = x_sh.shape[0]
+        _req(x_sh, "x_sh", dtype=dt, shape=(T_sh, h), device=dev)
+        _req(w1_sh, "w1_sh", dtype=dt, shape=(n1 * F, h), device=dev)
+        _req(w2_sh, "w2_sh", dtype=dt, shape=(h, F), device=dev)
+    out = dict(
+        act=torch.empty((P + T_sh, F), dtype=dt, device=dev),
+        gu=torch.empty((P + T_sh, n1 * F), dtype=dt, device=dev) if keep_gu else None,
+        y=torch.empty((P, h), dtype=dt, device=dev),
+        y_sh=torch.empty((T_sh, h), dtype=dt, device=dev) if T_sh else None,
+    )
+    rc = lib().moe_grouped_ffn(_ptr(x_perm), DTYPE[dt], P, h, F, E, _ptr(offsets), ACT[act],
+                               _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(x_sh), T_sh,
+                               _ptr(w1_sh), _ptr(w2_sh), _ptr(out["act"]), _ptr(out["gu"]),
+                               _ptr(out["y"]), _ptr(out["y_sh"]), _stream(x_perm))
+    _check(rc, "moe_grouped_ffn")
+    return out
+
+
+def moe_unpermute(y, row_of, topk_w, y_sh=None, out=None):
+    _req(y, "y")
+    dev = y.device
+    T, k = row_of.shape
+    h = y.shape[1]
+    _req(row_of, "row_of", dtype=torch.int32, device=dev)
+    _req(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    _opt(y_sh, "y_sh", dtype=y.dtype, shape=(T, h), device=dev)
+    if out is None:
+        out = torch.empty((T, h), dtype=y.dtype, device=dev)
+    _req(out, "out", dtype=y.dtype, shape=(T, h), device=dev)
+    rc = lib().moe_unpermute(_ptr(y), DTYPE[y.dtype], T, h, k, _ptr(row_of), _ptr(topk_w),
+                             _ptr(y_sh), _ptr(out), _stream(y))
+    _check(rc, "moe_unpermute")
+    return out
+
+
+# ---------------------------------------------------------------- backward
+
+def moe_unpermute_bwd(grad_out, y, row_of, topk_w):
+    _req(grad_out, "grad_out")
+    dev = grad_out.device
+    T, h = grad_out.shape
+    k = row_of.shape[1]
+    _req(y, "y", dtype=grad_out.dtype, shape=(T * k, h), device=dev)
+    _req(row_of, "row_of", dtype=torch.int32, shape=(T, k), device=dev)
+    _req(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    grad_y = torch.empty((T * k, h), dtype=grad_out.dtype, device=dev)
+    grad_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    rc = lib().moe_unpermute_bwd(_ptr(grad_out), _ptr(y), DTYPE[y.dtype], T, h, k, _ptr(row_of),
+                                 _ptr(topk_w), _ptr(grad_y), _ptr(grad_w), _stream(grad_out))
+    _check(rc, "moe_unpermute_bwd")
+    return grad_y, grad_w
+
+
+def moe_grouped_ffn_bwd(grad_y, x_perm, act_out, gu, offsets, w1, w2, act: str = "swiglu"):
+    _req(grad_y, "grad_y")
+    dev = grad_y.device
+    dt = grad_y.dtype
+    P, h = grad_y.shape
+    E = w1.shape[0]
+    F = w2.shape[2]
+    n1 = 2 if act == "swiglu" else 1
+    _req(x_perm, "x_perm", dtype=dt, shape=(P, h), device=dev)
+    _req(act_out, "act", dtype=dt, device=dev)
+    _req(gu, "gu", dtype=dt, device=dev)
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(w1, "w1", dtype=dt, shape=(E, n1 * F, h), device=dev)
+    _req(w2, "w2", dtype=dt, shape=(E, h, F), device=dev)
+    grad_gu = torch.empty((P, n1 * F), dtype=dt, device=dev)
+    grad_x_perm = torch.empty((P, h), dtype=dt, device=dev)
+    grad_w1 = torch.empty((E, n1 * F, h), dtype=torch.float32, device=dev)
+    grad_w2 = torch.empty((E, h, F), dtype=torch.float32, device=dev)
+    rc = lib().moe_grouped_ffn_bwd(_ptr(grad_y), _ptr(x_perm), _ptr(act_out), _ptr(gu), DTYPE[dt], P,
+                                   h, F, E, _ptr(offsets), ACT[act], _ptr(w1), _ptr(w2),
+                                   _ptr(grad_gu), _ptr(grad_x_perm), _ptr(grad_w1), _ptr(grad_w2),
+                                   _stream(grad_y))
+    _check(rc, "moe_grouped_ffn_bwd")
+    return dict(grad_gu=grad_gu, grad_x_perm=grad_x_perm, grad_w1=grad_w1, grad_w2=grad_w2)
+
+
+def moe_route_bwd(x, E: int, topk_idx, topk_w, grad_topk_w, offsets, sorted_token,
+                  score: str = "softmax", logits=None, want_b_grad: bool = False):
+    _req(x, "x")
+    dev = x.device
+    T, h = x.shape
+    k = topk_idx.shape[1]
+    _req(topk_idx, "topk_idx", dtype=torch.int32, shape=(T, k), device=dev)
+    _req(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    _req(grad_topk_w, "grad_topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(sorted_token, "sorted_token", dtype=torch.int32, shape=(T * k,), device=dev)
+    _opt(logits, "logits", dtype=torch.float32, shape=(T, E), device=dev)
+    ws_bytes = lib().moe_route_bwd_workspace_size(T, h, E, k)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    out = dict(
+        grad_logits_sel=torch.empty((T, k), dtype=torch.float32, device=dev),
+        grad_w_gate=torch.empty((E, h), dtype=torch.float32, device=dev),
+        grad_b_gate=torch.empty((E,), dtype=torch.float32, device=dev) if want_b_grad else None,
+    )
+    rc = lib().moe_route_bwd(_ptr(x), DTYPE[x.dtype], T, h, E, k, SCORE[score], _ptr(logits),
+                             _ptr(topk_idx), _ptr(topk_w), _ptr(grad_topk_w), _ptr(offsets),
+                             _ptr(sorted_token), _ptr(out["grad_logits_sel"]),
+                             _ptr(out["grad_w_gate"]), _ptr(out["grad_b_gate"]), _ptr(ws),
+                             ws.numel(), _stream(x))
+    _check(rc, "moe_route_bwd")
+    return out
+
+
+def moe_permute_bwd(grad_x_perm, row_of, grad_logits_sel=None, topk_idx=None, w_gate=None):
+    _req(grad_x_perm, "grad_x_perm")
+    dev = grad_x_perm.device
+    T, k = row_of.shape
+    h = grad_x_perm.shape[1]
+    _req(row_of, "row_of", dtype=torch.int32, device=dev)
+    E = 0
+    if grad_logits_sel is not None:
+        _req(grad_logits_sel, "grad_logits_sel", dtype=torch.float32, shape=(T, k), device=dev)
+        _req(topk_idx, "topk_idx", dtype=torch.int32, shape=(T, k), device=dev)
+        _req(w_gate, "w_gate", dtype=grad_x_perm.dtype, device=dev)
+        E = w_gate.shape[0]
+    grad_x = torch.empty((T, h), dtype=grad_x_perm.dtype, device=dev)
+    rc = lib().moe_permute_bwd(_ptr(grad_x_perm), DTYPE[grad_x_perm.dtype], T, h, k, _ptr(row_of),
+                               _ptr(grad_logits_sel), _ptr(topk_idx), _ptr(w_gate), E,
+                               _ptr(grad_x), _stream(grad_x_perm))
+    _check(rc, "moe_permute_bwd")
+    return grad_x

@@ -1,0 +1,250 @@
+// Combine stage and the two row-wise backward passes around the experts.
+//
+//   unpermute:      out[t] = sum_j w[t,j] y[row_of[t,j]] (+ y_sh[t])
+//   unpermute_bwd:  grad_y[row_of[t,j]] = w[t,j] grad_out[t];
+//                   grad_w[t,j] = <grad_out[t], y[row_of[t,j]]>
+//   permute_bwd:    grad_x[t] = sum_j grad_x_perm[row_of[t,j]]
+//                             + sum_j grad_l[t,j] w_gate[topk_idx[t,j]]
+//
+// Combine: "Scalable Training of Mixture-of-Experts Models with Megatron
+// Core", section 2.1 stage 4 (inverse of the dispatch, restoring token order)
+// and section 1.1 (MoE(x) = sum over the top-k of p_i E_i(x)). The shared
+// expert's output is added with weight 1.
+//
+// All three are HBM-bound row streams: one workgroup per token, 16-byte
+// accesses, fp32 accumulation in a fixed order (j ascending), one rounding
+// to the output type. Reductions use a fixed shuffle tree, so results are
+// deterministic.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+template <typename TE>
+__global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y, int h, int k,
+                                                        const int32_t *__restrict__ row_of,
+                                                        const float *__restrict__ topk_w,
+                                                        const TE *__restrict__ y_sh,
+                                                        TE *__restrict__ out) {
+    const int t = blockIdx.x;
+    int rows[8];
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        w[j] = j < k ? topk_w[static_cast<int64_t>(t) * k + j] : 0.0f;
+    }
+    const int nv = h / 8;
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] >= 0) {
+                float yv[8];
+                load8(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[i], acc[i]);
+            }
+        }
+        if (y_sh) {
+            float sv[8];
+            load8(y_sh + static_cast<int64_t>(t) * h + 8 * v, sv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += sv[i];
+        }
+        store8(out + static_cast<int64_t>(t) * h + 8 * v, acc);
+    }
+}
+
+template <typename TE>
+__global__ __launch_bounds__(256) void unpermute_bwd_kernel(
+    const TE *__restrict__ gout, const TE *__restrict__ y, int h, int k,
+    const int32_t *__restrict__ row_of, const float *__restrict__ topk_w, TE *__restrict__ gy,
+    float *__restrict__ gw) {
+    __shared__ float red[8][4];
+    const int t = blockIdx.x;
+    int rows[8];
+    float w[8], dot[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        w[j] = j < k ? topk_w[static_cast<int64_t>(t) * k + j] : 0.0f;
+        dot[j] = 0.0f;
+    }
+    const int nv = h / 8;
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+        float g[8];
+        load8(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] >= 0) {
+                float yv[8], d[8];
+                load8(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    dot[j] = fmaf(g[i], yv[i], dot[j]);
+                    d[i] = w[j] * g[i];
+                }
+                store8(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
+            }
+        }
+    }
+    // fixed-order reduction: shuffle tree in each wave, then waves 0..3
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float s = dot[j];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off);
+        if (lane == 0) red[j][wave] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+        const int j = threadIdx.x;
+        float s = red[j][0];
+        for (int wv = 1; wv < static_cast<int>(blockDim.x >> 6); ++wv) s += red[j][wv];
+        gw[static_cast<int64_t>(t) * k + j] = s;
+    }
+}
+
+template <typename TE>
+__global__ __launch_bounds__(256) void permute_bwd_kernel(
+    const TE *__restrict__ gxp, int h, int k, const int32_t *__restrict__ row_of,
+    const float *__restrict__ gl, const int32_t *__restrict__ topk_idx,
+    const TE *__restrict__ wg, int E, TE *__restrict__ gx) {
+    const int t = blockIdx.x;
+    int rows[8], ex[8];
+    float dl[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        ex[j] = -1;
+        dl[j] = 0.0f;
+        if (gl && j < k) {
+            const int e = topk_idx[static_cast<int64_t>(t) * k + j];
+            ex[j] = (e >= 0 && e < E) ? e : -1;
+            dl[j] = gl[static_cast<int64_t>(t) * k + j];
+        }
+    }
+    const int nv = h / 8;
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] >= 0) {
+                float d[8];
+                load8(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += d[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (ex[j] >= 0) {
+                float wv[8];
+                load8(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], wv[i], acc[i]);
+            }
+        }
+        store8(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
+    }
+}
+
+int check_common(const char *fn, int dtype, int64_t T, int64_t h, int k) {
+    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
+                  "%s: bad dtype %d", fn, dtype);
+    MOE_CHECK_ARG(T >= 0 && h > 0 && k > 0, MOE_ERR_INVALID_ARG, "%s: bad sizes", fn);
+    MOE_CHECK_ARG(k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: need k <= 8, h %% 64 == 0", fn);
+    MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && T < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+                  "%s: T*k must be < 2^31", fn);
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int k,
+                             const int32_t *row_of, const float *topk_w, const void *y_sh,
+                             void *out, void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(y && row_of && topk_w && out, MOE_ERR_INVALID_ARG,
+                  "moe_unpermute: null required pointer");
+    int st = check_common("moe_unpermute", dtype, T, h, k);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(aligned16(y) && aligned16(out) && (!y_sh || aligned16(y_sh)), MOE_ERR_INVALID_ARG,
+                  "moe_unpermute: pointers must be 16-byte aligned");
+    if (T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    if (dtype == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL(unpermute_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t *>(y),
+                           static_cast<int>(h), k, row_of, topk_w,
+                           static_cast<const bf16_t *>(y_sh), static_cast<bf16_t *>(out));
+    else
+        hipLaunchKernelGGL(unpermute_kernel<float>, grid, block, 0, s, static_cast<const float *>(y),
+                           static_cast<int>(h), k, row_of, topk_w, static_cast<const float *>(y_sh),
+                           static_cast<float *>(out));
+    return check_launch("moe_unpermute");
+}
+
+extern "C" int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype, int64_t T,
+                                 int64_t h, int k, const int32_t *row_of, const float *topk_w,
+                                 void *grad_y, float *grad_topk_w, void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(grad_out && y && row_of && topk_w && grad_y && grad_topk_w, MOE_ERR_INVALID_ARG,
+                  "moe_unpermute_bwd: null required pointer");
+    int st = check_common("moe_unpermute_bwd", dtype, T, h, k);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(aligned16(grad_out) && aligned16(y) && aligned16(grad_y), MOE_ERR_INVALID_ARG,
+                  "moe_unpermute_bwd: pointers must be 16-byte aligned");
+    if (T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    if (dtype == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL(unpermute_bwd_kernel<bf16_t>, grid, block, 0, s,
+                           static_cast<const bf16_t *>(grad_out), static_cast<const bf16_t *>(y),
+                           static_cast<int>(h), k, row_of, topk_w, static_cast<bf16_t *>(grad_y),
+                           grad_topk_w);
+    else
+        hipLaunchKernelGGL(unpermute_bwd_kernel<float>, grid, block, 0, s,
+                           static_cast<const float *>(grad_out), static_cast<const float *>(y),
+                           static_cast<int>(h), k, row_of, topk_w, static_cast<float *>(grad_y),
+                           grad_topk_w);
+    return check_launch("moe_unpermute_bwd");
+}
+
+extern "C" int moe_permute_bwd(const void *grad_x_perm, int dtype, int64_t T, int64_t h, int k,
+                               const int32_t *row_of, const float *grad_logits_sel,
+                               const int32_t *topk_idx, const void *w_gate, int E, void *grad_x,
+                               void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(grad_x_perm && row_of && grad_x, MOE_ERR_INVALID_ARG,
+                  "moe_permute_bwd: null required pointer");
+    MOE_CHECK_ARG(grad_logits_sel == nullptr || (topk_idx && w_gate && E > 0), MOE_ERR_INVALID_ARG,
+                  "moe_permute_bwd: the router term needs topk_idx, w_gate and E");
+    int st = check_common("moe_permute_bwd", dtype, T, h, k);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(aligned16(grad_x_perm) && aligned16(grad_x) && (!w_gate || aligned16(w_gate)),
+                  MOE_ERR_INVALID_ARG, "moe_permute_bwd: pointers must be 16-byte aligned");
+    if (T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    if (dtype == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, grid, block, 0, s,
+                           static_cast<const bf16_t *>(grad_x_perm), static_cast<int>(h), k, row_of,
+                           grad_logits_sel, topk_idx, static_cast<const bf16_t *>(w_gate), E,
+                           static_cast<bf16_t *>(grad_x));
+    else
+        hipLaunchKernelGGL(permute_bwd_kernel<float>, grid, block, 0, s,
+                           static_cast<const float *>(grad_x_perm), static_cast<int>(h), k, row_of,
+                           grad_logits_sel, topk_idx, static_cast<const float *>(w_gate), E,
+                           static_cast<float *>(grad_x));
+    return check_launch("moe_permute_bwd");
+}

@@ -1,0 +1,190 @@
+// Shared pieces of the grouped GEMM kernels: segment/tile scheduling on the
+// device and the fused epilogues.
+//
+// A grouped GEMM here computes, for every segment s (one expert's rows of the
+// permuted activations, plus optionally the shared expert's rows),
+//   C_s[m, n] = epilogue( sum_k A_s[m, k] * B_s[n, k] )
+// with A_s row-major [M_s, K] and B_s row-major [N, K] (both K-contiguous).
+// Segment sizes are read from `offsets` on the device, so the host never
+// waits for the routing result.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+enum GemmMode { kModePlain = 0, kModeSwiGLU = 1, kModeGELU = 2 };
+
+struct GGArgs {
+    const void *A;          // activations; segment s starts at row offsets[s]
+    const void *B;          // weights, [E][nb_rows][K]
+    const void *bias;       // [E][nb_rows] or null
+    void *C;                // output, rows as A, N_out columns
+    void *GU;               // SwiGLU only: pre-activations [rows][2*N_out] or null
+    const void *A_sh;       // shared-expert segment (M_sh = 0: none)
+    const void *B_sh;
+    void *C_sh;
+    void *GU_sh;
+    int M_sh;
+    const int32_t *offsets; // [E+1]
+    int E;
+    int N_out;              // output columns
+    int K;                  // reduction length
+    int n_tiles;            // ceil(N_out / tile width)
+    int grid;               // blocks launched (persistent)
+};
+
+constexpr int kMaxSeg = 260;
+
+// Builds, in LDS, s_cum[s] = number of tiles of segments < s and returns the
+// total. 256 threads; each thread covers two segments.
+__device__ __forceinline__ int build_tile_prefix(const GGArgs &a, int BM, int *s_cum, int *s_tmp) {
+    const int S = a.E + (a.M_sh > 0 ? 1 : 0);
+    const int t = threadIdx.x;
+    int v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = 2 * t + i;
+        int m = 0;
+        if (s < a.E) m = a.offsets[s + 1] - a.offsets[s];
+        else if (s < S) m = a.M_sh;
+        if (m < 0) m = 0;
+        v[i] = s < S ? ((m + BM - 1) / BM) * a.n_tiles : 0;
+    }
+    s_tmp[t] = v[0] + v[1];
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int add = t >= d ? s_tmp[t - d] : 0;
+        __syncthreads();
+        s_tmp[t] += add;
+        __syncthreads();
+    }
+    const int incl = s_tmp[t];
+    const int excl = incl - v[0] - v[1];
+    if (2 * t < kMaxSeg) s_cum[2 * t] = excl;
+    if (2 * t + 1 < kMaxSeg) s_cum[2 * t + 1] = excl + v[0];
+    __syncthreads();
+    return s_tmp[255];
+}
+
+// Balanced m-tiling of a segment of M rows for tiles of at most 256 rows:
+// nmt = ceil(M/256) tiles of R = ceil(M/nmt) rounded up to 32 rows (the last
+// one shorter). (nmt-1)*R < M always holds because R <= 256.
+__device__ __forceinline__ int bal_ntiles(int M) { return M > 0 ? (M + 255) >> 8 : 0; }
+__device__ __forceinline__ int bal_rows(int M, int nmt) {
+    const int r = (M + nmt - 1) / nmt;
+    return (r + 31) & ~31;
+}
+
+// Same prefix as build_tile_prefix, with the balanced m-tiling. Any block
+// size >= 256: threads 256.. only take part in the barriers.
+__device__ __forceinline__ int build_tile_prefix_bal(const GGArgs &a, int *s_cum, int *s_tmp) {
+    const int S = a.E + (a.M_sh > 0 ? 1 : 0);
+    const int t = threadIdx.x;
+    const bool on = t < 256;
+    int v[2] = {0, 0};
+    if (on) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int s = 2 * t + i;
+            int m = 0;
+            if (s < a.E) m = a.offsets[s + 1] - a.offsets[s];
+            else if (s < S) m = a.M_sh;
+            if (m < 0) m = 0;
+            v[i] = s < S ? bal_ntiles(m) * a.n_tiles : 0;
+        }
+        s_tmp[t] = v[0] + v[1];
+    }
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int add = (on && t >= d) ? s_tmp[t - d] : 0;
+        __syncthreads();
+        if (on) s_tmp[t] += add;
+        __syncthreads();
+    }
+    if (on) {
+        const int excl = s_tmp[t] - v[0] - v[1];
+        if (2 * t < kMaxSeg) s_cum[2 * t] = excl;
+        if (2 * t + 1 < kMaxSeg) s_cum[2 * t + 1] = excl + v[0];
+    }
+    __syncthreads();
+    return s_tmp[255];
+}
+
+// Segment containing tile L: the largest s with s_cum[s] <= L.
+__device__ __forceinline__ int find_segment(const int *s_cum, int S, int L) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cum[mid] <= L) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block b on XCD b % 8).
+// Renumber so that the blocks of one XCD take consecutive tile indices:
+// consecutive tiles share a weight panel, which then stays in that XCD's L2.
+__device__ __forceinline__ int xcd_block_index(int b, int G) {
+    if (G % 8 != 0) return b;
+    return (b % 8) * (G / 8) + b / 8;
+}
+
+struct TileInfo {
+    int seg, m0, n_tile, M, row0;   // row0: first row of the segment in A/C
+    bool shared;
+};
+
+__device__ __forceinline__ TileInfo decode_tile(const GGArgs &a, const int *s_cum, int L, int BM) {
+    const int S = a.E + (a.M_sh > 0 ? 1 : 0);
+    TileInfo ti;
+    ti.seg = find_segment(s_cum, S, L);
+    ti.shared = ti.seg >= a.E;
+    if (ti.shared) {
+        ti.M = a.M_sh;
+        ti.row0 = 0;
+    } else {
+        ti.row0 = a.offsets[ti.seg];
+        ti.M = a.offsets[ti.seg + 1] - ti.row0;
+    }
+    const int mt = (ti.M + BM - 1) / BM;
+    const int local = L - s_cum[ti.seg];
+    // m fastest: consecutive tiles reuse the same weight panel
+    ti.m0 = (local % mt) * BM;
+    ti.n_tile = local / mt;
+    return ti;
+}
+
+struct BalTile {
+    int seg, n_tile, M, row0, row_lo, rows;   // rows [row_lo, row_lo + rows) of the segment
+    bool shared;
+};
+
+__device__ __forceinline__ BalTile decode_tile_bal(const GGArgs &a, const int *s_cum, int L) {
+    const int S = a.E + (a.M_sh > 0 ? 1 : 0);
+    BalTile ti;
+    ti.seg = find_segment(s_cum, S, L);
+    ti.shared = ti.seg >= a.E;
+    if (ti.shared) {
+        ti.M = a.M_sh;
+        ti.row0 = 0;
+    } else {
+        ti.row0 = a.offsets[ti.seg];
+        ti.M = a.offsets[ti.seg + 1] - ti.row0;
+    }
+    const int nmt = bal_ntiles(ti.M);
+    const int R = bal_rows(ti.M, nmt);
+    const int local = L - s_cum[ti.seg];
+    const int mi = local % nmt;   // m fastest: consecutive tiles share a weight panel
+    ti.n_tile = local / nmt;
+    ti.row_lo = mi * R;
+    ti.rows = min(R, ti.M - ti.row_lo);
+    return ti;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float gelu_erf_f(float a) {
+    return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+}
+
+}  // namespace moe

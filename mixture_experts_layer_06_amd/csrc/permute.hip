@@ -1,0 +1,193 @@
+// Dispatch stage: regroup the (token, expert) pairs into expert-contiguous
+// order and copy token rows there ("Scalable Training of Mixture-of-Experts
+// Models with Megatron Core", section 2.1 stage 2; every expert is local, so
+// there is no all-to-all).
+//
+// Row of pair (t, e) = offsets[e] + #{t' < t : t' selected e}, i.e. stable
+// ascending token order inside each expert segment. Four launches, all
+// integer work except the copy:
+//   1. block_hist: per block of 256 tokens, tokens per expert (LDS integer
+//      atomics; order cannot change an integer count).
+//   2. scan: one workgroup; offsets = exclusive prefix over experts, and the
+//      base row of each (block, expert).
+//   3. ranks: per block, a 256-bit mask per expert in LDS; the rank of token
+//      t among the block's tokens of expert e is a popcount of the mask bits
+//      below t. Writes row_of and sorted_token.
+//   4. copy: each token row is read once from HBM and written to its k
+//      permuted rows with 16-byte accesses.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kBlockTok = 256;
+constexpr int kMaxE = 256;
+
+__global__ __launch_bounds__(256) void block_hist_kernel(const int32_t *__restrict__ topk_idx,
+                                                         int T, int E, int k,
+                                                         int32_t *__restrict__ blockcounts) {
+    __shared__ int cnt[kMaxE];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * kBlockTok + threadIdx.x;
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_idx[static_cast<int64_t>(t) * k + j];
+            if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        blockcounts[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// One workgroup of 256 threads; thread e owns expert e.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t *__restrict__ blockcounts,
+                                                   int nb, int E, int32_t *__restrict__ blockbase,
+                                                   int32_t *__restrict__ offsets) {
+    __shared__ int tot[kMaxE];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E)
+        for (int b = 0; b < nb; ++b) run += blockcounts[static_cast<int64_t>(b) * E + e];
+    tot[e] = e < E ? run : 0;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over 256 entries
+    for (int d = 1; d < kMaxE; d <<= 1) {
+        const int v = e >= d ? tot[e - d] : 0;
+        __syncthreads();
+        tot[e] += v;
+        __syncthreads();
+    }
+    if (e < E) {
+        const int start = tot[e] - run;   // exclusive prefix
+        offsets[e] = start;
+        if (e == E - 1) offsets[E] = tot[e];
+        int base = start;
+        for (int b = 0; b < nb; ++b) {
+            blockbase[static_cast<int64_t>(b) * E + e] = base;
+            base += blockcounts[static_cast<int64_t>(b) * E + e];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ topk_idx, int T,
+                                                   int E, int k,
+                                                   const int32_t *__restrict__ blockbase,
+                                                   int P, int32_t *__restrict__ row_of,
+                                                   int32_t *__restrict__ sorted_token) {
+    __shared__ unsigned long long mask[kMaxE][kBlockTok / 64];
+    for (int i = threadIdx.x; i < E * (kBlockTok / 64); i += blockDim.x)
+        (&mask[0][0])[i] = 0ull;
+    __syncthreads();
+    const int lt = threadIdx.x;
+    const int t = blockIdx.x * kBlockTok + lt;
+    const int word = lt >> 6;
+    const unsigned long long bit = 1ull << (lt & 63);
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_idx[static_cast<int64_t>(t) * k + j];
+            if (e >= 0 && e < E) atomicOr(&mask[e][word], bit);
+        }
+    }
+    __syncthreads();
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_idx[static_cast<int64_t>(t) * k + j];
+            int row = -1;
+            if (e >= 0 && e < E) {
+                int rank = __popcll(mask[e][word] & (bit - 1ull));
+                for (int w = 0; w < word; ++w) rank += __popcll(mask[e][w]);
+                row = blockbase[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+                if (row < 0 || row >= P) row = -1;
+            }
+            row_of[static_cast<int64_t>(t) * k + j] = row;
+            if (row >= 0) sorted_token[row] = t;
+        }
+    }
+}
+
+// Block of 256 threads per token row; each thread moves 16-byte pieces.
+template <typename TE>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x, int T,
+                                                        int h, int k,
+                                                        const int32_t *__restrict__ row_of,
+                                                        TE *__restrict__ x_perm) {
+    constexpr int kVec = 16 / sizeof(TE);
+    const int t = blockIdx.x;
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * h);
+    const int nv = h / kVec;
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+        const u32x4 d = __builtin_nontemporal_load(src + v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] >= 0) {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(rows[j]) * h);
+                __builtin_nontemporal_store(d, dst + v);
+            }
+        }
+    }
+    (void)T;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int E, int k) {
+    (void)k;
+    if (T < 0 || E <= 0) return 0;
+    const int64_t nb = (T + kBlockTok - 1) / kBlockTok;
+    return static_cast<size_t>(2 * nb * E) * sizeof(int32_t) + 256;
+}
+
+extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
+                           const int32_t *topk_idx, int32_t *offsets, int32_t *sorted_token,
+                           int32_t *row_of, void *x_perm, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(topk_idx && offsets && sorted_token && row_of, MOE_ERR_INVALID_ARG,
+                  "moe_permute: null required pointer");
+    MOE_CHECK_ARG(x_perm == nullptr || x != nullptr, MOE_ERR_INVALID_ARG,
+                  "moe_permute: x_perm requested without x");
+    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
+                  "moe_permute: bad dtype %d", dtype);
+    MOE_CHECK_ARG(T >= 0 && h > 0 && E > 0 && k > 0, MOE_ERR_INVALID_ARG,
+                  "moe_permute: bad sizes");
+    MOE_CHECK_ARG(k <= E && E <= kMaxE && k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED,
+                  "moe_permute: need k <= E <= 256, k <= 8, h %% 64 == 0");
+    MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+                  "moe_permute: T*k must be < 2^31");
+    const size_t need = moe_permute_workspace_size(T, E, k);
+    MOE_CHECK_ARG(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+                  "moe_permute: workspace of %zu bytes needed", need);
+    MOE_CHECK_ARG(aligned16(workspace) && (x_perm == nullptr || (aligned16(x) && aligned16(x_perm))),
+                  MOE_ERR_INVALID_ARG, "moe_permute: pointers must be 16-byte aligned");
+    hipStream_t s = as_stream(stream);
+    const int nb = static_cast<int>((T + kBlockTok - 1) / kBlockTok);
+    int32_t *blockcounts = static_cast<int32_t *>(workspace);
+    int32_t *blockbase = blockcounts + static_cast<int64_t>(nb) * E;
+    const int P = static_cast<int>(T * k);
+    if (nb > 0)
+        hipLaunchKernelGGL(block_hist_kernel, dim3(nb), dim3(256), 0, s, topk_idx,
+                           static_cast<int>(T), E, k, blockcounts);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blockcounts, nb, E, blockbase, offsets);
+    if (nb > 0)
+        hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(256), 0, s, topk_idx, static_cast<int>(T), E,
+                           k, blockbase, P, row_of, sorted_token);
+    if (x_perm && T > 0) {
+        if (dtype == MOE_DTYPE_BF16)
+            hipLaunchKernelGGL(copy_rows_kernel<bf16_t>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
+                               s, static_cast<const bf16_t *>(x), static_cast<int>(T),
+                               static_cast<int>(h), k, row_of, static_cast<bf16_t *>(x_perm));
+        else
+            hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
+                               s, static_cast<const float *>(x), static_cast<int>(T),
+                               static_cast<int>(h), k, row_of, static_cast<float *>(x_perm));
+    }
+    return check_launch("moe_permute");
+}

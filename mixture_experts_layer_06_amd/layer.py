@@ -1,0 +1,50 @@
+"""The whole MoE layer as a chain of C-ABI calls (Route -> Permute -> Grouped
+FFN -> Unpermute, and the backward in reverse), on torch's current stream.
+
+Only orchestration lives here: every step runs in libmoe.so's HIP kernels.
+The stage order is that of "Scalable Training of Mixture-of-Experts Models
+with Megatron Core", section 2.1.
+"""
+from __future__ import annotations
+
+from . import binding as B
+
+
+def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False):
+    """One forward pass. ``inp`` holds device tensors named as in
+    ``workloads.make_inputs``. Returns a dict with ``out`` and the
+    intermediate results of every stage."""
+    x = inp["x"]
+    E = inp["w_gate"].shape[0]
+    r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
+                    sel_bias=inp.get("sel_bias"), want_logits=keep_for_backward)
+    p = B.moe_permute(x, r["topk_idx"], E)
+    has_sh = inp.get("w1_sh") is not None
+    f = B.moe_grouped_ffn(p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act,
+                          b1=inp.get("b1"), b2=inp.get("b2"),
+                          x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"),
+                          w2_sh=inp.get("w2_sh"),
+                          keep_gu=keep_for_backward and act == "swiglu")
+    out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"])
+    res = dict(out=out)
+    res.update(r)
+    res.update(p)
+    res.update(f)
+    return res
+
+
+def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str):
+    """Gradients of sum(grad_out * out) for a forward run with
+    keep_for_backward=True (routed experts; no shared expert)."""
+    E = inp["w_gate"].shape[0]
+    grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
+    g = B.moe_grouped_ffn_bwd(grad_y, fwd["x_perm"], fwd["act"], fwd["gu"], fwd["offsets"],
+                              inp["w1"], inp["w2"], act)
+    r = B.moe_route_bwd(inp["x"], E, fwd["topk_idx"], fwd["topk_w"], grad_w, fwd["offsets"],
+                        fwd["sorted_token"], score=score, logits=fwd.get("logits"),
+                        want_b_grad=inp.get("b_gate") is not None)
+    grad_x = B.moe_permute_bwd(g["grad_x_perm"], fwd["row_of"], r["grad_logits_sel"],
+                               fwd["topk_idx"], inp["w_gate"])
+    return dict(grad_x=grad_x, grad_topk_w=grad_w, grad_y=grad_y, grad_w1=g["grad_w1"],
+                grad_w2=g["grad_w2"], grad_w_gate=r["grad_w_gate"], grad_b_gate=r["grad_b_gate"],
+                grad_logits_sel=r["grad_logits_sel"])

@@ -7,6 +7,7 @@ library and never imports it.
 from .moe import (  # noqa: F401
     backward,
     build,
+    combine,
     exp_c,
     expert_backward,
     expert_forward,

@@ -306,6 +306,19 @@ def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bi
     return res
 
 
+def combine(y_perm, row_of, topk_w, y_shared=None):
+    """Combine stage on its own (fp64): out[t] = sum_j w[t,j] y_perm[row_of[t,j]]
+    (+ y_shared[t]), j ascending."""
+    y_perm = np.asarray(y_perm, dtype=np.float64)
+    T, k = row_of.shape
+    out = np.zeros((T, y_perm.shape[1]), dtype=np.float64)
+    for j in range(k):
+        out += np.asarray(topk_w, dtype=np.float64)[:, j:j + 1] * y_perm[np.asarray(row_of)[:, j]]
+    if y_shared is not None:
+        out += np.asarray(y_shared, dtype=np.float64)
+    return out
+
+
 # ------------------------------------------------------------------ backward
 
 def _dsilu(g):

@@ -1,0 +1,220 @@
+"""GPU parity of the forward path, through the C ABI, against the CPU oracle.
+
+Routing (logits, top-k indices, routing map, counts) and the permutation
+indices must match bit for bit; floating-point outputs within 2e-2 (bf16) or
+1e-4 (fp32) under the error measure of tests/parity.py. Shapes are reduced
+versions of the five workloads that the oracle finishes in seconds, chosen to
+span several tiles with ragged tails."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_06_amd import workloads as wl
+from parity import TOL, oracle_inputs, rel_err, to_device, to_np32
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "c1": (wl.CONFIGS[1], {}),
+    "c1_bias": (wl.CONFIGS[1], {"nonzero_expert_bias": True}),
+    "c2s": (wl.small_variant(wl.CONFIGS[2], T=600, h=256, F=384), {}),
+    "c3s": (wl.small_variant(wl.CONFIGS[3], T=1000, h=512, F=192), {}),
+    "c4s": (wl.small_variant(wl.CONFIGS[4], T=520, h=448, F=128), {}),
+    "c5s": (wl.small_variant(wl.CONFIGS[5], T=300, h=256, F=128, E=32), {}),
+}
+
+_cache = {}
+
+
+def _run(name):
+    if name in _cache:
+        return _cache[name]
+    print("case", name, flush=True)
+    sys.stdout.flush()
+    cfg, kw = CASES[name]
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=False, **kw)
+    dinp = to_device(inp)
+    from mixture_experts_layer_06_amd import layer
+    g = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True)
+    torch.cuda.synchronize()
+    o = oracle_inputs(inp)
+    ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                         b_gate=o["b_gate"], sel_bias=o["sel_bias"], b1=o["b1"], b2=o["b2"],
+                         w1_sh=o["w1_sh"], w2_sh=o["w2_sh"])
+    perm = oracle.permutation(ref["topk_idx"], cfg.E)
+    _cache[name] = (cfg, inp, g, ref, perm)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_parity(moe_lib, name):
+    cfg, inp, g, ref, perm = _run(name)
+    logits = g["logits"].cpu().numpy()
+    assert np.array_equal(logits.view(np.uint32), ref["logits"].view(np.uint32)), \
+        "gate logits differ bitwise"
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(g["counts"].cpu().numpy(), ref["counts"])
+    assert rel_err(g["topk_w"].cpu().numpy(), ref["topk_w"]) <= 1e-5
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_permute_parity(moe_lib, name):
+    cfg, inp, g, ref, perm = _run(name)
+    assert np.array_equal(g["offsets"].cpu().numpy(), perm["offsets"])
+    assert np.array_equal(g["sorted_token"].cpu().numpy(), perm["sorted_token"])
+    assert np.array_equal(g["row_of"].cpu().numpy(), perm["row_of"])
+    xp = g["x_perm"].cpu()
+    assert torch.equal(xp, inp["x"][torch.as_tensor(perm["sorted_token"])])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_grouped_ffn_parity(moe_lib, name):
+    cfg, inp, g, ref, perm = _run(name)
+    y = to_np32(g["y"])
+    T, k = ref["topk_idx"].shape
+    y_ref = np.zeros_like(y, dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            y_ref[perm["row_of"][t, j]] = ref["y_pair"][t, j]
+    err = rel_err(y, y_ref)
+    assert err <= TOL[cfg.dtype], err
+    if cfg.n_shared:
+        err = rel_err(to_np32(g["y_sh"]), ref["y_shared"])
+        assert err <= TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_output_parity(moe_lib, name):
+    cfg, inp, g, ref, perm = _run(name)
+    err = rel_err(to_np32(g["out"]), ref["out"])
+    assert err <= TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_unpermute_alone(moe_lib, dtype):
+    """Combine stage fed with seeded expert outputs (not the GPU's)."""
+    from mixture_experts_layer_06_amd import binding as B
+    rng = np.random.default_rng(3)
+    T, h, E, k = 333, 192, 12, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    perm = oracle.permutation(idx, E)
+    y = torch.randn(T * k, h, generator=torch.Generator().manual_seed(5)).to(dtype)
+    y_sh = torch.randn(T, h, generator=torch.Generator().manual_seed(6)).to(dtype)
+    row_of = torch.as_tensor(perm["row_of"].astype(np.int32)).cuda()
+    out = B.moe_unpermute(y.cuda(), row_of, torch.as_tensor(w).cuda(), y_sh=y_sh.cuda())
+    ref = oracle.combine(to_np32(y), perm["row_of"], w, to_np32(y_sh))
+    tol = TOL["bf16" if dtype == torch.bfloat16 else "f32"]
+    assert rel_err(to_np32(out), ref) <= tol
+
+
+def _route_only(x, wg, k, score="softmax", b_gate=None, sel_bias=None):
+    from mixture_experts_layer_06_amd import binding as B
+    r = B.moe_route(x.cuda(), wg.cuda(), k, score,
+                    b_gate=None if b_gate is None else b_gate.cuda(),
+                    sel_bias=None if sel_bias is None else sel_bias.cuda(),
+                    want_logits=True, want_map=True)
+    torch.cuda.synchronize()
+    ref = oracle.route(to_np32(x), to_np32(wg), k, score,
+                       None if b_gate is None else b_gate.numpy(),
+                       None if sel_bias is None else sel_bias.numpy())
+    return r, ref
+
+
+def _assert_route_equal(r, ref):
+    assert np.array_equal(r["logits"].cpu().numpy().view(np.uint32), ref["logits"].view(np.uint32))
+    assert np.array_equal(r["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(r["routing_map"].cpu().numpy(), ref["routing_map"])
+    assert np.array_equal(r["counts"].cpu().numpy(), ref["counts"])
+
+
+def test_route_adversarial_ties(moe_lib):
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(257, 128, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(16, 128, generator=g) / 11).to(torch.bfloat16)
+    wg[5] = wg[2]
+    wg[9] = wg[2]        # exact ties: lowest index first
+    x[3] = 0             # all logits equal
+    x[100] = -0.0
+    r, ref = _route_only(x, wg, 4)
+    _assert_route_equal(r, ref)
+    assert list(r["topk_idx"][3].cpu().numpy()) == [0, 1, 2, 3]
+
+
+def test_route_one_ulp_apart(moe_lib):
+    x = torch.zeros(4, 64, dtype=torch.float32)
+    x[:, 0] = 1.0
+    wg = torch.zeros(6, 64, dtype=torch.float32)
+    wg[:, 0] = 1.0
+    wg[4, 0] = float(np.nextafter(np.float32(1), np.float32(2)))
+    r, ref = _route_only(x, wg, 2)
+    _assert_route_equal(r, ref)
+    assert list(r["topk_idx"][0].cpu().numpy()) == [4, 0]
+
+
+def test_route_sigmoid_bias_ties_and_k_equals_e(moe_lib):
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn(130, 256, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(8, 256, generator=g) / 16).to(torch.bfloat16)
+    bias = (torch.rand(8, generator=g) * 0.2 - 0.1).float()
+    bias[3] = bias[6]
+    r, ref = _route_only(x, wg, 8, "sigmoid", sel_bias=bias)
+    _assert_route_equal(r, ref)
+    assert rel_err(r["topk_w"].cpu().numpy(), ref["topk_w"]) <= 1e-5
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (256, 8), (64, 1)])
+def test_layer_edge_shapes(moe_lib, E, k):
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[3], T=77, h=128, F=64, E=E, k=k)
+    inp = wl.make_inputs(cfg, device="cpu", variant=E + k)
+    g = layer.forward(to_device(inp), k, cfg.score, cfg.act)
+    o = oracle_inputs(inp)
+    ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], k, cfg.score, cfg.act)
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert rel_err(to_np32(g["out"]), ref["out"]) <= TOL["bf16"]
+
+
+def test_layer_all_tokens_to_one_expert_and_empty_experts(moe_lib):
+    """A dominant gate bias sends every token to expert 5 first: one segment
+    holds all T rows, many segments are empty."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[5], T=700, h=128, F=128, E=16, k=2)
+    inp = wl.make_inputs(cfg, device="cpu")
+    b = torch.full((16,), -30.0)
+    b[5] = 30.0
+    b[11] = 0.0
+    inp["b_gate"] = b
+    g = layer.forward(to_device(inp), cfg.k, cfg.score, cfg.act)
+    o = oracle_inputs(inp)
+    ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                         b_gate=o["b_gate"])
+    counts = g["counts"].cpu().numpy()
+    assert counts[5] == 700 and counts[11] == 700 and counts.sum() == 1400
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert rel_err(to_np32(g["out"]), ref["out"]) <= TOL["bf16"]
+
+
+def test_single_token(moe_lib):
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[4], T=1, h=256, F=128, E=32, k=8)
+    inp = wl.make_inputs(cfg, device="cpu")
+    g = layer.forward(to_device(inp), cfg.k, cfg.score, cfg.act)
+    o = oracle_inputs(inp)
+    ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                         sel_bias=o["sel_bias"], w1_sh=o["w1_sh"], w2_sh=o["w2_sh"])
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert rel_err(to_np32(g["out"]), ref["out"]) <= TOL["bf16"]
+
+
+def test_forward_is_deterministic(moe_lib):
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[3], T=512, h=256, F=128)
+    inp = to_device(wl.make_inputs(cfg, device="cpu"))
+    a = layer.forward(inp, cfg.k, cfg.score, cfg.act)
+    b = layer.forward(inp, cfg.k, cfg.score, cfg.act)
+    for key in ("out", "y", "act", "topk_w", "row_of"):
+        assert torch.equal(a[key], b[key]), key

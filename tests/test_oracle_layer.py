@@ -302,3 +302,16 @@ def test_imbalanced_workload_realises_zipf_load():
     s = -np.polyfit(np.log(ranks), np.log(live), 1)[0]
     assert 1.1 <= s <= 1.3, s
     assert c.sum() == cfg.T * cfg.k
+
+
+def test_combine_matches_forward():
+    rng = np.random.default_rng(59)
+    x, wg, w1, w2, _, _ = _rand_layer(rng, 30, 32, 6, 16, "swiglu")
+    r = oracle.forward(x, wg, w1, w2, 3, "softmax", "swiglu")
+    p = oracle.permutation(r["topk_idx"], 6)
+    y_perm = np.zeros((30 * 3, 32))
+    for t in range(30):
+        for j in range(3):
+            y_perm[p["row_of"][t, j]] = r["y_pair"][t, j]
+    assert np.allclose(oracle.combine(y_perm, p["row_of"], r["topk_w"]), r["out"], rtol=1e-13,
+                       atol=1e-13)

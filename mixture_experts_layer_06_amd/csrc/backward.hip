@@ -211,11 +211,3 @@ extern "C" int moe_route_bwd(const void *x, int dtype, int64_t T, int64_t h, int
     return check_launch("moe_route_bwd");
 }
 
-// Grouped FFN backward: not available yet.
-extern "C" int moe_grouped_ffn_bwd(const void *, const void *, const void *, const void *, int,
-                                   int64_t, int64_t, int64_t, int, const int32_t *, int, const void *,
-                                   const void *, void *, void *, float *, float *, void *) {
-    clear_error();
-    set_error("moe_grouped_ffn_bwd: not implemented in this build");
-    return MOE_ERR_UNSUPPORTED;
-}

@@ -39,6 +39,16 @@ def rel_err(got, ref) -> float:
     return float(max(whole, rows.max()))
 
 
+def rel_err_tensor(got, ref) -> float:
+    """max |got - ref| / max |ref| over the whole tensor."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    amax = np.abs(ref).max() if ref.size else 0.0
+    d = np.abs(got - ref).max() if ref.size else 0.0
+    return float(d / amax) if amax > 0 else float(d)
+
+
 def oracle_inputs(inp: dict) -> dict:
     """numpy fp32 views of the seeded tensors, named as the oracle's arguments."""
     return dict(x=to_np32(inp["x"]), w_gate=to_np32(inp["w_gate"]),

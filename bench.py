@@ -130,12 +130,16 @@ def main():
     cfg = wl.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = wl.make_inputs(cfg, device=dev, with_grad_out=False)
+    inp = wl.make_inputs(cfg, device=dev)
     es = 2 if cfg.dtype == "bf16" else 4
-    flops = cfg.active_flops_forward()
+    train = cfg.backward
+    flops = cfg.active_flops_forward() + (cfg.active_flops_backward() if train else 0.0)
 
     def step():
-        return layer.forward(inp, cfg.k, cfg.score, cfg.act)
+        f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train)
+        if train:
+            layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act)
+        return f
 
     for _ in range(args.warmup):
         step()
@@ -162,7 +166,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.h, "experts": cfg.E,
                    "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
-                   "shared_experts": cfg.n_shared},
+                   "shared_experts": cfg.n_shared,
+                   "step": "forward + backward" if train else "forward"},
         "tokens_per_s": cfg.T / dt,
         "frac_of_bf16_peak": flops / dt / 1e12 / PEAK_BF16_TFLOPS,
         "active_gflop_per_step": flops / 1e9,
@@ -190,6 +195,24 @@ def main():
                 w2_sh=inp.get("w2_sh")),
             "unpermute": lambda: B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"]),
         }
+        if train:
+            f2 = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=True)
+            gy, gw = B.moe_unpermute_bwd(inp["grad_out"], f2["y"], f2["row_of"], f2["topk_w"])
+            gf = B.moe_grouped_ffn_bwd(gy, f2["x_perm"], f2["act"], f2["gu"], f2["offsets"],
+                                       inp["w1"], inp["w2"], cfg.act)
+            gr = B.moe_route_bwd(inp["x"], E, f2["topk_idx"], f2["topk_w"], gw, f2["offsets"],
+                                 f2["sorted_token"], score=cfg.score, logits=f2["logits"],
+                                 want_b_grad=inp.get("b_gate") is not None)
+            calls["unpermute_bwd"] = lambda: B.moe_unpermute_bwd(inp["grad_out"], f2["y"],
+                                                                 f2["row_of"], f2["topk_w"])
+            calls["grouped_ffn_bwd"] = lambda: B.moe_grouped_ffn_bwd(
+                gy, f2["x_perm"], f2["act"], f2["gu"], f2["offsets"], inp["w1"], inp["w2"], cfg.act)
+            calls["route_bwd"] = lambda: B.moe_route_bwd(
+                inp["x"], E, f2["topk_idx"], f2["topk_w"], gw, f2["offsets"], f2["sorted_token"],
+                score=cfg.score, logits=f2["logits"], want_b_grad=inp.get("b_gate") is not None)
+            calls["permute_bwd"] = lambda: B.moe_permute_bwd(gf["grad_x_perm"], f2["row_of"],
+                                                             gr["grad_logits_sel"], f2["topk_idx"],
+                                                             inp["w_gate"])
         stages = {}
         for name, fn in calls.items():
             fn()
@@ -216,6 +239,12 @@ def main():
         stages["grouped_ffn"]["tflops"] = ff / t / 1e12
         stages["grouped_ffn"]["mfma_frac"] = ff / t / 1e12 / peak
         stages["grouped_ffn"]["weight_gb_per_s"] = ffn_weight_bytes(cfg, es) / t / 1e9
+        if train:
+            nmat = 3 if cfg.act == "swiglu" else 2
+            bflops = 2.0 * cfg.P * nmat * 2.0 * cfg.h * cfg.F
+            t = stages["grouped_ffn_bwd"]["s_median"]
+            stages["grouped_ffn_bwd"]["tflops"] = bflops / t / 1e12
+            stages["grouped_ffn_bwd"]["mfma_frac"] = bflops / t / 1e12 / peak
         out["stages"] = stages
         out["roofline"] = {
             "kernel": "grouped_ffn: grouped_gemm_bf16 SwiGLU + plain launches",

@@ -6,21 +6,21 @@
 // matrices) or GELU(erf) experts with biases ("emerging-techniques-moe-
 // training", Quick Start).
 //
-// bf16 kernel, CDNA4 (gfx950):
-// - MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulators. The weight tile is the
-//   MFMA "A" operand and the token tile the "B" operand, so a lane's four
-//   accumulators are four consecutive output columns of one token row and the
-//   epilogue writes 8-byte row pieces.
-// - Tiles BM tokens x BN weight rows x 64 deep; 4 waves in a 2 x 2 grid.
-//   Operands are staged global -> registers -> LDS (double-buffered, one
-//   barrier per k-step) with 16-byte accesses; LDS rows are 128 bytes and
-//   16-byte chunk c of row r is stored at chunk c ^ (r % 8), so the 16 rows a
-//   fragment read touches fall in distinct bank groups.
-// - SwiGLU: the weight tile interleaves 16-row blocks of gate rows and up rows
-//   of the same 16 output columns, so each lane holds the gate and up values
-//   of the same output element and applies silu(g) * u in registers.
-// - Persistent blocks walk a device-built tile list (segments x m-tiles x
-//   n-tiles, m fastest) with XCD-aware numbering.
+// bf16 kernel, CDNA4 (gfx950), one persistent launch per projection:
+// - every expert segment (and the shared expert's rows) is cut into balanced
+//   tiles of at most 256 token rows; tiles are 256 weight rows wide; the tile
+//   list is built on the device from the segment offsets, numbered m-fastest
+//   (consecutive tiles share a weight panel) and mapped so that the blocks of
+//   one XCD take consecutive tiles (their shared panels stay in that XCD's L2);
+// - 8 waves per block, v_mfma_f32_32x32x16_bf16 with fp32 accumulators; the
+//   weight tile is the MFMA "A" operand, so a lane's accumulators are runs of
+//   4 consecutive output columns of one token row;
+// - operands reach LDS through global_load_lds_dwordx4 in a 4-stage ring
+//   (details at the kernel);
+// - SwiGLU: the weight tile interleaves 32-row blocks of gate rows and up rows
+//   of the same 32 output columns, so each lane holds the gate and up values
+//   of the same output element and applies silu(g) * u in registers; GELU and
+//   biases are applied in the same epilogue.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -31,21 +31,50 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// Tile: 256 weight rows (n) x up to 256 token rows (m) x 64 deep, 8 waves.
-// Wave w owns weight rows [64 (w%4), +64) (two 32-row MFMA subtiles) and
+// Tile: 256 weight rows (n) x up to 256 token rows (m), 8 waves. Wave w owns
+// weight rows [64 (w%4), +64) of the tile (two 32-row MFMA subtiles) and
 // token rows [128 (w/4), +128) (four 32-row subtiles). Waves w and w+4 share a
 // SIMD, so a tile with few rows leaves half of each SIMD's work undone rather
 // than idling whole SIMDs; subtiles past the tile's row count are skipped.
+//
 // MFMA v_mfma_f32_32x32x16_bf16: lane l supplies row l%32, k = 8(l/32)..+7
 // of each operand; accumulator element i of lane l is row
 // 8(i/4) + 4(l/32) + i%4 (weight row) and column l%32 (token row).
+//
+// Operand staging: a ring of kStages LDS stages, each 256 weight rows and 256
+// token rows of kBK = 32 bf16 (64-byte rows, four 16-byte chunks; chunk c of
+// row r sits at chunk c ^ ((r >> 2) & 3), so the 16 rows one read phase
+// touches cover all 64 banks). Global -> LDS moves use global_load_lds_dwordx4:
+// one instruction fills 1 KB of LDS (16 rows) with lane l's 16 bytes at byte
+// 16 l, so each lane fetches the global chunk that the swizzle puts there. No
+// VGPR staging, no ds_write. Loads run kStages - 1 k-steps ahead; a k-step
+// waits only for its own stage (s_waitcnt vmcnt on the wave's later loads,
+// then s_barrier).
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+
+#define MOE_AS3(p) ((__attribute__((address_space(3))) void *)(p))
+
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ ((r >> 2) & 3)) << 3); }
+
+// s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15 = no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16(GGArgs a) {
-    constexpr int BK = 64;
     constexpr int TILE = 256;
     constexpr int NS = 2, MS = 4;
-    constexpr int STAGE = 2 * TILE * BK;        // elements per LDS stage (weights + tokens)
-    __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+    constexpr int STAGE = 2 * TILE * kBK;       // elements per LDS stage (weights + tokens)
+    // one array per stage: the compiler then sees which stage a pending
+    // global->LDS load writes and does not wait for all of them before a read
+    __shared__ __attribute__((aligned(16))) bf16_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t st1[STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t st2[STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t st3[STAGE];
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
 
@@ -58,38 +87,47 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16(GGArgs a) {
     const int total = build_tile_prefix_bal(a, s_cum, s_tmp);
     const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
     const int K = a.K;
-    const int nk = K / BK;
-    const int chunk = tid & 7;
-    const int rbase = tid >> 3;                 // rows rbase and rbase + 64 of each operand
+    const int nk = K / kBK;
+    // this wave fills LDS regions 4w..4w+3 of each stage (16 rows each):
+    // waves 0..3 the weight rows, waves 4..7 the token rows
+    const bool fills_w = wave < 4;
+    const int prow0 = (wave & 3) * 64 + (lane >> 2);   // tile row of load i: prow0 + 16 i
+    const int pchunk = lane & 3;
 
     for (int L = xcd_block_index(blockIdx.x, a.grid); L < total; L += a.grid) {
         const BalTile ti = decode_tile_bal(a, s_cum, L);
         const int nact = (ti.rows + 31) >> 5;   // active 32-row token subtiles of the tile
         int nw = nact - wm * MS;                // ... of this wave
         nw = nw < 0 ? 0 : (nw > MS ? MS : nw);
-        const bf16_t *Aseg = ti.shared ? static_cast<const bf16_t *>(a.A_sh)
-                                       : static_cast<const bf16_t *>(a.A) + static_cast<int64_t>(ti.row0) * K;
-        const bf16_t *xb = Aseg + static_cast<int64_t>(ti.row_lo) * K + chunk * 8;
-        const bf16_t *wb = (ti.shared ? static_cast<const bf16_t *>(a.B_sh)
-                                      : static_cast<const bf16_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K) +
-                           chunk * 8;
-        int woff[4], xoff[4], soff[4];
+
+        // global source of each of this lane's 4 chunks per stage
+        const bf16_t *src[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = rbase + 64 * j;
-            int wrow;
-            if (MODE == kModeSwiGLU) {
-                const int f = ti.n_tile * (TILE / 2) + (r >> 6) * 32 + (r & 31);
-                wrow = ((r >> 5) & 1) ? a.N_out + f : f;
-                if (f >= a.N_out) wrow = 0;
+        for (int i = 0; i < 4; ++i) {
+            const int r = prow0 + 16 * i;                       // tile row
+            const int c = pchunk ^ ((r >> 2) & 3);              // logical 16-byte chunk
+            if (fills_w) {
+                int wrow;
+                if (MODE == kModeSwiGLU) {
+                    const int f = ti.n_tile * (TILE / 2) + (r >> 6) * 32 + (r & 31);
+                    wrow = ((r >> 5) & 1) ? a.N_out + f : f;
+                    if (f >= a.N_out) wrow = 0;
+                } else {
+                    wrow = ti.n_tile * TILE + r;
+                    if (wrow >= nb_rows) wrow = 0;
+                }
+                const bf16_t *Bseg = ti.shared ? static_cast<const bf16_t *>(a.B_sh)
+                                               : static_cast<const bf16_t *>(a.B) +
+                                                     static_cast<int64_t>(ti.seg) * nb_rows * K;
+                src[i] = Bseg + static_cast<int64_t>(wrow) * K + c * 8;
             } else {
-                wrow = ti.n_tile * TILE + r;
-                if (wrow >= nb_rows) wrow = 0;
+                const bf16_t *Aseg = ti.shared ? static_cast<const bf16_t *>(a.A_sh)
+                                               : static_cast<const bf16_t *>(a.A) + static_cast<int64_t>(ti.row0) * K;
+                const int m = r < ti.rows ? r : ti.rows - 1;   // clamped: in bounds, never stored
+                src[i] = Aseg + (static_cast<int64_t>(ti.row_lo) + m) * K + c * 8;
             }
-            woff[j] = wrow * K;
-            xoff[j] = (r < ti.rows ? r : ti.rows - 1) * K;
-            soff[j] = r * BK + ((chunk ^ (r & 7)) << 3);
         }
+        const int dsto = (fills_w ? 0 : TILE * kBK) + (wave & 3) * 64 * kBK;   // region of load 0
 
         floatx16 acc[NS][MS];
 #pragma unroll
@@ -99,76 +137,81 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16(GGArgs a) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-        // rows past the tile were clamped to its last row above: every load is
-        // in bounds and unconditional (their products land in skipped subtiles
-        // or in rows the epilogue does not store)
-        u32x4 rw[4], rx[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            rw[j] = *reinterpret_cast<const u32x4 *>(wb + woff[j]);
-            rx[j] = *reinterpret_cast<const u32x4 *>(xb + xoff[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<u32x4 *>(smem + soff[j]) = rw[j];
-            *reinterpret_cast<u32x4 *>(smem + TILE * BK + soff[j]) = rx[j];
-        }
-        __syncthreads();
+#define MOE_FILL(ARR, KT)                                                                       \
+    do {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
+            __builtin_amdgcn_global_load_lds(src[i] + (KT) * kBK, MOE_AS3(ARR + dsto + 16 * i * kBK), 16, 0, 0); \
+    } while (0)
 
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = (kt & 1) * STAGE;
-            if (kt + 1 < nk) {
-                const int ko = (kt + 1) * BK;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    rw[j] = *reinterpret_cast<const u32x4 *>(wb + woff[j] + ko);
-                    rx[j] = *reinterpret_cast<const u32x4 *>(xb + xoff[j] + ko);
-                }
-            }
-            const bf16_t *sw = smem + cur;
-            const bf16_t *sx = smem + cur + TILE * BK;
-            if (nw > 0) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int ch = ks * 2 + lhi;
-                    bf16x8_t af[NS], bfr[MS];
-#pragma unroll
-                    for (int i = 0; i < NS; ++i) {
-                        const int r = wn * 64 + i * 32 + l32;
-                        af[i] = *reinterpret_cast<const bf16x8_t *>(sw + r * BK + ((ch ^ (r & 7)) << 3));
-                    }
-#pragma unroll
-                    for (int j = 0; j < MS; ++j) {
-                        const int r = wm * 128 + j * 32 + l32;
-                        bfr[j] = *reinterpret_cast<const bf16x8_t *>(sx + r * BK + ((ch ^ (r & 7)) << 3));
-                    }
-                    if (nw == MS) {
-#pragma unroll
-                        for (int j = 0; j < MS; ++j)
-#pragma unroll
-                            for (int i = 0; i < NS; ++i)
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < MS; ++j)
-                            if (j < nw)
-#pragma unroll
-                                for (int i = 0; i < NS; ++i)
-                                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                    }
-                }
-            }
-            if (kt + 1 < nk) {
-                const int nxt = ((kt + 1) & 1) * STAGE;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    *reinterpret_cast<u32x4 *>(smem + nxt + soff[j]) = rw[j];
-                    *reinterpret_cast<u32x4 *>(smem + nxt + TILE * BK + soff[j]) = rx[j];
-                }
-            }
-            __syncthreads();
-        }
+        // prologue: stages 0 .. kStages-2
+        if (0 < nk) MOE_FILL(st0, 0);
+        if (1 < nk) MOE_FILL(st1, 1);
+        if (2 < nk) MOE_FILL(st2, 2);
 
+// One k-step on stage CUR; refills NXT (the stage read one step earlier)
+// with k-step KT + kStages - 1. UNIFORM: every step issues its loads (the
+// tail re-fetches the last k-step into a stage nobody reads again), so the
+// wave always waits for exactly the 8 later loads and the compiler can prove
+// that the stage being read has landed.
+#define MOE_KSTEP(CUR, NXT, KT, UNIFORM)                                                        \
+    do {                                                                                      \
+        const int kt_ = (KT);                                                                 \
+        if (UNIFORM) {                                                                        \
+            wait_vmcnt<8>();                                                                  \
+        } else {                                                                              \
+            const int later_ = nk - 1 - kt_;                                                  \
+            if (later_ >= 2) wait_vmcnt<8>();                                                 \
+            else if (later_ == 1) wait_vmcnt<4>();                                            \
+            else wait_vmcnt<0>();                                                             \
+        }                                                                                     \
+        __builtin_amdgcn_s_barrier();                                                         \
+        if (UNIFORM) MOE_FILL(NXT, min(kt_ + kStages - 1, nk - 1));                           \
+        else if (kt_ + kStages - 1 < nk) MOE_FILL(NXT, kt_ + kStages - 1);                    \
+        if (nw > 0) {                                                                         \
+            const bf16_t *sw_ = CUR;                                                          \
+            const bf16_t *sx_ = CUR + TILE * kBK;                                             \
+            _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                \
+                const int ch = ks * 2 + lhi;                                                  \
+                bf16x8_t af[NS], bfr[MS];                                                     \
+                _Pragma("unroll") for (int i = 0; i < NS; ++i)                                \
+                    af[i] = *reinterpret_cast<const bf16x8_t *>(sw_ + lds_off(wn * 64 + i * 32 + l32, ch)); \
+                _Pragma("unroll") for (int j = 0; j < MS; ++j)                                \
+                    bfr[j] = *reinterpret_cast<const bf16x8_t *>(sx_ + lds_off(wm * 128 + j * 32 + l32, ch)); \
+                if (nw == MS) {                                                               \
+                    _Pragma("unroll") for (int j = 0; j < MS; ++j)                            \
+                        _Pragma("unroll") for (int i = 0; i < NS; ++i)                        \
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+                } else {                                                                      \
+                    _Pragma("unroll") for (int j = 0; j < MS; ++j)                            \
+                        if (j < nw)                                                           \
+                            _Pragma("unroll") for (int i = 0; i < NS; ++i)                    \
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+                }                                                                             \
+            }                                                                                 \
+        }                                                                                     \
+    } while (0)
+
+        if (nk % kStages == 0) {
+            for (int kt = 0; kt < nk; kt += kStages) {
+                MOE_KSTEP(st0, st3, kt, true);
+                MOE_KSTEP(st1, st0, kt + 1, true);
+                MOE_KSTEP(st2, st1, kt + 2, true);
+                MOE_KSTEP(st3, st2, kt + 3, true);
+            }
+        } else {
+            for (int kt = 0; kt < nk; kt += kStages) {
+                MOE_KSTEP(st0, st3, kt, false);
+                if (kt + 1 < nk) MOE_KSTEP(st1, st0, kt + 1, false);
+                if (kt + 2 < nk) MOE_KSTEP(st2, st1, kt + 2, false);
+                if (kt + 3 < nk) MOE_KSTEP(st3, st2, kt + 3, false);
+            }
+        }
+#undef MOE_KSTEP
+#undef MOE_FILL
+        // drain the tail loads and make sure every wave is past its last read
+        // of the ring before the next tile starts refilling it
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
         // ------------------------------------------------------- epilogue
         const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.row_lo;
         bf16_t *Cseg = ti.shared ? static_cast<bf16_t *>(a.C_sh) + static_cast<int64_t>(ti.row_lo) * a.N_out

@@ -61,7 +61,7 @@ __device__ __forceinline__ u32x4 column8(const u32x4 *in, int c) {
     return o;
 }
 
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
 
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void bwd_gemm(BGArgs a) {

@@ -7,16 +7,20 @@
 // training", Quick Start).
 //
 // bf16 kernel, CDNA4 (gfx950), one persistent launch per projection:
-// - every expert segment (and the shared expert's rows) is cut into balanced
-//   tiles of at most 256 token rows; tiles are 256 weight rows wide; the tile
-//   list is built on the device from the segment offsets, numbered m-fastest
-//   (consecutive tiles share a weight panel) and mapped so that the blocks of
-//   one XCD take consecutive tiles (their shared panels stay in that XCD's L2);
-// - 8 waves per block, v_mfma_f32_32x32x16_bf16 with fp32 accumulators; the
-//   weight tile is the MFMA "A" operand, so a lane's accumulators are runs of
-//   4 consecutive output columns of one token row;
-// - operands reach LDS through global_load_lds_dwordx4 in a 4-stage ring
-//   (details at the kernel);
+// - every expert segment (and the shared expert's rows) is cut into tiles of
+//   256 token rows (the last one shorter); tiles are 256 weight rows wide; the
+//   tile list is built on the device from the segment offsets, numbered
+//   m-fastest (consecutive tiles share a weight panel) and mapped so that the
+//   blocks of one XCD take consecutive tiles (their shared panels stay in that
+//   XCD's L2);
+// - 4 waves per block, one per SIMD, each with a 128 x 128 (or, for tiles of
+//   at most 128 token rows, 64 x 128) slice of v_mfma_f32_32x32x16_bf16
+//   accumulators in AGPRs; the weight tile is the MFMA "A" operand, so a
+//   lane's accumulators are runs of 4 consecutive output columns of one token
+//   row;
+// - operands move global -> VGPR -> LDS one k-step ahead of their use, with
+//   the LDS reads, LDS writes and global loads of a k-step interleaved
+//   between its MFMAs (details at the kernel);
 // - SwiGLU: the weight tile interleaves 32-row blocks of gate rows and up rows
 //   of the same 32 output columns, so each lane holds the gate and up values
 //   of the same output element and applies silu(g) * u in registers; GELU and
@@ -31,217 +35,242 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// Tile: 256 weight rows (n) x up to 256 token rows (m), 8 waves. Wave w owns
-// weight rows [64 (w%4), +64) of the tile (two 32-row MFMA subtiles) and
-// token rows [128 (w/4), +128) (four 32-row subtiles). Waves w and w+4 share a
-// SIMD, so a tile with few rows leaves half of each SIMD's work undone rather
-// than idling whole SIMDs; subtiles past the tile's row count are skipped.
+// Tile: 256 weight rows (n) x up to 256 token rows (m), 4 waves (256
+// threads, one wave per SIMD). Full tiles (more than 128 token rows): wave w
+// owns weight rows [128 (w%2), +128) and token rows [128 (w/2), +128), i.e.
+// 4 x 4 MFMA subtiles of 32 x 32 (256 accumulators). Half tiles (at most 128
+// token rows): wave w owns weight rows [64 w, +64) and token rows [0, 128),
+// 2 x 4 subtiles. Token rows past the tile's count are computed from a
+// clamped (valid) row and never stored.
 //
 // MFMA v_mfma_f32_32x32x16_bf16: lane l supplies row l%32, k = 8(l/32)..+7
 // of each operand; accumulator element i of lane l is row
 // 8(i/4) + 4(l/32) + i%4 (weight row) and column l%32 (token row).
 //
-// Operand staging: a ring of kStages LDS stages, each 256 weight rows and 256
-// token rows of kBK = 32 bf16 (64-byte rows, four 16-byte chunks; chunk c of
-// row r sits at chunk c ^ ((r >> 2) & 3), so the 16 rows one read phase
-// touches cover all 64 banks). Global -> LDS moves use global_load_lds_dwordx4:
-// one instruction fills 1 KB of LDS (16 rows) with lane l's 16 bytes at byte
-// 16 l, so each lane fetches the global chunk that the swizzle puts there. No
-// VGPR staging, no ds_write. Loads run kStages - 1 k-steps ahead; a k-step
-// waits only for its own stage (s_waitcnt vmcnt on the wave's later loads,
-// then s_barrier).
-constexpr int kBK = 32;
-constexpr int kStages = 4;
+// k-steps of kBK = 64: an LDS stage holds 256 weight rows and 256 token rows
+// of 64 bf16 (128-byte rows, eight 16-byte chunks; chunk c of row r sits at
+// chunk c ^ ((r >> 1) & 7), which keeps both the 16-byte row-chunk writes and
+// the MFMA fragment reads free of bank conflicts). Two stages alternate. Each
+// thread moves 8 weight chunks and 8 (half tile: 4) token chunks per k-step,
+// rows rb + 32 j, chunk tid % 8, with raw buffer loads (a uniform base per
+// tile and a 32-bit per-lane offset) into VGPRs, then ds_write_b128.
+//
+// One k-step t reads stage t%2 in four quarters (k = 16 each). Fragments for
+// quarter q+1 are read during the MFMAs of quarter q. During quarters 1 and
+// 2 the VGPRs holding k-step t+1 are written to stage (t+1)%2 and refilled
+// with k-step t+2 from global memory, so a global load has about one k-step
+// of MFMA work to land. After quarter 2: wait for this wave's LDS traffic,
+// s_barrier (stage (t+1)%2 complete, stage t%2 no longer read), then the
+// MFMAs of quarter 3 run while quarter 0 of the next stage is read.
+// sched_group_barrier fixes the interleaving inside each quarter; the last
+// k-step of a tile runs the same code (its extra loads re-read the last
+// k-step, its extra writes go to a stage nobody reads again).
+constexpr int kBK = 64;
+constexpr int kTile = 256;
+constexpr int kRegion = kTile * kBK;   // elements of one operand region of a stage
+constexpr int kStage = 2 * kRegion;
 
-#define MOE_AS3(p) ((__attribute__((address_space(3))) void *)(p))
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ ((r >> 2) & 3)) << 3); }
-
-// s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15 = no wait).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+// Raw buffer resource over [p, p + 2 GiB) (out-of-range reads return zero;
+// every offset used here is in range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo),
+                                             static_cast<short>(0), 0x7fffffff, 0x00020000);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(512, 1) void grouped_gemm_bf16(GGArgs a) {
-    constexpr int TILE = 256;
-    constexpr int NS = 2, MS = 4;
-    constexpr int STAGE = 2 * TILE * kBK;       // elements per LDS stage (weights + tokens)
-    // one array per stage: the compiler then sees which stage a pending
-    // global->LDS load writes and does not wait for all of them before a read
-    __shared__ __attribute__((aligned(16))) bf16_t st0[STAGE];
-    __shared__ __attribute__((aligned(16))) bf16_t st1[STAGE];
-    __shared__ __attribute__((aligned(16))) bf16_t st2[STAGE];
-    __shared__ __attribute__((aligned(16))) bf16_t st3[STAGE];
-    __shared__ int s_cum[kMaxSeg];
-    __shared__ int s_tmp[256];
+#define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200, kSgVmemRead = 0x020;
+// all LDS traffic of this wave done, then the workgroup barrier; the memory
+// clobber keeps the compiler from moving LDS accesses across it
+#define MOE_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+template <int MODE, bool ODD, bool HALF>
+__device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, bf16_t *LB0, bf16_t *LB1) {
+    constexpr int NI = HALF ? 2 : 4;    // 32-row weight subtiles per wave
+    constexpr int NJ = 4;               // 32-row token subtiles per wave
+    constexpr int XJ = HALF ? 4 : 8;    // token chunks per thread per k-step
+    constexpr int NMF = NI * NJ;        // MFMAs per quarter
+    constexpr int NRD = NI + NJ;        // fragment reads per quarter
+    constexpr int NWR = 4 + XJ / 2;     // chunk writes (and loads) per heavy quarter
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wn = wave & 3, wm = wave >> 2;
+    const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, lhi = lane >> 5;
-
-    const int total = build_tile_prefix_bal(a, s_cum, s_tmp);
+    const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int tok0 = HALF ? 0 : (wave >> 1) * 128;
+    const int K = a.K, nk = K / kBK;
+    const int chunk = tid & 7, rb = tid >> 3;
+    const int so = swz(rb, chunk);      // + 32 j rows: same swizzle
+    const int rows = min(kTile, ti.M - ti.m0);
     const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
-    const int K = a.K;
-    const int nk = K / kBK;
-    // this wave fills LDS regions 4w..4w+3 of each stage (16 rows each):
-    // waves 0..3 the weight rows, waves 4..7 the token rows
-    const bool fills_w = wave < 4;
-    const int prow0 = (wave & 3) * 64 + (lane >> 2);   // tile row of load i: prow0 + 16 i
-    const int pchunk = lane & 3;
 
-    for (int L = xcd_block_index(blockIdx.x, a.grid); L < total; L += a.grid) {
-        const BalTile ti = decode_tile_bal(a, s_cum, L);
-        const int nact = (ti.rows + 31) >> 5;   // active 32-row token subtiles of the tile
-        int nw = nact - wm * MS;                // ... of this wave
-        nw = nw < 0 ? 0 : (nw > MS ? MS : nw);
+    const bf16_t *wseg = ti.shared ? static_cast<const bf16_t *>(a.B_sh)
+                                   : static_cast<const bf16_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
+    const bf16_t *xbase = (ti.shared ? static_cast<const bf16_t *>(a.A_sh)
+                                     : static_cast<const bf16_t *>(a.A) + static_cast<int64_t>(ti.row0) * K) +
+                          static_cast<int64_t>(ti.m0) * K;
+    // weight rows of the tile: SwiGLU j even -> gate rows f, j odd -> up rows
+    // N_out + f, f = n_tile*128 + (j/2)*32 + rb; plain: n_tile*256 + rb + 32 j
+    const int wfirst = MODE == kModeSwiGLU ? ti.n_tile * (kTile / 2) : ti.n_tile * kTile;
+    const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wseg + static_cast<int64_t>(wfirst) * K);
+    const __amdgpu_buffer_rsrc_t rwu =
+        make_rsrc(wseg + static_cast<int64_t>(MODE == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase);
+    int wv[8], xv[XJ];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int rl = MODE == kModeSwiGLU ? (j >> 1) * 32 + rb : rb + 32 * j;   // row past the base
+        const int lim = MODE == kModeSwiGLU ? a.N_out : nb_rows;
+        wv[j] = ((wfirst + rl < lim ? rl : 0) * K + chunk * 8) * 2;            // base row is valid
+    }
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+        const int r = rb + 32 * j;
+        xv[j] = ((r < rows ? r : rows - 1) * K + chunk * 8) * 2;
+    }
 
-        // global source of each of this lane's 4 chunks per stage
-        const bf16_t *src[4];
+    floatx16 acc[NI][NJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = prow0 + 16 * i;                       // tile row
-            const int c = pchunk ^ ((r >> 2) & 3);              // logical 16-byte chunk
-            if (fills_w) {
-                int wrow;
-                if (MODE == kModeSwiGLU) {
-                    const int f = ti.n_tile * (TILE / 2) + (r >> 6) * 32 + (r & 31);
-                    wrow = ((r >> 5) & 1) ? a.N_out + f : f;
-                    if (f >= a.N_out) wrow = 0;
-                } else {
-                    wrow = ti.n_tile * TILE + r;
-                    if (wrow >= nb_rows) wrow = 0;
-                }
-                const bf16_t *Bseg = ti.shared ? static_cast<const bf16_t *>(a.B_sh)
-                                               : static_cast<const bf16_t *>(a.B) +
-                                                     static_cast<int64_t>(ti.seg) * nb_rows * K;
-                src[i] = Bseg + static_cast<int64_t>(wrow) * K + c * 8;
-            } else {
-                const bf16_t *Aseg = ti.shared ? static_cast<const bf16_t *>(a.A_sh)
-                                               : static_cast<const bf16_t *>(a.A) + static_cast<int64_t>(ti.row0) * K;
-                const int m = r < ti.rows ? r : ti.rows - 1;   // clamped: in bounds, never stored
-                src[i] = Aseg + (static_cast<int64_t>(ti.row_lo) + m) * K + c * 8;
-            }
-        }
-        const int dsto = (fills_w ? 0 : TILE * kBK) + (wave & 3) * 64 * kBK;   // region of load 0
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    u32x4 RW[8], RX[XJ];
+    bf16x8_t fa0[NI], fb0[NJ], fa1[NI], fb1[NJ];
 
-        floatx16 acc[NS][MS];
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-#pragma unroll
-            for (int j = 0; j < MS; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-#define MOE_FILL(ARR, KT)                                                                       \
+#define MOE_LD(KT, H)                                                                           \
     do {                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
-            __builtin_amdgcn_global_load_lds(src[i] + (KT) * kBK, MOE_AS3(ARR + dsto + 16 * i * kBK), 16, 0, 0); \
+        _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                          \
+            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((j & 1) ? rwu : rwg, wv[j], (KT) * kBK * 2, 0); \
+        _Pragma("unroll") for (int j = (XJ / 2) * (H); j < (XJ / 2) * (H) + XJ / 2; ++j)      \
+            RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], (KT) * kBK * 2, 0);      \
     } while (0)
-
-        // prologue: stages 0 .. kStages-2
-        if (0 < nk) MOE_FILL(st0, 0);
-        if (1 < nk) MOE_FILL(st1, 1);
-        if (2 < nk) MOE_FILL(st2, 2);
-
-// One k-step on stage CUR; refills NXT (the stage read one step earlier)
-// with k-step KT + kStages - 1. UNIFORM: every step issues its loads (the
-// tail re-fetches the last k-step into a stage nobody reads again), so the
-// wave always waits for exactly the 8 later loads and the compiler can prove
-// that the stage being read has landed.
-#define MOE_KSTEP(CUR, NXT, KT, UNIFORM)                                                        \
+#define MOE_WR(LB, H)                                                                           \
     do {                                                                                      \
-        const int kt_ = (KT);                                                                 \
-        if (UNIFORM) {                                                                        \
-            wait_vmcnt<8>();                                                                  \
-        } else {                                                                              \
-            const int later_ = nk - 1 - kt_;                                                  \
-            if (later_ >= 2) wait_vmcnt<8>();                                                 \
-            else if (later_ == 1) wait_vmcnt<4>();                                            \
-            else wait_vmcnt<0>();                                                             \
+        _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                          \
+            *reinterpret_cast<u32x4 *>((LB) + so + j * 32 * kBK) = RW[j];                      \
+        _Pragma("unroll") for (int j = (XJ / 2) * (H); j < (XJ / 2) * (H) + XJ / 2; ++j)      \
+            *reinterpret_cast<u32x4 *>((LB) + kRegion + so + j * 32 * kBK) = RX[j];           \
+    } while (0)
+#define MOE_RD(FA, FB, LB, KS)                                                                  \
+    do {                                                                                      \
+        const int ch_ = (KS) * 2 + lhi;                                                       \
+        _Pragma("unroll") for (int i = 0; i < NI; ++i)                                        \
+            FA[i] = *reinterpret_cast<const bf16x8_t *>((LB) + swz(wrow0 + i * 32 + l32, ch_)); \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                        \
+            FB[j] = *reinterpret_cast<const bf16x8_t *>((LB) + kRegion + swz(tok0 + j * 32 + l32, ch_)); \
+    } while (0)
+#define MOE_MF(FA, FB)                                                                          \
+    do {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < NI; ++i)                                        \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                    \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+    } while (0)
+// quarter with fragment reads only
+#define MOE_PAT_LIGHT()                                                                         \
+    do {                                                                                      \
+        _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                     \
+            MOE_SGB(kSgMfma, 1);                                                              \
+            if ((HALF && q < NRD) || (!HALF && (q & 1))) MOE_SGB(kSgDsRead, 1);               \
         }                                                                                     \
-        __builtin_amdgcn_s_barrier();                                                         \
-        if (UNIFORM) MOE_FILL(NXT, min(kt_ + kStages - 1, nk - 1));                           \
-        else if (kt_ + kStages - 1 < nk) MOE_FILL(NXT, kt_ + kStages - 1);                    \
-        if (nw > 0) {                                                                         \
-            const bf16_t *sw_ = CUR;                                                          \
-            const bf16_t *sx_ = CUR + TILE * kBK;                                             \
-            _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                \
-                const int ch = ks * 2 + lhi;                                                  \
-                bf16x8_t af[NS], bfr[MS];                                                     \
-                _Pragma("unroll") for (int i = 0; i < NS; ++i)                                \
-                    af[i] = *reinterpret_cast<const bf16x8_t *>(sw_ + lds_off(wn * 64 + i * 32 + l32, ch)); \
-                _Pragma("unroll") for (int j = 0; j < MS; ++j)                                \
-                    bfr[j] = *reinterpret_cast<const bf16x8_t *>(sx_ + lds_off(wm * 128 + j * 32 + l32, ch)); \
-                if (nw == MS) {                                                               \
-                    _Pragma("unroll") for (int j = 0; j < MS; ++j)                            \
-                        _Pragma("unroll") for (int i = 0; i < NS; ++i)                        \
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
-                } else {                                                                      \
-                    _Pragma("unroll") for (int j = 0; j < MS; ++j)                            \
-                        if (j < nw)                                                           \
-                            _Pragma("unroll") for (int i = 0; i < NS; ++i)                    \
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
-                }                                                                             \
+    } while (0)
+// quarter with fragment reads, chunk writes and global loads
+#define MOE_PAT_HEAVY()                                                                         \
+    do {                                                                                      \
+        _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                     \
+            MOE_SGB(kSgMfma, 1);                                                              \
+            if (HALF) {                                                                       \
+                if (q < NRD) MOE_SGB(kSgDsRead, 1);                                           \
+                if (q < NWR) { MOE_SGB(kSgDsWrite, 1); MOE_SGB(kSgVmemRead, 1); }             \
+            } else if (q & 1) {                                                               \
+                MOE_SGB(kSgDsWrite, 1); MOE_SGB(kSgVmemRead, 1);                              \
+            } else {                                                                          \
+                MOE_SGB(kSgDsRead, 1);                                                        \
             }                                                                                 \
         }                                                                                     \
     } while (0)
+#define MOE_STEP(CUR, NXT, T)                                                                   \
+    do {                                                                                      \
+        const int kk_ = (T) + 2 < nk ? (T) + 2 : nk - 1;                                      \
+        MOE_MF(fa0, fb0); MOE_RD(fa1, fb1, CUR, 1);                                           \
+        MOE_PAT_LIGHT(); __builtin_amdgcn_sched_barrier(0);                                   \
+        MOE_MF(fa1, fb1); MOE_RD(fa0, fb0, CUR, 2); MOE_WR(NXT, 0); MOE_LD(kk_, 0);           \
+        MOE_PAT_HEAVY(); __builtin_amdgcn_sched_barrier(0);                                   \
+        MOE_MF(fa0, fb0); MOE_RD(fa1, fb1, CUR, 3); MOE_WR(NXT, 1); MOE_LD(kk_, 1);           \
+        MOE_PAT_HEAVY(); __builtin_amdgcn_sched_barrier(0);                                   \
+        MOE_LDS_BARRIER();                                                                    \
+        MOE_MF(fa1, fb1); MOE_RD(fa0, fb0, NXT, 0);                                           \
+        MOE_PAT_LIGHT(); __builtin_amdgcn_sched_barrier(0);                                   \
+    } while (0)
 
-        if (nk % kStages == 0) {
-            for (int kt = 0; kt < nk; kt += kStages) {
-                MOE_KSTEP(st0, st3, kt, true);
-                MOE_KSTEP(st1, st0, kt + 1, true);
-                MOE_KSTEP(st2, st1, kt + 2, true);
-                MOE_KSTEP(st3, st2, kt + 3, true);
-            }
-        } else {
-            for (int kt = 0; kt < nk; kt += kStages) {
-                MOE_KSTEP(st0, st3, kt, false);
-                if (kt + 1 < nk) MOE_KSTEP(st1, st0, kt + 1, false);
-                if (kt + 2 < nk) MOE_KSTEP(st2, st1, kt + 2, false);
-                if (kt + 3 < nk) MOE_KSTEP(st3, st2, kt + 3, false);
-            }
+    // prologue: k-step 0 into stage 0, k-step 1 into the VGPRs
+    MOE_LD(0, 0);
+    MOE_LD(0, 1);
+    MOE_LDS_BARRIER();   // every wave is done reading the previous tile's stages
+    MOE_WR(LB0, 0);
+    MOE_WR(LB0, 1);
+    {
+        const int k1 = nk > 1 ? 1 : 0;
+        MOE_LD(k1, 0);
+        MOE_LD(k1, 1);
+    }
+    MOE_LDS_BARRIER();
+    MOE_RD(fa0, fb0, LB0, 0);
+    if (ODD) {
+        for (int t = 0; t + 1 < nk; t += 2) {
+            MOE_STEP(LB0, LB1, t);
+            MOE_STEP(LB1, LB0, t + 1);
         }
-#undef MOE_KSTEP
-#undef MOE_FILL
-        // drain the tail loads and make sure every wave is past its last read
-        // of the ring before the next tile starts refilling it
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        // ------------------------------------------------------- epilogue
-        const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.row_lo;
-        bf16_t *Cseg = ti.shared ? static_cast<bf16_t *>(a.C_sh) + static_cast<int64_t>(ti.row_lo) * a.N_out
-                                 : static_cast<bf16_t *>(a.C) + crow0 * a.N_out;
-        bf16_t *GUseg = nullptr;
-        if (MODE == kModeSwiGLU) {
-            if (ti.shared)
-                GUseg = a.GU_sh ? static_cast<bf16_t *>(a.GU_sh) + static_cast<int64_t>(ti.row_lo) * 2 * a.N_out
-                                : nullptr;
-            else
-                GUseg = a.GU ? static_cast<bf16_t *>(a.GU) + crow0 * 2 * a.N_out : nullptr;
+        MOE_STEP(LB0, LB1, nk - 1);
+    } else {
+        for (int t = 0; t < nk; t += 2) {
+            MOE_STEP(LB0, LB1, t);
+            MOE_STEP(LB1, LB0, t + 1);
         }
-        const bf16_t *bias = (a.bias && !ti.shared)
-                                 ? static_cast<const bf16_t *>(a.bias) + static_cast<int64_t>(ti.seg) * nb_rows
-                                 : nullptr;
+    }
+#undef MOE_LD
+#undef MOE_WR
+#undef MOE_RD
+#undef MOE_MF
+#undef MOE_PAT_LIGHT
+#undef MOE_PAT_HEAVY
+#undef MOE_STEP
+
+    // ------------------------------------------------------------ epilogue
+    const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
+    bf16_t *Cseg = ti.shared ? static_cast<bf16_t *>(a.C_sh) + static_cast<int64_t>(ti.m0) * a.N_out
+                             : static_cast<bf16_t *>(a.C) + crow0 * a.N_out;
+    bf16_t *GUseg = nullptr;
+    if (MODE == kModeSwiGLU) {
+        if (ti.shared)
+            GUseg = a.GU_sh ? static_cast<bf16_t *>(a.GU_sh) + static_cast<int64_t>(ti.m0) * 2 * a.N_out : nullptr;
+        else
+            GUseg = a.GU ? static_cast<bf16_t *>(a.GU) + crow0 * 2 * a.N_out : nullptr;
+    }
+    const bf16_t *bias = (a.bias && !ti.shared)
+                             ? static_cast<const bf16_t *>(a.bias) + static_cast<int64_t>(ti.seg) * nb_rows
+                             : nullptr;
 #pragma unroll
-        for (int j = 0; j < MS; ++j) {
-            const int m = wm * 128 + j * 32 + l32;
-            if (j >= nw || m >= ti.rows) continue;
+    for (int j = 0; j < NJ; ++j) {
+        const int m = tok0 + j * 32 + l32;
+        if (m >= rows) continue;
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int nl = 8 * gq + 4 * lhi;   // row offset inside a 32-row subtile
-                if (MODE == kModeSwiGLU) {
-                    const int f = ti.n_tile * (TILE / 2) + wn * 32 + nl;
+        for (int gq = 0; gq < 4; ++gq) {
+            const int nl = 8 * gq + 4 * lhi;   // row offset inside a 32-row subtile
+            if (MODE == kModeSwiGLU) {
+#pragma unroll
+                for (int p = 0; p < NI / 2; ++p) {
+                    const int f = ti.n_tile * (kTile / 2) + wrow0 / 2 + p * 32 + nl;
                     if (f >= a.N_out) continue;
                     float g[4], u[4], hv[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        g[q] = acc[0][j][4 * gq + q];
-                        u[q] = acc[1][j][4 * gq + q];
+                        g[q] = acc[2 * p][j][4 * gq + q];
+                        u[q] = acc[2 * p + 1][j][4 * gq + q];
                         if (bias) {
                             g[q] += bf16_to_f32(bias[f + q]);
                             u[q] += bf16_to_f32(bias[a.N_out + f + q]);
@@ -262,26 +291,41 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16(GGArgs a) {
                         *reinterpret_cast<uint2 *>(gr + f) = og;
                         *reinterpret_cast<uint2 *>(gr + a.N_out + f) = ou;
                     }
-                } else {
+                }
+            } else {
 #pragma unroll
-                    for (int i = 0; i < NS; ++i) {
-                        const int n = ti.n_tile * TILE + wn * 64 + i * 32 + nl;
-                        if (n >= a.N_out) continue;
-                        float v[4];
+                for (int i = 0; i < NI; ++i) {
+                    const int n = ti.n_tile * kTile + wrow0 + i * 32 + nl;
+                    if (n >= a.N_out) continue;
+                    float v[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            v[q] = acc[i][j][4 * gq + q];
-                            if (bias) v[q] += bf16_to_f32(bias[n + q]);
-                            if (MODE == kModeGELU) v[q] = gelu_erf_f(v[q]);
-                        }
-                        uint2 o;
-                        o.x = pack_bf16x2(v[0], v[1]);
-                        o.y = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + n) = o;
+                    for (int q = 0; q < 4; ++q) {
+                        v[q] = acc[i][j][4 * gq + q];
+                        if (bias) v[q] += bf16_to_f32(bias[n + q]);
+                        if (MODE == kModeGELU) v[q] = gelu_erf_f(v[q]);
                     }
+                    uint2 o;
+                    o.x = pack_bf16x2(v[0], v[1]);
+                    o.y = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + n) = o;
                 }
             }
         }
+    }
+}
+
+// ODD: the number of k-steps K / 64 is odd.
+template <int MODE, bool ODD>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16(GGArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16_t LB0[kStage];
+    __shared__ __attribute__((aligned(16))) bf16_t LB1[kStage];
+    __shared__ int s_cum[kMaxSeg];
+    __shared__ int s_tmp[256];
+    const int total = build_tile_prefix(a, kTile, s_cum, s_tmp);
+    for (int L = xcd_block_index(blockIdx.x, a.grid); L < total; L += a.grid) {
+        const TileInfo ti = decode_tile(a, s_cum, L, kTile);
+        if (ti.M - ti.m0 > kTile / 2) gemm_tile<MODE, ODD, false>(a, ti, LB0, LB1);
+        else gemm_tile<MODE, ODD, true>(a, ti, LB0, LB1);
     }
 }
 
@@ -434,9 +478,12 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
     a.grid = static_cast<int>(grid);
-    if (dtype == MOE_DTYPE_BF16)
-        hipLaunchKernelGGL((grouped_gemm_bf16<MODE>), dim3(a.grid), dim3(512), 0, s, a);
-    else
+    if (dtype == MOE_DTYPE_BF16) {
+        if ((a.K / kBK) & 1)
+            hipLaunchKernelGGL((grouped_gemm_bf16<MODE, true>), dim3(a.grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((grouped_gemm_bf16<MODE, false>), dim3(a.grid), dim3(256), 0, s, a);
+    } else
         hipLaunchKernelGGL((grouped_gemm_f32<MODE>), dim3(a.grid), dim3(256), 0, s, a);
     return check_launch(what);
 }

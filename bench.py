@@ -7,14 +7,21 @@ default workload is the Mixtral-8x7B-shaped layer (T=4096 tokens, h=4096,
 E=8, top-2, SwiGLU 14336, bf16 with fp32 accumulation).
 
 Prints one JSON line: active TFLOP/s (router GEMM plus every routed
-token's expert FLOPs, no padding credited) and tokens/s, per-stage times with
+token's expert FLOPs, no padding credited) and tokens/s; the roofline of the
+dominant call (the grouped FFN, or its backward in a training step), timed
+with HIP events around that call inside the timed steps; per-stage times with
 their roofline fractions (stages timed separately with HIP events after an
-eviction of the 256 MB last-level cache), the roofline of the dominant stage,
-and the CPU oracle timed on a bounded sample of the same workload.
+eviction of the 256 MB last-level cache); and the CPU oracle timed on a
+bounded sample of the same workload.
+
+``--copy-calibration`` runs only a plain elementwise copy of 1 GiB (fp32
+negation, 1 GiB read and 1 GiB written per launch): the HBM byte counters
+read for it give the scale factor applied to the counters of the GEMMs.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +37,11 @@ METRIC = "MoE layer active TFLOP/s + tokens/s at 1 MI355X; % of MFMA/HBM rooflin
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# measured HBM traffic of the grouped FFN (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# scaled by the same counters on a plain copy); valid while the GEMM sources
+# hash to the recorded value
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_ffn_mixtral_8x7b_layer_hbm_traffic.md")
+GEMM_SOURCES = ["ffn.hip", "gemm_common.hpp", "common.hpp"]
 
 
 def parse():
@@ -43,7 +55,47 @@ def parse():
                    help="tokens of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB elementwise copy (counter calibration)")
     return p.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_06_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per grouped-FFN call from the committed counter summary, or
+    None when it is missing, for another workload, or for other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    rec = json.loads(text[start + 7:end])
+    if rec.get("workload") != workload or rec.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    return rec
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28                                   # fp32 elements: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n,
+                                           "launches": 3}}), flush=True)
 
 
 def stage_bytes(cfg, P, es):
@@ -121,6 +173,9 @@ def main():
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
               "(no collectives or sharding in this build); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from mixture_experts_layer_06_amd import binding as B
     from mixture_experts_layer_06_amd import layer
@@ -135,21 +190,24 @@ def main():
     train = cfg.backward
     flops = cfg.active_flops_forward() + (cfg.active_flops_backward() if train else 0.0)
 
-    def step():
-        f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train)
+    def step(timers=None):
+        f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers)
         if train:
-            layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act)
+            layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers)
         return f
 
     for _ in range(args.warmup):
         step()
+    timers = {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        res = step()
+        res = step(timers)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     counts = res["counts"].cpu().numpy()
+    live = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
+            for name, pairs in timers.items()}
 
     out = {
         "metric": METRIC,
@@ -173,6 +231,29 @@ def main():
         "active_gflop_per_step": flops / 1e9,
         "expert_load": {"min": int(counts.min()), "max": int(counts.max())},
     }
+
+    # roofline of the dominant call, from the events inside the timed steps
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    nmat = 3 if cfg.act == "swiglu" else 2
+    bwd_flops = 2.0 * cfg.P * nmat * 2.0 * cfg.h * cfg.F
+    call_flops = {"grouped_ffn": ffn_flops(cfg), "grouped_ffn_bwd": bwd_flops}
+    dom = max(live, key=lambda n: live[n])
+    rec = recorded_traffic(cfg.name) if dom == "grouped_ffn" else None
+    kernels = {"grouped_ffn": "grouped_gemm_bf16 SwiGLU launch + grouped_gemm_bf16 plain launch "
+                              "(one moe_grouped_ffn call)",
+               "grouped_ffn_bwd": "moe_grouped_ffn_bwd call (SwiGLU backward, data and weight "
+                                  "gradient launches)"}
+    out["roofline"] = {
+        "kernel": kernels[dom], "bound": "mfma",
+        "achieved": call_flops[dom] / live[dom] / 1e12, "peak": peak, "unit": "TFLOP/s",
+        "frac": call_flops[dom] / live[dom] / 1e12 / peak,
+        "traffic": rec["traffic_bytes_per_call"] if rec else None,
+        "flops_per_call": call_flops[dom], "ms_per_call": live[dom] * 1e3,
+        "timing": "HIP events around the call on its stream, mean over the %d timed steps"
+                  % args.steps,
+    }
+    if rec:
+        out["roofline"]["traffic_note"] = rec["note"]
 
     if not args.no_stages:
         stream = torch.cuda.current_stream(dev)
@@ -235,23 +316,14 @@ def main():
             stages[name]["algorithmic_bytes"] = sb[name]
         t = stages["grouped_ffn"]["s_median"]
         ff = ffn_flops(cfg)
-        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
         stages["grouped_ffn"]["tflops"] = ff / t / 1e12
         stages["grouped_ffn"]["mfma_frac"] = ff / t / 1e12 / peak
         stages["grouped_ffn"]["weight_gb_per_s"] = ffn_weight_bytes(cfg, es) / t / 1e9
         if train:
-            nmat = 3 if cfg.act == "swiglu" else 2
-            bflops = 2.0 * cfg.P * nmat * 2.0 * cfg.h * cfg.F
-            t = stages["grouped_ffn_bwd"]["s_median"]
-            stages["grouped_ffn_bwd"]["tflops"] = bflops / t / 1e12
-            stages["grouped_ffn_bwd"]["mfma_frac"] = bflops / t / 1e12 / peak
+            tb = stages["grouped_ffn_bwd"]["s_median"]
+            stages["grouped_ffn_bwd"]["tflops"] = bwd_flops / tb / 1e12
+            stages["grouped_ffn_bwd"]["mfma_frac"] = bwd_flops / tb / 1e12 / peak
         out["stages"] = stages
-        out["roofline"] = {
-            "kernel": "grouped_ffn: grouped_gemm_bf16 SwiGLU + plain launches",
-            "bound": "mfma", "achieved": ff / t / 1e12, "peak": peak, "unit": "TFLOP/s",
-            "frac": ff / t / 1e12 / peak, "traffic": None,
-            "flops_per_launch": ff,
-        }
         del flush
 
     if not args.no_cpu_baseline:

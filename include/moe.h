@@ -148,12 +148,23 @@ int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
  *   y    [P,h] dtype          expert outputs in permuted order
  *   y_sh [T_sh,h] dtype|NULL  shared-expert output
  * Arithmetic: fp32 accumulation on MFMA; act, gu and y are rounded to dtype.
+ *
+ * Workspace (optional; NULL with workspace_bytes 0 is valid): device memory
+ * of moe_grouped_ffn_workspace_size(dtype) bytes (0 for fp32; for bf16 about
+ * 256 KB per compute unit of the current device), 16-byte aligned, owned by
+ * the caller and free to reuse once the call's work on the stream is done.
+ * With it, a GEMM whose last round of tiles would leave most of the GPU idle
+ * splits those tiles along h (resp. F) and sums the fp32 partial results in
+ * a fixed order, so results stay deterministic for a given device and
+ * workspace choice (with and without a workspace they may differ in
+ * rounding). A smaller non-null workspace is used as far as it goes.
  */
+size_t moe_grouped_ffn_workspace_size(int dtype);
 int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t h, int64_t F, int E,
                     const int32_t *offsets, int act_kind, const void *w1, const void *b1,
                     const void *w2, const void *b2, const void *x_sh, int64_t T_sh,
                     const void *w1_sh, const void *w2_sh, void *act, void *gu, void *y,
-                    void *y_sh, void *stream);
+                    void *y_sh, void *workspace, size_t workspace_bytes, void *stream);
 
 /* -------------------------------------------------------------- Unpermute
  * Combine stage ("Scalable Training ... with Megatron Core", section 2.1

@@ -88,8 +88,28 @@ constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200, kSgVmemRea
 // clobber keeps the compiler from moving LDS accesses across it
 #define MOE_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+// Epilogue of a tile: bias, activation, rounding, stores (C and, for SwiGLU
+// with a.GU, the pre-activations). acc as laid out by gemm_tile; JONLY >= 0:
+// token subtile JONLY of the wave only.
+template <int MODE, bool HALF, int JONLY = -1>
+__device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
+                                           floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane);
+
+// Split workspace: an int header of 64 KB ([0..2] the plan: split tiles,
+// pieces per tile, k-steps per piece; from int 64, 8 ints per split tile:
+// seg, m0, n_tile, M, row0, shared), then fp32 partial tiles of kPartFloats
+// each, piece p of split tile t at index t * s + p.
+constexpr int kWsHeaderFloats = 16384;
+constexpr int kWsMaxSplitTiles = (kWsHeaderFloats - 64) / 8;
+constexpr int kPartFloats = 256 * 256;
+
+// One tile over k-steps [k0, k0 + nks), then the epilogue; or, for a piece
+// of a split tile (part != null), its raw fp32 accumulators to part:
+// element e = 16 (i*4 + j) + q of thread tid's accumulators, in float4
+// groups, at float4 index (e/4) * 256 + tid.
 template <int MODE, bool ODD, bool HALF>
-__device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, bf16_t *LB0, bf16_t *LB1) {
+__device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, bf16_t *LB0, bf16_t *LB1,
+                                          int k0, int nks, float *part) {
     constexpr int NI = HALF ? 2 : 4;    // 32-row weight subtiles per wave
     constexpr int NJ = 4;               // 32-row token subtiles per wave
     constexpr int XJ = HALF ? 4 : 8;    // token chunks per thread per k-step
@@ -101,7 +121,10 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int tok0 = HALF ? 0 : (wave >> 1) * 128;
-    const int K = a.K, nk = K / kBK;
+    // uniform by construction; say so, so that they live in SGPRs (buffer
+    // load offsets and loop bounds)
+    k0 = __builtin_amdgcn_readfirstlane(k0);
+    const int K = a.K, nk = __builtin_amdgcn_readfirstlane(nks);
     const int chunk = tid & 7, rb = tid >> 3;
     const int so = swz(rb, chunk);      // + 32 j rows: same swizzle
     const int rows = min(kTile, ti.M - ti.m0);
@@ -145,9 +168,9 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
 #define MOE_LD(KT, H)                                                                           \
     do {                                                                                      \
         _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                          \
-            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((j & 1) ? rwu : rwg, wv[j], (KT) * kBK * 2, 0); \
+            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((j & 1) ? rwu : rwg, wv[j], (k0 + (KT)) * kBK * 2, 0); \
         _Pragma("unroll") for (int j = (XJ / 2) * (H); j < (XJ / 2) * (H) + XJ / 2; ++j)      \
-            RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], (KT) * kBK * 2, 0);      \
+            RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], (k0 + (KT)) * kBK * 2, 0); \
     } while (0)
 #define MOE_WR(LB, H)                                                                           \
     do {                                                                                      \
@@ -240,7 +263,30 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
 #undef MOE_PAT_HEAVY
 #undef MOE_STEP
 
-    // ------------------------------------------------------------ epilogue
+    if (part) {
+        float4 *P4 = reinterpret_cast<float4 *>(part);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    P4[((i * NJ + j) * 4 + q) * 256 + tid] =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        return;
+    }
+    store_tile<MODE, HALF>(a, ti, acc, wave, lane);
+}
+
+template <int MODE, bool HALF, int JONLY>
+__device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
+                                           floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane) {
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int tok0 = HALF ? 0 : (wave >> 1) * 128;
+    const int rows = min(kTile, ti.M - ti.m0);
+    const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
     const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
     bf16_t *Cseg = ti.shared ? static_cast<bf16_t *>(a.C_sh) + static_cast<int64_t>(ti.m0) * a.N_out
                              : static_cast<bf16_t *>(a.C) + crow0 * a.N_out;
@@ -256,6 +302,7 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
                              : nullptr;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+        if (JONLY >= 0 && j != JONLY) continue;
         const int m = tok0 + j * 32 + l32;
         if (m >= rows) continue;
 #pragma unroll
@@ -314,18 +361,141 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
     }
 }
 
-// ODD: the number of k-steps K / 64 is odd.
+// Work split. With T tiles and G persistent blocks, floor(T / G) rounds run
+// whole tiles. When a workspace is given and the last round would leave at
+// least half of the blocks idle, its rem tiles are cut along k into s pieces
+// of ps k-steps each (ps even), so that the last round keeps up to G blocks
+// busy; split_reduce then sums each tile's pieces in piece order
+// (deterministic) and runs the epilogue. Every block derives the same plan
+// from the segment offsets.
+struct SplitPlan {
+    int full, s, ps, items;   // whole tiles, pieces per split tile, k-steps per piece, work items
+};
+
+__device__ __forceinline__ SplitPlan split_plan(const GGArgs &a, int total, int nk, bool odd) {
+    SplitPlan p{total, 0, 0, total};
+    const int G = a.grid, rem = total % G;
+    if (odd || a.ws == nullptr || rem == 0 || 2 * rem > G || nk < 4) return p;
+    int s = min(G / rem, nk / 2);
+    const int ps = 2 * ((nk + 2 * s - 1) / (2 * s));
+    s = (nk + ps - 1) / ps;
+    if (s < 2 || rem * s > a.ws_tiles || rem > kWsMaxSplitTiles) return p;
+    p.full = total - rem;
+    p.s = s;
+    p.ps = ps;
+    p.items = p.full + rem * s;
+    return p;
+}
+
+// ODD: the number of k-steps K / 64 is odd (no split then).
 template <int MODE, bool ODD>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16(GGArgs a) {
     __shared__ __attribute__((aligned(16))) bf16_t LB0[kStage];
     __shared__ __attribute__((aligned(16))) bf16_t LB1[kStage];
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
-    const int total = build_tile_prefix(a, kTile, s_cum, s_tmp);
-    for (int L = xcd_block_index(blockIdx.x, a.grid); L < total; L += a.grid) {
+    const int total = __builtin_amdgcn_readfirstlane(build_tile_prefix(a, kTile, s_cum, s_tmp));
+    const int nk = a.K / kBK;
+    const SplitPlan sp = split_plan(a, total, nk, ODD);
+    int *hdr = reinterpret_cast<int *>(a.ws);
+    if (hdr && blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[0] = sp.s ? total - sp.full : 0;
+        hdr[1] = sp.s;
+        hdr[2] = sp.ps;
+    }
+    for (int w = xcd_block_index(blockIdx.x, a.grid); w < sp.items; w += a.grid) {
+        int L = w, k0 = 0, nks = nk;
+        float *part = nullptr;
+        if (sp.s && w >= sp.full) {
+            const int q = w - sp.full;
+            L = sp.full + q / sp.s;
+            k0 = (q % sp.s) * sp.ps;
+            nks = min(sp.ps, nk - k0);
+            part = a.ws + kWsHeaderFloats + static_cast<int64_t>(q) * kPartFloats;
+        }
         const TileInfo ti = decode_tile(a, s_cum, L, kTile);
-        if (ti.M - ti.m0 > kTile / 2) gemm_tile<MODE, ODD, false>(a, ti, LB0, LB1);
-        else gemm_tile<MODE, ODD, true>(a, ti, LB0, LB1);
+        if (part && k0 == 0 && threadIdx.x == 0) {
+            int *d = hdr + 64 + (L - sp.full) * 8;
+            d[0] = ti.seg;
+            d[1] = ti.m0;
+            d[2] = ti.n_tile;
+            d[3] = ti.M;
+            d[4] = ti.row0;
+            d[5] = ti.shared ? 1 : 0;
+        }
+        if (ti.M - ti.m0 > kTile / 2) gemm_tile<MODE, ODD, false>(a, ti, LB0, LB1, k0, nks, part);
+        else gemm_tile<MODE, ODD, true>(a, ti, LB0, LB1, k0, nks, part);
+    }
+}
+
+// Token subtile J of wave `wave` of a split tile: sum of the pieces (piece
+// order), then that subtile's epilogue.
+template <int MODE, bool HALF, int J>
+__device__ __forceinline__ void reduce_subtile(const GGArgs &a, const TileInfo &ti, const float4 *P4, int s,
+                                               int wave, int lane) {
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    const int tid = wave * 64 + lane;
+    floatx16 acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][J][q] = 0.0f;
+    for (int p = 0; p < s; ++p) {
+        const float4 *Pp = P4 + static_cast<int64_t>(p) * (kPartFloats / 4);
+        float4 v[NI][4];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[i][q] = Pp[((i * NJ + J) * 4 + q) * 256 + tid];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[i][J][4 * q] += v[i][q].x;
+                acc[i][J][4 * q + 1] += v[i][q].y;
+                acc[i][J][4 * q + 2] += v[i][q].z;
+                acc[i][J][4 * q + 3] += v[i][q].w;
+            }
+    }
+    store_tile<MODE, HALF, J>(a, ti, acc, wave, lane);
+}
+
+// Block b: split tile b / 16, wave (b / 4) % 4, token subtile b % 4.
+template <int MODE>
+__global__ __launch_bounds__(64) void split_reduce(GGArgs a) {
+    const int *hdr = reinterpret_cast<const int *>(a.ws);
+    const int rem = hdr[0], s = hdr[1];
+    const int t = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, J = blockIdx.x & 3;
+    if (s == 0 || t >= rem) return;
+    const int *d = hdr + 64 + t * 8;
+    TileInfo ti;
+    ti.seg = d[0];
+    ti.m0 = d[1];
+    ti.n_tile = d[2];
+    ti.M = d[3];
+    ti.row0 = d[4];
+    ti.shared = d[5] != 0;
+    const float4 *P4 = reinterpret_cast<const float4 *>(a.ws + kWsHeaderFloats) +
+                       static_cast<int64_t>(t) * s * (kPartFloats / 4);
+    const bool half = ti.M - ti.m0 <= kTile / 2;
+    const int lane = threadIdx.x;
+    switch (J) {
+    case 0:
+        if (half) reduce_subtile<MODE, true, 0>(a, ti, P4, s, wave, lane);
+        else reduce_subtile<MODE, false, 0>(a, ti, P4, s, wave, lane);
+        break;
+    case 1:
+        if (half) reduce_subtile<MODE, true, 1>(a, ti, P4, s, wave, lane);
+        else reduce_subtile<MODE, false, 1>(a, ti, P4, s, wave, lane);
+        break;
+    case 2:
+        if (half) reduce_subtile<MODE, true, 2>(a, ti, P4, s, wave, lane);
+        else reduce_subtile<MODE, false, 2>(a, ti, P4, s, wave, lane);
+        break;
+    default:
+        if (half) reduce_subtile<MODE, true, 3>(a, ti, P4, s, wave, lane);
+        else reduce_subtile<MODE, false, 3>(a, ti, P4, s, wave, lane);
+        break;
     }
 }
 
@@ -479,10 +649,19 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
     if (grid < 1) grid = 1;
     a.grid = static_cast<int>(grid);
     if (dtype == MOE_DTYPE_BF16) {
-        if ((a.K / kBK) & 1)
+        if ((a.K / kBK) & 1) {
+            a.ws = nullptr;
             hipLaunchKernelGGL((grouped_gemm_bf16<MODE, true>), dim3(a.grid), dim3(256), 0, s, a);
-        else
+        } else {
             hipLaunchKernelGGL((grouped_gemm_bf16<MODE, false>), dim3(a.grid), dim3(256), 0, s, a);
+            if (a.ws) {
+                const int st = check_launch(what);
+                if (st != MOE_OK) return st;
+                // at most grid / 2 split tiles, 16 blocks each
+                hipLaunchKernelGGL((split_reduce<MODE>), dim3(16 * (a.grid / 2 > 0 ? a.grid / 2 : 1)), dim3(64),
+                                   0, s, a);
+            }
+        }
     } else
         hipLaunchKernelGGL((grouped_gemm_f32<MODE>), dim3(a.grid), dim3(256), 0, s, a);
     return check_launch(what);
@@ -493,11 +672,18 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
 
 using namespace moe;
 
+extern "C" size_t moe_grouped_ffn_workspace_size(int dtype) {
+    if (dtype != MOE_DTYPE_BF16) return 0;
+    return sizeof(float) * (static_cast<size_t>(kWsHeaderFloats) +
+                            static_cast<size_t>(num_cus()) * kPartFloats);
+}
+
 extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t h, int64_t F,
                                int E, const int32_t *offsets, int act_kind, const void *w1,
                                const void *b1, const void *w2, const void *b2, const void *x_sh,
                                int64_t T_sh, const void *w1_sh, const void *w2_sh, void *act,
-                               void *gu, void *y, void *y_sh, void *stream) {
+                               void *gu, void *y, void *y_sh, void *workspace,
+                               size_t workspace_bytes, void *stream) {
     clear_error();
     MOE_CHECK_ARG(offsets && w1 && w2 && act && y, MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: null required pointer");
@@ -517,13 +703,24 @@ extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t
                   "moe_grouped_ffn: shared expert needs x_sh, w1_sh, w2_sh and y_sh");
     MOE_CHECK_ARG(gu == nullptr || act_kind == MOE_ACT_SWIGLU, MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: gu is kept for SwiGLU only");
-    const void *ptrs[] = {x_perm, w1, b1, w2, b2, x_sh, w1_sh, w2_sh, act, gu, y, y_sh};
+    MOE_CHECK_ARG(workspace_bytes == 0 || workspace, MOE_ERR_INVALID_ARG,
+                  "moe_grouped_ffn: workspace_bytes > 0 with a null workspace");
+    const void *ptrs[] = {x_perm, w1, b1, w2, b2, x_sh, w1_sh, w2_sh, act, gu, y, y_sh, workspace};
     for (const void *p : ptrs)
         MOE_CHECK_ARG(p == nullptr || aligned16(p), MOE_ERR_INVALID_ARG,
                       "moe_grouped_ffn: pointers must be 16-byte aligned");
     hipStream_t s = as_stream(stream);
     const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
     const int n1 = act_kind == MOE_ACT_SWIGLU ? 2 : 1;
+    // split workspace: header plus at least two partial tiles, else unused
+    const size_t hdr_bytes = sizeof(float) * kWsHeaderFloats, part_bytes = sizeof(float) * kPartFloats;
+    float *ws = nullptr;
+    int ws_tiles = 0;
+    if (dtype == MOE_DTYPE_BF16 && workspace && workspace_bytes >= hdr_bytes + 2 * part_bytes) {
+        ws = static_cast<float *>(workspace);
+        const size_t n = (workspace_bytes - hdr_bytes) / part_bytes;
+        ws_tiles = n > (size_t(1) << 20) ? (1 << 20) : static_cast<int>(n);
+    }
 
     // first projection + activation
     GGArgs g1{};
@@ -541,6 +738,8 @@ extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t
     g1.E = E;
     g1.N_out = static_cast<int>(F);
     g1.K = static_cast<int>(h);
+    g1.ws = ws;
+    g1.ws_tiles = ws_tiles;
     int st = act_kind == MOE_ACT_SWIGLU ? launch_gemm<kModeSwiGLU>(g1, dtype, P, s, "moe_grouped_ffn gemm1")
                                         : launch_gemm<kModeGELU>(g1, dtype, P, s, "moe_grouped_ffn gemm1");
     if (st != MOE_OK) return st;
@@ -559,5 +758,7 @@ extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t
     g2.E = E;
     g2.N_out = static_cast<int>(h);
     g2.K = static_cast<int>(F);
+    g2.ws = ws;
+    g2.ws_tiles = ws_tiles;
     return launch_gemm<kModePlain>(g2, dtype, P, s, "moe_grouped_ffn gemm2");
 }

@@ -32,6 +32,8 @@ struct GGArgs {
     int K;                  // reduction length
     int n_tiles;            // ceil(N_out / tile width)
     int grid;               // blocks launched (persistent)
+    float *ws;              // split workspace or null (bf16 forward kernel)
+    int ws_tiles;           // fp32 partial tiles the workspace holds
 };
 
 constexpr int kMaxSeg = 260;

@@ -7,24 +7,42 @@ with Megatron Core", section 2.1.
 """
 from __future__ import annotations
 
+import torch
+
 from . import binding as B
 
 
-def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False):
+def _timed(timers, name, fn):
+    """Runs fn(); with a timers dict, brackets it with HIP events on the
+    current stream and appends the (start, end) pair under name."""
+    if timers is None:
+        return fn()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    r = fn()
+    e1.record(s)
+    timers.setdefault(name, []).append((e0, e1))
+    return r
+
+
+def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False,
+            timers: dict | None = None):
     """One forward pass. ``inp`` holds device tensors named as in
     ``workloads.make_inputs``. Returns a dict with ``out`` and the
-    intermediate results of every stage."""
+    intermediate results of every stage. With ``timers``, the grouped FFN
+    call is bracketed by HIP events (key "grouped_ffn")."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
                     sel_bias=inp.get("sel_bias"), want_logits=keep_for_backward)
     p = B.moe_permute(x, r["topk_idx"], E)
     has_sh = inp.get("w1_sh") is not None
-    f = B.moe_grouped_ffn(p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act,
-                          b1=inp.get("b1"), b2=inp.get("b2"),
-                          x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"),
-                          w2_sh=inp.get("w2_sh"),
-                          keep_gu=keep_for_backward and act == "swiglu")
+    f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn(
+        p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"), b2=inp.get("b2"),
+        x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"),
+        keep_gu=keep_for_backward and act == "swiglu"))
     out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"])
     res = dict(out=out)
     res.update(r)
@@ -33,13 +51,16 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     return res
 
 
-def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str):
+def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
+             timers: dict | None = None):
     """Gradients of sum(grad_out * out) for a forward run with
-    keep_for_backward=True (routed experts; no shared expert)."""
+    keep_for_backward=True (routed experts; no shared expert). With
+    ``timers``, the grouped FFN backward call is bracketed by HIP events
+    (key "grouped_ffn_bwd")."""
     E = inp["w_gate"].shape[0]
     grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
-    g = B.moe_grouped_ffn_bwd(grad_y, fwd["x_perm"], fwd["act"], fwd["gu"], fwd["offsets"],
-                              inp["w1"], inp["w2"], act)
+    g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd(
+        grad_y, fwd["x_perm"], fwd["act"], fwd["gu"], fwd["offsets"], inp["w1"], inp["w2"], act))
     r = B.moe_route_bwd(inp["x"], E, fwd["topk_idx"], fwd["topk_w"], grad_w, fwd["offsets"],
                         fwd["sorted_token"], score=score, logits=fwd.get("logits"),
                         want_b_grad=inp.get("b_gate") is not None)

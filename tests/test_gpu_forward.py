@@ -218,3 +218,60 @@ def test_forward_is_deterministic(moe_lib):
     b = layer.forward(inp, cfg.k, cfg.score, cfg.act)
     for key in ("out", "y", "act", "topk_w", "row_of"):
         assert torch.equal(a[key], b[key]), key
+
+
+def _expected_split(counts, n_tiles, nk, P, E, cus):
+    """The last-round split plan the GEMM kernel derives (rem, s, ps), or
+    (0, 0, 0): tiles of 256 token rows, grid as the launcher sizes it."""
+    total = int(sum((int(m) + 255) // 256 for m in counts)) * n_tiles
+    upper = (P // 256 + E) * n_tiles
+    G = min(cus, upper)
+    if G >= 8:
+        G -= G % 8
+    rem = total % G
+    if rem == 0 or 2 * rem > G or nk < 4 or nk % 2:
+        return (0, 0, 0)
+    s = min(G // rem, nk // 2)
+    ps = 2 * ((nk + 2 * s - 1) // (2 * s))
+    s = (nk + ps - 1) // ps
+    return (rem, s, ps) if s >= 2 else (0, 0, 0)
+
+
+def test_grouped_ffn_split_last_round(moe_lib):
+    """A second GEMM with 384 tiles: on 256 compute units its last round of
+    128 tiles is split in two along F through the workspace. Outputs against
+    the oracle, the plan in the workspace header against the expected one,
+    and the result against the unsplit run (same values up to the fp32
+    summation order of two halves)."""
+    from mixture_experts_layer_06_amd import binding as B
+    cfg = wl.small_variant(wl.CONFIGS[2], T=2400, h=4096, F=256)
+    print("case split T=2400 h=4096 F=256", flush=True)
+    inp = wl.make_inputs(cfg, device="cpu")
+    dinp = to_device(inp)
+    r = B.moe_route(dinp["x"], dinp["w_gate"], cfg.k, cfg.score)
+    p = B.moe_permute(dinp["x"], r["topk_idx"], cfg.E)
+    ws = torch.zeros(B.lib().moe_grouped_ffn_workspace_size(1), dtype=torch.uint8, device="cuda")
+    f = B.moe_grouped_ffn(p["x_perm"], p["offsets"], dinp["w1"], dinp["w2"], cfg.act,
+                          keep_gu=True, workspace=ws)
+    f0 = B.moe_grouped_ffn(p["x_perm"], p["offsets"], dinp["w1"], dinp["w2"], cfg.act,
+                           keep_gu=True, use_workspace=False)
+    torch.cuda.synchronize()
+    counts = r["counts"].cpu().numpy()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hdr = tuple(int(v) for v in ws[:12].view(torch.int32).cpu().numpy()[:3])
+    want = _expected_split(counts, (cfg.h + 255) // 256, cfg.F // 64, cfg.P, cfg.E, cus)
+    print("counts", counts.tolist(), "plan", hdr, "expected", want, flush=True)
+    assert hdr == want
+    if cus == 256:
+        assert want[1] >= 2, "shape chosen to split on 256 compute units"
+    o = oracle_inputs(inp)
+    ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act)
+    perm = oracle.permutation(ref["topk_idx"], cfg.E)
+    y = to_np32(f["y"])
+    y_ref = np.zeros_like(y, dtype=np.float64)
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            y_ref[perm["row_of"][t, j]] = ref["y_pair"][t, j]
+    assert rel_err(y, y_ref) <= TOL["bf16"]
+    assert torch.equal(f["act"], f0["act"]) and torch.equal(f["gu"], f0["gu"])
+    assert rel_err(to_np32(f["y"]), to_np32(f0["y"])) <= 1e-2

@@ -72,22 +72,6 @@ constexpr int kStage = 2 * kRegion;
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// Raw buffer resource over [p, p + 2 GiB) (out-of-range reads return zero;
-// every offset used here is in range).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo),
-                                             static_cast<short>(0), 0x7fffffff, 0x00020000);
-}
-
-#define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200, kSgVmemRead = 0x020;
-// all LDS traffic of this wave done, then the workgroup barrier; the memory
-// clobber keeps the compiler from moving LDS accesses across it
-#define MOE_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-
 // Epilogue of a tile: bias, activation, rounding, stores (C and, for SwiGLU
 // with a.GU, the pre-activations). acc as laid out by gemm_tile; JONLY >= 0:
 // token subtile JONLY of the wave only.

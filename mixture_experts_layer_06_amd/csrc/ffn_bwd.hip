@@ -12,14 +12,19 @@
 // ("Scalable Training of Mixture-of-Experts Models with Megatron Core",
 // section 2.1 stage 3).
 //
-// One kernel template serves all four. The MFMA (v_mfma_f32_32x32x16_bf16)
-// reads both operands K-contiguous from LDS. Operands stored with K as the
-// slow index (weights [K][cols] in the two data-gradient GEMMs, activations
-// [tokens][cols] in the weight-gradient GEMMs) are transposed on the way to
-// LDS: a thread loads an 8 x 8 block (eight 16-byte rows), transposes it in
-// registers with byte permutes and writes eight K-contiguous 16-byte rows.
-// Weight-gradient tiles cover the whole K range of their expert (no split-K,
-// so results are deterministic), are ordered heaviest expert first, and
+// One kernel template serves all four, built like the forward kernel: 4
+// waves, 128 x 128 (or 64 x 128) wave tiles of v_mfma_f32_32x32x16_bf16
+// accumulators, 64-deep k-steps staged global -> VGPR -> LDS one k-step ahead,
+// the LDS reads, LDS writes and global loads of each k-step interleaved
+// between its MFMAs. Operands whose storage has K as the slow index (the
+// weights [K][cols] of the two data-gradient GEMMs, the activations
+// [tokens][cols] of the two weight-gradient GEMMs) are copied to LDS as they
+// are, K rows of 256 contiguous columns, and read out with
+// ds_read_b64_tr_b16, which hands each lane of a 16-lane group one column
+// of a 4-row block: two such reads give a lane the 8 consecutive k of its
+// MFMA row. Weight-gradient tiles cover the whole K range of their expert
+// (no split-K, so results are deterministic), rows past the expert's tokens
+// read as zero (buffer range), tiles are ordered heaviest expert first, and
 // experts without tokens get zero gradients.
 #include "gemm_common.hpp"
 
@@ -27,7 +32,10 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 enum BwdKind { kDgradSwiGLU = 0, kDgradPlain = 1, kWgrad = 2 };
 
@@ -48,45 +56,277 @@ struct BGArgs {
     int grid;
 };
 
-constexpr int TILE = 256, BK = 64, STAGE = 2 * TILE * BK;
+constexpr int kBK = 64, kTile = 256, kRegion = kTile * kBK, kStage = 2 * kRegion;
 
-// Column c of an 8 x 8 bf16 block whose row j is in[j] (8 elements in 4
-// dwords): element j of the result is in[j][c]. Built from byte permutes.
-__device__ __forceinline__ u32x4 column8(const u32x4 *in, int c) {
-    const int p = c >> 1;
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-    u32x4 o;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] = __builtin_amdgcn_perm(in[2 * t + 1][p], in[2 * t][p], sel);
-    return o;
+// Row-major token region [256 rows][64 k]: chunk c of row r at c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz_k(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
+// K-row region [64 k][256 cols]: 16-byte chunk q of row k at q ^ ((k & 3) << 2),
+// so the 4 rows x 4 chunks that 32 lanes of a transposing read touch fall in
+// 16 different bank groups.
+__device__ __forceinline__ int swz_mn(int k, int col) {
+    return k * kTile + (((col >> 3) ^ ((k & 3) << 2)) << 3) + (col & 7);
 }
 
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
+// MFMA operand for rows c0..c0+31 (columns of the K-row region) and
+// k = 16 ks .. 16 ks + 15: lane group g = lane / 16 covers rows
+// c0 + 16 (g & 1) .. +15 and k 8 (g >> 1) .. +7; lane j of the group names
+// row 4-block j / 4, chunk j % 4, and receives column j of each 4-row block.
+__device__ __forceinline__ bf16x8_t frag_mn(const bf16_t *R, int c0, int ks, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int k = ks * 16 + 8 * (g >> 1) + (j >> 2);
+    const int col = c0 + 16 * (g & 1) + 4 * (j & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(R + swz_mn(k, col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(R + swz_mn(k + 4, col)));
+    const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
 
-template <int KIND>
-__global__ __launch_bounds__(512, 1) void bwd_gemm(BGArgs a) {
-    constexpr int NS = 2, MS = 4;
-    __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+// Even spread of NRD fragment reads and NWR (write, load) pairs over the NMF
+// MFMAs of a quarter.
+template <int NMF, int NRD, int NWR, int Q = 0>
+__device__ __forceinline__ void sched_quarter() {
+    if constexpr (Q < NMF) {
+        MOE_SGB(kSgMfma, 1);
+        constexpr int r = (Q + 1) * NRD / NMF - Q * NRD / NMF;
+        if constexpr (r > 0) MOE_SGB(kSgDsRead, r);
+        constexpr int w = (Q + 1) * NWR / NMF - Q * NWR / NMF;
+        if constexpr (w > 0) {
+            MOE_SGB(kSgDsWrite, w);
+            MOE_SGB(kSgVmemRead, w);
+        }
+        sched_quarter<NMF, NRD, NWR, Q + 1>();
+    }
+}
+
+// One output tile. dgrad: token rows [row0, row0 + rows) of P (all of one
+// expert e), columns [a0, a0 + 256) of C, K = a.K. wgrad: rows [b0, b0 + 256)
+// of C = dW[e], columns [a0, a0 + 256), K = the nk_tok tokens of expert e
+// starting at row0. FULL (HALF = false): wave w owns columns 128 (w % 2) ..
+// and rows 128 (w / 2) ..; HALF: columns 64 w .. +63, rows 0..127.
+template <int KIND, bool ODD, bool HALF>
+__device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0, int row0, int rows,
+                                         int nk_tok, bf16_t *LB0, bf16_t *LB1) {
+    constexpr bool WG = KIND == kWgrad;
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    constexpr int XB = WG ? 8 : (HALF ? 4 : 8);     // B chunks per thread per k-step
+    constexpr int NMF = NI * NJ;
+    constexpr int NRD = 2 * NI + (WG ? 2 : 1) * NJ;
+    constexpr int NWR = (8 + XB) / 2;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int acol0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int brow0 = HALF ? 0 : (wave >> 1) * 128;
+
+    // reduction length in k-steps; wgrad: rounded up to even, rows past the
+    // expert's tokens read as zero
+    const int Krows = WG ? nk_tok : a.K;
+    int nk = (Krows + kBK - 1) / kBK;
+    if (WG) nk = max(2, (nk + 1) & ~1);
+    nk = __builtin_amdgcn_readfirstlane(nk);
+
+    // A: K-row storage; thread t moves chunk t % 32 of k-rows t / 32 + 8 j
+    const bf16_t *abase = WG ? a.A + static_cast<int64_t>(row0) * a.lda
+                             : a.A + static_cast<int64_t>(e) * a.a_expert_stride;
+    const int ca = tid & 31, kr0 = tid >> 5;
+    const int acol = min(a0 + 8 * ca, a.a_dim - 8);
+    const int va0 = (kr0 * a.lda + acol) * 2;
+    const int vstep_a = 16 * a.lda;                     // 8 rows, bytes
+    const int offa = swz_mn(kr0, 8 * ca);              // + 8 j rows
+    // B: wgrad K-row storage like A; dgrad row-major token rows rb + 32 j
+    const bf16_t *bbase = a.B + static_cast<int64_t>(row0) * a.ldb;
+    int vb[XB];
+    int offb;
+    if (WG) {
+        const int bcol = min(b0 + 8 * ca, a.b_dim - 8);
+        vb[0] = (kr0 * a.ldb + bcol) * 2;
+#pragma unroll
+        for (int j = 1; j < XB; ++j) vb[j] = vb[0] + j * 16 * a.ldb;
+        offb = swz_mn(kr0, 8 * ca);
+    } else {
+        const int chunk = tid & 7, rb = tid >> 3;
+#pragma unroll
+        for (int j = 0; j < XB; ++j) {
+            const int r = rb + 32 * j;
+            vb[j] = ((r < rows ? r : rows - 1) * a.ldb + chunk * 8) * 2;
+        }
+        offb = swz_k(rb, chunk);
+    }
+    const __amdgpu_buffer_rsrc_t rb_tok = make_rsrc(bbase);   // dgrad B (k advances within rows)
+
+    floatx16 acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    u32x4 RA[8], RB[XB];
+    bf16x8_t fa0[NI], fb0[NJ], fa1[NI], fb1[NJ];
+
+// K-row operands: a resource over the k-step's remaining rows, so rows past
+// the end read as zero
+#define MOE_KROWS_RSRC(BASE, LD, KT)                                                              \
+    make_rsrc((BASE) + static_cast<int64_t>(KT) * kBK * (LD),                                   \
+              static_cast<uint32_t>(max(0, Krows - (KT) * kBK)) * static_cast<uint32_t>(LD) * 2u)
+#define MOE_LD(KT, H)                                                                             \
+    do {                                                                                        \
+        const __amdgpu_buffer_rsrc_t ra_ = MOE_KROWS_RSRC(abase, a.lda, KT);                    \
+        _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                            \
+            RA[j] = __builtin_amdgcn_raw_buffer_load_b128(ra_, va0 + j * vstep_a, 0, 0);        \
+        if (WG) {                                                                               \
+            const __amdgpu_buffer_rsrc_t rbk_ = MOE_KROWS_RSRC(bbase, a.ldb, KT);               \
+            _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                        \
+                RB[j] = __builtin_amdgcn_raw_buffer_load_b128(rbk_, vb[j], 0, 0);               \
+        } else {                                                                                \
+            _Pragma("unroll") for (int j = (XB / 2) * (H); j < (XB / 2) * (H) + XB / 2; ++j)    \
+                RB[j] = __builtin_amdgcn_raw_buffer_load_b128(rb_tok, vb[j], (KT) * kBK * 2, 0); \
+        }                                                                                       \
+    } while (0)
+#define MOE_WR(LB, H)                                                                             \
+    do {                                                                                        \
+        _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                            \
+            *reinterpret_cast<u32x4 *>((LB) + offa + j * 8 * kTile) = RA[j];                     \
+        if (WG) {                                                                               \
+            _Pragma("unroll") for (int j = 4 * (H); j < 4 * (H) + 4; ++j)                        \
+                *reinterpret_cast<u32x4 *>((LB) + kRegion + offb + j * 8 * kTile) = RB[j];       \
+        } else {                                                                                \
+            _Pragma("unroll") for (int j = (XB / 2) * (H); j < (XB / 2) * (H) + XB / 2; ++j)    \
+                *reinterpret_cast<u32x4 *>((LB) + kRegion + offb + j * 32 * kBK) = RB[j];        \
+        }                                                                                       \
+    } while (0)
+#define MOE_RD(FA, FB, LB, KS)                                                                    \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < NI; ++i) FA[i] = frag_mn((LB), acol0 + 32 * i, (KS), lane); \
+        if (WG) {                                                                               \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                      \
+                FB[j] = frag_mn((LB) + kRegion, brow0 + 32 * j, (KS), lane);                    \
+        } else {                                                                                \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                      \
+                FB[j] = *reinterpret_cast<const bf16x8_t *>((LB) + kRegion +                    \
+                                                            swz_k(brow0 + 32 * j + l32, (KS) * 2 + lhi)); \
+        }                                                                                       \
+    } while (0)
+#define MOE_MF(FA, FB)                                                                            \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < NI; ++i)                                          \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                      \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+    } while (0)
+#define MOE_STEP(CUR, NXT, T)                                                                     \
+    do {                                                                                        \
+        const int kk_ = (T) + 2 < nk ? (T) + 2 : nk - 1;                                        \
+        MOE_MF(fa0, fb0); MOE_RD(fa1, fb1, CUR, 1);                                             \
+        sched_quarter<NMF, NRD, 0>(); __builtin_amdgcn_sched_barrier(0);                        \
+        MOE_MF(fa1, fb1); MOE_RD(fa0, fb0, CUR, 2); MOE_WR(NXT, 0); MOE_LD(kk_, 0);             \
+        sched_quarter<NMF, NRD, NWR>(); __builtin_amdgcn_sched_barrier(0);                      \
+        MOE_MF(fa0, fb0); MOE_RD(fa1, fb1, CUR, 3); MOE_WR(NXT, 1); MOE_LD(kk_, 1);             \
+        sched_quarter<NMF, NRD, NWR>(); __builtin_amdgcn_sched_barrier(0);                      \
+        MOE_LDS_BARRIER();                                                                      \
+        MOE_MF(fa1, fb1); MOE_RD(fa0, fb0, NXT, 0);                                             \
+        sched_quarter<NMF, NRD, 0>(); __builtin_amdgcn_sched_barrier(0);                        \
+    } while (0)
+
+    MOE_LD(0, 0);
+    MOE_LD(0, 1);
+    MOE_LDS_BARRIER();   // every wave is done reading the previous tile's stages
+    MOE_WR(LB0, 0);
+    MOE_WR(LB0, 1);
+    {
+        const int k1 = nk > 1 ? 1 : 0;
+        MOE_LD(k1, 0);
+        MOE_LD(k1, 1);
+    }
+    MOE_LDS_BARRIER();
+    MOE_RD(fa0, fb0, LB0, 0);
+    if (ODD) {
+        for (int t = 0; t + 1 < nk; t += 2) {
+            MOE_STEP(LB0, LB1, t);
+            MOE_STEP(LB1, LB0, t + 1);
+        }
+        MOE_STEP(LB0, LB1, nk - 1);
+    } else {
+        for (int t = 0; t < nk; t += 2) {
+            MOE_STEP(LB0, LB1, t);
+            MOE_STEP(LB1, LB0, t + 1);
+        }
+    }
+#undef MOE_KROWS_RSRC
+#undef MOE_LD
+#undef MOE_WR
+#undef MOE_RD
+#undef MOE_MF
+#undef MOE_STEP
+
+    // ------------------------------------------------------------ epilogue
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int bl = brow0 + j * 32 + l32;   // row of C within the tile
+        if (!WG && bl >= rows) continue;
+        if (WG && b0 + bl >= a.b_dim) continue;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int col = a0 + acol0 + i * 32 + 8 * gq + 4 * lhi;
+                if (col >= a.a_dim) continue;
+                if (KIND == kWgrad) {
+                    const float4 o = make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                                                 acc[i][j][4 * gq + 3]);
+                    float *C = static_cast<float *>(a.C) + (static_cast<int64_t>(e) * a.b_dim + b0 + bl) * a.a_dim + col;
+                    *reinterpret_cast<float4 *>(C) = o;
+                } else if (KIND == kDgradPlain) {
+                    uint2 o;
+                    o.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+                    o.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+                    bf16_t *C = static_cast<bf16_t *>(a.C) + (static_cast<int64_t>(row0) + bl) * a.a_dim + col;
+                    *reinterpret_cast<uint2 *>(C) = o;
+                } else {
+                    const int64_t r = static_cast<int64_t>(row0) + bl;
+                    const bf16_t *gr = a.GU + r * 2 * a.a_dim;
+                    const uint2 gv = *reinterpret_cast<const uint2 *>(gr + col);
+                    const uint2 uv = *reinterpret_cast<const uint2 *>(gr + a.a_dim + col);
+                    const float g[4] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y)};
+                    const float u[4] = {bf16lo(uv.x), bf16hi(uv.x), bf16lo(uv.y), bf16hi(uv.y)};
+                    float dg[4], du[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float d = acc[i][j][4 * gq + q];
+                        // hardware exp and reciprocal (a few ulp): with the
+                        // IEEE divide the epilogue needs so many registers
+                        // that the accumulators get spilled inside the k-loop
+                        const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-g[q]));
+                        dg[q] = d * u[q] * (s * (1.0f + g[q] * (1.0f - s)));
+                        du[q] = d * (g[q] * s);
+                    }
+                    bf16_t *dr = a.dGU + r * 2 * a.a_dim;
+                    uint2 og, ou;
+                    og.x = pack_bf16x2(dg[0], dg[1]);
+                    og.y = pack_bf16x2(dg[2], dg[3]);
+                    ou.x = pack_bf16x2(du[0], du[1]);
+                    ou.y = pack_bf16x2(du[2], du[3]);
+                    *reinterpret_cast<uint2 *>(dr + col) = og;
+                    *reinterpret_cast<uint2 *>(dr + a.a_dim + col) = ou;
+                }
+            }
+        }
+    }
+}
+
+// ODD (data-gradient GEMMs only): K / 64 is odd.
+template <int KIND, bool ODD>
+__global__ __launch_bounds__(256, 1) void bwd_gemm(BGArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16_t LB0[kStage];
+    __shared__ __attribute__((aligned(16))) bf16_t LB1[kStage];
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
     __shared__ int s_order[256];
-
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & 3, wm = wave >> 2;
-    const int l32 = lane & 31, lhi = lane >> 5;
-    const bool loads_a = wave < 4;       // waves 0..3 stage A, waves 4..7 stage B
-    const int lt = tid & 255;
 
-    // ---------------------------------------------------------- schedule
     int total;
     if (KIND == kWgrad) {
         // experts by decreasing token count (ties: lower index first)
-        if (tid < 256) {
-            const int m = tid < a.E ? a.offsets[tid + 1] - a.offsets[tid] : -1;
-            s_tmp[tid] = m;
-        }
+        s_tmp[tid] = tid < a.E ? a.offsets[tid + 1] - a.offsets[tid] : -1;
         __syncthreads();
         if (tid < a.E) {
             const int m = s_tmp[tid];
@@ -104,207 +344,53 @@ __global__ __launch_bounds__(512, 1) void bwd_gemm(BGArgs a) {
         g.offsets = a.offsets;
         g.E = a.E;
         g.n_tiles = a.n_tiles_a;
-        total = build_tile_prefix_bal(g, s_cum, s_tmp);
+        total = build_tile_prefix(g, kTile, s_cum, s_tmp);
     }
+    total = __builtin_amdgcn_readfirstlane(total);
 
     for (int L = xcd_block_index(blockIdx.x, a.grid); L < total; L += a.grid) {
-        int e, a_tile, row0, K, nact, rows = 0, b0 = 0, row_lo = 0;
         if (KIND == kWgrad) {
             const int per = a.n_tiles_a * a.n_tiles_b;
-            e = s_order[L / per];
+            const int e = s_order[L / per];
             const int local = L % per;
-            a_tile = local % a.n_tiles_a;
-            b0 = (local / a.n_tiles_a) * TILE;
-            row0 = a.offsets[e];
-            K = a.offsets[e + 1] - row0;
-            nact = MS * 2;
+            const int row0 = a.offsets[e];
+            bwd_tile<KIND, false, false>(a, e, (local % a.n_tiles_a) * kTile, (local / a.n_tiles_a) * kTile, row0,
+                                         0, a.offsets[e + 1] - row0, LB0, LB1);
         } else {
             GGArgs g{};
             g.offsets = a.offsets;
             g.E = a.E;
             g.n_tiles = a.n_tiles_a;
-            const BalTile ti = decode_tile_bal(g, s_cum, L);
-            e = ti.seg;
-            a_tile = ti.n_tile;
-            row0 = ti.row0;
-            row_lo = ti.row_lo;
-            rows = ti.rows;
-            K = a.K;
-            nact = (rows + 31) >> 5;
-        }
-        int nw = nact - wm * MS;
-        nw = nw < 0 ? 0 : (nw > MS ? MS : nw);
-        nw = __builtin_amdgcn_readfirstlane(nw);   // wave-uniform
-        const int a0 = a_tile * TILE;
-        const int nk = (K + BK - 1) / BK;
-
-        // ---- per-thread staging geometry: waves 0..3 stage A, waves 4..7 B.
-        // K-major operand: block (cb = lt & 31, kb = lt >> 5) covers storage
-        // rows k0 + 8 kb + j (j < 8) and columns c0 + 8 cb .. +7, transposed
-        // into LDS rows 8 cb + c. Row-major operand (B of the data-gradient
-        // GEMMs): 16-byte chunk lt & 7 of tile rows (lt >> 3) + 32 j.
-        const bool ks_loader = loads_a || KIND == kWgrad;
-        const int cb = lt & 31, kb = lt >> 5;
-        const int ks_ld = loads_a ? a.lda : a.ldb;
-        const bool col_ok = loads_a ? (a0 + 8 * cb < a.a_dim) : (KIND != kWgrad || b0 + 8 * cb < a.b_dim);
-        const bf16_t *base;
-        if (loads_a)
-            base = (KIND == kWgrad ? a.A + static_cast<int64_t>(row0) * a.lda
-                                   : a.A + static_cast<int64_t>(e) * a.a_expert_stride) + a0 + 8 * cb;
-        else if (KIND == kWgrad)
-            base = a.B + static_cast<int64_t>(row0) * a.ldb + b0 + 8 * cb;
-        else
-            base = a.B + (static_cast<int64_t>(row0) + row_lo) * a.ldb + (lt & 7) * 8;
-        const int ks_off = loads_a ? 0 : TILE * BK;
-
-        floatx16 acc[NS][MS];
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-#pragma unroll
-            for (int j = 0; j < MS; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-        u32x4 v[8];
-
-#define MOE_BWD_LOAD(kt_)                                                                     \
-    do {                                                                                    \
-        const int k0_ = (kt_) * BK;                                                         \
-        if (ks_loader) {                                                                    \
-            _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                 \
-                const int k = k0_ + 8 * kb + j;                                             \
-                u32x4 z = {0u, 0u, 0u, 0u};                                                 \
-                if (col_ok && k < K)                                                        \
-                    z = *reinterpret_cast<const u32x4 *>(base + static_cast<int64_t>(k) * ks_ld); \
-                v[j] = z;                                                                   \
-            }                                                                               \
-        } else {                                                                            \
-            _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                 \
-                const int r = (lt >> 3) + 32 * j;                                           \
-                v[j] = *reinterpret_cast<const u32x4 *>(base + (r < rows ? r : rows - 1) * ks_ld + k0_); \
-            }                                                                               \
-        }                                                                                   \
-    } while (0)
-
-#define MOE_BWD_STORE(buf_)                                                                   \
-    do {                                                                                    \
-        bf16_t *s_ = smem + (buf_) * STAGE + ks_off;                                        \
-        if (ks_loader) {                                                                    \
-            _Pragma("unroll") for (int c = 0; c < 8; ++c)                                   \
-                *reinterpret_cast<u32x4 *>(s_ + swz(8 * cb + c, kb)) = column8(v, c);       \
-        } else {                                                                            \
-            _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
-                *reinterpret_cast<u32x4 *>(s_ + swz((lt >> 3) + 32 * j, lt & 7)) = v[j];    \
-        }                                                                                   \
-    } while (0)
-
-        if (nk > 0) {
-            MOE_BWD_LOAD(0);
-            MOE_BWD_STORE(0);
-        }
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            if (kt + 1 < nk) MOE_BWD_LOAD(kt + 1);
-            const bf16_t *sa = smem + (kt & 1) * STAGE;
-            const bf16_t *sb = sa + TILE * BK;
-            if (nw > 0) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int ch = ks * 2 + lhi;
-                    bf16x8_t af[NS], bfr[MS];
-#pragma unroll
-                    for (int i = 0; i < NS; ++i)
-                        af[i] = *reinterpret_cast<const bf16x8_t *>(sa + swz(wn * 64 + i * 32 + l32, ch));
-#pragma unroll
-                    for (int j = 0; j < MS; ++j)
-                        bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + swz(wm * 128 + j * 32 + l32, ch));
-#pragma unroll
-                    for (int j = 0; j < MS; ++j)
-                        if (j < nw)
-#pragma unroll
-                            for (int i = 0; i < NS; ++i)
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                }
-            }
-            if (kt + 1 < nk) MOE_BWD_STORE((kt + 1) & 1);
-            __syncthreads();
-        }
-#undef MOE_BWD_LOAD
-#undef MOE_BWD_STORE
-
-        // ---------------------------------------------------------- epilogue
-#pragma unroll
-        for (int j = 0; j < MS; ++j) {
-            const int bl = wm * 128 + j * 32 + l32;   // row of C within the tile
-            if (j >= nw) continue;
-            if (KIND != kWgrad && bl >= rows) continue;
-            if (KIND == kWgrad && b0 + bl >= a.b_dim) continue;
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int col = a0 + wn * 64 + i * 32 + 8 * gq + 4 * lhi;
-                    if (col >= a.a_dim) continue;
-                    if (KIND == kWgrad) {
-                        float4 o = make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                                               acc[i][j][4 * gq + 3]);
-                        float *C = static_cast<float *>(a.C) +
-                                   (static_cast<int64_t>(e) * a.b_dim + b0 + bl) * a.a_dim + col;
-                        *reinterpret_cast<float4 *>(C) = o;
-                    } else if (KIND == kDgradPlain) {
-                        uint2 o;
-                        o.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
-                        o.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-                        bf16_t *C = static_cast<bf16_t *>(a.C) +
-                                    (static_cast<int64_t>(row0) + row_lo + bl) * a.a_dim + col;
-                        *reinterpret_cast<uint2 *>(C) = o;
-                    } else {
-                        const int64_t r = static_cast<int64_t>(row0) + row_lo + bl;
-                        const bf16_t *gr = a.GU + r * 2 * a.a_dim;
-                        const uint2 gv = *reinterpret_cast<const uint2 *>(gr + col);
-                        const uint2 uv = *reinterpret_cast<const uint2 *>(gr + a.a_dim + col);
-                        const float g[4] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y)};
-                        const float u[4] = {bf16lo(uv.x), bf16hi(uv.x), bf16lo(uv.y), bf16hi(uv.y)};
-                        float dg[4], du[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float d = acc[i][j][4 * gq + q];
-                            const float s = 1.0f / (1.0f + expf(-g[q]));
-                            dg[q] = d * u[q] * (s * (1.0f + g[q] * (1.0f - s)));
-                            du[q] = d * (g[q] * s);
-                        }
-                        bf16_t *dr = a.dGU + r * 2 * a.a_dim;
-                        uint2 og, ou;
-                        og.x = pack_bf16x2(dg[0], dg[1]);
-                        og.y = pack_bf16x2(dg[2], dg[3]);
-                        ou.x = pack_bf16x2(du[0], du[1]);
-                        ou.y = pack_bf16x2(du[2], du[3]);
-                        *reinterpret_cast<uint2 *>(dr + col) = og;
-                        *reinterpret_cast<uint2 *>(dr + a.a_dim + col) = ou;
-                    }
-                }
-            }
+            const TileInfo ti = decode_tile(g, s_cum, L, kTile);
+            const int rows = min(kTile, ti.M - ti.m0);
+            if (rows > kTile / 2)
+                bwd_tile<KIND, ODD, false>(a, ti.seg, ti.n_tile * kTile, 0, ti.row0 + ti.m0, rows, 0, LB0, LB1);
+            else
+                bwd_tile<KIND, ODD, true>(a, ti.seg, ti.n_tile * kTile, 0, ti.row0 + ti.m0, rows, 0, LB0, LB1);
         }
     }
 }
 
 template <int KIND>
 int launch_bwd(BGArgs a, int64_t P, hipStream_t s, const char *what) {
-    a.n_tiles_a = (a.a_dim + TILE - 1) / TILE;
+    a.n_tiles_a = (a.a_dim + kTile - 1) / kTile;
     int64_t upper;
     if (KIND == kWgrad) {
-        a.n_tiles_b = (a.b_dim + TILE - 1) / TILE;
+        a.n_tiles_b = (a.b_dim + kTile - 1) / kTile;
         upper = static_cast<int64_t>(a.E) * a.n_tiles_a * a.n_tiles_b;
     } else {
         a.n_tiles_b = 1;
-        upper = (P / 256 + a.E) * static_cast<int64_t>(a.n_tiles_a);
+        upper = (P / kTile + a.E) * static_cast<int64_t>(a.n_tiles_a);
     }
     int64_t grid = num_cus();
     if (grid > upper) grid = upper;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
     a.grid = static_cast<int>(grid);
-    hipLaunchKernelGGL((bwd_gemm<KIND>), dim3(a.grid), dim3(512), 0, s, a);
+    if (KIND != kWgrad && ((a.K / kBK) & 1))
+        hipLaunchKernelGGL((bwd_gemm<KIND, true>), dim3(a.grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_gemm<KIND, false>), dim3(a.grid), dim3(256), 0, s, a);
     return check_launch(what);
 }
 

@@ -184,6 +184,22 @@ __device__ __forceinline__ BalTile decode_tile_bal(const GGArgs &a, const int *s
     return ti;
 }
 
+// Raw buffer resource over [p, p + bytes) (reads past the end return zero).
+// p must be uniform across the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes = 0x7fffffffu) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo),
+                                             static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+}
+
+#define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200, kSgVmemRead = 0x020;
+// all LDS traffic of this wave done, then the workgroup barrier; the memory
+// clobber keeps the compiler from moving LDS accesses across it
+#define MOE_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 __device__ __forceinline__ float gelu_erf_f(float a) {
     return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));

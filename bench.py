@@ -86,6 +86,112 @@ def recorded_traffic(workload: str):
     return rec
 
 
+class ClockSampler:
+    """Samples the GPU core clock (MHz) on a background thread while the timed
+    steps run: amdsmi's current GFX clock, else the active level of sysfs
+    pp_dpm_sclk (a DPM level, coarser than the real clock)."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.period = period_s
+        self.smi = None
+        self.source = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            self.smi = (amdsmi, h)
+            self.source = "amdsmi current GFX clock"
+        except Exception:
+            self.smi = None
+        self.files = [] if self.smi else sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if self.files:
+            self.source = "sysfs pp_dpm_sclk active level"
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        if self.smi:
+            amdsmi, h = self.smi
+            try:
+                return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+            except Exception:
+                return None
+        for f in self.files:
+            try:
+                with open(f) as fh:
+                    for line in fh:
+                        if line.strip().endswith("*"):
+                            return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+            except OSError:
+                continue
+        return None
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.asarray(self.samples)
+        return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
+                "samples": int(v.size), "source": self.source}
+
+
+def host_info():
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    info["host_ram_gib"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    info["visible_cpus"] = os.cpu_count()
+    return info
+
+
+def copy_bandwidth(torch, reps=5):
+    """Plain 1 GiB fp32 elementwise copy (read 1 GiB, write 1 GiB), best of reps."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    best = None
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(src, out=dst)
+        e1.record()
+        e1.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del src, dst
+    return 2.0 * 4 * n / best / 1e9
+
+
 def copy_calibration():
     import torch
     n = 1 << 28                                   # fp32 elements: 1 GiB
@@ -99,10 +205,14 @@ def copy_calibration():
 
 
 def stage_bytes(cfg, P, es):
-    """Algorithmic HBM bytes of the memory-bound stages (index traffic included)."""
+    """Algorithmic HBM bytes of the memory-bound stages (index traffic included).
+    Inference permutes indices only (the first GEMM gathers rows); training
+    also writes x_perm."""
     T, h, k, E = cfg.T, cfg.h, cfg.k, cfg.E
     route = T * h * es + E * h * es + T * k * 8 + E * 4
-    permute = T * h * es + P * h * es + T * k * 4 * 3 + P * 4
+    permute = T * k * 4 * 3 + P * 4
+    if cfg.backward:
+        permute += T * h * es + P * h * es
     unpermute = P * h * es + T * h * es + T * k * 8 + (T * h * es if cfg.n_shared else 0)
     return dict(route=route, permute=permute, unpermute=unpermute)
 
@@ -200,11 +310,12 @@ def main():
         step()
     timers = {}
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        res = step(timers)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            res = step(timers)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
     counts = res["counts"].cpu().numpy()
     live = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
             for name, pairs in timers.items()}
@@ -230,6 +341,7 @@ def main():
         "frac_of_bf16_peak": flops / dt / 1e12 / PEAK_BF16_TFLOPS,
         "active_gflop_per_step": flops / 1e9,
         "expert_load": {"min": int(counts.min()), "max": int(counts.max())},
+        "gpu_clock": clock.summary(),
     }
 
     # roofline of the dominant call, from the events inside the timed steps
@@ -261,19 +373,23 @@ def main():
         E = cfg.E
         r = B.moe_route(inp["x"], inp["w_gate"], cfg.k, cfg.score, b_gate=inp.get("b_gate"),
                         sel_bias=inp.get("sel_bias"))
-        p = B.moe_permute(inp["x"], r["topk_idx"], E)
+        # as layer.forward runs them: inference gathers token rows inside the
+        # first GEMM (no dispatch copy); training materialises x_perm
+        p = B.moe_permute(inp["x"], r["topk_idx"], E, with_x_perm=train)
         has_sh = inp.get("w1_sh") is not None
-        f = B.moe_grouped_ffn(p["x_perm"], p["offsets"], inp["w1"], inp["w2"], cfg.act,
+        a_in = p["x_perm"] if train else inp["x"]
+        g_rows = None if train else p["sorted_token"]
+        f = B.moe_grouped_ffn(a_in, p["offsets"], inp["w1"], inp["w2"], cfg.act,
                               b1=inp.get("b1"), b2=inp.get("b2"), x_sh=inp["x"] if has_sh else None,
-                              w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"))
+                              w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"), gather_rows=g_rows)
         calls = {
             "route": lambda: B.moe_route(inp["x"], inp["w_gate"], cfg.k, cfg.score,
                                          b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias")),
-            "permute": lambda: B.moe_permute(inp["x"], r["topk_idx"], E),
+            "permute": lambda: B.moe_permute(inp["x"], r["topk_idx"], E, with_x_perm=train),
             "grouped_ffn": lambda: B.moe_grouped_ffn(
-                p["x_perm"], p["offsets"], inp["w1"], inp["w2"], cfg.act, b1=inp.get("b1"),
+                a_in, p["offsets"], inp["w1"], inp["w2"], cfg.act, b1=inp.get("b1"),
                 b2=inp.get("b2"), x_sh=inp["x"] if has_sh else None, w1_sh=inp.get("w1_sh"),
-                w2_sh=inp.get("w2_sh")),
+                w2_sh=inp.get("w2_sh"), gather_rows=g_rows),
             "unpermute": lambda: B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"]),
         }
         if train:
@@ -326,9 +442,11 @@ def main():
         out["stages"] = stages
         del flush
 
+    out["hbm_copy_gbs"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.T))
+            out["cpu_baseline"].update(host_info())
         except Exception as exc:   # report, never hide, a failing baseline
             out["cpu_baseline"] = {"error": repr(exc)}
     print(json.dumps(out), flush=True)

@@ -134,7 +134,14 @@ int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
  * Quick Start). Segment e is rows [offsets[e], offsets[e+1]) of x_perm and
  * uses expert e's weights; segment sizes are read on the device.
  *
- *   x_perm  [P,h] dtype       permuted tokens (P = T*k)
+ *   x_perm  [P,h] dtype       permuted tokens (P = T*k); or, when
+ *                             gather_rows is not NULL, the unpermuted tokens
+ *                             [x_rows,h], permuted row r being
+ *                             x_perm[gather_rows[r]] (the sorted_token of
+ *                             moe_permute: the dispatch copy is then skipped).
+ *                             An index outside [0, x_rows) reads zeros.
+ *                             Gathering needs x_rows * h * 4 < 2^31.
+ *   gather_rows [P] int32|NULL, x_rows: see x_perm (x_rows ignored if NULL)
  *   offsets [E+1] int32       segment starts, offsets[E] = P
  *   w1      [E,n1*F,h] dtype  first projection; SwiGLU (n1 = 2): rows 0..F-1
  *                             gate, rows F..2F-1 up; GELU: n1 = 1
@@ -160,7 +167,8 @@ int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
  * rounding). A smaller non-null workspace is used as far as it goes.
  */
 size_t moe_grouped_ffn_workspace_size(int dtype);
-int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t h, int64_t F, int E,
+int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, int dtype,
+                    int64_t P, int64_t h, int64_t F, int E,
                     const int32_t *offsets, int act_kind, const void *w1, const void *b1,
                     const void *w2, const void *b2, const void *x_sh, int64_t T_sh,
                     const void *w1_sh, const void *w2_sh, void *act, void *gu, void *y,

@@ -39,8 +39,8 @@ _SIGS = {
     "moe_permute_workspace_size": ([_i64, _int, _int], _sz),
     "moe_permute": ([_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_grouped_ffn_workspace_size": ([_int], _sz),
-    "moe_grouped_ffn": ([_vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp, _i64,
-                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_grouped_ffn": ([_vp, _vp, _i64, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp,
+                         _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_unpermute": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_unpermute_bwd": ([_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd": ([_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
@@ -168,11 +168,19 @@ def moe_permute(x, topk_idx, E: int, with_x_perm: bool = True):
 
 def moe_grouped_ffn(x_perm, offsets, w1, w2, act: str = "swiglu", b1=None, b2=None, x_sh=None,
                     w1_sh=None, w2_sh=None, keep_gu: bool = False, use_workspace: bool = True,
-                    workspace=None):
+                    workspace=None, gather_rows=None):
+    """Grouped expert FFN. With gather_rows (the sorted_token of
+    moe_permute), x_perm is the unpermuted x [T,h] and the first GEMM reads
+    its rows in permuted order itself."""
     _req(x_perm, "x_perm")
     dev = x_perm.device
     dt = x_perm.dtype
-    P, h = x_perm.shape
+    x_rows, h = x_perm.shape
+    if gather_rows is not None:
+        _req(gather_rows, "gather_rows", dtype=torch.int32, device=dev)
+        P = gather_rows.numel()
+    else:
+        P = x_rows
     E = w1.shape[0]
     n1 = 2 if act == "swiglu" else 1
     F = w2.shape[2]
@@ -199,7 +207,8 @@ def moe_grouped_ffn(x_perm, offsets, w1, w2, act: str = "swiglu", b1=None, b2=No
     else:
         nws = lib().moe_grouped_ffn_workspace_size(DTYPE[dt]) if use_workspace else 0
         ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
-    rc = lib().moe_grouped_ffn(_ptr(x_perm), DTYPE[dt], P, h, F, E, _ptr(offsets), ACT[act],
+    rc = lib().moe_grouped_ffn(_ptr(x_perm), _ptr(gather_rows), x_rows, DTYPE[dt], P, h, F, E,
+                               _ptr(offsets), ACT[act],
                                _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(x_sh), T_sh,
                                _ptr(w1_sh), _ptr(w2_sh), _ptr(out["act"]), _ptr(out["gu"]),
                                _ptr(out["y"]), _ptr(out["y_sh"]), _ptr(ws), nws, _stream(x_perm))

@@ -116,16 +116,22 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
 
     const bf16_t *wseg = ti.shared ? static_cast<const bf16_t *>(a.B_sh)
                                    : static_cast<const bf16_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
-    const bf16_t *xbase = (ti.shared ? static_cast<const bf16_t *>(a.A_sh)
-                                     : static_cast<const bf16_t *>(a.A) + static_cast<int64_t>(ti.row0) * K) +
-                          static_cast<int64_t>(ti.m0) * K;
+    // token rows: rows m0.. of the segment, or (gather) the rows of A that
+    // a.gather names for them; a resource over all of A then, so that an
+    // out-of-range index reads zeros instead of faulting
+    const bool gather = a.gather != nullptr && !ti.shared;
+    const bf16_t *xbase = gather ? static_cast<const bf16_t *>(a.A)
+                                 : (ti.shared ? static_cast<const bf16_t *>(a.A_sh)
+                                              : static_cast<const bf16_t *>(a.A) + static_cast<int64_t>(ti.row0) * K) +
+                                       static_cast<int64_t>(ti.m0) * K;
     // weight rows of the tile: SwiGLU j even -> gate rows f, j odd -> up rows
     // N_out + f, f = n_tile*128 + (j/2)*32 + rb; plain: n_tile*256 + rb + 32 j
     const int wfirst = MODE == kModeSwiGLU ? ti.n_tile * (kTile / 2) : ti.n_tile * kTile;
     const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wseg + static_cast<int64_t>(wfirst) * K);
     const __amdgpu_buffer_rsrc_t rwu =
         make_rsrc(wseg + static_cast<int64_t>(MODE == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase);
+    const __amdgpu_buffer_rsrc_t rx =
+        gather ? make_rsrc(xbase, static_cast<uint32_t>(a.a_rows) * static_cast<uint32_t>(K) * 2u) : make_rsrc(xbase);
     int wv[8], xv[XJ];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -136,7 +142,9 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
 #pragma unroll
     for (int j = 0; j < XJ; ++j) {
         const int r = rb + 32 * j;
-        xv[j] = ((r < rows ? r : rows - 1) * K + chunk * 8) * 2;
+        int m = r < rows ? r : rows - 1;
+        if (gather) m = a.gather[ti.row0 + ti.m0 + m];
+        xv[j] = (m * K + chunk * 8) * 2;
     }
 
     floatx16 acc[NI][NJ];
@@ -524,6 +532,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
         if (m >= ti.M) m = ti.M - 1;
         const float *gw = Bseg + static_cast<int64_t>(wrow) * K + c4;
         const float *gx = Aseg + static_cast<int64_t>(m) * K + c4;
+        if (a.gather && !ti.shared) {
+            // gathered token row (indices checked on the device: out of range reads row 0)
+            int src = a.gather[ti.row0 + m];
+            if (src < 0 || src >= a.a_rows) src = 0;
+            gx = static_cast<const float *>(a.A) + static_cast<int64_t>(src) * K + c4;
+        }
 
         floatx4 acc[NT][MT];
 #pragma unroll
@@ -662,7 +676,8 @@ extern "C" size_t moe_grouped_ffn_workspace_size(int dtype) {
                             static_cast<size_t>(num_cus()) * kPartFloats);
 }
 
-extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t h, int64_t F,
+extern "C" int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, int dtype,
+                               int64_t P, int64_t h, int64_t F,
                                int E, const int32_t *offsets, int act_kind, const void *w1,
                                const void *b1, const void *w2, const void *b2, const void *x_sh,
                                int64_t T_sh, const void *w1_sh, const void *w2_sh, void *act,
@@ -672,6 +687,9 @@ extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t
     MOE_CHECK_ARG(offsets && w1 && w2 && act && y, MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: null required pointer");
     MOE_CHECK_ARG(P == 0 || x_perm, MOE_ERR_INVALID_ARG, "moe_grouped_ffn: null x_perm");
+    MOE_CHECK_ARG(gather_rows == nullptr || (x_rows > 0 && x_rows * h * 4 < (int64_t(1) << 31)),
+                  gather_rows == nullptr || x_rows > 0 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG,
+                  "moe_grouped_ffn: gathering needs 0 < x_rows and x_rows * h * 4 < 2^31");
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: bad dtype %d", dtype);
     MOE_CHECK_ARG(act_kind == MOE_ACT_GELU || act_kind == MOE_ACT_SWIGLU, MOE_ERR_INVALID_ARG,
@@ -709,6 +727,8 @@ extern "C" int moe_grouped_ffn(const void *x_perm, int dtype, int64_t P, int64_t
     // first projection + activation
     GGArgs g1{};
     g1.A = x_perm;
+    g1.gather = gather_rows;
+    g1.a_rows = static_cast<int>(gather_rows ? x_rows : 0);
     g1.B = w1;
     g1.bias = b1;
     g1.C = act;

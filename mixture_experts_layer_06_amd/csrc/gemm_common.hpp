@@ -34,6 +34,8 @@ struct GGArgs {
     int grid;               // blocks launched (persistent)
     float *ws;              // split workspace or null (bf16 forward kernel)
     int ws_tiles;           // fp32 partial tiles the workspace holds
+    const int32_t *gather;  // null, or: row r of the segments is row gather[r] of A
+    int a_rows;             // rows of A when gathering
 };
 
 constexpr int kMaxSeg = 260;

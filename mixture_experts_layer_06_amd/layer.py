@@ -37,12 +37,15 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
                     sel_bias=inp.get("sel_bias"), want_logits=keep_for_backward)
-    p = B.moe_permute(x, r["topk_idx"], E)
+    # inference: the first GEMM gathers token rows itself (no dispatch copy);
+    # training keeps x_perm for the weight gradient of the first projection
+    gather = not keep_for_backward
+    p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=not gather)
     has_sh = inp.get("w1_sh") is not None
     f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn(
-        p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"), b2=inp.get("b2"),
-        x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"),
-        keep_gu=keep_for_backward and act == "swiglu"))
+        x if gather else p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"),
+        b2=inp.get("b2"), x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"),
+        keep_gu=keep_for_backward and act == "swiglu", gather_rows=p["sorted_token"] if gather else None))
     out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"])
     res = dict(out=out)
     res.update(r)

@@ -90,17 +90,21 @@ def test_host_validation_rejects_bad_arguments(lib):
     rc = L.moe_permute(dummy, 1, 1000, 64, 16, 2, dummy, dummy, dummy, dummy, dummy, None, need, None)
     assert rc == 3
     # grouped ffn: F not a multiple of 64, gu with GELU, shared expert without weights
-    rc = L.moe_grouped_ffn(dummy, 1, 64, 128, 100, 4, dummy, 1, dummy, None, dummy, None, None, 0,
+    rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 100, 4, dummy, 1, dummy, None, dummy, None, None, 0,
                            None, None, dummy, None, dummy, None, None, 0, None)
     assert rc == 2
-    rc = L.moe_grouped_ffn(dummy, 1, 64, 128, 128, 4, dummy, 0, dummy, None, dummy, None, None, 0,
+    rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 0, dummy, None, dummy, None, None, 0,
                            None, None, dummy, dummy, dummy, None, None, 0, None)
     assert rc == 1
-    rc = L.moe_grouped_ffn(dummy, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, dummy, 16,
+    rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, dummy, 16,
+                           None, None, dummy, None, dummy, None, None, 0, None)
+    assert rc == 1
+    # gathering with no source rows
+    rc = L.moe_grouped_ffn(dummy, dummy, 0, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, None, 0,
                            None, None, dummy, None, dummy, None, None, 0, None)
     assert rc == 1
     # ... and a workspace size without a workspace
-    rc = L.moe_grouped_ffn(dummy, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, None, 0,
+    rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, None, 0,
                            None, None, dummy, None, dummy, None, None, 1 << 20, None)
     assert rc == 1
     # unpermute: negative T

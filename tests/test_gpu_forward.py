@@ -210,6 +210,21 @@ def test_single_token(moe_lib):
     assert rel_err(to_np32(g["out"]), ref["out"]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_gathering_first_gemm_matches_dispatch_copy(moe_lib, name):
+    """The inference path (first GEMM gathers x rows through sorted_token, no
+    x_perm) gives bitwise the results of the path that copies x_perm."""
+    cfg, inp, g, ref, perm = _run(name)
+    from mixture_experts_layer_06_amd import layer
+    g2 = layer.forward(to_device(inp), cfg.k, cfg.score, cfg.act, keep_for_backward=False)
+    torch.cuda.synchronize()
+    assert g2["x_perm"] is None
+    for key in ("act", "y", "out"):
+        assert torch.equal(g2[key], g[key]), key
+    if g["y_sh"] is not None:
+        assert torch.equal(g2["y_sh"], g["y_sh"])
+
+
 def test_forward_is_deterministic(moe_lib):
     from mixture_experts_layer_06_amd import layer
     cfg = wl.small_variant(wl.CONFIGS[3], T=512, h=256, F=128)

@@ -95,11 +95,19 @@ const char *moe_last_error(void);
  * index ascending; -0 equals +0; a NaN key ranks as -inf. Weights: softmax
  * renormalised over the k selected (= softmax of the selected logits);
  * sigmoid: sigma(l_j) / sum of the selected sigma(l_i).
+ *
+ * Workspace (optional; NULL with 0 bytes is valid): device memory of
+ * moe_route_workspace_size(T,E) bytes, 16-byte aligned. With it, bf16, at
+ * least 32 experts and no logits output, the route first computes all logits
+ * with bf16 MFMA and proven error bounds, then the fixed-order logits only of
+ * the experts that can still reach the top k; the outputs are identical, bit
+ * for bit, to those of the fixed-order pass over all experts.
  */
+size_t moe_route_workspace_size(int64_t T, int E);
 int moe_route(const void *x, int dtype, int64_t T, int64_t h, const void *w_gate,
               const float *b_gate, int E, int k, int score, const float *sel_bias,
               float *logits, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
-              int32_t *counts, void *stream);
+              int32_t *counts, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------- Permute
  * Dispatch stage ("Scalable Training ... with Megatron Core", section 2.1

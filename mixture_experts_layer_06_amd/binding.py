@@ -34,8 +34,9 @@ _SIGS = {
     "moe_abi_version": ([], _int),
     "moe_status_string": ([_int], ctypes.c_char_p),
     "moe_last_error": ([], ctypes.c_char_p),
+    "moe_route_workspace_size": ([_i64, _int], _sz),
     "moe_route": ([_vp, _int, _i64, _i64, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp,
-                   _vp], _int),
+                   _vp, _sz, _vp], _int),
     "moe_permute_workspace_size": ([_i64, _int, _int], _sz),
     "moe_permute": ([_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_grouped_ffn_workspace_size": ([_int], _sz),
@@ -121,7 +122,10 @@ def abi_version() -> int:
 # ----------------------------------------------------------------- forward
 
 def moe_route(x, w_gate, k: int, score: str = "softmax", b_gate=None, sel_bias=None,
-              want_logits: bool = False, want_map: bool = False):
+              want_logits: bool = False, want_map: bool = False, use_workspace: bool = True):
+    """Route stage. Without want_logits the library may take its MFMA-filtered
+    path (given a workspace); its outputs are bitwise those of the fixed-order
+    pass."""
     _req(x, "x")
     dev = x.device
     T, h = x.shape
@@ -136,10 +140,12 @@ def moe_route(x, w_gate, k: int, score: str = "softmax", b_gate=None, sel_bias=N
         logits=torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None,
         routing_map=torch.empty((T, E), dtype=torch.uint8, device=dev) if want_map else None,
     )
+    nws = lib().moe_route_workspace_size(T, E) if (use_workspace and not want_logits) else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     rc = lib().moe_route(_ptr(x), DTYPE[x.dtype], T, h, _ptr(w_gate), _ptr(b_gate), E, k,
                          SCORE[score], _ptr(sel_bias), _ptr(out["logits"]), _ptr(out["topk_idx"]),
                          _ptr(out["topk_w"]), _ptr(out["routing_map"]), _ptr(out["counts"]),
-                         _stream(x))
+                         _ptr(ws), nws, _stream(x))
     _check(rc, "moe_route")
     return out
 

@@ -331,6 +331,21 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
                         *reinterpret_cast<uint2 *>(gr + a.N_out + f) = ou;
                     }
                 }
+            } else if (MODE == kModeF32Out) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int n = ti.n_tile * kTile + wrow0 + i * 32 + nl;
+                    if (n >= a.N_out) continue;
+                    float *Cf = static_cast<float *>(a.C) + (crow0 + m) * a.N_out + n;
+                    if (n + 4 <= a.N_out && (a.N_out & 3) == 0) {
+                        *reinterpret_cast<float4 *>(Cf) = make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1],
+                                                                      acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < a.N_out) Cf[q] = acc[i][j][4 * gq + q];
+                    }
+                }
             } else {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
@@ -452,7 +467,33 @@ __device__ __forceinline__ void reduce_subtile(const GGArgs &a, const TileInfo &
     store_tile<MODE, HALF, J>(a, ti, acc, wave, lane);
 }
 
-// Block b: split tile b / 16, wave (b / 4) % 4, token subtile b % 4.
+// Sum of every split tile's pieces, in piece order, into piece 0 (one
+// float4 per thread, all tiles' positions spread over the grid).
+__global__ __launch_bounds__(256) void split_sum_kernel(GGArgs a) {
+    const int *hdr = reinterpret_cast<const int *>(a.ws);
+    const int rem = hdr[0], s = hdr[1];
+    if (s < 2) return;
+    constexpr int kQ = kPartFloats / 4;
+    const int64_t n = static_cast<int64_t>(rem) * kQ;
+    float4 *P4 = reinterpret_cast<float4 *>(a.ws + kWsHeaderFloats);
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t t = i / kQ, f = i - t * kQ;
+        float4 *base = P4 + t * s * kQ + f;
+        float4 acc = base[0];
+        for (int p = 1; p < s; ++p) {
+            const float4 v = base[static_cast<int64_t>(p) * kQ];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        base[0] = acc;
+    }
+}
+
+// Block b: split tile b / 16, wave (b / 4) % 4, token subtile b % 4 (the
+// pieces already summed into piece 0 by split_sum_kernel).
 template <int MODE>
 __global__ __launch_bounds__(64) void split_reduce(GGArgs a) {
     const int *hdr = reinterpret_cast<const int *>(a.ws);
@@ -470,23 +511,24 @@ __global__ __launch_bounds__(64) void split_reduce(GGArgs a) {
     const float4 *P4 = reinterpret_cast<const float4 *>(a.ws + kWsHeaderFloats) +
                        static_cast<int64_t>(t) * s * (kPartFloats / 4);
     const bool half = ti.M - ti.m0 <= kTile / 2;
+    const int s1 = 1;   // summed into piece 0
     const int lane = threadIdx.x;
     switch (J) {
     case 0:
-        if (half) reduce_subtile<MODE, true, 0>(a, ti, P4, s, wave, lane);
-        else reduce_subtile<MODE, false, 0>(a, ti, P4, s, wave, lane);
+        if (half) reduce_subtile<MODE, true, 0>(a, ti, P4, s1, wave, lane);
+        else reduce_subtile<MODE, false, 0>(a, ti, P4, s1, wave, lane);
         break;
     case 1:
-        if (half) reduce_subtile<MODE, true, 1>(a, ti, P4, s, wave, lane);
-        else reduce_subtile<MODE, false, 1>(a, ti, P4, s, wave, lane);
+        if (half) reduce_subtile<MODE, true, 1>(a, ti, P4, s1, wave, lane);
+        else reduce_subtile<MODE, false, 1>(a, ti, P4, s1, wave, lane);
         break;
     case 2:
-        if (half) reduce_subtile<MODE, true, 2>(a, ti, P4, s, wave, lane);
-        else reduce_subtile<MODE, false, 2>(a, ti, P4, s, wave, lane);
+        if (half) reduce_subtile<MODE, true, 2>(a, ti, P4, s1, wave, lane);
+        else reduce_subtile<MODE, false, 2>(a, ti, P4, s1, wave, lane);
         break;
     default:
-        if (half) reduce_subtile<MODE, true, 3>(a, ti, P4, s, wave, lane);
-        else reduce_subtile<MODE, false, 3>(a, ti, P4, s, wave, lane);
+        if (half) reduce_subtile<MODE, true, 3>(a, ti, P4, s1, wave, lane);
+        else reduce_subtile<MODE, false, 3>(a, ti, P4, s1, wave, lane);
         break;
     }
 }
@@ -642,7 +684,10 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
         upper = ((P + a.M_sh) / 64 + S) * static_cast<int64_t>(a.n_tiles);
     }
     int64_t grid = static_cast<int64_t>(num_cus()) * (dtype == MOE_DTYPE_BF16 ? 1 : 2);
-    if (grid > upper) grid = upper;
+    // with a split workspace every CU gets a block: a GEMM of few tiles is
+    // then cut along k over the whole GPU (blocks without work exit)
+    const bool splits = dtype == MOE_DTYPE_BF16 && a.ws && ((a.K / kBK) & 1) == 0;
+    if (grid > upper && !splits) grid = upper;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
     a.grid = static_cast<int>(grid);
@@ -655,6 +700,7 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
             if (a.ws) {
                 const int st = check_launch(what);
                 if (st != MOE_OK) return st;
+                hipLaunchKernelGGL(split_sum_kernel, dim3(2048), dim3(256), 0, s, a);
                 // at most grid / 2 split tiles, 16 blocks each
                 hipLaunchKernelGGL((split_reduce<MODE>), dim3(16 * (a.grid / 2 > 0 ? a.grid / 2 : 1)), dim3(64),
                                    0, s, a);
@@ -669,6 +715,35 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
 }  // namespace moe
 
 using namespace moe;
+
+namespace moe {
+
+size_t gemm_split_workspace_bytes() {
+    return sizeof(float) * (static_cast<size_t>(kWsHeaderFloats) + static_cast<size_t>(num_cus()) * kPartFloats);
+}
+
+int gemm_bf16_f32out(const void *A, const void *B, int T, int K, int N, float *C, int32_t *offsets, void *ws,
+                     size_t ws_bytes, hipStream_t s) {
+    launch_fill<int32_t>(offsets, 1, 0, s);
+    launch_fill<int32_t>(offsets + 1, 1, T, s);
+    GGArgs g{};
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.offsets = offsets;
+    g.E = 1;
+    g.N_out = N;
+    g.K = K;
+    const size_t hdr_bytes = sizeof(float) * kWsHeaderFloats, part_bytes = sizeof(float) * kPartFloats;
+    if (ws && ws_bytes >= hdr_bytes + 2 * part_bytes) {
+        g.ws = static_cast<float *>(ws);
+        const size_t n = (ws_bytes - hdr_bytes) / part_bytes;
+        g.ws_tiles = n > (size_t(1) << 20) ? (1 << 20) : static_cast<int>(n);
+    }
+    return launch_gemm<kModeF32Out>(g, MOE_DTYPE_BF16, T, s, "moe_route logits GEMM");
+}
+
+}  // namespace moe
 
 extern "C" size_t moe_grouped_ffn_workspace_size(int dtype) {
     if (dtype != MOE_DTYPE_BF16) return 0;

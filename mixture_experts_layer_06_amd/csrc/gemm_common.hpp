@@ -13,7 +13,15 @@
 
 namespace moe {
 
-enum GemmMode { kModePlain = 0, kModeSwiGLU = 1, kModeGELU = 2 };
+enum GemmMode { kModePlain = 0, kModeSwiGLU = 1, kModeGELU = 2, kModeF32Out = 3 };
+
+// fp32 C = A B^T for one segment of T rows (bf16 A [T][K], B [N][K]) on the
+// grouped GEMM kernel, split along K when few tiles; ws: the grouped FFN's
+// split workspace layout, offsets: 2 device ints set here. Used for the
+// router's MFMA logits.
+int gemm_bf16_f32out(const void *A, const void *B, int T, int K, int N, float *C, int32_t *offsets, void *ws,
+                     size_t ws_bytes, hipStream_t s);
+size_t gemm_split_workspace_bytes();
 
 struct GGArgs {
     const void *A;          // activations; segment s starts at row offsets[s]

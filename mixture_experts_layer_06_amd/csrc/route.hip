@@ -18,7 +18,7 @@
 // x and of each gate row per chunk. The halving tree of the order maps to:
 // s=32 -> lane q+4, s=16 -> lane q+2, s=8 -> lane q+1, then s=4,2,1 inside
 // lane 0's registers.
-#include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
 namespace {
@@ -63,6 +63,24 @@ __device__ __forceinline__ float sigmoid_canonical(float l) {
 // and a lower expert index.
 __device__ __forceinline__ bool precedes(float ka, int ia, float kb, int ib) {
     return ka > kb || (ka == kb && ia < ib);
+}
+
+// Routing weights of the k selected experts (logits sel_l, best first):
+// softmax renormalised over them, or sigma(l_j) / sum of the selected sigmas.
+__device__ __forceinline__ void route_weights(const float *sel_l, int k, int sigmoid, float *wv) {
+    float wsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        wv[j] = 0.0f;
+        if (j < k) {
+            if (sigmoid) wv[j] = 1.0f / (1.0f + expf(-sel_l[j]));
+            else wv[j] = expf(sel_l[j] - sel_l[0]);
+            wsum += wv[j];
+        }
+    }
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[j] = wv[j] * inv;
 }
 
 // Raw 16-byte piece of 8 elements (bf16) or half of one (fp32 needs two).
@@ -235,22 +253,13 @@ __global__ __launch_bounds__(256) void route_kernel(
                 if (jj == j) { sel_e[jj] = bi; sel_l[jj] = s_logit[g][bi < E ? bi : 0]; }
         }
         if (q == 0) {
-            float wsum = 0.0f, wv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                wv[j] = 0.0f;
-                if (j < k) {
-                    if (sigmoid) wv[j] = 1.0f / (1.0f + expf(-sel_l[j]));
-                    else wv[j] = expf(sel_l[j] - sel_l[0]);
-                    wsum += wv[j];
-                }
-            }
-            const float inv = 1.0f / wsum;
+            float wv[8];
+            route_weights(sel_l, k, sigmoid, wv);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if (j < k) {
                     topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
-                    topk_w[static_cast<int64_t>(t) * k + j] = wv[j] * inv;
+                    topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
                     if (sel_e[j] >= 0 && sel_e[j] < E) atomicAdd(&s_cnt[sel_e[j]], 1);
                 }
             }
@@ -270,15 +279,310 @@ __global__ __launch_bounds__(256) void route_kernel(
         if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
 }
 
+
+// ---------------------------------------------------------------------------
+// Fast path with the same results (many experts, bf16, no logits output).
+//
+// 1. l'(t,e) by bf16 MFMA with fp32 accumulation: the grouped GEMM kernel
+//    (v_mfma_f32_32x32x16_bf16, one accumulator chain along h per piece, at
+//    most 8 pieces summed in fp32 when the few tiles are split along h),
+//    and |x_t|_2, |w_e|_2.
+// 2. Both l' and the fixed-order logit l differ from the exact dot product
+//    by at most a multiple of u * S, S = sum_i |x_i w_i| <= |x_t| |w_e|
+//    (products of bf16 values are exact in fp32; every fp32 addition or fma
+//    rounds once): the MFMA chain by (h/16 + 16) u S (h/16 accumulations
+//    into C, up to 16 roundings inside one instruction, the final sum of
+//    pieces included), the fixed order by
+//    (h/64 + 6) u S (chains of h/64 fmas, a 6-level tree). Both terms are
+//    doubled, and the sum doubled again, for the interval half-width.
+// 3. Keys of the interval ends (the sigmoid key is monotone in l, and so is
+//    adding the selection bias), L_k = the k-th largest lower end; the
+//    experts whose upper end reaches L_k contain the top-k (every other
+//    expert is beaten by k experts for certain).
+// 4. Those candidates get their logits in the fixed order (the same code as
+//    route_kernel), and the top-k and the weights are taken from them
+//    exactly as route_kernel does: identical results, bit for bit.
+
+__global__ __launch_bounds__(64) void row_norm_kernel(const bf16_t *__restrict__ w, int h, float *__restrict__ out) {
+    const bf16_t *row = w + static_cast<int64_t>(blockIdx.x) * h;
+    float s = 0.0f;
+    for (int i = 8 * threadIdx.x; i < h; i += 8 * 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float a = bf16lo(v[c]), b = bf16hi(v[c]);
+            s = fmaf(a, a, s);
+            s = fmaf(b, b, s);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(s);
+}
+
+// Fixed-order logit of one (token, expert) pair by a group of 4 lanes: lane
+// q owns residues 16q..16q+15 of every 64-chunk (fma chains over ascending
+// chunks), then the halving tree: s=32 -> lane q+2, s=16 -> lane q+1, then
+// s=8,4,2,1 inside lane 0. The same additions as route_kernel's, so the
+// same bits. xs: the token's row in LDS; wrow: the expert's gate row.
+__device__ __forceinline__ float gate_dot4(const bf16_t *xs, const bf16_t *__restrict__ wrow, int h, int q) {
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    const int nchunk = h >> 6;
+    constexpr int U = 8;
+    int c = 0;
+    for (; c + U <= nchunk; c += U) {
+        u32x4 wv[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wv[u][0] = *reinterpret_cast<const u32x4 *>(wrow + 64 * (c + u) + 16 * q);
+            wv[u][1] = *reinterpret_cast<const u32x4 *>(wrow + 64 * (c + u) + 16 * q + 8);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xs + 64 * (c + u) + 16 * q);
+            const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xs + 64 * (c + u) + 16 * q + 8);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                acc[2 * d] = fmaf(bf16lo(x0[d]), bf16lo(wv[u][0][d]), acc[2 * d]);
+                acc[2 * d + 1] = fmaf(bf16hi(x0[d]), bf16hi(wv[u][0][d]), acc[2 * d + 1]);
+                acc[8 + 2 * d] = fmaf(bf16lo(x1[d]), bf16lo(wv[u][1][d]), acc[8 + 2 * d]);
+                acc[8 + 2 * d + 1] = fmaf(bf16hi(x1[d]), bf16hi(wv[u][1][d]), acc[8 + 2 * d + 1]);
+            }
+        }
+    }
+    for (; c < nchunk; ++c) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4 *>(wrow + 64 * c + 16 * q);
+        const u32x4 w1 = *reinterpret_cast<const u32x4 *>(wrow + 64 * c + 16 * q + 8);
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xs + 64 * c + 16 * q);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xs + 64 * c + 16 * q + 8);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            acc[2 * d] = fmaf(bf16lo(x0[d]), bf16lo(w0[d]), acc[2 * d]);
+            acc[2 * d + 1] = fmaf(bf16hi(x0[d]), bf16hi(w0[d]), acc[2 * d + 1]);
+            acc[8 + 2 * d] = fmaf(bf16lo(x1[d]), bf16lo(w1[d]), acc[8 + 2 * d]);
+            acc[8 + 2 * d + 1] = fmaf(bf16hi(x1[d]), bf16hi(w1[d]), acc[8 + 2 * d + 1]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = acc[i] + __shfl_down(acc[i], 2);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = acc[i] + __shfl_down(acc[i], 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + acc[i + 8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = acc[i] + acc[i + 4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i] = acc[i] + acc[i + 2];
+    return acc[0] + acc[1];
+}
+
+// One wave per token (4 per block). Lane l holds experts l + 64 m. The
+// token's row is copied to LDS (dynamic: 4 h bf16 per block) once.
+template <int SIGMOID>
+__global__ __launch_bounds__(256) void route_select_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ wg, const float *__restrict__ bg,
+    const float *__restrict__ sel_bias, const float *__restrict__ lp, const float *__restrict__ wnorm, int T,
+    int h, int E, int k, float cb, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    uint8_t *__restrict__ rmap, int32_t *__restrict__ counts) {
+    __shared__ int s_cand[4][kMaxE];
+    __shared__ float s_cl[4][kMaxE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    extern __shared__ __attribute__((aligned(16))) bf16_t s_xrows[];
+    if (t >= T) return;   // no block-wide barrier below
+    const bf16_t *xrow = x + static_cast<int64_t>(t) * h;
+    bf16_t *xl = s_xrows + static_cast<int64_t>(wave) * h;
+
+    // the row to LDS, and |x_t|_2 (fp32; its rounding is far inside the
+    // factor-2 margins)
+    float xs = 0.0f;
+#pragma unroll 4
+    for (int i = 8 * lane; i < h; i += 8 * 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(xrow + i);
+        *reinterpret_cast<u32x4 *>(xl + i) = v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float a = bf16lo(v[c]), b = bf16hi(v[c]);
+            xs = fmaf(a, a, xs);
+            xs = fmaf(b, b, xs);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) xs += __shfl_xor(xs, off);
+    const float xn = sqrtf(xs);
+
+    // key intervals
+    constexpr int M = kMaxE / 64;
+    float klo[M], khi[M];
+    bool bad = false;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int e = lane + 64 * m;
+        klo[m] = -INFINITY;
+        khi[m] = -INFINITY;
+        if (e < E) {
+            float l = lp[static_cast<int64_t>(t) * E + e];
+            if (bg) l = l + bg[e];
+            const float d = cb * xn * wnorm[e] + 4.0f * 0x1p-24f * (fabsf(l) + (bg ? fabsf(bg[e]) : 0.0f));
+            float lo = l - d, hi = l + d;
+            if (!(lo == lo) || !(hi == hi) || isinf(lo) || isinf(hi)) bad = true;
+            if (SIGMOID) {
+                lo = sigmoid_canonical(lo);
+                hi = sigmoid_canonical(hi);
+                if (sel_bias) {
+                    lo = lo + sel_bias[e];
+                    hi = hi + sel_bias[e];
+                }
+            }
+            klo[m] = lo;
+            khi[m] = hi;
+        }
+    }
+    bad = __any(bad);
+
+    // L_k: the k-th largest lower end
+    float Lk = -INFINITY;
+    {
+        uint32_t removed = 0;
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int e = lane + 64 * m;
+                if (e < E && !((removed >> m) & 1u) && precedes(klo[m], e, bv, bi)) {
+                    bv = klo[m];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (precedes(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            }
+            if (bi < E && (bi & 63) == lane) removed |= 1u << (bi >> 6);
+            Lk = bv;
+        }
+    }
+
+    // candidates: upper end reaching L_k (all of them if a bound is not finite)
+    int nc = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int e = lane + 64 * m;
+        const bool c = e < E && (bad || !(khi[m] < Lk));
+        const uint64_t mask = __ballot(c);
+        if (c) s_cand[wave][nc + __popcll(mask & ((uint64_t(1) << lane) - 1))] = e;
+        nc += __popcll(mask);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+    // exact logits of the candidates, 16 at a time (lane group g, lane q)
+    const int g = lane >> 2, q = lane & 3;
+    for (int c0 = 0; c0 < nc; c0 += 16) {
+        const int ci = c0 + g;
+        if (ci < nc) {
+            const int e = s_cand[wave][ci];
+            const float l = gate_dot4(xl, wg + static_cast<int64_t>(e) * h, h, q);
+            if (q == 0) s_cl[wave][ci] = bg ? l + bg[e] : l;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+    // exact top-k among the candidates (lane-strided), as route_kernel
+    float sel_l[8];
+    int sel_e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sel_l[j] = 0.0f; sel_e[j] = 0; }
+    uint32_t removed = 0;   // bit m: candidate lane + 64 m taken
+    for (int j = 0; j < k; ++j) {
+        float bk = 0.0f;
+        int bi = 0x7fffffff;
+        bool have = false;
+        for (int m = 0; m < M; ++m) {
+            const int ci = lane + 64 * m;
+            if (ci >= nc || ((removed >> m) & 1u)) continue;
+            const int e = s_cand[wave][ci];
+            const float l = s_cl[wave][ci];
+            float key = l;
+            if (SIGMOID) {
+                key = sigmoid_canonical(l);
+                if (sel_bias) key = key + sel_bias[e];
+            }
+            if (key != key) key = -INFINITY;
+            key = key + 0.0f;
+            if (!have || precedes(key, e, bk, bi)) { bk = key; bi = e; have = true; }
+        }
+        if (!have) { bk = -INFINITY; bi = 0x7fffffff; }
+        int bci = have ? 0 : -1;   // candidate slot of this lane's best (recomputed below)
+        (void)bci;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ok = __shfl_xor(bk, off);
+            const int oi = __shfl_xor(bi, off);
+            if (precedes(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+        }
+        // mark the winner's candidate slot and fetch its logit
+        for (int m = 0; m < M; ++m) {
+            const int ci = lane + 64 * m;
+            if (ci < nc && s_cand[wave][ci] == bi) removed |= 1u << m;
+        }
+        float bl = 0.0f;
+        for (int ci = 0; ci < nc; ++ci)
+            if (s_cand[wave][ci] == bi) bl = s_cl[wave][ci];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            if (jj == j) { sel_e[jj] = bi; sel_l[jj] = bl; }
+    }
+    if (lane == 0) {
+        float wv[8];
+        route_weights(sel_l, k, SIGMOID, wv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < k) {
+                topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
+                topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
+                if (sel_e[j] >= 0 && sel_e[j] < E) atomicAdd(&counts[sel_e[j]], 1);
+            }
+        }
+    }
+    if (rmap) {
+        uint8_t *row = rmap + static_cast<int64_t>(t) * E;
+        for (int e = lane; e < E; e += 64) {
+            bool on = false;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) on |= (j < k) && (sel_e[j] == e);
+            row[e] = on ? 1 : 0;
+        }
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
 
+// Workspace: l' [T][E] fp32, |w_e| [E] fp32, 2 ints of GEMM offsets, then
+// the GEMM's split workspace (256-byte aligned).
+static size_t route_ws_head(int64_t T, int E) {
+    const size_t b = sizeof(float) * (static_cast<size_t>(T) * E + E) + 2 * sizeof(int32_t);
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+extern "C" size_t moe_route_workspace_size(int64_t T, int E) {
+    if (T <= 0 || E <= 0) return 0;
+    return route_ws_head(T, E) + gemm_split_workspace_bytes();
+}
+
 extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const void *w_gate,
                          const float *b_gate, int E, int k, int score, const float *sel_bias,
                          float *logits, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
-                         int32_t *counts, void *stream) {
+                         int32_t *counts, void *workspace, size_t workspace_bytes, void *stream) {
     clear_error();
     MOE_CHECK_ARG(x && w_gate && topk_idx && topk_w && counts, MOE_ERR_INVALID_ARG,
                   "moe_route: null required pointer");
@@ -298,13 +602,43 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
                   "moe_route: sel_bias applies to sigmoid scoring only");
     MOE_CHECK_ARG(aligned16(x) && aligned16(w_gate), MOE_ERR_INVALID_ARG,
                   "moe_route: x and w_gate must be 16-byte aligned");
+    MOE_CHECK_ARG(workspace_bytes == 0 || workspace, MOE_ERR_INVALID_ARG,
+                  "moe_route: workspace_bytes > 0 with a null workspace");
     hipStream_t s = as_stream(stream);
     launch_fill<int32_t>(counts, E, 0, s);
     if (T == 0) return check_launch("moe_route fill");
-    const dim3 grid(static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock));
-    const dim3 block(256);
     const int sig = score == MOE_SCORE_SIGMOID;
     const int hh = static_cast<int>(h), TT = static_cast<int>(T);
+    if (dtype == MOE_DTYPE_BF16 && logits == nullptr && E >= 32 && workspace && h <= 8192 &&
+        workspace_bytes >= moe_route_workspace_size(T, E) && T * E < (int64_t(1) << 31)) {
+        const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
+        float *lp = static_cast<float *>(workspace);
+        float *wn = lp + static_cast<size_t>(T) * E;
+        int32_t *offs = reinterpret_cast<int32_t *>(wn + E);
+        char *gws = static_cast<char *>(workspace) + route_ws_head(T, E);
+        hipLaunchKernelGGL(row_norm_kernel, dim3(E), dim3(64), 0, s, wp, hh, wn);
+        const int st = gemm_bf16_f32out(xp, wp, TT, hh, E, lp, offs, gws, gemm_split_workspace_bytes(), s);
+        if (st != MOE_OK) return st;
+        // interval half-width per unit |x||w|: 2 * (2 (h/16 + 16) + 2 (h/64 + 6)) u
+        const float cb = static_cast<float>(2.0 * (2.0 * (h / 16 + 16) + 2.0 * (h / 64 + 6)) * 0x1p-24 * 1.001);
+        const dim3 g2(static_cast<unsigned>((T + 3) / 4));
+        const size_t lds = 4 * static_cast<size_t>(h) * sizeof(bf16_t);   // <= 64 KB
+        if (sig)
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&route_select_kernel<1>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        else
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&route_select_kernel<0>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (sig)
+            hipLaunchKernelGGL((route_select_kernel<1>), g2, dim3(256), lds, s, xp, wp, b_gate, sel_bias, lp, wn, TT,
+                               hh, E, k, cb, topk_idx, topk_w, routing_map, counts);
+        else
+            hipLaunchKernelGGL((route_select_kernel<0>), g2, dim3(256), lds, s, xp, wp, b_gate, sel_bias, lp, wn, TT,
+                               hh, E, k, cb, topk_idx, topk_w, routing_map, counts);
+        return check_launch("moe_route (MFMA filter)");
+    }
+    const dim3 grid(static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock));
+    const dim3 block(256);
     if (dtype == MOE_DTYPE_BF16) {
         const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
         if (E <= 16)

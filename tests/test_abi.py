@@ -59,28 +59,31 @@ def test_host_validation_rejects_bad_arguments(lib):
     vp = ctypes.c_void_p
     dummy = vp(4096)   # never dereferenced: every call below fails validation first
     # null required pointer
-    rc = L.moe_route(None, 1, 16, 64, dummy, None, 8, 2, 0, None, None, dummy, dummy, None, dummy, None)
+    rc = L.moe_route(None, 1, 16, 64, dummy, None, 8, 2, 0, None, None, dummy, dummy, None, dummy, None, 0, None)
     assert rc == 1 and b"null" in L.moe_last_error()
     # h not a multiple of 64
     rc = L.moe_route(dummy, 1, 16, 100, dummy, None, 8, 2, 0, None, None, dummy, dummy, None, dummy,
-                     None)
+                     None, 0, None)
     assert rc == 2
     # k > E, E > 256, k > 8
     for E, k in [(4, 5), (300, 2), (64, 9)]:
         rc = L.moe_route(dummy, 1, 16, 64, dummy, None, E, k, 0, None, None, dummy, dummy, None,
-                         dummy, None)
+                         dummy, None, 0, None)
         assert rc == 2, (E, k)
     # bad enums
     assert L.moe_route(dummy, 7, 16, 64, dummy, None, 8, 2, 0, None, None, dummy, dummy, None, dummy,
-                       None) == 1
+                       None, 0, None) == 1
     assert L.moe_route(dummy, 1, 16, 64, dummy, None, 8, 2, 5, None, None, dummy, dummy, None, dummy,
-                       None) == 1
+                       None, 0, None) == 1
     # selection bias with softmax scoring
     assert L.moe_route(dummy, 1, 16, 64, dummy, None, 8, 2, 0, dummy, None, dummy, dummy, None, dummy,
-                       None) == 1
+                       None, 0, None) == 1
+    # workspace size without a workspace
+    assert L.moe_route(dummy, 1, 16, 64, dummy, None, 64, 2, 0, None, None, dummy, dummy, None, dummy,
+                       None, 1 << 20, None) == 1
     # misaligned pointer
     assert L.moe_route(vp(4098), 1, 16, 64, dummy, None, 8, 2, 0, None, None, dummy, dummy, None,
-                       dummy, None) == 1
+                       dummy, None, 0, None) == 1
     # permute: workspace too small
     need = L.moe_permute_workspace_size(1000, 16, 2)
     assert need > 0

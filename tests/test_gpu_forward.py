@@ -166,6 +166,71 @@ def test_route_sigmoid_bias_ties_and_k_equals_e(moe_lib):
     assert rel_err(r["topk_w"].cpu().numpy(), ref["topk_w"]) <= 1e-5
 
 
+def _route_both(x, wg, k, score="softmax", b_gate=None, sel_bias=None):
+    """The MFMA-filtered route (no logits requested) and the fixed-order pass."""
+    from mixture_experts_layer_06_amd import binding as B
+    kw = dict(b_gate=None if b_gate is None else b_gate.cuda(),
+              sel_bias=None if sel_bias is None else sel_bias.cuda(), want_map=True)
+    fast = B.moe_route(x.cuda(), wg.cuda(), k, score, **kw)
+    slow = B.moe_route(x.cuda(), wg.cuda(), k, score, want_logits=True, **kw)
+    torch.cuda.synchronize()
+    return fast, slow
+
+
+def _assert_same_routing(fast, slow):
+    for key in ("topk_idx", "routing_map", "counts"):
+        assert torch.equal(fast[key], slow[key]), key
+    # bitwise, NaN weights included
+    assert torch.equal(fast["topk_w"].view(torch.int32), slow["topk_w"].view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["c3s", "c4s", "c5s"])
+def test_route_mfma_filter_matches_fixed_order(moe_lib, name):
+    """Bitwise: the filtered route of the many-expert cases (bf16 MFMA
+    logits with error bounds, fixed-order logits only for the experts that
+    can still be selected) against the fixed-order pass, and against the
+    oracle's indices."""
+    cfg, kw = CASES[name]
+    inp = wl.make_inputs(cfg, device="cpu", router_only=True, **kw)
+    fast, slow = _route_both(inp["x"], inp["w_gate"], cfg.k, cfg.score, inp.get("b_gate"),
+                             inp.get("sel_bias"))
+    _assert_same_routing(fast, slow)
+    o = oracle_inputs(inp)
+    ref = oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score, o["b_gate"], o["sel_bias"])
+    assert np.array_equal(fast["topk_idx"].cpu().numpy(), ref["topk_idx"])
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_route_mfma_filter_adversarial(moe_lib, score):
+    """Exact ties between experts (duplicate gate rows), logits one ulp apart,
+    an all-zero token, tokens of very different scale, and a token holding
+    inf (non-finite bounds: every expert is recomputed)."""
+    g = torch.Generator().manual_seed(21)
+    E, h, k = 64, 256, 6
+    x = torch.randn(300, h, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(E, h, generator=g) / 16).to(torch.bfloat16)
+    wg[40] = wg[7]
+    wg[41] = wg[7]
+    wg[63] = wg[0]
+    x[5] = 0
+    x[6] *= 1e4
+    x[7] *= 1e-4
+    x[8] = 0
+    x[8, 0] = 1.0
+    wg[:, 0] = 0.0
+    wg[10, 0] = 1.0
+    wg[11, 0] = 1.0078125   # one bf16 ulp above 1
+    x[9, 3] = float("inf")
+    sel = None
+    if score == "sigmoid":
+        sel = (torch.rand(E, generator=g) * 0.2 - 0.1).float()
+        sel[7] = sel[40]
+    fast, slow = _route_both(x, wg, k, score, sel_bias=sel)
+    _assert_same_routing(fast, slow)
+    ref = oracle.route(to_np32(x), to_np32(wg), k, score, None, None if sel is None else sel.numpy())
+    assert np.array_equal(fast["topk_idx"].cpu().numpy(), ref["topk_idx"])
+
+
 @pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (256, 8), (64, 1)])
 def test_layer_edge_shapes(moe_lib, E, k):
     from mixture_experts_layer_06_amd import layer
@@ -237,10 +302,10 @@ def test_forward_is_deterministic(moe_lib):
 
 def _expected_split(counts, n_tiles, nk, P, E, cus):
     """The last-round split plan the GEMM kernel derives (rem, s, ps), or
-    (0, 0, 0): tiles of 256 token rows, grid as the launcher sizes it."""
+    (0, 0, 0): tiles of 256 token rows; with a workspace the launcher gives
+    every compute unit a block."""
     total = int(sum((int(m) + 255) // 256 for m in counts)) * n_tiles
-    upper = (P // 256 + E) * n_tiles
-    G = min(cus, upper)
+    G = cus
     if G >= 8:
         G -= G % 8
     rem = total % G
@@ -254,10 +319,10 @@ def _expected_split(counts, n_tiles, nk, P, E, cus):
 
 def test_grouped_ffn_split_last_round(moe_lib):
     """A second GEMM with 384 tiles: on 256 compute units its last round of
-    128 tiles is split in two along F through the workspace. Outputs against
-    the oracle, the plan in the workspace header against the expected one,
-    and the result against the unsplit run (same values up to the fp32
-    summation order of two halves)."""
+    128 tiles is split in two along F through the workspace (the first GEMM,
+    48 tiles, is split along h). Outputs against the oracle, the plan in the
+    workspace header against the expected one, and the results against the
+    unsplit run (same values up to the fp32 summation order of the pieces)."""
     from mixture_experts_layer_06_amd import binding as B
     cfg = wl.small_variant(wl.CONFIGS[2], T=2400, h=4096, F=256)
     print("case split T=2400 h=4096 F=256", flush=True)
@@ -288,5 +353,5 @@ def test_grouped_ffn_split_last_round(moe_lib):
         for j in range(cfg.k):
             y_ref[perm["row_of"][t, j]] = ref["y_pair"][t, j]
     assert rel_err(y, y_ref) <= TOL["bf16"]
-    assert torch.equal(f["act"], f0["act"]) and torch.equal(f["gu"], f0["gu"])
-    assert rel_err(to_np32(f["y"]), to_np32(f0["y"])) <= 1e-2
+    for key in ("act", "gu", "y"):
+        assert rel_err(to_np32(f[key]), to_np32(f0[key])) <= 1e-2, key

@@ -88,8 +88,10 @@ def recorded_traffic(workload: str):
 
 class ClockSampler:
     """Samples the GPU core clock (MHz) on a background thread while the timed
-    steps run: amdsmi's current GFX clock, else the active level of sysfs
-    pp_dpm_sclk (a DPM level, coarser than the real clock)."""
+    steps run: the mean over XCDs of amdsmi's GPU-metrics current_gfxclks,
+    else the active level of sysfs pp_dpm_sclk (a DPM level, coarser than
+    the real clock). The driver refreshes these values on its own schedule,
+    so short runs get few distinct readings."""
 
     def __init__(self, period_s=0.002):
         import glob
@@ -101,9 +103,9 @@ class ClockSampler:
             import amdsmi
             amdsmi.amdsmi_init()
             h = amdsmi.amdsmi_get_processor_handles()[0]
-            amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            amdsmi.amdsmi_get_gpu_metrics_info(h)["current_gfxclks"]
             self.smi = (amdsmi, h)
-            self.source = "amdsmi current GFX clock"
+            self.source = "amdsmi gpu metrics current_gfxclks, mean over XCDs"
         except Exception:
             self.smi = None
         self.files = [] if self.smi else sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
@@ -117,7 +119,9 @@ class ClockSampler:
         if self.smi:
             amdsmi, h = self.smi
             try:
-                return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+                v = [c for c in amdsmi.amdsmi_get_gpu_metrics_info(h)["current_gfxclks"]
+                     if isinstance(c, (int, float)) and 0 < c < 10000]
+                return float(sum(v) / len(v)) if v else None
             except Exception:
                 return None
         for f in self.files:

@@ -10,6 +10,7 @@ from .moe import (  # noqa: F401
     combine,
     exp_c,
     expert_backward,
+    expert_fraction,
     expert_forward,
     forward,
     gate_logits,
@@ -18,6 +19,8 @@ from .moe import (  # noqa: F401
     permutation,
     route,
     router_backward_dlogits,
+    router_losses,
+    router_losses_dlogits,
     routing_weights,
     select_topk,
     selection_key,

@@ -40,6 +40,15 @@ Definitions followed (page titles are the pages' own):
   p_i E_i(x): out[t] = sum_j w[t,j] y_{e_j}(x_t), plus the shared expert's
   output with weight 1 (the shared expert is named in the handbook page's
   introduction; its weight is not given, 1 is taken).
+* Auxiliary router losses ("emerging-techniques-moe-training", section 3
+  Load Balancing): the load-balancing loss E * sum_e f_e P_e, with f_e the
+  share of the T*k routing slots that chose expert e and P_e the mean over
+  tokens of the softmax over all E logits, and the router z-loss, the mean
+  over tokens of logsumexp(l)^2. Readings: both read the router's raw logits
+  (gate bias included, aux-loss-free selection bias excluded) whatever the
+  scoring function; f_e counts the selection actually made, a piecewise
+  constant function of the logits, so it carries no gradient; an empty batch
+  (T = 0) gives 0 for both.
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, invariants, brute force and finite differences; the
@@ -373,10 +382,68 @@ def router_backward_dlogits(topk_w, d_topk_w, score, logits_sel=None):
     return s * (1.0 - s) / S * centred
 
 
+def _log_softmax_parts(logits):
+    """Per-token softmax over all experts and logsumexp (fp64), both with
+    the row maximum taken out before exponentiating."""
+    l = np.asarray(logits, dtype=np.float64)
+    m = l.max(axis=1, keepdims=True)
+    ex = np.exp(l - m)
+    s = ex.sum(axis=1, keepdims=True)
+    return ex / s, (m + np.log(s))[:, 0]
+
+
+def expert_fraction(topk_idx, E: int) -> np.ndarray:
+    """f_e: routing slots that chose expert e over all T*k slots (fp64)."""
+    idx = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    if idx.size == 0:
+        return np.zeros(E)
+    return np.bincount(idx, minlength=E)[:E].astype(np.float64) / idx.size
+
+
+def router_losses(logits, topk_idx, E: int):
+    """(aux, z) in fp64 ("emerging-techniques-moe-training", section 3 Load
+    Balancing):
+
+        aux = E * sum_e f_e * P_e,  P_e = mean_t softmax(l_t)_e
+        z   = mean_t logsumexp(l_t)^2
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    T = l.shape[0]
+    if T == 0:
+        return 0.0, 0.0
+    p, lse = _log_softmax_parts(l)
+    f = expert_fraction(topk_idx, E)
+    P = p.mean(axis=0)
+    aux = E * float((f * P).sum())
+    z = float((lse * lse).mean())
+    return aux, z
+
+
+def router_losses_dlogits(logits, topk_idx, E: int, coef_aux: float, coef_z: float):
+    """d(coef_aux * aux + coef_z * z) / d logits, [T,E] fp64.
+
+    With p = softmax(l_t), dP_e/dl_{t,j} = p_{t,e} (delta_ej - p_{t,j}) / T,
+    so the load-balancing term is (E/T) p_{t,j} (f_j - sum_e f_e p_{t,e});
+    d lse_t / d l_{t,j} = p_{t,j}, so the z term is (2/T) lse_t p_{t,j}.
+    f_e is held fixed (see the header).
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    T = l.shape[0]
+    if T == 0:
+        return np.zeros((0, E))
+    p, lse = _log_softmax_parts(l)
+    f = expert_fraction(topk_idx, E)
+    a = (p * f[None, :]).sum(axis=1, keepdims=True)
+    d_aux = (E / T) * p * (f[None, :] - a)
+    d_z = (2.0 / T) * lse[:, None] * p
+    return coef_aux * d_aux + coef_z * d_z
+
+
 def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
-             b1=None, b2=None, routing=None, experts=None):
-    """Gradients of L = sum(grad_out * out) for the routed layer (no shared
-    expert). Top-k indices carry no gradient.
+             b1=None, b2=None, routing=None, experts=None, coef_aux=0.0, coef_z=0.0):
+    """Gradients of L = sum(grad_out * out) + coef_aux * aux + coef_z * z
+    for the routed layer (no shared expert); aux and z as in
+    ``router_losses``. Top-k indices carry no gradient.
 
     Returns dx [T,h], d_topk_w [T,k], d_logits_sel [T,k], dw_gate [E,h],
     db_gate [E], and dicts dw1/dw2/db1/db2 keyed by expert (all experts, or
@@ -423,6 +490,8 @@ def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=N
     dl = router_backward_dlogits(topk_w, d_topk_w, score, logits_sel)
     dlogits = np.zeros((T, E), dtype=np.float64)
     np.put_along_axis(dlogits, topk_idx.astype(np.int64), dl, axis=1)
+    if coef_aux != 0.0 or coef_z != 0.0:
+        dlogits += router_losses_dlogits(routing["logits"], topk_idx, E, coef_aux, coef_z)
     wg = np.asarray(w_gate, dtype=np.float64)
     dw_gate = dlogits.T @ x64
     db_gate = dlogits.sum(axis=0)
@@ -434,8 +503,9 @@ def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=N
 # ----------------------------------------------------- fp64 forward for FD
 
 def loss_fp64(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
-              b1=None, b2=None, expect_idx=None):
-    """L = sum(grad_out * out) with every step, logits included, in fp64.
+              b1=None, b2=None, expect_idx=None, coef_aux=0.0, coef_z=0.0):
+    """L = sum(grad_out * out) + coef_aux * aux + coef_z * z with every
+    step, logits included, in fp64.
 
     Used only to check the backward by finite differences: the fp32 gate order
     would quantise small perturbations of the router weights. Selection uses
@@ -468,4 +538,8 @@ def loss_fp64(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=
         y, _ = expert_forward(x[tok], w1[e], w2[e], act,
                               None if b1 is None else b1[e], None if b2 is None else b2[e])
         np.add.at(out, tok, w[tok, slot][:, None] * y)
-    return float((np.asarray(grad_out, dtype=np.float64) * out).sum()), topk_idx, logits, w
+    L = float((np.asarray(grad_out, dtype=np.float64) * out).sum())
+    if coef_aux != 0.0 or coef_z != 0.0:
+        aux, z = router_losses(logits, topk_idx, E)
+        L += coef_aux * aux + coef_z * z
+    return L, topk_idx, logits, w

@@ -41,6 +41,7 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16-byte vector
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));  // 8-byte vector
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
@@ -58,8 +59,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Two values rounded to nearest even in one v_cvt_pk_bf16_f32 (lo in the
+// low half); NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    const f32x2_t f = {lo, hi};
+    const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
 }
 
 template <typename T> struct Elem;

@@ -314,7 +314,7 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
                             g[q] += bf16_to_f32(bias[f + q]);
                             u[q] += bf16_to_f32(bias[a.N_out + f + q]);
                         }
-                        hv[q] = silu_f(g[q]) * u[q];
+                        hv[q] = silu_fast(g[q]) * u[q];
                     }
                     uint2 o;
                     o.x = pack_bf16x2(hv[0], hv[1]);

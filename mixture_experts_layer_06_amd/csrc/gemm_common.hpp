@@ -194,14 +194,18 @@ __device__ __forceinline__ BalTile decode_tile_bal(const GGArgs &a, const int *s
     return ti;
 }
 
-// Raw buffer resource over [p, p + bytes) (reads past the end return zero).
-// p must be uniform across the wave.
+// Raw buffer resource over [p, p + bytes): reads past the end return zero,
+// writes past it are dropped; the bound applies to voffset + soffset. p and
+// bytes must be uniform across the wave.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes = 0x7fffffffu) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    // the size too must be provably uniform, or every buffer access gets a
+    // loop over the lanes' distinct descriptors
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
     return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo),
-                                             static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+                                             static_cast<short>(0), static_cast<int>(n), 0x00020000);
 }
 
 #define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
@@ -211,6 +215,14 @@ constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200, kSgVmemRea
 #define MOE_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+// g * sigmoid(g) with the hardware exp2 and reciprocal (about 2 ulp; the
+// result is rounded to bf16): six VALU operations instead of a library exp
+// and an IEEE divide in the GEMM epilogue. Saturates correctly: g -> -inf
+// gives exp2 -> inf, rcp -> 0, product -0; g -> +inf gives g.
+__device__ __forceinline__ float silu_fast(float g) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 __device__ __forceinline__ float gelu_erf_f(float a) {
     return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
 }

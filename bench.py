@@ -150,9 +150,13 @@ class ClockSampler:
         self.thread.join()
 
     def summary(self):
-        if not self.samples:
-            return None
-        v = np.asarray(self.samples)
+        # the metrics table is refreshed by the driver on its own schedule and
+        # often holds idle-state values during short bursts of work; readings
+        # below 500 MHz are not a loaded GPU's clock and are dropped
+        v = np.asarray([x for x in self.samples if x >= 500.0])
+        if v.size == 0:
+            return {"mhz_median": None, "samples": len(self.samples), "source": self.source,
+                    "note": "no plausible reading (all below 500 MHz)" if self.samples else "no reading"}
         return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
                 "samples": int(v.size), "source": self.source}
 
@@ -355,8 +359,9 @@ def main():
     call_flops = {"grouped_ffn": ffn_flops(cfg), "grouped_ffn_bwd": bwd_flops}
     dom = max(live, key=lambda n: live[n])
     rec = recorded_traffic(cfg.name) if dom == "grouped_ffn" else None
-    kernels = {"grouped_ffn": "grouped_gemm_bf16 SwiGLU launch + grouped_gemm_bf16 plain launch "
-                              "(one moe_grouped_ffn call)",
+    gk = "grouped_gemm_bf16" if cfg.dtype == "bf16" else "grouped_gemm_f32"
+    kernels = {"grouped_ffn": "%s %s launch + %s plain launch (one moe_grouped_ffn call)"
+                              % (gk, "SwiGLU" if cfg.act == "swiglu" else "GELU", gk),
                "grouped_ffn_bwd": "moe_grouped_ffn_bwd call (SwiGLU backward, data and weight "
                                   "gradient launches)"}
     out["roofline"] = {

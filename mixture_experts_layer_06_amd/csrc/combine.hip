@@ -11,51 +11,92 @@
 // and section 1.1 (MoE(x) = sum over the top-k of p_i E_i(x)). The shared
 // expert's output is added with weight 1.
 //
-// All three are HBM-bound row streams: one workgroup per token, 16-byte
-// accesses, fp32 accumulation in a fixed order (j ascending), one rounding
-// to the output type. Reductions use a fixed shuffle tree, so results are
+// All three are HBM-bound row streams (unpermute: one thread per 8-element
+// piece; the backward passes: one workgroup per token), 16-byte accesses,
+// fp32 accumulation in a fixed order (j ascending), one rounding to the
+// output type. Reductions use a fixed shuffle tree, so results are
 // deterministic.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
+// Streaming loads and stores of 8 elements (rows read or written once):
+// non-temporal, so they do not displace reusable lines from the caches.
+__device__ __forceinline__ void load8_nt(const bf16_t *p, float *v) {
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        v[2 * c] = bf16lo(q[c]);
+        v[2 * c + 1] = bf16hi(q[c]);
+    }
+}
+__device__ __forceinline__ void load8_nt(const float *p, float *v) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 4));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        v[c] = __uint_as_float(a[c]);
+        v[4 + c] = __uint_as_float(b[c]);
+    }
+}
+__device__ __forceinline__ void store8_nt(bf16_t *p, const float *v) {
+    u32x4 q;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void store8_nt(float *p, const float *v) {
+    __builtin_nontemporal_store(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                      __float_as_uint(v[3])},
+                                reinterpret_cast<u32x4 *>(p));
+    __builtin_nontemporal_store(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                      __float_as_uint(v[7])},
+                                reinterpret_cast<u32x4 *>(p + 4));
+}
+
+// One thread per 8-element piece of an output row (a flat grid over
+// T x h/8 pieces): the k source pieces are all loaded before the fixed-order
+// weighted sum, so each thread keeps k loads in flight.
 template <typename TE>
 __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y, int h, int k,
                                                         const int32_t *__restrict__ row_of,
                                                         const float *__restrict__ topk_w,
                                                         const TE *__restrict__ y_sh,
-                                                        TE *__restrict__ out) {
-    const int t = blockIdx.x;
+                                                        TE *__restrict__ out, int64_t npieces) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= npieces) return;
+    const int nv = h >> 3;
+    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
     int rows[8];
     float w[8];
+    const int64_t P = npieces / nv * k;   // rows of y
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        if (rows[j] >= P) rows[j] = -1;
         w[j] = j < k ? topk_w[static_cast<int64_t>(t) * k + j] : 0.0f;
     }
-    const int nv = h / 8;
-    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        float acc[8];
+    float yv[8][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < 8; ++j)
+        if (rows[j] >= 0) load8_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv[j]);
+    float acc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (rows[j] >= 0) {
-                float yv[8];
-                load8(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[i], acc[i]);
-            }
+    for (int j = 0; j < 8; ++j)
+        if (rows[j] >= 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[j][i], acc[i]);
         }
-        if (y_sh) {
-            float sv[8];
-            load8(y_sh + static_cast<int64_t>(t) * h + 8 * v, sv);
+    if (y_sh) {
+        float sv[8];
+        load8_nt(y_sh + static_cast<int64_t>(t) * h + 8 * v, sv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += sv[i];
-        }
-        store8(out + static_cast<int64_t>(t) * h + 8 * v, acc);
+        for (int i = 0; i < 8; ++i) acc[i] += sv[i];
     }
+    store8_nt(out + static_cast<int64_t>(t) * h + 8 * v, acc);
 }
 
 template <typename TE>
@@ -70,6 +111,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        if (rows[j] >= static_cast<int64_t>(gridDim.x) * k) rows[j] = -1;   // rows of y: T k
         w[j] = j < k ? topk_w[static_cast<int64_t>(t) * k + j] : 0.0f;
         dot[j] = 0.0f;
     }
@@ -120,6 +162,7 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        if (rows[j] >= static_cast<int64_t>(gridDim.x) * k) rows[j] = -1;   // rows of grad_x_perm: T k
         ex[j] = -1;
         dl[j] = 0.0f;
         if (gl && j < k) {
@@ -182,15 +225,16 @@ extern "C" int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int
                   "moe_unpermute: pointers must be 16-byte aligned");
     if (T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
-    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    const int64_t npieces = T * (h / 8);
+    const dim3 grid(static_cast<unsigned>((npieces + 255) / 256)), block(256);
     if (dtype == MOE_DTYPE_BF16)
         hipLaunchKernelGGL(unpermute_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t *>(y),
                            static_cast<int>(h), k, row_of, topk_w,
-                           static_cast<const bf16_t *>(y_sh), static_cast<bf16_t *>(out));
+                           static_cast<const bf16_t *>(y_sh), static_cast<bf16_t *>(out), npieces);
     else
         hipLaunchKernelGGL(unpermute_kernel<float>, grid, block, 0, s, static_cast<const float *>(y),
                            static_cast<int>(h), k, row_of, topk_w, static_cast<const float *>(y_sh),
-                           static_cast<float *>(out));
+                           static_cast<float *>(out), npieces);
     return check_launch("moe_unpermute");
 }
 

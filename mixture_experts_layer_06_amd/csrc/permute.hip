@@ -108,29 +108,27 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ t
 }
 
 // Block of 256 threads per token row; each thread moves 16-byte pieces.
+// One thread per 16-byte piece of a token row (a flat grid over T x pieces):
+// the piece is read once and stored to the token's k rows of x_perm (rows
+// outside [0, T k) are skipped).
 template <typename TE>
-__global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x, int T,
-                                                        int h, int k,
+__global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x, int h, int k,
                                                         const int32_t *__restrict__ row_of,
-                                                        TE *__restrict__ x_perm) {
+                                                        TE *__restrict__ x_perm, int64_t npieces) {
     constexpr int kVec = 16 / sizeof(TE);
-    const int t = blockIdx.x;
-    int rows[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * h);
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= npieces) return;
     const int nv = h / kVec;
-    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        const u32x4 d = __builtin_nontemporal_load(src + v);
+    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * h) + v);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (rows[j] >= 0) {
-                u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(rows[j]) * h);
-                __builtin_nontemporal_store(d, dst + v);
-            }
+    for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+            const int r = row_of[static_cast<int64_t>(t) * k + j];
+            if (r >= 0 && static_cast<int64_t>(r) < npieces / nv * k)
+                __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(r) * h) + v);
         }
     }
-    (void)T;
 }
 
 }  // namespace
@@ -181,13 +179,13 @@ extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E
                            k, blockbase, P, row_of, sorted_token);
     if (x_perm && T > 0) {
         if (dtype == MOE_DTYPE_BF16)
-            hipLaunchKernelGGL(copy_rows_kernel<bf16_t>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
-                               s, static_cast<const bf16_t *>(x), static_cast<int>(T),
-                               static_cast<int>(h), k, row_of, static_cast<bf16_t *>(x_perm));
+            hipLaunchKernelGGL(copy_rows_kernel<bf16_t>, dim3(static_cast<unsigned>((T * (h / 8) + 255) / 256)),
+                               dim3(256), 0, s, static_cast<const bf16_t *>(x), static_cast<int>(h), k, row_of,
+                               static_cast<bf16_t *>(x_perm), T * (h / 8));
         else
-            hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
-                               s, static_cast<const float *>(x), static_cast<int>(T),
-                               static_cast<int>(h), k, row_of, static_cast<float *>(x_perm));
+            hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(static_cast<unsigned>((T * (h / 4) + 255) / 256)),
+                               dim3(256), 0, s, static_cast<const float *>(x), static_cast<int>(h), k, row_of,
+                               static_cast<float *>(x_perm), T * (h / 4));
     }
     return check_launch("moe_permute");
 }

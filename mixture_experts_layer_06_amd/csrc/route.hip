@@ -167,15 +167,29 @@ __device__ __forceinline__ void gate_item(const TIn *__restrict__ xrow, const TI
 
 // Work items of a block: (token tt in [0,8), expert group eg); lane group lg
 // of the block (32 per block, 8 per wave) takes items lg, lg + 32, ...
-template <typename TIn, int EPG, int U>
+// WLDS (few experts, E*h*sizeof(TIn) <= 64 KB): the block first copies the
+// whole gate matrix into LDS (dynamic shared memory) and the items read their
+// gate rows from there; with EPG = ceil(E/4) the 32 items of a block cover 8
+// tokens, so each token row of x is read from memory ceil(E/EPG) <= 4 times
+// instead of E times. MAXE bounds E (LDS arrays).
+template <typename TIn, int EPG, int U, bool WLDS = false, int MAXE = kMaxE>
 __global__ __launch_bounds__(256) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wg, const float *__restrict__ bg,
     const float *__restrict__ sel_bias, int T, int h, int E, int k, int sigmoid,
     float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     uint8_t *__restrict__ rmap, int32_t *__restrict__ counts) {
-    __shared__ float s_logit[kTokPerBlock][kMaxE];
-    __shared__ float s_key[kTokPerBlock][kMaxE];
-    __shared__ int s_cnt[kMaxE];
+    __shared__ float s_logit[kTokPerBlock][MAXE];
+    __shared__ float s_key[kTokPerBlock][MAXE];
+    __shared__ int s_cnt[MAXE];
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_wdyn[];
+
+    if (WLDS) {
+        const int n16 = static_cast<int>(static_cast<int64_t>(E) * h * sizeof(TIn) / 16);
+        for (int i = threadIdx.x; i < n16; i += blockDim.x)
+            reinterpret_cast<u32x4 *>(s_wdyn)[i] = reinterpret_cast<const u32x4 *>(wg)[i];
+        __syncthreads();
+        wg = reinterpret_cast<const TIn *>(s_wdyn);
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -639,6 +653,32 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
     }
     const dim3 grid(static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock));
     const dim3 block(256);
+    const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    const size_t wbytes = static_cast<size_t>(E) * static_cast<size_t>(h) * es;
+    if (E <= 16 && wbytes <= 65536) {
+        // few experts: the gate matrix lives in LDS, each token row is read
+        // ceil(E / EPG) times
+#define MOE_ROUTE_WLDS(TIN, EPG_, U_)                                                                   \
+    do {                                                                                              \
+        auto kfn = &route_kernel<TIN, EPG_, U_, true, 16>;                                            \
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),                                 \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(wbytes)); \
+        hipLaunchKernelGGL(kfn, grid, block, wbytes, s, static_cast<const TIN *>(x),                  \
+                           static_cast<const TIN *>(w_gate), b_gate, sel_bias, TT, hh, E, k, sig, logits, \
+                           topk_idx, topk_w, routing_map, counts);                                    \
+    } while (0)
+        if (dtype == MOE_DTYPE_BF16) {
+            if (E <= 4) MOE_ROUTE_WLDS(bf16_t, 1, 8);
+            else if (E <= 8) MOE_ROUTE_WLDS(bf16_t, 2, 8);
+            else MOE_ROUTE_WLDS(bf16_t, 4, 4);
+        } else {
+            if (E <= 4) MOE_ROUTE_WLDS(float, 1, 4);
+            else if (E <= 8) MOE_ROUTE_WLDS(float, 2, 4);
+            else MOE_ROUTE_WLDS(float, 4, 2);
+        }
+#undef MOE_ROUTE_WLDS
+        return check_launch("moe_route");
+    }
     if (dtype == MOE_DTYPE_BF16) {
         const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
         if (E <= 16)

@@ -11,10 +11,10 @@
 // and section 1.1 (MoE(x) = sum over the top-k of p_i E_i(x)). The shared
 // expert's output is added with weight 1.
 //
-// All three are HBM-bound row streams (unpermute: one thread per 8-element
-// piece; the backward passes: one workgroup per token), 16-byte accesses,
-// fp32 accumulation in a fixed order (j ascending), one rounding to the
-// output type. Reductions use a fixed shuffle tree, so results are
+// All three are HBM-bound row streams (one thread per 8-element piece;
+// unpermute_bwd: one workgroup per token for its dot products), 16-byte
+// accesses, fp32 accumulation in a fixed order (j ascending), one rounding to
+// the output type. Reductions use a fixed shuffle tree, so results are
 // deterministic.
 #include "common.hpp"
 
@@ -99,12 +99,17 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
     store8_nt(out + static_cast<int64_t>(t) * h + 8 * v, acc);
 }
 
+// One block per token with one thread per 8-element piece (blockDim =
+// h/8 rounded up to a wave, at most 1024; a thread takes pieces v, v +
+// blockDim, ...): the piece of grad_out and the k pieces of y are loaded
+// before use. The dot products are reduced in a fixed order: a shuffle tree
+// in each wave, then the waves in order.
 template <typename TE>
-__global__ __launch_bounds__(256) void unpermute_bwd_kernel(
+__global__ __launch_bounds__(1024) void unpermute_bwd_kernel(
     const TE *__restrict__ gout, const TE *__restrict__ y, int h, int k,
     const int32_t *__restrict__ row_of, const float *__restrict__ topk_w, TE *__restrict__ gy,
     float *__restrict__ gw) {
-    __shared__ float red[8][4];
+    __shared__ float red[8][16];
     const int t = blockIdx.x;
     int rows[8];
     float w[8], dot[8];
@@ -117,52 +122,59 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(
     }
     const int nv = h / 8;
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        float g[8];
-        load8(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+        float g[8], yv[8][8];
+        load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (rows[j] >= 0) load8_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv[j]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if (rows[j] >= 0) {
-                float yv[8], d[8];
-                load8(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv);
+                float d[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    dot[j] = fmaf(g[i], yv[i], dot[j]);
+                    dot[j] = fmaf(g[i], yv[j][i], dot[j]);
                     d[i] = w[j] * g[i];
                 }
-                store8(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
+                store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
             }
         }
     }
-    // fixed-order reduction: shuffle tree in each wave, then waves 0..3
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        float s = dot[j];
+        float sdot = dot[j];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off);
-        if (lane == 0) red[j][wave] = s;
+        for (int off = 32; off > 0; off >>= 1) sdot += __shfl_down(sdot, off);
+        if (lane == 0) red[j][wave] = sdot;
     }
     __syncthreads();
     if (threadIdx.x < k) {
         const int j = threadIdx.x;
-        float s = red[j][0];
-        for (int wv = 1; wv < static_cast<int>(blockDim.x >> 6); ++wv) s += red[j][wv];
-        gw[static_cast<int64_t>(t) * k + j] = s;
+        float sdot = red[j][0];
+        for (int wv = 1; wv < nw; ++wv) sdot += red[j][wv];
+        gw[static_cast<int64_t>(t) * k + j] = sdot;
     }
 }
 
+// One thread per 8-element piece (flat grid over T x h/8): the k pieces of
+// grad_x_perm and the router term's gate pieces are loaded before use.
 template <typename TE>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(
     const TE *__restrict__ gxp, int h, int k, const int32_t *__restrict__ row_of,
     const float *__restrict__ gl, const int32_t *__restrict__ topk_idx,
-    const TE *__restrict__ wg, int E, TE *__restrict__ gx) {
-    const int t = blockIdx.x;
+    const TE *__restrict__ wg, int E, TE *__restrict__ gx, int64_t npieces) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= npieces) return;
+    const int nv = h >> 3;
+    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    const int64_t P = npieces / nv * k;   // rows of grad_x_perm
     int rows[8], ex[8];
     float dl[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
-        if (rows[j] >= static_cast<int64_t>(gridDim.x) * k) rows[j] = -1;   // rows of grad_x_perm: T k
+        if (rows[j] >= P) rows[j] = -1;
         ex[j] = -1;
         dl[j] = 0.0f;
         if (gl && j < k) {
@@ -171,31 +183,29 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
             dl[j] = gl[static_cast<int64_t>(t) * k + j];
         }
     }
-    const int nv = h / 8;
-    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        float acc[8];
+    float d[8][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < 8; ++j)
+        if (rows[j] >= 0) load8_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
+    float acc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (rows[j] >= 0) {
-                float d[8];
-                load8(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += d[i];
-            }
+    for (int j = 0; j < 8; ++j)
+        if (rows[j] >= 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += d[j][i];
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (ex[j] >= 0) {
-                float wv[8];
-                load8(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wv);
+    for (int j = 0; j < 8; ++j) {
+        if (ex[j] >= 0) {
+            float wv[8];
+            load8(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wv);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], wv[i], acc[i]);
-            }
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], wv[i], acc[i]);
         }
-        store8(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
     }
+    store8_nt(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
 }
 
 int check_common(const char *fn, int dtype, int64_t T, int64_t h, int k) {
@@ -250,7 +260,9 @@ extern "C" int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype,
                   "moe_unpermute_bwd: pointers must be 16-byte aligned");
     if (T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
-    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    int bs = static_cast<int>(((h / 8 + 63) / 64) * 64);
+    if (bs > 1024) bs = 1024;
+    const dim3 grid(static_cast<unsigned>(T)), block(static_cast<unsigned>(bs));
     if (dtype == MOE_DTYPE_BF16)
         hipLaunchKernelGGL(unpermute_bwd_kernel<bf16_t>, grid, block, 0, s,
                            static_cast<const bf16_t *>(grad_out), static_cast<const bf16_t *>(y),
@@ -279,16 +291,17 @@ extern "C" int moe_permute_bwd(const void *grad_x_perm, int dtype, int64_t T, in
                   MOE_ERR_INVALID_ARG, "moe_permute_bwd: pointers must be 16-byte aligned");
     if (T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
-    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    const int64_t npieces = T * (h / 8);
+    const dim3 grid(static_cast<unsigned>((npieces + 255) / 256)), block(256);
     if (dtype == MOE_DTYPE_BF16)
         hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, grid, block, 0, s,
                            static_cast<const bf16_t *>(grad_x_perm), static_cast<int>(h), k, row_of,
                            grad_logits_sel, topk_idx, static_cast<const bf16_t *>(w_gate), E,
-                           static_cast<bf16_t *>(grad_x));
+                           static_cast<bf16_t *>(grad_x), npieces);
     else
         hipLaunchKernelGGL(permute_bwd_kernel<float>, grid, block, 0, s,
                            static_cast<const float *>(grad_x_perm), static_cast<int>(h), k, row_of,
                            grad_logits_sel, topk_idx, static_cast<const float *>(w_gate), E,
-                           static_cast<float *>(grad_x));
+                           static_cast<float *>(grad_x), npieces);
     return check_launch("moe_permute_bwd");
 }

@@ -165,6 +165,43 @@ __device__ __forceinline__ void gate_item(const TIn *__restrict__ xrow, const TI
     }
 }
 
+// gate_item with the gate matrix in LDS: U chunks of x are loaded before
+// use (the only global loads), the gate pieces are read from LDS at their
+// point of use. Same fma order as gate_item.
+template <typename TIn, int EPG, int U>
+__device__ __forceinline__ void gate_item_lds(const TIn *__restrict__ xrow, const TIn *wl, int h, int E, int e0,
+                                              int q, float (*acc)[8]) {
+#pragma unroll
+    for (int ee = 0; ee < EPG; ++ee)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc[ee][s] = 0.0f;
+    int woff[EPG];
+#pragma unroll
+    for (int ee = 0; ee < EPG; ++ee) {
+        const int e = e0 + ee < E ? e0 + ee : E - 1;
+        woff[ee] = e * h + 8 * q;
+    }
+    const int nchunk = h >> 6;
+    for (int c = 0; c < nchunk; c += U) {
+        Piece<TIn> xp[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c + u < nchunk) xp[u].load(xrow + 64 * (c + u));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c + u < nchunk) {
+#pragma unroll
+                for (int ee = 0; ee < EPG; ++ee) {
+                    Piece<TIn> wp;
+                    wp.load(wl + woff[ee] + 64 * (c + u));
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) acc[ee][s] = fmaf(xp[u].at(s), wp.at(s), acc[ee][s]);
+                }
+            }
+        }
+    }
+}
+
 // Work items of a block: (token tt in [0,8), expert group eg); lane group lg
 // of the block (32 per block, 8 per wave) takes items lg, lg + 32, ...
 // WLDS (few experts, E*h*sizeof(TIn) <= 64 KB): the block first copies the
@@ -182,11 +219,28 @@ __global__ __launch_bounds__(256) void route_kernel(
     __shared__ float s_key[kTokPerBlock][MAXE];
     __shared__ int s_cnt[MAXE];
     extern __shared__ __attribute__((aligned(16))) unsigned char s_wdyn[];
+    // few experts (MAXE <= 16): the block's counts go to `counts` with one
+    // atomic per expert at the end; otherwise count_kernel runs afterwards
+    constexpr bool kCountHere = MAXE <= 16;
+    if (kCountHere)
+        for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
 
     if (WLDS) {
+        // 16 pieces of 16 bytes per thread in flight at once (64 KB per pass)
         const int n16 = static_cast<int>(static_cast<int64_t>(E) * h * sizeof(TIn) / 16);
-        for (int i = threadIdx.x; i < n16; i += blockDim.x)
-            reinterpret_cast<u32x4 *>(s_wdyn)[i] = reinterpret_cast<const u32x4 *>(wg)[i];
+        for (int base = 0; base < n16; base += 16 * 256) {
+            u32x4 tmp[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int i = base + u * 256 + static_cast<int>(threadIdx.x);
+                if (i < n16) tmp[u] = reinterpret_cast<const u32x4 *>(wg)[i];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int i = base + u * 256 + static_cast<int>(threadIdx.x);
+                if (i < n16) reinterpret_cast<u32x4 *>(s_wdyn)[i] = tmp[u];
+            }
+        }
         __syncthreads();
         wg = reinterpret_cast<const TIn *>(s_wdyn);
     }
@@ -198,7 +252,6 @@ __global__ __launch_bounds__(256) void route_kernel(
     const int lg = wave * 8 + g;
     const int t0 = blockIdx.x * kTokPerBlock;
 
-    for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
 
     const int ngroups = (E + EPG - 1) / EPG;
     const int nitems = kTokPerBlock * ngroups;
@@ -208,7 +261,8 @@ __global__ __launch_bounds__(256) void route_kernel(
         int t = t0 + tt;
         t = t < T ? t : T - 1;   // rows past T are read, never stored
         float acc[EPG][8];
-        gate_item<TIn, EPG, U>(x + static_cast<int64_t>(t) * h + 8 * q, wg, h, E, e0, q, acc);
+        if (WLDS) gate_item_lds<TIn, EPG, U>(x + static_cast<int64_t>(t) * h + 8 * q, wg, h, E, e0, q, acc);
+        else gate_item<TIn, EPG, U>(x + static_cast<int64_t>(t) * h + 8 * q, wg, h, E, e0, q, acc);
 #pragma unroll
         for (int ee = 0; ee < EPG; ++ee) {
             const float l = gate_tree(acc[ee]);
@@ -274,7 +328,7 @@ __global__ __launch_bounds__(256) void route_kernel(
                 if (j < k) {
                     topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
                     topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
-                    if (sel_e[j] >= 0 && sel_e[j] < E) atomicAdd(&s_cnt[sel_e[j]], 1);
+                    if (kCountHere && sel_e[j] >= 0 && sel_e[j] < E) atomicAdd(&s_cnt[sel_e[j]], 1);
                 }
             }
         }
@@ -288,11 +342,56 @@ __global__ __launch_bounds__(256) void route_kernel(
             }
         }
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
+    if (kCountHere) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += blockDim.x)
+            if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
+    }
 }
 
+
+// Tokens per expert from topk_idx: a histogram in LDS per block of
+// kCountChunk entries, then (one block) the bins written directly or (more
+// blocks) added into counts, which the caller has zeroed. Per-token global
+// atomics into E adjacent counters would serialise in a few L2 lines.
+constexpr int kCountChunk = 65536;
+__global__ __launch_bounds__(1024) void count_kernel(const int32_t *__restrict__ topk_idx, int64_t n, int E,
+                                                     int32_t *__restrict__ counts) {
+    __shared__ int s_hist[16][kMaxE];   // one sub-histogram per wave: fewer colliding LDS atomics
+    const int wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 16 * kMaxE; i += blockDim.x) s_hist[i / kMaxE][i % kMaxE] = 0;
+    __syncthreads();
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * kCountChunk;
+    const int64_t hi = lo + kCountChunk < n ? lo + kCountChunk : n;
+    // 16 loads of 4 entries per thread, all in flight (kCountChunk = 1024 *
+    // 64); the chunk start is a multiple of 4 entries, so 16-byte loads are
+    // aligned when topk_idx is
+    int v[16][4];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int64_t i = lo + 4 * (static_cast<int64_t>(u) * blockDim.x + threadIdx.x);
+        if (i + 4 <= hi) {
+            const int4 q = *reinterpret_cast<const int4 *>(topk_idx + i);
+            v[u][0] = q.x; v[u][1] = q.y; v[u][2] = q.z; v[u][3] = q.w;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[u][r] = i + r < hi ? topk_idx[i + r] : -1;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (v[u][r] >= 0 && v[u][r] < E) atomicAdd(&s_hist[wave][v[u][r]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) c += s_hist[w][e];
+        if (gridDim.x == 1) counts[e] = c;
+        else if (c) atomicAdd(&counts[e], c);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Fast path with the same results (many experts, bf16, no logits output).
@@ -334,66 +433,49 @@ __global__ __launch_bounds__(64) void row_norm_kernel(const bf16_t *__restrict__
     if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(s);
 }
 
-// Fixed-order logit of one (token, expert) pair by a group of 4 lanes: lane
-// q owns residues 16q..16q+15 of every 64-chunk (fma chains over ascending
-// chunks), then the halving tree: s=32 -> lane q+2, s=16 -> lane q+1, then
-// s=8,4,2,1 inside lane 0. The same additions as route_kernel's, so the
-// same bits. xs: the token's row in LDS; wrow: the expert's gate row.
-__device__ __forceinline__ float gate_dot4(const bf16_t *xs, const bf16_t *__restrict__ wrow, int h, int q) {
-    float acc[16];
+// Fixed-order logits of two (token, expert) pairs by a whole wave: lane r
+// owns residue r, i.e. the fma chain of partial sum r over ascending chunks
+// (x[64 c + r] from the token's row, read from memory: the norm pass just
+// brought it into the caches), then the halving tree s = 32..1
+// across lanes (part[j] += part[j+s] is lane j adding lane j+s). The same
+// operations as route_kernel's, so the same bits; the result is in lane 0.
+// Two experts at a time, 16 chunks per step: 32 gate loads in flight.
+__device__ __forceinline__ void gate_dot_pair(const bf16_t *__restrict__ xl, const bf16_t *__restrict__ w0,
+                                              const bf16_t *__restrict__ w1, int nch, int lane, float &l0,
+                                              float &l1) {
+    float a0 = 0.0f, a1 = 0.0f;
+    int c0 = 0;
+    for (; c0 + 16 <= nch; c0 += 16) {
+        bf16_t v0[16], v1[16], xv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    const int nchunk = h >> 6;
-    constexpr int U = 8;
-    int c = 0;
-    for (; c + U <= nchunk; c += U) {
-        u32x4 wv[U][2];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            wv[u][0] = *reinterpret_cast<const u32x4 *>(wrow + 64 * (c + u) + 16 * q);
-            wv[u][1] = *reinterpret_cast<const u32x4 *>(wrow + 64 * (c + u) + 16 * q + 8);
+        for (int c = 0; c < 16; ++c) {
+            v0[c] = w0[64 * (c0 + c) + lane];
+            v1[c] = w1[64 * (c0 + c) + lane];
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xs + 64 * (c + u) + 16 * q);
-            const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xs + 64 * (c + u) + 16 * q + 8);
+        for (int c = 0; c < 16; ++c) xv[c] = xl[64 * (c0 + c) + lane];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                acc[2 * d] = fmaf(bf16lo(x0[d]), bf16lo(wv[u][0][d]), acc[2 * d]);
-                acc[2 * d + 1] = fmaf(bf16hi(x0[d]), bf16hi(wv[u][0][d]), acc[2 * d + 1]);
-                acc[8 + 2 * d] = fmaf(bf16lo(x1[d]), bf16lo(wv[u][1][d]), acc[8 + 2 * d]);
-                acc[8 + 2 * d + 1] = fmaf(bf16hi(x1[d]), bf16hi(wv[u][1][d]), acc[8 + 2 * d + 1]);
-            }
+        for (int c = 0; c < 16; ++c) {
+            const float xf = bf16_to_f32(xv[c]);
+            a0 = fmaf(xf, bf16_to_f32(v0[c]), a0);
+            a1 = fmaf(xf, bf16_to_f32(v1[c]), a1);
         }
     }
-    for (; c < nchunk; ++c) {
-        const u32x4 w0 = *reinterpret_cast<const u32x4 *>(wrow + 64 * c + 16 * q);
-        const u32x4 w1 = *reinterpret_cast<const u32x4 *>(wrow + 64 * c + 16 * q + 8);
-        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xs + 64 * c + 16 * q);
-        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xs + 64 * c + 16 * q + 8);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            acc[2 * d] = fmaf(bf16lo(x0[d]), bf16lo(w0[d]), acc[2 * d]);
-            acc[2 * d + 1] = fmaf(bf16hi(x0[d]), bf16hi(w0[d]), acc[2 * d + 1]);
-            acc[8 + 2 * d] = fmaf(bf16lo(x1[d]), bf16lo(w1[d]), acc[8 + 2 * d]);
-            acc[8 + 2 * d + 1] = fmaf(bf16hi(x1[d]), bf16hi(w1[d]), acc[8 + 2 * d + 1]);
-        }
+    for (; c0 < nch; ++c0) {
+        const float xf = bf16_to_f32(xl[64 * c0 + lane]);
+        a0 = fmaf(xf, bf16_to_f32(w0[64 * c0 + lane]), a0);
+        a1 = fmaf(xf, bf16_to_f32(w1[64 * c0 + lane]), a1);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = acc[i] + __shfl_down(acc[i], 2);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = acc[i] + __shfl_down(acc[i], 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + acc[i + 8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = acc[i] + acc[i + 4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] = acc[i] + acc[i + 2];
-    return acc[0] + acc[1];
+    for (int off = 32; off > 0; off >>= 1) {
+        a0 = a0 + __shfl_down(a0, off);
+        a1 = a1 + __shfl_down(a1, off);
+    }
+    l0 = a0;
+    l1 = a1;
 }
 
-// One wave per token (4 per block). Lane l holds experts l + 64 m. The
-// token's row is copied to LDS (dynamic: 4 h bf16 per block) once.
+// One wave per token (4 per block). Lane l holds experts l + 64 m.
 template <int SIGMOID>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ wg, const float *__restrict__ bg,
@@ -404,18 +486,15 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     __shared__ float s_cl[4][kMaxE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
-    extern __shared__ __attribute__((aligned(16))) bf16_t s_xrows[];
     if (t >= T) return;   // no block-wide barrier below
     const bf16_t *xrow = x + static_cast<int64_t>(t) * h;
-    bf16_t *xl = s_xrows + static_cast<int64_t>(wave) * h;
+    const int nch = h >> 6;
 
-    // the row to LDS, and |x_t|_2 (fp32; its rounding is far inside the
-    // factor-2 margins)
+    // |x_t|_2 (fp32; its rounding is far inside the factor-2 margins)
     float xs = 0.0f;
 #pragma unroll 4
     for (int i = 8 * lane; i < h; i += 8 * 64) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(xrow + i);
-        *reinterpret_cast<u32x4 *>(xl + i) = v;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float a = bf16lo(v[c]), b = bf16hi(v[c]);
@@ -495,29 +574,30 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-    // exact logits of the candidates, 16 at a time (lane group g, lane q)
-    const int g = lane >> 2, q = lane & 3;
-    for (int c0 = 0; c0 < nc; c0 += 16) {
-        const int ci = c0 + g;
-        if (ci < nc) {
-            const int e = s_cand[wave][ci];
-            const float l = gate_dot4(xl, wg + static_cast<int64_t>(e) * h, h, q);
-            if (q == 0) s_cl[wave][ci] = bg ? l + bg[e] : l;
+    // exact logits of the candidates, two at a time over the whole wave
+    for (int ci = 0; ci < nc; ci += 2) {
+        const int e0 = s_cand[wave][ci];
+        const int e1 = ci + 1 < nc ? s_cand[wave][ci + 1] : e0;
+        float l0, l1;
+        gate_dot_pair(xrow, wg + static_cast<int64_t>(e0) * h, wg + static_cast<int64_t>(e1) * h, nch, lane, l0, l1);
+        if (lane == 0) {
+            s_cl[wave][ci] = bg ? l0 + bg[e0] : l0;
+            if (ci + 1 < nc) s_cl[wave][ci + 1] = bg ? l1 + bg[e1] : l1;
         }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-    // exact top-k among the candidates (lane-strided), as route_kernel
+    // exact top-k among the candidates (lane-strided), as route_kernel; the
+    // winner's logit travels with its key and index through the reduction
     float sel_l[8];
     int sel_e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) { sel_l[j] = 0.0f; sel_e[j] = 0; }
     uint32_t removed = 0;   // bit m: candidate lane + 64 m taken
     for (int j = 0; j < k; ++j) {
-        float bk = 0.0f;
-        int bi = 0x7fffffff;
-        bool have = false;
+        float bk = -INFINITY, bl = 0.0f;
+        int bi = 0x7fffffff, bm = -1;
         for (int m = 0; m < M; ++m) {
             const int ci = lane + 64 * m;
             if (ci >= nc || ((removed >> m) & 1u)) continue;
@@ -530,25 +610,17 @@ __global__ __launch_bounds__(256) void route_select_kernel(
             }
             if (key != key) key = -INFINITY;
             key = key + 0.0f;
-            if (!have || precedes(key, e, bk, bi)) { bk = key; bi = e; have = true; }
+            if (bm < 0 || precedes(key, e, bk, bi)) { bk = key; bi = e; bl = l; bm = m; }
         }
-        if (!have) { bk = -INFINITY; bi = 0x7fffffff; }
-        int bci = have ? 0 : -1;   // candidate slot of this lane's best (recomputed below)
-        (void)bci;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             const float ok = __shfl_xor(bk, off);
             const int oi = __shfl_xor(bi, off);
-            if (precedes(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+            const float ol = __shfl_xor(bl, off);
+            if (precedes(ok, oi, bk, bi)) { bk = ok; bi = oi; bl = ol; }
         }
-        // mark the winner's candidate slot and fetch its logit
-        for (int m = 0; m < M; ++m) {
-            const int ci = lane + 64 * m;
-            if (ci < nc && s_cand[wave][ci] == bi) removed |= 1u << m;
-        }
-        float bl = 0.0f;
-        for (int ci = 0; ci < nc; ++ci)
-            if (s_cand[wave][ci] == bi) bl = s_cl[wave][ci];
+        // the lane that held the winner marks its slot
+        if (bm >= 0 && s_cand[wave][lane + 64 * bm] == bi) removed |= 1u << bm;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
             if (jj == j) { sel_e[jj] = bi; sel_l[jj] = bl; }
@@ -561,7 +633,6 @@ __global__ __launch_bounds__(256) void route_select_kernel(
             if (j < k) {
                 topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
                 topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
-                if (sel_e[j] >= 0 && sel_e[j] < E) atomicAdd(&counts[sel_e[j]], 1);
             }
         }
     }
@@ -614,13 +685,25 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
                   "moe_route: T*k must be < 2^31");
     MOE_CHECK_ARG(sel_bias == nullptr || score == MOE_SCORE_SIGMOID, MOE_ERR_INVALID_ARG,
                   "moe_route: sel_bias applies to sigmoid scoring only");
-    MOE_CHECK_ARG(aligned16(x) && aligned16(w_gate), MOE_ERR_INVALID_ARG,
-                  "moe_route: x and w_gate must be 16-byte aligned");
+    MOE_CHECK_ARG(aligned16(x) && aligned16(w_gate) && aligned16(topk_idx), MOE_ERR_INVALID_ARG,
+                  "moe_route: x, w_gate and topk_idx must be 16-byte aligned");
     MOE_CHECK_ARG(workspace_bytes == 0 || workspace, MOE_ERR_INVALID_ARG,
                   "moe_route: workspace_bytes > 0 with a null workspace");
     hipStream_t s = as_stream(stream);
-    launch_fill<int32_t>(counts, E, 0, s);
+    const int64_t npairs = T * k;
+    const unsigned count_blocks = static_cast<unsigned>((npairs + kCountChunk - 1) / kCountChunk);
+    const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    const size_t wbytes = static_cast<size_t>(E) * static_cast<size_t>(h) * es;
+    const bool few = E <= 16 && wbytes <= 65536;   // route_kernel with the gate in LDS; counts in-kernel
+    if (T == 0 || few || count_blocks > 1) launch_fill<int32_t>(counts, E, 0, s);
     if (T == 0) return check_launch("moe_route fill");
+    // the histogram of the selections, after whichever routing kernel ran
+    auto count = [&](const char *what) {
+        const int st = check_launch(what);
+        if (st != MOE_OK) return st;
+        hipLaunchKernelGGL(count_kernel, dim3(count_blocks), dim3(1024), 0, s, topk_idx, npairs, E, counts);
+        return check_launch("moe_route counts");
+    };
     const int sig = score == MOE_SCORE_SIGMOID;
     const int hh = static_cast<int>(h), TT = static_cast<int>(T);
     if (dtype == MOE_DTYPE_BF16 && logits == nullptr && E >= 32 && workspace && h <= 8192 &&
@@ -636,26 +719,17 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
         // interval half-width per unit |x||w|: 2 * (2 (h/16 + 16) + 2 (h/64 + 6)) u
         const float cb = static_cast<float>(2.0 * (2.0 * (h / 16 + 16) + 2.0 * (h / 64 + 6)) * 0x1p-24 * 1.001);
         const dim3 g2(static_cast<unsigned>((T + 3) / 4));
-        const size_t lds = 4 * static_cast<size_t>(h) * sizeof(bf16_t);   // <= 64 KB
         if (sig)
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&route_select_kernel<1>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        else
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&route_select_kernel<0>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (sig)
-            hipLaunchKernelGGL((route_select_kernel<1>), g2, dim3(256), lds, s, xp, wp, b_gate, sel_bias, lp, wn, TT,
+            hipLaunchKernelGGL((route_select_kernel<1>), g2, dim3(256), 0, s, xp, wp, b_gate, sel_bias, lp, wn, TT,
                                hh, E, k, cb, topk_idx, topk_w, routing_map, counts);
         else
-            hipLaunchKernelGGL((route_select_kernel<0>), g2, dim3(256), lds, s, xp, wp, b_gate, sel_bias, lp, wn, TT,
+            hipLaunchKernelGGL((route_select_kernel<0>), g2, dim3(256), 0, s, xp, wp, b_gate, sel_bias, lp, wn, TT,
                                hh, E, k, cb, topk_idx, topk_w, routing_map, counts);
-        return check_launch("moe_route (MFMA filter)");
+        return count("moe_route (MFMA filter)");
     }
     const dim3 grid(static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock));
     const dim3 block(256);
-    const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
-    const size_t wbytes = static_cast<size_t>(E) * static_cast<size_t>(h) * es;
-    if (E <= 16 && wbytes <= 65536) {
+    if (few) {
         // few experts: the gate matrix lives in LDS, each token row is read
         // ceil(E / EPG) times
 #define MOE_ROUTE_WLDS(TIN, EPG_, U_)                                                                   \
@@ -668,13 +742,13 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
                            topk_idx, topk_w, routing_map, counts);                                    \
     } while (0)
         if (dtype == MOE_DTYPE_BF16) {
-            if (E <= 4) MOE_ROUTE_WLDS(bf16_t, 1, 8);
-            else if (E <= 8) MOE_ROUTE_WLDS(bf16_t, 2, 8);
-            else MOE_ROUTE_WLDS(bf16_t, 4, 4);
+            if (E <= 4) MOE_ROUTE_WLDS(bf16_t, 1, 16);
+            else if (E <= 8) MOE_ROUTE_WLDS(bf16_t, 2, 16);
+            else MOE_ROUTE_WLDS(bf16_t, 4, 16);
         } else {
-            if (E <= 4) MOE_ROUTE_WLDS(float, 1, 4);
-            else if (E <= 8) MOE_ROUTE_WLDS(float, 2, 4);
-            else MOE_ROUTE_WLDS(float, 4, 2);
+            if (E <= 4) MOE_ROUTE_WLDS(float, 1, 8);
+            else if (E <= 8) MOE_ROUTE_WLDS(float, 2, 8);
+            else MOE_ROUTE_WLDS(float, 4, 8);
         }
 #undef MOE_ROUTE_WLDS
         return check_launch("moe_route");
@@ -696,5 +770,5 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
             hipLaunchKernelGGL((route_kernel<float, 8, 1>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
                                hh, E, k, sig, logits, topk_idx, topk_w, routing_map, counts);
     }
-    return check_launch("moe_route");
+    return count("moe_route");
 }

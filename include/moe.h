@@ -245,6 +245,51 @@ int moe_permute_bwd(const void *grad_x_perm, int dtype, int64_t T, int64_t h, in
                     const int32_t *topk_idx, const void *w_gate, int E, void *grad_x,
                     void *stream);
 
+/* ------------------------------------------------ auxiliary router losses
+ *
+ * "emerging-techniques-moe-training", section 3 (Load Balancing): the
+ * load-balancing loss and the router z-loss, both on the router's logits l
+ * [T,E] fp32 as moe_route writes them (gate bias included, selection bias
+ * not), for either scoring function:
+ *   aux = E * sum_e f_e P_e,  f_e = counts[e] / (T k),
+ *                             P_e = mean_t softmax(l_t)_e (over all E)
+ *   z   = mean_t logsumexp(l_t)^2
+ * counts [E] int32 are the per-expert routing counts moe_route writes
+ * (offsets[e+1] - offsets[e] serves as well). f_e is piecewise constant in l
+ * and carries no gradient. Supported: k <= E <= 256. T = 0 gives
+ * aux = z = 0. Sums over tokens run in a fixed order (deterministic). */
+size_t moe_router_losses_workspace_size(int64_t T, int E);
+/* losses [2] fp32 device: {aux, z}. probs_mean [E] fp32 (P_e) or NULL.
+ * Workspace: moe_router_losses_workspace_size(T,E) bytes of device memory
+ * (0 and NULL allowed when T = 0). */
+int moe_router_losses(const float *logits, const int32_t *counts, int64_t T, int E, int k,
+                      float *losses, float *probs_mean, void *workspace, size_t workspace_bytes,
+                      void *stream);
+/* grad_logits [T,E] fp32 = d(coef_aux * aux + coef_z * z)/dl (written, not
+ * accumulated):
+ *   coef_aux (E/T) p_tj (f_j - sum_e f_e p_te) + coef_z (2/T) lse_t p_tj,
+ * p_t = softmax(l_t), lse_t = logsumexp(l_t). */
+int moe_router_losses_bwd(const float *logits, const int32_t *counts, int64_t T, int E, int k,
+                          float coef_aux, float coef_z, float *grad_logits, void *stream);
+
+/* Router backward of a dense logit gradient D [T,E] fp32 (such as
+ * moe_router_losses_bwd's), ACCUMULATED into the gradients that
+ * moe_route_bwd and moe_permute_bwd wrote (call it after them):
+ *   grad_w_gate [E,h] fp32 += D^T x       (NULL: skipped; needs x)
+ *   grad_b_gate [E] fp32   += column sums of D   (NULL: skipped)
+ *   grad_x [T,h] dtype     += D w_gate    (NULL: skipped; needs w_gate;
+ *                             the sum is formed in fp32, then added and
+ *                             rounded once to dtype)
+ * x [T,h] and w_gate [E,h] are dtype. Sums run in a fixed order. Needs
+ * h % 64 == 0, E <= 256, 16-byte aligned x, w_gate, grad_w_gate, grad_x and
+ * workspace. Workspace (grad_w_gate only):
+ * moe_router_dense_bwd_workspace_size(T,h,E) bytes of device memory. */
+size_t moe_router_dense_bwd_workspace_size(int64_t T, int64_t h, int E);
+int moe_router_dense_bwd(const void *x, const void *w_gate, int dtype, int64_t T, int64_t h,
+                         int E, const float *grad_logits, float *grad_w_gate,
+                         float *grad_b_gate, void *grad_x, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,13 @@ _SIGS = {
     "moe_route_bwd": ([_vp, _int, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        _vp, _vp, _vp, _sz, _vp], _int),
     "moe_permute_bwd": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _int, _vp, _vp], _int),
+    "moe_router_losses_workspace_size": ([_i64, _int], _sz),
+    "moe_router_losses": ([_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_router_losses_bwd": ([_vp, _vp, _i64, _int, _int, ctypes.c_float, ctypes.c_float, _vp, _vp],
+                              _int),
+    "moe_router_dense_bwd_workspace_size": ([_i64, _i64, _int], _sz),
+    "moe_router_dense_bwd": ([_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                             _int),
 }
 
 
@@ -329,3 +336,55 @@ def moe_permute_bwd(grad_x_perm, row_of, grad_logits_sel=None, topk_idx=None, w_
                                _ptr(grad_x), _stream(grad_x_perm))
     _check(rc, "moe_permute_bwd")
     return grad_x
+
+
+# ------------------------------------------------- auxiliary router losses
+
+def moe_router_losses(logits, counts, k: int, want_probs_mean: bool = False):
+    """(losses [2] fp32 = {aux, z}, probs_mean [E] or None) on the device."""
+    _req(logits, "logits", dtype=torch.float32)
+    dev = logits.device
+    T, E = logits.shape
+    _req(counts, "counts", dtype=torch.int32, shape=(E,), device=dev)
+    losses = torch.empty((2,), dtype=torch.float32, device=dev)
+    pmean = torch.empty((E,), dtype=torch.float32, device=dev) if want_probs_mean else None
+    nws = lib().moe_router_losses_workspace_size(T, E)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev)
+    rc = lib().moe_router_losses(_ptr(logits), _ptr(counts), T, E, k, _ptr(losses), _ptr(pmean),
+                                 _ptr(ws), ws.numel(), _stream(logits))
+    _check(rc, "moe_router_losses")
+    return losses, pmean
+
+
+def moe_router_losses_bwd(logits, counts, k: int, coef_aux: float, coef_z: float):
+    """Dense d(coef_aux * aux + coef_z * z)/d logits, [T,E] fp32."""
+    _req(logits, "logits", dtype=torch.float32)
+    dev = logits.device
+    T, E = logits.shape
+    _req(counts, "counts", dtype=torch.int32, shape=(E,), device=dev)
+    grad = torch.empty((T, E), dtype=torch.float32, device=dev)
+    rc = lib().moe_router_losses_bwd(_ptr(logits), _ptr(counts), T, E, k, float(coef_aux),
+                                     float(coef_z), _ptr(grad), _stream(logits))
+    _check(rc, "moe_router_losses_bwd")
+    return grad
+
+
+def moe_router_dense_bwd(x, w_gate, grad_logits, grad_w_gate=None, grad_b_gate=None, grad_x=None):
+    """Accumulate a dense logit gradient into the router's gradients in place:
+    grad_w_gate += D^T x, grad_b_gate += sum_t D, grad_x += D w_gate (each
+    skipped when None)."""
+    _req(x, "x")
+    dev = x.device
+    T, h = x.shape
+    E = w_gate.shape[0]
+    _req(w_gate, "w_gate", dtype=x.dtype, shape=(E, h), device=dev)
+    _req(grad_logits, "grad_logits", dtype=torch.float32, shape=(T, E), device=dev)
+    _opt(grad_w_gate, "grad_w_gate", dtype=torch.float32, shape=(E, h), device=dev)
+    _opt(grad_b_gate, "grad_b_gate", dtype=torch.float32, shape=(E,), device=dev)
+    _opt(grad_x, "grad_x", dtype=x.dtype, shape=(T, h), device=dev)
+    nws = lib().moe_router_dense_bwd_workspace_size(T, h, E) if grad_w_gate is not None else 0
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev)
+    rc = lib().moe_router_dense_bwd(_ptr(x), _ptr(w_gate), DTYPE[x.dtype], T, h, E, _ptr(grad_logits),
+                                    _ptr(grad_w_gate), _ptr(grad_b_gate), _ptr(grad_x), _ptr(ws),
+                                    ws.numel(), _stream(x))
+    _check(rc, "moe_router_dense_bwd")

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["status.hip", "route.hip", "permute.hip", "combine.hip", "ffn.hip", "ffn_bwd.hip", "backward.hip"]
+SOURCES = ["status.hip", "route.hip", "permute.hip", "combine.hip", "ffn.hip", "ffn_bwd.hip", "backward.hip",
+           "losses.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -28,15 +28,17 @@ def _timed(timers, name, fn):
 
 
 def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False,
-            timers: dict | None = None):
+            timers: dict | None = None, router_losses: bool = False):
     """One forward pass. ``inp`` holds device tensors named as in
     ``workloads.make_inputs``. Returns a dict with ``out`` and the
     intermediate results of every stage. With ``timers``, the grouped FFN
-    call is bracketed by HIP events (key "grouped_ffn")."""
+    call is bracketed by HIP events (key "grouped_ffn"). With
+    ``router_losses``, also ``losses`` = {aux, z} (load-balancing loss and
+    router z-loss, "emerging-techniques-moe-training", section 3)."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
-                    sel_bias=inp.get("sel_bias"), want_logits=keep_for_backward)
+                    sel_bias=inp.get("sel_bias"), want_logits=keep_for_backward or router_losses)
     # inference: the first GEMM gathers token rows itself (no dispatch copy);
     # training keeps x_perm for the weight gradient of the first projection
     gather = not keep_for_backward
@@ -48,6 +50,8 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
         keep_gu=keep_for_backward and act == "swiglu", gather_rows=p["sorted_token"] if gather else None))
     out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"])
     res = dict(out=out)
+    if router_losses:
+        res["losses"], _ = B.moe_router_losses(r["logits"], r["counts"], k)
     res.update(r)
     res.update(p)
     res.update(f)
@@ -55,11 +59,12 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
 
 
 def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
-             timers: dict | None = None):
-    """Gradients of sum(grad_out * out) for a forward run with
-    keep_for_backward=True (routed experts; no shared expert). With
-    ``timers``, the grouped FFN backward call is bracketed by HIP events
-    (key "grouped_ffn_bwd")."""
+             timers: dict | None = None, coef_aux: float = 0.0, coef_z: float = 0.0):
+    """Gradients of sum(grad_out * out) + coef_aux * aux + coef_z * z for a
+    forward run with keep_for_backward=True (routed experts; no shared
+    expert); aux and z are the load-balancing and z-losses of the router's
+    logits. With ``timers``, the grouped FFN backward call is bracketed by
+    HIP events (key "grouped_ffn_bwd")."""
     E = inp["w_gate"].shape[0]
     grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
     g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd(
@@ -69,6 +74,10 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
                         want_b_grad=inp.get("b_gate") is not None)
     grad_x = B.moe_permute_bwd(g["grad_x_perm"], fwd["row_of"], r["grad_logits_sel"],
                                fwd["topk_idx"], inp["w_gate"])
+    if coef_aux != 0.0 or coef_z != 0.0:
+        dl = B.moe_router_losses_bwd(fwd["logits"], fwd["counts"], k, coef_aux, coef_z)
+        B.moe_router_dense_bwd(inp["x"], inp["w_gate"], dl, grad_w_gate=r["grad_w_gate"],
+                               grad_b_gate=r["grad_b_gate"], grad_x=grad_x)
     return dict(grad_x=grad_x, grad_topk_w=grad_w, grad_y=grad_y, grad_w1=g["grad_w1"],
                 grad_w2=g["grad_w2"], grad_w_gate=r["grad_w_gate"], grad_b_gate=r["grad_b_gate"],
                 grad_logits_sel=r["grad_logits_sel"])

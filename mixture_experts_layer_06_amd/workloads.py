@@ -40,7 +40,7 @@ SWIGLU = "swiglu"
 
 # tensor ids used in seeds: seed = 1000 * config_id + tensor_id (+ 100 * variant)
 _TID = dict(x=1, w_gate=2, b_gate=3, w1=4, b1=5, w2=6, b2=7, w1_sh=8, w2_sh=9,
-            sel_bias=10, grad_out=11, skew_perm=12)
+            sel_bias=10, grad_out=11, skew_perm=12, logits=13, dlogits=14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -201,6 +201,19 @@ def make_inputs(cfg: LayerConfig, device="cpu", variant: int = 0,
     if with_grad_out:
         inp["grad_out"] = _normal((T, h), 1.0, cfg, "grad_out", device, variant, dt)
     return inp
+
+
+def router_logit_draw(cfg: LayerConfig, device="cpu", variant: int = 0):
+    """Seeded stand-ins for a router's logits and a logit gradient, [T,E] fp32
+    each: the logits N(0,1) per element (the spread of x . w_gate for the
+    seeded x and w_gate) with the per-expert skew offsets of the imbalanced
+    workload added where it has them; the gradient N(0, 1e-4)."""
+    T, E = cfg.T, cfg.E
+    logits = torch.randn((T, E), generator=_gen(cfg, "logits", "cpu", variant), dtype=torch.float32)
+    if cfg.skew:
+        logits += skew_gate_bias(cfg, "cpu", variant)[None, :]
+    dl = torch.randn((T, E), generator=_gen(cfg, "dlogits", "cpu", variant), dtype=torch.float32) * 1e-2
+    return logits.to(device), dl.to(device)
 
 
 def skew_gate_bias(cfg: LayerConfig, device="cpu", variant: int = 0) -> torch.Tensor:

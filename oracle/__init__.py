@@ -16,9 +16,11 @@ from .moe import (  # noqa: F401
     gate_logits,
     gelu_erf,
     loss_fp64,
+    mean_router_probs,
     permutation,
     route,
     router_backward_dlogits,
+    router_grads,
     router_losses,
     router_losses_dlogits,
     routing_weights,

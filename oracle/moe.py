@@ -413,10 +413,18 @@ def router_losses(logits, topk_idx, E: int):
         return 0.0, 0.0
     p, lse = _log_softmax_parts(l)
     f = expert_fraction(topk_idx, E)
-    P = p.mean(axis=0)
-    aux = E * float((f * P).sum())
+    aux = E * float((f * p.mean(axis=0)).sum())
     z = float((lse * lse).mean())
     return aux, z
+
+
+def mean_router_probs(logits) -> np.ndarray:
+    """P_e = mean over tokens of softmax(l_t)_e, [E] fp64 (zeros for T = 0)."""
+    l = np.asarray(logits, dtype=np.float64)
+    if l.shape[0] == 0:
+        return np.zeros(l.shape[1])
+    p, _ = _log_softmax_parts(l)
+    return p.mean(axis=0)
 
 
 def router_losses_dlogits(logits, topk_idx, E: int, coef_aux: float, coef_z: float):
@@ -437,6 +445,15 @@ def router_losses_dlogits(logits, topk_idx, E: int, coef_aux: float, coef_z: flo
     d_aux = (E / T) * p * (f[None, :] - a)
     d_z = (2.0 / T) * lse[:, None] * p
     return coef_aux * d_aux + coef_z * d_z
+
+
+def router_grads(x, w_gate, dlogits):
+    """Gradients through l = W_r x + b of a logit gradient D [T,E] (fp64):
+    dW_r = D^T x [E,h], db = sum_t D_t [E], dx = D W_r [T,h]."""
+    D = np.asarray(dlogits, dtype=np.float64)
+    x64 = np.asarray(x, dtype=np.float64)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    return dict(dw_gate=D.T @ x64, db_gate=D.sum(axis=0), dx=D @ wg)
 
 
 def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
@@ -492,10 +509,9 @@ def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=N
     np.put_along_axis(dlogits, topk_idx.astype(np.int64), dl, axis=1)
     if coef_aux != 0.0 or coef_z != 0.0:
         dlogits += router_losses_dlogits(routing["logits"], topk_idx, E, coef_aux, coef_z)
-    wg = np.asarray(w_gate, dtype=np.float64)
-    dw_gate = dlogits.T @ x64
-    db_gate = dlogits.sum(axis=0)
-    dx += dlogits @ wg
+    rg = router_grads(x64, w_gate, dlogits)
+    dw_gate, db_gate = rg["dw_gate"], rg["db_gate"]
+    dx += rg["dx"]
     return dict(dx=dx, d_topk_w=d_topk_w, d_logits_sel=dl, d_logits=dlogits,
                 dw_gate=dw_gate, db_gate=db_gate, dw1=dw1, dw2=dw2, db1=db1, db2=db2)
 

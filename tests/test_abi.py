@@ -121,6 +121,38 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert rc == 3
     # permute backward: router term without its inputs
     assert L.moe_permute_bwd(dummy, 1, 16, 64, 2, dummy, dummy, None, None, 0, dummy, None) == 1
+    # router losses: too many experts, k > E, missing output, workspace too small
+    assert L.moe_router_losses(dummy, dummy, 16, 300, 2, dummy, None, dummy, 1 << 20, None) == 2
+    assert L.moe_router_losses(dummy, dummy, 16, 4, 5, dummy, None, dummy, 1 << 20, None) == 2
+    assert L.moe_router_losses(dummy, dummy, 16, 8, 2, None, None, dummy, 1 << 20, None) == 1
+    assert L.moe_router_losses(dummy, dummy, 1000, 8, 2, dummy, None, dummy, 16, None) == 3
+    assert L.moe_router_losses_bwd(None, dummy, 16, 8, 2, 1.0, 1.0, dummy, None) == 1
+    assert L.moe_router_losses_bwd(dummy, dummy, -1, 8, 2, 1.0, 1.0, dummy, None) == 1
+    # dense router backward: bad dtype, h % 64, misaligned pointer, workspace
+    rc = L.moe_router_dense_bwd(dummy, dummy, 7, 16, 64, 8, dummy, dummy, None, None, dummy, 1 << 30, None)
+    assert rc == 1
+    rc = L.moe_router_dense_bwd(dummy, dummy, 1, 16, 96, 8, dummy, dummy, None, None, dummy, 1 << 30, None)
+    assert rc == 2
+    rc = L.moe_router_dense_bwd(vp(4098), dummy, 1, 16, 64, 8, dummy, dummy, None, None, dummy, 1 << 30, None)
+    assert rc == 1
+    rc = L.moe_router_dense_bwd(dummy, dummy, 1, 16, 64, 8, dummy, dummy, None, None, dummy, 8, None)
+    assert rc == 3
+    # x is needed only for the weight gradient, w_gate only for the input gradient
+    rc = L.moe_router_dense_bwd(None, dummy, 1, 16, 64, 8, dummy, dummy, None, None, dummy, 1 << 30, None)
+    assert rc == 1
+    rc = L.moe_router_dense_bwd(dummy, None, 1, 16, 64, 8, dummy, None, None, dummy, None, 0, None)
+    assert rc == 1
+
+
+def test_router_loss_workspace_sizes(lib):
+    b = _binding()
+    L = b.lib()
+    # one fp32 partial row of E+1 sums per 32 tokens
+    assert L.moe_router_losses_workspace_size(1000, 8) == 32 * 9 * 4
+    assert L.moe_router_losses_workspace_size(0, 8) == 0
+    # one fp32 [E,h] partial per 256 tokens
+    assert L.moe_router_dense_bwd_workspace_size(300, 128, 8) == 2 * 8 * 128 * 4
+    assert L.moe_router_dense_bwd_workspace_size(0, 128, 8) == 0
 
 
 def test_binding_refuses_host_tensors():

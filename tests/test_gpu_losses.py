@@ -1,0 +1,165 @@
+"""GPU parity of the auxiliary router losses (load-balancing loss and router
+z-loss, "emerging-techniques-moe-training", section 3 Load Balancing), of
+their dense logit gradient and of the router backward of a dense logit
+gradient, through the C ABI, against the oracle (router_losses,
+mean_router_probs, router_losses_dlogits, router_grads and the layer
+backward with the losses added).
+
+Inputs: seeded logits drawn by ``workloads.router_logit_draw`` (the spread
+of the gate's logits, with the imbalanced workload's skew offsets), the
+selection made on them by the oracle, and the seeded layer tensors."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_06_amd import workloads as wl
+from parity import TOL, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
+
+pytestmark = pytest.mark.gpu
+
+# fp32 sums of at most 8192 terms in [0, 1] (P_e) or of squares of O(1)
+# values (z), against fp64: a few 1e-7 relative.
+LOSS_TOL = 1e-5
+
+CASES = {
+    "tiny_E8_k2": wl.small_variant(wl.CONFIGS[1], T=256, h=128, F=512),
+    "ragged_E16_k4": wl.small_variant(wl.CONFIGS[4], T=333, h=192, F=192, E=16, k=4),
+    "mixtral_8x7b_layer": wl.CONFIGS[2],
+    "qwen3_235b_layer": wl.CONFIGS[3],
+    "deepseek_v3_layer": wl.CONFIGS[4],
+    "qwen3_imbalanced_train": wl.CONFIGS[5],
+}
+
+
+def _routing(cfg, logits_np):
+    """The oracle's selection on the given logits and its counts."""
+    r = oracle.route(None, None, cfg.k, cfg.score, logits=logits_np)
+    idx = r["topk_idx"]
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E).astype(np.int32)
+    return idx, counts
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_losses_and_logit_gradient(moe_lib, name):
+    cfg = CASES[name]
+    print("case losses", name, cfg.T, cfg.E, cfg.k, flush=True)
+    logits, _ = wl.router_logit_draw(cfg)
+    l_np = logits.numpy()
+    idx, counts = _routing(cfg, l_np)
+    dl_, dc = logits.cuda(), torch.as_tensor(counts).cuda()
+    losses, pmean = moe_lib.moe_router_losses(dl_, dc, cfg.k, want_probs_mean=True)
+    aux_ref, z_ref = oracle.router_losses(l_np, idx, cfg.E)
+    got = losses.cpu().numpy().astype(np.float64)
+    err = {"aux": abs(got[0] - aux_ref) / abs(aux_ref), "z": abs(got[1] - z_ref) / abs(z_ref),
+           "P": rel_err_tensor(pmean.cpu().numpy(), oracle.mean_router_probs(l_np))}
+    for ca, cz in ((1.0, 0.0), (0.0, 1.0), (1e-2, 1e-3)):
+        g = moe_lib.moe_router_losses_bwd(dl_, dc, cfg.k, ca, cz)
+        ref = oracle.router_losses_dlogits(l_np, idx, cfg.E, ca, cz)
+        err["dlogits(%g,%g)" % (ca, cz)] = rel_err(g.cpu().numpy(), ref)
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    assert err["aux"] <= LOSS_TOL and err["z"] <= LOSS_TOL and err["P"] <= LOSS_TOL, err
+    assert all(v <= TOL["f32"] for k, v in err.items() if k.startswith("dlogits")), err
+    # fixed-order sums: a second call is bitwise equal
+    again, _ = moe_lib.moe_router_losses(dl_, dc, cfg.k)
+    assert torch.equal(again, losses)
+
+
+def test_losses_edge_cases(moe_lib):
+    """One expert: aux is exactly 1, the load-balancing gradient exactly 0,
+    z the mean square of the logits. Empty batch: both losses 0."""
+    cfg = wl.small_variant(wl.CONFIGS[1], T=77, h=128, F=512, E=1, k=1)
+    logits, _ = wl.router_logit_draw(cfg)
+    counts = torch.tensor([cfg.T * cfg.k], dtype=torch.int32)
+    losses, pmean = moe_lib.moe_router_losses(logits.cuda(), counts.cuda(), 1, want_probs_mean=True)
+    got = losses.cpu().numpy()
+    assert got[0] == 1.0 and pmean.item() == 1.0
+    l64 = logits.numpy().astype(np.float64)[:, 0]
+    assert abs(got[1] - np.mean(l64 ** 2)) <= LOSS_TOL * np.mean(l64 ** 2)
+    g = moe_lib.moe_router_losses_bwd(logits.cuda(), counts.cuda(), 1, 1.0, 0.0)
+    assert not g.any()
+    empty = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    c0 = torch.zeros(8, dtype=torch.int32, device="cuda")
+    losses, pmean = moe_lib.moe_router_losses(empty, c0, 2, want_probs_mean=True)
+    assert not losses.any() and not pmean.any()
+    assert moe_lib.moe_router_losses_bwd(empty, c0, 2, 1.0, 1.0).shape == (0, 8)
+
+
+@pytest.mark.parametrize("name", ["tiny_E8_k2", "ragged_E16_k4", "qwen3_235b_layer", "deepseek_v3_layer"])
+def test_router_dense_backward(moe_lib, name):
+    """grad_w_gate += D^T x, grad_b_gate += sum_t D, grad_x += D w_gate on
+    nonzero starting values, against the oracle's router_grads."""
+    cfg = CASES[name]
+    print("case dense router backward", name, cfg.T, cfg.h, cfg.E, flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", router_only=True)
+    _, D = wl.router_logit_draw(cfg)
+    x, wg = inp["x"], inp["w_gate"]
+    gw0 = torch.full((cfg.E, cfg.h), 0.25, dtype=torch.float32)
+    gb0 = torch.linspace(-1.0, 1.0, cfg.E, dtype=torch.float32)
+    gx0 = (x.float() * 1e-3).to(x.dtype)
+    gw, gb, gx = gw0.cuda(), gb0.cuda(), gx0.cuda()
+    moe_lib.moe_router_dense_bwd(x.cuda(), wg.cuda(), D.cuda(), grad_w_gate=gw, grad_b_gate=gb, grad_x=gx)
+    ref = oracle.router_grads(to_np32(x), to_np32(wg), D.numpy())
+    tol = TOL[cfg.dtype]
+    err = {"grad_w_gate": rel_err_tensor(gw.cpu().numpy(), gw0.numpy() + ref["dw_gate"]),
+           "grad_b_gate": rel_err_tensor(gb.cpu().numpy(), gb0.numpy() + ref["db_gate"]),
+           "grad_x": rel_err(to_np32(gx), to_np32(gx0) + ref["dx"])}
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    # the weight and bias sums are fp32 whatever the layer dtype
+    assert err["grad_w_gate"] <= TOL["f32"] and err["grad_b_gate"] <= TOL["f32"], err
+    assert err["grad_x"] <= tol, err
+    # each part alone (NULL skips the others) gives the same bits
+    gw2 = gw0.cuda()
+    moe_lib.moe_router_dense_bwd(x.cuda(), wg.cuda(), D.cuda(), grad_w_gate=gw2)
+    assert torch.equal(gw2, gw)
+    gx2 = gx0.cuda()
+    moe_lib.moe_router_dense_bwd(x.cuda(), wg.cuda(), D.cuda(), grad_x=gx2)
+    assert torch.equal(gx2, gx)
+
+
+def _layer_step(cfg, inp, coef_aux, coef_z, zero_grad_out=False):
+    from mixture_experts_layer_06_amd import layer
+    dinp = to_device(inp)
+    if zero_grad_out:
+        dinp["grad_out"] = torch.zeros_like(dinp["grad_out"])
+    f = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True, router_losses=True)
+    g = layer.backward(dinp, f, dinp["grad_out"], cfg.k, cfg.score, cfg.act, coef_aux=coef_aux,
+                       coef_z=coef_z)
+    torch.cuda.synchronize()
+    return dinp, f, g
+
+
+@pytest.mark.parametrize("case", ["imbalanced_softmax", "sigmoid_ragged", "losses_only"])
+def test_layer_backward_with_losses(moe_lib, case):
+    """The whole layer step with coef_aux * aux + coef_z * z added, against
+    the oracle's backward; "losses_only" zeroes grad_out so that every
+    router gradient comes from the losses alone."""
+    if case == "sigmoid_ragged":
+        cfg = wl.small_variant(wl.CONFIGS[5], T=333, h=192, F=192, E=16, k=4).with_shape(
+            score="sigmoid", skew=False, gate_bias=False)
+    else:
+        cfg = wl.small_variant(wl.CONFIGS[5], T=300, h=256, F=128, E=32)
+    ca, cz = (0.5, 0.05)
+    print("case layer with losses", case, flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=True)
+    zero = case == "losses_only"
+    _, f, g = _layer_step(cfg, inp, ca, cz, zero_grad_out=zero)
+    o = oracle_inputs(inp)
+    gout = np.zeros_like(to_np32(inp["grad_out"])) if zero else to_np32(inp["grad_out"])
+    routing = oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score, o["b_gate"], o["sel_bias"])
+    assert np.array_equal(f["topk_idx"].cpu().numpy(), routing["topk_idx"])
+    aux_ref, z_ref = oracle.router_losses(routing["logits"], routing["topk_idx"], cfg.E)
+    got = f["losses"].cpu().numpy().astype(np.float64)
+    assert abs(got[0] - aux_ref) <= LOSS_TOL * abs(aux_ref), (got, aux_ref)
+    assert abs(got[1] - z_ref) <= LOSS_TOL * abs(z_ref), (got, z_ref)
+    ref = oracle.backward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act, gout,
+                          b_gate=o["b_gate"], routing=routing, coef_aux=ca, coef_z=cz)
+    tol = TOL[cfg.dtype]
+    err = {"grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
+           "grad_w_gate": rel_err_tensor(g["grad_w_gate"].cpu().numpy(), ref["dw_gate"])}
+    if g["grad_b_gate"] is not None:
+        err["grad_b_gate"] = rel_err_tensor(g["grad_b_gate"].cpu().numpy(), ref["db_gate"])
+    if not zero:
+        err["grad_topk_w"] = rel_err(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"])
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    assert all(v <= tol for v in err.values()), err

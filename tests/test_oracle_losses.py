@@ -46,6 +46,23 @@ def test_hand_worked_two_tokens():
     assert z == pytest.approx(math.log(4.0) ** 2, rel=1e-15)
 
 
+def test_mean_router_probs_hand_worked_and_invariants():
+    """Logits (0, ln 3) and (ln 3, 0): softmaxes (1/4, 3/4) and (3/4, 1/4),
+    so P = (1/2, 1/2). For any logits P is a distribution; equal logits give
+    1/E; an empty batch gives zeros; aux = E <f, P>."""
+    l = np.array([[0.0, math.log(3.0)], [math.log(3.0), 0.0]])
+    assert oracle.mean_router_probs(l) == pytest.approx([0.5, 0.5], rel=1e-15)
+    rng = np.random.default_rng(9)
+    l = 4 * rng.standard_normal((50, 7))
+    P = oracle.mean_router_probs(l)
+    assert P.sum() == pytest.approx(1.0, rel=1e-14) and (P > 0).all()
+    assert oracle.mean_router_probs(np.zeros((5, 8))) == pytest.approx(np.full(8, 1 / 8), rel=1e-15)
+    assert not oracle.mean_router_probs(np.zeros((0, 3))).any()
+    idx = _topk(l, 2)
+    aux, _ = oracle.router_losses(l, idx, 7)
+    assert aux == pytest.approx(7 * float(oracle.expert_fraction(idx, 7) @ P), rel=1e-14)
+
+
 def test_uniform_router_gives_one_whatever_the_load():
     """Equal logits within each token: P_e = 1/E, so aux = sum_e f_e = 1 even
     for a skewed selection."""

@@ -37,6 +37,10 @@ METRIC = "MoE layer active TFLOP/s + tokens/s at 1 MI355X; % of MFMA/HBM rooflin
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# fp32 FMA on the vector ALUs without packed instructions (which this library
+# does not emit): 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz
+PEAK_F32_VALU_TFLOPS = 78.6
+COEF_AUX, COEF_Z = 1e-2, 1e-3
 # measured HBM traffic of the grouped FFN (rocprofv3 FETCH_SIZE / WRITE_SIZE,
 # scaled by the same counters on a plain copy); valid while the GEMM sources
 # hash to the recorded value
@@ -55,6 +59,9 @@ def parse():
                    help="tokens of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")
+    p.add_argument("--router-losses", action="store_true",
+                   help="add the load-balancing loss (coefficient 1e-2) and router z-loss "
+                        "(1e-3) to a training step, and time their kernels as stages")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB elementwise copy (counter calibration)")
     return p.parse_args()
@@ -308,10 +315,14 @@ def main():
     train = cfg.backward
     flops = cfg.active_flops_forward() + (cfg.active_flops_backward() if train else 0.0)
 
+    losses = args.router_losses and train
+    coefs = dict(coef_aux=COEF_AUX, coef_z=COEF_Z) if losses else {}
+
     def step(timers=None):
-        f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers)
+        f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers,
+                          router_losses=losses)
         if train:
-            layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers)
+            layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers, **coefs)
         return f
 
     for _ in range(args.warmup):
@@ -344,7 +355,8 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.h, "experts": cfg.E,
                    "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
                    "shared_experts": cfg.n_shared,
-                   "step": "forward + backward" if train else "forward"},
+                   "step": "forward + backward" if train else "forward",
+                   "router_losses": {"coef_aux": COEF_AUX, "coef_z": COEF_Z} if losses else None},
         "tokens_per_s": cfg.T / dt,
         "frac_of_bf16_peak": flops / dt / 1e12 / PEAK_BF16_TFLOPS,
         "active_gflop_per_step": flops / 1e9,
@@ -419,6 +431,15 @@ def main():
             calls["permute_bwd"] = lambda: B.moe_permute_bwd(gf["grad_x_perm"], f2["row_of"],
                                                              gr["grad_logits_sel"], f2["topk_idx"],
                                                              inp["w_gate"])
+            if losses:
+                gx = torch.zeros_like(inp["x"])
+                dl = B.moe_router_losses_bwd(f2["logits"], f2["counts"], cfg.k, COEF_AUX, COEF_Z)
+                calls["router_losses"] = lambda: B.moe_router_losses(f2["logits"], f2["counts"], cfg.k)
+                calls["router_losses_bwd"] = lambda: B.moe_router_losses_bwd(
+                    f2["logits"], f2["counts"], cfg.k, COEF_AUX, COEF_Z)
+                calls["router_dense_bwd"] = lambda: B.moe_router_dense_bwd(
+                    inp["x"], inp["w_gate"], dl, grad_w_gate=gr["grad_w_gate"],
+                    grad_b_gate=gr["grad_b_gate"], grad_x=gx)
         stages = {}
         for name, fn in calls.items():
             fn()
@@ -448,6 +469,17 @@ def main():
             tb = stages["grouped_ffn_bwd"]["s_median"]
             stages["grouped_ffn_bwd"]["tflops"] = bwd_flops / tb / 1e12
             stages["grouped_ffn_bwd"]["mfma_frac"] = bwd_flops / tb / 1e12 / peak
+        if "router_losses" in stages:
+            lb = cfg.T * cfg.E * 4 + cfg.E * 4 + 8       # logits and counts read, losses written
+            for name, nbytes in (("router_losses", lb), ("router_losses_bwd", lb + cfg.T * cfg.E * 4)):
+                t = stages[name]["s_median"]
+                stages[name].update(algorithmic_bytes=nbytes, gb_per_s=nbytes / t / 1e9,
+                                    hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS)
+            # D^T x and D w_gate: 2 T E h FLOP each, fp32 FMA on the vector ALUs
+            fl = 4.0 * cfg.T * cfg.E * cfg.h
+            t = stages["router_dense_bwd"]["s_median"]
+            stages["router_dense_bwd"].update(flops=fl, tflops=fl / t / 1e12,
+                                              valu_frac=fl / t / 1e12 / PEAK_F32_VALU_TFLOPS)
         out["stages"] = stages
         del flush
 

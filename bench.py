@@ -59,6 +59,9 @@ def parse():
                    help="tokens of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")
+    p.add_argument("--memory-efficient", action="store_true",
+                   help="apply the routing weight before the second projection (experts without "
+                        "output bias) and rebuild the activation in the backward")
     p.add_argument("--router-losses", action="store_true",
                    help="add the load-balancing loss (coefficient 1e-2) and router z-loss "
                         "(1e-3) to a training step, and time their kernels as stages")
@@ -317,10 +320,15 @@ def main():
 
     losses = args.router_losses and train
     coefs = dict(coef_aux=COEF_AUX, coef_z=COEF_Z) if losses else {}
+    meff = args.memory_efficient
+    if meff and inp.get("b2") is not None:
+        if inp["b2"].any():
+            sys.exit("--memory-efficient needs experts without output bias")
+        inp["b2"] = None
 
     def step(timers=None):
         f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers,
-                          router_losses=losses)
+                          router_losses=losses, memory_efficient=meff)
         if train:
             layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers, **coefs)
         return f
@@ -356,11 +364,16 @@ def main():
                    "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
                    "shared_experts": cfg.n_shared,
                    "step": "forward + backward" if train else "forward",
-                   "router_losses": {"coef_aux": COEF_AUX, "coef_z": COEF_Z} if losses else None},
+                   "router_losses": {"coef_aux": COEF_AUX, "coef_z": COEF_Z} if losses else None,
+                   "memory_efficient_permutation": meff},
         "tokens_per_s": cfg.T / dt,
         "frac_of_bf16_peak": flops / dt / 1e12 / PEAK_BF16_TFLOPS,
         "active_gflop_per_step": flops / 1e9,
         "expert_load": {"min": int(counts.min()), "max": int(counts.max())},
+        # activations the forward keeps for the backward (training step only)
+        "saved_for_backward_bytes": int(sum(res[n].numel() * res[n].element_size()
+                                            for n in ("x_perm", "gu", "act", "y", "row_w", "logits")
+                                            if res.get(n) is not None)) if train else None,
         "gpu_clock": clock.summary(),
     }
 
@@ -400,9 +413,11 @@ def main():
         has_sh = inp.get("w1_sh") is not None
         a_in = p["x_perm"] if train else inp["x"]
         g_rows = None if train else p["sorted_token"]
+        row_w = B.moe_permute_weights(r["topk_w"], p["row_of"]) if meff else None
         f = B.moe_grouped_ffn(a_in, p["offsets"], inp["w1"], inp["w2"], cfg.act,
                               b1=inp.get("b1"), b2=inp.get("b2"), x_sh=inp["x"] if has_sh else None,
-                              w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"), gather_rows=g_rows)
+                              w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"), gather_rows=g_rows,
+                              row_w=row_w)
         calls = {
             "route": lambda: B.moe_route(inp["x"], inp["w_gate"], cfg.k, cfg.score,
                                          b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias")),
@@ -410,21 +425,34 @@ def main():
             "grouped_ffn": lambda: B.moe_grouped_ffn(
                 a_in, p["offsets"], inp["w1"], inp["w2"], cfg.act, b1=inp.get("b1"),
                 b2=inp.get("b2"), x_sh=inp["x"] if has_sh else None, w1_sh=inp.get("w1_sh"),
-                w2_sh=inp.get("w2_sh"), gather_rows=g_rows),
-            "unpermute": lambda: B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"]),
+                w2_sh=inp.get("w2_sh"), gather_rows=g_rows, row_w=row_w),
+            "unpermute": lambda: B.moe_unpermute(f["y"], p["row_of"], None if meff else r["topk_w"],
+                                                 y_sh=f["y_sh"]),
         }
         if train:
-            f2 = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=True)
-            gy, gw = B.moe_unpermute_bwd(inp["grad_out"], f2["y"], f2["row_of"], f2["topk_w"])
-            gf = B.moe_grouped_ffn_bwd(gy, f2["x_perm"], f2["act"], f2["gu"], f2["offsets"],
-                                       inp["w1"], inp["w2"], cfg.act)
+            f2 = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=True,
+                               memory_efficient=meff)
+            if meff:
+                gy, _ = B.moe_unpermute_bwd(inp["grad_out"], None, f2["row_of"], None)
+                gf = B.moe_grouped_ffn_bwd_recompute(gy, f2["x_perm"], f2["gu"], f2["offsets"],
+                                                     inp["w1"], inp["w2"], cfg.act, row_w=f2["row_w"])
+                gw = B.moe_permute_weights_bwd(gf["grad_row_w"], f2["row_of"])
+                calls["unpermute_bwd"] = lambda: B.moe_unpermute_bwd(inp["grad_out"], None,
+                                                                     f2["row_of"], None)
+                calls["grouped_ffn_bwd"] = lambda: B.moe_grouped_ffn_bwd_recompute(
+                    gy, f2["x_perm"], f2["gu"], f2["offsets"], inp["w1"], inp["w2"], cfg.act,
+                    row_w=f2["row_w"])
+            else:
+                gy, gw = B.moe_unpermute_bwd(inp["grad_out"], f2["y"], f2["row_of"], f2["topk_w"])
+                gf = B.moe_grouped_ffn_bwd(gy, f2["x_perm"], f2["act"], f2["gu"], f2["offsets"],
+                                           inp["w1"], inp["w2"], cfg.act)
+                calls["unpermute_bwd"] = lambda: B.moe_unpermute_bwd(inp["grad_out"], f2["y"],
+                                                                     f2["row_of"], f2["topk_w"])
+                calls["grouped_ffn_bwd"] = lambda: B.moe_grouped_ffn_bwd(
+                    gy, f2["x_perm"], f2["act"], f2["gu"], f2["offsets"], inp["w1"], inp["w2"], cfg.act)
             gr = B.moe_route_bwd(inp["x"], E, f2["topk_idx"], f2["topk_w"], gw, f2["offsets"],
                                  f2["sorted_token"], score=cfg.score, logits=f2["logits"],
                                  want_b_grad=inp.get("b_gate") is not None)
-            calls["unpermute_bwd"] = lambda: B.moe_unpermute_bwd(inp["grad_out"], f2["y"],
-                                                                 f2["row_of"], f2["topk_w"])
-            calls["grouped_ffn_bwd"] = lambda: B.moe_grouped_ffn_bwd(
-                gy, f2["x_perm"], f2["act"], f2["gu"], f2["offsets"], inp["w1"], inp["w2"], cfg.act)
             calls["route_bwd"] = lambda: B.moe_route_bwd(
                 inp["x"], E, f2["topk_idx"], f2["topk_w"], gw, f2["offsets"], f2["sorted_token"],
                 score=cfg.score, logits=f2["logits"], want_b_grad=inp.get("b_gate") is not None)

@@ -182,13 +182,41 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_ro
                     const void *w1_sh, const void *w2_sh, void *act, void *gu, void *y,
                     void *y_sh, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Memory-efficient permutation ("Scalable Training ... with Megatron Core",
+ * section 4.1.1): for experts without an output bias,
+ *   sum_i p_i W2 phi(W1 x) = sum_i W2 (p_i phi(W1 x)),
+ * so the routing weight can be applied to the activation before the second
+ * projection. moe_grouped_ffn with the activation of permuted row r scaled by
+ * row_w[r] (fp32 [P], e.g. from moe_permute_weights; shared-expert rows are
+ * not scaled): act = p * silu(g) * u or p * GELU(a), and y = W2 act is then
+ * the weighted expert output, to be combined by moe_unpermute with
+ * topk_w = NULL. The expert output y is not needed by the backward
+ * (moe_grouped_ffn_bwd_recompute derives the routing-weight gradient from the
+ * pre-activations). There is no b2 argument: with an output bias the two
+ * forms differ by (k-1) b2. gu keeps the unscaled pre-activations. */
+int moe_grouped_ffn_weighted(const void *x_perm, const int32_t *gather_rows, int64_t x_rows,
+                             int dtype, int64_t P, int64_t h, int64_t F, int E,
+                             const int32_t *offsets, int act_kind, const void *w1, const void *b1,
+                             const void *w2, const void *x_sh, int64_t T_sh, const void *w1_sh,
+                             const void *w2_sh, const float *row_w, void *act, void *gu, void *y,
+                             void *y_sh, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Routing weights in permuted-row order: row_w[row_of[t,j]] = topk_w[t,j]
+ * (row_w [T*k] fp32, row_of [T,k] as moe_permute writes it), and the
+ * backward gather grad_topk_w[t,j] = grad_row_w[row_of[t,j]]. */
+int moe_permute_weights(const float *topk_w, int64_t T, int k, const int32_t *row_of,
+                        float *row_w, void *stream);
+int moe_permute_weights_bwd(const float *grad_row_w, int64_t T, int k, const int32_t *row_of,
+                            float *grad_topk_w, void *stream);
+
 /* -------------------------------------------------------------- Unpermute
  * Combine stage ("Scalable Training ... with Megatron Core", section 2.1
  * stage 4 and section 1.1's MoE(x) = sum over the top-k of p_i E_i(x)):
  *   out[t] = sum_{j<k, ascending} topk_w[t,j] * y[row_of[t,j]]  (+ y_sh[t])
  * accumulated in fp32, rounded once to dtype.
- *   y [P,h] dtype, row_of [T,k], topk_w [T,k] fp32, y_sh [T,h] dtype|NULL
- *   out [T,h] dtype (output)
+ *   y [P,h] dtype, row_of [T,k], topk_w [T,k] fp32 or NULL (weights 1: the
+ *   rows of moe_grouped_ffn_weighted are already weighted), y_sh [T,h]
+ *   dtype|NULL, out [T,h] dtype (output)
  */
 int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int k,
                   const int32_t *row_of, const float *topk_w, const void *y_sh, void *out,
@@ -201,7 +229,10 @@ int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int k,
  */
 
 /* Combine backward: grad_y[row_of[t,j]] = topk_w[t,j] * grad_out[t] (dtype)
- * and grad_topk_w[t,j] = <grad_out[t], y[row_of[t,j]]> (fp32). */
+ * and grad_topk_w[t,j] = <grad_out[t], y[row_of[t,j]]> (fp32). With
+ * topk_w = NULL (the unweighted combine of weighted expert outputs):
+ * grad_y[row_of[t,j]] = grad_out[t]; y and grad_topk_w are then not used and
+ * may be NULL. */
 int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype, int64_t T, int64_t h,
                       int k, const int32_t *row_of, const float *topk_w, void *grad_y,
                       float *grad_topk_w, void *stream);
@@ -218,6 +249,30 @@ int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const void *act,
                         const int32_t *offsets, int act_kind, const void *w1, const void *w2,
                         void *grad_gu, void *grad_x_perm, float *grad_w1, float *grad_w2,
                         void *stream);
+
+/* Grouped FFN backward with the activation recomputed ("Scalable Training ...
+ * with Megatron Core", section 4.1.2, recomputing the activation function):
+ * act is not read; act = p * silu(g) * u is rebuilt from gu in the workspace
+ * (p = row_w[r], or 1 when row_w is NULL), with the forward epilogue's
+ * expression. With row_w (memory-efficient permutation, see
+ * moe_grouped_ffn_weighted; grad_y is then the unweighted
+ * moe_unpermute_bwd result):
+ *   dact = grad_y W2[e];  da = p dact;  (dg, du) from da as above
+ *   grad_row_w[r] = <dact_r, silu(g_r) * u_r>   [P] fp32 (dL/dp; fixed-order
+ *                                               sum, moe_permute_weights_bwd
+ *                                               maps it to [T,k])
+ *   grad_w2[e] = grad_y_e^T act_e, grad_w1, grad_x_perm as above.
+ * row_w and grad_row_w are both NULL or both set. Workspace:
+ * moe_grouped_ffn_bwd_recompute_workspace_size(P, F, row_w != NULL) bytes of
+ * 16-byte aligned device memory. bf16 SwiGLU only. */
+size_t moe_grouped_ffn_bwd_recompute_workspace_size(int64_t P, int64_t F, int weighted);
+int moe_grouped_ffn_bwd_recompute(const void *grad_y, const void *x_perm, const void *gu,
+                                  int dtype, int64_t P, int64_t h, int64_t F, int E,
+                                  const int32_t *offsets, int act_kind, const void *w1,
+                                  const void *w2, const float *row_w, void *grad_gu,
+                                  void *grad_x_perm, float *grad_w1, float *grad_w2,
+                                  float *grad_row_w, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /* Router backward. grad_logits_sel[t,j] = dL/dl for the selected expert
  * topk_idx[t,j] (unselected logits get 0):

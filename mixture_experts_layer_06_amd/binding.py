@@ -55,6 +55,13 @@ _SIGS = {
     "moe_router_losses_bwd": ([_vp, _vp, _i64, _int, _int, ctypes.c_float, ctypes.c_float, _vp, _vp],
                               _int),
     "moe_router_dense_bwd_workspace_size": ([_i64, _i64, _int], _sz),
+    "moe_grouped_ffn_weighted": ([_vp, _vp, _i64, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp,
+                                  _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_permute_weights": ([_vp, _i64, _int, _vp, _vp, _vp], _int),
+    "moe_permute_weights_bwd": ([_vp, _i64, _int, _vp, _vp, _vp], _int),
+    "moe_grouped_ffn_bwd_recompute_workspace_size": ([_i64, _i64, _int], _sz),
+    "moe_grouped_ffn_bwd_recompute": ([_vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_router_dense_bwd": ([_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              _int),
 }
@@ -181,10 +188,12 @@ def moe_permute(x, topk_idx, E: int, with_x_perm: bool = True):
 
 def moe_grouped_ffn(x_perm, offsets, w1, w2, act: str = "swiglu", b1=None, b2=None, x_sh=None,
                     w1_sh=None, w2_sh=None, keep_gu: bool = False, use_workspace: bool = True,
-                    workspace=None, gather_rows=None):
+                    workspace=None, gather_rows=None, row_w=None):
     """Grouped expert FFN. With gather_rows (the sorted_token of
     moe_permute), x_perm is the unpermuted x [T,h] and the first GEMM reads
-    its rows in permuted order itself."""
+    its rows in permuted order itself. With row_w ([P] fp32, from
+    moe_permute_weights) the activation of permuted row r is scaled by
+    row_w[r] (moe_grouped_ffn_weighted; no b2)."""
     _req(x_perm, "x_perm")
     dev = x_perm.device
     dt = x_perm.dtype
@@ -220,6 +229,17 @@ def moe_grouped_ffn(x_perm, offsets, w1, w2, act: str = "swiglu", b1=None, b2=No
     else:
         nws = lib().moe_grouped_ffn_workspace_size(DTYPE[dt]) if use_workspace else 0
         ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    if row_w is not None:
+        _req(row_w, "row_w", dtype=torch.float32, shape=(P,), device=dev)
+        if b2 is not None:
+            raise MoeError("moe_grouped_ffn: row weights need an expert without output bias")
+        rc = lib().moe_grouped_ffn_weighted(_ptr(x_perm), _ptr(gather_rows), x_rows, DTYPE[dt], P, h, F,
+                                            E, _ptr(offsets), ACT[act], _ptr(w1), _ptr(b1), _ptr(w2),
+                                            _ptr(x_sh), T_sh, _ptr(w1_sh), _ptr(w2_sh), _ptr(row_w),
+                                            _ptr(out["act"]), _ptr(out["gu"]), _ptr(out["y"]),
+                                            _ptr(out["y_sh"]), _ptr(ws), nws, _stream(x_perm))
+        _check(rc, "moe_grouped_ffn_weighted")
+        return out
     rc = lib().moe_grouped_ffn(_ptr(x_perm), _ptr(gather_rows), x_rows, DTYPE[dt], P, h, F, E,
                                _ptr(offsets), ACT[act],
                                _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(x_sh), T_sh,
@@ -230,12 +250,13 @@ def moe_grouped_ffn(x_perm, offsets, w1, w2, act: str = "swiglu", b1=None, b2=No
 
 
 def moe_unpermute(y, row_of, topk_w, y_sh=None, out=None):
+    """Weighted combine; topk_w None: weights 1 (rows already weighted)."""
     _req(y, "y")
     dev = y.device
     T, k = row_of.shape
     h = y.shape[1]
     _req(row_of, "row_of", dtype=torch.int32, device=dev)
-    _req(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    _opt(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
     _opt(y_sh, "y_sh", dtype=y.dtype, shape=(T, h), device=dev)
     if out is None:
         out = torch.empty((T, h), dtype=y.dtype, device=dev)
@@ -249,16 +270,21 @@ def moe_unpermute(y, row_of, topk_w, y_sh=None, out=None):
 # ---------------------------------------------------------------- backward
 
 def moe_unpermute_bwd(grad_out, y, row_of, topk_w):
+    """(grad_y, grad_topk_w). topk_w None (unweighted combine): y is not
+    used, grad_y rows are copies of grad_out and grad_topk_w is None."""
     _req(grad_out, "grad_out")
     dev = grad_out.device
     T, h = grad_out.shape
     k = row_of.shape[1]
-    _req(y, "y", dtype=grad_out.dtype, shape=(T * k, h), device=dev)
     _req(row_of, "row_of", dtype=torch.int32, shape=(T, k), device=dev)
-    _req(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    if topk_w is not None:
+        _req(y, "y", dtype=grad_out.dtype, shape=(T * k, h), device=dev)
+        _req(topk_w, "topk_w", dtype=torch.float32, shape=(T, k), device=dev)
+    else:
+        y = None
     grad_y = torch.empty((T * k, h), dtype=grad_out.dtype, device=dev)
-    grad_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    rc = lib().moe_unpermute_bwd(_ptr(grad_out), _ptr(y), DTYPE[y.dtype], T, h, k, _ptr(row_of),
+    grad_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is not None else None
+    rc = lib().moe_unpermute_bwd(_ptr(grad_out), _ptr(y), DTYPE[grad_out.dtype], T, h, k, _ptr(row_of),
                                  _ptr(topk_w), _ptr(grad_y), _ptr(grad_w), _stream(grad_out))
     _check(rc, "moe_unpermute_bwd")
     return grad_y, grad_w
@@ -288,6 +314,63 @@ def moe_grouped_ffn_bwd(grad_y, x_perm, act_out, gu, offsets, w1, w2, act: str =
                                    _stream(grad_y))
     _check(rc, "moe_grouped_ffn_bwd")
     return dict(grad_gu=grad_gu, grad_x_perm=grad_x_perm, grad_w1=grad_w1, grad_w2=grad_w2)
+
+
+def moe_grouped_ffn_bwd_recompute(grad_y, x_perm, gu, offsets, w1, w2, act: str = "swiglu",
+                                  row_w=None):
+    """Grouped FFN backward with the activation rebuilt from gu; with row_w
+    (memory-efficient permutation) also grad_row_w [P] = dL/d row_w."""
+    _req(grad_y, "grad_y")
+    dev = grad_y.device
+    dt = grad_y.dtype
+    P, h = grad_y.shape
+    E = w1.shape[0]
+    F = w2.shape[2]
+    n1 = 2 if act == "swiglu" else 1
+    _req(x_perm, "x_perm", dtype=dt, shape=(P, h), device=dev)
+    _req(gu, "gu", dtype=dt, device=dev)
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(w1, "w1", dtype=dt, shape=(E, n1 * F, h), device=dev)
+    _req(w2, "w2", dtype=dt, shape=(E, h, F), device=dev)
+    _opt(row_w, "row_w", dtype=torch.float32, shape=(P,), device=dev)
+    out = dict(grad_gu=torch.empty((P, n1 * F), dtype=dt, device=dev),
+               grad_x_perm=torch.empty((P, h), dtype=dt, device=dev),
+               grad_w1=torch.empty((E, n1 * F, h), dtype=torch.float32, device=dev),
+               grad_w2=torch.empty((E, h, F), dtype=torch.float32, device=dev),
+               grad_row_w=torch.empty((P,), dtype=torch.float32, device=dev) if row_w is not None else None)
+    nws = lib().moe_grouped_ffn_bwd_recompute_workspace_size(P, F, int(row_w is not None))
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev)
+    rc = lib().moe_grouped_ffn_bwd_recompute(
+        _ptr(grad_y), _ptr(x_perm), _ptr(gu), DTYPE[dt], P, h, F, E, _ptr(offsets), ACT[act], _ptr(w1),
+        _ptr(w2), _ptr(row_w), _ptr(out["grad_gu"]), _ptr(out["grad_x_perm"]), _ptr(out["grad_w1"]),
+        _ptr(out["grad_w2"]), _ptr(out["grad_row_w"]), _ptr(ws), ws.numel(), _stream(grad_y))
+    _check(rc, "moe_grouped_ffn_bwd_recompute")
+    return out
+
+
+def moe_permute_weights(topk_w, row_of):
+    """row_w [T*k] fp32 with row_w[row_of[t,j]] = topk_w[t,j]."""
+    _req(topk_w, "topk_w", dtype=torch.float32)
+    dev = topk_w.device
+    T, k = topk_w.shape
+    _req(row_of, "row_of", dtype=torch.int32, shape=(T, k), device=dev)
+    row_w = torch.empty((T * k,), dtype=torch.float32, device=dev)
+    rc = lib().moe_permute_weights(_ptr(topk_w), T, k, _ptr(row_of), _ptr(row_w), _stream(topk_w))
+    _check(rc, "moe_permute_weights")
+    return row_w
+
+
+def moe_permute_weights_bwd(grad_row_w, row_of):
+    """grad_topk_w [T,k] with grad_topk_w[t,j] = grad_row_w[row_of[t,j]]."""
+    _req(grad_row_w, "grad_row_w", dtype=torch.float32)
+    dev = grad_row_w.device
+    T, k = row_of.shape
+    _req(row_of, "row_of", dtype=torch.int32, shape=(T, k), device=dev)
+    _req(grad_row_w, "grad_row_w", dtype=torch.float32, shape=(T * k,), device=dev)
+    g = torch.empty((T, k), dtype=torch.float32, device=dev)
+    rc = lib().moe_permute_weights_bwd(_ptr(grad_row_w), T, k, _ptr(row_of), _ptr(g), _stream(grad_row_w))
+    _check(rc, "moe_permute_weights_bwd")
+    return g
 
 
 def moe_route_bwd(x, E: int, topk_idx, topk_w, grad_topk_w, offsets, sorted_token,

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
     for (int j = 0; j < 8; ++j) {
         rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
         if (rows[j] >= P) rows[j] = -1;
-        w[j] = j < k ? topk_w[static_cast<int64_t>(t) * k + j] : 0.0f;
+        w[j] = j < k ? (topk_w ? topk_w[static_cast<int64_t>(t) * k + j] : 1.0f) : 0.0f;
     }
     float yv[8][8];
 #pragma unroll
@@ -208,6 +208,25 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     store8_nt(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
 }
 
+// Unweighted combine backward: grad_y[row_of[t,j]] = grad_out[t] for every
+// j, one 8-element piece of grad_out per thread (loaded once, stored k times).
+template <typename TE>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const TE *__restrict__ gout, int h, int k,
+                                                           const int32_t *__restrict__ row_of, TE *__restrict__ gy,
+                                                           int64_t npieces) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= npieces) return;
+    const int nv = h >> 3;
+    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    const int64_t P = npieces / nv * k;
+    float g[8];
+    load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+    for (int j = 0; j < k; ++j) {
+        const int r = row_of[static_cast<int64_t>(t) * k + j];
+        if (r >= 0 && r < P) store8_nt(gy + static_cast<int64_t>(r) * h + 8 * v, g);
+    }
+}
+
 int check_common(const char *fn, int dtype, int64_t T, int64_t h, int k) {
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
                   "%s: bad dtype %d", fn, dtype);
@@ -227,8 +246,7 @@ extern "C" int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int
                              const int32_t *row_of, const float *topk_w, const void *y_sh,
                              void *out, void *stream) {
     clear_error();
-    MOE_CHECK_ARG(y && row_of && topk_w && out, MOE_ERR_INVALID_ARG,
-                  "moe_unpermute: null required pointer");
+    MOE_CHECK_ARG(y && row_of && out, MOE_ERR_INVALID_ARG, "moe_unpermute: null required pointer");
     int st = check_common("moe_unpermute", dtype, T, h, k);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(aligned16(y) && aligned16(out) && (!y_sh || aligned16(y_sh)), MOE_ERR_INVALID_ARG,
@@ -252,10 +270,25 @@ extern "C" int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype,
                                  int64_t h, int k, const int32_t *row_of, const float *topk_w,
                                  void *grad_y, float *grad_topk_w, void *stream) {
     clear_error();
-    MOE_CHECK_ARG(grad_out && y && row_of && topk_w && grad_y && grad_topk_w, MOE_ERR_INVALID_ARG,
+    MOE_CHECK_ARG(grad_out && row_of && grad_y && (topk_w == nullptr || (y && grad_topk_w)), MOE_ERR_INVALID_ARG,
                   "moe_unpermute_bwd: null required pointer");
     int st = check_common("moe_unpermute_bwd", dtype, T, h, k);
     if (st != MOE_OK) return st;
+    if (topk_w == nullptr) {
+        MOE_CHECK_ARG(aligned16(grad_out) && aligned16(grad_y), MOE_ERR_INVALID_ARG,
+                      "moe_unpermute_bwd: pointers must be 16-byte aligned");
+        if (T == 0) return MOE_OK;
+        hipStream_t s = as_stream(stream);
+        const int64_t npieces = T * (h / 8);
+        const dim3 grid(static_cast<unsigned>((npieces + 255) / 256)), block(256);
+        if (dtype == MOE_DTYPE_BF16)
+            hipLaunchKernelGGL(scatter_rows_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t *>(grad_out),
+                               static_cast<int>(h), k, row_of, static_cast<bf16_t *>(grad_y), npieces);
+        else
+            hipLaunchKernelGGL(scatter_rows_kernel<float>, grid, block, 0, s, static_cast<const float *>(grad_out),
+                               static_cast<int>(h), k, row_of, static_cast<float *>(grad_y), npieces);
+        return check_launch("moe_unpermute_bwd");
+    }
     MOE_CHECK_ARG(aligned16(grad_out) && aligned16(y) && aligned16(grad_y), MOE_ERR_INVALID_ARG,
                   "moe_unpermute_bwd: pointers must be 16-byte aligned");
     if (T == 0) return MOE_OK;

@@ -112,7 +112,7 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
     const int chunk = tid & 7, rb = tid >> 3;
     const int so = swz(rb, chunk);      // + 32 j rows: same swizzle
     const int rows = min(kTile, ti.M - ti.m0);
-    const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
+    const int nb_rows = (MODE & 7) == kModeSwiGLU ? 2 * a.N_out : a.N_out;
 
     const bf16_t *wseg = ti.shared ? static_cast<const bf16_t *>(a.B_sh)
                                    : static_cast<const bf16_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
@@ -126,17 +126,17 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
                                        static_cast<int64_t>(ti.m0) * K;
     // weight rows of the tile: SwiGLU j even -> gate rows f, j odd -> up rows
     // N_out + f, f = n_tile*128 + (j/2)*32 + rb; plain: n_tile*256 + rb + 32 j
-    const int wfirst = MODE == kModeSwiGLU ? ti.n_tile * (kTile / 2) : ti.n_tile * kTile;
+    const int wfirst = (MODE & 7) == kModeSwiGLU ? ti.n_tile * (kTile / 2) : ti.n_tile * kTile;
     const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wseg + static_cast<int64_t>(wfirst) * K);
     const __amdgpu_buffer_rsrc_t rwu =
-        make_rsrc(wseg + static_cast<int64_t>(MODE == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K);
+        make_rsrc(wseg + static_cast<int64_t>((MODE & 7) == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K);
     const __amdgpu_buffer_rsrc_t rx =
         gather ? make_rsrc(xbase, static_cast<uint32_t>(a.a_rows) * static_cast<uint32_t>(K) * 2u) : make_rsrc(xbase);
     int wv[8], xv[XJ];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int rl = MODE == kModeSwiGLU ? (j >> 1) * 32 + rb : rb + 32 * j;   // row past the base
-        const int lim = MODE == kModeSwiGLU ? a.N_out : nb_rows;
+        const int rl = (MODE & 7) == kModeSwiGLU ? (j >> 1) * 32 + rb : rb + 32 * j;   // row past the base
+        const int lim = (MODE & 7) == kModeSwiGLU ? a.N_out : nb_rows;
         wv[j] = ((wfirst + rl < lim ? rl : 0) * K + chunk * 8) * 2;            // base row is valid
     }
 #pragma unroll
@@ -278,12 +278,12 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
     const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int tok0 = HALF ? 0 : (wave >> 1) * 128;
     const int rows = min(kTile, ti.M - ti.m0);
-    const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
+    const int nb_rows = (MODE & 7) == kModeSwiGLU ? 2 * a.N_out : a.N_out;
     const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
     bf16_t *Cseg = ti.shared ? static_cast<bf16_t *>(a.C_sh) + static_cast<int64_t>(ti.m0) * a.N_out
                              : static_cast<bf16_t *>(a.C) + crow0 * a.N_out;
     bf16_t *GUseg = nullptr;
-    if (MODE == kModeSwiGLU) {
+    if ((MODE & 7) == kModeSwiGLU) {
         if (ti.shared)
             GUseg = a.GU_sh ? static_cast<bf16_t *>(a.GU_sh) + static_cast<int64_t>(ti.m0) * 2 * a.N_out : nullptr;
         else
@@ -292,15 +292,17 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
     const bf16_t *bias = (a.bias && !ti.shared)
                              ? static_cast<const bf16_t *>(a.bias) + static_cast<int64_t>(ti.seg) * nb_rows
                              : nullptr;
+    const float *roww = (MODE & kRowW) && !ti.shared ? a.row_w + crow0 : nullptr;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (JONLY >= 0 && j != JONLY) continue;
         const int m = tok0 + j * 32 + l32;
         if (m >= rows) continue;
+        const float rw = roww ? roww[m] : 1.0f;
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int nl = 8 * gq + 4 * lhi;   // row offset inside a 32-row subtile
-            if (MODE == kModeSwiGLU) {
+            if ((MODE & 7) == kModeSwiGLU) {
 #pragma unroll
                 for (int p = 0; p < NI / 2; ++p) {
                     const int f = ti.n_tile * (kTile / 2) + wrow0 / 2 + p * 32 + nl;
@@ -314,7 +316,7 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
                             g[q] += bf16_to_f32(bias[f + q]);
                             u[q] += bf16_to_f32(bias[a.N_out + f + q]);
                         }
-                        hv[q] = silu_fast(g[q]) * u[q];
+                        hv[q] = silu_fast(g[q]) * u[q] * rw;
                     }
                     uint2 o;
                     o.x = pack_bf16x2(hv[0], hv[1]);
@@ -331,7 +333,7 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
                         *reinterpret_cast<uint2 *>(gr + a.N_out + f) = ou;
                     }
                 }
-            } else if (MODE == kModeF32Out) {
+            } else if ((MODE & 7) == kModeF32Out) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int n = ti.n_tile * kTile + wrow0 + i * 32 + nl;
@@ -356,7 +358,7 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
                     for (int q = 0; q < 4; ++q) {
                         v[q] = acc[i][j][4 * gq + q];
                         if (bias) v[q] += bf16_to_f32(bias[n + q]);
-                        if (MODE == kModeGELU) v[q] = gelu_erf_f(v[q]);
+                        if ((MODE & 7) == kModeGELU) v[q] = gelu_erf_f(v[q]) * rw;
                     }
                     uint2 o;
                     o.x = pack_bf16x2(v[0], v[1]);
@@ -549,8 +551,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
     const int wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     const int total = build_tile_prefix(a, BM, s_cum, s_tmp);
-    const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
-    const int BN_out = MODE == kModeSwiGLU ? BN / 2 : BN;
+    const int nb_rows = (MODE & 7) == kModeSwiGLU ? 2 * a.N_out : a.N_out;
+    const int BN_out = (MODE & 7) == kModeSwiGLU ? BN / 2 : BN;
     const int K = a.K;
     const int r = tid >> 2, c4 = (tid & 3) * 4;
 
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
         const float *Bseg = ti.shared ? static_cast<const float *>(a.B_sh)
                                       : static_cast<const float *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
         int wrow;
-        if (MODE == kModeSwiGLU) {
+        if ((MODE & 7) == kModeSwiGLU) {
             const int blk = r >> 4;
             const int f = ti.n_tile * (BN / 2) + (blk >> 1) * 16 + (r & 15);
             wrow = (blk & 1) ? a.N_out + f : f;
@@ -615,19 +617,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
         float *Cseg = ti.shared ? static_cast<float *>(a.C_sh)
                                 : static_cast<float *>(a.C) + static_cast<int64_t>(ti.row0) * a.N_out;
         float *GUseg = nullptr;
-        if (MODE == kModeSwiGLU)
+        if ((MODE & 7) == kModeSwiGLU)
             GUseg = ti.shared ? static_cast<float *>(a.GU_sh)
                               : (a.GU ? static_cast<float *>(a.GU) + static_cast<int64_t>(ti.row0) * 2 * a.N_out
                                       : nullptr);
         const float *bias = (a.bias && !ti.shared)
                                 ? static_cast<const float *>(a.bias) + static_cast<int64_t>(ti.seg) * nb_rows
                                 : nullptr;
+        const float *roww = (MODE & kRowW) && !ti.shared ? a.row_w + ti.row0 : nullptr;
         const int ng = lane >> 4;
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
             const int mm = ti.m0 + wm * 32 + j * 16 + (lane & 15);
             if (mm >= ti.M) continue;
-            if (MODE == kModeSwiGLU) {
+            const float rw = roww ? roww[mm] : 1.0f;
+            if ((MODE & 7) == kModeSwiGLU) {
                 const int f = ti.n_tile * BN_out + wn * 16 + 4 * ng;
                 if (f >= a.N_out) continue;
                 float4 hv, gv, uv;
@@ -641,7 +645,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
                     }
                     gp[i] = g;
                     up[i] = u;
-                    hp[i] = silu_f(g) * u;
+                    hp[i] = silu_f(g) * u * rw;
                 }
                 *reinterpret_cast<float4 *>(Cseg + static_cast<int64_t>(mm) * a.N_out + f) = hv;
                 if (GUseg) {
@@ -660,7 +664,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
                     for (int q = 0; q < 4; ++q) {
                         float v = acc[i][j][q];
                         if (bias) v += bias[n + q];
-                        if (MODE == kModeGELU) v = gelu_erf_f(v);
+                        if ((MODE & 7) == kModeGELU) v = gelu_erf_f(v) * rw;
                         op[q] = v;
                     }
                     *reinterpret_cast<float4 *>(Cseg + static_cast<int64_t>(mm) * a.N_out + n) = o;
@@ -675,11 +679,11 @@ int launch_gemm(GGArgs a, int dtype, int64_t P, hipStream_t s, const char *what)
     const int S = a.E + (a.M_sh > 0 ? 1 : 0);
     int64_t upper;
     if (dtype == MOE_DTYPE_BF16) {
-        const int BNo = MODE == kModeSwiGLU ? 128 : 256;
+        const int BNo = (MODE & 7) == kModeSwiGLU ? 128 : 256;
         a.n_tiles = (a.N_out + BNo - 1) / BNo;
         upper = ((P + a.M_sh) / 256 + S) * static_cast<int64_t>(a.n_tiles);
     } else {
-        const int BNo = MODE == kModeSwiGLU ? 32 : 64;
+        const int BNo = (MODE & 7) == kModeSwiGLU ? 32 : 64;
         a.n_tiles = (a.N_out + BNo - 1) / BNo;
         upper = ((P + a.M_sh) / 64 + S) * static_cast<int64_t>(a.n_tiles);
     }
@@ -751,14 +755,13 @@ extern "C" size_t moe_grouped_ffn_workspace_size(int dtype) {
                             static_cast<size_t>(num_cus()) * kPartFloats);
 }
 
-extern "C" int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, int dtype,
-                               int64_t P, int64_t h, int64_t F,
-                               int E, const int32_t *offsets, int act_kind, const void *w1,
-                               const void *b1, const void *w2, const void *b2, const void *x_sh,
-                               int64_t T_sh, const void *w1_sh, const void *w2_sh, void *act,
-                               void *gu, void *y, void *y_sh, void *workspace,
-                               size_t workspace_bytes, void *stream) {
-    clear_error();
+namespace {
+
+int grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, int dtype, int64_t P, int64_t h,
+                int64_t F, int E, const int32_t *offsets, int act_kind, const void *w1, const void *b1,
+                const void *w2, const void *b2, const void *x_sh, int64_t T_sh, const void *w1_sh,
+                const void *w2_sh, const float *row_w, void *act, void *gu, void *y, void *y_sh, void *workspace,
+                size_t workspace_bytes, void *stream) {
     MOE_CHECK_ARG(offsets && w1 && w2 && act && y, MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: null required pointer");
     MOE_CHECK_ARG(P == 0 || x_perm, MOE_ERR_INVALID_ARG, "moe_grouped_ffn: null x_perm");
@@ -814,12 +817,18 @@ extern "C" int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, i
     g1.C_sh = has_sh ? static_cast<char *>(act) + static_cast<size_t>(P) * F * es : nullptr;
     g1.GU_sh = (has_sh && gu) ? static_cast<char *>(gu) + static_cast<size_t>(P) * n1 * F * es : nullptr;
     g1.offsets = offsets;
+    g1.row_w = row_w;
     g1.E = E;
     g1.N_out = static_cast<int>(F);
     g1.K = static_cast<int>(h);
     g1.ws = ws;
     g1.ws_tiles = ws_tiles;
-    int st = act_kind == MOE_ACT_SWIGLU ? launch_gemm<kModeSwiGLU>(g1, dtype, P, s, "moe_grouped_ffn gemm1")
+    int st;
+    if (row_w)
+        st = act_kind == MOE_ACT_SWIGLU ? launch_gemm<kModeSwiGLU | kRowW>(g1, dtype, P, s, "moe_grouped_ffn gemm1")
+                                        : launch_gemm<kModeGELU | kRowW>(g1, dtype, P, s, "moe_grouped_ffn gemm1");
+    else
+        st = act_kind == MOE_ACT_SWIGLU ? launch_gemm<kModeSwiGLU>(g1, dtype, P, s, "moe_grouped_ffn gemm1")
                                         : launch_gemm<kModeGELU>(g1, dtype, P, s, "moe_grouped_ffn gemm1");
     if (st != MOE_OK) return st;
 
@@ -840,4 +849,30 @@ extern "C" int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, i
     g2.ws = ws;
     g2.ws_tiles = ws_tiles;
     return launch_gemm<kModePlain>(g2, dtype, P, s, "moe_grouped_ffn gemm2");
+}
+
+}  // namespace
+
+extern "C" int moe_grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, int dtype,
+                               int64_t P, int64_t h, int64_t F,
+                               int E, const int32_t *offsets, int act_kind, const void *w1,
+                               const void *b1, const void *w2, const void *b2, const void *x_sh,
+                               int64_t T_sh, const void *w1_sh, const void *w2_sh, void *act,
+                               void *gu, void *y, void *y_sh, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    clear_error();
+    return grouped_ffn(x_perm, gather_rows, x_rows, dtype, P, h, F, E, offsets, act_kind, w1, b1, w2, b2, x_sh,
+                       T_sh, w1_sh, w2_sh, nullptr, act, gu, y, y_sh, workspace, workspace_bytes, stream);
+}
+
+extern "C" int moe_grouped_ffn_weighted(const void *x_perm, const int32_t *gather_rows, int64_t x_rows,
+                                        int dtype, int64_t P, int64_t h, int64_t F, int E,
+                                        const int32_t *offsets, int act_kind, const void *w1, const void *b1,
+                                        const void *w2, const void *x_sh, int64_t T_sh, const void *w1_sh,
+                                        const void *w2_sh, const float *row_w, void *act, void *gu, void *y,
+                                        void *y_sh, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(P == 0 || row_w, MOE_ERR_INVALID_ARG, "moe_grouped_ffn_weighted: null row_w");
+    return grouped_ffn(x_perm, gather_rows, x_rows, dtype, P, h, F, E, offsets, act_kind, w1, b1, w2, nullptr,
+                       x_sh, T_sh, w1_sh, w2_sh, row_w, act, gu, y, y_sh, workspace, workspace_bytes, stream);
 }

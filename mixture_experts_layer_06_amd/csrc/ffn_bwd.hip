@@ -37,7 +37,10 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-enum BwdKind { kDgradSwiGLU = 0, kDgradPlain = 1, kWgrad = 2 };
+// kDgradSwiGLUW: the SwiGLU backward of an activation scaled by a per-row
+// weight p (row_w): d(p a)/da = p, and the row's dL/dp = <dact, a> is summed
+// per tile into dp_part.
+enum BwdKind { kDgradSwiGLU = 0, kDgradPlain = 1, kWgrad = 2, kDgradSwiGLUW = 3 };
 
 struct BGArgs {
     const bf16_t *A;          // MFMA "A": K-major storage, element (k, a) at A[k * lda + a]
@@ -54,6 +57,8 @@ struct BGArgs {
     int64_t a_expert_stride;  // dgrad: elements between experts' weights; wgrad: 0
     int n_tiles_a, n_tiles_b;
     int grid;
+    const float *row_w;       // kDgradSwiGLUW: [P] per-row weights of the activation
+    float *dp_part;           // kDgradSwiGLUW: [P][n_tiles_a] per-tile sums of <dact, a>
 };
 
 constexpr int kBK = 64, kTile = 256, kRegion = kTile * kBK, kStage = 2 * kRegion;
@@ -105,7 +110,7 @@ __device__ __forceinline__ void sched_quarter() {
 // and rows 128 (w / 2) ..; HALF: columns 64 w .. +63, rows 0..127.
 template <int KIND, bool ODD, bool HALF>
 __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0, int row0, int rows,
-                                         int nk_tok, bf16_t *LB0, bf16_t *LB1) {
+                                         int nk_tok, bf16_t *LB0, bf16_t *LB1, float (*s_dp)[kTile]) {
     constexpr bool WG = KIND == kWgrad;
     constexpr int NI = HALF ? 2 : 4, NJ = 4;
     constexpr int XB = WG ? 8 : (HALF ? 4 : 8);     // B chunks per thread per k-step
@@ -259,11 +264,15 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
 #undef MOE_STEP
 
     // ------------------------------------------------------------ epilogue
+    float dpacc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dpacc[j] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int bl = brow0 + j * 32 + l32;   // row of C within the tile
         if (!WG && bl >= rows) continue;
         if (WG && b0 + bl >= a.b_dim) continue;
+        const float pw = KIND == kDgradSwiGLUW ? a.row_w[row0 + bl] : 1.0f;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -291,11 +300,15 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
                     float dg[4], du[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float d = acc[i][j][4 * gq + q];
+                        float d = acc[i][j][4 * gq + q];
                         // hardware exp and reciprocal (a few ulp): with the
                         // IEEE divide the epilogue needs so many registers
                         // that the accumulators get spilled inside the k-loop
                         const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-g[q]));
+                        if (KIND == kDgradSwiGLUW) {
+                            dpacc[j] = fmaf(d, g[q] * s * u[q], dpacc[j]);
+                            d *= pw;
+                        }
                         dg[q] = d * u[q] * (s * (1.0f + g[q] * (1.0f - s)));
                         du[q] = d * (g[q] * s);
                     }
@@ -311,6 +324,21 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
             }
         }
     }
+    if constexpr (KIND == kDgradSwiGLUW) {
+        // <dact, a> of each row: this lane's columns, then its partner half
+        // (lane ^ 32), then the waves sharing the row in a fixed order
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const float v = dpacc[j] + __shfl_xor(dpacc[j], 32);
+            if (lhi == 0) s_dp[HALF ? wave : (wave & 1)][brow0 + j * 32 + l32] = v;
+        }
+        __syncthreads();
+        const int r = threadIdx.x;
+        if (r < rows) {
+            const float v = HALF ? ((s_dp[0][r] + s_dp[1][r]) + s_dp[2][r]) + s_dp[3][r] : s_dp[0][r] + s_dp[1][r];
+            a.dp_part[static_cast<int64_t>(row0 + r) * a.n_tiles_a + a0 / kTile] = v;
+        }
+    }
 }
 
 // ODD (data-gradient GEMMs only): K / 64 is odd.
@@ -321,6 +349,7 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm(BGArgs a) {
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
     __shared__ int s_order[256];
+    __shared__ float s_dp[KIND == kDgradSwiGLUW ? 4 : 1][kTile];
     const int tid = threadIdx.x;
 
     int total;
@@ -355,7 +384,7 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm(BGArgs a) {
             const int local = L % per;
             const int row0 = a.offsets[e];
             bwd_tile<KIND, false, false>(a, e, (local % a.n_tiles_a) * kTile, (local / a.n_tiles_a) * kTile, row0,
-                                         0, a.offsets[e + 1] - row0, LB0, LB1);
+                                         0, a.offsets[e + 1] - row0, LB0, LB1, s_dp);
         } else {
             GGArgs g{};
             g.offsets = a.offsets;
@@ -364,9 +393,11 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm(BGArgs a) {
             const TileInfo ti = decode_tile(g, s_cum, L, kTile);
             const int rows = min(kTile, ti.M - ti.m0);
             if (rows > kTile / 2)
-                bwd_tile<KIND, ODD, false>(a, ti.seg, ti.n_tile * kTile, 0, ti.row0 + ti.m0, rows, 0, LB0, LB1);
+                bwd_tile<KIND, ODD, false>(a, ti.seg, ti.n_tile * kTile, 0, ti.row0 + ti.m0, rows, 0, LB0, LB1,
+                                           s_dp);
             else
-                bwd_tile<KIND, ODD, true>(a, ti.seg, ti.n_tile * kTile, 0, ti.row0 + ti.m0, rows, 0, LB0, LB1);
+                bwd_tile<KIND, ODD, true>(a, ti.seg, ti.n_tile * kTile, 0, ti.row0 + ti.m0, rows, 0, LB0, LB1,
+                                          s_dp);
         }
     }
 }
@@ -399,35 +430,72 @@ int launch_bwd(BGArgs a, int64_t P, hipStream_t s, const char *what) {
 
 using namespace moe;
 
-extern "C" int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const void *act,
-                                   const void *gu, int dtype, int64_t P, int64_t h, int64_t F, int E,
-                                   const int32_t *offsets, int act_kind, const void *w1,
-                                   const void *w2, void *grad_gu, void *grad_x_perm, float *grad_w1,
-                                   float *grad_w2, void *stream) {
-    clear_error();
-    MOE_CHECK_ARG(grad_y && x_perm && act && gu && offsets && w1 && w2 && grad_gu && grad_x_perm &&
-                      grad_w1 && grad_w2,
-                  MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd: null required pointer");
-    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
-                  "moe_grouped_ffn_bwd: bad dtype %d", dtype);
+namespace {
+
+// act[r][f] = bf16(silu(g) * u * p_r) from the saved pre-activations, with
+// the forward epilogue's expression (p = 1 without row weights): one 8-column
+// piece per thread.
+__global__ __launch_bounds__(256) void swiglu_recompute_kernel(const bf16_t *__restrict__ gu,
+                                                               const float *__restrict__ row_w, int F,
+                                                               bf16_t *__restrict__ act, int64_t npieces) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= npieces) return;
+    const int nv = F >> 3;
+    const int64_t r = idx / nv;
+    const int v = static_cast<int>(idx - r * nv);
+    const bf16_t *gr = gu + r * 2 * F + 8 * v;
+    float g[8], u[8], o[8];
+    load8(gr, g);
+    load8(gr + F, u);
+    const float p = row_w ? row_w[r] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = silu_fast(g[i]) * u[i] * p;
+    store8(act + r * F + 8 * v, o);
+}
+
+// grad_row_w[r] = sum of the row's per-tile partials, tiles ascending.
+__global__ __launch_bounds__(256) void dp_reduce_kernel(const float *__restrict__ part, int nt, int64_t P,
+                                                        float *__restrict__ grad_row_w) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (r >= P) return;
+    float s = 0.0f;
+    for (int t = 0; t < nt; ++t) s += part[r * nt + t];
+    grad_row_w[r] = s;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int check_bwd_args(const char *what, const void *grad_y, const void *x_perm, const void *gu, int dtype, int64_t P,
+                   int64_t h, int64_t F, int E, const int32_t *offsets, int act_kind, const void *w1,
+                   const void *w2, const void *grad_gu, const void *grad_x_perm, const float *grad_w1,
+                   const float *grad_w2) {
+    MOE_CHECK_ARG(grad_y && x_perm && gu && offsets && w1 && w2 && grad_gu && grad_x_perm && grad_w1 && grad_w2,
+                  MOE_ERR_INVALID_ARG, "%s: null required pointer", what);
+    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG, "%s: bad dtype %d", what,
+                  dtype);
     MOE_CHECK_ARG(act_kind == MOE_ACT_GELU || act_kind == MOE_ACT_SWIGLU, MOE_ERR_INVALID_ARG,
-                  "moe_grouped_ffn_bwd: bad activation %d", act_kind);
-    MOE_CHECK_ARG(P >= 0 && h > 0 && F > 0 && E > 0, MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd: bad sizes");
+                  "%s: bad activation %d", what, act_kind);
+    MOE_CHECK_ARG(P >= 0 && h > 0 && F > 0 && E > 0, MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
     MOE_CHECK_ARG(dtype == MOE_DTYPE_BF16 && act_kind == MOE_ACT_SWIGLU, MOE_ERR_UNSUPPORTED,
-                  "moe_grouped_ffn_bwd: bf16 SwiGLU experts only");
+                  "%s: bf16 SwiGLU experts only", what);
     MOE_CHECK_ARG(h % 64 == 0 && F % 64 == 0 && E <= 256, MOE_ERR_UNSUPPORTED,
-                  "moe_grouped_ffn_bwd: need h %% 64 == 0, F %% 64 == 0, E <= 256");
+                  "%s: need h %% 64 == 0, F %% 64 == 0, E <= 256", what);
     MOE_CHECK_ARG(P < (int64_t(1) << 31) && h < (int64_t(1) << 20) && F < (int64_t(1) << 20) &&
                       P * (2 * F > h ? 2 * F : h) < (int64_t(1) << 31),
-                  MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_bwd: sizes too large");
-    const void *ptrs[] = {grad_y, x_perm, act, gu, w1, w2, grad_gu, grad_x_perm, grad_w1, grad_w2};
+                  MOE_ERR_UNSUPPORTED, "%s: sizes too large", what);
+    const void *ptrs[] = {grad_y, x_perm, gu, w1, w2, grad_gu, grad_x_perm, grad_w1, grad_w2};
     for (const void *p : ptrs)
-        MOE_CHECK_ARG(aligned16(p), MOE_ERR_INVALID_ARG, "moe_grouped_ffn_bwd: pointers must be 16-byte aligned");
-    hipStream_t s = as_stream(stream);
-    const bf16_t *dY = static_cast<const bf16_t *>(grad_y);
-    const bf16_t *X = static_cast<const bf16_t *>(x_perm);
-    const bf16_t *H = static_cast<const bf16_t *>(act);
-    bf16_t *dGU = static_cast<bf16_t *>(grad_gu);
+        MOE_CHECK_ARG(aligned16(p), MOE_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", what);
+    return MOE_OK;
+}
+
+// The four GEMMs of the backward; with row_w, the data gradient of the
+// activation uses the weighted SwiGLU backward and leaves per-tile partials of
+// dL/dp in dp_part.
+int ffn_bwd_gemms(const bf16_t *dY, const bf16_t *X, const bf16_t *H, const void *gu, int64_t P, int64_t h,
+                  int64_t F, int E, const int32_t *offsets, const void *w1, const void *w2, bf16_t *dGU,
+                  void *grad_x_perm, float *grad_w1, float *grad_w2, const float *row_w, float *dp_part,
+                  hipStream_t s) {
     const int hi = static_cast<int>(h), Fi = static_cast<int>(F);
 
     // dact = dY W2[e] with the SwiGLU backward fused: A = W2[e] as [h][F]
@@ -443,7 +511,10 @@ extern "C" int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const
     d2.lda = Fi;
     d2.ldb = hi;
     d2.a_expert_stride = static_cast<int64_t>(h) * F;
-    int st = launch_bwd<kDgradSwiGLU>(d2, P, s, "moe_grouped_ffn_bwd dact");
+    d2.row_w = row_w;
+    d2.dp_part = dp_part;
+    int st = row_w ? launch_bwd<kDgradSwiGLUW>(d2, P, s, "moe_grouped_ffn_bwd dact")
+                   : launch_bwd<kDgradSwiGLU>(d2, P, s, "moe_grouped_ffn_bwd dact");
     if (st != MOE_OK) return st;
 
     // dX = [dg du] W1[e]: A = W1[e] as [2F][h]
@@ -487,4 +558,66 @@ extern "C" int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const
     w1g.lda = hi;
     w1g.ldb = 2 * Fi;
     return launch_bwd<kWgrad>(w1g, P, s, "moe_grouped_ffn_bwd dW1");
+}
+
+}  // namespace
+
+extern "C" int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const void *act,
+                                   const void *gu, int dtype, int64_t P, int64_t h, int64_t F, int E,
+                                   const int32_t *offsets, int act_kind, const void *w1,
+                                   const void *w2, void *grad_gu, void *grad_x_perm, float *grad_w1,
+                                   float *grad_w2, void *stream) {
+    clear_error();
+    int st = check_bwd_args("moe_grouped_ffn_bwd", grad_y, x_perm, gu, dtype, P, h, F, E, offsets, act_kind, w1,
+                            w2, grad_gu, grad_x_perm, grad_w1, grad_w2);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(act && aligned16(act), MOE_ERR_INVALID_ARG,
+                  "moe_grouped_ffn_bwd: act must be a 16-byte aligned pointer");
+    return ffn_bwd_gemms(static_cast<const bf16_t *>(grad_y), static_cast<const bf16_t *>(x_perm),
+                         static_cast<const bf16_t *>(act), gu, P, h, F, E, offsets, w1, w2,
+                         static_cast<bf16_t *>(grad_gu), grad_x_perm, grad_w1, grad_w2, nullptr, nullptr,
+                         as_stream(stream));
+}
+
+extern "C" size_t moe_grouped_ffn_bwd_recompute_workspace_size(int64_t P, int64_t F, int weighted) {
+    if (P <= 0 || F <= 0) return 0;
+    const size_t act = align256(static_cast<size_t>(P) * static_cast<size_t>(F) * sizeof(bf16_t));
+    const size_t nt = static_cast<size_t>((F + kTile - 1) / kTile);
+    return act + (weighted ? static_cast<size_t>(P) * nt * sizeof(float) : 0);
+}
+
+extern "C" int moe_grouped_ffn_bwd_recompute(const void *grad_y, const void *x_perm, const void *gu, int dtype,
+                                             int64_t P, int64_t h, int64_t F, int E, const int32_t *offsets,
+                                             int act_kind, const void *w1, const void *w2, const float *row_w,
+                                             void *grad_gu, void *grad_x_perm, float *grad_w1, float *grad_w2,
+                                             float *grad_row_w, void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+    clear_error();
+    int st = check_bwd_args("moe_grouped_ffn_bwd_recompute", grad_y, x_perm, gu, dtype, P, h, F, E, offsets,
+                            act_kind, w1, w2, grad_gu, grad_x_perm, grad_w1, grad_w2);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG((row_w == nullptr) == (grad_row_w == nullptr), MOE_ERR_INVALID_ARG,
+                  "moe_grouped_ffn_bwd_recompute: row_w and grad_row_w go together");
+    const size_t need = moe_grouped_ffn_bwd_recompute_workspace_size(P, F, row_w != nullptr);
+    MOE_CHECK_ARG(need == 0 || (workspace && workspace_bytes >= need && aligned16(workspace)), MOE_ERR_WORKSPACE,
+                  "moe_grouped_ffn_bwd_recompute: a 16-byte aligned workspace of %zu bytes is needed", need);
+    hipStream_t s = as_stream(stream);
+    bf16_t *H = static_cast<bf16_t *>(workspace);
+    float *dp_part = row_w ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                       align256(static_cast<size_t>(P) * F * sizeof(bf16_t)))
+                           : nullptr;
+    if (P > 0) {
+        const int64_t npieces = P * (F / 8);
+        hipLaunchKernelGGL(swiglu_recompute_kernel, dim3(static_cast<unsigned>((npieces + 255) / 256)), dim3(256),
+                           0, s, static_cast<const bf16_t *>(gu), row_w, static_cast<int>(F), H, npieces);
+        st = check_launch("moe_grouped_ffn_bwd_recompute act");
+        if (st != MOE_OK) return st;
+    }
+    st = ffn_bwd_gemms(static_cast<const bf16_t *>(grad_y), static_cast<const bf16_t *>(x_perm), H, gu, P, h, F, E,
+                       offsets, w1, w2, static_cast<bf16_t *>(grad_gu), grad_x_perm, grad_w1, grad_w2, row_w,
+                       dp_part, s);
+    if (st != MOE_OK || !row_w || P == 0) return st;
+    hipLaunchKernelGGL(dp_reduce_kernel, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0, s, dp_part,
+                       static_cast<int>((F + kTile - 1) / kTile), P, grad_row_w);
+    return check_launch("moe_grouped_ffn_bwd_recompute dp");
 }

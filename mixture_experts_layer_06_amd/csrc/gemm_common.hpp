@@ -14,6 +14,10 @@
 namespace moe {
 
 enum GemmMode { kModePlain = 0, kModeSwiGLU = 1, kModeGELU = 2, kModeF32Out = 3 };
+// Added to kModeSwiGLU / kModeGELU: the activation of segment row r is scaled
+// by GGArgs::row_w[r]. A separate instantiation, so the unscaled kernels are
+// unchanged.
+constexpr int kRowW = 8;
 
 // fp32 C = A B^T for one segment of T rows (bf16 A [T][K], B [N][K]) on the
 // grouped GEMM kernel, split along K when few tiles; ws: the grouped FFN's
@@ -44,6 +48,8 @@ struct GGArgs {
     int ws_tiles;           // fp32 partial tiles the workspace holds
     const int32_t *gather;  // null, or: row r of the segments is row gather[r] of A
     int a_rows;             // rows of A when gathering
+    const float *row_w;     // null, or: the activation of segment row r is scaled by row_w[r]
+                            // (shared-expert rows are not scaled)
 };
 
 constexpr int kMaxSeg = 260;

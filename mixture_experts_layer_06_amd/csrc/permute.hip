@@ -131,6 +131,27 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x
     }
 }
 
+// Routing weights in permuted-row order and back:
+//   row_w[row_of[t,j]] = topk_w[t,j];   grad_topk_w[t,j] = grad_row_w[row_of[t,j]]
+// (one (t, j) pair per thread; rows outside [0, T k) are skipped, or read as 0).
+__global__ __launch_bounds__(256) void permute_weights_kernel(const float *__restrict__ topk_w,
+                                                              const int32_t *__restrict__ row_of, int64_t P,
+                                                              float *__restrict__ row_w) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= P) return;
+    const int r = row_of[i];
+    if (r >= 0 && r < P) row_w[r] = topk_w[i];
+}
+
+__global__ __launch_bounds__(256) void permute_weights_bwd_kernel(const float *__restrict__ grad_row_w,
+                                                                  const int32_t *__restrict__ row_of, int64_t P,
+                                                                  float *__restrict__ grad_topk_w) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= P) return;
+    const int r = row_of[i];
+    grad_topk_w[i] = (r >= 0 && r < P) ? grad_row_w[r] : 0.0f;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -188,4 +209,32 @@ extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E
                                static_cast<float *>(x_perm), T * (h / 4));
     }
     return check_launch("moe_permute");
+}
+
+extern "C" int moe_permute_weights(const float *topk_w, int64_t T, int k, const int32_t *row_of, float *row_w,
+                                   void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(T >= 0 && k > 0, MOE_ERR_INVALID_ARG, "moe_permute_weights: bad sizes");
+    MOE_CHECK_ARG(T == 0 || (topk_w && row_of && row_w), MOE_ERR_INVALID_ARG,
+                  "moe_permute_weights: null required pointer");
+    MOE_CHECK_ARG(T * k < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "moe_permute_weights: T*k must be < 2^31");
+    if (T == 0) return MOE_OK;
+    const int64_t P = T * k;
+    hipLaunchKernelGGL(permute_weights_kernel, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0,
+                       as_stream(stream), topk_w, row_of, P, row_w);
+    return check_launch("moe_permute_weights");
+}
+
+extern "C" int moe_permute_weights_bwd(const float *grad_row_w, int64_t T, int k, const int32_t *row_of,
+                                       float *grad_topk_w, void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(T >= 0 && k > 0, MOE_ERR_INVALID_ARG, "moe_permute_weights_bwd: bad sizes");
+    MOE_CHECK_ARG(T == 0 || (grad_row_w && row_of && grad_topk_w), MOE_ERR_INVALID_ARG,
+                  "moe_permute_weights_bwd: null required pointer");
+    MOE_CHECK_ARG(T * k < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "moe_permute_weights_bwd: T*k must be < 2^31");
+    if (T == 0) return MOE_OK;
+    const int64_t P = T * k;
+    hipLaunchKernelGGL(permute_weights_bwd_kernel, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0,
+                       as_stream(stream), grad_row_w, row_of, P, grad_topk_w);
+    return check_launch("moe_permute_weights_bwd");
 }

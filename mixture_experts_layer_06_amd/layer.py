@@ -28,13 +28,22 @@ def _timed(timers, name, fn):
 
 
 def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False,
-            timers: dict | None = None, router_losses: bool = False):
+            timers: dict | None = None, router_losses: bool = False,
+            memory_efficient: bool = False, recompute: bool = False):
     """One forward pass. ``inp`` holds device tensors named as in
     ``workloads.make_inputs``. Returns a dict with ``out`` and the
     intermediate results of every stage. With ``timers``, the grouped FFN
     call is bracketed by HIP events (key "grouped_ffn"). With
     ``router_losses``, also ``losses`` = {aux, z} (load-balancing loss and
-    router z-loss, "emerging-techniques-moe-training", section 3)."""
+    router z-loss, "emerging-techniques-moe-training", section 3).
+
+    ``memory_efficient`` ("Scalable Training of Mixture-of-Experts Models
+    with Megatron Core", section 4.1.1; experts without output bias): the
+    routing weight scales the activation before the second projection and the
+    combine is an unweighted sum; the backward then needs neither the expert
+    outputs nor the activation, which are not kept. ``recompute`` (section
+    4.1.2) alone drops only the activation, which the backward rebuilds from
+    the pre-activations."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
@@ -44,12 +53,18 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     gather = not keep_for_backward
     p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=not gather)
     has_sh = inp.get("w1_sh") is not None
+    row_w = B.moe_permute_weights(r["topk_w"], p["row_of"]) if memory_efficient else None
     f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn(
         x if gather else p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"),
         b2=inp.get("b2"), x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"),
-        keep_gu=keep_for_backward and act == "swiglu", gather_rows=p["sorted_token"] if gather else None))
-    out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"], y_sh=f["y_sh"])
-    res = dict(out=out)
+        keep_gu=keep_for_backward and act == "swiglu", gather_rows=p["sorted_token"] if gather else None,
+        row_w=row_w))
+    out = B.moe_unpermute(f["y"], p["row_of"], None if memory_efficient else r["topk_w"], y_sh=f["y_sh"])
+    if memory_efficient or recompute:
+        f["act"] = None          # rebuilt from gu in the backward
+    if memory_efficient:
+        f["y"] = None            # the backward needs no expert output
+    res = dict(out=out, row_w=row_w, recompute=memory_efficient or recompute)
     if router_losses:
         res["losses"], _ = B.moe_router_losses(r["logits"], r["counts"], k)
     res.update(r)
@@ -66,9 +81,19 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
     logits. With ``timers``, the grouped FFN backward call is bracketed by
     HIP events (key "grouped_ffn_bwd")."""
     E = inp["w_gate"].shape[0]
-    grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
-    g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd(
-        grad_y, fwd["x_perm"], fwd["act"], fwd["gu"], fwd["offsets"], inp["w1"], inp["w2"], act))
+    row_w = fwd.get("row_w")
+    if row_w is not None:
+        grad_y, _ = B.moe_unpermute_bwd(grad_out, None, fwd["row_of"], None)
+    else:
+        grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
+    if fwd.get("recompute"):
+        g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd_recompute(
+            grad_y, fwd["x_perm"], fwd["gu"], fwd["offsets"], inp["w1"], inp["w2"], act, row_w=row_w))
+    else:
+        g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd(
+            grad_y, fwd["x_perm"], fwd["act"], fwd["gu"], fwd["offsets"], inp["w1"], inp["w2"], act))
+    if row_w is not None:
+        grad_w = B.moe_permute_weights_bwd(g["grad_row_w"], fwd["row_of"])
     r = B.moe_route_bwd(inp["x"], E, fwd["topk_idx"], fwd["topk_w"], grad_w, fwd["offsets"],
                         fwd["sorted_token"], score=score, logits=fwd.get("logits"),
                         want_b_grad=inp.get("b_gate") is not None)

@@ -128,6 +128,21 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert L.moe_router_losses(dummy, dummy, 1000, 8, 2, dummy, None, dummy, 16, None) == 3
     assert L.moe_router_losses_bwd(None, dummy, 16, 8, 2, 1.0, 1.0, dummy, None) == 1
     assert L.moe_router_losses_bwd(dummy, dummy, -1, 8, 2, 1.0, 1.0, dummy, None) == 1
+    # weighted grouped FFN without row weights; recompute without its workspace or with
+    # row_w but no grad_row_w; permute weights with a negative size
+    rc = L.moe_grouped_ffn_weighted(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, 0,
+                                    None, None, None, dummy, None, dummy, None, None, 0, None)
+    assert rc == 1
+    rc = L.moe_grouped_ffn_bwd_recompute(dummy, dummy, dummy, 1, 64, 128, 128, 4, dummy, 1, dummy, dummy, None,
+                                         dummy, dummy, dummy, dummy, None, None, 0, None)
+    assert rc == 3
+    rc = L.moe_grouped_ffn_bwd_recompute(dummy, dummy, dummy, 1, 64, 128, 128, 4, dummy, 1, dummy, dummy, dummy,
+                                         dummy, dummy, dummy, dummy, None, dummy, 1 << 30, None)
+    assert rc == 1
+    assert L.moe_permute_weights(dummy, -1, 2, dummy, dummy, None) == 1
+    assert L.moe_permute_weights_bwd(None, 16, 2, dummy, dummy, None) == 1
+    # unweighted combine backward still needs its output
+    assert L.moe_unpermute_bwd(dummy, None, 1, 16, 64, 2, dummy, None, None, None, None) == 1
     # dense router backward: bad dtype, h % 64, misaligned pointer, workspace
     rc = L.moe_router_dense_bwd(dummy, dummy, 7, 16, 64, 8, dummy, dummy, None, None, dummy, 1 << 30, None)
     assert rc == 1
@@ -153,6 +168,16 @@ def test_router_loss_workspace_sizes(lib):
     # one fp32 [E,h] partial per 256 tokens
     assert L.moe_router_dense_bwd_workspace_size(300, 128, 8) == 2 * 8 * 128 * 4
     assert L.moe_router_dense_bwd_workspace_size(0, 128, 8) == 0
+
+
+def test_recompute_workspace_size(lib):
+    b = _binding()
+    L = b.lib()
+    # the rebuilt activation (bf16, rounded up to 256 bytes) plus, with row
+    # weights, one fp32 partial per row and 256-column tile
+    assert L.moe_grouped_ffn_bwd_recompute_workspace_size(100, 1536, 0) == 307200
+    assert L.moe_grouped_ffn_bwd_recompute_workspace_size(100, 1536, 1) == 307200 + 100 * 6 * 4
+    assert L.moe_grouped_ffn_bwd_recompute_workspace_size(3, 64, 0) == 512
 
 
 def test_binding_refuses_host_tensors():

@@ -1,0 +1,225 @@
+"""GPU parity of the memory-efficient permutation and of the activation
+recompute ("Scalable Training of Mixture-of-Experts Models with Megatron
+Core", sections 4.1.1 and 4.1.2), through the C ABI, against the oracle.
+
+For experts without an output bias, applying the routing weight to the
+activation before the second projection gives the same layer output and the
+same gradients as applying it to the expert output (the oracle's identity
+pin), so the oracle's forward and backward are the reference for both forms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_06_amd import workloads as wl
+from parity import TOL, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
+
+pytestmark = pytest.mark.gpu
+
+FWD_CASES = {
+    "tiny_fp32_gelu": wl.CONFIGS[1],
+    "mixtral_small": wl.small_variant(wl.CONFIGS[2], T=600, h=256, F=384),
+    "qwen3_small": wl.small_variant(wl.CONFIGS[3], T=1000, h=512, F=192),
+    "deepseek_small_shared": wl.small_variant(wl.CONFIGS[4], T=520, h=448, F=128),
+    "imbalanced_small": wl.small_variant(wl.CONFIGS[5], T=300, h=256, F=128, E=32),
+}
+
+
+def _inputs(cfg, with_grad_out=False):
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=with_grad_out)
+    inp["b2"] = None    # the weight-before-W2 form needs experts without output bias
+    return inp
+
+
+def _oracle_forward(cfg, inp):
+    o = oracle_inputs(inp)
+    return oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                          b_gate=o["b_gate"], sel_bias=o["sel_bias"], b1=o["b1"], b2=None,
+                          w1_sh=o["w1_sh"], w2_sh=o["w2_sh"])
+
+
+@pytest.mark.parametrize("name", list(FWD_CASES))
+@pytest.mark.parametrize("train", [False, True])
+def test_weighted_forward_parity(moe_lib, name, train):
+    """Output of the folded forward (inference gathers rows; training keeps
+    x_perm) against the oracle; expert outputs and activations not kept."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = FWD_CASES[name]
+    print("case folded forward", name, "train" if train else "inference", flush=True)
+    inp = _inputs(cfg)
+    dinp = to_device(inp)
+    g = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, memory_efficient=True)
+    plain = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=train)
+    torch.cuda.synchronize()
+    ref = _oracle_forward(cfg, inp)
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert g["y"] is None and g["act"] is None
+    tol = TOL[cfg.dtype]
+    err = rel_err(to_np32(g["out"]), ref["out"])
+    err_plain = rel_err(to_np32(plain["out"]), ref["out"])
+    print("folded %.3g, weight after the expert %.3g" % (err, err_plain), flush=True)
+    assert err <= tol, err
+
+
+def test_permute_weights_roundtrip(moe_lib):
+    """row_w[row_of[t,j]] = topk_w[t,j] and the backward gather inverts it,
+    bit for bit; the unweighted combine equals the weighted one with weights
+    1 bit for bit."""
+    cfg = wl.small_variant(wl.CONFIGS[3], T=777, h=256, F=128)
+    inp = to_device(wl.make_inputs(cfg, device="cpu", router_only=True))
+    r = moe_lib.moe_route(inp["x"], inp["w_gate"], cfg.k, cfg.score)
+    p = moe_lib.moe_permute(inp["x"], r["topk_idx"], cfg.E)
+    row_w = moe_lib.moe_permute_weights(r["topk_w"], p["row_of"])
+    ro = p["row_of"].long()
+    assert torch.equal(row_w[ro], r["topk_w"])
+    back = moe_lib.moe_permute_weights_bwd(row_w, p["row_of"])
+    assert torch.equal(back, r["topk_w"])
+    y = p["x_perm"]
+    ones = torch.ones_like(r["topk_w"])
+    assert torch.equal(moe_lib.moe_unpermute(y, p["row_of"], None), moe_lib.moe_unpermute(y, p["row_of"], ones))
+    gy, gw = moe_lib.moe_unpermute_bwd(inp["x"], None, p["row_of"], None)
+    assert gw is None
+    assert torch.equal(gy[ro.reshape(-1)], inp["x"].repeat_interleave(cfg.k, dim=0))
+
+
+def _fwd_bwd(cfg, dinp, **kw):
+    from mixture_experts_layer_06_amd import layer
+    f = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True, **kw)
+    g = layer.backward(dinp, f, dinp["grad_out"], cfg.k, cfg.score, cfg.act)
+    torch.cuda.synchronize()
+    return f, g
+
+
+def _check_grads(cfg, f, g, ref, experts):
+    """The layer's gradients (input, router weight, expert weights) to the
+    tolerance under the row-wise measure; the intermediate routing-weight and
+    selected-logit gradients per tensor, their row-wise errors reported.
+    Folded, dL/dp is a dot product of the activation gradient with the
+    activation rebuilt from the bf16 pre-activations, so on short rows (F =
+    192) it carries about twice the rounding of <dL/dout, y> with a kept y, and
+    the selected-logit gradient is a centred difference of those values."""
+    tol = TOL[cfg.dtype]
+    err = {"grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
+           "grad_topk_w": rel_err_tensor(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"]),
+           "grad_logits_sel": rel_err_tensor(g["grad_logits_sel"].cpu().numpy(), ref["d_logits_sel"]),
+           "grad_w_gate": rel_err_tensor(g["grad_w_gate"].cpu().numpy(), ref["dw_gate"])}
+    rowwise = {"grad_topk_w": rel_err(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"]),
+               "grad_logits_sel": rel_err(g["grad_logits_sel"].cpu().numpy(), ref["d_logits_sel"])}
+    print("row-wise (reported only):", {k: float("%.3g" % v) for k, v in rowwise.items()}, flush=True)
+    counts = f["counts"].cpu().numpy()
+    for e in experts:
+        if counts[e] == 0:
+            assert not g["grad_w1"][e].any() and not g["grad_w2"][e].any()
+            continue
+        err["grad_w1[%d]" % e] = rel_err_tensor(g["grad_w1"][e].cpu().numpy(), ref["dw1"][e])
+        err["grad_w2[%d]" % e] = rel_err_tensor(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e])
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    bad = {k: v for k, v in err.items() if not v <= tol}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("case", ["imbalanced_softmax", "sigmoid_ragged"])
+@pytest.mark.parametrize("mode", ["memory_efficient", "recompute"])
+def test_backward_parity(moe_lib, case, mode):
+    if case == "sigmoid_ragged":
+        cfg = wl.small_variant(wl.CONFIGS[5], T=333, h=192, F=192, E=16, k=4).with_shape(
+            score="sigmoid", skew=False, gate_bias=False)
+    else:
+        cfg = wl.small_variant(wl.CONFIGS[5], T=300, h=256, F=128, E=32)
+    print("case backward", case, mode, flush=True)
+    inp = _inputs(cfg, with_grad_out=True)
+    dinp = to_device(inp)
+    f, g = _fwd_bwd(cfg, dinp, **{mode: True})
+    o = oracle_inputs(inp)
+    ref = oracle.backward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                          to_np32(inp["grad_out"]), b_gate=o["b_gate"])
+    assert np.array_equal(f["topk_idx"].cpu().numpy(), ref_topk(cfg, o))
+    _check_grads(cfg, f, g, ref, range(cfg.E))
+    _, g0 = _fwd_bwd(cfg, dinp)
+    if mode == "recompute":
+        # the activation is rebuilt, everything upstream of it is unchanged
+        for key in ("grad_x", "grad_w1", "grad_topk_w", "grad_w_gate"):
+            assert torch.equal(g[key], g0[key]), key
+    else:
+        print("weight after the expert, row-wise (reported only):",
+              {k: float("%.3g" % rel_err(g0[k].cpu().numpy(), ref[r])) for k, r in
+               (("grad_topk_w", "d_topk_w"), ("grad_logits_sel", "d_logits_sel"))}, flush=True)
+
+
+def ref_topk(cfg, o):
+    return oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score, o["b_gate"], o["sel_bias"])["topk_idx"]
+
+
+def test_backward_slice_of_imbalanced_workload(moe_lib):
+    """The first 64 tokens of the imbalanced workload with its full weights,
+    folded forward and backward; gradients of the experts those tokens reach
+    (and of a few they do not)."""
+    cfg = wl.CONFIGS[5]
+    print("case T=64 slice, memory-efficient", flush=True)
+    full = wl.make_inputs(cfg, device="cuda")
+    inp = wl.slice_tokens(full, 64)
+    sub = cfg.with_shape(T=64)
+    f, g = _fwd_bwd(sub, inp, memory_efficient=True)
+    counts = f["counts"].cpu().numpy()
+    live = [int(e) for e in np.nonzero(counts)[0]][:6]
+    dead = [int(e) for e in np.nonzero(counts == 0)[0]][:3]
+
+    class Lazy:
+        def __init__(self, t):
+            self.t = t
+            self.shape = tuple(t.shape)
+
+        def __getitem__(self, e):
+            return self.t[e].float().cpu().numpy()
+
+    ref = oracle.backward(to_np32(inp["x"]), to_np32(inp["w_gate"]), Lazy(inp["w1"]), Lazy(inp["w2"]),
+                          cfg.k, cfg.score, cfg.act, to_np32(inp["grad_out"]),
+                          b_gate=to_np32(inp["b_gate"]), experts=live + dead)
+    _check_grads(sub, f, g, ref, live + dead)
+
+
+def test_full_size_step_sampled(moe_lib):
+    """Full imbalanced step (T=8192), folded and recomputing: input
+    gradients and routing-weight gradients of sampled tokens, and weight
+    gradients of the two most lightly loaded experts computed from all their
+    tokens, against the oracle; empty experts get exact zeros; two runs are
+    bitwise equal; neither the expert outputs nor the activation are kept."""
+    cfg = wl.CONFIGS[5]
+    print("case full size, memory-efficient", flush=True)
+    inp = wl.make_inputs(cfg, device="cuda")
+    f, g = _fwd_bwd(cfg, inp, memory_efficient=True)
+    assert f["y"] is None and f["act"] is None
+    counts = f["counts"].cpu().numpy()
+    topk = f["topk_idx"].cpu().numpy()
+    for e in np.nonzero(counts == 0)[0]:
+        assert not g["grad_w1"][int(e)].any() and not g["grad_w2"][int(e)].any()
+    order = np.argsort(counts, kind="stable")
+    light = [int(e) for e in order if counts[e] > 0][:2]
+    tok = sorted(set(np.nonzero(np.isin(topk, light).any(axis=1))[0].tolist())
+                 | set(np.linspace(0, cfg.T - 1, 6).astype(int).tolist()))
+    ti = torch.as_tensor(np.asarray(tok, dtype=np.int64), device="cuda")
+
+    class Lazy:
+        def __init__(self, t):
+            self.t = t
+            self.shape = tuple(t.shape)
+
+        def __getitem__(self, e):
+            return self.t[e].float().cpu().numpy()
+
+    ref = oracle.backward(to_np32(inp["x"][ti]), to_np32(inp["w_gate"]), Lazy(inp["w1"]), Lazy(inp["w2"]),
+                          cfg.k, cfg.score, cfg.act, to_np32(inp["grad_out"][ti]),
+                          b_gate=to_np32(inp["b_gate"]), experts=light)
+    tol = TOL[cfg.dtype]
+    err = {"grad_x(sampled)": rel_err(to_np32(g["grad_x"][ti]), ref["dx"]),
+           "grad_topk_w(sampled)": rel_err_tensor(g["grad_topk_w"][ti].cpu().numpy(), ref["d_topk_w"])}
+    for e in light:
+        err["grad_w1[%d]" % e] = rel_err_tensor(g["grad_w1"][e].cpu().numpy(), ref["dw1"][e])
+        err["grad_w2[%d]" % e] = rel_err_tensor(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e])
+        err["grad_w_gate[%d]" % e] = rel_err_tensor(g["grad_w_gate"][e].cpu().numpy(), ref["dw_gate"][e])
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    assert all(v <= tol for v in err.values()), err
+    _, g2 = _fwd_bwd(cfg, inp, memory_efficient=True)
+    for key in ("grad_x", "grad_w1", "grad_w2", "grad_w_gate", "grad_topk_w"):
+        assert torch.equal(g[key], g2[key]), key

@@ -7,8 +7,12 @@ library and never imports it.
 from .moe import (  # noqa: F401
     backward,
     build,
+    capacity_keep,
     combine,
     exp_c,
+    expert_capacity,
+    expert_choice,
+    expert_choice_forward,
     expert_backward,
     expert_fraction,
     expert_forward,

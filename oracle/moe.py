@@ -50,6 +50,15 @@ Definitions followed (page titles are the pages' own):
   constant function of the logits, so it carries no gradient; an empty batch
   (T = 0) gives 0 for both.
 
+* Capacity and token dropping ("emerging-techniques-moe-training", Capacity
+  Factor Tuning and the DeepSpeed config): capacity = int(T*k/E * factor),
+  at least min_capacity; pairs past an expert's capacity, in ascending token
+  order, are dropped and the kept pairs keep their weights (the pages say
+  neither which pairs go nor whether weights are renormalised).
+* Expert-choice routing (same page, Routing Mechanisms): each expert takes
+  the `capacity` tokens with the largest logits (ties: lower token index);
+  a chosen pair is weighted by the token's softmax gate probability.
+
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, invariants, brute force and finite differences; the
 absolute output values of the four model-shaped workloads rest on those pins
@@ -274,17 +283,45 @@ def expert_forward(xe, w1e, w2e, act: str, b1e=None, b2e=None):
     return y, dict(a=a, hid=hid)
 
 
+def expert_capacity(T: int, E: int, k: int, capacity_factor: float, min_capacity: int = 4) -> int:
+    """Tokens an expert may take ("emerging-techniques-moe-training",
+    Capacity Factor Tuning: int(tokens / experts * capacity_factor); the
+    DeepSpeed config on that page adds min_capacity 4). Reading: with top-k
+    routing the tokens counted are the T*k routing slots, so a factor of 1
+    is the mean load and 1.25 a 25 % buffer, as the page describes it."""
+    return max(int(min_capacity), int((T * k / E) * capacity_factor))
+
+
+def capacity_keep(topk_idx, E: int, capacity: int) -> np.ndarray:
+    """keep[t,j]: pair (t, topk_idx[t,j]) is among the first `capacity`
+    pairs of its expert in ascending token order ("drop_tokens": pairs past
+    an expert's capacity are dropped; the pages do not say which, the
+    plainest reading is arrival order)."""
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    keep = np.zeros((T, k), dtype=bool)
+    for e in range(E):
+        tok, slot = np.nonzero(idx == e)          # ascending t
+        keep[tok[:capacity], slot[:capacity]] = True
+    return keep
+
+
 def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bias=None,
-            b1=None, b2=None, w1_sh=None, w2_sh=None, tokens=None, routing=None):
+            b1=None, b2=None, w1_sh=None, w2_sh=None, tokens=None, routing=None, capacity=None):
     """Whole layer in fp64 (router fp32). All arrays numpy; x [T,h].
 
     ``tokens`` restricts the evaluation to those token indices (routing is
-    per-token, so this equals the full computation on those rows). Returns
-    the route dict plus out [n,h] fp64, y_pair [n,k,h] (expert outputs per
-    selected pair) and y_shared [n,h] or None.
+    per-token, so this equals the full computation on those rows; not with
+    ``capacity``, which depends on every token). With ``capacity``, pairs
+    past an expert's capacity (``capacity_keep``) contribute nothing; the
+    kept pairs keep their weights. Returns the route dict plus out [n,h]
+    fp64, y_pair [n,k,h] (expert outputs per selected pair, zero for dropped
+    pairs), keep [n,k] and y_shared [n,h] or None.
     """
     x = np.asarray(x, dtype=np.float32)
     if tokens is not None:
+        if capacity is not None:
+            raise ValueError("capacity depends on every token; evaluate all of them")
         tokens = np.asarray(tokens, dtype=np.int64)
         x = x[tokens]
     if routing is None:
@@ -297,8 +334,9 @@ def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bi
     y_pair = np.zeros((n, k, h), dtype=np.float64)
     # Per expert, as in the pages' loop over experts: gather the tokens that
     # chose it, run the expert, weight and add back.
+    keep = np.ones(topk_idx.shape, dtype=bool) if capacity is None else capacity_keep(topk_idx, E, capacity)
     for e in range(E):
-        tok, slot = np.nonzero(topk_idx == e)
+        tok, slot = np.nonzero((topk_idx == e) & keep)
         if tok.size == 0:
             continue
         y, _ = expert_forward(x[tok], w1[e], w2[e], act,
@@ -311,8 +349,52 @@ def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bi
         y_sh, _ = expert_forward(x, w1_sh, w2_sh, act)
         out += y_sh
     res = dict(routing)
-    res.update(out=out, y_pair=y_pair, y_shared=y_sh)
+    res.update(out=out, y_pair=y_pair, y_shared=y_sh, keep=keep)
     return res
+
+
+def expert_choice(logits, capacity: int):
+    """Expert-choice selection ("emerging-techniques-moe-training", Routing
+    Mechanisms, Expert Choice Routing: the router's scores transposed to
+    [experts, tokens], then each expert takes its top-`capacity` tokens).
+    Order: logit descending, then token index ascending. Returns chosen
+    [E, capacity] (each expert's tokens in ascending token order) and the
+    weights [E, capacity] = softmax over all E logits of the token, at the
+    choosing expert (the page gives no weights; the gate probability is the
+    weight used everywhere else on it)."""
+    l = np.asarray(logits, dtype=np.float32)
+    T, E = l.shape
+    C = int(capacity)
+    chosen = np.zeros((E, C), dtype=np.int64)
+    t_idx = np.arange(T)
+    for e in range(E):
+        order = np.lexsort((t_idx, -l[:, e].astype(np.float64)))
+        chosen[e] = np.sort(order[:C])
+    p, _ = _log_softmax_parts(l)
+    weights = np.take_along_axis(p.T, chosen, axis=1)
+    return chosen, weights
+
+
+def expert_choice_forward(x, w_gate, w1, w2, capacity: int, act: str, b_gate=None, b1=None, b2=None,
+                          logits=None):
+    """out[t] = sum over the experts that chose token t (ascending) of
+    softmax(l_t)_e * E_e(x_t), fp64 (logits fp32 in gate order G). A token
+    no expert chose gets 0."""
+    x = np.asarray(x, dtype=np.float32)
+    if logits is None:
+        logits = gate_logits(x, w_gate, b_gate)
+    chosen, weights = expert_choice(logits, capacity)
+    T, h = x.shape
+    out = np.zeros((T, h), dtype=np.float64)
+    x64 = x.astype(np.float64)
+    for e in range(chosen.shape[0]):
+        tok = chosen[e]
+        if tok.size == 0:
+            continue
+        y, _ = expert_forward(x64[tok], w1[e], w2[e], act,
+                              None if b1 is None else b1[e], None if b2 is None else b2[e])
+        np.add.at(out, tok, weights[e][:, None] * y)
+    return dict(logits=logits, chosen=chosen, weights=weights, out=out)
 
 
 def combine(y_perm, row_of, topk_w, y_shared=None):
@@ -457,7 +539,7 @@ def router_grads(x, w_gate, dlogits):
 
 
 def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
-             b1=None, b2=None, routing=None, experts=None, coef_aux=0.0, coef_z=0.0):
+             b1=None, b2=None, routing=None, experts=None, coef_aux=0.0, coef_z=0.0, capacity=None):
     """Gradients of L = sum(grad_out * out) + coef_aux * aux + coef_z * z
     for the routed layer (no shared expert); aux and z as in
     ``router_losses``. Top-k indices carry no gradient.
@@ -465,6 +547,9 @@ def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=N
     Returns dx [T,h], d_topk_w [T,k], d_logits_sel [T,k], dw_gate [E,h],
     db_gate [E], and dicts dw1/dw2/db1/db2 keyed by expert (all experts, or
     those listed in ``experts``; an expert with no tokens gets exact zeros).
+    With ``capacity``, dropped pairs (``capacity_keep``) reach no expert and
+    get d_topk_w = 0; the router's gradient still runs over every selected
+    pair, since the kept weights depend on all selected logits.
     """
     x = np.asarray(x, dtype=np.float32)
     T, h = x.shape
@@ -479,8 +564,9 @@ def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=N
     dx = np.zeros((T, h), dtype=np.float64)
     d_topk_w = np.zeros((T, k), dtype=np.float64)
     dw1, dw2, db1, db2 = {}, {}, {}, {}
+    keep = np.ones(topk_idx.shape, dtype=bool) if capacity is None else capacity_keep(topk_idx, E, capacity)
     for e in range(E):
-        tok, slot = np.nonzero(topk_idx == e)
+        tok, slot = np.nonzero((topk_idx == e) & keep)
         n1F = w1.shape[1]
         if tok.size == 0:
             if e in want:
@@ -519,7 +605,7 @@ def backward(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=N
 # ----------------------------------------------------- fp64 forward for FD
 
 def loss_fp64(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
-              b1=None, b2=None, expect_idx=None, coef_aux=0.0, coef_z=0.0):
+              b1=None, b2=None, expect_idx=None, coef_aux=0.0, coef_z=0.0, capacity=None):
     """L = sum(grad_out * out) + coef_aux * aux + coef_z * z with every
     step, logits included, in fp64.
 
@@ -547,8 +633,9 @@ def loss_fp64(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=
     sel = np.take_along_axis(logits, topk_idx, axis=1)
     w = routing_weights(sel, logits, score)
     out = np.zeros_like(x)
+    keep = np.ones(topk_idx.shape, dtype=bool) if capacity is None else capacity_keep(topk_idx, E, capacity)
     for e in range(w1.shape[0]):
-        tok, slot = np.nonzero(topk_idx == e)
+        tok, slot = np.nonzero((topk_idx == e) & keep)
         if tok.size == 0:
             continue
         y, _ = expert_forward(x[tok], w1[e], w2[e], act,

@@ -62,6 +62,10 @@ def parse():
     p.add_argument("--memory-efficient", action="store_true",
                    help="apply the routing weight before the second projection (experts without "
                         "output bias) and rebuild the activation in the backward")
+    p.add_argument("--capacity-factor", type=float, default=None,
+                   help="drop pairs past int(T*k/E * factor) per expert (min 4), in token order")
+    p.add_argument("--expert-choice", action="store_true",
+                   help="expert-choice routing, capacity T*k/E per expert (forward only)")
     p.add_argument("--router-losses", action="store_true",
                    help="add the load-balancing loss (coefficient 1e-2) and router z-loss "
                         "(1e-3) to a training step, and time their kernels as stages")
@@ -326,9 +330,19 @@ def main():
             sys.exit("--memory-efficient needs experts without output bias")
         inp["b2"] = None
 
+    cap = None
+    if args.capacity_factor is not None:
+        cap = layer.capacity_from_factor(cfg.T, cfg.E, cfg.k, args.capacity_factor)
+    if args.expert_choice:
+        if train:
+            sys.exit("--expert-choice runs the forward only; pick a forward workload")
+        ec_cap = cfg.T * cfg.k // cfg.E
+
     def step(timers=None):
+        if args.expert_choice:
+            return layer.forward_expert_choice(inp, ec_cap, cfg.act, timers=timers)
         f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers,
-                          router_losses=losses, memory_efficient=meff)
+                          router_losses=losses, memory_efficient=meff, capacity=cap)
         if train:
             layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers, **coefs)
         return f
@@ -343,7 +357,16 @@ def main():
             res = step(timers)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
-    counts = res["counts"].cpu().numpy()
+    if args.expert_choice:
+        counts = np.full(cfg.E, ec_cap)
+    else:
+        counts = res["counts"].cpu().numpy()
+    if cap is not None:
+        # only the kept pairs reach an expert
+        kept = int(res["kept"]["offsets"][-1].item())
+        dropped_frac = 1.0 - kept / cfg.P
+        nmat = 3 if cfg.act == "swiglu" else 2
+        flops -= (cfg.P - kept) * nmat * 2.0 * cfg.h * cfg.F * (3.0 if train else 1.0)
     live = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
             for name, pairs in timers.items()}
 
@@ -365,11 +388,15 @@ def main():
                    "shared_experts": cfg.n_shared,
                    "step": "forward + backward" if train else "forward",
                    "router_losses": {"coef_aux": COEF_AUX, "coef_z": COEF_Z} if losses else None,
-                   "memory_efficient_permutation": meff},
+                   "memory_efficient_permutation": meff,
+                   "routing": ("expert_choice, capacity %d per expert" % ec_cap if args.expert_choice else
+                               "top-k, capacity %d per expert (factor %g)" % (cap, args.capacity_factor)
+                               if cap is not None else "top-k, dropless")},
         "tokens_per_s": cfg.T / dt,
         "frac_of_bf16_peak": flops / dt / 1e12 / PEAK_BF16_TFLOPS,
         "active_gflop_per_step": flops / 1e9,
         "expert_load": {"min": int(counts.min()), "max": int(counts.max())},
+        "dropped_pair_fraction": dropped_frac if cap is not None else None,
         # activations the forward keeps for the backward (training step only)
         "saved_for_backward_bytes": int(sum(res[n].numel() * res[n].element_size()
                                             for n in ("x_perm", "gu", "act", "y", "row_w", "logits")
@@ -401,7 +428,8 @@ def main():
     if rec:
         out["roofline"]["traffic_note"] = rec["note"]
 
-    if not args.no_stages:
+    # the stage-by-stage timings cover the top-k dropless chain
+    if not args.no_stages and not args.expert_choice and cap is None:
         stream = torch.cuda.current_stream(dev)
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         E = cfg.E

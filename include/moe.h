@@ -222,6 +222,62 @@ int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int k,
                   const int32_t *row_of, const float *topk_w, const void *y_sh, void *out,
                   void *stream);
 
+/* ------------------------------------------------------- Routing variants
+ * "emerging-techniques-moe-training".
+ *
+ * Capacity-factor token dropping (Capacity Factor Tuning; the DeepSpeed MoE
+ * config's drop_tokens): expert e takes at most `capacity` of its pairs, the
+ * first in ascending token order (the order of moe_permute's segments); the
+ * other pairs are dropped: they reach no expert, add nothing to the output
+ * and keep no row; the kept pairs keep their routing weights. The page's
+ * capacity is int(tokens / experts * capacity_factor) (e.g. with the T*k
+ * routing slots as tokens and a floor of min_capacity); the caller passes
+ * the resulting integer. From moe_permute's topk_idx, offsets and row_of:
+ *   offsets_kept      [E+1] int32  segment starts of the kept rows
+ *   row_of_kept       [T,k] int32  kept row of each pair, -1 if dropped
+ *   sorted_token_kept [T*k] int32  token of each kept row (rows past
+ *                                  offsets_kept[E] are not written)
+ *   x_perm_kept [T*k,h] dtype|NULL x rows in kept-row order (needs x)
+ * The forward then runs moe_grouped_ffn on offsets_kept (with x_perm_kept,
+ * or x and gather_rows = sorted_token_kept) and moe_unpermute with
+ * row_of_kept (rows of -1 are skipped). In the backward, moe_unpermute_bwd,
+ * moe_grouped_ffn_bwd and moe_permute_bwd take the kept arrays, while
+ * moe_route_bwd keeps the full offsets and sorted_token: every selected
+ * pair's logit gradient reaches the router (a dropped pair's routing-weight
+ * gradient is 0, the kept weights still depend on its logit). */
+int moe_capacity_drop(const int32_t *topk_idx, const int32_t *offsets, const int32_t *row_of,
+                      const void *x, int dtype, int64_t T, int64_t h, int E, int k, int capacity,
+                      int32_t *offsets_kept, int32_t *row_of_kept, int32_t *sorted_token_kept,
+                      void *x_perm_kept, void *stream);
+
+/* Expert-choice routing (Routing Mechanisms, Expert Choice Routing): with
+ * the router's logits [T,E] fp32 (moe_route's logits output), expert e takes
+ * the `capacity` tokens with the largest logits l[t,e] (ties: lower token
+ * index; -0 = +0), 1 <= capacity <= T. Outputs:
+ *   offsets      [E+1] int32       e * capacity
+ *   sorted_token [E*capacity] int32 chosen tokens, expert-major, ascending
+ *                                  within an expert
+ *   row_w        [E*capacity] fp32 weight of each chosen pair: softmax over
+ *                                  all E logits of the token, at e
+ *   token_rows   [T,E] int32       rows of token t in ascending expert order
+ *                                  (first token_nrows[t] entries written)
+ *   token_nrows  [T] int32         number of experts that chose token t
+ * The forward then runs moe_grouped_ffn_weighted(x, gather_rows =
+ * sorted_token, P = E*capacity, row_w) and moe_combine_rows. Workspace:
+ * moe_expert_choice_workspace_size(T,E) bytes, 16-byte aligned. */
+size_t moe_expert_choice_workspace_size(int64_t T, int E);
+int moe_expert_choice(const float *logits, int64_t T, int E, int capacity, int32_t *offsets,
+                      int32_t *sorted_token, float *row_w, int32_t *token_rows,
+                      int32_t *token_nrows, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Combine by per-token row lists: out[t] = sum over i < token_nrows[t]
+ * (ascending) of y[token_rows[t*E + i]] (+ y_sh[t]), fp32, rounded once to
+ * dtype. y [P,h] (already weighted), out [T,h]. */
+int moe_combine_rows(const void *y, int dtype, int64_t T, int64_t h, int E, int64_t P,
+                     const int32_t *token_rows, const int32_t *token_nrows, const void *y_sh,
+                     void *out, void *stream);
+
 /* =============================== backward ===============================
  * Gradients of L = sum(grad_out * out) (grad_out = dL/dout). Top-k indices
  * carry no gradient. Order of use: moe_unpermute_bwd, moe_grouped_ffn_bwd,

@@ -60,6 +60,11 @@ _SIGS = {
     "moe_permute_weights": ([_vp, _i64, _int, _vp, _vp, _vp], _int),
     "moe_permute_weights_bwd": ([_vp, _i64, _int, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd_recompute_workspace_size": ([_i64, _i64, _int], _sz),
+    "moe_capacity_drop": ([_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp],
+                          _int),
+    "moe_expert_choice_workspace_size": ([_i64, _int], _sz),
+    "moe_expert_choice": ([_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_combine_rows": ([_vp, _int, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd_recompute": ([_vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_router_dense_bwd": ([_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -471,3 +476,65 @@ def moe_router_dense_bwd(x, w_gate, grad_logits, grad_w_gate=None, grad_b_gate=N
                                     _ptr(grad_w_gate), _ptr(grad_b_gate), _ptr(grad_x), _ptr(ws),
                                     ws.numel(), _stream(x))
     _check(rc, "moe_router_dense_bwd")
+
+
+
+# -------------------------------------------------------- routing variants
+
+def moe_capacity_drop(topk_idx, offsets, row_of, capacity: int, x=None, with_x_perm: bool = False):
+    """Capacity-limited permutation from moe_permute's outputs: offsets_kept,
+    row_of_kept (-1 = dropped), sorted_token_kept and optionally x_perm_kept."""
+    _req(topk_idx, "topk_idx", dtype=torch.int32)
+    dev = topk_idx.device
+    T, k = topk_idx.shape
+    E = offsets.numel() - 1
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(row_of, "row_of", dtype=torch.int32, shape=(T, k), device=dev)
+    h, dt = 64, torch.bfloat16
+    if with_x_perm:
+        _req(x, "x", shape=(T, x.shape[1]), device=dev)
+        h, dt = x.shape[1], x.dtype
+    out = dict(offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               row_of=torch.empty((T, k), dtype=torch.int32, device=dev),
+               sorted_token=torch.empty((T * k,), dtype=torch.int32, device=dev),
+               x_perm=torch.empty((T * k, h), dtype=dt, device=dev) if with_x_perm else None)
+    rc = lib().moe_capacity_drop(_ptr(topk_idx), _ptr(offsets), _ptr(row_of), _ptr(x if with_x_perm else None),
+                                 DTYPE[dt], T, h, E, k, int(capacity), _ptr(out["offsets"]), _ptr(out["row_of"]),
+                                 _ptr(out["sorted_token"]), _ptr(out["x_perm"]), _stream(topk_idx))
+    _check(rc, "moe_capacity_drop")
+    return out
+
+
+def moe_expert_choice(logits, capacity: int):
+    """Expert-choice selection from router logits [T,E] fp32."""
+    _req(logits, "logits", dtype=torch.float32)
+    dev = logits.device
+    T, E = logits.shape
+    C = int(capacity)
+    out = dict(offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               sorted_token=torch.empty((E * C,), dtype=torch.int32, device=dev),
+               row_w=torch.empty((E * C,), dtype=torch.float32, device=dev),
+               token_rows=torch.empty((T, E), dtype=torch.int32, device=dev),
+               token_nrows=torch.empty((T,), dtype=torch.int32, device=dev))
+    nws = lib().moe_expert_choice_workspace_size(T, E)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev)
+    rc = lib().moe_expert_choice(_ptr(logits), T, E, C, _ptr(out["offsets"]), _ptr(out["sorted_token"]),
+                                 _ptr(out["row_w"]), _ptr(out["token_rows"]), _ptr(out["token_nrows"]), _ptr(ws),
+                                 ws.numel(), _stream(logits))
+    _check(rc, "moe_expert_choice")
+    return out
+
+
+def moe_combine_rows(y, token_rows, token_nrows, y_sh=None):
+    _req(y, "y")
+    dev = y.device
+    P, h = y.shape
+    T, E = token_rows.shape
+    _req(token_rows, "token_rows", dtype=torch.int32, device=dev)
+    _req(token_nrows, "token_nrows", dtype=torch.int32, shape=(T,), device=dev)
+    _opt(y_sh, "y_sh", dtype=y.dtype, shape=(T, h), device=dev)
+    out = torch.empty((T, h), dtype=y.dtype, device=dev)
+    rc = lib().moe_combine_rows(_ptr(y), DTYPE[y.dtype], T, h, E, P, _ptr(token_rows), _ptr(token_nrows),
+                                _ptr(y_sh), _ptr(out), _stream(y))
+    _check(rc, "moe_combine_rows")
+    return out

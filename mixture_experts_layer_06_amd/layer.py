@@ -29,7 +29,7 @@ def _timed(timers, name, fn):
 
 def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False,
             timers: dict | None = None, router_losses: bool = False,
-            memory_efficient: bool = False, recompute: bool = False):
+            memory_efficient: bool = False, recompute: bool = False, capacity: int | None = None):
     """One forward pass. ``inp`` holds device tensors named as in
     ``workloads.make_inputs``. Returns a dict with ``out`` and the
     intermediate results of every stage. With ``timers``, the grouped FFN
@@ -43,7 +43,13 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     combine is an unweighted sum; the backward then needs neither the expert
     outputs nor the activation, which are not kept. ``recompute`` (section
     4.1.2) alone drops only the activation, which the backward rebuilds from
-    the pre-activations."""
+    the pre-activations.
+
+    ``capacity`` ("emerging-techniques-moe-training", Capacity Factor
+    Tuning): every expert takes at most that many of its pairs, the first in
+    token order; the rest are dropped. The result then also holds ``kept``,
+    the capacity-limited dispatch the expert stages use, while the full one
+    stays for the router's backward."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
@@ -51,15 +57,19 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     # inference: the first GEMM gathers token rows itself (no dispatch copy);
     # training keeps x_perm for the weight gradient of the first projection
     gather = not keep_for_backward
-    p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=not gather)
+    p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=not gather and capacity is None)
+    d = p
+    if capacity is not None:
+        d = B.moe_capacity_drop(r["topk_idx"], p["offsets"], p["row_of"], capacity, x=x,
+                                with_x_perm=not gather)
     has_sh = inp.get("w1_sh") is not None
-    row_w = B.moe_permute_weights(r["topk_w"], p["row_of"]) if memory_efficient else None
+    row_w = B.moe_permute_weights(r["topk_w"], d["row_of"]) if memory_efficient else None
     f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn(
-        x if gather else p["x_perm"], p["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"),
+        x if gather else d["x_perm"], d["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"),
         b2=inp.get("b2"), x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"),
-        keep_gu=keep_for_backward and act == "swiglu", gather_rows=p["sorted_token"] if gather else None,
+        keep_gu=keep_for_backward and act == "swiglu", gather_rows=d["sorted_token"] if gather else None,
         row_w=row_w))
-    out = B.moe_unpermute(f["y"], p["row_of"], None if memory_efficient else r["topk_w"], y_sh=f["y_sh"])
+    out = B.moe_unpermute(f["y"], d["row_of"], None if memory_efficient else r["topk_w"], y_sh=f["y_sh"])
     if memory_efficient or recompute:
         f["act"] = None          # rebuilt from gu in the backward
     if memory_efficient:
@@ -70,6 +80,37 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     res.update(r)
     res.update(p)
     res.update(f)
+    if capacity is not None:
+        res["kept"] = d
+    return res
+
+
+def capacity_from_factor(T: int, E: int, k: int, capacity_factor: float, min_capacity: int = 4) -> int:
+    """Expert capacity int(T*k/E * factor), at least min_capacity
+    ("emerging-techniques-moe-training", Capacity Factor Tuning, with the
+    T*k routing slots counted as the tokens; min_capacity from the DeepSpeed
+    config on that page)."""
+    return max(int(min_capacity), int((T * k / E) * capacity_factor))
+
+
+def forward_expert_choice(inp: dict, capacity: int, act: str, timers: dict | None = None):
+    """Forward with expert-choice routing ("emerging-techniques-moe-training",
+    Routing Mechanisms): every expert takes the ``capacity`` tokens with its
+    largest logits; a chosen pair is weighted by the token's softmax gate
+    probability. The experts' rows are gathered from x inside the first
+    grouped GEMM, the weight is applied to the activation, and each token
+    sums the rows of the experts that chose it."""
+    x = inp["x"]
+    T = x.shape[0]
+    r = B.moe_route(x, inp["w_gate"], 1, "softmax", b_gate=inp.get("b_gate"), want_logits=True)
+    c = B.moe_expert_choice(r["logits"], capacity)
+    has_sh = inp.get("w1_sh") is not None
+    f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn(
+        x, c["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"), x_sh=x if has_sh else None,
+        w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"), gather_rows=c["sorted_token"], row_w=c["row_w"]))
+    out = B.moe_combine_rows(f["y"], c["token_rows"], c["token_nrows"], y_sh=f["y_sh"])
+    res = dict(out=out, logits=r["logits"], T=T)
+    res.update(c)
     return res
 
 
@@ -79,25 +120,28 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
     forward run with keep_for_backward=True (routed experts; no shared
     expert); aux and z are the load-balancing and z-losses of the router's
     logits. With ``timers``, the grouped FFN backward call is bracketed by
-    HIP events (key "grouped_ffn_bwd")."""
+    HIP events (key "grouped_ffn_bwd"). A forward with ``capacity`` runs the
+    expert stages on its kept dispatch and the router's backward on the full
+    one."""
     E = inp["w_gate"].shape[0]
     row_w = fwd.get("row_w")
+    d = fwd.get("kept") or fwd        # the dispatch the expert stages used
     if row_w is not None:
-        grad_y, _ = B.moe_unpermute_bwd(grad_out, None, fwd["row_of"], None)
+        grad_y, _ = B.moe_unpermute_bwd(grad_out, None, d["row_of"], None)
     else:
-        grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
+        grad_y, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], d["row_of"], fwd["topk_w"])
     if fwd.get("recompute"):
         g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd_recompute(
-            grad_y, fwd["x_perm"], fwd["gu"], fwd["offsets"], inp["w1"], inp["w2"], act, row_w=row_w))
+            grad_y, d["x_perm"], fwd["gu"], d["offsets"], inp["w1"], inp["w2"], act, row_w=row_w))
     else:
         g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd(
-            grad_y, fwd["x_perm"], fwd["act"], fwd["gu"], fwd["offsets"], inp["w1"], inp["w2"], act))
+            grad_y, d["x_perm"], fwd["act"], fwd["gu"], d["offsets"], inp["w1"], inp["w2"], act))
     if row_w is not None:
-        grad_w = B.moe_permute_weights_bwd(g["grad_row_w"], fwd["row_of"])
+        grad_w = B.moe_permute_weights_bwd(g["grad_row_w"], d["row_of"])
     r = B.moe_route_bwd(inp["x"], E, fwd["topk_idx"], fwd["topk_w"], grad_w, fwd["offsets"],
                         fwd["sorted_token"], score=score, logits=fwd.get("logits"),
                         want_b_grad=inp.get("b_gate") is not None)
-    grad_x = B.moe_permute_bwd(g["grad_x_perm"], fwd["row_of"], r["grad_logits_sel"],
+    grad_x = B.moe_permute_bwd(g["grad_x_perm"], d["row_of"], r["grad_logits_sel"],
                                fwd["topk_idx"], inp["w_gate"])
     if coef_aux != 0.0 or coef_z != 0.0:
         dl = B.moe_router_losses_bwd(fwd["logits"], fwd["counts"], k, coef_aux, coef_z)

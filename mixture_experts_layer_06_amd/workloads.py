@@ -109,6 +109,11 @@ CONFIGS = {
     5: LayerConfig(5, "qwen3_imbalanced_train", T=8192, h=4096, E=128, k=8, F=1536,
                    dtype="bf16", score=SOFTMAX, act=SWIGLU, gate_bias=True, skew=True,
                    backward=True),
+    # the MoE layer of the training handbook ("Mixture-of-Experts from
+    # Architecture to Large-Scale Training", section 2.5): 64 experts of width
+    # 1024, top-8, hidden 2048; one micro-batch of 8 sequences of 4096 tokens
+    6: LayerConfig(6, "handbook_moe_train", T=32768, h=2048, E=64, k=8, F=1024,
+                   dtype="bf16", score=SOFTMAX, act=SWIGLU, backward=True),
 }
 
 # Zipf-skew recipe for the imbalanced step: gate bias b_e = GAMMA * ln(r_e ** -S)

@@ -311,30 +311,37 @@ def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bi
     """Whole layer in fp64 (router fp32). All arrays numpy; x [T,h].
 
     ``tokens`` restricts the evaluation to those token indices (routing is
-    per-token, so this equals the full computation on those rows; not with
-    ``capacity``, which depends on every token). With ``capacity``, pairs
+    per-token, so this equals the full computation on those rows; with
+    ``capacity`` the kept pairs are found from the routing of every token
+    first). With ``capacity``, pairs
     past an expert's capacity (``capacity_keep``) contribute nothing; the
     kept pairs keep their weights. Returns the route dict plus out [n,h]
     fp64, y_pair [n,k,h] (expert outputs per selected pair, zero for dropped
     pairs), keep [n,k] and y_shared [n,h] or None.
     """
     x = np.asarray(x, dtype=np.float32)
+    E = w1.shape[0]
+    keep = None
     if tokens is not None:
-        if capacity is not None:
-            raise ValueError("capacity depends on every token; evaluate all of them")
         tokens = np.asarray(tokens, dtype=np.int64)
+        if capacity is not None:
+            # which pairs an expert keeps depends on every token before them
+            if routing is not None:
+                raise ValueError("pass the full routing without tokens")
+            full = route(x, w_gate, k, score, b_gate, sel_bias)
+            keep = capacity_keep(full["topk_idx"], E, capacity)[tokens]
         x = x[tokens]
     if routing is None:
         routing = route(x, w_gate, k, score, b_gate, sel_bias)
     topk_idx = routing["topk_idx"]
     topk_w = routing["topk_w"]
     n, h = x.shape
-    E = w1.shape[0]
     out = np.zeros((n, h), dtype=np.float64)
     y_pair = np.zeros((n, k, h), dtype=np.float64)
     # Per expert, as in the pages' loop over experts: gather the tokens that
     # chose it, run the expert, weight and add back.
-    keep = np.ones(topk_idx.shape, dtype=bool) if capacity is None else capacity_keep(topk_idx, E, capacity)
+    if keep is None:
+        keep = np.ones(topk_idx.shape, dtype=bool) if capacity is None else capacity_keep(topk_idx, E, capacity)
     for e in range(E):
         tok, slot = np.nonzero((topk_idx == e) & keep)
         if tok.size == 0:
@@ -376,24 +383,28 @@ def expert_choice(logits, capacity: int):
 
 
 def expert_choice_forward(x, w_gate, w1, w2, capacity: int, act: str, b_gate=None, b1=None, b2=None,
-                          logits=None):
+                          logits=None, tokens=None):
     """out[t] = sum over the experts that chose token t (ascending) of
     softmax(l_t)_e * E_e(x_t), fp64 (logits fp32 in gate order G). A token
-    no expert chose gets 0."""
+    no expert chose gets 0. ``tokens``: evaluate the output of those tokens
+    only (the selection still sees every token)."""
     x = np.asarray(x, dtype=np.float32)
     if logits is None:
         logits = gate_logits(x, w_gate, b_gate)
     chosen, weights = expert_choice(logits, capacity)
     T, h = x.shape
-    out = np.zeros((T, h), dtype=np.float64)
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    where = {int(t): i for i, t in enumerate(rows)}
+    out = np.zeros((rows.size, h), dtype=np.float64)
     x64 = x.astype(np.float64)
     for e in range(chosen.shape[0]):
-        tok = chosen[e]
-        if tok.size == 0:
+        sel = [i for i, t in enumerate(chosen[e]) if int(t) in where]
+        if not sel:
             continue
+        tok = chosen[e][sel]
         y, _ = expert_forward(x64[tok], w1[e], w2[e], act,
                               None if b1 is None else b1[e], None if b2 is None else b2[e])
-        np.add.at(out, tok, weights[e][:, None] * y)
+        np.add.at(out, [where[int(t)] for t in tok], weights[e][sel][:, None] * y)
     return dict(logits=logits, chosen=chosen, weights=weights, out=out)
 
 

@@ -143,6 +143,11 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert L.moe_permute_weights_bwd(None, 16, 2, dummy, dummy, None) == 1
     # unweighted combine backward still needs its output
     assert L.moe_unpermute_bwd(dummy, None, 1, 16, 64, 2, dummy, None, None, None, None) == 1
+    # routing variants: negative capacity, capacity above T, too small a workspace
+    assert L.moe_capacity_drop(dummy, dummy, dummy, None, 1, 16, 64, 8, 2, -1, dummy, dummy, dummy, None, None) == 1
+    assert L.moe_expert_choice(dummy, 16, 8, 17, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None) == 2
+    assert L.moe_expert_choice(dummy, 16, 8, 4, dummy, dummy, dummy, dummy, dummy, dummy, 8, None) == 3
+    assert L.moe_combine_rows(dummy, 1, 16, 96, 8, 32, dummy, dummy, None, dummy, None) == 2
     # dense router backward: bad dtype, h % 64, misaligned pointer, workspace
     rc = L.moe_router_dense_bwd(dummy, dummy, 7, 16, 64, 8, dummy, dummy, None, None, dummy, 1 << 30, None)
     assert rc == 1

@@ -25,7 +25,7 @@ class _LazyExperts:
         return self.t[e].float().cpu().numpy()
 
 
-@pytest.mark.parametrize("cid,n_sample", [(2, 12), (3, 12), (4, 5), (5, 8)])
+@pytest.mark.parametrize("cid,n_sample", [(2, 12), (3, 12), (4, 5), (5, 8), (6, 8)])
 def test_full_size_forward(moe_lib, cid, n_sample):
     from mixture_experts_layer_06_amd import layer
     cfg = wl.CONFIGS[cid]

@@ -1,0 +1,269 @@
+"""GPU parity of the routing variants of "emerging-techniques-moe-training"
+(capacity-factor token dropping, expert-choice routing) and of the training
+handbook's own layer ("Mixture-of-Experts from Architecture to Large-Scale
+Training", section 2.5), through the C ABI, against the oracle.
+
+Which pairs are kept or chosen is integer work and must match the oracle
+bit for bit; outputs and gradients are held to the usual tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_06_amd import workloads as wl
+from parity import TOL, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
+
+pytestmark = pytest.mark.gpu
+
+
+class _Lazy:
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, e):
+        return self.t[e].float().cpu().numpy()
+
+
+# ------------------------------------------------------------ dropping
+
+CAP_CASES = {
+    "imbalanced_small": (wl.small_variant(wl.CONFIGS[5], T=300, h=256, F=128, E=32), 1.25),
+    "sigmoid_ragged": (wl.small_variant(wl.CONFIGS[4], T=333, h=192, F=192, E=16, k=4), 1.0),
+    "tiny_fp32_gelu": (wl.CONFIGS[1], 0.75),
+}
+
+
+def _kept_reference(topk_idx, E, C):
+    keep = oracle.capacity_keep(topk_idx, E, C)
+    counts = np.bincount(topk_idx.reshape(-1), minlength=E)
+    kc = np.minimum(counts, C)
+    offs = np.concatenate([[0], np.cumsum(kc)]).astype(np.int64)
+    return keep, offs
+
+
+@pytest.mark.parametrize("name", list(CAP_CASES))
+@pytest.mark.parametrize("train", [False, True])
+def test_capacity_forward(moe_lib, name, train):
+    from mixture_experts_layer_06_amd import layer
+    cfg, cf = CAP_CASES[name]
+    C = oracle.expert_capacity(cfg.T, cfg.E, cfg.k, cf)
+    print("case capacity forward", name, "C", C, "train" if train else "inference", flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=False)
+    dinp = to_device(inp)
+    g = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, capacity=C)
+    torch.cuda.synchronize()
+    o = oracle_inputs(inp)
+    ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act, b_gate=o["b_gate"],
+                         sel_bias=o["sel_bias"], b1=o["b1"], b2=o["b2"], w1_sh=o["w1_sh"], w2_sh=o["w2_sh"],
+                         capacity=C)
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    keep, offs = _kept_reference(ref["topk_idx"], cfg.E, C)
+    kept = g["kept"]
+    ro = kept["row_of"].cpu().numpy()
+    assert np.array_equal(ro >= 0, keep)
+    assert (~keep).any(), "the case should drop pairs"
+    assert np.array_equal(kept["offsets"].cpu().numpy(), offs)
+    # kept rows: expert-major, tokens ascending inside an expert
+    perm_ref = oracle.permutation(ref["topk_idx"], cfg.E)
+    rank = perm_ref["row_of"] - perm_ref["offsets"][ref["topk_idx"]]
+    expect_row = np.where(keep, offs[ref["topk_idx"]] + rank, -1)
+    assert np.array_equal(ro, expect_row)
+    st = kept["sorted_token"].cpu().numpy()[:offs[-1]]
+    t_of = np.repeat(np.arange(cfg.T)[:, None], cfg.k, axis=1)
+    assert np.array_equal(st[ro[keep]], t_of[keep])
+    if train:
+        rows = kept["x_perm"][: int(offs[-1])]
+        assert torch.equal(rows, dinp["x"][kept["sorted_token"][: int(offs[-1])].long()])
+    err = rel_err(to_np32(g["out"]), ref["out"])
+    print("out rel err", err, flush=True)
+    assert err <= TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("case", ["imbalanced_softmax", "sigmoid_ragged"])
+@pytest.mark.parametrize("memory_efficient", [False, True])
+def test_capacity_backward(moe_lib, case, memory_efficient):
+    from mixture_experts_layer_06_amd import layer
+    if case == "sigmoid_ragged":
+        cfg = wl.small_variant(wl.CONFIGS[5], T=333, h=192, F=192, E=16, k=4).with_shape(
+            score="sigmoid", skew=False, gate_bias=False)
+        cf = 0.9
+    else:
+        cfg = wl.small_variant(wl.CONFIGS[5], T=300, h=256, F=128, E=32)
+        cf = 1.25
+    C = oracle.expert_capacity(cfg.T, cfg.E, cfg.k, cf)
+    print("case capacity backward", case, "C", C, "memory-efficient" if memory_efficient else "", flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=True)
+    dinp = to_device(inp)
+    f = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True, capacity=C,
+                      memory_efficient=memory_efficient)
+    g = layer.backward(dinp, f, dinp["grad_out"], cfg.k, cfg.score, cfg.act)
+    torch.cuda.synchronize()
+    o = oracle_inputs(inp)
+    ref = oracle.backward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                          to_np32(inp["grad_out"]), b_gate=o["b_gate"], capacity=C)
+    keep = f["kept"]["row_of"].cpu().numpy() >= 0
+    assert (~keep).any()
+    gw = g["grad_topk_w"].cpu().numpy()
+    assert not gw[~keep].any(), "dropped pairs carry routing-weight gradient"
+    tol = TOL[cfg.dtype]
+    err = {"grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
+           "grad_topk_w": rel_err_tensor(gw, ref["d_topk_w"]),
+           "grad_w_gate": rel_err_tensor(g["grad_w_gate"].cpu().numpy(), ref["dw_gate"])}
+    counts = np.bincount(f["topk_idx"].cpu().numpy()[keep], minlength=cfg.E)
+    for e in range(cfg.E):
+        if counts[e] == 0:
+            assert not g["grad_w1"][e].any() and not g["grad_w2"][e].any()
+            continue
+        err["grad_w1[%d]" % e] = rel_err_tensor(g["grad_w1"][e].cpu().numpy(), ref["dw1"][e])
+        err["grad_w2[%d]" % e] = rel_err_tensor(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e])
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    bad = {k: v for k, v in err.items() if not v <= tol}
+    assert not bad, bad
+
+
+def test_capacity_full_size_sampled(moe_lib):
+    """The imbalanced workload at full size with capacity factor 1.25 (640
+    pairs per expert against a hottest expert of about 6,300): the kept set
+    bit for bit, sampled tokens' outputs against the oracle."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.CONFIGS[5]
+    C = oracle.expert_capacity(cfg.T, cfg.E, cfg.k, 1.25)
+    print("case capacity full size, C", C, flush=True)
+    inp = wl.make_inputs(cfg, device="cuda", with_grad_out=False)
+    g = layer.forward(inp, cfg.k, cfg.score, cfg.act, capacity=C)
+    torch.cuda.synchronize()
+    x, wg, bg = to_np32(inp["x"]), to_np32(inp["w_gate"]), to_np32(inp["b_gate"])
+    r = oracle.route(x, wg, cfg.k, cfg.score, bg)
+    assert np.array_equal(g["topk_idx"].cpu().numpy(), r["topk_idx"])
+    keep, offs = _kept_reference(r["topk_idx"], cfg.E, C)
+    assert np.array_equal(g["kept"]["row_of"].cpu().numpy() >= 0, keep)
+    assert np.array_equal(g["kept"]["offsets"].cpu().numpy(), offs)
+    tokens = np.unique(np.concatenate([np.linspace(0, cfg.T - 1, 6).astype(np.int64),
+                                       np.nonzero(~keep.all(axis=1))[0][-3:]]))
+    o = oracle.forward(x, wg, _Lazy(inp["w1"]), _Lazy(inp["w2"]), cfg.k, cfg.score, cfg.act, b_gate=bg,
+                       tokens=tokens, capacity=C)
+    err = rel_err(to_np32(g["out"][torch.as_tensor(tokens, device="cuda")]), o["out"])
+    print("sampled out rel err", err, flush=True)
+    assert err <= TOL[cfg.dtype], err
+
+
+# -------------------------------------------------------- expert choice
+
+EC_CASES = {
+    "tiny_fp32_gelu": wl.CONFIGS[1],
+    "qwen3_small": wl.small_variant(wl.CONFIGS[3], T=1000, h=512, F=192),
+    "mixtral_small": wl.small_variant(wl.CONFIGS[2], T=600, h=256, F=384),
+}
+
+
+def _check_choice(g, chosen, weights, T, E, C):
+    st = g["sorted_token"].cpu().numpy().reshape(E, C)
+    assert np.array_equal(st, chosen)
+    assert np.array_equal(g["offsets"].cpu().numpy(), np.arange(E + 1) * C)
+    assert rel_err_tensor(g["row_w"].cpu().numpy().reshape(E, C), weights) <= 1e-5
+    nrows = g["token_nrows"].cpu().numpy()
+    assert np.array_equal(nrows, np.bincount(chosen.reshape(-1), minlength=T))
+    tr = g["token_rows"].cpu().numpy()
+    for t in np.linspace(0, T - 1, 7).astype(int):
+        e_of, i_of = np.nonzero(chosen == t)
+        assert tr[t, :nrows[t]].tolist() == (e_of * C + i_of).tolist()
+
+
+@pytest.mark.parametrize("name", list(EC_CASES))
+def test_expert_choice_forward(moe_lib, name):
+    from mixture_experts_layer_06_amd import layer
+    cfg = EC_CASES[name]
+    C = cfg.T * cfg.k // cfg.E
+    print("case expert choice", name, "C", C, flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=False)
+    dinp = to_device(inp)
+    g = layer.forward_expert_choice(dinp, C, cfg.act)
+    torch.cuda.synchronize()
+    o = oracle_inputs(inp)
+    ref = oracle.expert_choice_forward(o["x"], o["w_gate"], o["w1"], o["w2"], C, cfg.act, b_gate=o["b_gate"],
+                                       b1=o["b1"], b2=o["b2"])
+    assert np.array_equal(g["logits"].cpu().numpy().view(np.uint32), ref["logits"].view(np.uint32))
+    _check_choice(g, ref["chosen"], ref["weights"], cfg.T, cfg.E, C)
+    err = rel_err(to_np32(g["out"]), ref["out"])
+    print("out rel err", err, flush=True)
+    assert err <= TOL[cfg.dtype], err
+
+
+def test_expert_choice_ties_and_full_capacity(moe_lib):
+    """Repeated token rows give equal logits across tokens, cut by the
+    capacity: the lower token indices win. Capacity T: every expert takes
+    every token."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[3], T=256, h=128, F=64, E=16, k=2)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=False)
+    x = inp["x"].clone()
+    x[40:120] = x[7]              # 81 copies of token 7
+    inp["x"] = x
+    o = oracle_inputs(inp)
+    for C in (32, 100, cfg.T):
+        g = layer.forward_expert_choice(to_device(inp), C, cfg.act)
+        torch.cuda.synchronize()
+        ref = oracle.expert_choice_forward(o["x"], o["w_gate"], o["w1"], o["w2"], C, cfg.act)
+        _check_choice(g, ref["chosen"], ref["weights"], cfg.T, cfg.E, C)
+        err = rel_err(to_np32(g["out"]), ref["out"])
+        print("C", C, "out rel err", err, flush=True)
+        assert err <= TOL[cfg.dtype], err
+
+
+def test_expert_choice_full_size_sampled(moe_lib):
+    """Qwen3-shaped layer at full size, capacity T*k/E = 512 per expert:
+    every expert's choice bit for bit, sampled tokens' outputs."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.CONFIGS[3]
+    C = cfg.T * cfg.k // cfg.E
+    print("case expert choice full size, C", C, flush=True)
+    inp = wl.make_inputs(cfg, device="cuda", with_grad_out=False)
+    g = layer.forward_expert_choice(inp, C, cfg.act)
+    torch.cuda.synchronize()
+    x, wg = to_np32(inp["x"]), to_np32(inp["w_gate"])
+    logits = oracle.gate_logits(x, wg)
+    chosen, weights = oracle.expert_choice(logits, C)
+    _check_choice(g, chosen, weights, cfg.T, cfg.E, C)
+    tokens = np.linspace(0, cfg.T - 1, 8).astype(np.int64)
+    ref = oracle.expert_choice_forward(x, wg, _Lazy(inp["w1"]), _Lazy(inp["w2"]), C, cfg.act, logits=logits,
+                                       tokens=tokens)
+    err = rel_err(to_np32(g["out"][torch.as_tensor(tokens, device="cuda")]), ref["out"])
+    print("sampled out rel err", err, flush=True)
+    assert err <= TOL[cfg.dtype], err
+
+
+# ----------------------------------------------------- handbook layer
+
+def test_handbook_layer_slice_forward_backward(moe_lib):
+    """The handbook's training layer (h 2048, 64 experts of width 1024,
+    top-8): the first 64 tokens with the full weights, forward and backward,
+    against the oracle."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.CONFIGS[6]
+    print("case handbook layer, 64-token slice", flush=True)
+    full = wl.make_inputs(cfg, device="cuda")
+    inp = wl.slice_tokens(full, 64)
+    sub = cfg.with_shape(T=64)
+    f = layer.forward(inp, sub.k, sub.score, sub.act, keep_for_backward=True)
+    g = layer.backward(inp, f, inp["grad_out"], sub.k, sub.score, sub.act)
+    torch.cuda.synchronize()
+    counts = f["counts"].cpu().numpy()
+    experts = [int(e) for e in np.nonzero(counts)[0]][:5] + [int(e) for e in np.nonzero(counts == 0)[0]][:2]
+    x, wg = to_np32(inp["x"]), to_np32(inp["w_gate"])
+    fr = oracle.forward(x, wg, _Lazy(inp["w1"]), _Lazy(inp["w2"]), sub.k, sub.score, sub.act)
+    assert np.array_equal(f["topk_idx"].cpu().numpy(), fr["topk_idx"])
+    ref = oracle.backward(x, wg, _Lazy(inp["w1"]), _Lazy(inp["w2"]), sub.k, sub.score, sub.act,
+                          to_np32(inp["grad_out"]), experts=experts)
+    tol = TOL[cfg.dtype]
+    err = {"out": rel_err(to_np32(f["out"]), fr["out"]),
+           "grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
+           "grad_w_gate": rel_err_tensor(g["grad_w_gate"].cpu().numpy(), ref["dw_gate"])}
+    for e in experts:
+        if counts[e] == 0:
+            assert not g["grad_w1"][e].any() and not g["grad_w2"][e].any()
+            continue
+        err["grad_w1[%d]" % e] = rel_err_tensor(g["grad_w1"][e].cpu().numpy(), ref["dw1"][e])
+        err["grad_w2[%d]" % e] = rel_err_tensor(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e])
+    print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
+    assert all(v <= tol for v in err.values()), err

@@ -81,8 +81,8 @@ def test_dropping_forward_brute_force_and_limits():
     assert not zero["out"].any()
     whole = r["keep"].all(axis=1)
     assert np.array_equal(r["out"][whole], free["out"][whole])
-    with pytest.raises(ValueError):
-        oracle.forward(x, wg, w1, w2, k, "softmax", "swiglu", capacity=C, tokens=[0, 1])
+    sub = oracle.forward(x, wg, w1, w2, k, "softmax", "swiglu", capacity=C, tokens=[3, 0, 17])
+    assert np.allclose(sub["out"], r["out"][[3, 0, 17]], rtol=1e-13, atol=1e-14)
 
 
 @pytest.mark.parametrize("score", ["softmax", "sigmoid"])
@@ -171,3 +171,5 @@ def test_expert_choice_load_is_exactly_balanced():
     assert all(np.all(np.diff(row) > 0) for row in r["chosen"])
     untaken = np.setdiff1d(np.arange(40), r["chosen"].reshape(-1))
     assert not r["out"][untaken].any()
+    sub = oracle.expert_choice_forward(x, wg, w1, w2, 10, "swiglu", tokens=[5, 0, 33])
+    assert np.allclose(sub["out"], r["out"][[5, 0, 33]], rtol=1e-13, atol=1e-14)

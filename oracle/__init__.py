@@ -16,11 +16,18 @@ from .moe import (  # noqa: F401
     expert_backward,
     expert_fraction,
     expert_forward,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_round,
     forward,
+    forward_mxfp8,
     gate_logits,
     gelu_erf,
     loss_fp64,
     mean_router_probs,
+    mx_dequantize,
+    mx_quantize,
+    mx_roundtrip,
     permutation,
     route,
     router_backward_dlogits,

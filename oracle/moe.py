@@ -59,6 +59,12 @@ Definitions followed (page titles are the pages' own):
   the `capacity` tokens with the largest logits (ties: lower token index);
   a chosen pair is weighted by the token's softmax gate probability.
 
+* MXFP8 ("Scalable Training ... with Megatron Core", section 5.3.3: 1 x 32
+  blocks, E8M0 scales; E4M3 elements as in the page's FP8 recipes). The
+  page does not say how a block's scale is chosen: the shared exponent is
+  floor(log2(max |v|)) - 8, so the largest element lands in [256, 512) and
+  is rounded to nearest-even on the E4M3 grid with saturation at 448.
+
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, invariants, brute force and finite differences; the
 absolute output values of the four model-shaped workloads rest on those pins
@@ -357,6 +363,131 @@ def forward(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bi
         out += y_sh
     res = dict(routing)
     res.update(out=out, y_pair=y_pair, y_shared=y_sh, keep=keep)
+    return res
+
+
+# ----------------------------------------------------------------- MXFP8
+
+E4M3_MAX = 448.0          # largest finite E4M3 value (1.75 * 2^8)
+E4M3_EMAX = 8             # exponent of the largest E4M3 binade
+E4M3_MIN_NORMAL = 2.0 ** -6
+E4M3_SUB_STEP = 2.0 ** -9  # spacing of the subnormals
+
+
+def e4m3_round(y):
+    """Round float64 values to the E4M3 grid, nearest with ties to the even
+    mantissa, magnitudes above 448 saturated to 448 (fp64 arithmetic on the
+    grid's definition: 3 mantissa bits, exponent bias 7, subnormal step
+    2^-9, no infinities)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    out = np.zeros_like(a)
+    sub = a < E4M3_MIN_NORMAL
+    out[sub] = np.round(a[sub] / E4M3_SUB_STEP) * E4M3_SUB_STEP      # np.round: ties to even
+    nrm = ~sub
+    e = np.floor(np.log2(np.where(nrm, a, 1.0)))
+    step = 2.0 ** (e - 3)
+    out[nrm] = (np.round(a / step) * step)[nrm]
+    out = np.minimum(out, E4M3_MAX)
+    return np.copysign(out, y)
+
+
+def e4m3_encode(v):
+    """Bit codes (uint8) of values already on the E4M3 grid."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < E4M3_MIN_NORMAL
+    code[sub] = np.rint(a[sub] / E4M3_SUB_STEP).astype(np.int64)
+    nrm = ~sub & (a > 0)
+    e = np.floor(np.log2(np.where(nrm, a, 1.0))).astype(np.int64)
+    m = np.rint(a / 2.0 ** e * 8 - 8).astype(np.int64)
+    code[nrm] = ((e + 7) * 8 + m)[nrm]
+    code |= np.where(np.signbit(v), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def e4m3_decode(code):
+    """float64 values of E4M3 bit codes (0x7f / 0xff, the NaN codes, decode
+    as NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    val = np.where(e == 0, m * E4M3_SUB_STEP, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    val = np.where((c & 0x7f) == 0x7f, np.nan, val)
+    return s * val
+
+
+def mx_quantize(v):
+    """MXFP8 quantisation along the last axis ("Scalable Training of
+    Mixture-of-Experts Models with Megatron Core", section 5.3.3: 1 x 32
+    blocks, E8M0 scales, E4M3 elements). Per block of 32: the shared
+    exponent is floor(log2 of the block's largest magnitude) - 8 (the E4M3
+    exponent of its largest binade), clamped to [-127, 127]; elements are
+    v / 2^exponent rounded by ``e4m3_round``. An all-zero block gets
+    exponent -127. Returns (codes uint8 [..., K], scale codes uint8
+    [..., K/32] = exponent + 127)."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    blk = v.reshape(v.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    exp = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, -127)
+    exp = np.clip(exp, -127, 127)
+    q = e4m3_round(blk / 2.0 ** exp[..., None])
+    codes = e4m3_encode(q).reshape(v.shape)
+    return codes, (exp + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales):
+    """float64 values of MXFP8 data: element * 2^(scale - 127)."""
+    c = np.asarray(codes)
+    K = c.shape[-1]
+    val = e4m3_decode(c).reshape(c.shape[:-1] + (K // 32, 32))
+    val = val * 2.0 ** (np.asarray(scales, dtype=np.float64) - 127)[..., None]
+    return val.reshape(c.shape)
+
+
+def mx_roundtrip(v):
+    """v quantised to MXFP8 and back (float64)."""
+    return mx_dequantize(*mx_quantize(v))
+
+
+def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bias=None,
+                  routing=None, tokens=None):
+    """The layer with the expert GEMMs in MXFP8: routing as ``forward``; the
+    token rows, both weight matrices (along their reduction axes: h for W1,
+    F for W2) and the activation (along F) quantised by ``mx_quantize``;
+    products and sums in fp64 on the dequantised values. SwiGLU or GELU
+    without biases, no shared expert."""
+    x = np.asarray(x, dtype=np.float32)
+    if tokens is not None:
+        x = x[np.asarray(tokens, dtype=np.int64)]
+    if routing is None:
+        routing = route(x, w_gate, k, score, b_gate, sel_bias)
+    topk_idx, topk_w = routing["topk_idx"], routing["topk_w"]
+    n, h = x.shape
+    E = w1.shape[0]
+    xq = mx_roundtrip(x)
+    out = np.zeros((n, h), dtype=np.float64)
+    for e in range(E):
+        tok, slot = np.nonzero(topk_idx == e)
+        if tok.size == 0:
+            continue
+        w1q = mx_roundtrip(np.asarray(w1[e], dtype=np.float64))
+        w2q = mx_roundtrip(np.asarray(w2[e], dtype=np.float64))
+        a = xq[tok] @ w1q.T
+        if act == "swiglu":
+            F = w2q.shape[1]
+            hid = silu(a[:, :F]) * a[:, F:]
+        else:
+            hid = gelu_erf(a)
+        y = mx_roundtrip(hid) @ w2q.T
+        out[tok] += topk_w[tok, slot][:, None] * y
+    res = dict(routing)
+    res.update(out=out)
     return res
 
 

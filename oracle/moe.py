@@ -450,6 +450,19 @@ def mx_dequantize(codes, scales):
     return val.reshape(c.shape)
 
 
+def round_bf16(v):
+    """float64 values rounded to bfloat16 (8 significant bits, nearest with
+    ties to even, fp32's exponent range; overflow to inf)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)                 # subnormals share the smallest binade's step
+    step = 2.0 ** (e - 7)
+    out = np.round(a / step) * step
+    out = np.where(out > 3.3895313892515355e38, np.inf, out)
+    return np.copysign(np.where(a > 0, out, 0.0), v)
+
+
 def mx_roundtrip(v):
     """v quantised to MXFP8 and back (float64)."""
     return mx_dequantize(*mx_quantize(v))
@@ -460,8 +473,10 @@ def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, 
     """The layer with the expert GEMMs in MXFP8: routing as ``forward``; the
     token rows, both weight matrices (along their reduction axes: h for W1,
     F for W2) and the activation (along F) quantised by ``mx_quantize``;
-    products and sums in fp64 on the dequantised values. SwiGLU or GELU
-    without biases, no shared expert."""
+    products and sums in fp64 on the dequantised values. The activation is
+    quantised from its bf16 rounding: the bf16 layer stores it in bf16, and
+    the MXFP8 layer quantises that stored tensor. SwiGLU or GELU without
+    biases, no shared expert."""
     x = np.asarray(x, dtype=np.float32)
     if tokens is not None:
         x = x[np.asarray(tokens, dtype=np.int64)]
@@ -484,7 +499,7 @@ def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, 
             hid = silu(a[:, :F]) * a[:, F:]
         else:
             hid = gelu_erf(a)
-        y = mx_roundtrip(hid) @ w2q.T
+        y = mx_roundtrip(round_bf16(hid)) @ w2q.T
         out[tok] += topk_w[tok, slot][:, None] * y
     res = dict(routing)
     res.update(out=out)

@@ -109,8 +109,21 @@ def test_mxfp8_layer_identical_experts_is_the_dense_fp8_ffn(act):
     r = oracle.forward_mxfp8(x, wg, w1, w2, k, "softmax", act)
     a = oracle.mx_roundtrip(x.astype(np.float64)) @ oracle.mx_roundtrip(w1[0]).T
     hid = oracle.silu(a[:, :F]) * a[:, F:] if act == "swiglu" else oracle.gelu_erf(a)
-    dense = oracle.mx_roundtrip(hid) @ oracle.mx_roundtrip(w2[0]).T
+    dense = oracle.mx_roundtrip(oracle.round_bf16(hid)) @ oracle.mx_roundtrip(w2[0]).T
     assert np.allclose(r["out"], dense, rtol=1e-12, atol=1e-12)
     plain = oracle.forward(x, wg, w1, w2, k, "softmax", act)
     rel = np.abs(r["out"] - plain["out"]).max() / np.abs(plain["out"]).max()
     assert 1e-3 < rel < 0.1, rel
+
+
+def test_round_bf16_matches_torch_and_ties():
+    """fp32 inputs rounded by torch's bfloat16 conversion (nearest-even);
+    exact halfway cases go to the even mantissa; huge values overflow."""
+    import torch
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-60, 60, 20000))).astype(np.float32)
+    ref = torch.as_tensor(v).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(v.astype(np.float64)), ref)
+    assert oracle.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0              # tie -> even
+    assert oracle.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2 ** -6   # tie -> even (up)
+    assert np.isinf(oracle.round_bf16(np.array([3.4e38, -3.4e38]))).all()

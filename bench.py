@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "MoE layer active TFLOP/s + tokens/s at 1 MI355X; % of MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 # fp32 FMA on the vector ALUs without packed instructions (which this library
 # does not emit): 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz
@@ -66,6 +67,9 @@ def parse():
                    help="drop pairs past int(T*k/E * factor) per expert (min 4), in token order")
     p.add_argument("--expert-choice", action="store_true",
                    help="expert-choice routing, capacity T*k/E per expert (forward only)")
+    p.add_argument("--mxfp8", action="store_true",
+                   help="expert GEMMs in MXFP8 (1x32 blocks, E8M0 scales; weights quantised before "
+                        "timing, tokens and activation inside the step); forward only")
     p.add_argument("--router-losses", action="store_true",
                    help="add the load-balancing loss (coefficient 1e-2) and router z-loss "
                         "(1e-3) to a training step, and time their kernels as stages")
@@ -337,8 +341,14 @@ def main():
         if train:
             sys.exit("--expert-choice runs the forward only; pick a forward workload")
         ec_cap = cfg.T * cfg.k // cfg.E
+    if args.mxfp8:
+        if train or cfg.act != "swiglu" or cfg.n_shared or cfg.dtype != "bf16":
+            sys.exit("--mxfp8 runs the forward of bf16 SwiGLU layers without a shared expert")
+        wq = layer.quantize_experts_mx(inp)
 
     def step(timers=None):
+        if args.mxfp8:
+            return layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers)
         if args.expert_choice:
             return layer.forward_expert_choice(inp, ec_cap, cfg.act, timers=timers)
         f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers,
@@ -381,7 +391,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "mxfp8 (e4m3, e8m0 1x32)" if args.mxfp8 else cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.h, "experts": cfg.E,
                    "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
@@ -406,16 +416,23 @@ def main():
 
     # roofline of the dominant call, from the events inside the timed steps
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    if args.mxfp8:
+        peak = PEAK_FP8_TFLOPS
     nmat = 3 if cfg.act == "swiglu" else 2
     bwd_flops = 2.0 * cfg.P * nmat * 2.0 * cfg.h * cfg.F
     call_flops = {"grouped_ffn": ffn_flops(cfg), "grouped_ffn_bwd": bwd_flops}
     dom = max(live, key=lambda n: live[n])
-    rec = recorded_traffic(cfg.name) if dom == "grouped_ffn" else None
+    rec = recorded_traffic(cfg.name) if dom == "grouped_ffn" and not args.mxfp8 else None
     gk = "grouped_gemm_bf16" if cfg.dtype == "bf16" else "grouped_gemm_f32"
+    if args.mxfp8:
+        gk = "grouped_gemm_mx (MXFP8)"
     kernels = {"grouped_ffn": "%s %s launch + %s plain launch (one moe_grouped_ffn call)"
                               % (gk, "SwiGLU" if cfg.act == "swiglu" else "GELU", gk),
                "grouped_ffn_bwd": "moe_grouped_ffn_bwd call (SwiGLU backward, data and weight "
                                   "gradient launches)"}
+    if args.mxfp8:
+        kernels["grouped_ffn"] = ("grouped_gemm_mx SwiGLU launch + activation quantisation + "
+                                  "grouped_gemm_mx plain launch (one moe_grouped_ffn_mx call)")
     out["roofline"] = {
         "kernel": kernels[dom], "bound": "mfma",
         "achieved": call_flops[dom] / live[dom] / 1e12, "peak": peak, "unit": "TFLOP/s",
@@ -429,7 +446,7 @@ def main():
         out["roofline"]["traffic_note"] = rec["note"]
 
     # the stage-by-stage timings cover the top-k dropless chain
-    if not args.no_stages and not args.expert_choice and cap is None:
+    if not args.no_stages and not args.expert_choice and cap is None and not args.mxfp8:
         stream = torch.cuda.current_stream(dev)
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         E = cfg.E

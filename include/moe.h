@@ -222,6 +222,36 @@ int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int k,
                   const int32_t *row_of, const float *topk_w, const void *y_sh, void *out,
                   void *stream);
 
+/* ------------------------------------------------------------------ MXFP8
+ * "Scalable Training ... with Megatron Core", section 5.3.3: activations and
+ * weights quantised in 1 x 32 blocks with E8M0 scales (E4M3 elements); the
+ * expert GEMMs run on CDNA4's scaled fp8 matrix instruction.
+ *
+ * moe_mx_quantize: src [rows,K] dtype (K % 32 == 0) to codes [rows,K] uint8
+ * (E4M3) and scales [rows,K/32] uint8 (E8M0, 2^(s-127)). Per block of 32:
+ * shared exponent floor(log2 max|v|) - 8, clamped to [-127,127] (-127 for an
+ * all-zero block); elements v * 2^-exp rounded to nearest-even on the E4M3
+ * grid, saturated at 448. Deterministic bit for bit. Weights are quantised
+ * along their reduction axis: w1 [E,2F,h] as E*2F rows of h, w2 [E,h,F] as
+ * E*h rows of F. */
+int moe_mx_quantize(const void *src, int dtype, int64_t rows, int64_t K, uint8_t *codes,
+                    uint8_t *scales, void *stream);
+
+/* Grouped SwiGLU FFN in MXFP8 (no bias, no shared expert): tokens x_codes /
+ * x_scales (rows quantised along h; permuted rows [P,h], or with gather_rows
+ * the unpermuted [x_rows,h] as in moe_grouped_ffn), weights as quantised by
+ * moe_mx_quantize. Writes act [P,F] bf16 = silu(g)*u of the first
+ * projection, its quantisation act_codes [P,F] / act_scales [P,F/32], and
+ * y [P,h] bf16 of the second. fp32 accumulation. Needs h % 128 == 0,
+ * F % 128 == 0; code and output pointers 16-byte aligned, scale pointers
+ * 4-byte aligned. */
+int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scales, const int32_t *gather_rows,
+                       int64_t x_rows, int64_t P, int64_t h, int64_t F, int E,
+                       const int32_t *offsets, int act_kind, const uint8_t *w1_codes,
+                       const uint8_t *w1_scales, const uint8_t *w2_codes,
+                       const uint8_t *w2_scales, void *act, uint8_t *act_codes,
+                       uint8_t *act_scales, void *y, void *stream);
+
 /* ------------------------------------------------------- Routing variants
  * "emerging-techniques-moe-training".
  *

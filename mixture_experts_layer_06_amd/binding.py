@@ -63,6 +63,9 @@ _SIGS = {
     "moe_capacity_drop": ([_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp],
                           _int),
     "moe_expert_choice_workspace_size": ([_i64, _int], _sz),
+    "moe_mx_quantize": ([_vp, _int, _i64, _i64, _vp, _vp, _vp], _int),
+    "moe_grouped_ffn_mx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _vp, _vp, _vp], _int),
     "moe_expert_choice": ([_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_combine_rows": ([_vp, _int, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd_recompute": ([_vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
@@ -537,4 +540,48 @@ def moe_combine_rows(y, token_rows, token_nrows, y_sh=None):
     rc = lib().moe_combine_rows(_ptr(y), DTYPE[y.dtype], T, h, E, P, _ptr(token_rows), _ptr(token_nrows),
                                 _ptr(y_sh), _ptr(out), _stream(y))
     _check(rc, "moe_combine_rows")
+    return out
+
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def moe_mx_quantize(src):
+    """(codes uint8 [..., K], scales uint8 [..., K/32]) of src (bf16/fp32),
+    quantised along its last axis."""
+    _req(src, "src")
+    dev = src.device
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    codes = torch.empty(src.shape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(tuple(src.shape[:-1]) + (K // 32,), dtype=torch.uint8, device=dev)
+    rc = lib().moe_mx_quantize(_ptr(src), DTYPE[src.dtype], rows, K, _ptr(codes), _ptr(scales), _stream(src))
+    _check(rc, "moe_mx_quantize")
+    return codes, scales
+
+
+def moe_grouped_ffn_mx(x_codes, x_scales, offsets, w1_codes, w1_scales, w2_codes, w2_scales,
+                       gather_rows=None, act: str = "swiglu"):
+    _req(x_codes, "x_codes", dtype=torch.uint8)
+    dev = x_codes.device
+    x_rows, h = x_codes.shape
+    P = gather_rows.numel() if gather_rows is not None else x_rows
+    E = w1_codes.shape[0]
+    F = w2_codes.shape[2]
+    _req(x_scales, "x_scales", dtype=torch.uint8, shape=(x_rows, h // 32), device=dev)
+    _opt(gather_rows, "gather_rows", dtype=torch.int32, device=dev)
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(w1_codes, "w1_codes", dtype=torch.uint8, shape=(E, 2 * F, h), device=dev)
+    _req(w1_scales, "w1_scales", dtype=torch.uint8, shape=(E, 2 * F, h // 32), device=dev)
+    _req(w2_codes, "w2_codes", dtype=torch.uint8, shape=(E, h, F), device=dev)
+    _req(w2_scales, "w2_scales", dtype=torch.uint8, shape=(E, h, F // 32), device=dev)
+    out = dict(act=torch.empty((P, F), dtype=torch.bfloat16, device=dev),
+               act_codes=torch.empty((P, F), dtype=torch.uint8, device=dev),
+               act_scales=torch.empty((P, F // 32), dtype=torch.uint8, device=dev),
+               y=torch.empty((P, h), dtype=torch.bfloat16, device=dev))
+    rc = lib().moe_grouped_ffn_mx(_ptr(x_codes), _ptr(x_scales), _ptr(gather_rows), x_rows, P, h, F, E,
+                                  _ptr(offsets), ACT[act], _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
+                                  _ptr(w2_scales), _ptr(out["act"]), _ptr(out["act_codes"]),
+                                  _ptr(out["act_scales"]), _ptr(out["y"]), _stream(x_codes))
+    _check(rc, "moe_grouped_ffn_mx")
     return out

@@ -1,0 +1,491 @@
+// Expert computation in MXFP8 ("Scalable Training of Mixture-of-Experts
+// Models with Megatron Core", section 5.3.3: activations and weights
+// quantised in 1 x 32 blocks with E8M0 scales; E4M3 elements), on CDNA4's
+// scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4, which applies a
+// block's E8M0 scale inside the product.
+//
+// * moe_mx_quantize: rows of K values (bf16 or fp32) to E4M3 codes and one
+//   E8M0 scale per 32 consecutive values. Shared exponent of a block:
+//   floor(log2 max|v|) - 8 (the largest element lands in [256, 512)),
+//   clamped to [-127, 127]; elements v * 2^-exp rounded to nearest-even on
+//   the E4M3 grid, saturated at 448. One thread per block of 32, in integer
+//   and exact float operations only, so the codes are those of any correct
+//   implementation of the same rule.
+// * grouped_gemm_mx: the bf16 grouped kernel's design with fp8 operands:
+//   a k-step is 128 fp8 values, i.e. the same 128-byte rows, 16-byte chunks,
+//   LDS swizzle and global -> VGPR -> LDS staging; each k-step runs two
+//   halves of 16 scaled MFMAs (k = 64 each). Operand layout of the
+//   instruction (checked on the device): lane l supplies row l % 32; bytes
+//   0-15 of lanes l and l + 32 hold the row's first block of 32 k values (k
+//   0..15 and 16..31), bytes 16-31 its second block (32..47, 48..63), and the
+//   scale of block b of row r comes from lane r + 32 b. So lane half g reads
+//   chunks 4s + g and 4s + 2 + g of k-sub s and supplies the scale of block
+//   2s + g (a byte load, opsel 0). Accumulators as in the bf16 kernel.
+// * moe_grouped_ffn_mx: first projection with SwiGLU (bf16 activation),
+//   quantisation of the activation along F, second projection (bf16 expert
+//   outputs). Tokens enter quantised along h, optionally gathered.
+#include <type_traits>
+
+#include "gemm_common.hpp"
+
+namespace moe {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ quantise
+
+// E4M3 code of |y| < 2^9 given as fp32 (exact scaled value), sign apart.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t s = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a >= 448.0f) return s | 0x7eu;                       // saturate (all of [448, 512) rounds to 448)
+    if (a < 0.015625f) return s | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // subnormals; 8 = 2^-6
+    const uint32_t b = __float_as_uint(a);
+    int e = static_cast<int>(b >> 23) - 127;                 // -6 .. 8
+    const uint32_t mant = b & 0x7fffffu;
+    uint32_t m = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, nearest-even
+    if (m == 8) {
+        m = 0;
+        ++e;
+    }
+    uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | m;
+    if (code > 0x7eu) code = 0x7eu;
+    return s | code;
+}
+
+// One thread per block of 32 values of a row.
+template <typename TE>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const TE *__restrict__ src, int64_t nblocks,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) load8(src + b * 32 + 8 * c, v + 8 * c);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int ex = -127;
+    if (amax > 0.0f) {
+        const int eb = static_cast<int>(__float_as_uint(amax) >> 23);   // 0 for fp32 subnormals
+        ex = eb == 0 ? -127 : eb - 127 - 8;
+        if (ex < -127) ex = -127;
+    }
+    u32x4 out[2];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) word |= e4m3_code(ldexpf(v[4 * w + q], -ex)) << (8 * q);
+        out[w >> 2][w & 3] = word;
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(codes + b * 32);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    scales[b] = static_cast<uint8_t>(ex + 127);
+}
+
+template <typename TE>
+void launch_quantize(const TE *src, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales, hipStream_t s) {
+    const int64_t nb = rows * (K / 32);
+    if (nb == 0) return;
+    hipLaunchKernelGGL(mx_quantize_kernel<TE>, dim3(static_cast<unsigned>((nb + 255) / 256)), dim3(256), 0, s, src,
+                       nb, codes, scales);
+}
+
+// --------------------------------------------------------------- GEMM
+
+constexpr int kMxBK = 128;                   // fp8 values (bytes) per k-step
+constexpr int kMxTile = 256;
+constexpr int kMxRegion = kMxTile * kMxBK;   // bytes of one operand region of a stage
+constexpr int kMxStage = 2 * kMxRegion;
+
+// byte offset of 16-byte chunk c of row r in a region
+__device__ __forceinline__ int mswz(int r, int c) { return r * kMxBK + ((c ^ ((r >> 1) & 7)) << 4); }
+
+struct MXArgs {
+    GGArgs g;              // A: weight codes [E][nb_rows][K]; tokens: g.A (codes, rows of the
+                           // segments or, with g.gather, rows of the unpermuted tokens)
+    const uint8_t *ws;     // weight scales [E][nb_rows][K/32]
+    const uint8_t *xs;     // token scales, rows as g.A
+};
+
+// Weight row (within the expert) of LDS row r of tile n_tile.
+template <int MODE>
+__device__ __forceinline__ int weight_row(int n_tile, int r, int N_out) {
+    if (MODE == kModeSwiGLU) {
+        const int jb = r >> 5;
+        const int f = n_tile * (kMxTile / 2) + (jb >> 1) * 32 + (r & 31);
+        return f < N_out ? ((jb & 1) ? N_out + f : f) : 0;
+    }
+    const int n = n_tile * kMxTile + r;
+    return n < N_out ? n : 0;
+}
+
+// Even spread of NRD fragment reads, NWR LDS writes and NLD global loads
+// over the NMF MFMAs of a half k-step.
+template <int NMF, int NRD, int NWR, int NLD, int Q = 0>
+__device__ __forceinline__ void mx_sched() {
+    if constexpr (Q < NMF) {
+        MOE_SGB(kSgMfma, 1);
+        constexpr int r = (Q + 1) * NRD / NMF - Q * NRD / NMF;
+        if constexpr (r > 0) MOE_SGB(kSgDsRead, r);
+        constexpr int w = (Q + 1) * NWR / NMF - Q * NWR / NMF;
+        if constexpr (w > 0) MOE_SGB(kSgDsWrite, w);
+        constexpr int l = (Q + 1) * NLD / NMF - Q * NLD / NMF;
+        if constexpr (l > 0) MOE_SGB(kSgVmemRead, l);
+        mx_sched<NMF, NRD, NWR, NLD, Q + 1>();
+    }
+}
+
+template <int MODE, bool HALF>
+__device__ __forceinline__ void store_tile_mx(const GGArgs &a, const TileInfo &ti,
+                                              floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane) {
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int tok0 = HALF ? 0 : (wave >> 1) * 128;
+    const int rows = min(kMxTile, ti.M - ti.m0);
+    bf16_t *Cseg = static_cast<bf16_t *>(a.C) + (static_cast<int64_t>(ti.row0) + ti.m0) * a.N_out;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int m = tok0 + j * 32 + l32;
+        if (m >= rows) continue;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int nl = 8 * gq + 4 * lhi;
+            if (MODE == kModeSwiGLU) {
+#pragma unroll
+                for (int p = 0; p < NI / 2; ++p) {
+                    const int f = ti.n_tile * (kMxTile / 2) + wrow0 / 2 + p * 32 + nl;
+                    if (f >= a.N_out) continue;
+                    float hv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[2 * p][j][4 * gq + q]) * acc[2 * p + 1][j][4 * gq + q];
+                    uint2 o;
+                    o.x = pack_bf16x2(hv[0], hv[1]);
+                    o.y = pack_bf16x2(hv[2], hv[3]);
+                    *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + f) = o;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int n = ti.n_tile * kMxTile + wrow0 + i * 32 + nl;
+                    if (n >= a.N_out) continue;
+                    uint2 o;
+                    o.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+                    o.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+                    *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + n) = o;
+                }
+            }
+        }
+    }
+}
+
+// One tile over all k-steps. Each k-step t runs two halves (k-subs s = 0,
+// 1) of NI x NJ scaled MFMAs, weight-subtile-major. Fragments stream one
+// weight subtile ahead: during the MFMAs of weight subtile i the next weight
+// fragment is read, and one (half tile: two) of the token fragments of the
+// next k-sub, so a half ends with the next k-sub's token fragments and its
+// first weight fragment in registers (80 fragment VGPRs instead of 128 for
+// two full sets). Half 0 also writes k-step t+1 (held in VGPRs) to the
+// other stage and loads k-step t+2 and the scales of k-step t+1; then this
+// wave's LDS traffic is waited for and the block synchronises; half 1 reads
+// the next k-sub from the other stage. Weight rows and (without gathering)
+// token rows are addressed as one per-lane offset plus a per-row-group
+// scalar offset, through buffer resources bounded to the tile's valid rows
+// (rows past them read as zeros and are never stored).
+template <int MODE, bool ODD, bool HALF, bool GATHER>
+__device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti, uint8_t *LB0, uint8_t *LB1) {
+    const GGArgs &a = x.g;
+    constexpr int NI = HALF ? 2 : 4;
+    constexpr int NJ = 4;
+    constexpr int NBR = NJ / NI;          // token fragments read per weight subtile
+    constexpr int XJ = HALF ? 4 : 8;      // token chunks per thread per k-step
+    constexpr int NMF = NI * NJ;          // MFMAs per half
+    constexpr int NRD = NI * 2 * (1 + NBR);   // 16-byte fragment reads per half
+    constexpr int NWR = 8 + XJ;           // chunk writes (and loads) per k-step
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int tok0 = HALF ? 0 : (wave >> 1) * 128;
+    const int K = a.K, nk = K / kMxBK, KS = K / 32;
+    const int chunk = tid & 7, rb = tid >> 3;
+    const int so = mswz(rb, chunk);
+    const int rows = min(kMxTile, ti.M - ti.m0);
+    const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
+
+    const uint8_t *wseg = static_cast<const uint8_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
+    const uint8_t *wsseg = x.ws + static_cast<int64_t>(ti.seg) * nb_rows * KS;
+    // weight rows of the tile: SwiGLU j even -> gate rows wfirst + (j/2)*32 + rb,
+    // j odd -> the up rows N_out + the same; plain: wfirst + 32 j + rb
+    const int wfirst = MODE == kModeSwiGLU ? ti.n_tile * (kMxTile / 2) : ti.n_tile * kMxTile;
+    const int wvalid = min(MODE == kModeSwiGLU ? kMxTile / 2 : kMxTile, a.N_out - wfirst);
+    const uint32_t wbytes = static_cast<uint32_t>(wvalid) * static_cast<uint32_t>(K);
+    const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wseg + static_cast<int64_t>(wfirst) * K, wbytes);
+    const __amdgpu_buffer_rsrc_t rwu =
+        make_rsrc(wseg + static_cast<int64_t>(MODE == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K, wbytes);
+    const int wlane = rb * K + chunk * 16;
+    const uint8_t *xbase = GATHER ? static_cast<const uint8_t *>(a.A)
+                                  : static_cast<const uint8_t *>(a.A) + (static_cast<int64_t>(ti.row0) + ti.m0) * K;
+    const uint8_t *xsbase = GATHER ? x.xs : x.xs + (static_cast<int64_t>(ti.row0) + ti.m0) * KS;
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(xbase, static_cast<uint32_t>(GATHER ? a.a_rows : rows) * static_cast<uint32_t>(K));
+    const __amdgpu_buffer_rsrc_t rws = make_rsrc(wsseg);
+    const __amdgpu_buffer_rsrc_t rxs =
+        make_rsrc(xsbase, static_cast<uint32_t>(GATHER ? a.a_rows : rows) * static_cast<uint32_t>(KS));
+    int xv[GATHER ? XJ : 1];
+    if constexpr (GATHER) {
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const int r = rb + 32 * j;
+            xv[j] = a.gather[ti.row0 + ti.m0 + (r < rows ? r : rows - 1)] * K + chunk * 16;
+        }
+    } else {
+        xv[0] = rb * K + chunk * 16;
+    }
+    int wsv[NI], xsv[NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wsv[i] = weight_row<MODE>(ti.n_tile, wrow0 + i * 32 + l32, a.N_out) * KS + lhi;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int r = tok0 + j * 32 + l32;
+        const int m = r < rows ? r : rows - 1;
+        xsv[j] = (GATHER ? a.gather[ti.row0 + ti.m0 + m] : m) * KS + lhi;
+    }
+
+    floatx16 acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    u32x4 RW[8], RX[XJ];
+    // scale bytes of the lane's blocks, per k-sub: [s][i] = block 2s + lhi of
+    // the row; one set for even and one for odd k-steps (byte loads, so no
+    // VALU work waits on them before their use a k-step later)
+    uint32_t SA0[2][NI], SB0[2][NJ], SA1[2][NI], SB1[2][NJ];
+    v8i fx, fy, fb0[NJ], fb1[NJ];
+
+    auto frag = [&](const uint8_t *LB, int row, int sub) -> v8i {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(LB + mswz(row, 4 * sub + lhi));
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(LB + mswz(row, 4 * sub + 2 + lhi));
+        v8i f;
+        f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+        f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+        return f;
+    };
+    auto load_step = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int soff = (MODE == kModeSwiGLU ? (j >> 1) : j) * 32 * K + kt * kMxBK;
+            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (j & 1)) ? rwu : rwg, wlane, soff, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            if constexpr (GATHER)
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], kt * kMxBK, 0);
+            else
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + kt * kMxBK, 0);
+        }
+    };
+    auto load_scales = [&](uint32_t (&SA)[2][NI], uint32_t (&SB)[2][NJ], int kt) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) SA[sub][i] = __builtin_amdgcn_raw_buffer_load_b8(rws, wsv[i], kt * 4 + 2 * sub, 0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) SB[sub][j] = __builtin_amdgcn_raw_buffer_load_b8(rxs, xsv[j], kt * 4 + 2 * sub, 0);
+        }
+    };
+    auto write_step = [&](uint8_t *LB) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(LB + so + j * 32 * kMxBK) = RW[j];
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + j * 32 * kMxBK) = RX[j];
+    };
+    // One half: MFMAs of k-sub S of stage LBc (weight fragment 0 in fx,
+    // token fragments in FBc), streaming in weight fragments of the same
+    // k-sub and the next k-sub (stage LBn, k-sub SN) into FBn and fx.
+    auto half = [&](auto s_tag, auto sn_tag, const uint8_t *LBc, const uint8_t *LBn, v8i (&FBc)[NJ],
+                    v8i (&FBn)[NJ], const uint32_t (&SA)[2][NI], const uint32_t (&SB)[2][NJ]) {
+        constexpr int S = decltype(s_tag)::value, SN = decltype(sn_tag)::value;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            v8i &fa = (i & 1) ? fy : fx;
+            v8i &fo = (i & 1) ? fx : fy;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, FBc[j], acc[i][j], 0, 0, 0, SA[S][i],
+                                                                            0, SB[S][j]);
+            fo = (i + 1 < NI) ? frag(LBc, wrow0 + (i + 1) * 32 + l32, S) : frag(LBn, wrow0 + l32, SN);
+#pragma unroll
+            for (int r = 0; r < NBR; ++r) FBn[i * NBR + r] = frag(LBn + kMxRegion, tok0 + (i * NBR + r) * 32 + l32, SN);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto step = [&](const uint8_t *CUR, uint8_t *NXT, int t, uint32_t (&SAc)[2][NI], uint32_t (&SBc)[2][NJ],
+                    uint32_t (&SAn)[2][NI], uint32_t (&SBn)[2][NJ]) {
+        const int kk = t + 2 < nk ? t + 2 : nk - 1;
+        const int kn = t + 1 < nk ? t + 1 : nk - 1;
+        half(I0{}, I1{}, CUR, CUR, fb0, fb1, SAc, SBc);
+        // the scale bytes of the next k-step, then the data of the one after
+        write_step(NXT);
+        load_scales(SAn, SBn, kn);
+        load_step(kk);
+        mx_sched<NMF, NRD, NWR, NWR>();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_LDS_BARRIER();
+        half(I1{}, I0{}, CUR, NXT, fb1, fb0, SAc, SBc);
+        mx_sched<NMF, NRD, 0, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: k-step 0 into stage 0 with its scales, k-step 1 into VGPRs
+    load_step(0);
+    load_scales(SA0, SB0, 0);
+    MOE_LDS_BARRIER();   // every wave is done reading the previous tile's stages
+    write_step(LB0);
+    load_step(nk > 1 ? 1 : 0);
+    MOE_LDS_BARRIER();
+    fx = frag(LB0, wrow0 + l32, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb0[j] = frag(LB0 + kMxRegion, tok0 + j * 32 + l32, 0);
+    if (ODD) {
+        for (int t = 0; t + 1 < nk; t += 2) {
+            step(LB0, LB1, t, SA0, SB0, SA1, SB1);
+            step(LB1, LB0, t + 1, SA1, SB1, SA0, SB0);
+        }
+        step(LB0, LB1, nk - 1, SA0, SB0, SA1, SB1);
+    } else {
+        for (int t = 0; t < nk; t += 2) {
+            step(LB0, LB1, t, SA0, SB0, SA1, SB1);
+            step(LB1, LB0, t + 1, SA1, SB1, SA0, SB0);
+        }
+    }
+    store_tile_mx<MODE, HALF>(a, ti, acc, wave, lane);
+}
+
+template <int MODE, bool ODD, bool GATHER>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
+    __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage];
+    __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage];
+    __shared__ int s_cum[kMaxSeg];
+    __shared__ int s_tmp[256];
+    const int total = __builtin_amdgcn_readfirstlane(build_tile_prefix(x.g, kMxTile, s_cum, s_tmp));
+    for (int L = xcd_block_index(blockIdx.x, x.g.grid); L < total; L += x.g.grid) {
+        const TileInfo ti = decode_tile(x.g, s_cum, L, kMxTile);
+        if (ti.M - ti.m0 > kMxTile / 2) gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LB0, LB1);
+        else gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LB0, LB1);
+    }
+}
+
+template <int MODE>
+int launch_mx(MXArgs x, int64_t P, hipStream_t s, const char *what) {
+    const int BNo = MODE == kModeSwiGLU ? 128 : 256;
+    x.g.n_tiles = (x.g.N_out + BNo - 1) / BNo;
+    const int64_t upper = (P / 256 + x.g.E) * static_cast<int64_t>(x.g.n_tiles);
+    int64_t grid = num_cus();
+    if (grid > upper) grid = upper;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid < 1) grid = 1;
+    x.g.grid = static_cast<int>(grid);
+    const bool odd = (x.g.K / kMxBK) & 1;
+    if (x.g.gather) {
+        if (odd) hipLaunchKernelGGL((grouped_gemm_mx<MODE, true, true>), dim3(x.g.grid), dim3(256), 0, s, x);
+        else hipLaunchKernelGGL((grouped_gemm_mx<MODE, false, true>), dim3(x.g.grid), dim3(256), 0, s, x);
+    } else {
+        if (odd) hipLaunchKernelGGL((grouped_gemm_mx<MODE, true, false>), dim3(x.g.grid), dim3(256), 0, s, x);
+        else hipLaunchKernelGGL((grouped_gemm_mx<MODE, false, false>), dim3(x.g.grid), dim3(256), 0, s, x);
+    }
+    return check_launch(what);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_mx_quantize(const void *src, int dtype, int64_t rows, int64_t K, uint8_t *codes,
+                               uint8_t *scales, void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(rows >= 0 && K > 0, MOE_ERR_INVALID_ARG, "moe_mx_quantize: bad sizes");
+    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
+                  "moe_mx_quantize: bad dtype %d", dtype);
+    MOE_CHECK_ARG(rows == 0 || (src && codes && scales), MOE_ERR_INVALID_ARG, "moe_mx_quantize: null pointer");
+    MOE_CHECK_ARG(K % 32 == 0, MOE_ERR_UNSUPPORTED, "moe_mx_quantize: K must be a multiple of 32");
+    MOE_CHECK_ARG(rows == 0 || (aligned16(src) && aligned16(codes)), MOE_ERR_INVALID_ARG,
+                  "moe_mx_quantize: pointers must be 16-byte aligned");
+    hipStream_t s = as_stream(stream);
+    if (dtype == MOE_DTYPE_BF16)
+        launch_quantize(static_cast<const bf16_t *>(src), rows, K, codes, scales, s);
+    else
+        launch_quantize(static_cast<const float *>(src), rows, K, codes, scales, s);
+    return check_launch("moe_mx_quantize");
+}
+
+extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scales, const int32_t *gather_rows,
+                                  int64_t x_rows, int64_t P, int64_t h, int64_t F, int E, const int32_t *offsets,
+                                  int act_kind, const uint8_t *w1_codes, const uint8_t *w1_scales,
+                                  const uint8_t *w2_codes, const uint8_t *w2_scales, void *act, uint8_t *act_codes,
+                                  uint8_t *act_scales, void *y, void *stream) {
+    clear_error();
+    MOE_CHECK_ARG(x_codes && x_scales && offsets && w1_codes && w1_scales && w2_codes && w2_scales && act &&
+                      act_codes && act_scales && y,
+                  MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: null required pointer");
+    MOE_CHECK_ARG(P >= 0 && h > 0 && F > 0 && E > 0, MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: bad sizes");
+    MOE_CHECK_ARG(act_kind == MOE_ACT_SWIGLU, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_mx: SwiGLU experts only");
+    MOE_CHECK_ARG(h % 128 == 0 && F % 128 == 0 && E <= 256, MOE_ERR_UNSUPPORTED,
+                  "moe_grouped_ffn_mx: need h %% 128 == 0, F %% 128 == 0, E <= 256");
+    MOE_CHECK_ARG(gather_rows == nullptr || x_rows > 0, MOE_ERR_INVALID_ARG,
+                  "moe_grouped_ffn_mx: gathering needs x_rows > 0");
+    const int64_t xr = gather_rows ? x_rows : P;
+    MOE_CHECK_ARG(P < (int64_t(1) << 31) && xr * h < (int64_t(1) << 31) && P * F < (int64_t(1) << 31) &&
+                      2 * F * h < (int64_t(1) << 31),
+                  MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_mx: sizes too large");
+    const void *ptrs[] = {x_codes, w1_codes, w2_codes, act, act_codes, y};
+    for (const void *p : ptrs)
+        MOE_CHECK_ARG(aligned16(p), MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: code and output pointers must be "
+                                                         "16-byte aligned");
+    const void *sp[] = {x_scales, w1_scales, w2_scales, act_scales};
+    for (const void *p : sp)
+        MOE_CHECK_ARG((reinterpret_cast<uintptr_t>(p) & 3u) == 0, MOE_ERR_INVALID_ARG,
+                      "moe_grouped_ffn_mx: scale pointers must be 4-byte aligned");
+    hipStream_t s = as_stream(stream);
+
+    MXArgs g1{};
+    g1.g.A = x_codes;
+    g1.g.gather = gather_rows;
+    g1.g.a_rows = static_cast<int>(gather_rows ? x_rows : 0);
+    g1.g.B = w1_codes;
+    g1.g.C = act;
+    g1.g.offsets = offsets;
+    g1.g.E = E;
+    g1.g.N_out = static_cast<int>(F);
+    g1.g.K = static_cast<int>(h);
+    g1.ws = w1_scales;
+    g1.xs = x_scales;
+    int st = launch_mx<kModeSwiGLU>(g1, P, s, "moe_grouped_ffn_mx gemm1");
+    if (st != MOE_OK) return st;
+
+    launch_quantize(static_cast<const bf16_t *>(act), P, F, act_codes, act_scales, s);
+    st = check_launch("moe_grouped_ffn_mx quantize");
+    if (st != MOE_OK) return st;
+
+    MXArgs g2{};
+    g2.g.A = act_codes;
+    g2.g.B = w2_codes;
+    g2.g.C = y;
+    g2.g.offsets = offsets;
+    g2.g.E = E;
+    g2.g.N_out = static_cast<int>(h);
+    g2.g.K = static_cast<int>(F);
+    g2.ws = w2_scales;
+    g2.xs = act_scales;
+    return launch_mx<kModePlain>(g2, P, s, "moe_grouped_ffn_mx gemm2");
+}

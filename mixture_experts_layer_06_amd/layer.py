@@ -150,3 +150,33 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
     return dict(grad_x=grad_x, grad_topk_w=grad_w, grad_y=grad_y, grad_w1=g["grad_w1"],
                 grad_w2=g["grad_w2"], grad_w_gate=r["grad_w_gate"], grad_b_gate=r["grad_b_gate"],
                 grad_logits_sel=r["grad_logits_sel"])
+
+
+def quantize_experts_mx(inp: dict) -> dict:
+    """MXFP8 codes and scales of the expert weights, each along its reduction
+    axis (done once, before inference)."""
+    w1q, w1s = B.moe_mx_quantize(inp["w1"])
+    w2q, w2s = B.moe_mx_quantize(inp["w2"])
+    return dict(w1_codes=w1q, w1_scales=w1s, w2_codes=w2q, w2_scales=w2s)
+
+
+def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None = None):
+    """Inference forward with the expert GEMMs in MXFP8 ("Scalable Training of
+    Mixture-of-Experts Models with Megatron Core", section 5.3.3): the router
+    as in ``forward`` (fp32 logits), the token rows quantised along h and
+    gathered by the first GEMM, the activation quantised along F between the
+    two GEMMs, the weighted combine in fp32. SwiGLU experts without bias."""
+    x = inp["x"]
+    E = inp["w_gate"].shape[0]
+    r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias"))
+    p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=False)
+    xq, xs = B.moe_mx_quantize(x)
+    f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn_mx(
+        xq, xs, p["offsets"], wq["w1_codes"], wq["w1_scales"], wq["w2_codes"], wq["w2_scales"],
+        gather_rows=p["sorted_token"]))
+    out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"])
+    res = dict(out=out)
+    res.update(r)
+    res.update(p)
+    res.update(f)
+    return res

@@ -143,6 +143,14 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert L.moe_permute_weights_bwd(None, 16, 2, dummy, dummy, None) == 1
     # unweighted combine backward still needs its output
     assert L.moe_unpermute_bwd(dummy, None, 1, 16, 64, 2, dummy, None, None, None, None) == 1
+    # MXFP8: K not a multiple of 32; h not a multiple of 128; a GELU expert
+    assert L.moe_mx_quantize(dummy, 1, 4, 48, dummy, dummy, None) == 2
+    rc = L.moe_grouped_ffn_mx(dummy, dummy, None, 0, 64, 192, 256, 4, dummy, 1, dummy, dummy, dummy, dummy, dummy,
+                              dummy, dummy, dummy, None)
+    assert rc == 2
+    rc = L.moe_grouped_ffn_mx(dummy, dummy, None, 0, 64, 256, 256, 4, dummy, 0, dummy, dummy, dummy, dummy, dummy,
+                              dummy, dummy, dummy, None)
+    assert rc == 2
     # routing variants: negative capacity, capacity above T, too small a workspace
     assert L.moe_capacity_drop(dummy, dummy, dummy, None, 1, 16, 64, 8, 2, -1, dummy, dummy, dummy, None, None) == 1
     assert L.moe_expert_choice(dummy, 16, 8, 17, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None) == 2

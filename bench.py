@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--stage-reps", type=int, default=10)
-    p.add_argument("--cpu-tokens", type=int, default=256,
+    p.add_argument("--cpu-tokens", type=int, default=2560,
                    help="tokens of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")

@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--stage-reps", type=int, default=10)
-    p.add_argument("--cpu-tokens", type=int, default=2560,
+    p.add_argument("--cpu-tokens", type=int, default=4096,
                    help="tokens of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")
@@ -476,7 +476,7 @@ def main():
         }
         if train:
             f2 = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=True,
-                               memory_efficient=meff)
+                               memory_efficient=meff, router_losses=losses)
             if meff:
                 gy, _ = B.moe_unpermute_bwd(inp["grad_out"], None, f2["row_of"], None)
                 gf = B.moe_grouped_ffn_bwd_recompute(gy, f2["x_perm"], f2["gu"], f2["offsets"],

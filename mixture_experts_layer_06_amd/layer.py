@@ -29,7 +29,8 @@ def _timed(timers, name, fn):
 
 def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = False,
             timers: dict | None = None, router_losses: bool = False,
-            memory_efficient: bool = False, recompute: bool = False, capacity: int | None = None):
+            memory_efficient: bool = False, recompute: bool = False, capacity: int | None = None,
+            want_logits: bool | None = None):
     """One forward pass. ``inp`` holds device tensors named as in
     ``workloads.make_inputs``. Returns a dict with ``out`` and the
     intermediate results of every stage. With ``timers``, the grouped FFN
@@ -49,11 +50,18 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     Tuning): every expert takes at most that many of its pairs, the first in
     token order; the rest are dropped. The result then also holds ``kept``,
     the capacity-limited dispatch the expert stages use, while the full one
-    stays for the router's backward."""
+    stays for the router's backward.
+
+    The router's logits are kept (``logits``) when the losses or the
+    backward need them (the losses; the sigmoid router's backward) or when
+    ``want_logits`` asks for them; otherwise the route may take its
+    MFMA-filtered path, whose selection and weights are the same bits."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
+    if want_logits is None:
+        want_logits = router_losses or (keep_for_backward and score == "sigmoid")
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"),
-                    sel_bias=inp.get("sel_bias"), want_logits=keep_for_backward or router_losses)
+                    sel_bias=inp.get("sel_bias"), want_logits=want_logits or router_losses)
     # inference: the first GEMM gathers token rows itself (no dispatch copy);
     # training keeps x_perm for the weight gradient of the first projection
     gather = not keep_for_backward
@@ -144,6 +152,9 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
     grad_x = B.moe_permute_bwd(g["grad_x_perm"], d["row_of"], r["grad_logits_sel"],
                                fwd["topk_idx"], inp["w_gate"])
     if coef_aux != 0.0 or coef_z != 0.0:
+        if fwd.get("logits") is None:
+            raise B.MoeError("the auxiliary losses' backward needs the forward's logits "
+                             "(run the forward with router_losses=True)")
         dl = B.moe_router_losses_bwd(fwd["logits"], fwd["counts"], k, coef_aux, coef_z)
         B.moe_router_dense_bwd(inp["x"], inp["w_gate"], dl, grad_w_gate=r["grad_w_gate"],
                                grad_b_gate=r["grad_b_gate"], grad_x=grad_x)

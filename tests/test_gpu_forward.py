@@ -38,7 +38,7 @@ def _run(name):
     inp = wl.make_inputs(cfg, device="cpu", with_grad_out=False, **kw)
     dinp = to_device(inp)
     from mixture_experts_layer_06_amd import layer
-    g = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True)
+    g = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True, want_logits=True)
     torch.cuda.synchronize()
     o = oracle_inputs(inp)
     ref = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,

@@ -31,7 +31,7 @@ def test_full_size_forward(moe_lib, cid, n_sample):
     cfg = wl.CONFIGS[cid]
     print("full-size forward, config", cid, cfg.name, flush=True)
     inp = wl.make_inputs(cfg, device="cuda", with_grad_out=False)
-    g = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=True)
+    g = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=True, want_logits=True)
     torch.cuda.synchronize()
     x = to_np32(inp["x"])
     wg = to_np32(inp["w_gate"])

@@ -548,11 +548,19 @@ def main():
                 t = stages[name]["s_median"]
                 stages[name].update(algorithmic_bytes=nbytes, gb_per_s=nbytes / t / 1e9,
                                     hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS)
-            # D^T x and D w_gate: 2 T E h FLOP each, fp32 FMA on the vector ALUs
+            # D^T x and D w_gate: 2 T E h FLOP each; with bf16 tokens and a
+            # multiple of 32 experts they run as bf16 MFMA products on D split
+            # into two bf16 halves (twice the FLOP executed), else as fp32 FMA
+            # on the vector ALUs
             fl = 4.0 * cfg.T * cfg.E * cfg.h
             t = stages["router_dense_bwd"]["s_median"]
-            stages["router_dense_bwd"].update(flops=fl, tflops=fl / t / 1e12,
-                                              valu_frac=fl / t / 1e12 / PEAK_F32_VALU_TFLOPS)
+            st = stages["router_dense_bwd"]
+            st.update(flops=fl, tflops=fl / t / 1e12)
+            if cfg.dtype == "bf16" and cfg.E % 32 == 0:
+                st.update(path="mfma, D as bf16 high + low parts", executed_flops=2 * fl,
+                          mfma_frac=2 * fl / t / 1e12 / PEAK_BF16_TFLOPS)
+            else:
+                st.update(path="vector ALU, fp32", valu_frac=fl / t / 1e12 / PEAK_F32_VALU_TFLOPS)
         out["stages"] = stages
         del flush
 

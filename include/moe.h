@@ -423,8 +423,13 @@ int moe_router_losses_bwd(const float *logits, const int32_t *counts, int64_t T,
  *                             rounded once to dtype)
  * x [T,h] and w_gate [E,h] are dtype. Sums run in a fixed order. Needs
  * h % 64 == 0, E <= 256, 16-byte aligned x, w_gate, grad_w_gate, grad_x and
- * workspace. Workspace (grad_w_gate only):
- * moe_router_dense_bwd_workspace_size(T,h,E) bytes of device memory. */
+ * workspace. With bf16 and E a multiple of 32 (and T * max(h, 2E) < 2^31)
+ * the two products run on the matrix cores: D is split into bf16 parts
+ * hi + lo (|D - hi - lo| <= 2^-16 |D| or so), every product of bf16 values is
+ * exact in fp32 and the sums are fp32; there D w_gate is rounded to bf16
+ * before the add, so grad_x takes two roundings. Workspace:
+ * moe_router_dense_bwd_workspace_size(T,h,E) bytes of device memory
+ * (required for grad_w_gate, and for grad_x on the matrix-core path). */
 size_t moe_router_dense_bwd_workspace_size(int64_t T, int64_t h, int E);
 int moe_router_dense_bwd(const void *x, const void *w_gate, int dtype, int64_t T, int64_t h,
                          int E, const float *grad_logits, float *grad_w_gate,

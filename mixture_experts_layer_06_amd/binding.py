@@ -473,7 +473,7 @@ def moe_router_dense_bwd(x, w_gate, grad_logits, grad_w_gate=None, grad_b_gate=N
     _opt(grad_w_gate, "grad_w_gate", dtype=torch.float32, shape=(E, h), device=dev)
     _opt(grad_b_gate, "grad_b_gate", dtype=torch.float32, shape=(E,), device=dev)
     _opt(grad_x, "grad_x", dtype=x.dtype, shape=(T, h), device=dev)
-    nws = lib().moe_router_dense_bwd_workspace_size(T, h, E) if grad_w_gate is not None else 0
+    nws = lib().moe_router_dense_bwd_workspace_size(T, h, E)
     ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev)
     rc = lib().moe_router_dense_bwd(_ptr(x), _ptr(w_gate), DTYPE[x.dtype], T, h, E, _ptr(grad_logits),
                                     _ptr(grad_w_gate), _ptr(grad_b_gate), _ptr(grad_x), _ptr(ws),

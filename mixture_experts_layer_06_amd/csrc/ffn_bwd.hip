@@ -426,6 +426,44 @@ int launch_bwd(BGArgs a, int64_t P, hipStream_t s, const char *what) {
 }
 
 }  // namespace
+
+// Plain grouped GEMMs of the backward kernel for other callers (the router's
+// dense backward). Weight-gradient form: C[s] [b_dim][a_dim] (fp32) =
+// B_s^T A_s over the rows of segment s (A [rows][a_dim], B [rows][b_dim],
+// both K-major with row strides lda, ldb). Data-gradient form: C [P][a_dim]
+// (bf16) = B A, B [P][K] row-major (stride ldb), A [K][a_dim] (stride lda),
+// over the segments of offsets (all with the same A).
+int bwd_wgrad_segments(const bf16_t *A, int lda, int a_dim, const bf16_t *B, int ldb, int b_dim,
+                       const int32_t *offsets, int nseg, int64_t rows, float *C, hipStream_t s) {
+    BGArgs w{};
+    w.A = A;
+    w.B = B;
+    w.C = C;
+    w.offsets = offsets;
+    w.E = nseg;
+    w.a_dim = a_dim;
+    w.b_dim = b_dim;
+    w.lda = lda;
+    w.ldb = ldb;
+    return launch_bwd<kWgrad>(w, rows, s, "wgrad gemm");
+}
+
+int bwd_dgrad_plain(const bf16_t *B, int ldb, const bf16_t *A, int lda, int a_dim, int K, const int32_t *offsets,
+                    int nseg, int64_t P, bf16_t *C, hipStream_t s) {
+    BGArgs d{};
+    d.A = A;
+    d.B = B;
+    d.C = C;
+    d.offsets = offsets;
+    d.E = nseg;
+    d.a_dim = a_dim;
+    d.K = K;
+    d.lda = lda;
+    d.ldb = ldb;
+    d.a_expert_stride = 0;
+    return launch_bwd<kDgradPlain>(d, P, s, "dgrad gemm");
+}
+
 }  // namespace moe
 
 using namespace moe;

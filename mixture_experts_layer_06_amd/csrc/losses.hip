@@ -17,7 +17,9 @@
 //
 // Every reduction has a fixed order (no floating-point atomics): per-token
 // quantities over the experts by a wave-wide shuffle tree, sums over tokens
-// in token-chunk order.
+// in token-chunk order. With bf16 operands and a multiple of 32 experts the
+// two dense products of the router backward run on MFMA (see below), else on
+// the vector ALU.
 #include "common.hpp"
 
 namespace moe {
@@ -271,7 +273,120 @@ __global__ __launch_bounds__(64) void dense_xgrad_kernel(const TE *__restrict__ 
     }
 }
 
+// ------------------------------------------------ dense backward on MFMA
+//
+// With bf16 token rows and router weights, D^T x and D w_gate run as bf16
+// matrix products on the backward's GEMM kernel: D is split into a bf16
+// high part and a bf16 low part (D = hi + lo to about 2^-16 relative), the
+// two side by side as D2 [T][2E], so that each product is exact in fp32 and
+// the sums keep fp32 accuracy:
+//   D^T x   = rows 0..E-1 + rows E..2E-1 of D2^T x  (weight-gradient GEMM
+//             over token chunks, partial sums added in chunk order)
+//   D w_gate = D2 [w_gate; w_gate]                  (data-gradient GEMM)
+
+// D2[t][e] = hi, D2[t][E + e] = lo.
+__global__ __launch_bounds__(256) void split_hilo_kernel(const float *__restrict__ D, int64_t n, int E,
+                                                         bf16_t *__restrict__ D2) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t t = i / E;
+    const int e = static_cast<int>(i - t * E);
+    const float d = D[i];
+    const bf16_t hi = f32_to_bf16(d);
+    const bf16_t lo = f32_to_bf16(d - bf16_to_f32(hi));
+    D2[t * 2 * E + e] = hi;
+    D2[t * 2 * E + E + e] = lo;
+}
+
+// W2 = [w; w]: 8 elements per thread.
+__global__ __launch_bounds__(256) void stack_twice_kernel(const bf16_t *__restrict__ w, int64_t npieces,
+                                                          bf16_t *__restrict__ w2) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= npieces) return;
+    const uint4 q = reinterpret_cast<const uint4 *>(w)[i];
+    reinterpret_cast<uint4 *>(w2)[i] = q;
+    reinterpret_cast<uint4 *>(w2)[npieces + i] = q;
+}
+
+// offs[i] = min(i * chunk, T) for i <= nchunk; then {0, T}.
+__global__ void chunk_offsets_kernel(int32_t *offs, int nchunk, int chunk, int T) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i <= nchunk) offs[i] = min(i * chunk, T);
+    if (i == 0) {
+        offs[nchunk + 1] = 0;
+        offs[nchunk + 2] = T;
+    }
+}
+
+// gw[e][c] += sum over chunks (in order) of P[ch][e][c] + P[ch][E + e][c].
+__global__ __launch_bounds__(256) void hilo_reduce_kernel(const float *__restrict__ P, int nchunk, int E, int h,
+                                                          float *__restrict__ gw) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n = static_cast<int64_t>(E) * h;
+    if (i >= n) return;
+    const int64_t stride = 2 * n;
+    float s = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < nchunk; ++c) s += P[c * stride + i] + P[c * stride + n + i];
+    gw[i] += s;
+}
+
+// gx += xo (bf16, fp32 add, one rounding): 8 elements per thread.
+__global__ __launch_bounds__(256) void add_rows_kernel(const bf16_t *__restrict__ xo, int64_t npieces,
+                                                       bf16_t *__restrict__ gx) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= npieces) return;
+    float a[8], b[8];
+    load8(gx + 8 * i, a);
+    load8(xo + 8 * i, b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] += b[q];
+    store8(gx + 8 * i, a);
+}
+
+struct DenseMfmaPlan {
+    int nchunk, chunk;
+    size_t off_w2, off_offs, off_part, off_xo, total;
+};
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Token chunks so that the weight-gradient GEMM has about one tile per
+// compute unit (tiles per chunk: ceil(h/256) * ceil(2E/256)), chunks of at
+// least 256 tokens, a multiple of 64.
+DenseMfmaPlan dense_mfma_plan(int64_t T, int64_t h, int E) {
+    DenseMfmaPlan p{};
+    const int64_t tiles = ((h + 255) / 256) * ((2 * E + 255) / 256);
+    int64_t nchunk = (256 + tiles - 1) / tiles;
+    const int64_t maxchunks = (T + 255) / 256;
+    if (nchunk > maxchunks) nchunk = maxchunks;
+    if (nchunk < 1) nchunk = 1;
+    int64_t chunk = (T + nchunk - 1) / nchunk;
+    chunk = (chunk + 63) & ~int64_t(63);
+    nchunk = (T + chunk - 1) / chunk;
+    p.nchunk = static_cast<int>(nchunk);
+    p.chunk = static_cast<int>(chunk);
+    p.off_w2 = align256(static_cast<size_t>(T) * 2 * E * sizeof(bf16_t));
+    p.off_offs = p.off_w2 + align256(static_cast<size_t>(2 * E) * h * sizeof(bf16_t));
+    p.off_part = p.off_offs + align256((nchunk + 3) * sizeof(int32_t));
+    p.off_xo = p.off_part + align256(static_cast<size_t>(nchunk) * 2 * E * h * sizeof(float));
+    p.total = p.off_xo + align256(static_cast<size_t>(T) * h * sizeof(bf16_t));
+    return p;
+}
+
+// The GEMM kernel indexes a whole operand with 32-bit offsets.
+bool dense_mfma_ok(int dtype, int64_t T, int64_t h, int E) {
+    return dtype == MOE_DTYPE_BF16 && E >= 32 && E % 32 == 0 && h < (int64_t(1) << 20) &&
+           T * (h > 2 * E ? h : 2 * E) < (int64_t(1) << 31);
+}
+
 }  // namespace
+
+int bwd_wgrad_segments(const bf16_t *A, int lda, int a_dim, const bf16_t *B, int ldb, int b_dim,
+                       const int32_t *offsets, int nseg, int64_t rows, float *C, hipStream_t s);
+int bwd_dgrad_plain(const bf16_t *B, int ldb, const bf16_t *A, int lda, int a_dim, int K, const int32_t *offsets,
+                    int nseg, int64_t P, bf16_t *C, hipStream_t s);
+
 }  // namespace moe
 
 using namespace moe;
@@ -326,7 +441,9 @@ extern "C" int moe_router_losses_bwd(const float *logits, const int32_t *counts,
 extern "C" size_t moe_router_dense_bwd_workspace_size(int64_t T, int64_t h, int E) {
     if (T <= 0 || h <= 0 || E <= 0) return 0;
     const int64_t nchunk = (T + kDenseChunk - 1) / kDenseChunk;
-    return static_cast<size_t>(nchunk) * static_cast<size_t>(E) * static_cast<size_t>(h) * sizeof(float);
+    const size_t valu = static_cast<size_t>(nchunk) * static_cast<size_t>(E) * static_cast<size_t>(h) * sizeof(float);
+    const size_t mfma = E >= 32 && E % 32 == 0 ? dense_mfma_plan(T, h, E).total : 0;
+    return valu > mfma ? valu : mfma;
 }
 
 extern "C" int moe_router_dense_bwd(const void *x, const void *w_gate, int dtype, int64_t T, int64_t h, int E,
@@ -348,6 +465,46 @@ extern "C" int moe_router_dense_bwd(const void *x, const void *w_gate, int dtype
     hipStream_t s = as_stream(stream);
     const int TT = static_cast<int>(T), hh = static_cast<int>(h);
     const unsigned ncb = static_cast<unsigned>((h + kDenseCols - 1) / kDenseCols);
+    if (dense_mfma_ok(dtype, T, h, E) && (grad_w_gate || grad_x)) {
+        const DenseMfmaPlan pl = dense_mfma_plan(T, h, E);
+        MOE_CHECK_ARG(workspace && workspace_bytes >= pl.total, MOE_ERR_WORKSPACE,
+                      "moe_router_dense_bwd: workspace of %zu bytes needed", pl.total);
+        char *ws = static_cast<char *>(workspace);
+        bf16_t *D2 = reinterpret_cast<bf16_t *>(ws);
+        int32_t *offs = reinterpret_cast<int32_t *>(ws + pl.off_offs);
+        const int64_t nd = T * E;
+        hipLaunchKernelGGL(split_hilo_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, s,
+                           grad_logits, nd, E, D2);
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(static_cast<unsigned>((pl.nchunk + 256) / 256)), dim3(256), 0,
+                           s, offs, pl.nchunk, pl.chunk, TT);
+        int st = check_launch("moe_router_dense_bwd split");
+        if (st != MOE_OK) return st;
+        if (grad_w_gate) {
+            float *part = reinterpret_cast<float *>(ws + pl.off_part);
+            st = bwd_wgrad_segments(static_cast<const bf16_t *>(x), hh, hh, D2, 2 * E, 2 * E, offs, pl.nchunk, T,
+                                    part, s);
+            if (st != MOE_OK) return st;
+            const int64_t n = static_cast<int64_t>(E) * h;
+            hipLaunchKernelGGL(hilo_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                               part, pl.nchunk, E, hh, grad_w_gate);
+        }
+        if (grad_x) {
+            bf16_t *W2 = reinterpret_cast<bf16_t *>(ws + pl.off_w2);
+            bf16_t *xo = reinterpret_cast<bf16_t *>(ws + pl.off_xo);
+            const int64_t nw = static_cast<int64_t>(E) * h / 8;
+            hipLaunchKernelGGL(stack_twice_kernel, dim3(static_cast<unsigned>((nw + 255) / 256)), dim3(256), 0, s,
+                               static_cast<const bf16_t *>(w_gate), nw, W2);
+            st = bwd_dgrad_plain(D2, 2 * E, W2, hh, hh, 2 * E, offs + pl.nchunk + 1, 1, T, xo, s);
+            if (st != MOE_OK) return st;
+            const int64_t np = T * h / 8;
+            hipLaunchKernelGGL(add_rows_kernel, dim3(static_cast<unsigned>((np + 255) / 256)), dim3(256), 0, s, xo,
+                               np, static_cast<bf16_t *>(grad_x));
+        }
+        if (grad_b_gate)
+            hipLaunchKernelGGL(dense_bgrad_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, s, grad_logits, TT, E,
+                               grad_b_gate);
+        return check_launch("moe_router_dense_bwd");
+    }
     if (grad_w_gate) {
         const size_t need = moe_router_dense_bwd_workspace_size(T, h, E);
         MOE_CHECK_ARG(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,

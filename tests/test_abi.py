@@ -181,6 +181,11 @@ def test_router_loss_workspace_sizes(lib):
     # one fp32 [E,h] partial per 256 tokens
     assert L.moe_router_dense_bwd_workspace_size(300, 128, 8) == 2 * 8 * 128 * 4
     assert L.moe_router_dense_bwd_workspace_size(0, 128, 8) == 0
+    # 32 experts: the matrix-core path's buffers, each rounded up to 256
+    # bytes: D split in two bf16 halves (300 x 64 x 2), [w; w] (64 x 128 x 2),
+    # 2 + 3 chunk offsets, 2 token chunks of fp32 partials (2 x 64 x 128 x 4),
+    # the bf16 token-gradient product (300 x 128 x 2)
+    assert L.moe_router_dense_bwd_workspace_size(300, 128, 32) == 38400 + 16384 + 256 + 65536 + 76800
 
 
 def test_recompute_workspace_size(lib):

@@ -25,6 +25,7 @@ LOSS_TOL = 1e-5
 CASES = {
     "tiny_E8_k2": wl.small_variant(wl.CONFIGS[1], T=256, h=128, F=512),
     "ragged_E16_k4": wl.small_variant(wl.CONFIGS[4], T=333, h=192, F=192, E=16, k=4),
+    "ragged_E32_k4": wl.small_variant(wl.CONFIGS[4], T=333, h=192, F=192, E=32, k=4),
     "mixtral_8x7b_layer": wl.CONFIGS[2],
     "qwen3_235b_layer": wl.CONFIGS[3],
     "deepseek_v3_layer": wl.CONFIGS[4],
@@ -85,10 +86,13 @@ def test_losses_edge_cases(moe_lib):
     assert moe_lib.moe_router_losses_bwd(empty, c0, 2, 1.0, 1.0).shape == (0, 8)
 
 
-@pytest.mark.parametrize("name", ["tiny_E8_k2", "ragged_E16_k4", "qwen3_235b_layer", "deepseek_v3_layer"])
+@pytest.mark.parametrize("name", ["tiny_E8_k2", "ragged_E16_k4", "ragged_E32_k4", "qwen3_235b_layer",
+                                  "deepseek_v3_layer"])
 def test_router_dense_backward(moe_lib, name):
     """grad_w_gate += D^T x, grad_b_gate += sum_t D, grad_x += D w_gate on
-    nonzero starting values, against the oracle's router_grads."""
+    nonzero starting values, against the oracle's router_grads. With bf16
+    tokens and a multiple of 32 experts the two products run on the matrix
+    cores (D split into bf16 high and low parts), else on the vector ALU."""
     cfg = CASES[name]
     print("case dense router backward", name, cfg.T, cfg.h, cfg.E, flush=True)
     inp = wl.make_inputs(cfg, device="cpu", router_only=True)

@@ -123,11 +123,11 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
     const int acol0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int brow0 = HALF ? 0 : (wave >> 1) * 128;
 
-    // reduction length in k-steps; wgrad: rounded up to even, rows past the
-    // expert's tokens read as zero
+    // reduction length in k-steps (wgrad: at least one, so that an expert
+    // without tokens gets zeros); rows past the expert's tokens read as zero
     const int Krows = WG ? nk_tok : a.K;
     int nk = (Krows + kBK - 1) / kBK;
-    if (WG) nk = max(2, (nk + 1) & ~1);
+    if (WG) nk = max(1, nk);
     nk = __builtin_amdgcn_readfirstlane(nk);
 
     // A: K-row storage; thread t moves chunk t % 32 of k-rows t / 32 + 8 j
@@ -215,8 +215,12 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
 #define MOE_MF(FA, FB)                                                                            \
     do {                                                                                        \
         _Pragma("unroll") for (int i = 0; i < NI; ++i)                                          \
-            _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                      \
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                    \
+                if constexpr (WG)                                                               \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[j], FA[i], acc[i][j], 0, 0, 0); \
+                else                                                                            \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+            }                                                                                   \
     } while (0)
 #define MOE_STEP(CUR, NXT, T)                                                                     \
     do {                                                                                        \
@@ -244,18 +248,13 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
     }
     MOE_LDS_BARRIER();
     MOE_RD(fa0, fb0, LB0, 0);
-    if (ODD) {
-        for (int t = 0; t + 1 < nk; t += 2) {
-            MOE_STEP(LB0, LB1, t);
-            MOE_STEP(LB1, LB0, t + 1);
-        }
-        MOE_STEP(LB0, LB1, nk - 1);
-    } else {
-        for (int t = 0; t < nk; t += 2) {
-            MOE_STEP(LB0, LB1, t);
-            MOE_STEP(LB1, LB0, t + 1);
-        }
+    // pairs of k-steps, then the odd one (dgrad: known at compile time;
+    // wgrad: the expert's token count decides)
+    for (int t = 0; t + 1 < nk; t += 2) {
+        MOE_STEP(LB0, LB1, t);
+        MOE_STEP(LB1, LB0, t + 1);
     }
+    if (ODD || (WG && (nk & 1))) MOE_STEP(LB0, LB1, nk - 1);
 #undef MOE_KROWS_RSRC
 #undef MOE_LD
 #undef MOE_WR
@@ -264,6 +263,28 @@ __device__ __forceinline__ void bwd_tile(const BGArgs &a, int e, int a0, int b0,
 #undef MOE_STEP
 
     // ------------------------------------------------------------ epilogue
+    if constexpr (WG) {
+        // The weight-gradient products run with the operands swapped, so
+        // lane l holds column acol0 + 32 i + l % 32 of rows
+        // brow0 + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4: each store writes two
+        // whole 128-byte row pieces of the fp32 tile.
+        float *Ce = static_cast<float *>(a.C) + static_cast<int64_t>(e) * a.b_dim * a.a_dim;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int col = a0 + acol0 + 32 * i + l32;
+            if (col >= a.a_dim) continue;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = b0 + brow0 + 32 * j + 8 * (v >> 2) + 4 * lhi + (v & 3);
+                    // streamed past the caches: nothing reads the tile again here
+                    if (row < a.b_dim)
+                        __builtin_nontemporal_store(acc[i][j][v], Ce + static_cast<int64_t>(row) * a.a_dim + col);
+                }
+        }
+        return;
+    }
     float dpacc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) dpacc[j] = 0.0f;
@@ -377,7 +398,12 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm(BGArgs a) {
     }
     total = __builtin_amdgcn_readfirstlane(total);
 
-    for (int L = xcd_block_index(blockIdx.x, a.grid); L < total; L += a.grid) {
+    const int cu = xcd_block_index(blockIdx.x, a.grid);
+    for (int L0 = 0; L0 < total; L0 += a.grid) {
+        // wgrad: experts by decreasing size, and every other round of tiles
+        // in reverse block order, so that the blocks' token totals even out
+        const int L = KIND == kWgrad && ((L0 / a.grid) & 1) ? L0 + a.grid - 1 - cu : L0 + cu;
+        if (L >= total) continue;
         if (KIND == kWgrad) {
             const int per = a.n_tiles_a * a.n_tiles_b;
             const int e = s_order[L / per];

@@ -20,7 +20,11 @@
 //   0..15 and 16..31), bytes 16-31 its second block (32..47, 48..63), and the
 //   scale of block b of row r comes from lane r + 32 b. So lane half g reads
 //   chunks 4s + g and 4s + 2 + g of k-sub s and supplies the scale of block
-//   2s + g (a byte load, opsel 0). Accumulators as in the bf16 kernel.
+//   2s + g. The four block scales of a row and k-step (one 4-byte word) are
+//   staged through LDS with the k-step's data, one word of weight rows and
+//   one of token rows per thread; a lane reads its row's word, shifted right
+//   by 8 g bits, so that k-sub s takes byte 2s (opsel 2s). Accumulators as
+//   in the bf16 kernel.
 // * moe_grouped_ffn_mx: first projection with SwiGLU (bf16 activation),
 //   quantisation of the activation along F, second projection (bf16 expert
 //   outputs). Tokens enter quantised along h, optionally gathered.
@@ -101,6 +105,7 @@ constexpr int kMxBK = 128;                   // fp8 values (bytes) per k-step
 constexpr int kMxTile = 256;
 constexpr int kMxRegion = kMxTile * kMxBK;   // bytes of one operand region of a stage
 constexpr int kMxStage = 2 * kMxRegion;
+constexpr int kMxScaleBytes = 2 * kMxTile * 4;   // per stage: a scale word per weight row and per token row
 
 // byte offset of 16-byte chunk c of row r in a region
 __device__ __forceinline__ int mswz(int r, int c) { return r * kMxBK + ((c ^ ((r >> 1) & 7)) << 4); }
@@ -193,7 +198,9 @@ __device__ __forceinline__ void store_tile_mx(const GGArgs &a, const TileInfo &t
 // two full sets). Half 0 also writes k-step t+1 (held in VGPRs) to the
 // other stage and loads k-step t+2 and the scales of k-step t+1; then this
 // wave's LDS traffic is waited for and the block synchronises; half 1 reads
-// the next k-sub from the other stage. Weight rows and (without gathering)
+// the next k-sub from the other stage. Half 1 still reads the current
+// stage (its weight fragments), so each k-step starts with a second block
+// synchronisation before that stage is written again. Weight rows and (without gathering)
 // token rows are addressed as one per-lane offset plus a per-row-group
 // scalar offset, through buffer resources bounded to the tile's valid rows
 // (rows past them read as zeros and are never stored).
@@ -247,15 +254,9 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     } else {
         xv[0] = rb * K + chunk * 16;
     }
-    int wsv[NI], xsv[NJ];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) wsv[i] = weight_row<MODE>(ti.n_tile, wrow0 + i * 32 + l32, a.N_out) * KS + lhi;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int r = tok0 + j * 32 + l32;
-        const int m = r < rows ? r : rows - 1;
-        xsv[j] = (GATHER ? a.gather[ti.row0 + ti.m0 + m] : m) * KS + lhi;
-    }
+    // the scale words this thread stages: weight row and token row tid of the tile
+    const int wsr = weight_row<MODE>(ti.n_tile, tid, a.N_out) * KS;
+    const int xsr = (GATHER ? a.gather[ti.row0 + ti.m0 + min(tid, rows - 1)] : min(tid, rows - 1)) * KS;
 
     floatx16 acc[NI][NJ];
 #pragma unroll
@@ -265,10 +266,10 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
     u32x4 RW[8], RX[XJ];
-    // scale bytes of the lane's blocks, per k-sub: [s][i] = block 2s + lhi of
-    // the row; one set for even and one for odd k-steps (byte loads, so no
-    // VALU work waits on them before their use a k-step later)
-    uint32_t SA0[2][NI], SB0[2][NJ], SA1[2][NI], SB1[2][NJ];
+    // the scale words of the lane's rows, shifted to its blocks; one set for
+    // even and one for odd k-steps
+    uint32_t SA0[NI], SB0[NJ], SA1[NI], SB1[NJ];
+    uint32_t RS[2];
     v8i fx, fy, fb0[NJ], fb1[NJ];
 
     auto frag = [&](const uint8_t *LB, int row, int sub) -> v8i {
@@ -292,27 +293,29 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
             else
                 RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + kt * kMxBK, 0);
         }
+        RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, kt * 4, 0);
+        RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, kt * 4, 0);
     };
-    auto load_scales = [&](uint32_t (&SA)[2][NI], uint32_t (&SB)[2][NJ], int kt) {
+    auto read_scales = [&](const uint8_t *LB, uint32_t (&SA)[NI], uint32_t (&SB)[NJ]) {
+        const uint32_t *LS = reinterpret_cast<const uint32_t *>(LB + kMxStage);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int i = 0; i < NI; ++i) SA[i] = LS[wrow0 + i * 32 + l32] >> (8 * lhi);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) SA[sub][i] = __builtin_amdgcn_raw_buffer_load_b8(rws, wsv[i], kt * 4 + 2 * sub, 0);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) SB[sub][j] = __builtin_amdgcn_raw_buffer_load_b8(rxs, xsv[j], kt * 4 + 2 * sub, 0);
-        }
+        for (int j = 0; j < NJ; ++j) SB[j] = LS[kMxTile + tok0 + j * 32 + l32] >> (8 * lhi);
     };
     auto write_step = [&](uint8_t *LB) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(LB + so + j * 32 * kMxBK) = RW[j];
 #pragma unroll
         for (int j = 0; j < XJ; ++j) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + j * 32 * kMxBK) = RX[j];
+        reinterpret_cast<uint32_t *>(LB + kMxStage)[tid] = RS[0];
+        reinterpret_cast<uint32_t *>(LB + kMxStage)[kMxTile + tid] = RS[1];
     };
     // One half: MFMAs of k-sub S of stage LBc (weight fragment 0 in fx,
     // token fragments in FBc), streaming in weight fragments of the same
     // k-sub and the next k-sub (stage LBn, k-sub SN) into FBn and fx.
     auto half = [&](auto s_tag, auto sn_tag, const uint8_t *LBc, const uint8_t *LBn, v8i (&FBc)[NJ],
-                    v8i (&FBn)[NJ], const uint32_t (&SA)[2][NI], const uint32_t (&SB)[2][NJ]) {
+                    v8i (&FBn)[NJ], const uint32_t (&SA)[NI], const uint32_t (&SB)[NJ]) {
         constexpr int S = decltype(s_tag)::value, SN = decltype(sn_tag)::value;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -320,8 +323,8 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
             v8i &fo = (i & 1) ? fx : fy;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, FBc[j], acc[i][j], 0, 0, 0, SA[S][i],
-                                                                            0, SB[S][j]);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, FBc[j], acc[i][j], 0, 0, 2 * S, SA[i],
+                                                                            2 * S, SB[j]);
             fo = (i + 1 < NI) ? frag(LBc, wrow0 + (i + 1) * 32 + l32, S) : frag(LBn, wrow0 + l32, SN);
 #pragma unroll
             for (int r = 0; r < NBR; ++r) FBn[i * NBR + r] = frag(LBn + kMxRegion, tok0 + (i * NBR + r) * 32 + l32, SN);
@@ -329,30 +332,33 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    auto step = [&](const uint8_t *CUR, uint8_t *NXT, int t, uint32_t (&SAc)[2][NI], uint32_t (&SBc)[2][NJ],
-                    uint32_t (&SAn)[2][NI], uint32_t (&SBn)[2][NJ]) {
+    auto step = [&](const uint8_t *CUR, uint8_t *NXT, int t, const uint32_t (&SAc)[NI], const uint32_t (&SBc)[NJ],
+                    uint32_t (&SAn)[NI], uint32_t (&SBn)[NJ]) {
         const int kk = t + 2 < nk ? t + 2 : nk - 1;
-        const int kn = t + 1 < nk ? t + 1 : nk - 1;
+        // NXT held k-step t-1, whose second k-sub every wave read during the
+        // second half of the previous step: all of them are past it before
+        // anyone overwrites it
+        MOE_LDS_BARRIER();
         half(I0{}, I1{}, CUR, CUR, fb0, fb1, SAc, SBc);
-        // the scale bytes of the next k-step, then the data of the one after
+        // k-step t+1 (data and scale words) to the other stage, k-step t+2 in
         write_step(NXT);
-        load_scales(SAn, SBn, kn);
         load_step(kk);
-        mx_sched<NMF, NRD, NWR, NWR>();
+        mx_sched<NMF, NRD, NWR + 2, NWR + 2>();
         __builtin_amdgcn_sched_barrier(0);
         MOE_LDS_BARRIER();
+        read_scales(NXT, SAn, SBn);
         half(I1{}, I0{}, CUR, NXT, fb1, fb0, SAc, SBc);
-        mx_sched<NMF, NRD, 0, 0>();
+        mx_sched<NMF, NRD + NI + NJ, 0, 0>();
         __builtin_amdgcn_sched_barrier(0);
     };
 
     // prologue: k-step 0 into stage 0 with its scales, k-step 1 into VGPRs
     load_step(0);
-    load_scales(SA0, SB0, 0);
     MOE_LDS_BARRIER();   // every wave is done reading the previous tile's stages
     write_step(LB0);
     load_step(nk > 1 ? 1 : 0);
     MOE_LDS_BARRIER();
+    read_scales(LB0, SA0, SB0);
     fx = frag(LB0, wrow0 + l32, 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb0[j] = frag(LB0 + kMxRegion, tok0 + j * 32 + l32, 0);
@@ -373,8 +379,8 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
 
 template <int MODE, bool ODD, bool GATHER>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
-    __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage];
-    __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage];
+    __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage + kMxScaleBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage + kMxScaleBytes];
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
     const int total = __builtin_amdgcn_readfirstlane(build_tile_prefix(x.g, kMxTile, s_cum, s_tmp));

@@ -243,14 +243,22 @@ int moe_mx_quantize(const void *src, int dtype, int64_t rows, int64_t K, uint8_t
  * moe_mx_quantize. Writes act [P,F] bf16 = silu(g)*u of the first
  * projection, its quantisation act_codes [P,F] / act_scales [P,F/32], and
  * y [P,h] bf16 of the second. fp32 accumulation. Needs h % 128 == 0,
- * F % 128 == 0; code and output pointers 16-byte aligned, scale pointers
- * 4-byte aligned. */
+ * F % 128 == 0; code, output and workspace pointers 16-byte aligned, scale
+ * pointers 4-byte aligned. Workspace (optional, NULL allowed): device memory
+ * of moe_grouped_ffn_mx_workspace_size(P,h,F,E) bytes (less is allowed); with
+ * it, when the second projection's last round of tiles would leave more
+ * than half of the compute units idle, those tiles are split along F into
+ * pieces whose fp32 partial sums are added in piece order (deterministic:
+ * the result does not depend on the grid, but differs from the unsplit sum
+ * by the reassociation). */
+size_t moe_grouped_ffn_mx_workspace_size(int64_t P, int64_t h, int64_t F, int E);
 int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scales, const int32_t *gather_rows,
                        int64_t x_rows, int64_t P, int64_t h, int64_t F, int E,
                        const int32_t *offsets, int act_kind, const uint8_t *w1_codes,
                        const uint8_t *w1_scales, const uint8_t *w2_codes,
                        const uint8_t *w2_scales, void *act, uint8_t *act_codes,
-                       uint8_t *act_scales, void *y, void *stream);
+                       uint8_t *act_scales, void *y, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /* ------------------------------------------------------- Routing variants
  * "emerging-techniques-moe-training".

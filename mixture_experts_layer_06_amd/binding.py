@@ -64,8 +64,9 @@ _SIGS = {
                           _int),
     "moe_expert_choice_workspace_size": ([_i64, _int], _sz),
     "moe_mx_quantize": ([_vp, _int, _i64, _i64, _vp, _vp, _vp], _int),
+    "moe_grouped_ffn_mx_workspace_size": ([_i64, _i64, _i64, _int], _sz),
     "moe_grouped_ffn_mx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp,
-                            _vp, _vp, _vp, _vp], _int),
+                            _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_expert_choice": ([_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_combine_rows": ([_vp, _int, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd_recompute": ([_vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
@@ -561,7 +562,9 @@ def moe_mx_quantize(src):
 
 
 def moe_grouped_ffn_mx(x_codes, x_scales, offsets, w1_codes, w1_scales, w2_codes, w2_scales,
-                       gather_rows=None, act: str = "swiglu"):
+                       gather_rows=None, act: str = "swiglu", split: bool = True):
+    """The grouped SwiGLU FFN in MXFP8. ``split``: pass a workspace, so that
+    the second projection may split its last round of tiles along F."""
     _req(x_codes, "x_codes", dtype=torch.uint8)
     dev = x_codes.device
     x_rows, h = x_codes.shape
@@ -579,9 +582,11 @@ def moe_grouped_ffn_mx(x_codes, x_scales, offsets, w1_codes, w1_scales, w2_codes
                act_codes=torch.empty((P, F), dtype=torch.uint8, device=dev),
                act_scales=torch.empty((P, F // 32), dtype=torch.uint8, device=dev),
                y=torch.empty((P, h), dtype=torch.bfloat16, device=dev))
+    nws = lib().moe_grouped_ffn_mx_workspace_size(P, h, F, E) if split else 0
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev) if nws else None
     rc = lib().moe_grouped_ffn_mx(_ptr(x_codes), _ptr(x_scales), _ptr(gather_rows), x_rows, P, h, F, E,
                                   _ptr(offsets), ACT[act], _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
                                   _ptr(w2_scales), _ptr(out["act"]), _ptr(out["act_codes"]),
-                                  _ptr(out["act_scales"]), _ptr(out["y"]), _stream(x_codes))
+                                  _ptr(out["act_scales"]), _ptr(out["y"]), _ptr(ws), nws, _stream(x_codes))
     _check(rc, "moe_grouped_ffn_mx")
     return out

@@ -205,7 +205,8 @@ __device__ __forceinline__ void store_tile_mx(const GGArgs &a, const TileInfo &t
 // scalar offset, through buffer resources bounded to the tile's valid rows
 // (rows past them read as zeros and are never stored).
 template <int MODE, bool ODD, bool HALF, bool GATHER>
-__device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti, uint8_t *LB0, uint8_t *LB1) {
+__device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti, uint8_t *LB0, uint8_t *LB1, int k0,
+                                             int nks, float *part) {
     const GGArgs &a = x.g;
     constexpr int NI = HALF ? 2 : 4;
     constexpr int NJ = 4;
@@ -219,7 +220,10 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int tok0 = HALF ? 0 : (wave >> 1) * 128;
-    const int K = a.K, nk = K / kMxBK, KS = K / 32;
+    // k-steps [k0, k0 + nks) of the tile (all of them unless a split piece)
+    const int K = a.K, KS = K / 32;
+    k0 = __builtin_amdgcn_readfirstlane(k0);
+    const int nk = __builtin_amdgcn_readfirstlane(nks);
     const int chunk = tid & 7, rb = tid >> 3;
     const int so = mswz(rb, chunk);
     const int rows = min(kMxTile, ti.M - ti.m0);
@@ -284,17 +288,18 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int soff = (MODE == kModeSwiGLU ? (j >> 1) : j) * 32 * K + kt * kMxBK;
-            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (j & 1)) ? rwu : rwg, wlane, soff, 0);
+            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (j & 1)) ? rwu : rwg, wlane,
+                                                          soff + k0 * kMxBK, 0);
         }
 #pragma unroll
         for (int j = 0; j < XJ; ++j) {
             if constexpr (GATHER)
-                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], kt * kMxBK, 0);
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], (k0 + kt) * kMxBK, 0);
             else
-                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + kt * kMxBK, 0);
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + (k0 + kt) * kMxBK, 0);
         }
-        RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, kt * 4, 0);
-        RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, kt * 4, 0);
+        RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, (k0 + kt) * 4, 0);
+        RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, (k0 + kt) * 4, 0);
     };
     auto read_scales = [&](const uint8_t *LB, uint32_t (&SA)[NI], uint32_t (&SB)[NJ]) {
         const uint32_t *LS = reinterpret_cast<const uint32_t *>(LB + kMxStage);
@@ -374,7 +379,53 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
             step(LB1, LB0, t + 1, SA1, SB1, SA0, SB0);
         }
     }
+    if (part) {
+        // a split piece: the raw accumulators, element e = 16 (i*4 + j) + q of
+        // thread tid at float4 index (e/4) * 256 + tid
+        float4 *P4 = reinterpret_cast<float4 *>(part);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    P4[((i * NJ + j) * 4 + q) * 256 + tid] =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        return;
+    }
     store_tile_mx<MODE, HALF>(a, ti, acc, wave, lane);
+}
+
+// Split workspace (second projection only): an int header of 64 KB ([0..2]:
+// split tiles, pieces per tile, k-steps per piece; from int 64, 8 ints per
+// split tile: seg, m0, n_tile, M, row0), then fp32 partial tiles of
+// kMxPartFloats each, piece p of split tile t at index t * s + p.
+constexpr int kMxWsHeaderInts = 16384;
+constexpr int kMxWsMaxSplitTiles = (kMxWsHeaderInts - 64) / 8;
+constexpr int kMxPartFloats = kMxTile * kMxTile;
+
+// When the last round of tiles would leave more than half of the blocks
+// idle, its tiles are split along K into s pieces of ps k-steps (ps even)
+// so that it keeps up to G blocks busy; split_reduce_mx sums each tile's
+// pieces in piece order (deterministic) and runs the epilogue. Every block
+// derives the same plan from the segment offsets.
+struct MxSplitPlan {
+    int full, s, ps, items;   // whole tiles, pieces per split tile, k-steps per piece, work items
+};
+
+__device__ __forceinline__ MxSplitPlan mx_split_plan(const GGArgs &a, int total, int nk, bool odd) {
+    MxSplitPlan p{total, 0, 0, total};
+    const int G = a.grid, rem = total % G;
+    if (odd || a.ws == nullptr || rem == 0 || 2 * rem > G || nk < 4) return p;
+    int s = min(G / rem, nk / 2);
+    const int ps = 2 * ((nk + 2 * s - 1) / (2 * s));
+    s = (nk + ps - 1) / ps;
+    if (s < 2 || rem * s > a.ws_tiles || rem > kMxWsMaxSplitTiles) return p;
+    p.full = total - rem;
+    p.s = s;
+    p.ps = ps;
+    p.items = p.full + rem * s;
+    return p;
 }
 
 template <int MODE, bool ODD, bool GATHER>
@@ -384,11 +435,112 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
     const int total = __builtin_amdgcn_readfirstlane(build_tile_prefix(x.g, kMxTile, s_cum, s_tmp));
-    for (int L = xcd_block_index(blockIdx.x, x.g.grid); L < total; L += x.g.grid) {
-        const TileInfo ti = decode_tile(x.g, s_cum, L, kMxTile);
-        if (ti.M - ti.m0 > kMxTile / 2) gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LB0, LB1);
-        else gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LB0, LB1);
+    const int nk = x.g.K / kMxBK;
+    // split pieces only in the plain (second) projection
+    const MxSplitPlan sp = mx_split_plan(x.g, total, nk, ODD || MODE != kModePlain || GATHER);
+    int *hdr = reinterpret_cast<int *>(x.g.ws);
+    if (MODE == kModePlain && hdr && blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[0] = sp.s ? total - sp.full : 0;
+        hdr[1] = sp.s;
+        hdr[2] = sp.ps;
     }
+    for (int w = xcd_block_index(blockIdx.x, x.g.grid); w < sp.items; w += x.g.grid) {
+        int L = w, k0 = 0, nks = nk;
+        float *part = nullptr;
+        if (sp.s && w >= sp.full) {
+            const int q = w - sp.full;
+            L = sp.full + q / sp.s;
+            k0 = (q % sp.s) * sp.ps;
+            nks = min(sp.ps, nk - k0);
+            part = x.g.ws + kMxWsHeaderInts + static_cast<int64_t>(q) * kMxPartFloats;
+        }
+        const TileInfo ti = decode_tile(x.g, s_cum, L, kMxTile);
+        if (part && k0 == 0 && threadIdx.x == 0) {
+            int *d = hdr + 64 + (L - sp.full) * 8;
+            d[0] = ti.seg;
+            d[1] = ti.m0;
+            d[2] = ti.n_tile;
+            d[3] = ti.M;
+            d[4] = ti.row0;
+        }
+        if (ti.M - ti.m0 > kMxTile / 2) gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LB0, LB1, k0, nks, part);
+        else gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LB0, LB1, k0, nks, part);
+    }
+}
+
+// A split tile's partial sums (s pieces, piece order), then the plain epilogue.
+template <bool HALF>
+__device__ __forceinline__ void mx_reduce_tile(const GGArgs &a, const TileInfo &ti, const float4 *P4, int s) {
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    const int tid = threadIdx.x;
+    floatx16 acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    for (int p = 0; p < s; ++p) {
+        const float4 *Pp = P4 + static_cast<int64_t>(p) * (kMxPartFloats / 4);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = Pp[((i * NJ + j) * 4 + q) * 256 + tid];
+                    acc[i][j][4 * q] += v.x;
+                    acc[i][j][4 * q + 1] += v.y;
+                    acc[i][j][4 * q + 2] += v.z;
+                    acc[i][j][4 * q + 3] += v.w;
+                }
+    }
+    store_tile_mx<kModePlain, HALF>(a, ti, acc, tid >> 6, tid & 63);
+}
+
+// Sum of every split tile's pieces, in piece order, into piece 0 (one
+// float4 per thread, all tiles' positions spread over the grid).
+__global__ __launch_bounds__(256) void split_sum_mx(GGArgs a) {
+    const int *hdr = reinterpret_cast<const int *>(a.ws);
+    const int rem = hdr[0], s = hdr[1];
+    if (s < 2) return;
+    constexpr int kQ = kMxPartFloats / 4;
+    const int64_t n = static_cast<int64_t>(rem) * kQ;
+    float4 *P4 = reinterpret_cast<float4 *>(a.ws + kMxWsHeaderInts);
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t t = i / kQ, f = i - t * kQ;
+        float4 *base = P4 + t * s * kQ + f;
+        float4 acc = base[0];
+        for (int p = 1; p < s; ++p) {
+            const float4 v = base[static_cast<int64_t>(p) * kQ];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        base[0] = acc;
+    }
+}
+
+// One block per split tile: its summed piece 0, then the plain epilogue.
+__global__ __launch_bounds__(256, 1) void split_reduce_mx(GGArgs a) {
+    const int *hdr = reinterpret_cast<const int *>(a.ws);
+    const int rem = hdr[0], s = hdr[1] > 0 ? 1 : 0;   // the pieces are summed into piece 0
+    const int t = blockIdx.x;
+    if (s == 0 || t >= rem) return;
+    const int *d = hdr + 64 + t * 8;
+    TileInfo ti;
+    ti.seg = d[0];
+    ti.m0 = d[1];
+    ti.n_tile = d[2];
+    ti.M = d[3];
+    ti.row0 = d[4];
+    ti.shared = false;
+    const float4 *P4 = reinterpret_cast<const float4 *>(a.ws + kMxWsHeaderInts) +
+                       static_cast<int64_t>(t) * hdr[1] * (kMxPartFloats / 4);
+    if (ti.M - ti.m0 <= kMxTile / 2) mx_reduce_tile<true>(a, ti, P4, s);
+    else mx_reduce_tile<false>(a, ti, P4, s);
 }
 
 template <int MODE>
@@ -408,6 +560,12 @@ int launch_mx(MXArgs x, int64_t P, hipStream_t s, const char *what) {
     } else {
         if (odd) hipLaunchKernelGGL((grouped_gemm_mx<MODE, true, false>), dim3(x.g.grid), dim3(256), 0, s, x);
         else hipLaunchKernelGGL((grouped_gemm_mx<MODE, false, false>), dim3(x.g.grid), dim3(256), 0, s, x);
+    }
+    // split tiles: at most half the grid (the plan's condition)
+    if (MODE == kModePlain && x.g.ws != nullptr && !odd && !x.g.gather) {
+        hipLaunchKernelGGL(split_sum_mx, dim3(1024), dim3(256), 0, s, x.g);
+        hipLaunchKernelGGL(split_reduce_mx, dim3(static_cast<unsigned>(x.g.grid / 2 > 0 ? x.g.grid / 2 : 1)), dim3(256), 0,
+                           s, x.g);
     }
     return check_launch(what);
 }
@@ -435,11 +593,19 @@ extern "C" int moe_mx_quantize(const void *src, int dtype, int64_t rows, int64_t
     return check_launch("moe_mx_quantize");
 }
 
+extern "C" size_t moe_grouped_ffn_mx_workspace_size(int64_t P, int64_t h, int64_t F, int E) {
+    if (P <= 0 || h <= 0 || F <= 0 || E <= 0) return 0;
+    // the header and 256 partial tiles (one per compute unit of the MI355X;
+    // a grid of more blocks would split fewer tiles)
+    return static_cast<size_t>(kMxWsHeaderInts) * 4 + static_cast<size_t>(256) * kMxPartFloats * 4;
+}
+
 extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scales, const int32_t *gather_rows,
                                   int64_t x_rows, int64_t P, int64_t h, int64_t F, int E, const int32_t *offsets,
                                   int act_kind, const uint8_t *w1_codes, const uint8_t *w1_scales,
                                   const uint8_t *w2_codes, const uint8_t *w2_scales, void *act, uint8_t *act_codes,
-                                  uint8_t *act_scales, void *y, void *stream) {
+                                  uint8_t *act_scales, void *y, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
     clear_error();
     MOE_CHECK_ARG(x_codes && x_scales && offsets && w1_codes && w1_scales && w2_codes && w2_scales && act &&
                       act_codes && act_scales && y,
@@ -454,10 +620,10 @@ extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scale
     MOE_CHECK_ARG(P < (int64_t(1) << 31) && xr * h < (int64_t(1) << 31) && P * F < (int64_t(1) << 31) &&
                       2 * F * h < (int64_t(1) << 31),
                   MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_mx: sizes too large");
-    const void *ptrs[] = {x_codes, w1_codes, w2_codes, act, act_codes, y};
+    const void *ptrs[] = {x_codes, w1_codes, w2_codes, act, act_codes, y, workspace};
     for (const void *p : ptrs)
-        MOE_CHECK_ARG(aligned16(p), MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: code and output pointers must be "
-                                                         "16-byte aligned");
+        MOE_CHECK_ARG(p == workspace && p == nullptr ? true : aligned16(p), MOE_ERR_INVALID_ARG,
+                      "moe_grouped_ffn_mx: code, output and workspace pointers must be 16-byte aligned");
     const void *sp[] = {x_scales, w1_scales, w2_scales, act_scales};
     for (const void *p : sp)
         MOE_CHECK_ARG((reinterpret_cast<uintptr_t>(p) & 3u) == 0, MOE_ERR_INVALID_ARG,
@@ -493,5 +659,12 @@ extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scale
     g2.g.K = static_cast<int>(F);
     g2.ws = w2_scales;
     g2.xs = act_scales;
+    // split pieces of the last round of tiles, when a workspace is given
+    const size_t hdr = static_cast<size_t>(kMxWsHeaderInts) * 4;
+    if (workspace && workspace_bytes >= hdr + static_cast<size_t>(kMxPartFloats) * 4) {
+        g2.g.ws = static_cast<float *>(workspace);
+        const size_t nt = (workspace_bytes - hdr) / (static_cast<size_t>(kMxPartFloats) * 4);
+        g2.g.ws_tiles = static_cast<int>(nt < (1u << 20) ? nt : (1u << 20));
+    }
     return launch_mx<kModePlain>(g2, P, s, "moe_grouped_ffn_mx gemm2");
 }

@@ -146,11 +146,15 @@ def test_host_validation_rejects_bad_arguments(lib):
     # MXFP8: K not a multiple of 32; h not a multiple of 128; a GELU expert
     assert L.moe_mx_quantize(dummy, 1, 4, 48, dummy, dummy, None) == 2
     rc = L.moe_grouped_ffn_mx(dummy, dummy, None, 0, 64, 192, 256, 4, dummy, 1, dummy, dummy, dummy, dummy, dummy,
-                              dummy, dummy, dummy, None)
+                              dummy, dummy, dummy, None, 0, None)
     assert rc == 2
     rc = L.moe_grouped_ffn_mx(dummy, dummy, None, 0, 64, 256, 256, 4, dummy, 0, dummy, dummy, dummy, dummy, dummy,
-                              dummy, dummy, dummy, None)
+                              dummy, dummy, dummy, None, 0, None)
     assert rc == 2
+    # a misaligned workspace
+    rc = L.moe_grouped_ffn_mx(dummy, dummy, None, 0, 64, 256, 256, 4, dummy, 1, dummy, dummy, dummy, dummy, dummy,
+                              dummy, dummy, dummy, vp(4098), 1 << 20, None)
+    assert rc == 1
     # routing variants: negative capacity, capacity above T, too small a workspace
     assert L.moe_capacity_drop(dummy, dummy, dummy, None, 1, 16, 64, 8, 2, -1, dummy, dummy, dummy, None, None) == 1
     assert L.moe_expert_choice(dummy, 16, 8, 17, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None) == 2
@@ -186,6 +190,14 @@ def test_router_loss_workspace_sizes(lib):
     # 2 + 3 chunk offsets, 2 token chunks of fp32 partials (2 x 64 x 128 x 4),
     # the bf16 token-gradient product (300 x 128 x 2)
     assert L.moe_router_dense_bwd_workspace_size(300, 128, 32) == 38400 + 16384 + 256 + 65536 + 76800
+
+
+def test_mx_ffn_workspace_size(lib):
+    """64 KB of header and 256 fp32 partial tiles of 256 x 256 (host logic:
+    no device needed)."""
+    L = lib
+    assert L.moe_grouped_ffn_mx_workspace_size(8192, 4096, 14336, 8) == 65536 + 256 * 256 * 256 * 4
+    assert L.moe_grouped_ffn_mx_workspace_size(0, 4096, 14336, 8) == 0
 
 
 def test_recompute_workspace_size(lib):

@@ -154,3 +154,43 @@ def test_mxfp8_handbook_layer_full_size_sampled(moe_lib):
     err = rel_err_tensor(got, ref["out"])
     print("sampled out rel err: tensor %.3g, row-wise %.3g" % (err, rel_err(got, ref["out"])), flush=True)
     assert err <= TOL["bf16"], err
+
+
+def test_mxfp8_split_second_projection(moe_lib):
+    """A layer whose second projection leaves a short last round of tiles
+    (4096 tokens, top-2 of 8 experts, h = 2048: about 288 tiles of 256 x 256
+    for 256 compute units), so its last tiles are split along F into
+    pieces: tokens of the last expert (whose tiles are the split ones) and a
+    spread of others against the oracle's MXFP8 layer, and the split result
+    against the unsplit one (the same products, summed in another order)."""
+    from mixture_experts_layer_06_amd import binding as B
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[2], T=4096, h=2048, F=1024)
+    print("case mxfp8 split", cfg.T, cfg.h, cfg.F, flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=False)
+    o = oracle_inputs(inp)
+    rt = oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score)
+    counts = np.bincount(rt["topk_idx"].reshape(-1), minlength=cfg.E)
+    tiles = int(sum((int(c) + 255) // 256 for c in counts)) * (cfg.h // 256)
+    rem = tiles % 256
+    assert 0 < 2 * rem <= 256, (tiles, rem)   # the split plan's condition on a 256-block grid
+    last = np.nonzero((rt["topk_idx"] == cfg.E - 1).any(axis=1))[0]
+    tokens = np.unique(np.concatenate([last[:: max(1, len(last) // 24)], np.linspace(0, cfg.T - 1, 8).astype(np.int64)]))
+    dinp = to_device(inp)
+    wq = layer.quantize_experts_mx(dinp)
+    g = layer.forward_mxfp8(dinp, wq, cfg.k, cfg.score)
+    torch.cuda.synchronize()
+    ref = oracle.forward_mxfp8(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act, tokens=tokens)
+    got = to_np32(g["out"][torch.as_tensor(tokens, device="cuda")])
+    err = rel_err_tensor(got, ref["out"])
+    print("sampled out rel err: tensor %.3g, row-wise %.3g" % (err, rel_err(got, ref["out"])), flush=True)
+    assert err <= TOL["bf16"], err
+    xq, xs = B.moe_mx_quantize(dinp["x"])
+    args = (xq, xs, g["offsets"], wq["w1_codes"], wq["w1_scales"], wq["w2_codes"], wq["w2_scales"])
+    a = B.moe_grouped_ffn_mx(*args, gather_rows=g["sorted_token"], split=True)
+    b = B.moe_grouped_ffn_mx(*args, gather_rows=g["sorted_token"], split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a["act_codes"], b["act_codes"])
+    d = rel_err_tensor(to_np32(a["y"]), to_np32(b["y"]))
+    print("split vs unsplit y: %.3g" % d, flush=True)
+    assert d <= 1e-2, d

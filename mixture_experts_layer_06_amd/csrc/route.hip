@@ -433,48 +433,6 @@ __global__ __launch_bounds__(64) void row_norm_kernel(const bf16_t *__restrict__
     if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(s);
 }
 
-// Fixed-order logits of two (token, expert) pairs by a whole wave: lane r
-// owns residue r, i.e. the fma chain of partial sum r over ascending chunks
-// (x[64 c + r] from the token's row, read from memory: the norm pass just
-// brought it into the caches), then the halving tree s = 32..1
-// across lanes (part[j] += part[j+s] is lane j adding lane j+s). The same
-// operations as route_kernel's, so the same bits; the result is in lane 0.
-// Two experts at a time, 16 chunks per step: 32 gate loads in flight.
-__device__ __forceinline__ void gate_dot_pair(const bf16_t *__restrict__ xl, const bf16_t *__restrict__ w0,
-                                              const bf16_t *__restrict__ w1, int nch, int lane, float &l0,
-                                              float &l1) {
-    float a0 = 0.0f, a1 = 0.0f;
-    int c0 = 0;
-    for (; c0 + 16 <= nch; c0 += 16) {
-        bf16_t v0[16], v1[16], xv[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            v0[c] = w0[64 * (c0 + c) + lane];
-            v1[c] = w1[64 * (c0 + c) + lane];
-        }
-#pragma unroll
-        for (int c = 0; c < 16; ++c) xv[c] = xl[64 * (c0 + c) + lane];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const float xf = bf16_to_f32(xv[c]);
-            a0 = fmaf(xf, bf16_to_f32(v0[c]), a0);
-            a1 = fmaf(xf, bf16_to_f32(v1[c]), a1);
-        }
-    }
-    for (; c0 < nch; ++c0) {
-        const float xf = bf16_to_f32(xl[64 * c0 + lane]);
-        a0 = fmaf(xf, bf16_to_f32(w0[64 * c0 + lane]), a0);
-        a1 = fmaf(xf, bf16_to_f32(w1[64 * c0 + lane]), a1);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        a0 = a0 + __shfl_down(a0, off);
-        a1 = a1 + __shfl_down(a1, off);
-    }
-    l0 = a0;
-    l1 = a1;
-}
-
 // One wave per token (4 per block). Lane l holds experts l + 64 m.
 template <int SIGMOID>
 __global__ __launch_bounds__(256) void route_select_kernel(
@@ -488,7 +446,6 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;   // no block-wide barrier below
     const bf16_t *xrow = x + static_cast<int64_t>(t) * h;
-    const int nch = h >> 6;
 
     // |x_t|_2 (fp32; its rounding is far inside the factor-2 margins)
     float xs = 0.0f;
@@ -574,15 +531,19 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-    // exact logits of the candidates, two at a time over the whole wave
-    for (int ci = 0; ci < nc; ci += 2) {
-        const int e0 = s_cand[wave][ci];
-        const int e1 = ci + 1 < nc ? s_cand[wave][ci + 1] : e0;
-        float l0, l1;
-        gate_dot_pair(xrow, wg + static_cast<int64_t>(e0) * h, wg + static_cast<int64_t>(e1) * h, nch, lane, l0, l1);
-        if (lane == 0) {
-            s_cl[wave][ci] = bg ? l0 + bg[e0] : l0;
-            if (ci + 1 < nc) s_cl[wave][ci + 1] = bg ? l1 + bg[e1] : l1;
+    // exact logits of the candidates, eight at a time: lane group g (8
+    // lanes) takes candidate c0 + g with route_kernel's fixed-order dot
+    // product (lane q: residues 8q..8q+7 of each 64-chunk, 16-byte pieces),
+    // so the same bits as the fixed-order pass
+    {
+        const int g = lane >> 3, q = lane & 7;
+        for (int c0 = 0; c0 < nc; c0 += 8) {
+            const int ci = c0 + g;
+            const int e = s_cand[wave][ci < nc ? ci : nc - 1];
+            float acc[1][8];
+            gate_item<bf16_t, 1, 8>(xrow + 8 * q, wg, h, E, e, q, acc);
+            const float l = gate_tree(acc[0]);
+            if (q == 0 && ci < nc) s_cl[wave][ci] = bg ? l + bg[e] : l;
         }
     }
     __builtin_amdgcn_wave_barrier();

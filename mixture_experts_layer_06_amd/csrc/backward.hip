@@ -17,7 +17,9 @@
 // expert over many workgroups without floating-point atomics, each segment is
 // cut into chunks of kRC rows; pass 1 writes one partial sum per chunk, pass 2
 // adds an expert's chunks in chunk order. Both orders are fixed, so the
-// result is deterministic.
+// result is deterministic. The logit gradient of each permuted row is looked
+// up once beforehand (one thread per row), so that pass 1 only streams rows
+// of x, four rows per thread in flight.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -52,6 +54,28 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(int T, int k, int E, 
     }
 }
 
+// dl_row[r] = dl of permuted row r: the token t = sorted_token[r] of expert
+// e's segment (the largest e with offsets[e] <= r) at the slot j where
+// topk_idx[t][j] == e.
+__global__ __launch_bounds__(256) void route_bwd_rowdl_kernel(int P, int E, int k, const int32_t *__restrict__ offsets,
+                                                              const int32_t *__restrict__ sorted_token,
+                                                              const int32_t *__restrict__ topk_idx,
+                                                              const float *__restrict__ dl, float *__restrict__ dl_row) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= P) return;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    const int64_t t = sorted_token[r];
+    float d = 0.0f;
+    for (int j = 0; j < k; ++j)
+        if (topk_idx[t * k + j] == lo) d = dl[t * k + j];
+    dl_row[r] = d;
+}
+
 // Chunk prefix over experts in LDS: s_ck[e] = chunks of experts < e.
 __device__ int build_chunk_prefix(const int32_t *offsets, int E, int *s_ck, int *s_tmp) {
     const int t = threadIdx.x;
@@ -72,9 +96,9 @@ __device__ int build_chunk_prefix(const int32_t *offsets, int E, int *s_ck, int 
 
 template <typename TE>
 __global__ __launch_bounds__(256) void route_bwd_partial_kernel(
-    const TE *__restrict__ x, int h, int E, int k, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ sorted_token, const int32_t *__restrict__ topk_idx,
-    const float *__restrict__ dl, float *__restrict__ partial, float *__restrict__ partial_b) {
+    const TE *__restrict__ x, int h, int E, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_token, const float *__restrict__ dl_row, float *__restrict__ partial,
+    float *__restrict__ partial_b) {
     __shared__ int s_ck[256];
     __shared__ int s_tmp[256];
     __shared__ float s_acc[4][kCB];
@@ -96,17 +120,26 @@ __global__ __launch_bounds__(256) void route_bwd_partial_kernel(
     const int col = blockIdx.y * kCB + (threadIdx.x & 63) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float bsum = 0.0f;
-    for (int r = r0 + grp; r < r1; r += 4) {
-        const int t = sorted_token[r];
-        float d = 0.0f;
-        for (int j = 0; j < k; ++j)
-            if (topk_idx[static_cast<int64_t>(t) * k + j] == e) d = dl[static_cast<int64_t>(t) * k + j];
-        bsum += d;
-        if (col < h) {
-            float xv[8];
-            load8(x + static_cast<int64_t>(t) * h + col, xv);
+    // rows r0 + grp + 4 i, ascending; four of them loaded before use
+    const int cc = col < h ? col : 0;   // out-of-range columns load column 0, never stored
+    for (int rb = r0 + grp; rb < r1; rb += 16) {
+        float d[4], xv[4][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(d, xv[i], acc[i]);
+        for (int u = 0; u < 4; ++u) {
+            const int r = rb + 4 * u;
+            d[u] = 0.0f;
+            if (r < r1) {
+                d[u] = dl_row[r];
+                load8(x + static_cast<int64_t>(sorted_token[r]) * h + cc, xv[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (rb + 4 * u < r1) {
+                bsum += d[u];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(d[u], xv[u][i], acc[i]);
+            }
         }
     }
     const int c0 = (threadIdx.x & 63) * 8;
@@ -159,7 +192,7 @@ using namespace moe;
 extern "C" size_t moe_route_bwd_workspace_size(int64_t T, int64_t h, int E, int k) {
     if (T < 0 || h <= 0 || E <= 0 || k <= 0) return 0;
     const int64_t nq = (T * k) / kRC + E + 1;
-    return static_cast<size_t>(nq * h + nq) * sizeof(float) + 256;
+    return static_cast<size_t>(nq * h + nq + T * k) * sizeof(float) + 256;
 }
 
 extern "C" int moe_route_bwd(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
@@ -192,19 +225,24 @@ extern "C" int moe_route_bwd(const void *x, int dtype, int64_t T, int64_t h, int
     const int64_t nq = (T * k) / kRC + E + 1;
     float *partial = static_cast<float *>(workspace);
     float *partial_b = partial + nq * h;
+    float *dl_row = partial_b + nq;
+    const int P = static_cast<int>(T * k);
     if (T > 0)
         hipLaunchKernelGGL(route_bwd_dl_kernel, dim3(static_cast<unsigned>((T + 255) / 256)), dim3(256), 0,
                            s, static_cast<int>(T), k, E, score == MOE_SCORE_SIGMOID, logits, topk_idx,
                            topk_w, grad_topk_w, grad_logits_sel);
+    if (P > 0)
+        hipLaunchKernelGGL(route_bwd_rowdl_kernel, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0, s, P,
+                           E, k, offsets, sorted_token, topk_idx, grad_logits_sel, dl_row);
     const dim3 g1(static_cast<unsigned>(nq), static_cast<unsigned>((h + kCB - 1) / kCB));
     if (dtype == MOE_DTYPE_BF16)
         hipLaunchKernelGGL(route_bwd_partial_kernel<bf16_t>, g1, dim3(256), 0, s,
-                           static_cast<const bf16_t *>(x), static_cast<int>(h), E, k, offsets,
-                           sorted_token, topk_idx, grad_logits_sel, partial, partial_b);
+                           static_cast<const bf16_t *>(x), static_cast<int>(h), E, offsets, sorted_token, dl_row,
+                           partial, partial_b);
     else
         hipLaunchKernelGGL(route_bwd_partial_kernel<float>, g1, dim3(256), 0, s,
-                           static_cast<const float *>(x), static_cast<int>(h), E, k, offsets,
-                           sorted_token, topk_idx, grad_logits_sel, partial, partial_b);
+                           static_cast<const float *>(x), static_cast<int>(h), E, offsets, sorted_token, dl_row,
+                           partial, partial_b);
     unsigned gy = static_cast<unsigned>((h + 2047) / 2048);
     hipLaunchKernelGGL(route_bwd_reduce_kernel, dim3(E, gy), dim3(256), 0, s, static_cast<int>(h), E,
                        offsets, partial, partial_b, grad_w_gate, grad_b_gate);

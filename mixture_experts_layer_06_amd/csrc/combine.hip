@@ -40,6 +40,35 @@ __device__ __forceinline__ void load8_nt(const float *p, float *v) {
         v[4 + c] = __uint_as_float(b[c]);
     }
 }
+// Raw 8-element pieces: the load only (converted to fp32 where used), so a
+// load under a condition does not make the wave wait for it right there.
+template <typename TE> struct Raw8 {
+    u32x4 q[sizeof(TE) / 2];   // bf16: one 16-byte piece, fp32: two
+};
+template <typename TE> __device__ __forceinline__ void raw8_load_nt(const TE *p, Raw8<TE> &r) {
+#pragma unroll
+    for (int c = 0; c < static_cast<int>(sizeof(TE) / 2); ++c)
+        r.q[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + c);
+}
+template <typename TE> __device__ __forceinline__ void raw8_load(const TE *p, Raw8<TE> &r) {
+#pragma unroll
+    for (int c = 0; c < static_cast<int>(sizeof(TE) / 2); ++c) r.q[c] = reinterpret_cast<const u32x4 *>(p)[c];
+}
+__device__ __forceinline__ void raw8_f32(const Raw8<bf16_t> &r, float *v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        v[2 * c] = bf16lo(r.q[0][c]);
+        v[2 * c + 1] = bf16hi(r.q[0][c]);
+    }
+}
+__device__ __forceinline__ void raw8_f32(const Raw8<float> &r, float *v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        v[c] = __uint_as_float(r.q[0][c]);
+        v[4 + c] = __uint_as_float(r.q[1][c]);
+    }
+}
+
 __device__ __forceinline__ void store8_nt(bf16_t *p, const float *v) {
     u32x4 q;
 #pragma unroll
@@ -68,27 +97,38 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
     if (idx >= npieces) return;
     const int nv = h >> 3;
     const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    const int64_t P = npieces / nv * k;   // rows of y
+    const int64_t base = static_cast<int64_t>(t) * k;
+    // indices without branches (slots past k re-read slot k - 1), then every
+    // row piece loaded raw before any is used: one round trip per phase
     int rows[8];
     float w[8];
-    const int64_t P = npieces / nv * k;   // rows of y
+    bool ok[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
-        if (rows[j] >= P) rows[j] = -1;
-        w[j] = j < k ? (topk_w ? topk_w[static_cast<int64_t>(t) * k + j] : 1.0f) : 0.0f;
+        rows[j] = row_of[base + (j < k ? j : k - 1)];
+        w[j] = topk_w ? topk_w[base + (j < k ? j : k - 1)] : 1.0f;
     }
-    float yv[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ok[j] = j < k && rows[j] >= 0 && rows[j] < P;
+        rows[j] = ok[j] ? rows[j] : 0;
+    }
+    Raw8<TE> yr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        if (rows[j] >= 0) load8_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv[j]);
+        if (j < k) raw8_load_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yr[j]);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        if (rows[j] >= 0) {
+        if (j < k) {
+            float yv[8];
+            raw8_f32(yr[j], yv);
+            const float wj = ok[j] ? w[j] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[j][i], acc[i]);
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, yv[i], acc[i]);
         }
     if (y_sh) {
         float sv[8];
@@ -122,18 +162,22 @@ __global__ __launch_bounds__(1024) void unpermute_bwd_kernel(
     }
     const int nv = h / 8;
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        float g[8], yv[8][8];
-        load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+        // every piece loaded raw before any is used (one round trip)
+        Raw8<TE> gr, yr[8];
+        raw8_load_nt(gout + static_cast<int64_t>(t) * h + 8 * v, gr);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (rows[j] >= 0) load8_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yv[j]);
+            if (j < k) raw8_load_nt(y + static_cast<int64_t>(rows[j] >= 0 ? rows[j] : 0) * h + 8 * v, yr[j]);
+        float g[8];
+        raw8_f32(gr, g);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (rows[j] >= 0) {
-                float d[8];
+            if (j < k && rows[j] >= 0) {
+                float yv[8], d[8];
+                raw8_f32(yr[j], yv);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    dot[j] = fmaf(g[i], yv[j][i], dot[j]);
+                    dot[j] = fmaf(g[i], yv[i], dot[j]);
                     d[i] = w[j] * g[i];
                 }
                 store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
@@ -169,41 +213,66 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     const int nv = h >> 3;
     const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
     const int64_t P = npieces / nv * k;   // rows of grad_x_perm
+    const int64_t base = static_cast<int64_t>(t) * k;
+    // every load of a phase is issued before any of its values is used (k is
+    // uniform, so `j < k` is a scalar branch; out-of-range indices are
+    // clamped to a valid address and their terms dropped by a select), so
+    // the phases cost one memory round trip each
+    // index loads without branches: slots past k re-read slot k - 1
     int rows[8], ex[8];
     float dl[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
-        if (rows[j] >= P) rows[j] = -1;
-        ex[j] = -1;
-        dl[j] = 0.0f;
-        if (gl && j < k) {
-            const int e = topk_idx[static_cast<int64_t>(t) * k + j];
-            ex[j] = (e >= 0 && e < E) ? e : -1;
-            dl[j] = gl[static_cast<int64_t>(t) * k + j];
+    for (int j = 0; j < 8; ++j) rows[j] = row_of[base + (j < k ? j : k - 1)];
+    if (gl) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ex[j] = topk_idx[base + (j < k ? j : k - 1)];
+            dl[j] = gl[base + (j < k ? j : k - 1)];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ex[j] = -1;
+            dl[j] = 0.0f;
         }
     }
-    float d[8][8];
+    bool rok[8], eok[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rok[j] = j < k && rows[j] >= 0 && rows[j] < P;
+        eok[j] = j < k && ex[j] >= 0 && ex[j] < E;
+        rows[j] = rok[j] ? rows[j] : 0;
+        ex[j] = eok[j] ? ex[j] : 0;
+    }
+    Raw8<TE> d[8], wr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        if (rows[j] >= 0) load8_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
+        if (j < k) raw8_load_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
+    if (gl) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) raw8_load(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wr[j]);
+    }
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        if (rows[j] >= 0) {
+        if (j < k) {
+            float dv[8];
+            raw8_f32(d[j], dv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += d[j][i];
+            for (int i = 0; i < 8; ++i) acc[i] += rok[j] ? dv[i] : 0.0f;
         }
+    if (gl) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (ex[j] >= 0) {
-            float wv[8];
-            load8(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wv);
+        for (int j = 0; j < 8; ++j)
+            if (j < k) {
+                float wv[8];
+                raw8_f32(wr[j], wv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], wv[i], acc[i]);
-        }
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(eok[j] ? dl[j] : 0.0f, wv[i], acc[i]);
+            }
     }
     store8_nt(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
 }
@@ -219,12 +288,16 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const TE *__restrict_
     const int nv = h >> 3;
     const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
     const int64_t P = npieces / nv * k;
+    // the piece and all k row indices in flight together (slots past k
+    // re-read slot k - 1 and store nothing)
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
     float g[8];
     load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
-    for (int j = 0; j < k; ++j) {
-        const int r = row_of[static_cast<int64_t>(t) * k + j];
-        if (r >= 0 && r < P) store8_nt(gy + static_cast<int64_t>(r) * h + 8 * v, g);
-    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k && rows[j] >= 0 && rows[j] < P) store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, g);
 }
 
 int check_common(const char *fn, int dtype, int64_t T, int64_t h, int k) {

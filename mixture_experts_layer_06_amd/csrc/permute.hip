@@ -120,15 +120,20 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x
     if (idx >= npieces) return;
     const int nv = h / kVec;
     const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
-    const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * h) + v);
+    // the piece and all k row indices in flight together (slots past k
+    // re-read slot k - 1 and store nothing)
+    int rows[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (j < k) {
-            const int r = row_of[static_cast<int64_t>(t) * k + j];
-            if (r >= 0 && static_cast<int64_t>(r) < npieces / nv * k)
-                __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(r) * h) + v);
-        }
-    }
+    for (int j = 0; j < 8; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
+    const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * h) + v);
+    // the piece is waited for here, once: a wait inside the conditional
+    // stores below would, with the in-order memory counter, also wait for
+    // the stores issued before it
+    __asm__ volatile("" ::"v"(d));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k && rows[j] >= 0 && static_cast<int64_t>(rows[j]) < npieces / nv * k)
+            __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(rows[j]) * h) + v);
 }
 
 // Routing weights in permuted-row order and back:

@@ -467,23 +467,34 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     constexpr int M = kMaxE / 64;
     float klo[M], khi[M];
     bool bad = false;
+    // this lane's experts' inputs, all loaded before use (experts past E read
+    // expert E - 1 and are dropped below)
+    float lv[M], bv[M], nv[M], sv[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int ec = min(lane + 64 * m, E - 1);
+        lv[m] = lp[static_cast<int64_t>(t) * E + ec];
+        bv[m] = bg ? bg[ec] : 0.0f;
+        nv[m] = wnorm[ec];
+        sv[m] = (SIGMOID && sel_bias) ? sel_bias[ec] : 0.0f;
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const int e = lane + 64 * m;
         klo[m] = -INFINITY;
         khi[m] = -INFINITY;
         if (e < E) {
-            float l = lp[static_cast<int64_t>(t) * E + e];
-            if (bg) l = l + bg[e];
-            const float d = cb * xn * wnorm[e] + 4.0f * 0x1p-24f * (fabsf(l) + (bg ? fabsf(bg[e]) : 0.0f));
+            float l = lv[m];
+            if (bg) l = l + bv[m];
+            const float d = cb * xn * nv[m] + 4.0f * 0x1p-24f * (fabsf(l) + (bg ? fabsf(bv[m]) : 0.0f));
             float lo = l - d, hi = l + d;
             if (!(lo == lo) || !(hi == hi) || isinf(lo) || isinf(hi)) bad = true;
             if (SIGMOID) {
                 lo = sigmoid_canonical(lo);
                 hi = sigmoid_canonical(hi);
                 if (sel_bias) {
-                    lo = lo + sel_bias[e];
-                    hi = hi + sel_bias[e];
+                    lo = lo + sv[m];
+                    hi = hi + sv[m];
                 }
             }
             klo[m] = lo;
@@ -555,23 +566,38 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     int sel_e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) { sel_l[j] = 0.0f; sel_e[j] = 0; }
+    // the keys of this lane's candidate slots, computed once (their
+    // selection biases loaded together)
+    int ce[M];
+    float cl[M], ck[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int ci = lane + 64 * m;
+        ce[m] = ci < nc ? s_cand[wave][ci] : 0;
+        cl[m] = ci < nc ? s_cl[wave][ci] : 0.0f;
+    }
+    float cb_sel[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) cb_sel[m] = (SIGMOID && sel_bias) ? sel_bias[ce[m]] : 0.0f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float key = cl[m];
+        if (SIGMOID) {
+            key = sigmoid_canonical(cl[m]);
+            if (sel_bias) key = key + cb_sel[m];
+        }
+        if (key != key) key = -INFINITY;
+        ck[m] = key + 0.0f;
+    }
     uint32_t removed = 0;   // bit m: candidate lane + 64 m taken
     for (int j = 0; j < k; ++j) {
         float bk = -INFINITY, bl = 0.0f;
         int bi = 0x7fffffff, bm = -1;
+#pragma unroll
         for (int m = 0; m < M; ++m) {
             const int ci = lane + 64 * m;
             if (ci >= nc || ((removed >> m) & 1u)) continue;
-            const int e = s_cand[wave][ci];
-            const float l = s_cl[wave][ci];
-            float key = l;
-            if (SIGMOID) {
-                key = sigmoid_canonical(l);
-                if (sel_bias) key = key + sel_bias[e];
-            }
-            if (key != key) key = -INFINITY;
-            key = key + 0.0f;
-            if (bm < 0 || precedes(key, e, bk, bi)) { bk = key; bi = e; bl = l; bm = m; }
+            if (bm < 0 || precedes(ck[m], ce[m], bk, bi)) { bk = ck[m]; bi = ce[m]; bl = cl[m]; bm = m; }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {

@@ -34,6 +34,9 @@
  *   break the invariants.
  * - Results are deterministic: identical inputs give bitwise identical
  *   outputs (no floating-point atomics).
+ * - An empty batch (T = 0 tokens, so P = 0 pairs) is valid everywhere:
+ *   pointers to arrays with T or P rows may then be NULL, per-expert outputs
+ *   (counts, offsets, weight and bias gradients) are still written (zeros).
  *
  * Supported sizes (MOE_ERR_UNSUPPORTED otherwise): h % 64 == 0, F % 64 == 0,
  * 1 <= k <= E <= 256, k <= 8, T*k < 2^31.

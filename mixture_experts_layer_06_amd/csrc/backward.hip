@@ -202,8 +202,8 @@ extern "C" int moe_route_bwd(const void *x, int dtype, int64_t T, int64_t h, int
                              float *grad_logits_sel, float *grad_w_gate, float *grad_b_gate,
                              void *workspace, size_t workspace_bytes, void *stream) {
     clear_error();
-    MOE_CHECK_ARG(x && topk_idx && topk_w && grad_topk_w && offsets && sorted_token &&
-                      grad_logits_sel && grad_w_gate,
+    MOE_CHECK_ARG(offsets && grad_w_gate &&
+                      (T == 0 || (x && topk_idx && topk_w && grad_topk_w && sorted_token && grad_logits_sel)),
                   MOE_ERR_INVALID_ARG, "moe_route_bwd: null required pointer");
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
                   "moe_route_bwd: bad dtype %d", dtype);

@@ -319,7 +319,7 @@ extern "C" int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int
                              const int32_t *row_of, const float *topk_w, const void *y_sh,
                              void *out, void *stream) {
     clear_error();
-    MOE_CHECK_ARG(y && row_of && out, MOE_ERR_INVALID_ARG, "moe_unpermute: null required pointer");
+    MOE_CHECK_ARG(T == 0 || (y && row_of && out), MOE_ERR_INVALID_ARG, "moe_unpermute: null required pointer");
     int st = check_common("moe_unpermute", dtype, T, h, k);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(aligned16(y) && aligned16(out) && (!y_sh || aligned16(y_sh)), MOE_ERR_INVALID_ARG,
@@ -343,8 +343,8 @@ extern "C" int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype,
                                  int64_t h, int k, const int32_t *row_of, const float *topk_w,
                                  void *grad_y, float *grad_topk_w, void *stream) {
     clear_error();
-    MOE_CHECK_ARG(grad_out && row_of && grad_y && (topk_w == nullptr || (y && grad_topk_w)), MOE_ERR_INVALID_ARG,
-                  "moe_unpermute_bwd: null required pointer");
+    MOE_CHECK_ARG(T == 0 || (grad_out && row_of && grad_y && (topk_w == nullptr || (y && grad_topk_w))),
+                  MOE_ERR_INVALID_ARG, "moe_unpermute_bwd: null required pointer");
     int st = check_common("moe_unpermute_bwd", dtype, T, h, k);
     if (st != MOE_OK) return st;
     if (topk_w == nullptr) {
@@ -387,7 +387,7 @@ extern "C" int moe_permute_bwd(const void *grad_x_perm, int dtype, int64_t T, in
                                const int32_t *topk_idx, const void *w_gate, int E, void *grad_x,
                                void *stream) {
     clear_error();
-    MOE_CHECK_ARG(grad_x_perm && row_of && grad_x, MOE_ERR_INVALID_ARG,
+    MOE_CHECK_ARG(T == 0 || (grad_x_perm && row_of && grad_x), MOE_ERR_INVALID_ARG,
                   "moe_permute_bwd: null required pointer");
     MOE_CHECK_ARG(grad_logits_sel == nullptr || (topk_idx && w_gate && E > 0), MOE_ERR_INVALID_ARG,
                   "moe_permute_bwd: the router term needs topk_idx, w_gate and E");

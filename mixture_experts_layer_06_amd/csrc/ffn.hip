@@ -762,7 +762,7 @@ int grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, 
                 const void *w2, const void *b2, const void *x_sh, int64_t T_sh, const void *w1_sh,
                 const void *w2_sh, const float *row_w, void *act, void *gu, void *y, void *y_sh, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    MOE_CHECK_ARG(offsets && w1 && w2 && act && y, MOE_ERR_INVALID_ARG,
+    MOE_CHECK_ARG(offsets && w1 && w2 && (P == 0 || (act && y)), MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: null required pointer");
     MOE_CHECK_ARG(P == 0 || x_perm, MOE_ERR_INVALID_ARG, "moe_grouped_ffn: null x_perm");
     MOE_CHECK_ARG(gather_rows == nullptr || (x_rows > 0 && x_rows * h * 4 < (int64_t(1) << 31)),

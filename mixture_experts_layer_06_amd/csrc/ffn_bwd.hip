@@ -533,7 +533,8 @@ int check_bwd_args(const char *what, const void *grad_y, const void *x_perm, con
                    int64_t h, int64_t F, int E, const int32_t *offsets, int act_kind, const void *w1,
                    const void *w2, const void *grad_gu, const void *grad_x_perm, const float *grad_w1,
                    const float *grad_w2) {
-    MOE_CHECK_ARG(grad_y && x_perm && gu && offsets && w1 && w2 && grad_gu && grad_x_perm && grad_w1 && grad_w2,
+    MOE_CHECK_ARG(offsets && w1 && w2 && grad_w1 && grad_w2 &&
+                      (P == 0 || (grad_y && x_perm && gu && grad_gu && grad_x_perm)),
                   MOE_ERR_INVALID_ARG, "%s: null required pointer", what);
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG, "%s: bad dtype %d", what,
                   dtype);
@@ -635,7 +636,7 @@ extern "C" int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const
     int st = check_bwd_args("moe_grouped_ffn_bwd", grad_y, x_perm, gu, dtype, P, h, F, E, offsets, act_kind, w1,
                             w2, grad_gu, grad_x_perm, grad_w1, grad_w2);
     if (st != MOE_OK) return st;
-    MOE_CHECK_ARG(act && aligned16(act), MOE_ERR_INVALID_ARG,
+    MOE_CHECK_ARG(P == 0 || (act && aligned16(act)), MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn_bwd: act must be a 16-byte aligned pointer");
     return ffn_bwd_gemms(static_cast<const bf16_t *>(grad_y), static_cast<const bf16_t *>(x_perm),
                          static_cast<const bf16_t *>(act), gu, P, h, F, E, offsets, w1, w2,

@@ -607,8 +607,8 @@ extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scale
                                   uint8_t *act_scales, void *y, void *workspace, size_t workspace_bytes,
                                   void *stream) {
     clear_error();
-    MOE_CHECK_ARG(x_codes && x_scales && offsets && w1_codes && w1_scales && w2_codes && w2_scales && act &&
-                      act_codes && act_scales && y,
+    MOE_CHECK_ARG(offsets && w1_codes && w1_scales && w2_codes && w2_scales &&
+                      (P == 0 || (x_codes && x_scales && act && act_codes && act_scales && y)),
                   MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: null required pointer");
     MOE_CHECK_ARG(P >= 0 && h > 0 && F > 0 && E > 0, MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: bad sizes");
     MOE_CHECK_ARG(act_kind == MOE_ACT_SWIGLU, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_mx: SwiGLU experts only");

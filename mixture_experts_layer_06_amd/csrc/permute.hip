@@ -174,7 +174,7 @@ extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E
                            int32_t *row_of, void *x_perm, void *workspace, size_t workspace_bytes,
                            void *stream) {
     clear_error();
-    MOE_CHECK_ARG(topk_idx && offsets && sorted_token && row_of, MOE_ERR_INVALID_ARG,
+    MOE_CHECK_ARG(offsets && (T == 0 || (topk_idx && sorted_token && row_of)), MOE_ERR_INVALID_ARG,
                   "moe_permute: null required pointer");
     MOE_CHECK_ARG(x_perm == nullptr || x != nullptr, MOE_ERR_INVALID_ARG,
                   "moe_permute: x_perm requested without x");

@@ -656,7 +656,7 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
                          float *logits, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
                          int32_t *counts, void *workspace, size_t workspace_bytes, void *stream) {
     clear_error();
-    MOE_CHECK_ARG(x && w_gate && topk_idx && topk_w && counts, MOE_ERR_INVALID_ARG,
+    MOE_CHECK_ARG(w_gate && counts && (T == 0 || (x && topk_idx && topk_w)), MOE_ERR_INVALID_ARG,
                   "moe_route: null required pointer");
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
                   "moe_route: bad dtype %d", dtype);

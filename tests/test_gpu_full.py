@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from mixture_experts_layer_06_amd import workloads as wl
-from parity import TOL, rel_err, to_np32
+from parity import TOL, rel_err, to_device, to_np32
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +84,37 @@ def test_imbalanced_load_profile(moe_lib):
     assert c.sum() == cfg.P
     assert (c == 0).sum() >= 4
     assert c.max() > 8 * cfg.P / cfg.E
+
+
+@pytest.mark.parametrize("memory_efficient", [False, True])
+def test_empty_batch_forward_backward(moe_lib, memory_efficient):
+    """T = 0: every stage runs on an empty batch without error, the output
+    and the input gradient are empty, and the weight gradients are exactly
+    zero (no token reaches any expert or the router)."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[5], T=0, h=128, F=64, E=16)
+    print("case empty batch, memory_efficient", memory_efficient, flush=True)
+    dinp = to_device(wl.make_inputs(cfg, device="cpu"))
+    if memory_efficient:
+        dinp.pop("b_gate", None)
+    f = layer.forward(dinp, cfg.k, cfg.score, cfg.act, keep_for_backward=True,
+                      memory_efficient=memory_efficient, recompute=memory_efficient)
+    g = layer.backward(dinp, f, dinp["grad_out"], cfg.k, cfg.score, cfg.act)
+    torch.cuda.synchronize()
+    assert tuple(f["out"].shape) == (0, cfg.h)
+    assert tuple(g["grad_x"].shape) == (0, cfg.h)
+    for key in ("grad_w1", "grad_w2", "grad_w_gate"):
+        assert not g[key].any(), key
+    if g.get("grad_b_gate") is not None:
+        assert not g["grad_b_gate"].any()
+
+
+def test_empty_batch_mxfp8(moe_lib):
+    """T = 0 through the MXFP8 layer: empty output, no error."""
+    from mixture_experts_layer_06_amd import layer
+    cfg = wl.small_variant(wl.CONFIGS[2], T=0, h=256, F=128)
+    dinp = to_device(wl.make_inputs(cfg, device="cpu", with_grad_out=False))
+    wq = layer.quantize_experts_mx(dinp)
+    f = layer.forward_mxfp8(dinp, wq, cfg.k, cfg.score)
+    torch.cuda.synchronize()
+    assert tuple(f["out"].shape) == (0, cfg.h)

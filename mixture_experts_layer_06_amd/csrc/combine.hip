@@ -126,9 +126,13 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
         if (j < k) {
             float yv[8];
             raw8_f32(yr[j], yv);
-            const float wj = ok[j] ? w[j] : 0.0f;
+            // a dropped pair (row -1) loaded row 0 only to keep the loads
+            // uniform: its value is masked, not just its weight, so that a
+            // non-finite row 0 cannot reach this token (0 * inf = NaN)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, yv[i], acc[i]);
+            for (int i = 0; i < 8; ++i) yv[i] = ok[j] ? yv[i] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[i], acc[i]);
         }
     if (y_sh) {
         float sv[8];
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
                 float wv[8];
                 raw8_f32(wr[j], wv);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(eok[j] ? dl[j] : 0.0f, wv[i], acc[i]);
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], eok[j] ? wv[i] : 0.0f, acc[i]);
             }
     }
     store8_nt(gx + static_cast<int64_t>(t) * h + 8 * v, acc);

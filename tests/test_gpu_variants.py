@@ -148,6 +148,44 @@ def test_capacity_full_size_sampled(moe_lib):
     assert err <= TOL[cfg.dtype], err
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_capacity_zero_and_nonfinite_row0(moe_lib, dtype):
+    """Capacity 0 drops every pair: no expert row is written, and the combine
+    must give exactly 0 even when the (unwritten) expert outputs hold Inf and
+    NaN. With capacity 1, a non-finite kept row 0 reaches only the token that
+    owns it; tokens whose pairs were dropped stay exactly 0."""
+    B = moe_lib
+    T, h, E, k = 96, 128, 8, 2
+    gen = torch.Generator().manual_seed(7)
+    x = torch.randn(T, h, generator=gen).to(dtype).cuda()
+    wg = (torch.randn(E, h, generator=gen) / h ** 0.5).to(dtype).cuda()
+    print("case capacity 0 / non-finite row 0", dtype, flush=True)
+    r = B.moe_route(x, wg, k, "softmax")
+    p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=False)
+    d0 = B.moe_capacity_drop(r["topk_idx"], p["offsets"], p["row_of"], 0)
+    assert (d0["row_of"] == -1).all() and (d0["offsets"] == 0).all()
+    y = torch.full((T * k, h), float("nan"), dtype=dtype, device="cuda")
+    y[0].fill_(float("inf"))
+    out = B.moe_unpermute(y, d0["row_of"], r["topk_w"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out))
+    # capacity 1: one kept row per expert; row 0 is expert 0's kept row
+    d1 = B.moe_capacity_drop(r["topk_idx"], p["offsets"], p["row_of"], 1)
+    ro = d1["row_of"].cpu().numpy()
+    nk = int(d1["offsets"][-1].item())
+    y = torch.randn(T * k, h, generator=gen).to(dtype).cuda()
+    y[0].fill_(float("inf"))
+    y[nk:].fill_(float("nan"))       # rows past the kept ones are never read
+    out = B.moe_unpermute(y, d1["row_of"], r["topk_w"]).float().cpu()
+    owner = np.nonzero((ro == 0).any(axis=1))[0]
+    dropped = np.nonzero((ro < 0).all(axis=1))[0]
+    assert len(owner) == 1 and len(dropped) > 0
+    others = np.setdiff1d(np.arange(T), owner)
+    assert torch.isfinite(out[others]).all()
+    assert not torch.isfinite(out[owner]).any()
+    assert not out[dropped].any()
+
+
 # -------------------------------------------------------- expert choice
 
 EC_CASES = {

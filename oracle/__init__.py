@@ -29,7 +29,6 @@ from .moe import (  # noqa: F401
     mx_quantize,
     mx_roundtrip,
     permutation,
-    round_bf16,
     route,
     router_backward_dlogits,
     router_grads,

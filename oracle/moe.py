@@ -450,33 +450,24 @@ def mx_dequantize(codes, scales):
     return val.reshape(c.shape)
 
 
-def round_bf16(v):
-    """float64 values rounded to bfloat16 (8 significant bits, nearest with
-    ties to even, fp32's exponent range; overflow to inf)."""
-    v = np.asarray(v, dtype=np.float64)
-    a = np.abs(v)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(e, -126.0)                 # subnormals share the smallest binade's step
-    step = 2.0 ** (e - 7)
-    out = np.round(a / step) * step
-    out = np.where(out > 3.3895313892515355e38, np.inf, out)
-    return np.copysign(np.where(a > 0, out, 0.0), v)
-
-
 def mx_roundtrip(v):
     """v quantised to MXFP8 and back (float64)."""
     return mx_dequantize(*mx_quantize(v))
 
 
 def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bias=None,
-                  routing=None, tokens=None):
+                  routing=None, tokens=None, with_act: bool = False):
     """The layer with the expert GEMMs in MXFP8: routing as ``forward``; the
     token rows, both weight matrices (along their reduction axes: h for W1,
     F for W2) and the activation (along F) quantised by ``mx_quantize``;
     products and sums in fp64 on the dequantised values. The activation is
-    quantised from its bf16 rounding: the bf16 layer stores it in bf16, and
-    the MXFP8 layer quantises that stored tensor. SwiGLU or GELU without
-    biases, no shared expert."""
+    quantised as computed (fp64 here), with no intermediate rounding: the
+    page's recipe quantises the activations themselves. SwiGLU or GELU
+    without biases, no shared expert.
+
+    With ``with_act``, the result also holds the activation in permuted-row
+    order (expert-major, tokens ascending, as ``permutation``): ``act``
+    [P, F] fp64 and its quantisation ``act_codes``, ``act_scales``."""
     x = np.asarray(x, dtype=np.float32)
     if tokens is not None:
         x = x[np.asarray(tokens, dtype=np.int64)]
@@ -487,10 +478,13 @@ def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, 
     E = w1.shape[0]
     xq = mx_roundtrip(x)
     out = np.zeros((n, h), dtype=np.float64)
+    acts = []
     for e in range(E):
         tok, slot = np.nonzero(topk_idx == e)
         if tok.size == 0:
             continue
+        order = np.argsort(tok, kind="stable")
+        tok, slot = tok[order], slot[order]
         w1q = mx_roundtrip(np.asarray(w1[e], dtype=np.float64))
         w2q = mx_roundtrip(np.asarray(w2[e], dtype=np.float64))
         a = xq[tok] @ w1q.T
@@ -499,10 +493,18 @@ def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, 
             hid = silu(a[:, :F]) * a[:, F:]
         else:
             hid = gelu_erf(a)
-        y = mx_roundtrip(round_bf16(hid)) @ w2q.T
+        codes, scales = mx_quantize(hid)
+        y = mx_dequantize(codes, scales) @ w2q.T
         out[tok] += topk_w[tok, slot][:, None] * y
+        if with_act:
+            acts.append((hid, codes, scales))
     res = dict(routing)
     res.update(out=out)
+    if with_act:
+        F = w2.shape[2]
+        res.update(act=np.concatenate([a_[0] for a_ in acts]) if acts else np.zeros((0, F)),
+                   act_codes=np.concatenate([a_[1] for a_ in acts]) if acts else np.zeros((0, F), np.uint8),
+                   act_scales=np.concatenate([a_[2] for a_ in acts]) if acts else np.zeros((0, F // 32), np.uint8))
     return res
 
 

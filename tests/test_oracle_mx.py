@@ -95,10 +95,58 @@ def test_mx_error_bound_and_scale_invariance():
     assert np.array_equal(oracle.mx_roundtrip(d), d)
 
 
+def _torch_mx_roundtrip(v):
+    """An MXFP8 round trip written independently of the oracle: the block
+    exponent from frexp (largest magnitude m = f 2^e with f in [0.5, 1), so
+    floor(log2 m) = e - 1), the scaled elements clamped to +-448 and rounded by
+    torch's own float8_e4m3fn conversion (nearest-even). torch converts a
+    float64 through float32, which can round twice; the function checks that
+    no element sits where that could matter (a float32 rounding that lands
+    exactly on an E4M3 midpoint while the float64 value does not)."""
+    import torch
+    v = np.asarray(v, dtype=np.float64)
+    blk = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    _, e = np.frexp(amax)
+    exp = np.where(amax > 0, np.clip(e - 1 - 8, -127, 127), -127)
+    scaled = np.clip(np.ldexp(blk, -exp[..., None]), -448.0, 448.0)
+    s32 = scaled.astype(np.float32).astype(np.float64)
+    grid = np.unique(np.abs(oracle.e4m3_decode(np.arange(256, dtype=np.uint8))))
+    grid = grid[np.isfinite(grid)]
+    mids = (grid[1:] + grid[:-1]) / 2
+    risky = (s32 != scaled) & np.isin(np.abs(s32), mids)
+    assert not risky.any(), "double-rounding case in the reference quantiser"
+    q = torch.as_tensor(scaled).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return np.ldexp(q, exp[..., None]).reshape(v.shape)
+
+
+def test_mx_quantize_matches_an_independent_quantiser():
+    """Activation-like rows (SwiGLU values of random projections, several
+    magnitudes, zeros, exact E4M3 midpoints at a fixed scale) quantised by the
+    oracle equal the independent frexp + torch float8 round trip, element by
+    element."""
+    rng = np.random.default_rng(13)
+    g = rng.standard_normal((200, 256)) * 3
+    u = rng.standard_normal((200, 256))
+    act = oracle.silu(g) * u * np.exp(rng.uniform(-20, 20, (200, 1)))
+    act[3] = 0.0
+    act[4, :32] = 0.0
+    grid = np.unique(np.abs(oracle.e4m3_decode(np.arange(256, dtype=np.uint8))))
+    grid = grid[np.isfinite(grid)]
+    mids = (grid[1:] + grid[:-1]) / 2
+    act[5] = rng.choice(mids, 256) * rng.choice([-1.0, 1.0], 256)
+    act[5, ::32] = 448.0                      # block maximum 448: scale 2^0, midpoints stay midpoints
+    assert np.array_equal(oracle.mx_roundtrip(act), _torch_mx_roundtrip(act))
+
+
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 def test_mxfp8_layer_identical_experts_is_the_dense_fp8_ffn(act):
     """Identical experts, renormalised weights: the MXFP8 layer equals one
-    dense FFN on the quantised token rows, weights and activation."""
+    dense FFN on the quantised token rows, weights and (unrounded)
+    activation, evaluated here with torch's float64 SiLU/GELU and the
+    independent quantiser; the activation the oracle reports is that dense
+    activation in permuted-row order, with its codes."""
+    import torch
     rng = np.random.default_rng(9)
     T, h, E, F, k = 24, 64, 4, 64, 2
     n1 = 2 if act == "swiglu" else 1
@@ -106,24 +154,18 @@ def test_mxfp8_layer_identical_experts_is_the_dense_fp8_ffn(act):
     wg = (rng.standard_normal((E, h)) / 8).astype(np.float32)
     w1 = np.repeat((rng.standard_normal((1, n1 * F, h)) / 8), E, axis=0)
     w2 = np.repeat((rng.standard_normal((1, h, F)) / 8), E, axis=0)
-    r = oracle.forward_mxfp8(x, wg, w1, w2, k, "softmax", act)
-    a = oracle.mx_roundtrip(x.astype(np.float64)) @ oracle.mx_roundtrip(w1[0]).T
-    hid = oracle.silu(a[:, :F]) * a[:, F:] if act == "swiglu" else oracle.gelu_erf(a)
-    dense = oracle.mx_roundtrip(oracle.round_bf16(hid)) @ oracle.mx_roundtrip(w2[0]).T
+    r = oracle.forward_mxfp8(x, wg, w1, w2, k, "softmax", act, with_act=True)
+    a = torch.as_tensor(_torch_mx_roundtrip(x.astype(np.float64)) @ _torch_mx_roundtrip(w1[0]).T)
+    if act == "swiglu":
+        hid = (torch.nn.functional.silu(a[:, :F]) * a[:, F:]).numpy()
+    else:
+        hid = torch.nn.functional.gelu(a).numpy()
+    dense = _torch_mx_roundtrip(hid) @ _torch_mx_roundtrip(w2[0]).T
     assert np.allclose(r["out"], dense, rtol=1e-12, atol=1e-12)
+    perm = oracle.permutation(r["topk_idx"], E)
+    rows = perm["sorted_token"]
+    assert np.allclose(r["act"], hid[rows], rtol=1e-13, atol=1e-13)
+    assert np.array_equal(oracle.mx_dequantize(r["act_codes"], r["act_scales"]), _torch_mx_roundtrip(hid[rows]))
     plain = oracle.forward(x, wg, w1, w2, k, "softmax", act)
     rel = np.abs(r["out"] - plain["out"]).max() / np.abs(plain["out"]).max()
     assert 1e-3 < rel < 0.1, rel
-
-
-def test_round_bf16_matches_torch_and_ties():
-    """fp32 inputs rounded by torch's bfloat16 conversion (nearest-even);
-    exact halfway cases go to the even mantissa; huge values overflow."""
-    import torch
-    rng = np.random.default_rng(11)
-    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-60, 60, 20000))).astype(np.float32)
-    ref = torch.as_tensor(v).to(torch.bfloat16).float().numpy().astype(np.float64)
-    assert np.array_equal(oracle.round_bf16(v.astype(np.float64)), ref)
-    assert oracle.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0              # tie -> even
-    assert oracle.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2 ** -6   # tie -> even (up)
-    assert np.isinf(oracle.round_bf16(np.array([3.4e38, -3.4e38]))).all()

@@ -431,8 +431,8 @@ def main():
                "grouped_ffn_bwd": "moe_grouped_ffn_bwd call (SwiGLU backward, data and weight "
                                   "gradient launches)"}
     if args.mxfp8:
-        kernels["grouped_ffn"] = ("grouped_gemm_mx SwiGLU launch + activation quantisation + "
-                                  "grouped_gemm_mx plain launch (one moe_grouped_ffn_mx call)")
+        kernels["grouped_ffn"] = ("grouped_gemm_mx SwiGLU launch with the activation quantised in its "
+                                  "epilogue + grouped_gemm_mx plain launch (one moe_grouped_ffn_mx call)")
     out["roofline"] = {
         "kernel": kernels[dom], "bound": "mfma",
         "achieved": call_flops[dom] / live[dom] / 1e12, "peak": peak, "unit": "TFLOP/s",

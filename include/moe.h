@@ -104,7 +104,10 @@ const char *moe_last_error(void);
  * least 32 experts and no logits output, the route first computes all logits
  * with bf16 MFMA and proven error bounds, then the fixed-order logits only of
  * the experts that can still reach the top k; the outputs are identical, bit
- * for bit, to those of the fixed-order pass over all experts.
+ * for bit, to those of the fixed-order pass over all experts, for all finite
+ * inputs (the bounds hold down to fp32's subnormal range, including matrix
+ * products flushed to zero there; a token with a non-finite bound has all
+ * of its experts recomputed in the fixed order).
  */
 size_t moe_route_workspace_size(int64_t T, int E);
 int moe_route(const void *x, int dtype, int64_t T, int64_t h, const void *w_gate,
@@ -243,9 +246,11 @@ int moe_mx_quantize(const void *src, int dtype, int64_t rows, int64_t K, uint8_t
 /* Grouped SwiGLU FFN in MXFP8 (no bias, no shared expert): tokens x_codes /
  * x_scales (rows quantised along h; permuted rows [P,h], or with gather_rows
  * the unpermuted [x_rows,h] as in moe_grouped_ffn), weights as quantised by
- * moe_mx_quantize. Writes act [P,F] bf16 = silu(g)*u of the first
- * projection, its quantisation act_codes [P,F] / act_scales [P,F/32], and
- * y [P,h] bf16 of the second. fp32 accumulation. Needs h % 128 == 0,
+ * moe_mx_quantize. The first projection's epilogue quantises its fp32
+ * activation silu(g)*u along F by moe_mx_quantize's rule, writing
+ * act_codes [P,F] / act_scales [P,F/32] (and, when act is not NULL, the same
+ * activation rounded to bf16 in act [P,F]); the second projection reads
+ * those codes and writes y [P,h] bf16. fp32 accumulation. Needs h % 128 == 0,
  * F % 128 == 0; code, output and workspace pointers 16-byte aligned, scale
  * pointers 4-byte aligned. Workspace (optional, NULL allowed): device memory
  * of moe_grouped_ffn_mx_workspace_size(P,h,F,E) bytes (less is allowed); with

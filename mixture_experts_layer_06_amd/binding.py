@@ -562,9 +562,11 @@ def moe_mx_quantize(src):
 
 
 def moe_grouped_ffn_mx(x_codes, x_scales, offsets, w1_codes, w1_scales, w2_codes, w2_scales,
-                       gather_rows=None, act: str = "swiglu", split: bool = True):
+                       gather_rows=None, act: str = "swiglu", split: bool = True, want_act: bool = False):
     """The grouped SwiGLU FFN in MXFP8. ``split``: pass a workspace, so that
-    the second projection may split its last round of tiles along F."""
+    the second projection may split its last round of tiles along F.
+    ``want_act``: also return the bf16 activation (the codes and scales of
+    the activation are always returned)."""
     _req(x_codes, "x_codes", dtype=torch.uint8)
     dev = x_codes.device
     x_rows, h = x_codes.shape
@@ -578,7 +580,7 @@ def moe_grouped_ffn_mx(x_codes, x_scales, offsets, w1_codes, w1_scales, w2_codes
     _req(w1_scales, "w1_scales", dtype=torch.uint8, shape=(E, 2 * F, h // 32), device=dev)
     _req(w2_codes, "w2_codes", dtype=torch.uint8, shape=(E, h, F), device=dev)
     _req(w2_scales, "w2_scales", dtype=torch.uint8, shape=(E, h, F // 32), device=dev)
-    out = dict(act=torch.empty((P, F), dtype=torch.bfloat16, device=dev),
+    out = dict(act=torch.empty((P, F), dtype=torch.bfloat16, device=dev) if want_act else None,
                act_codes=torch.empty((P, F), dtype=torch.uint8, device=dev),
                act_scales=torch.empty((P, F // 32), dtype=torch.uint8, device=dev),
                y=torch.empty((P, h), dtype=torch.bfloat16, device=dev))

@@ -25,9 +25,10 @@
 //   one of token rows per thread; a lane reads its row's word, shifted right
 //   by 8 g bits, so that k-sub s takes byte 2s (opsel 2s). Accumulators as
 //   in the bf16 kernel.
-// * moe_grouped_ffn_mx: first projection with SwiGLU (bf16 activation),
-//   quantisation of the activation along F, second projection (bf16 expert
-//   outputs). Tokens enter quantised along h, optionally gathered.
+// * moe_grouped_ffn_mx: first projection with SwiGLU, whose epilogue
+//   quantises the fp32 activation along F (and optionally also stores it in
+//   bf16), then the second projection on those codes (bf16 expert outputs).
+//   Tokens enter quantised along h, optionally gathered.
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -59,6 +60,16 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return s | code;
 }
 
+// Shared exponent of a block whose largest magnitude is amax (>= 0):
+// floor(log2 amax) - 8 clamped to [-127, 127]; -127 for a zero block (fp32
+// subnormal maxima also land on -127, as floor(log2) - 8 < -127 for them).
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    const int eb = static_cast<int>(__float_as_uint(amax) >> 23);
+    const int ex = eb == 0 ? -127 : eb - 127 - 8;
+    return ex < -127 ? -127 : ex;
+}
+
 // One thread per block of 32 values of a row.
 template <typename TE>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const TE *__restrict__ src, int64_t nblocks,
@@ -71,12 +82,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const TE *__restrict__
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    int ex = -127;
-    if (amax > 0.0f) {
-        const int eb = static_cast<int>(__float_as_uint(amax) >> 23);   // 0 for fp32 subnormals
-        ex = eb == 0 ? -127 : eb - 127 - 8;
-        if (ex < -127) ex = -127;
-    }
+    const int ex = mx_block_exponent(amax);
     u32x4 out[2];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -145,8 +151,83 @@ __device__ __forceinline__ void mx_sched() {
     }
 }
 
+// Epilogue of a SwiGLU tile (the first projection): the activation
+// silu(g) * u of every output element in fp32, quantised at once, a
+// 32-column block at a time, into the codes a.GU [rows][N_out] and the
+// scales a.GU_sh [rows][N_out / 32] (GGArgs fields the fp8 kernels do not
+// otherwise use; the argument block of the second projection's launch is
+// then the same as without this epilogue). A lane
+// holds 16 of a block's values for one token row (columns 8 gq + 4 lhi + q)
+// and lane l ^ 32 the other 16, so the block maximum takes one exchange;
+// each lane then stores 16 bytes of codes (after one more exchange, so that
+// lane half 0 holds columns 0..15 and half 1 columns 16..31) and half 0 the
+// scale byte. The bf16 activation is stored too when a.C is set.
+template <bool HALF>
+__device__ __forceinline__ void store_tile_mx_swiglu(const GGArgs &a, const TileInfo &ti,
+                                                     floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane) {
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int tok0 = HALF ? 0 : (wave >> 1) * 128;
+    const int rows = min(kMxTile, ti.M - ti.m0);
+    const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
+    bf16_t *Cseg = a.C ? static_cast<bf16_t *>(a.C) + crow0 * a.N_out : nullptr;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int m = tok0 + j * 32 + l32;
+        if (m >= rows) continue;   // lanes l and l ^ 32 share m: both skip or neither
+#pragma unroll
+        for (int p = 0; p < NI / 2; ++p) {
+            // first column of the 32-column block (N_out % 128 == 0: whole blocks)
+            const int fb = ti.n_tile * (kMxTile / 2) + wrow0 / 2 + p * 32;
+            float hv[16];
+            float amax = 0.0f;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float v = silu_fast(acc[2 * p][j][4 * gq + q]) * acc[2 * p + 1][j][4 * gq + q];
+                    hv[4 * gq + q] = v;
+                    amax = fmaxf(amax, fabsf(v));
+                }
+            if (Cseg) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    uint2 o;
+                    o.x = pack_bf16x2(hv[4 * gq], hv[4 * gq + 1]);
+                    o.y = pack_bf16x2(hv[4 * gq + 2], hv[4 * gq + 3]);
+                    *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + fb + 8 * gq + 4 * lhi) = o;
+                }
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int ex = mx_block_exponent(amax);
+            uint32_t c[4];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                c[gq] = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c[gq] |= e4m3_code(ldexpf(hv[4 * gq + q], -ex)) << (8 * q);
+            }
+            // half 0 keeps columns 0..15 (its gq 0, 1 and the partner's), half 1
+            // columns 16..31 (gq 2, 3)
+            const uint32_t r0 = __shfl_xor(lhi ? c[0] : c[2], 32);
+            const uint32_t r1 = __shfl_xor(lhi ? c[1] : c[3], 32);
+            u32x4 w;
+            if (lhi) {
+                w[0] = r0; w[1] = c[2]; w[2] = r1; w[3] = c[3];
+            } else {
+                w[0] = c[0]; w[1] = r0; w[2] = c[1]; w[3] = r1;
+            }
+            const int64_t row = crow0 + m;
+            *reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(a.GU) + row * a.N_out + fb + 16 * lhi) = w;
+            if (!lhi) static_cast<uint8_t *>(a.GU_sh)[row * (a.N_out / 32) + fb / 32] = static_cast<uint8_t>(ex + 127);
+        }
+    }
+}
+
+// Epilogue of a plain tile (the second projection): the bf16 outputs.
 template <int MODE, bool HALF>
-__device__ __forceinline__ void store_tile_mx(const GGArgs &a, const TileInfo &ti,
+__device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileInfo &ti,
                                               floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane) {
     constexpr int NI = HALF ? 2 : 4, NJ = 4;
     const int l32 = lane & 31, lhi = lane >> 5;
@@ -161,20 +242,7 @@ __device__ __forceinline__ void store_tile_mx(const GGArgs &a, const TileInfo &t
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int nl = 8 * gq + 4 * lhi;
-            if (MODE == kModeSwiGLU) {
-#pragma unroll
-                for (int p = 0; p < NI / 2; ++p) {
-                    const int f = ti.n_tile * (kMxTile / 2) + wrow0 / 2 + p * 32 + nl;
-                    if (f >= a.N_out) continue;
-                    float hv[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[2 * p][j][4 * gq + q]) * acc[2 * p + 1][j][4 * gq + q];
-                    uint2 o;
-                    o.x = pack_bf16x2(hv[0], hv[1]);
-                    o.y = pack_bf16x2(hv[2], hv[3]);
-                    *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + f) = o;
-                }
-            } else {
+            {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int n = ti.n_tile * kMxTile + wrow0 + i * 32 + nl;
@@ -393,7 +461,8 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
                         make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         return;
     }
-    store_tile_mx<MODE, HALF>(a, ti, acc, wave, lane);
+    if constexpr (MODE == kModePlain) store_tile_mx_plain<MODE, HALF>(a, ti, acc, wave, lane);
+    else store_tile_mx_swiglu<HALF>(a, ti, acc, wave, lane);
 }
 
 // Split workspace (second projection only): an int header of 64 KB ([0..2]:
@@ -495,7 +564,7 @@ __device__ __forceinline__ void mx_reduce_tile(const GGArgs &a, const TileInfo &
                     acc[i][j][4 * q + 3] += v.w;
                 }
     }
-    store_tile_mx<kModePlain, HALF>(a, ti, acc, tid >> 6, tid & 63);
+    store_tile_mx_plain<kModePlain, HALF>(a, ti, acc, tid >> 6, tid & 63);
 }
 
 // Sum of every split tile's pieces, in piece order, into piece 0 (one
@@ -608,7 +677,7 @@ extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scale
                                   void *stream) {
     clear_error();
     MOE_CHECK_ARG(offsets && w1_codes && w1_scales && w2_codes && w2_scales &&
-                      (P == 0 || (x_codes && x_scales && act && act_codes && act_scales && y)),
+                      (P == 0 || (x_codes && x_scales && act_codes && act_scales && y)),
                   MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: null required pointer");
     MOE_CHECK_ARG(P >= 0 && h > 0 && F > 0 && E > 0, MOE_ERR_INVALID_ARG, "moe_grouped_ffn_mx: bad sizes");
     MOE_CHECK_ARG(act_kind == MOE_ACT_SWIGLU, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_mx: SwiGLU experts only");
@@ -622,7 +691,7 @@ extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scale
                   MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_mx: sizes too large");
     const void *ptrs[] = {x_codes, w1_codes, w2_codes, act, act_codes, y, workspace};
     for (const void *p : ptrs)
-        MOE_CHECK_ARG(p == workspace && p == nullptr ? true : aligned16(p), MOE_ERR_INVALID_ARG,
+        MOE_CHECK_ARG(p == nullptr || aligned16(p), MOE_ERR_INVALID_ARG,
                       "moe_grouped_ffn_mx: code, output and workspace pointers must be 16-byte aligned");
     const void *sp[] = {x_scales, w1_scales, w2_scales, act_scales};
     for (const void *p : sp)
@@ -642,11 +711,9 @@ extern "C" int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scale
     g1.g.K = static_cast<int>(h);
     g1.ws = w1_scales;
     g1.xs = x_scales;
-    int st = launch_mx<kModeSwiGLU>(g1, P, s, "moe_grouped_ffn_mx gemm1");
-    if (st != MOE_OK) return st;
-
-    launch_quantize(static_cast<const bf16_t *>(act), P, F, act_codes, act_scales, s);
-    st = check_launch("moe_grouped_ffn_mx quantize");
+    g1.g.GU = act_codes;
+    g1.g.GU_sh = act_scales;
+    const int st = launch_mx<kModeSwiGLU>(g1, P, s, "moe_grouped_ffn_mx gemm1");
     if (st != MOE_OK) return st;
 
     MXArgs g2{};

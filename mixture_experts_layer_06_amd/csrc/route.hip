@@ -401,13 +401,21 @@ __global__ __launch_bounds__(1024) void count_kernel(const int32_t *__restrict__
 //    most 8 pieces summed in fp32 when the few tiles are split along h),
 //    and |x_t|_2, |w_e|_2.
 // 2. Both l' and the fixed-order logit l differ from the exact dot product
-//    by at most a multiple of u * S, S = sum_i |x_i w_i| <= |x_t| |w_e|
-//    (products of bf16 values are exact in fp32; every fp32 addition or fma
-//    rounds once): the MFMA chain by (h/16 + 16) u S (h/16 accumulations
-//    into C, up to 16 roundings inside one instruction, the final sum of
-//    pieces included), the fixed order by
-//    (h/64 + 6) u S (chains of h/64 fmas, a 6-level tree). Both terms are
-//    doubled, and the sum doubled again, for the interval half-width.
+//    by at most a multiple of u * S, S = sum_i |x_i w_i| <= |x_t| |w_e|,
+//    plus an absolute term for results below fp32's normal range: every
+//    fp32 addition or fma rounds once, with an error of at most u times its
+//    result or, for a subnormal result, half the subnormal spacing (2^-150);
+//    the matrix instruction may also flush to zero a product of bf16 values
+//    below 2^-126 (each losing less than 2^-126) or a subnormal partial sum.
+//    Relative terms: the MFMA chain (h/16 + 16) u S (h/16 accumulations into
+//    C, up to 16 roundings inside one instruction, the final sum of pieces
+//    included), the fixed order (h/64 + 6) u S (chains of h/64 fmas, a
+//    6-level tree); both doubled, the sum doubled again. Absolute term:
+//    2 (h + h/16 + 70) 2^-126 (every product and every accumulation of the
+//    MFMA flushed, which also covers the fixed order's h + 64 roundings of at
+//    most 2^-150 each). The norms are computed in fp32, where the squares of
+//    elements below 2^-63 underflow: each norm is raised by sqrt(h) 2^-63,
+//    more than that loss can take away.
 // 3. Keys of the interval ends (the sigmoid key is monotone in l, and so is
 //    adding the selection bias), L_k = the k-th largest lower end; the
 //    experts whose upper end reaches L_k contain the top-k (every other
@@ -430,7 +438,8 @@ __global__ __launch_bounds__(64) void row_norm_kernel(const bf16_t *__restrict__
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(s);
+    // squares below 2^-126 are lost: sqrt(h) 2^-63 bounds what they add
+    if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(s) + sqrtf(static_cast<float>(h)) * 0x1p-63f;
 }
 
 // One wave per token (4 per block). Lane l holds experts l + 64 m.
@@ -447,7 +456,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     if (t >= T) return;   // no block-wide barrier below
     const bf16_t *xrow = x + static_cast<int64_t>(t) * h;
 
-    // |x_t|_2 (fp32; its rounding is far inside the factor-2 margins)
+    // |x_t|_2 (fp32; its rounding is far inside the factor-2 margins, its
+    // underflow is covered by the added term)
     float xs = 0.0f;
 #pragma unroll 4
     for (int i = 8 * lane; i < h; i += 8 * 64) {
@@ -461,7 +471,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) xs += __shfl_xor(xs, off);
-    const float xn = sqrtf(xs);
+    const float xn = sqrtf(xs) + sqrtf(static_cast<float>(h)) * 0x1p-63f;   // see row_norm_kernel
+    // absolute part of the half-width (results below the normal range)
+    const float dabs = 2.0f * static_cast<float>(h + h / 16 + 70) * 0x1p-126f;
 
     // key intervals
     constexpr int M = kMaxE / 64;
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
         if (e < E) {
             float l = lv[m];
             if (bg) l = l + bv[m];
-            const float d = cb * xn * nv[m] + 4.0f * 0x1p-24f * (fabsf(l) + (bg ? fabsf(bv[m]) : 0.0f));
+            const float d = cb * xn * nv[m] + 4.0f * 0x1p-24f * (fabsf(l) + (bg ? fabsf(bv[m]) : 0.0f)) + dabs;
             float lo = l - d, hi = l + d;
             if (!(lo == lo) || !(hi == hi) || isinf(lo) || isinf(hi)) bad = true;
             if (SIGMOID) {

@@ -175,8 +175,9 @@ def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None =
     """Inference forward with the expert GEMMs in MXFP8 ("Scalable Training of
     Mixture-of-Experts Models with Megatron Core", section 5.3.3): the router
     as in ``forward`` (fp32 logits), the token rows quantised along h and
-    gathered by the first GEMM, the activation quantised along F between the
-    two GEMMs, the weighted combine in fp32. SwiGLU experts without bias."""
+    gathered by the first GEMM, the activation quantised along F in the first
+    GEMM's epilogue (from fp32), the weighted combine in fp32. SwiGLU experts
+    without bias."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias"))

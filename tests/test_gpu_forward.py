@@ -231,6 +231,33 @@ def test_route_mfma_filter_adversarial(moe_lib, score):
     assert np.array_equal(fast["topk_idx"].cpu().numpy(), ref["topk_idx"])
 
 
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_route_mfma_filter_tiny_tokens(moe_lib, score):
+    """Tokens scaled down as far as 2^-124 against gate weights of about
+    2^-6: their products with the gate rows lie below fp32's normal range,
+    where the matrix instruction may flush them, and their squares underflow
+    in the norm. The filtered route must still equal the fixed-order pass and
+    the oracle bit for bit (its bounds carry an absolute term for this)."""
+    g = torch.Generator().manual_seed(23)
+    E, h, k = 64, 512, 8
+    exps = torch.tensor([0, 40, 60, 70, 100, 110, 115, 120, 122, 124], dtype=torch.float64)
+    x = torch.randn(10 * 30, h, generator=g, dtype=torch.float64)
+    x = (x * (2.0 ** -exps).repeat(30)[:, None]).float().to(torch.bfloat16)
+    wg = (torch.randn(E, h, generator=g) * 2.0 ** -6).to(torch.bfloat16)
+    wg[33] = wg[2]                           # exact ties survive the scaling
+    sel = None
+    if score == "sigmoid":
+        sel = (torch.rand(E, generator=g) * 0.2 - 0.1).float()
+    print("case filtered route, tiny tokens,", score, flush=True)
+    fast, slow = _route_both(x, wg, k, score, sel_bias=sel)
+    _assert_same_routing(fast, slow)
+    ref = oracle.route(to_np32(x), to_np32(wg), k, score, None, None if sel is None else sel.numpy())
+    assert np.array_equal(fast["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert np.array_equal(slow["logits"].cpu().numpy().view(np.uint32), ref["logits"].view(np.uint32))
+    tiny = np.abs(ref["logits"][7::10]).max()
+    assert 0 < tiny < 2.0 ** -100, tiny       # the smallest tokens' logits are tiny and non-zero
+
+
 @pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (256, 8), (64, 1)])
 def test_layer_edge_shapes(moe_lib, E, k):
     from mixture_experts_layer_06_amd import layer

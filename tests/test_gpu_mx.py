@@ -1,16 +1,19 @@
 """GPU parity of the MXFP8 path ("Scalable Training of Mixture-of-Experts
 Models with Megatron Core", section 5.3.3), through the C ABI, against the
 oracle: the quantisation bit for bit (codes and scales are integers), the
-MXFP8 layer within 2e-2 of the oracle's MXFP8 layer (products and sums in
-fp64 on the dequantised values) per tensor.
+activation's codes and scales (quantised from fp32 in the first projection's
+epilogue) equal to the oracle's wherever the GPU's fp32 activation is too
+close to a rounding boundary to decide it, and the MXFP8 layer within 2e-2
+of the oracle's MXFP8 layer (products and sums in fp64 on the dequantised
+values), per tensor and per token row.
 
-The activation's quantisation is discontinuous: where the GPU's bf16
-activation (fp32 accumulation) and the oracle's (fp64) differ by one bf16
-unit across an E4M3 rounding midpoint, the two codes differ by an eighth
-of the element. That noise is spread over the output rows, so a single
-token's row-wise error can approach 2 % while the tensor error stays a few
-tenths of a percent; the row-wise figure is reported, the per-tensor one
-is held to the bound."""
+Deciding a code is integer work done on a floating-point value, and the two
+sides compute that value differently (fp32 MFMA accumulation against fp64):
+a code may differ only where the interval [v - b, v + b] around the fp64
+activation v, b the fp32 computation's error bound, holds an E4M3 rounding
+boundary (or, for a block scale, a power of two of the block maximum). The
+test checks that every difference is of that kind and reports how many
+there are."""
 import numpy as np
 import pytest
 import torch
@@ -70,6 +73,90 @@ def test_quantize_weights_bit_exact(moe_lib):
     assert np.array_equal(scales[rows].cpu().numpy(), rs)
 
 
+def _mfma_gamma(K):
+    """Relative error bound (times sum |products|) of an fp32 dot product of
+    K exact products summed by the scaled fp8 MFMA. How one instruction adds
+    its 64 products is not specified (order, internal width, rounding or
+    truncation), so the bound is the classical one for any order: every
+    product added with its own error of at most 2u (u = 2^-24; truncation as
+    well as rounding), plus the K/64 accumulations into C and a margin of 8.
+    A tighter model, (K/64 + 8) roundings per element, was measured to be
+    exceeded by up to 3.75 times on the device."""
+    return (K + K / 64 + 8) * 2.0 ** -23
+
+
+def _check_act_codes(got_codes, got_scales, ref, o, perm, E, F):
+    """Codes and scales of the activation against the oracle's, with every
+    difference explained by the fp32 error bound (see the module docstring).
+    The bound on the GPU's silu(g) * u: the dot products' error (gamma times
+    the sums of absolute products) carried through the derivatives, plus the
+    epilogue's own roundings: hardware exp2 and reciprocal (about 1 ulp each,
+    the exp2 argument's rounding magnified by |g log2 e|), the add and the two
+    multiplies. Returns (differing blocks, differing codes, blocks, codes)."""
+    h = o["x"].shape[1]
+    xq = oracle.mx_roundtrip(o["x"].astype(np.float64))
+    gam = _mfma_gamma(h)
+    bound = np.zeros_like(ref["act"])
+    for e in range(E):
+        r0, r1 = int(perm["offsets"][e]), int(perm["offsets"][e + 1])
+        if r1 == r0:
+            continue
+        w1q = oracle.mx_roundtrip(np.asarray(o["w1"][e], dtype=np.float64))
+        xs = xq[perm["sorted_token"][r0:r1]]
+        a = xs @ w1q.T
+        S = np.abs(xs) @ np.abs(w1q).T
+        g, u = a[:, :F], a[:, F:]
+        sg = 1.0 / (1.0 + np.exp(-g))
+        dsilu = np.abs(sg * (1 + g * (1 - sg)))
+        bound[r0:r1] = (dsilu * gam * S[:, :F] * np.abs(u) + np.abs(g * sg) * gam * S[:, F:]
+                        + (4 + 2 * np.abs(g) + 8) * 2.0 ** -24 * np.abs(ref["act"][r0:r1]))
+    P = ref["act"].shape[0]
+    blk = ref["act"].reshape(P, F // 32, 32)
+    bb = bound.reshape(P, F // 32, 32)
+    amax = np.abs(blk).max(axis=-1)
+    bmax = bb.max(axis=-1)
+
+    def expo(m):
+        return np.where(m > 0, np.clip(np.floor(np.log2(np.where(m > 0, m, 1.0))) - 8, -127, 127), -127)
+
+    ex_ref = ref["act_scales"].astype(np.int64) - 127
+    ex_got = got_scales.astype(np.int64) - 127
+    lo, hi = expo(np.maximum(amax - bmax, 0.0)), expo(amax + bmax)
+    assert np.array_equal(expo(amax), ex_ref)
+    sdiff = ex_got != ex_ref
+    assert np.all((ex_got >= lo) & (ex_got <= hi)), "a block scale differs beyond the fp32 error bound"
+    # codes of the blocks whose scales agree, in scaled units
+    same = ~sdiff
+    v = blk / 2.0 ** ex_ref[..., None]
+    b = bb / 2.0 ** ex_ref[..., None]
+    gv = oracle.e4m3_decode(got_codes.reshape(P, F // 32, 32))
+    rv = oracle.e4m3_decode(ref["act_codes"].reshape(P, F // 32, 32))
+    rlo, rhi = oracle.e4m3_round(v - b), oracle.e4m3_round(v + b)
+    cdiff = (gv != rv) & same[..., None]
+    ok = (gv >= np.minimum(rlo, rhi)) & (gv <= np.maximum(rlo, rhi))
+    bad = ~ok & same[..., None]
+    if bad.any():
+        # how far the GPU value must have been from the fp64 one: the distance
+        # from v to the nearest value that rounds to the GPU's code, in units
+        # of the bound b
+        vb, gb, bbad = v[bad], gv[bad], b[bad]
+        grid = np.unique(oracle.e4m3_decode(np.arange(256, dtype=np.uint8)))
+        grid = grid[np.isfinite(grid)]
+        idx = np.searchsorted(grid, gb)
+        lo_edge = np.where(idx > 0, (grid[np.maximum(idx - 1, 0)] + gb) / 2, gb)
+        hi_edge = np.where(idx < grid.size - 1, (grid[np.minimum(idx + 1, grid.size - 1)] + gb) / 2, gb)
+        dist = np.where(vb < lo_edge, lo_edge - vb, np.where(vb > hi_edge, vb - hi_edge, 0.0))
+        steps = np.abs(np.searchsorted(grid, gb) - np.searchsorted(grid, rv[bad]))
+        raise AssertionError("%d codes differ beyond the fp32 error bound; needed / bound: max %.3g, median "
+                             "%.3g; grid steps apart: max %d; examples v=%s got=%s ref=%s b=%s"
+                             % (bad.sum(), (dist / bbad).max(), np.median(dist / bbad), steps.max(),
+                                vb[:4], gb[:4], rv[bad][:4], bbad[:4]))
+    nb, nc = int(sdiff.size), int(same.sum() * 32)
+    # a bug (a misplaced column, a wrong scale) would move far more codes
+    assert sdiff.sum() <= 0.01 * nb and cdiff.sum() <= 0.01 * nc, (int(sdiff.sum()), nb, int(cdiff.sum()), nc)
+    return int(sdiff.sum()), int(cdiff.sum()), nb, nc
+
+
 MX_CASES = {
     "mixtral_small": wl.small_variant(wl.CONFIGS[2], T=600, h=256, F=384),
     "qwen3_small": wl.small_variant(wl.CONFIGS[3], T=1000, h=512, F=256),
@@ -92,20 +179,25 @@ def test_mxfp8_layer_parity(moe_lib, name):
     torch.cuda.synchronize()
     o = oracle_inputs(inp)
     ref = oracle.forward_mxfp8(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
-                               b_gate=o["b_gate"], sel_bias=o["sel_bias"])
+                               b_gate=o["b_gate"], sel_bias=o["sel_bias"], with_act=True)
     assert np.array_equal(g["topk_idx"].cpu().numpy(), ref["topk_idx"])
     # the quantised tokens the first GEMM reads are the oracle's
     xq, xs = oracle.mx_quantize(o["x"].astype(np.float64))
     gxq, gxs = moe_lib.moe_mx_quantize(dinp["x"])
     assert np.array_equal(gxq.cpu().numpy(), xq) and np.array_equal(gxs.cpu().numpy(), xs)
+    perm = oracle.permutation(ref["topk_idx"], cfg.E)
+    assert np.array_equal(g["offsets"].cpu().numpy(), perm["offsets"])
+    nsb, ncd, nb, nc = _check_act_codes(g["act_codes"].cpu().numpy(), g["act_scales"].cpu().numpy(), ref, o,
+                                        perm, cfg.E, cfg.F)
     err = rel_err_tensor(to_np32(g["out"]), ref["out"])
     rows = rel_err(to_np32(g["out"]), ref["out"])
     plain = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
                            b_gate=o["b_gate"], sel_bias=o["sel_bias"])
-    print("vs oracle MXFP8 layer: tensor %.3g, row-wise %.3g (reported); MXFP8 vs unquantised: gpu %.3g, "
-          "oracle %.3g" % (err, rows, rel_err_tensor(to_np32(g["out"]), plain["out"]),
-                           rel_err_tensor(ref["out"], plain["out"])), flush=True)
-    assert err <= TOL["bf16"], err
+    print("activation: %d of %d block scales and %d of %d codes differ, each within the fp32 error bound; "
+          "out vs oracle MXFP8 layer: tensor %.3g, row-wise %.3g; MXFP8 vs unquantised: gpu %.3g, oracle %.3g"
+          % (nsb, nb, ncd, nc, err, rows, rel_err_tensor(to_np32(g["out"]), plain["out"]),
+             rel_err_tensor(ref["out"], plain["out"])), flush=True)
+    assert err <= TOL["bf16"] and rows <= TOL["bf16"], (err, rows)
 
 
 def test_mxfp8_grouped_ffn_dispatch_copy_equals_gather(moe_lib):
@@ -119,9 +211,10 @@ def test_mxfp8_grouped_ffn_dispatch_copy_equals_gather(moe_lib):
     w1q, w1s = B.moe_mx_quantize(inp["w1"])
     w2q, w2s = B.moe_mx_quantize(inp["w2"])
     xq, xs = B.moe_mx_quantize(inp["x"])
-    a = B.moe_grouped_ffn_mx(xq, xs, p["offsets"], w1q, w1s, w2q, w2s, gather_rows=p["sorted_token"])
+    a = B.moe_grouped_ffn_mx(xq, xs, p["offsets"], w1q, w1s, w2q, w2s, gather_rows=p["sorted_token"],
+                             want_act=True)
     pq, ps = B.moe_mx_quantize(p["x_perm"])
-    b = B.moe_grouped_ffn_mx(pq, ps, p["offsets"], w1q, w1s, w2q, w2s)
+    b = B.moe_grouped_ffn_mx(pq, ps, p["offsets"], w1q, w1s, w2q, w2s, want_act=True)
     torch.cuda.synchronize()
     for key in ("act", "act_codes", "act_scales", "y"):
         assert torch.equal(a[key], b[key]), key
@@ -151,9 +244,9 @@ def test_mxfp8_handbook_layer_full_size_sampled(moe_lib):
                                cfg.k, cfg.score, cfg.act, tokens=tokens)
     assert np.array_equal(g["topk_idx"][torch.as_tensor(tokens, device="cuda")].cpu().numpy(), ref["topk_idx"])
     got = to_np32(g["out"][torch.as_tensor(tokens, device="cuda")])
-    err = rel_err_tensor(got, ref["out"])
-    print("sampled out rel err: tensor %.3g, row-wise %.3g" % (err, rel_err(got, ref["out"])), flush=True)
-    assert err <= TOL["bf16"], err
+    err, rows = rel_err_tensor(got, ref["out"]), rel_err(got, ref["out"])
+    print("sampled out rel err: tensor %.3g, row-wise %.3g" % (err, rows), flush=True)
+    assert err <= TOL["bf16"] and rows <= TOL["bf16"], (err, rows)
 
 
 def test_mxfp8_split_second_projection(moe_lib):
@@ -182,9 +275,9 @@ def test_mxfp8_split_second_projection(moe_lib):
     torch.cuda.synchronize()
     ref = oracle.forward_mxfp8(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act, tokens=tokens)
     got = to_np32(g["out"][torch.as_tensor(tokens, device="cuda")])
-    err = rel_err_tensor(got, ref["out"])
-    print("sampled out rel err: tensor %.3g, row-wise %.3g" % (err, rel_err(got, ref["out"])), flush=True)
-    assert err <= TOL["bf16"], err
+    err, rows = rel_err_tensor(got, ref["out"]), rel_err(got, ref["out"])
+    print("sampled out rel err: tensor %.3g, row-wise %.3g" % (err, rows), flush=True)
+    assert err <= TOL["bf16"] and rows <= TOL["bf16"], (err, rows)
     xq, xs = B.moe_mx_quantize(dinp["x"])
     args = (xq, xs, g["offsets"], wq["w1_codes"], wq["w1_scales"], wq["w2_codes"], wq["w2_scales"])
     a = B.moe_grouped_ffn_mx(*args, gather_rows=g["sorted_token"], split=True)

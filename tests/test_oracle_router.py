@@ -64,6 +64,36 @@ def test_gate_within_fp32_error_bound(h):
             assert float(err) <= 1.01 * n * u * s, (t, e)
 
 
+@pytest.mark.parametrize("h", [128, 640])
+def test_gate_within_error_bound_with_subnormal_products(h):
+    """Tokens near fp32's smallest normal against small gate weights, so the
+    products and most partial sums are subnormal: there the error of a
+    rounding is absolute (at most half the subnormal spacing, 2^-150), so
+    |l - exact| <= (ceil(h/64) + 6) u sum|x_i w_i| + (h + 63) 2^-150 (one
+    rounding per fma and per tree addition), checked with exact rational
+    arithmetic; subnormal results are kept, not flushed."""
+    rng = np.random.default_rng(h + 1)
+    T, E = 4, 5
+    x = (rng.standard_normal((T, h)) * 2.0 ** -118).astype(np.float32)
+    x[1] *= 2.0 ** 40                      # a token of ordinary magnitude among them
+    x[2] *= 2.0 ** -8                      # logits themselves subnormal
+    w = (rng.standard_normal((E, h)) * 2.0 ** -9).astype(np.float32)
+    l = oracle.gate_logits(x, w)
+    u = 2.0 ** -24
+    n = -(-h // 64) + 6
+    tiny = 0
+    for t in range(T):
+        for e in range(E):
+            ex = _exact_dot(x[t], w[e])
+            prods = [abs(Fraction(float(a)) * Fraction(float(b))) for a, b in zip(x[t], w[e])]
+            tiny += sum(p < Fraction(2) ** -126 for p in prods)
+            s = float(sum(prods))
+            err = abs(Fraction(float(l[t, e])) - ex)
+            assert err <= Fraction(1.01 * n * u * s) + (h + 63) * Fraction(2) ** -150, (t, e)
+    assert tiny > (T - 1) * E * h // 2, "most products of the small tokens lie below the normal range"
+    assert np.all(l[2] != 0) and np.all(np.abs(l[2]) < 2.0 ** -126), "subnormal logits are kept"
+
+
 def test_gate_small_integers_exact_and_indexing():
     """Small integer inputs make every step exact: l = x @ w^T exactly."""
     rng = np.random.default_rng(7)

@@ -139,6 +139,21 @@ int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
                 int32_t *row_of, void *x_perm, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/* moe_permute without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops with a
+ * fixed memory plan, harnesses that forbid hipMalloc): the same launches and
+ * results, with the scratch in a static 1 MiB device array of the library
+ * (one copy per GPU, held until the process ends; its address is looked up
+ * once per device). Limit: ceil(T/256) * E <= 131072 (e.g. T = 131072 with
+ * E = 256), otherwise MOE_ERR_UNSUPPORTED and nothing runs. Every scratch
+ * entry a call reads it has first written in that call, so nothing needs
+ * clearing between calls; calls that overlap on one GPU (other streams,
+ * other threads) share the scratch and race, so the caller must order them.
+ * Allocates nothing. */
+int moe_permute_noalloc(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
+                        const int32_t *topk_idx, int32_t *offsets, int32_t *sorted_token,
+                        int32_t *row_of, void *x_perm, void *stream);
+
 /* ------------------------------------------------------------ Grouped FFN
  * Expert computation as one grouped GEMM over all experts ("Scalable
  * Training ... with Megatron Core", section 2.1 stage 3, TEGroupedMLP), each

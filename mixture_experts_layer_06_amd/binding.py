@@ -39,6 +39,7 @@ _SIGS = {
                    _vp, _sz, _vp], _int),
     "moe_permute_workspace_size": ([_i64, _int, _int], _sz),
     "moe_permute": ([_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_permute_noalloc": ([_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_workspace_size": ([_int], _sz),
     "moe_grouped_ffn": ([_vp, _vp, _i64, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp,
                          _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
@@ -192,6 +193,34 @@ def moe_permute(x, topk_idx, E: int, with_x_perm: bool = True):
                            _ptr(out["sorted_token"]), _ptr(out["row_of"]), _ptr(out["x_perm"]),
                            _ptr(ws), ws.numel(), _stream(x))
     _check(rc, "moe_permute")
+    return out
+
+
+def moe_permute_noalloc(x, topk_idx, E: int, with_x_perm: bool = True, out: dict | None = None):
+    """moe_permute with the library's static scratch instead of a workspace.
+    ``out`` (optional): preallocated offsets, sorted_token, row_of (and
+    x_perm) tensors to write, so that the call itself allocates nothing."""
+    _req(x, "x")
+    dev = x.device
+    T, h = x.shape
+    k = topk_idx.shape[1]
+    _req(topk_idx, "topk_idx", dtype=torch.int32, shape=(T, k), device=dev)
+    P = T * k
+    if out is None:
+        out = dict(
+            offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+            sorted_token=torch.empty((P,), dtype=torch.int32, device=dev),
+            row_of=torch.empty((T, k), dtype=torch.int32, device=dev),
+            x_perm=torch.empty((P, h), dtype=x.dtype, device=dev) if with_x_perm else None,
+        )
+    _req(out["offsets"], "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(out["sorted_token"], "sorted_token", dtype=torch.int32, shape=(P,), device=dev)
+    _req(out["row_of"], "row_of", dtype=torch.int32, shape=(T, k), device=dev)
+    _opt(out.get("x_perm"), "x_perm", dtype=x.dtype, shape=(P, h), device=dev)
+    rc = lib().moe_permute_noalloc(_ptr(x), DTYPE[x.dtype], T, h, E, k, _ptr(topk_idx), _ptr(out["offsets"]),
+                                   _ptr(out["sorted_token"]), _ptr(out["row_of"]), _ptr(out.get("x_perm")),
+                                   _stream(x))
+    _check(rc, "moe_permute_noalloc")
     return out
 
 

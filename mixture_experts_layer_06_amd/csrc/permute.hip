@@ -15,6 +15,8 @@
 //      below t. Writes row_of and sorted_token.
 //   4. copy: each token row is read once from HBM and written to its k
 //      permuted rows with 16-byte accesses.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -162,38 +164,35 @@ __global__ __launch_bounds__(256) void permute_weights_bwd_kernel(const float *_
 
 using namespace moe;
 
-extern "C" size_t moe_permute_workspace_size(int64_t T, int E, int k) {
-    (void)k;
-    if (T < 0 || E <= 0) return 0;
-    const int64_t nb = (T + kBlockTok - 1) / kBlockTok;
-    return static_cast<size_t>(2 * nb * E) * sizeof(int32_t) + 256;
+namespace {
+
+// Checks shared by moe_permute and moe_permute_noalloc (everything but the
+// workspace).
+int permute_check(const void *x, int dtype, int64_t T, int64_t h, int E, int k, const int32_t *topk_idx,
+                  const int32_t *offsets, const int32_t *sorted_token, const int32_t *row_of, const void *x_perm,
+                  const char *name) {
+    MOE_CHECK_ARG(offsets && (T == 0 || (topk_idx && sorted_token && row_of)), MOE_ERR_INVALID_ARG,
+                  "%s: null required pointer", name);
+    MOE_CHECK_ARG(x_perm == nullptr || x != nullptr, MOE_ERR_INVALID_ARG, "%s: x_perm requested without x", name);
+    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG, "%s: bad dtype %d", name,
+                  dtype);
+    MOE_CHECK_ARG(T >= 0 && h > 0 && E > 0 && k > 0, MOE_ERR_INVALID_ARG, "%s: bad sizes", name);
+    MOE_CHECK_ARG(k <= E && E <= kMaxE && k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED,
+                  "%s: need k <= E <= 256, k <= 8, h %% 64 == 0", name);
+    MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+                  "%s: T*k must be < 2^31", name);
+    MOE_CHECK_ARG(x_perm == nullptr || (aligned16(x) && aligned16(x_perm)), MOE_ERR_INVALID_ARG,
+                  "%s: pointers must be 16-byte aligned", name);
+    return MOE_OK;
 }
 
-extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
-                           const int32_t *topk_idx, int32_t *offsets, int32_t *sorted_token,
-                           int32_t *row_of, void *x_perm, void *workspace, size_t workspace_bytes,
-                           void *stream) {
-    clear_error();
-    MOE_CHECK_ARG(offsets && (T == 0 || (topk_idx && sorted_token && row_of)), MOE_ERR_INVALID_ARG,
-                  "moe_permute: null required pointer");
-    MOE_CHECK_ARG(x_perm == nullptr || x != nullptr, MOE_ERR_INVALID_ARG,
-                  "moe_permute: x_perm requested without x");
-    MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
-                  "moe_permute: bad dtype %d", dtype);
-    MOE_CHECK_ARG(T >= 0 && h > 0 && E > 0 && k > 0, MOE_ERR_INVALID_ARG,
-                  "moe_permute: bad sizes");
-    MOE_CHECK_ARG(k <= E && E <= kMaxE && k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED,
-                  "moe_permute: need k <= E <= 256, k <= 8, h %% 64 == 0");
-    MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
-                  "moe_permute: T*k must be < 2^31");
-    const size_t need = moe_permute_workspace_size(T, E, k);
-    MOE_CHECK_ARG(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
-                  "moe_permute: workspace of %zu bytes needed", need);
-    MOE_CHECK_ARG(aligned16(workspace) && (x_perm == nullptr || (aligned16(x) && aligned16(x_perm))),
-                  MOE_ERR_INVALID_ARG, "moe_permute: pointers must be 16-byte aligned");
-    hipStream_t s = as_stream(stream);
+// The four launches of the dispatch; ws: 2 nb E ints (block counts, then
+// block bases), every entry written by block_hist and scan before it is read.
+int permute_launch(const void *x, int dtype, int64_t T, int64_t h, int E, int k, const int32_t *topk_idx,
+                   int32_t *offsets, int32_t *sorted_token, int32_t *row_of, void *x_perm, int32_t *ws,
+                   hipStream_t s, const char *name) {
     const int nb = static_cast<int>((T + kBlockTok - 1) / kBlockTok);
-    int32_t *blockcounts = static_cast<int32_t *>(workspace);
+    int32_t *blockcounts = ws;
     int32_t *blockbase = blockcounts + static_cast<int64_t>(nb) * E;
     const int P = static_cast<int>(T * k);
     if (nb > 0)
@@ -213,7 +212,83 @@ extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E
                                dim3(256), 0, s, static_cast<const float *>(x), static_cast<int>(h), k, row_of,
                                static_cast<float *>(x_perm), T * (h / 4));
     }
-    return check_launch("moe_permute");
+    return check_launch(name);
+}
+
+// Scratch of moe_permute_noalloc: one copy per GPU, in the library's device
+// image, held until the process ends. Its name is a host-side stand-in: host
+// code uses only the device address that hipGetSymbolAddress returns for the
+// current device, cached per device below.
+constexpr int64_t kNoAllocScratchInts = 262144;   // 1 MiB: 2 nb E <= 262144
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current); null with the error set on failure.
+int32_t *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        set_error("moe_permute_noalloc: no current device");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            set_error(std::string("moe_permute_noalloc: hipGetSymbolAddress failed: ") + hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int E, int k) {
+    (void)k;
+    if (T < 0 || E <= 0) return 0;
+    const int64_t nb = (T + kBlockTok - 1) / kBlockTok;
+    return static_cast<size_t>(2 * nb * E) * sizeof(int32_t) + 256;
+}
+
+extern "C" int moe_permute(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
+                           const int32_t *topk_idx, int32_t *offsets, int32_t *sorted_token,
+                           int32_t *row_of, void *x_perm, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    clear_error();
+    const int st = permute_check(x, dtype, T, h, E, k, topk_idx, offsets, sorted_token, row_of, x_perm,
+                                 "moe_permute");
+    if (st != MOE_OK) return st;
+    const size_t need = moe_permute_workspace_size(T, E, k);
+    MOE_CHECK_ARG(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+                  "moe_permute: workspace of %zu bytes needed", need);
+    MOE_CHECK_ARG(aligned16(workspace), MOE_ERR_INVALID_ARG, "moe_permute: pointers must be 16-byte aligned");
+    return permute_launch(x, dtype, T, h, E, k, topk_idx, offsets, sorted_token, row_of, x_perm,
+                          static_cast<int32_t *>(workspace), as_stream(stream), "moe_permute");
+}
+
+extern "C" int moe_permute_noalloc(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
+                                   const int32_t *topk_idx, int32_t *offsets, int32_t *sorted_token,
+                                   int32_t *row_of, void *x_perm, void *stream) {
+    clear_error();
+    const int st = permute_check(x, dtype, T, h, E, k, topk_idx, offsets, sorted_token, row_of, x_perm,
+                                 "moe_permute_noalloc");
+    if (st != MOE_OK) return st;
+    const int64_t nb = (T + kBlockTok - 1) / kBlockTok;
+    MOE_CHECK_ARG(2 * nb * E <= kNoAllocScratchInts, MOE_ERR_UNSUPPORTED,
+                  "moe_permute_noalloc: ceil(T/256) * E = %lld exceeds the static scratch's %lld",
+                  static_cast<long long>(nb * E), static_cast<long long>(kNoAllocScratchInts / 2));
+    int32_t *ws = scratch_on_current_device();
+    if (ws == nullptr) return MOE_ERR_HIP;
+    return permute_launch(x, dtype, T, h, E, k, topk_idx, offsets, sorted_token, row_of, x_perm, ws,
+                          as_stream(stream), "moe_permute_noalloc");
 }
 
 extern "C" int moe_permute_weights(const float *topk_w, int64_t T, int k, const int32_t *row_of, float *row_w,

@@ -107,6 +107,11 @@ def _validation_cases():
     assert rc == 3
     rc = L.moe_permute(dummy, 1, 1000, 64, 16, 2, dummy, dummy, dummy, dummy, dummy, None, need, None)
     assert rc == 3
+    # the no-allocation permute: past its static scratch (ceil(T/256) * E > 131072), bad k
+    rc = L.moe_permute_noalloc(dummy, 1, 131073, 64, 256, 2, dummy, dummy, dummy, dummy, None, None)
+    assert rc == 2 and b"static scratch" in L.moe_last_error()
+    assert L.moe_permute_noalloc(dummy, 1, 16, 64, 8, 9, dummy, dummy, dummy, dummy, None, None) == 2
+    assert L.moe_permute_noalloc(dummy, 1, 16, 64, 8, 2, None, dummy, dummy, dummy, None, None) == 1
     # grouped ffn: F not a multiple of 64, gu with GELU, shared expert without weights
     rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 100, 4, dummy, 1, dummy, None, dummy, None, None, 0,
                            None, None, dummy, None, dummy, None, None, 0, None)

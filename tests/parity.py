@@ -6,6 +6,11 @@ rows (tokens), the largest of
   * max |got - ref| / max |ref| over the whole tensor, and
   * max over rows t of ||got_t - ref_t||_inf / max(||ref_t||_inf, 1e-6 * max|ref|),
 which stays meaningful where single elements of ref are near zero.
+
+Weight gradients are sums over an expert's tokens; their rows can cancel to
+near zero, so their row-wise measure is taken against the row's sum of
+absolute terms (``rel_err_terms``): the error a correct fp32/bf16 kernel
+makes on a sum is bounded by a multiple of that sum, not of its result.
 """
 import numpy as np
 import torch
@@ -60,3 +65,26 @@ def oracle_inputs(inp: dict) -> dict:
 
 def to_device(inp: dict, device="cuda") -> dict:
     return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def rel_err_terms(got, ref, terms) -> float:
+    """max over rows f of max_i |got - ref|[f, i] / max_i terms[f, i], where
+    terms[f, i] = sum over the summed index of |the products| (for a weight
+    gradient dW = sum_t a_t^T b_t: |a|^T |b|)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    terms = np.asarray(terms, dtype=np.float64)
+    assert got.shape == ref.shape == terms.shape
+    d = np.abs(got - ref).max(axis=1)
+    t = terms.max(axis=1)
+    floor = 1e-30 + 1e-9 * t.max()
+    return float((d / np.maximum(t, floor)).max())
+
+
+def expert_grad_terms(oracle, x_rows, w1e, w2e, act, dy):
+    """Sums of absolute terms of an expert's weight gradients over its rows
+    (x_rows [m,h], dy [m,h] = routing weight times dL/dout): |dgu|^T |x| for
+    dW1 and |dy|^T |act| for dW2, from the oracle's own expert backward."""
+    gb = oracle.expert_backward(x_rows, w1e, w2e, act, dy)
+    x64 = np.abs(np.asarray(x_rows, dtype=np.float64))
+    return np.abs(gb["dgu"]).T @ x64, np.abs(dy).T @ np.abs(gb["hid"])

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 from mixture_experts_layer_06_amd import workloads as wl
-from parity import TOL, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
+from parity import (TOL, expert_grad_terms, oracle_inputs, rel_err, rel_err_tensor, rel_err_terms, to_device,
+                    to_np32)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,10 +119,28 @@ def test_backward_slice_of_imbalanced_workload(moe_lib):
     _check_all(sub, inp, f, g, ref, experts)
 
 
+def _heavy_rows(cfg, inp, sub_inp, g, ref, experts, counts, errs):
+    """Row-wise errors of heavy experts' weight gradients against the sums of
+    absolute terms of each row (the oracle's own expert backward gives the
+    terms), added to errs."""
+    xs, Gs = to_np32(sub_inp["x"]), to_np32(sub_inp["grad_out"]).astype(np.float64)
+    r = oracle.route(xs, to_np32(inp["w_gate"]), cfg.k, cfg.score, to_np32(inp["b_gate"]))
+    for e in experts:
+        tk, sl = np.nonzero(r["topk_idx"] == e)
+        assert tk.size == counts[e], "every token of expert %d is in the sample" % e
+        dy = r["topk_w"][tk, sl][:, None] * Gs[tk]
+        t1, t2 = expert_grad_terms(oracle, xs[tk], to_np32(inp["w1"][e]), to_np32(inp["w2"][e]), cfg.act, dy)
+        errs["grad_w1[%d] rows/terms" % e] = rel_err_terms(g["grad_w1"][e].cpu().numpy(), ref["dw1"][e], t1)
+        errs["grad_w2[%d] rows/terms" % e] = rel_err_terms(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e], t2)
+
+
 def test_backward_full_size_sampled(moe_lib):
     """Full imbalanced step (T=8192): input gradients of sampled tokens, and
-    weight gradients of two lightly loaded experts computed from all their
-    tokens; empty experts' gradients exactly zero; two runs bitwise equal."""
+    weight gradients of the two lightest, a median and the hottest expert
+    (about 6,300 rows, about 99 k-steps per weight-gradient tile) computed
+    from all their tokens, per tensor and, for the two heavy ones, row by row
+    against each row's sum of absolute terms; empty experts' gradients exactly
+    zero; two runs bitwise equal."""
     cfg = wl.CONFIGS[5]
     print("case full size", flush=True)
     inp = wl.make_inputs(cfg, device="cuda")
@@ -132,7 +151,11 @@ def test_backward_full_size_sampled(moe_lib):
         assert not g["grad_w1"][int(e)].any() and not g["grad_w2"][int(e)].any()
         assert float(g["grad_w_gate"][int(e)].abs().max()) == 0.0
     order = np.argsort(counts, kind="stable")
-    light = [int(e) for e in order if counts[e] > 0][:2]
+    live = [int(e) for e in order if counts[e] > 0]
+    # the two lightest, a median and the hottest expert (about 6,300 rows),
+    # each over all of its tokens
+    light = live[:2] + [live[len(live) // 2], live[-1]]
+    assert counts[live[-1]] > 5000
     tok = sorted(set(np.nonzero(np.isin(topk, light).any(axis=1))[0].tolist())
                  | set(np.linspace(0, cfg.T - 1, 6).astype(int).tolist()))
     tok = np.asarray(tok, dtype=np.int64)
@@ -152,6 +175,7 @@ def test_backward_full_size_sampled(moe_lib):
         errs["grad_w2[%d]" % e] = rel_err_tensor(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e])
         errs["grad_w_gate[%d]" % e] = rel_err_tensor(g["grad_w_gate"][e].cpu().numpy(),
                                                      ref["dw_gate"][e])
+    _heavy_rows(cfg, inp, sub_inp, g, ref, light[2:], counts, errs)
     print({k: round(v, 5) for k, v in errs.items()}, flush=True)
     assert all(v <= tol for v in errs.values()), errs
     _, g2 = _gpu_fwd_bwd(cfg, inp)

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from mixture_experts_layer_06_amd import workloads as wl
-from parity import TOL, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
+from parity import (TOL, expert_grad_terms, oracle_inputs, rel_err, rel_err_tensor, rel_err_terms, to_device,
+                    to_np32)
 
 pytestmark = pytest.mark.gpu
 
@@ -182,8 +183,9 @@ def test_backward_slice_of_imbalanced_workload(moe_lib):
 def test_full_size_step_sampled(moe_lib):
     """Full imbalanced step (T=8192), folded and recomputing: input
     gradients and routing-weight gradients of sampled tokens, and weight
-    gradients of the two most lightly loaded experts computed from all their
-    tokens, against the oracle; empty experts get exact zeros; two runs are
+    gradients of the two lightest, a median and the hottest expert computed
+    from all their tokens (the heavy ones also row by row against each row's
+    sum of absolute terms), against the oracle; empty experts get exact zeros; two runs are
     bitwise equal; neither the expert outputs nor the activation are kept."""
     cfg = wl.CONFIGS[5]
     print("case full size, memory-efficient", flush=True)
@@ -195,7 +197,11 @@ def test_full_size_step_sampled(moe_lib):
     for e in np.nonzero(counts == 0)[0]:
         assert not g["grad_w1"][int(e)].any() and not g["grad_w2"][int(e)].any()
     order = np.argsort(counts, kind="stable")
-    light = [int(e) for e in order if counts[e] > 0][:2]
+    live = [int(e) for e in order if counts[e] > 0]
+    # the two lightest, a median and the hottest expert (about 6,300 rows),
+    # each over all of its tokens
+    light = live[:2] + [live[len(live) // 2], live[-1]]
+    assert counts[live[-1]] > 5000
     tok = sorted(set(np.nonzero(np.isin(topk, light).any(axis=1))[0].tolist())
                  | set(np.linspace(0, cfg.T - 1, 6).astype(int).tolist()))
     ti = torch.as_tensor(np.asarray(tok, dtype=np.int64), device="cuda")
@@ -218,6 +224,8 @@ def test_full_size_step_sampled(moe_lib):
         err["grad_w1[%d]" % e] = rel_err_tensor(g["grad_w1"][e].cpu().numpy(), ref["dw1"][e])
         err["grad_w2[%d]" % e] = rel_err_tensor(g["grad_w2"][e].cpu().numpy(), ref["dw2"][e])
         err["grad_w_gate[%d]" % e] = rel_err_tensor(g["grad_w_gate"][e].cpu().numpy(), ref["dw_gate"][e])
+    from test_gpu_backward import _heavy_rows
+    _heavy_rows(cfg, inp, dict(x=inp["x"][ti], grad_out=inp["grad_out"][ti]), g, ref, light[2:], counts, err)
     print({k: float("%.3g" % v) for k, v in err.items()}, flush=True)
     assert all(v <= tol for v in err.values()), err
     _, g2 = _fwd_bwd(cfg, inp, memory_efficient=True)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -180,7 +180,8 @@ int moe_permute_noalloc(const void *x, int dtype, int64_t T, int64_t h, int E, i
  * Outputs:
  *   act  [P+T_sh,F] dtype     activation silu(g)*u or GELU(a) (input of the
  *                             second GEMM; rows P.. are the shared expert's)
- *   gu   [P+T_sh,n1*F] dtype|NULL  pre-activations (kept for the backward)
+ *   gu   [P+T_sh,n1*F] dtype|NULL  pre-activations kept for the backward
+ *                             (SwiGLU: g then u; GELU: a, bias included)
  *   y    [P,h] dtype          expert outputs in permuted order
  *   y_sh [T_sh,h] dtype|NULL  shared-expert output
  * Arithmetic: fp32 accumulation on MFMA; act, gu and y are rounded to dtype.
@@ -354,18 +355,27 @@ int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype, int64_t T,
                       int k, const int32_t *row_of, const float *topk_w, void *grad_y,
                       float *grad_topk_w, void *stream);
 
-/* Grouped FFN backward (SwiGLU, no bias). Per segment e with rows X_e of
- * x_perm, saved pre-activations (g,u) = gu rows and act = silu(g)*u:
- *   dact = grad_y W2[e];  dg = dact * u * silu'(g);  du = dact * silu(g)
- *   grad_w2[e] = grad_y_e^T act_e          [h,F]  fp32
- *   grad_w1[e] = [dg du]_e^T X_e           [2F,h] fp32 (zeros for an empty e)
- *   grad_x_perm = [dg du] W1[e]            [P,h]  dtype
- * grad_gu [P,2F] dtype is caller-provided scratch that receives [dg du]. */
+/* Grouped FFN backward. Per segment e with rows X_e of x_perm, the
+ * activation act and the pre-activations gu the forward kept:
+ *   dact = grad_y W2[e]
+ *   SwiGLU (gu = [g u]): dg = dact * u * silu'(g), du = dact * silu(g),
+ *                        dA = [dg du] [P,2F]
+ *   GELU (gu = a = X W1[e]^T + b1[e]): dA = dact * gelu'(a) [P,F],
+ *                        gelu'(a) = Phi(a) + a phi(a)
+ *   grad_w2[e] = grad_y_e^T act_e          [h,F]    fp32
+ *   grad_w1[e] = dA_e^T X_e                [n1F,h]  fp32 (zeros for an empty e)
+ *   grad_x_perm = dA W1[e]                 [P,h]    dtype
+ *   grad_b1[e] = column sums of dA_e       [n1F]    fp32 (NULL: not computed)
+ *   grad_b2[e] = column sums of grad_y_e   [h]      fp32 (NULL: not computed)
+ * grad_gu [P,n1F] dtype is caller-provided scratch that receives dA. bf16
+ * SwiGLU runs on the matrix-core kernels; GELU (bf16 or fp32) and fp32
+ * SwiGLU on a plainer fp32-FMA segmented GEMM (the small layers that use
+ * them). Sums run in a fixed order (deterministic). */
 int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const void *act,
                         const void *gu, int dtype, int64_t P, int64_t h, int64_t F, int E,
                         const int32_t *offsets, int act_kind, const void *w1, const void *w2,
                         void *grad_gu, void *grad_x_perm, float *grad_w1, float *grad_w2,
-                        void *stream);
+                        float *grad_b1, float *grad_b2, void *stream);
 
 /* Grouped FFN backward with the activation recomputed ("Scalable Training ...
  * with Megatron Core", section 4.1.2, recomputing the activation function):

@@ -46,7 +46,7 @@ _SIGS = {
     "moe_unpermute": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_unpermute_bwd": ([_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd": ([_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
-                             _vp, _vp, _vp, _vp, _vp], _int),
+                             _vp, _vp, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_route_bwd_workspace_size": ([_i64, _i64, _int, _int], _sz),
     "moe_route_bwd": ([_vp, _int, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        _vp, _vp, _vp, _sz, _vp], _int),
@@ -328,7 +328,10 @@ def moe_unpermute_bwd(grad_out, y, row_of, topk_w):
     return grad_y, grad_w
 
 
-def moe_grouped_ffn_bwd(grad_y, x_perm, act_out, gu, offsets, w1, w2, act: str = "swiglu"):
+def moe_grouped_ffn_bwd(grad_y, x_perm, act_out, gu, offsets, w1, w2, act: str = "swiglu",
+                        want_bias_grads: bool = False):
+    """Expert gradients; with want_bias_grads also grad_b1 [E, n1 F] and
+    grad_b2 [E, h] (fp32)."""
     _req(grad_y, "grad_y")
     dev = grad_y.device
     dt = grad_y.dtype
@@ -346,12 +349,15 @@ def moe_grouped_ffn_bwd(grad_y, x_perm, act_out, gu, offsets, w1, w2, act: str =
     grad_x_perm = torch.empty((P, h), dtype=dt, device=dev)
     grad_w1 = torch.empty((E, n1 * F, h), dtype=torch.float32, device=dev)
     grad_w2 = torch.empty((E, h, F), dtype=torch.float32, device=dev)
+    grad_b1 = torch.empty((E, n1 * F), dtype=torch.float32, device=dev) if want_bias_grads else None
+    grad_b2 = torch.empty((E, h), dtype=torch.float32, device=dev) if want_bias_grads else None
     rc = lib().moe_grouped_ffn_bwd(_ptr(grad_y), _ptr(x_perm), _ptr(act_out), _ptr(gu), DTYPE[dt], P,
                                    h, F, E, _ptr(offsets), ACT[act], _ptr(w1), _ptr(w2),
                                    _ptr(grad_gu), _ptr(grad_x_perm), _ptr(grad_w1), _ptr(grad_w2),
-                                   _stream(grad_y))
+                                   _ptr(grad_b1), _ptr(grad_b2), _stream(grad_y))
     _check(rc, "moe_grouped_ffn_bwd")
-    return dict(grad_gu=grad_gu, grad_x_perm=grad_x_perm, grad_w1=grad_w1, grad_w2=grad_w2)
+    return dict(grad_gu=grad_gu, grad_x_perm=grad_x_perm, grad_w1=grad_w1, grad_w2=grad_w2,
+                grad_b1=grad_b1, grad_b2=grad_b2)
 
 
 def moe_grouped_ffn_bwd_recompute(grad_y, x_perm, gu, offsets, w1, w2, act: str = "swiglu",

@@ -282,12 +282,15 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
     const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
     bf16_t *Cseg = ti.shared ? static_cast<bf16_t *>(a.C_sh) + static_cast<int64_t>(ti.m0) * a.N_out
                              : static_cast<bf16_t *>(a.C) + crow0 * a.N_out;
+    // pre-activations kept for the backward: SwiGLU [rows][2 N_out] (g, u),
+    // GELU [rows][N_out] (with the bias)
     bf16_t *GUseg = nullptr;
-    if ((MODE & 7) == kModeSwiGLU) {
+    if ((MODE & 7) == kModeSwiGLU || (MODE & 7) == kModeGELU) {
+        const int gw = (MODE & 7) == kModeSwiGLU ? 2 * a.N_out : a.N_out;
         if (ti.shared)
-            GUseg = a.GU_sh ? static_cast<bf16_t *>(a.GU_sh) + static_cast<int64_t>(ti.m0) * 2 * a.N_out : nullptr;
+            GUseg = a.GU_sh ? static_cast<bf16_t *>(a.GU_sh) + static_cast<int64_t>(ti.m0) * gw : nullptr;
         else
-            GUseg = a.GU ? static_cast<bf16_t *>(a.GU) + crow0 * 2 * a.N_out : nullptr;
+            GUseg = a.GU ? static_cast<bf16_t *>(a.GU) + crow0 * gw : nullptr;
     }
     const bf16_t *bias = (a.bias && !ti.shared)
                              ? static_cast<const bf16_t *>(a.bias) + static_cast<int64_t>(ti.seg) * nb_rows
@@ -358,7 +361,16 @@ __device__ __forceinline__ void store_tile(const GGArgs &a, const TileInfo &ti,
                     for (int q = 0; q < 4; ++q) {
                         v[q] = acc[i][j][4 * gq + q];
                         if (bias) v[q] += bf16_to_f32(bias[n + q]);
-                        if ((MODE & 7) == kModeGELU) v[q] = gelu_erf_f(v[q]) * rw;
+                    }
+                    if ((MODE & 7) == kModeGELU) {
+                        if (GUseg) {
+                            uint2 og;
+                            og.x = pack_bf16x2(v[0], v[1]);
+                            og.y = pack_bf16x2(v[2], v[3]);
+                            *reinterpret_cast<uint2 *>(GUseg + static_cast<int64_t>(m) * a.N_out + n) = og;
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = gelu_erf_f(v[q]) * rw;
                     }
                     uint2 o;
                     o.x = pack_bf16x2(v[0], v[1]);
@@ -617,10 +629,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
         float *Cseg = ti.shared ? static_cast<float *>(a.C_sh)
                                 : static_cast<float *>(a.C) + static_cast<int64_t>(ti.row0) * a.N_out;
         float *GUseg = nullptr;
-        if ((MODE & 7) == kModeSwiGLU)
+        if ((MODE & 7) == kModeSwiGLU || (MODE & 7) == kModeGELU) {
+            const int gw = (MODE & 7) == kModeSwiGLU ? 2 * a.N_out : a.N_out;
             GUseg = ti.shared ? static_cast<float *>(a.GU_sh)
-                              : (a.GU ? static_cast<float *>(a.GU) + static_cast<int64_t>(ti.row0) * 2 * a.N_out
-                                      : nullptr);
+                              : (a.GU ? static_cast<float *>(a.GU) + static_cast<int64_t>(ti.row0) * gw : nullptr);
+        }
         const float *bias = (a.bias && !ti.shared)
                                 ? static_cast<const float *>(a.bias) + static_cast<int64_t>(ti.seg) * nb_rows
                                 : nullptr;
@@ -658,16 +671,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GGArgs a) {
                 for (int i = 0; i < NT; ++i) {
                     const int n = ti.n_tile * BN + wn * 32 + i * 16 + 4 * ng;
                     if (n >= a.N_out) continue;
-                    float4 o;
-                    float *op = &o.x;
+                    float4 o, pre;
+                    float *op = &o.x, *pp = &pre.x;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float v = acc[i][j][q];
                         if (bias) v += bias[n + q];
+                        pp[q] = v;
                         if ((MODE & 7) == kModeGELU) v = gelu_erf_f(v) * rw;
                         op[q] = v;
                     }
                     *reinterpret_cast<float4 *>(Cseg + static_cast<int64_t>(mm) * a.N_out + n) = o;
+                    if ((MODE & 7) == kModeGELU && GUseg)
+                        *reinterpret_cast<float4 *>(GUseg + static_cast<int64_t>(mm) * a.N_out + n) = pre;
                 }
             }
         }
@@ -781,8 +797,6 @@ int grouped_ffn(const void *x_perm, const int32_t *gather_rows, int64_t x_rows, 
     const bool has_sh = T_sh > 0;
     MOE_CHECK_ARG(!has_sh || (x_sh && w1_sh && w2_sh && y_sh), MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: shared expert needs x_sh, w1_sh, w2_sh and y_sh");
-    MOE_CHECK_ARG(gu == nullptr || act_kind == MOE_ACT_SWIGLU, MOE_ERR_INVALID_ARG,
-                  "moe_grouped_ffn: gu is kept for SwiGLU only");
     MOE_CHECK_ARG(workspace_bytes == 0 || workspace, MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn: workspace_bytes > 0 with a null workspace");
     const void *ptrs[] = {x_perm, w1, b1, w2, b2, x_sh, w1_sh, w2_sh, act, gu, y, y_sh, workspace};

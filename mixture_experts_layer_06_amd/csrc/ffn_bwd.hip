@@ -1,4 +1,5 @@
-// Backward of the grouped SwiGLU FFN: four grouped GEMMs per step.
+// Backward of the grouped bf16 SwiGLU FFN: four grouped GEMMs per step
+// (other expert kinds and fp32: ffn_bwd_generic.hip).
 //
 //   dact   = dY W2[e]                      (per segment; + SwiGLU backward)
 //   dg     = dact * u * silu'(g),  du = dact * silu(g)
@@ -532,7 +533,7 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 int check_bwd_args(const char *what, const void *grad_y, const void *x_perm, const void *gu, int dtype, int64_t P,
                    int64_t h, int64_t F, int E, const int32_t *offsets, int act_kind, const void *w1,
                    const void *w2, const void *grad_gu, const void *grad_x_perm, const float *grad_w1,
-                   const float *grad_w2) {
+                   const float *grad_w2, bool bf16_swiglu_only) {
     MOE_CHECK_ARG(offsets && w1 && w2 && grad_w1 && grad_w2 &&
                       (P == 0 || (grad_y && x_perm && gu && grad_gu && grad_x_perm)),
                   MOE_ERR_INVALID_ARG, "%s: null required pointer", what);
@@ -541,7 +542,7 @@ int check_bwd_args(const char *what, const void *grad_y, const void *x_perm, con
     MOE_CHECK_ARG(act_kind == MOE_ACT_GELU || act_kind == MOE_ACT_SWIGLU, MOE_ERR_INVALID_ARG,
                   "%s: bad activation %d", what, act_kind);
     MOE_CHECK_ARG(P >= 0 && h > 0 && F > 0 && E > 0, MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
-    MOE_CHECK_ARG(dtype == MOE_DTYPE_BF16 && act_kind == MOE_ACT_SWIGLU, MOE_ERR_UNSUPPORTED,
+    MOE_CHECK_ARG(!bf16_swiglu_only || (dtype == MOE_DTYPE_BF16 && act_kind == MOE_ACT_SWIGLU), MOE_ERR_UNSUPPORTED,
                   "%s: bf16 SwiGLU experts only", what);
     MOE_CHECK_ARG(h % 64 == 0 && F % 64 == 0 && E <= 256, MOE_ERR_UNSUPPORTED,
                   "%s: need h %% 64 == 0, F %% 64 == 0, E <= 256", what);
@@ -631,17 +632,26 @@ extern "C" int moe_grouped_ffn_bwd(const void *grad_y, const void *x_perm, const
                                    const void *gu, int dtype, int64_t P, int64_t h, int64_t F, int E,
                                    const int32_t *offsets, int act_kind, const void *w1,
                                    const void *w2, void *grad_gu, void *grad_x_perm, float *grad_w1,
-                                   float *grad_w2, void *stream) {
+                                   float *grad_w2, float *grad_b1, float *grad_b2, void *stream) {
     clear_error();
     int st = check_bwd_args("moe_grouped_ffn_bwd", grad_y, x_perm, gu, dtype, P, h, F, E, offsets, act_kind, w1,
-                            w2, grad_gu, grad_x_perm, grad_w1, grad_w2);
+                            w2, grad_gu, grad_x_perm, grad_w1, grad_w2, false);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(P == 0 || (act && aligned16(act)), MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn_bwd: act must be a 16-byte aligned pointer");
-    return ffn_bwd_gemms(static_cast<const bf16_t *>(grad_y), static_cast<const bf16_t *>(x_perm),
-                         static_cast<const bf16_t *>(act), gu, P, h, F, E, offsets, w1, w2,
-                         static_cast<bf16_t *>(grad_gu), grad_x_perm, grad_w1, grad_w2, nullptr, nullptr,
-                         as_stream(stream));
+    hipStream_t s = as_stream(stream);
+    if (dtype != MOE_DTYPE_BF16 || act_kind != MOE_ACT_SWIGLU)
+        return ffn_bwd_generic(grad_y, x_perm, act, gu, dtype, P, h, F, E, offsets, act_kind, w1, w2, grad_gu,
+                               grad_x_perm, grad_w1, grad_w2, grad_b1, grad_b2, s);
+    st = ffn_bwd_gemms(static_cast<const bf16_t *>(grad_y), static_cast<const bf16_t *>(x_perm),
+                       static_cast<const bf16_t *>(act), gu, P, h, F, E, offsets, w1, w2,
+                       static_cast<bf16_t *>(grad_gu), grad_x_perm, grad_w1, grad_w2, nullptr, nullptr, s);
+    if (st != MOE_OK) return st;
+    if (grad_b2) st = segment_colsums_bf16(grad_y, static_cast<int>(h), offsets, E, grad_b2, s, "moe_grouped_ffn_bwd db2");
+    if (st != MOE_OK) return st;
+    if (grad_b1)
+        st = segment_colsums_bf16(grad_gu, static_cast<int>(2 * F), offsets, E, grad_b1, s, "moe_grouped_ffn_bwd db1");
+    return st;
 }
 
 extern "C" size_t moe_grouped_ffn_bwd_recompute_workspace_size(int64_t P, int64_t F, int weighted) {
@@ -659,7 +669,7 @@ extern "C" int moe_grouped_ffn_bwd_recompute(const void *grad_y, const void *x_p
                                              void *stream) {
     clear_error();
     int st = check_bwd_args("moe_grouped_ffn_bwd_recompute", grad_y, x_perm, gu, dtype, P, h, F, E, offsets,
-                            act_kind, w1, w2, grad_gu, grad_x_perm, grad_w1, grad_w2);
+                            act_kind, w1, w2, grad_gu, grad_x_perm, grad_w1, grad_w2, true);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG((row_w == nullptr) == (grad_row_w == nullptr), MOE_ERR_INVALID_ARG,
                   "moe_grouped_ffn_bwd_recompute: row_w and grad_row_w go together");

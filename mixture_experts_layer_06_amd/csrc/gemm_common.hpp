@@ -27,6 +27,16 @@ int gemm_bf16_f32out(const void *A, const void *B, int T, int K, int N, float *C
                      size_t ws_bytes, hipStream_t s);
 size_t gemm_split_workspace_bytes();
 
+// Backward of the expert kinds the bf16 SwiGLU kernels do not cover (GELU in
+// bf16 or fp32, SwiGLU in fp32), bias gradients included (NULL: skipped);
+// and the per-segment column sums that give bias gradients (bf16 rows).
+int ffn_bwd_generic(const void *grad_y, const void *x_perm, const void *act, const void *gu, int dtype, int64_t P,
+                    int64_t h, int64_t F, int E, const int32_t *offsets, int act_kind, const void *w1, const void *w2,
+                    void *grad_gu, void *grad_x_perm, float *grad_w1, float *grad_w2, float *grad_b1,
+                    float *grad_b2, hipStream_t s);
+int segment_colsums_bf16(const void *M, int N, const int32_t *offsets, int E, float *db, hipStream_t s,
+                         const char *what);
+
 struct GGArgs {
     const void *A;          // activations; segment s starts at row offsets[s]
     const void *B;          // weights, [E][nb_rows][K]

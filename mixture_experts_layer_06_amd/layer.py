@@ -75,7 +75,7 @@ def forward(inp: dict, k: int, score: str, act: str, keep_for_backward: bool = F
     f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn(
         x if gather else d["x_perm"], d["offsets"], inp["w1"], inp["w2"], act, b1=inp.get("b1"),
         b2=inp.get("b2"), x_sh=x if has_sh else None, w1_sh=inp.get("w1_sh"), w2_sh=inp.get("w2_sh"),
-        keep_gu=keep_for_backward and act == "swiglu", gather_rows=d["sorted_token"] if gather else None,
+        keep_gu=keep_for_backward, gather_rows=d["sorted_token"] if gather else None,
         row_w=row_w))
     out = B.moe_unpermute(f["y"], d["row_of"], None if memory_efficient else r["topk_w"], y_sh=f["y_sh"])
     if memory_efficient or recompute:
@@ -142,8 +142,10 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
         g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd_recompute(
             grad_y, d["x_perm"], fwd["gu"], d["offsets"], inp["w1"], inp["w2"], act, row_w=row_w))
     else:
+        has_b = inp.get("b1") is not None or inp.get("b2") is not None
         g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd(
-            grad_y, d["x_perm"], fwd["act"], fwd["gu"], d["offsets"], inp["w1"], inp["w2"], act))
+            grad_y, d["x_perm"], fwd["act"], fwd["gu"], d["offsets"], inp["w1"], inp["w2"], act,
+            want_bias_grads=has_b))
     if row_w is not None:
         grad_w = B.moe_permute_weights_bwd(g["grad_row_w"], d["row_of"])
     r = B.moe_route_bwd(inp["x"], E, fwd["topk_idx"], fwd["topk_w"], grad_w, fwd["offsets"],
@@ -159,7 +161,8 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
         B.moe_router_dense_bwd(inp["x"], inp["w_gate"], dl, grad_w_gate=r["grad_w_gate"],
                                grad_b_gate=r["grad_b_gate"], grad_x=grad_x)
     return dict(grad_x=grad_x, grad_topk_w=grad_w, grad_y=grad_y, grad_w1=g["grad_w1"],
-                grad_w2=g["grad_w2"], grad_w_gate=r["grad_w_gate"], grad_b_gate=r["grad_b_gate"],
+                grad_w2=g["grad_w2"], grad_b1=g.get("grad_b1"), grad_b2=g.get("grad_b2"),
+                grad_w_gate=r["grad_w_gate"], grad_b_gate=r["grad_b_gate"],
                 grad_logits_sel=r["grad_logits_sel"])
 
 
@@ -192,3 +195,50 @@ def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None =
     res.update(p)
     res.update(f)
     return res
+
+
+class MoELayerFn(torch.autograd.Function):
+    """The layer as a torch autograd function over the C-ABI calls:
+
+        out, losses = MoELayerFn.apply(x, w_gate, w1, w2, b_gate, b1, b2, sel_bias,
+                                       k, score, act, router_losses)
+
+    ``out`` [T,h] is the layer output; ``losses`` is the fp32 pair (load-
+    balancing loss, router z-loss) of "emerging-techniques-moe-training",
+    section 3 when ``router_losses`` is true (then the forward keeps the
+    router's logits), else zeros that carry no gradient. The backward runs
+    ``backward`` with the upstream gradients of ``losses`` as the loss
+    coefficients (read on the host, one synchronisation, only when they
+    matter). Optional tensors may be None; ``sel_bias`` (the selection bias)
+    gets no gradient. Routed experts only (no shared expert). Weight and bias
+    gradients are computed in fp32 and returned in their parameters'
+    dtype."""
+
+    @staticmethod
+    def forward(ctx, x, w_gate, w1, w2, b_gate, b1, b2, sel_bias, k: int, score: str, act: str,
+                router_losses: bool = False):
+        inp = dict(x=x.contiguous(), w_gate=w_gate, w1=w1, w2=w2, b_gate=b_gate, b1=b1, b2=b2,
+                   sel_bias=sel_bias, w1_sh=None, w2_sh=None)
+        f = forward(inp, k, score, act, keep_for_backward=True, router_losses=router_losses)
+        ctx.inp, ctx.fwd, ctx.args, ctx.with_losses = inp, f, (k, score, act), router_losses
+        losses = f["losses"] if router_losses else torch.zeros(2, dtype=torch.float32, device=x.device)
+        if not router_losses:
+            ctx.mark_non_differentiable(losses)
+        return f["out"], losses
+
+    @staticmethod
+    def backward(ctx, grad_out, grad_losses):
+        inp, f = ctx.inp, ctx.fwd
+        coef_aux = coef_z = 0.0
+        if ctx.with_losses and grad_losses is not None:
+            coef_aux, coef_z = (float(v) for v in grad_losses.detach().cpu())
+        if grad_out is None:
+            grad_out = torch.zeros_like(f["out"])
+        g = backward(inp, f, grad_out.contiguous(), *ctx.args, coef_aux=coef_aux, coef_z=coef_z)
+
+        def cast(t, like):
+            return None if t is None or like is None else t.to(like.dtype)
+
+        return (g["grad_x"], cast(g["grad_w_gate"], inp["w_gate"]), cast(g["grad_w1"], inp["w1"]),
+                cast(g["grad_w2"], inp["w2"]), cast(g["grad_b_gate"], inp["b_gate"]),
+                cast(g["grad_b1"], inp["b1"]), cast(g["grad_b2"], inp["b2"]), None, None, None, None, None)

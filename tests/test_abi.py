@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_status_strings(lib):
     lib.moe_abi_version.restype = ctypes.c_int
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     lib.moe_status_string.restype = ctypes.c_char_p
     assert lib.moe_status_string(0) == b"ok"
     assert b"workspace" in lib.moe_status_string(3)
@@ -112,11 +112,11 @@ def _validation_cases():
     assert rc == 2 and b"static scratch" in L.moe_last_error()
     assert L.moe_permute_noalloc(dummy, 1, 16, 64, 8, 9, dummy, dummy, dummy, dummy, None, None) == 2
     assert L.moe_permute_noalloc(dummy, 1, 16, 64, 8, 2, None, dummy, dummy, dummy, None, None) == 1
-    # grouped ffn: F not a multiple of 64, gu with GELU, shared expert without weights
+    # grouped ffn: F not a multiple of 64, a bad activation, shared expert without weights
     rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 100, 4, dummy, 1, dummy, None, dummy, None, None, 0,
                            None, None, dummy, None, dummy, None, None, 0, None)
     assert rc == 2
-    rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 0, dummy, None, dummy, None, None, 0,
+    rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 7, dummy, None, dummy, None, None, 0,
                            None, None, dummy, dummy, dummy, None, None, 0, None)
     assert rc == 1
     rc = L.moe_grouped_ffn(dummy, None, 0, 1, 64, 128, 128, 4, dummy, 1, dummy, None, dummy, None, dummy, 16,
@@ -159,6 +159,13 @@ def _validation_cases():
     rc = L.moe_grouped_ffn_bwd_recompute(dummy, dummy, dummy, 1, 64, 128, 128, 4, dummy, 1, dummy, dummy, dummy,
                                          dummy, dummy, dummy, dummy, None, dummy, 1 << 30, None)
     assert rc == 1
+    # expert backward: a bad activation; the recompute variant is bf16 SwiGLU only
+    rc = L.moe_grouped_ffn_bwd(dummy, dummy, dummy, dummy, 1, 64, 128, 128, 4, dummy, 5, dummy, dummy, dummy,
+                               dummy, dummy, dummy, None, None, None)
+    assert rc == 1
+    rc = L.moe_grouped_ffn_bwd_recompute(dummy, dummy, dummy, 0, 64, 128, 128, 4, dummy, 0, dummy, dummy, None,
+                                         dummy, dummy, dummy, dummy, None, dummy, 1 << 30, None)
+    assert rc == 2
     assert L.moe_permute_weights(dummy, -1, 2, dummy, dummy, None) == 1
     assert L.moe_permute_weights_bwd(None, 16, 2, dummy, dummy, None) == 1
     # unweighted combine backward still needs its output

@@ -88,6 +88,10 @@ template <typename TIn> struct Piece;
 template <> struct Piece<bf16_t> {
     u32x4 v;
     __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const u32x4 *>(p); }
+    // through a buffer resource: per-lane byte offset, uniform byte offset
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+        v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    }
     __device__ __forceinline__ float at(int s) const {
         const uint32_t w = v[s >> 1];
         return (s & 1) ? bf16hi(w) : bf16lo(w);
@@ -98,6 +102,10 @@ template <> struct Piece<float> {
     __device__ __forceinline__ void load(const float *p) {
         a = *reinterpret_cast<const u32x4 *>(p);
         b = *reinterpret_cast<const u32x4 *>(p + 4);
+    }
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+        a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        b = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, 0);
     }
     __device__ __forceinline__ float at(int s) const {
         return __uint_as_float(s < 4 ? a[s] : b[s - 4]);
@@ -165,85 +173,16 @@ __device__ __forceinline__ void gate_item(const TIn *__restrict__ xrow, const TI
     }
 }
 
-// gate_item with the gate matrix in LDS: U chunks of x are loaded before
-// use (the only global loads), the gate pieces are read from LDS at their
-// point of use. Same fma order as gate_item.
-template <typename TIn, int EPG, int U>
-__device__ __forceinline__ void gate_item_lds(const TIn *__restrict__ xrow, const TIn *wl, int h, int E, int e0,
-                                              int q, float (*acc)[8]) {
-#pragma unroll
-    for (int ee = 0; ee < EPG; ++ee)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) acc[ee][s] = 0.0f;
-    int woff[EPG];
-#pragma unroll
-    for (int ee = 0; ee < EPG; ++ee) {
-        const int e = e0 + ee < E ? e0 + ee : E - 1;
-        woff[ee] = e * h + 8 * q;
-    }
-    const int nchunk = h >> 6;
-    for (int c = 0; c < nchunk; c += U) {
-        Piece<TIn> xp[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (c + u < nchunk) xp[u].load(xrow + 64 * (c + u));
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (c + u < nchunk) {
-#pragma unroll
-                for (int ee = 0; ee < EPG; ++ee) {
-                    Piece<TIn> wp;
-                    wp.load(wl + woff[ee] + 64 * (c + u));
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) acc[ee][s] = fmaf(xp[u].at(s), wp.at(s), acc[ee][s]);
-                }
-            }
-        }
-    }
-}
-
 // Work items of a block: (token tt in [0,8), expert group eg); lane group lg
 // of the block (32 per block, 8 per wave) takes items lg, lg + 32, ...
-// WLDS (few experts, E*h*sizeof(TIn) <= 64 KB): the block first copies the
-// whole gate matrix into LDS (dynamic shared memory) and the items read their
-// gate rows from there; with EPG = ceil(E/4) the 32 items of a block cover 8
-// tokens, so each token row of x is read from memory ceil(E/EPG) <= 4 times
-// instead of E times. MAXE bounds E (LDS arrays).
-template <typename TIn, int EPG, int U, bool WLDS = false, int MAXE = kMaxE>
+template <typename TIn, int EPG, int U>
 __global__ __launch_bounds__(256) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wg, const float *__restrict__ bg,
     const float *__restrict__ sel_bias, int T, int h, int E, int k, int sigmoid,
     float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-    uint8_t *__restrict__ rmap, int32_t *__restrict__ counts) {
-    __shared__ float s_logit[kTokPerBlock][MAXE];
-    __shared__ float s_key[kTokPerBlock][MAXE];
-    __shared__ int s_cnt[MAXE];
-    extern __shared__ __attribute__((aligned(16))) unsigned char s_wdyn[];
-    // few experts (MAXE <= 16): the block's counts go to `counts` with one
-    // atomic per expert at the end; otherwise count_kernel runs afterwards
-    constexpr bool kCountHere = MAXE <= 16;
-    if (kCountHere)
-        for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
-
-    if (WLDS) {
-        // 16 pieces of 16 bytes per thread in flight at once (64 KB per pass)
-        const int n16 = static_cast<int>(static_cast<int64_t>(E) * h * sizeof(TIn) / 16);
-        for (int base = 0; base < n16; base += 16 * 256) {
-            u32x4 tmp[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int i = base + u * 256 + static_cast<int>(threadIdx.x);
-                if (i < n16) tmp[u] = reinterpret_cast<const u32x4 *>(wg)[i];
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int i = base + u * 256 + static_cast<int>(threadIdx.x);
-                if (i < n16) reinterpret_cast<u32x4 *>(s_wdyn)[i] = tmp[u];
-            }
-        }
-        __syncthreads();
-        wg = reinterpret_cast<const TIn *>(s_wdyn);
-    }
+    uint8_t *__restrict__ rmap) {
+    __shared__ float s_logit[kTokPerBlock][kMaxE];
+    __shared__ float s_key[kTokPerBlock][kMaxE];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -261,8 +200,7 @@ __global__ __launch_bounds__(256) void route_kernel(
         int t = t0 + tt;
         t = t < T ? t : T - 1;   // rows past T are read, never stored
         float acc[EPG][8];
-        if (WLDS) gate_item_lds<TIn, EPG, U>(x + static_cast<int64_t>(t) * h + 8 * q, wg, h, E, e0, q, acc);
-        else gate_item<TIn, EPG, U>(x + static_cast<int64_t>(t) * h + 8 * q, wg, h, E, e0, q, acc);
+        gate_item<TIn, EPG, U>(x + static_cast<int64_t>(t) * h + 8 * q, wg, h, E, e0, q, acc);
 #pragma unroll
         for (int ee = 0; ee < EPG; ++ee) {
             const float l = gate_tree(acc[ee]);
@@ -328,7 +266,6 @@ __global__ __launch_bounds__(256) void route_kernel(
                 if (j < k) {
                     topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
                     topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
-                    if (kCountHere && sel_e[j] >= 0 && sel_e[j] < E) atomicAdd(&s_cnt[sel_e[j]], 1);
                 }
             }
         }
@@ -342,13 +279,231 @@ __global__ __launch_bounds__(256) void route_kernel(
             }
         }
     }
-    if (kCountHere) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += blockDim.x)
-            if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
-    }
 }
 
+
+// Few experts (E <= 16, gate matrix <= 64 KB): one persistent block of 8
+// waves per compute unit.
+// - The block stages the gate matrix in LDS once, widened to fp32 (at most
+//   128 KB; rows padded by 16 bytes), so the inner loop converts only the
+//   token's values; blocks start
+//   their staging at different offsets, so that the compute units of an XCD
+//   do not all ask its L2 for the same lines at once.
+// - It takes a contiguous run of tokens in rounds of R = 64 / ngroups tokens:
+//   lane group lg (8 lanes) computes token lg / ngroups of the round against
+//   EPG experts (lg % ngroups + m ngroups), in the fixed order of gate_item (lane q: residues 8q..8q+7
+//   of every 64-chunk, fma chains over ascending chunks, then gate_tree).
+// - x is streamed in batches of kFewU chunks, one batch ahead (the first
+//   before the staging), with loads that take no branch, so that the
+//   compiler waits for each chunk as it is used rather than for every load
+//   in flight.
+// - After each round one thread per token takes its keys, top-k (insertion
+//   into a list kept in key order, experts in ascending order, so equal keys
+//   keep the lower index first), weights and outputs: no shuffles or
+//   barriers on that path; it adds the token's experts to the block's LDS
+//   histogram, which is added into `counts` (zeroed by the caller) with one
+//   atomic per expert when the block ends.
+constexpr int kFewU = 8;
+constexpr int kFewMaxR = 64;
+
+template <typename TIn, int EPG>
+__global__ __launch_bounds__(512) void route_few_kernel(
+    const TIn *__restrict__ x, const TIn *__restrict__ wg, const float *__restrict__ bg,
+    const float *__restrict__ sel_bias, int T, int h, int E, int k, int sigmoid, int tpb,
+    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    uint8_t *__restrict__ rmap, int32_t *__restrict__ counts) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_wdyn[];   // fp32 [E][h]
+    __shared__ float s_logit[kFewMaxR][17];
+    __shared__ float s_bg[16], s_sel[16];   // gate bias, selection bias (0 when absent)
+    __shared__ int s_cnt[16];               // the block's selections per expert
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 3, q = lane & 7;
+    const int lg = wave * 8 + g;              // lane group 0..63
+    const int ngroups = (E + EPG - 1) / EPG;
+    const int R = kFewMaxR / ngroups;         // tokens per round
+    // lane group lg: token tt of the round, experts eg, eg + ngroups, ...
+    // (the two lane groups of a 16-lane quarter then read neighbouring
+    // experts, whose padded LDS rows start 16 bytes apart in the banks)
+    const int tt = lg / ngroups, eg = lg % ngroups;
+    const bool item = tt < R;                 // lane groups past R * ngroups idle in the gate phase
+    const int t_begin = blockIdx.x * tpb;
+    const int t_end = min(T, t_begin + tpb);
+    const int nrounds = (t_end - t_begin + R - 1) / R;
+    const int nchunk = h >> 6;
+    // batches per token, rounded up to even (an extra batch past the row
+    // loads but computes nothing), so that the two register buffers keep
+    // fixed roles: even batches in xa, odd ones in xb
+    const int nb = ((nchunk + kFewU - 1) / kFewU + 1) & ~1;
+    const int total = nrounds * nb;
+
+    // batch i: kFewU chunks of a token row, without branches (chunks past
+    // the row re-read its last chunk; rows past the block's range re-read a
+    // valid row), through a buffer resource over x: one per-lane offset (the
+    // row and the lane's residues) and a uniform offset per chunk, so no
+    // 64-bit address registers are built per load
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, static_cast<uint32_t>(static_cast<int64_t>(T) * h * sizeof(TIn)));
+    auto load_batch = [&](Piece<TIn> (&xp)[kFewU], int i) {
+        int t = t_begin + (i / nb) * R + (item ? tt : 0);
+        t = min(t, T - 1);
+        const int c0 = __builtin_amdgcn_readfirstlane((i % nb) * kFewU);
+        const int voff = (t * h + 8 * q) * static_cast<int>(sizeof(TIn));
+#pragma unroll
+        for (int u = 0; u < kFewU; ++u)
+            xp[u].load_buf(rx, voff, 64 * min(c0 + u, nchunk - 1) * static_cast<int>(sizeof(TIn)));
+    };
+
+    Piece<TIn> xa[kFewU], xb[kFewU];
+    load_batch(xa, 0);
+
+    // the biases into LDS too: a global load in the round's epilogue would
+    // make the wave wait for every token batch loaded ahead of it
+    if (tid < E) {
+        s_bg[tid] = bg ? bg[tid] : 0.0f;
+        s_sel[tid] = sel_bias ? sel_bias[tid] : 0.0f;
+        s_cnt[tid] = 0;
+    }
+    // the gate matrix, widened to fp32, into LDS: 8 elements per thread and
+    // step, the block's starting piece rotated by its index
+    float *wl = reinterpret_cast<float *>(s_wdyn);
+    const int hp = h + 4;   // LDS row stride of the gate matrix (floats)
+    {
+        // all of a thread's pieces loaded before any is stored (one round
+        // trip; E h / 8 <= 4096 pieces, so at most 8 per thread)
+        const int n8 = E * h / 8;
+        const int rot = static_cast<int>((static_cast<int64_t>(blockIdx.x) * 97) % n8);
+        Piece<TIn> w[8];
+        int jj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            int j = min(tid + 512 * u, n8 - 1) + rot;
+            jj[u] = j >= n8 ? j - n8 : j;
+            w[u].load(wg + 8 * static_cast<int64_t>(jj[u]));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (tid + 512 * u < n8) {
+                float4 lo, hi;
+                lo.x = w[u].at(0); lo.y = w[u].at(1); lo.z = w[u].at(2); lo.w = w[u].at(3);
+                hi.x = w[u].at(4); hi.y = w[u].at(5); hi.z = w[u].at(6); hi.w = w[u].at(7);
+                const int e = (8 * jj[u]) / h, c = 8 * jj[u] - e * h;
+                *reinterpret_cast<float4 *>(wl + e * hp + c) = lo;
+                *reinterpret_cast<float4 *>(wl + e * hp + c + 4) = hi;
+            }
+        }
+    }
+    __syncthreads();
+    int woff[EPG];
+#pragma unroll
+    for (int ee = 0; ee < EPG; ++ee) woff[ee] = min(eg + ee * ngroups, E - 1) * hp + 8 * q;
+
+    float acc[EPG][8];
+    auto zero = [&]() {
+#pragma unroll
+        for (int ee = 0; ee < EPG; ++ee)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) acc[ee][s] = 0.0f;
+    };
+    // fma chains over the batch's chunks, ascending (the fixed order)
+    auto compute = [&](const Piece<TIn> (&xp)[kFewU], int i) {
+        const int c0 = (i % nb) * kFewU;
+#pragma unroll
+        for (int u = 0; u < kFewU; ++u) {
+            if (c0 + u < nchunk) {
+                float xv[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) xv[s] = xp[u].at(s);
+#pragma unroll
+                for (int ee = 0; ee < EPG; ++ee) {
+                    const float *wp = wl + woff[ee] + 64 * (c0 + u);
+                    const float4 lo = *reinterpret_cast<const float4 *>(wp);
+                    const float4 hi = *reinterpret_cast<const float4 *>(wp + 4);
+                    const float wv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) acc[ee][s] = fmaf(xv[s], wv[s], acc[ee][s]);
+                }
+            }
+        }
+    };
+    // end of a round: logits to LDS, then one thread per token selects
+    auto finish_round = [&](int r) {
+#pragma unroll
+        for (int ee = 0; ee < EPG; ++ee) {
+            const float l = gate_tree(acc[ee]);
+            const int e = eg + ee * ngroups;
+            if (item && q == 0 && e < E) s_logit[tt][e] = bg ? l + s_bg[e] : l;
+        }
+        __syncthreads();
+        const int t = t_begin + r * R + tid;
+        if (tid < R && t < t_end) {
+            // the k best (key, expert) so far, in selection order
+            float sk[8], sl[8];
+            int se[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { sk[j] = -INFINITY; sl[j] = 0.0f; se[j] = 0x7fffffff; }
+            for (int e = 0; e < E; ++e) {
+                const float l = s_logit[tid][e];
+                if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
+                float key = l;
+                if (sigmoid) {
+                    key = sigmoid_canonical(l);
+                    if (sel_bias) key = key + s_sel[e];
+                }
+                if (key != key) key = -INFINITY;
+                key = key + 0.0f;   // -0 -> +0
+                // insert (key, e) before the first entry it precedes; experts
+                // arrive in ascending order, so it never precedes an equal key
+#pragma unroll
+                for (int j = 7; j >= 0; --j) {
+                    if (j >= k) continue;
+                    const bool here = precedes(key, e, sk[j], se[j]) && (j == 0 || !precedes(key, e, sk[j - 1], se[j - 1]));
+                    const bool shift = j > 0 && precedes(key, e, sk[j - 1], se[j - 1]);
+                    if (shift) { sk[j] = sk[j - 1]; sl[j] = sl[j - 1]; se[j] = se[j - 1]; }
+                    else if (here) { sk[j] = key; sl[j] = l; se[j] = e; }
+                }
+            }
+            float wv[8];
+            route_weights(sl, k, sigmoid, wv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < k) {
+                    topk_idx[static_cast<int64_t>(t) * k + j] = se[j];
+                    topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
+                    atomicAdd(&s_cnt[se[j]], 1);
+                }
+            }
+            if (rmap) {
+                uint8_t *row = rmap + static_cast<int64_t>(t) * E;
+                for (int e = 0; e < E; ++e) {
+                    bool on = false;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) on |= (j < k) && (se[j] == e);
+                    row[e] = on ? 1 : 0;
+                }
+            }
+        }
+        __syncthreads();   // s_logit is rewritten by the next round
+    };
+
+    // Two buffers, one batch ahead. Every prefetch is issued, clamped to the
+    // last batch at the end, so that every path keeps the same loads in
+    // flight and the compiler waits for each batch only when it is used.
+    for (int r = 0; r < nrounds; ++r) {
+        zero();
+        for (int b = 0; b < nb; b += 2) {
+            const int i = r * nb + b;
+            load_batch(xb, min(i + 1, total - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xa, i);
+            load_batch(xa, min(i + 2, total - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xb, i + 1);
+        }
+        finish_round(r);
+    }
+    // finish_round ends with a barrier, so the histogram is complete
+    if (tid < E && s_cnt[tid]) atomicAdd(&counts[tid], s_cnt[tid]);
+}
 
 // Tokens per expert from topk_idx: a histogram in LDS per block of
 // kCountChunk entries, then (one block) the bins written directly or (more
@@ -693,8 +848,9 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
     const unsigned count_blocks = static_cast<unsigned>((npairs + kCountChunk - 1) / kCountChunk);
     const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
     const size_t wbytes = static_cast<size_t>(E) * static_cast<size_t>(h) * es;
-    const bool few = E <= 16 && wbytes <= 65536;   // route_kernel with the gate in LDS; counts in-kernel
-    if (T == 0 || few || count_blocks > 1) launch_fill<int32_t>(counts, E, 0, s);
+    // route_few_kernel: the gate in LDS, x through a buffer resource (32-bit offsets)
+    const bool few = E <= 16 && wbytes <= 65536 && T * h * static_cast<int64_t>(es) < (int64_t(1) << 31);
+    if (T == 0 || count_blocks > 1 || few) launch_fill<int32_t>(counts, E, 0, s);
     if (T == 0) return check_launch("moe_route fill");
     // the histogram of the selections, after whichever routing kernel ran
     auto count = [&](const char *what) {
@@ -729,45 +885,46 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
     const dim3 grid(static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock));
     const dim3 block(256);
     if (few) {
-        // few experts: the gate matrix lives in LDS, each token row is read
-        // ceil(E / EPG) times
-#define MOE_ROUTE_WLDS(TIN, EPG_, U_)                                                                   \
+        // few experts: persistent blocks, the gate matrix staged in LDS once
+        // per block (fp32); each lane group takes EPG = 2 experts of a token;
+        // the blocks add their histograms into the zeroed counts
+        const int ngroups = (E + 1) / 2;
+        const int R = kFewMaxR / ngroups;
+        int64_t G = (T + R - 1) / R;
+        if (G > num_cus()) G = num_cus();
+        const int tpb = static_cast<int>((T + G - 1) / G);
+        G = (T + tpb - 1) / tpb;
+        const size_t lds = static_cast<size_t>(E) * static_cast<size_t>(h + 4) * sizeof(float);
+#define MOE_ROUTE_FEW(TIN)                                                                              \
     do {                                                                                              \
-        auto kfn = &route_kernel<TIN, EPG_, U_, true, 16>;                                            \
+        auto kfn = &route_few_kernel<TIN, 2>;                                                         \
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),                                 \
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(wbytes)); \
-        hipLaunchKernelGGL(kfn, grid, block, wbytes, s, static_cast<const TIN *>(x),                  \
-                           static_cast<const TIN *>(w_gate), b_gate, sel_bias, TT, hh, E, k, sig, logits, \
-                           topk_idx, topk_w, routing_map, counts);                                    \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));   \
+        hipLaunchKernelGGL(kfn, dim3(static_cast<unsigned>(G)), dim3(512), lds, s,                    \
+                           static_cast<const TIN *>(x), static_cast<const TIN *>(w_gate), b_gate, sel_bias, \
+                           TT, hh, E, k, sig, tpb, logits, topk_idx, topk_w, routing_map, counts);    \
     } while (0)
-        if (dtype == MOE_DTYPE_BF16) {
-            if (E <= 4) MOE_ROUTE_WLDS(bf16_t, 1, 16);
-            else if (E <= 8) MOE_ROUTE_WLDS(bf16_t, 2, 16);
-            else MOE_ROUTE_WLDS(bf16_t, 4, 16);
-        } else {
-            if (E <= 4) MOE_ROUTE_WLDS(float, 1, 8);
-            else if (E <= 8) MOE_ROUTE_WLDS(float, 2, 8);
-            else MOE_ROUTE_WLDS(float, 4, 8);
-        }
-#undef MOE_ROUTE_WLDS
+        if (dtype == MOE_DTYPE_BF16) MOE_ROUTE_FEW(bf16_t);
+        else MOE_ROUTE_FEW(float);
+#undef MOE_ROUTE_FEW
         return check_launch("moe_route");
     }
     if (dtype == MOE_DTYPE_BF16) {
         const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
         if (E <= 16)
             hipLaunchKernelGGL((route_kernel<bf16_t, 1, 8>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
-                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map, counts);
+                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
         else
             hipLaunchKernelGGL((route_kernel<bf16_t, 8, 2>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
-                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map, counts);
+                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
     } else {
         const float *xp = static_cast<const float *>(x), *wp = static_cast<const float *>(w_gate);
         if (E <= 16)
             hipLaunchKernelGGL((route_kernel<float, 1, 4>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
-                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map, counts);
+                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
         else
             hipLaunchKernelGGL((route_kernel<float, 8, 1>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
-                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map, counts);
+                               hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
     }
     return count("moe_route");
 }

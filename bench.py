@@ -14,6 +14,15 @@ their roofline fractions (stages timed separately with HIP events after an
 eviction of the 256 MB last-level cache); and the CPU oracle timed on a
 bounded sample of the same workload.
 
+The default run (the Mixtral-shaped layer, no variant flags) adds one
+sub-record per other workload under "configs": the tiny fp32 GELU layer, the
+Qwen3-235B and DeepSeek-V3 inference layers, the imbalanced Qwen3 training
+step and the handbook training step, each timed over a few steps with its
+dominant call's MFMA fraction from HIP events and the oracle timed on a few
+of its tokens. The GPU clock is sampled while the headline step is repeated
+for about three seconds after the timed steps (the driver's metrics table
+refreshes about once a second, too slowly for the timed steps alone).
+
 ``--copy-calibration`` runs only a plain elementwise copy of 1 GiB (fp32
 negation, 1 GiB read and 1 GiB written per launch): the HBM byte counters
 read for it give the scale factor applied to the counters of the GEMMs.
@@ -75,6 +84,13 @@ def parse():
                         "(1e-3) to a training step, and time their kernels as stages")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB elementwise copy (counter calibration)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the sub-records of the other workloads")
+    p.add_argument("--config-steps", type=int, default=5, help="timed steps per sub-record")
+    p.add_argument("--config-cpu-tokens", type=int, default=8,
+                   help="tokens of each sub-record's workload the oracle is timed on")
+    p.add_argument("--clock-seconds", type=float, default=3.0,
+                   help="length of the clock-sampling loop after the timed steps (0: none)")
     return p.parse_args()
 
 
@@ -176,7 +192,25 @@ class ClockSampler:
             return {"mhz_median": None, "samples": len(self.samples), "source": self.source,
                     "note": "no plausible reading (all below 500 MHz)" if self.samples else "no reading"}
         return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
-                "samples": int(v.size), "source": self.source}
+                "samples": int(v.size), "distinct_readings": int(np.unique(v).size),
+                "samples_below_500mhz": len(self.samples) - int(v.size), "source": self.source}
+
+
+def sample_clock(torch, step, seconds):
+    """Repeats step() for about `seconds` while the clock sampler runs; a
+    barrier every 20 steps keeps the queue short."""
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            step()
+            n += 1
+            if n % 20 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    out = clock.summary()
+    out["loop"] = "%d repeated steps over %.1f s after the timed steps" % (n, time.perf_counter() - t0)
+    return out
 
 
 def host_info():
@@ -303,6 +337,65 @@ def cpu_baseline(cfg, inp, n_tok):
                       % (n_tok, cfg.T)}
 
 
+SUB_CONFIGS = (1, 3, 4, 5, 6)
+
+
+def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu):
+    """One other workload's step: forward (plus backward for training
+    workloads), timed over `steps` steps after `warmup`, with the dominant
+    call's MFMA fraction from HIP events on its stream; the oracle's forward
+    on the first cpu_tokens tokens as its CPU baseline."""
+    cfg = wl.CONFIGS[cid]
+    inp = wl.make_inputs(cfg, device="cuda:0")
+    train = cfg.backward
+
+    def step(timers=None):
+        f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers)
+        if train:
+            layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers)
+        return f
+
+    for _ in range(warmup):
+        step()
+    timers = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timers)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    flops = cfg.active_flops_forward() + (cfg.active_flops_backward() if train else 0.0)
+    live = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
+            for name, pairs in timers.items()}
+    nmat = 3 if cfg.act == "swiglu" else 2
+    call_flops = {"grouped_ffn": ffn_flops(cfg), "grouped_ffn_bwd": 2.0 * cfg.P * nmat * 2.0 * cfg.h * cfg.F}
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    dom = max(live, key=lambda n: live[n])
+    rec = {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "tokens_per_s": cfg.T / dt,
+        "ms_per_step": dt * 1e3, "steps": steps, "warmup": warmup, "dtype": cfg.dtype,
+        "step": "forward + backward" if train else "forward",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.h, "experts": cfg.E,
+                   "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
+                   "shared_experts": cfg.n_shared},
+        "frac_of_peak": flops / dt / 1e12 / peak,
+        "dominant_call": {"call": dom, "ms": live[dom] * 1e3,
+                          "achieved_tflops": call_flops[dom] / live[dom] / 1e12, "peak_tflops": peak,
+                          "frac": call_flops[dom] / live[dom] / 1e12 / peak,
+                          "timing": "HIP events around the call on its stream, mean over the timed steps"},
+        "calls_ms": {n: v * 1e3 for n, v in live.items()},
+    }
+    if with_cpu:
+        try:
+            rec["cpu_baseline"] = cpu_baseline(cfg, inp, min(cpu_tokens, cfg.T))
+        except Exception as exc:
+            rec["cpu_baseline"] = {"error": repr(exc)}
+    del inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -361,12 +454,12 @@ def main():
         step()
     timers = {}
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            res = step(timers)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / args.steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step(timers)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    clock = sample_clock(torch, step, args.clock_seconds) if args.clock_seconds > 0 else None
     if args.expert_choice:
         counts = np.full(cfg.E, ec_cap)
     else:
@@ -411,7 +504,7 @@ def main():
         "saved_for_backward_bytes": int(sum(res[n].numel() * res[n].element_size()
                                             for n in ("x_perm", "gu", "act", "y", "row_w", "logits")
                                             if res.get(n) is not None)) if train else None,
-        "gpu_clock": clock.summary(),
+        "gpu_clock": clock,
     }
 
     # roofline of the dominant call, from the events inside the timed steps
@@ -528,7 +621,14 @@ def main():
                 ts.append(e0.elapsed_time(e1) * 1e-3)
             stages[name] = {"s_median": float(np.median(ts)), "s_min": float(np.min(ts))}
         sb = stage_bytes(cfg, cfg.P, es)
-        for name in ("route", "permute", "unpermute"):
+        hbm_stages = ("route", "permute", "unpermute") if train else ("route", "unpermute")
+        if not train:
+            # the inference permute moves index arrays only (the first GEMM
+            # gathers the token rows): launch latency, not a bandwidth figure
+            stages["permute"].update(latency_us=stages["permute"]["s_median"] * 1e6,
+                                     index_bytes=sb["permute"],
+                                     note="index-only (histogram scan and stable rank): latency-bound")
+        for name in hbm_stages:
             t = stages[name]["s_median"]
             stages[name]["gb_per_s"] = sb[name] / t / 1e9
             stages[name]["hbm_frac"] = sb[name] / t / 1e9 / PEAK_HBM_GBS
@@ -571,6 +671,16 @@ def main():
             out["cpu_baseline"].update(host_info())
         except Exception as exc:   # report, never hide, a failing baseline
             out["cpu_baseline"] = {"error": repr(exc)}
+    variant = (args.memory_efficient or args.capacity_factor is not None or args.expert_choice or args.mxfp8
+               or args.router_losses)
+    if args.config == 2 and not variant and not args.no_configs:
+        del inp, res
+        torch.cuda.empty_cache()
+        out["configs"] = {}
+        for cid in SUB_CONFIGS:
+            print("sub-record %s" % wl.CONFIGS[cid].name, file=sys.stderr, flush=True)
+            out["configs"][wl.CONFIGS[cid].name] = sub_record(
+                torch, layer, wl, cid, args.config_steps, 2, args.config_cpu_tokens, not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 

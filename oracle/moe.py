@@ -64,6 +64,19 @@ Definitions followed (page titles are the pages' own):
   page does not say how a block's scale is chosen: the shared exponent is
   floor(log2(max |v|)) - 8, so the largest element lands in [256, 512) and
   is rounded to nearest-even on the E4M3 grid with saturation at 448.
+  Training in MXFP8 (same page, sections 5.1 and 5.3.3; 5.4 for the
+  alignment to 32): the pages say only that the expert GEMMs run in low
+  precision while the router keeps fp32. The reading taken: every expert
+  GEMM, forward and backward, takes both operands in MXFP8 with the 1 x 32
+  blocks along that GEMM's own reduction axis. The input gradients then use
+  dY blocked along h against W2 blocked along h (column-wise), and the
+  gradient of the pre-activations blocked along 2F against W1 blocked along
+  2F; the weight gradients reduce over an expert's tokens, so both of their
+  operands are blocked along the tokens, each expert's segment on its own
+  from its first row, its last block padded with zero rows (the pages pad
+  the routing map to a multiple of 32 rather than the tokens; zero rows are
+  that padding). The SwiGLU backward itself runs in fp64 on the forward's
+  exact pre-activations.
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, invariants, brute force and finite differences; the
@@ -506,6 +519,117 @@ def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, 
                    act_codes=np.concatenate([a_[1] for a_ in acts]) if acts else np.zeros((0, F), np.uint8),
                    act_scales=np.concatenate([a_[2] for a_ in acts]) if acts else np.zeros((0, F // 32), np.uint8))
     return res
+
+
+def mx_roundtrip_axis0(v, starts=None):
+    """v [n, c] quantised to MXFP8 along axis 0 and back: blocks of 32
+    consecutive rows of one column share a scale. With ``starts`` (ascending
+    segment boundaries s_0 = 0 < ... < s_m = n, empty segments allowed), each
+    segment [s_i, s_{i+1}) is blocked on its own from its first row and its
+    last block is completed with zero rows, which set no scale and are not
+    returned."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    bounds = [0, n] if starts is None else [int(b) for b in starts]
+    out = np.zeros_like(v)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        m = hi - lo
+        if m <= 0:
+            continue
+        mp = -(-m // 32) * 32
+        pad = np.zeros((mp,) + v.shape[1:], dtype=np.float64)
+        pad[:m] = v[lo:hi]
+        out[lo:hi] = mx_roundtrip(pad.T).T[:m]
+    return out
+
+
+def expert_backward_mxfp8(xe, w1e, w2e, act, dy, quantise=True):
+    """Gradients of one expert with its GEMMs in MXFP8 (reading above), fp64
+    on dequantised operands. xe [m,h]: the expert's token rows in segment
+    order (tokens ascending); dy [m,h]: the gradient of its weighted outputs
+    in the same order. The forward's pre-activations are those of
+    ``forward_mxfp8`` (x and W1 blocked along h). SwiGLU or GELU, no biases.
+
+      dhid = Q_h(dy) Q_h(W2)                 (reduction over h)
+      da   = activation backward of dhid at the forward's pre-activations
+      dx   = Q_2F(da) Q_2F(W1)               (reduction over 2F, or F)
+      dW2  = Q_tok(dy)^T Q_tok(hid)          (reduction over the tokens)
+      dW1  = Q_tok(da)^T Q_tok(x)
+
+    With quantise=False every Q is the identity: the result is then the
+    plain fp64 backward of the same expert (``expert_backward``) evaluated at
+    the MXFP8 forward's pre-activations."""
+    xe = np.asarray(xe, dtype=np.float64)
+    w1e = np.asarray(w1e, dtype=np.float64)
+    w2e = np.asarray(w2e, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    rows = mx_roundtrip if quantise else (lambda v: np.asarray(v, dtype=np.float64))
+    cols = mx_roundtrip_axis0 if quantise else (lambda v: np.asarray(v, dtype=np.float64))
+    F = w2e.shape[1]
+    a = mx_roundtrip(xe) @ mx_roundtrip(w1e).T          # the forward's pre-activations (always MXFP8)
+    if act == "swiglu":
+        g, u = a[:, :F], a[:, F:]
+        hid = silu(g) * u
+    else:
+        hid = gelu_erf(a)
+    dhid = rows(dy) @ cols(w2e)                         # [m,F]
+    if act == "swiglu":
+        da = np.concatenate([dhid * u * _dsilu(g), dhid * silu(g)], axis=1)
+    else:
+        da = dhid * _dgelu(a)
+    dx = rows(da) @ cols(w1e)                           # [m,h]
+    dw2 = cols(dy).T @ cols(hid)                        # [h,F]
+    dw1 = cols(da).T @ cols(xe)                         # [n1F,h]
+    return dict(dx=dx, dw1=dw1, dw2=dw2, dgu=da, hid=hid, a=a)
+
+
+def backward_mxfp8(x, w_gate, w1, w2, k, score, act, grad_out, b_gate=None, sel_bias=None,
+                   routing=None, experts=None):
+    """``backward`` for the layer whose expert GEMMs run in MXFP8: the
+    routing-weight gradients use the MXFP8 forward's expert outputs, the
+    expert gradients ``expert_backward_mxfp8`` (each expert over all of its
+    tokens, ascending), the router's gradients stay as in ``backward``.
+    dw1/dw2 are keyed by expert (all, or those in ``experts``)."""
+    x = np.asarray(x, dtype=np.float32)
+    T, h = x.shape
+    E = w1.shape[0]
+    if routing is None:
+        routing = route(x, w_gate, k, score, b_gate, sel_bias)
+    topk_idx, topk_w = routing["topk_idx"], routing["topk_w"]
+    G = np.asarray(grad_out, dtype=np.float64)
+    x64 = x.astype(np.float64)
+    want = set(range(E)) if experts is None else set(int(e) for e in experts)
+    dx = np.zeros((T, h), dtype=np.float64)
+    d_topk_w = np.zeros((T, k), dtype=np.float64)
+    dw1, dw2 = {}, {}
+    for e in range(E):
+        tok, slot = np.nonzero(topk_idx == e)
+        if tok.size == 0:
+            if e in want:
+                dw1[e] = np.zeros((w1.shape[1], h))
+                dw2[e] = np.zeros((h, w2.shape[2]))
+            continue
+        order = np.argsort(tok, kind="stable")
+        tok, slot = tok[order], slot[order]
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        dy = topk_w[tok, slot][:, None] * G[tok]
+        gb = expert_backward_mxfp8(x64[tok], w1e, w2e, act, dy)
+        # the forward's expert outputs: activation quantised along F
+        y = mx_roundtrip(gb["hid"]) @ mx_roundtrip(w2e).T
+        d_topk_w[tok, slot] = (G[tok] * y).sum(axis=1)
+        np.add.at(dx, tok, gb["dx"])
+        if e in want:
+            dw1[e] = gb["dw1"]
+            dw2[e] = gb["dw2"]
+    logits_sel = np.take_along_axis(routing["logits"], topk_idx.astype(np.int64), axis=1)
+    dl = router_backward_dlogits(topk_w, d_topk_w, score, logits_sel)
+    dlogits = np.zeros((T, E), dtype=np.float64)
+    np.put_along_axis(dlogits, topk_idx.astype(np.int64), dl, axis=1)
+    rg = router_grads(x64, w_gate, dlogits)
+    dx += rg["dx"]
+    return dict(dx=dx, d_topk_w=d_topk_w, d_logits_sel=dl, dw_gate=rg["dw_gate"], db_gate=rg["db_gate"],
+                dw1=dw1, dw2=dw2)
 
 
 def expert_choice(logits, capacity: int):

@@ -391,17 +391,15 @@ def e4m3_round(y):
     """Round float64 values to the E4M3 grid, nearest with ties to the even
     mantissa, magnitudes above 448 saturated to 448 (fp64 arithmetic on the
     grid's definition: 3 mantissa bits, exponent bias 7, subnormal step
-    2^-9, no infinities)."""
+    2^-9, no infinities). With |y| = m 2^E, m in [0.5, 1), the grid step at
+    |y| is 2^(E-4) in the normal range and 2^-9 below 2^-6, i.e. 2^max(E-4, -9);
+    scaling by powers of two is exact, so the only rounding is np.rint's
+    (half to even)."""
     y = np.asarray(y, dtype=np.float64)
     a = np.abs(y)
-    out = np.zeros_like(a)
-    sub = a < E4M3_MIN_NORMAL
-    out[sub] = np.round(a[sub] / E4M3_SUB_STEP) * E4M3_SUB_STEP      # np.round: ties to even
-    nrm = ~sub
-    e = np.floor(np.log2(np.where(nrm, a, 1.0)))
-    step = 2.0 ** (e - 3)
-    out[nrm] = (np.round(a / step) * step)[nrm]
-    out = np.minimum(out, E4M3_MAX)
+    _, E = np.frexp(a)
+    s = np.maximum(E - 4, -9)
+    out = np.minimum(np.ldexp(np.rint(np.ldexp(a, -s)), s), E4M3_MAX)
     return np.copysign(out, y)
 
 
@@ -409,13 +407,9 @@ def e4m3_encode(v):
     """Bit codes (uint8) of values already on the E4M3 grid."""
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
-    code = np.zeros(a.shape, dtype=np.int64)
+    m, E = np.frexp(a)                      # a = m 2^E; normal values: exponent E - 1, mantissa 16 m - 8
     sub = a < E4M3_MIN_NORMAL
-    code[sub] = np.rint(a[sub] / E4M3_SUB_STEP).astype(np.int64)
-    nrm = ~sub & (a > 0)
-    e = np.floor(np.log2(np.where(nrm, a, 1.0))).astype(np.int64)
-    m = np.rint(a / 2.0 ** e * 8 - 8).astype(np.int64)
-    code[nrm] = ((e + 7) * 8 + m)[nrm]
+    code = np.where(sub, np.rint(a / E4M3_SUB_STEP), (E - 1 + 7) * 8 + np.rint(m * 16 - 8)).astype(np.int64)
     code |= np.where(np.signbit(v), 0x80, 0)
     return code.astype(np.uint8)
 
@@ -432,6 +426,14 @@ def e4m3_decode(code):
     return s * val
 
 
+def _mx_block_exponent(amax):
+    """Shared exponent of blocks with largest magnitude amax: floor(log2
+    amax) - 8 (= frexp exponent - 9), clamped to [-127, 127]; -127 for an
+    all-zero block."""
+    _, E = np.frexp(amax)
+    return np.where(amax > 0, np.clip(E - 1 - E4M3_EMAX, -127, 127), -127)
+
+
 def mx_quantize(v):
     """MXFP8 quantisation along the last axis ("Scalable Training of
     Mixture-of-Experts Models with Megatron Core", section 5.3.3: 1 x 32
@@ -446,10 +448,8 @@ def mx_quantize(v):
     if K % 32:
         raise ValueError("K must be a multiple of 32")
     blk = v.reshape(v.shape[:-1] + (K // 32, 32))
-    amax = np.abs(blk).max(axis=-1)
-    exp = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, -127)
-    exp = np.clip(exp, -127, 127)
-    q = e4m3_round(blk / 2.0 ** exp[..., None])
+    exp = _mx_block_exponent(np.abs(blk).max(axis=-1))
+    q = e4m3_round(np.ldexp(blk, -exp[..., None]))
     codes = e4m3_encode(q).reshape(v.shape)
     return codes, (exp + 127).astype(np.uint8)
 
@@ -464,8 +464,16 @@ def mx_dequantize(codes, scales):
 
 
 def mx_roundtrip(v):
-    """v quantised to MXFP8 and back (float64)."""
-    return mx_dequantize(*mx_quantize(v))
+    """v quantised to MXFP8 along the last axis and back (float64): the
+    values mx_dequantize(*mx_quantize(v)) gives, without the bit codes
+    (each element e4m3_round(v 2^-exp) 2^exp with its block's exponent)."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    blk = v.reshape(v.shape[:-1] + (K // 32, 32))
+    exp = _mx_block_exponent(np.abs(blk).max(axis=-1))[..., None]
+    return np.ldexp(e4m3_round(np.ldexp(blk, -exp)), exp).reshape(v.shape)
 
 
 def forward_mxfp8(x, w_gate, w1, w2, k: int, score: str, act: str, b_gate=None, sel_bias=None,

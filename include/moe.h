@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -283,6 +283,54 @@ int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scales, const in
                        const uint8_t *w2_scales, void *act, uint8_t *act_codes,
                        uint8_t *act_scales, void *y, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* Training in MXFP8 ("Scalable Training of Mixture-of-Experts Models with
+ * Megatron Core": section 5.1 quantises the expert GEMMs and keeps the router
+ * in FP32; section 5.3.3 MXFP8; section 5.4 aligns to 32 by padding the
+ * routing map). Every expert GEMM takes both operands in MXFP8 blocked along
+ * its own reduction axis (moe_mx_quantize's rule per block of 32).
+ *
+ * moe_mx_quantize_t: src [batch,R,C] dtype, each matrix quantised along R
+ * (blocks of 32 consecutive rows of a column), stored transposed: codes
+ * [batch,C,R], scales [batch,C,R/32]. For the input gradients: w1 [E,2F,h]
+ * gives w1t [E,h,2F] (blocked along 2F), w2 [E,h,F] gives w2t [E,F,h]
+ * (blocked along h). Needs R % 32 == 0, codes 16-byte aligned.
+ *
+ * moe_grouped_ffn_bwd_mx: the backward of moe_grouped_ffn_mx (SwiGLU),
+ * recomputing the first projection (selective recomputation, in the pages'
+ * optimisation stack) so that every quantised operand is formed from fp32
+ * values rather than from bf16 copies:
+ *   grad_out [T,h] bf16   dL/d(layer output)
+ *   row_w [P] fp32        routing weight of each permuted row
+ *                         (moe_permute_weights); dY row p = row_w[p] *
+ *                         grad_out[sorted_token[p]] in fp32
+ *   x [T,h] bf16, x_codes/x_scales: the tokens and the forward's codes of
+ *                         them (along h); rows gathered by sorted_token [P]
+ *   w1_codes/w1_scales    the forward's codes of w1 (moe_mx_quantize)
+ *   w1t_*, w2t_*          moe_mx_quantize_t of w1 and w2
+ * Computes gu = Q_h(x) Q_h(W1) (fp32 accumulation), act = silu(g) u, dgu =
+ * the SwiGLU backward of Q_h(dY) Q_h(W2) at (g, u), and writes grad_x_perm
+ * [P,h] bf16 = Q_2F(dgu) Q_2F(W1), grad_w1 [E,2F,h] = Q_tok(dgu)^T Q_tok(x)
+ * and grad_w2 [E,h,F] = Q_tok(dY)^T Q_tok(act) in fp32, where Q_tok blocks
+ * each expert's tokens from its first row in blocks of 32, the last one
+ * completed with zero rows (an expert without tokens gets zero weight
+ * gradients). fp32 accumulation, deterministic. The routing-weight gradient
+ * comes from moe_unpermute_bwd on the forward's y. Needs h % 128 == 0,
+ * F % 128 == 0, E <= 256, a workspace of
+ * moe_grouped_ffn_bwd_mx_workspace_size(P,h,F,E) bytes (MOE_ERR_WORKSPACE
+ * otherwise), tensor, code and workspace pointers 16-byte aligned, scale
+ * pointers 4-byte aligned. */
+int moe_mx_quantize_t(const void *src, int dtype, int64_t batch, int64_t R, int64_t C,
+                      uint8_t *codes, uint8_t *scales, void *stream);
+size_t moe_grouped_ffn_bwd_mx_workspace_size(int64_t P, int64_t h, int64_t F, int E);
+int moe_grouped_ffn_bwd_mx(const void *grad_out, const float *row_w, const void *x,
+                           const uint8_t *x_codes, const uint8_t *x_scales,
+                           const int32_t *sorted_token, int64_t T, int64_t P, int64_t h, int64_t F,
+                           int E, const int32_t *offsets, int act_kind, const uint8_t *w1_codes,
+                           const uint8_t *w1_scales, const uint8_t *w1t_codes,
+                           const uint8_t *w1t_scales, const uint8_t *w2t_codes,
+                           const uint8_t *w2t_scales, void *grad_x_perm, float *grad_w1,
+                           float *grad_w2, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------- Routing variants
  * "emerging-techniques-moe-training".

@@ -68,6 +68,10 @@ _SIGS = {
     "moe_grouped_ffn_mx_workspace_size": ([_i64, _i64, _i64, _int], _sz),
     "moe_grouped_ffn_mx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "moe_mx_quantize_t": ([_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp], _int),
+    "moe_grouped_ffn_bwd_mx_workspace_size": ([_i64, _i64, _i64, _int], _sz),
+    "moe_grouped_ffn_bwd_mx": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_expert_choice": ([_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "moe_combine_rows": ([_vp, _int, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp], _int),
     "moe_grouped_ffn_bwd_recompute": ([_vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp,
@@ -626,4 +630,67 @@ def moe_grouped_ffn_mx(x_codes, x_scales, offsets, w1_codes, w1_scales, w2_codes
                                   _ptr(w2_scales), _ptr(out["act"]), _ptr(out["act_codes"]),
                                   _ptr(out["act_scales"]), _ptr(out["y"]), _ptr(ws), nws, _stream(x_codes))
     _check(rc, "moe_grouped_ffn_mx")
+    return out
+
+
+def moe_mx_quantize_t(src):
+    """(codes uint8 [B, C, R], scales uint8 [B, C, R/32]) of src [B, R, C]
+    (bf16/fp32): each matrix quantised along R (its columns) and stored
+    transposed."""
+    _req(src, "src")
+    if src.dim() != 3:
+        raise MoeError("moe_mx_quantize_t: src must be [B, R, C]")
+    Bn, R, C = src.shape
+    dev = src.device
+    codes = torch.empty((Bn, C, R), dtype=torch.uint8, device=dev)
+    scales = torch.empty((Bn, C, R // 32), dtype=torch.uint8, device=dev)
+    rc = lib().moe_mx_quantize_t(_ptr(src), DTYPE[src.dtype], Bn, R, C, _ptr(codes), _ptr(scales), _stream(src))
+    _check(rc, "moe_mx_quantize_t")
+    return codes, scales
+
+
+def moe_grouped_ffn_bwd_mx(grad_out, row_w, x, x_codes, x_scales, sorted_token, offsets, w1_codes, w1_scales,
+                           w1t_codes, w1t_scales, w2t_codes, w2t_scales, act: str = "swiglu", workspace=None):
+    """Expert gradients with every GEMM in MXFP8 (the first projection
+    recomputed from the forward's codes): grad_x_perm [P, h] bf16, grad_w1
+    [E, 2F, h] and grad_w2 [E, h, F] fp32. grad_out [T, h] and x [T, h]
+    unpermuted (rows gathered by sorted_token), row_w [P] the routing weight
+    of each permuted row. ``workspace``: a uint8 device tensor of at least
+    moe_grouped_ffn_bwd_mx_workspace_size bytes to use (else one is
+    allocated)."""
+    _req(grad_out, "grad_out", dtype=torch.bfloat16)
+    dev = grad_out.device
+    T, h = grad_out.shape
+    P = sorted_token.numel()
+    E, F2, _ = w1_codes.shape
+    F = F2 // 2
+    _req(row_w, "row_w", dtype=torch.float32, shape=(P,), device=dev)
+    _req(x, "x", dtype=torch.bfloat16, shape=(T, h), device=dev)
+    _req(x_codes, "x_codes", dtype=torch.uint8, shape=(T, h), device=dev)
+    _req(x_scales, "x_scales", dtype=torch.uint8, shape=(T, h // 32), device=dev)
+    _req(sorted_token, "sorted_token", dtype=torch.int32, shape=(P,), device=dev)
+    _req(offsets, "offsets", dtype=torch.int32, shape=(E + 1,), device=dev)
+    _req(w1_codes, "w1_codes", dtype=torch.uint8, shape=(E, 2 * F, h), device=dev)
+    _req(w1_scales, "w1_scales", dtype=torch.uint8, shape=(E, 2 * F, h // 32), device=dev)
+    _req(w1t_codes, "w1t_codes", dtype=torch.uint8, shape=(E, h, 2 * F), device=dev)
+    _req(w1t_scales, "w1t_scales", dtype=torch.uint8, shape=(E, h, 2 * F // 32), device=dev)
+    _req(w2t_codes, "w2t_codes", dtype=torch.uint8, shape=(E, F, h), device=dev)
+    _req(w2t_scales, "w2t_scales", dtype=torch.uint8, shape=(E, F, h // 32), device=dev)
+    out = dict(grad_x_perm=torch.empty((P, h), dtype=torch.bfloat16, device=dev),
+               grad_w1=torch.empty((E, 2 * F, h), dtype=torch.float32, device=dev),
+               grad_w2=torch.empty((E, h, F), dtype=torch.float32, device=dev))
+    nws = lib().moe_grouped_ffn_bwd_mx_workspace_size(P, h, F, E)
+    if workspace is None:
+        ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    else:
+        _req(workspace, "workspace", dtype=torch.uint8, device=dev)
+        if workspace.numel() < nws:
+            raise MoeError("moe_grouped_ffn_bwd_mx: workspace smaller than %d bytes" % nws)
+        ws, nws = workspace, workspace.numel()
+    rc = lib().moe_grouped_ffn_bwd_mx(_ptr(grad_out), _ptr(row_w), _ptr(x), _ptr(x_codes), _ptr(x_scales),
+                                      _ptr(sorted_token), T, P, h, F, E, _ptr(offsets), ACT[act], _ptr(w1_codes),
+                                      _ptr(w1_scales), _ptr(w1t_codes), _ptr(w1t_scales), _ptr(w2t_codes),
+                                      _ptr(w2t_scales), _ptr(out["grad_x_perm"]), _ptr(out["grad_w1"]),
+                                      _ptr(out["grad_w2"]), _ptr(ws), nws, _stream(grad_out))
+    _check(rc, "moe_grouped_ffn_bwd_mx")
     return out

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["status.hip", "route.hip", "permute.hip", "combine.hip", "ffn.hip", "ffn_bwd.hip", "backward.hip",
-           "losses.hip", "variants.hip", "ffn_mx.hip", "ffn_bwd_generic.hip"]
+           "losses.hip", "variants.hip", "ffn_mx.hip", "ffn_mx_bwd.hip", "ffn_bwd_generic.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -229,9 +229,24 @@ __device__ __forceinline__ void gemm_tile(const GGArgs &a, const TileInfo &ti, b
     MOE_WR(LB0, 0);
     MOE_WR(LB0, 1);
     {
+        // issued one by one in the loop's order: the wait counter counts
+        // loads in issue order, and the loop's waits are derived from the
+        // order these arrive in at its first iteration (any other order here
+        // makes every iteration wait for loads issued a quarter earlier)
         const int k1 = nk > 1 ? 1 : 0;
-        MOE_LD(k1, 0);
-        MOE_LD(k1, 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 4 * h; j < 4 * h + 4; ++j) {
+                RW[j] = __builtin_amdgcn_raw_buffer_load_b128((j & 1) ? rwu : rwg, wv[j], (k0 + k1) * kBK * 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = (XJ / 2) * h; j < (XJ / 2) * h + XJ / 2; ++j) {
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], (k0 + k1) * kBK * 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
     MOE_LDS_BARRIER();
     MOE_RD(fa0, fb0, LB0, 0);

@@ -31,79 +31,11 @@
 //   Tokens enter quantised along h, optionally gathered.
 #include <type_traits>
 
-#include "gemm_common.hpp"
+#include "mx_common.hpp"
 
 namespace moe {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-
-// ------------------------------------------------------------ quantise
-
-// E4M3 code of |y| < 2^9 given as fp32 (exact scaled value), sign apart.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const uint32_t s = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (a >= 448.0f) return s | 0x7eu;                       // saturate (all of [448, 512) rounds to 448)
-    if (a < 0.015625f) return s | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // subnormals; 8 = 2^-6
-    const uint32_t b = __float_as_uint(a);
-    int e = static_cast<int>(b >> 23) - 127;                 // -6 .. 8
-    const uint32_t mant = b & 0x7fffffu;
-    uint32_t m = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, nearest-even
-    if (m == 8) {
-        m = 0;
-        ++e;
-    }
-    uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | m;
-    if (code > 0x7eu) code = 0x7eu;
-    return s | code;
-}
-
-// Shared exponent of a block whose largest magnitude is amax (>= 0):
-// floor(log2 amax) - 8 clamped to [-127, 127]; -127 for a zero block (fp32
-// subnormal maxima also land on -127, as floor(log2) - 8 < -127 for them).
-__device__ __forceinline__ int mx_block_exponent(float amax) {
-    if (!(amax > 0.0f)) return -127;
-    const int eb = static_cast<int>(__float_as_uint(amax) >> 23);
-    const int ex = eb == 0 ? -127 : eb - 127 - 8;
-    return ex < -127 ? -127 : ex;
-}
-
-// One thread per block of 32 values of a row.
-template <typename TE>
-__global__ __launch_bounds__(256) void mx_quantize_kernel(const TE *__restrict__ src, int64_t nblocks,
-                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (b >= nblocks) return;
-    float v[32];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) load8(src + b * 32 + 8 * c, v + 8 * c);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const int ex = mx_block_exponent(amax);
-    u32x4 out[2];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) word |= e4m3_code(ldexpf(v[4 * w + q], -ex)) << (8 * q);
-        out[w >> 2][w & 3] = word;
-    }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(codes + b * 32);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    scales[b] = static_cast<uint8_t>(ex + 127);
-}
-
-template <typename TE>
-void launch_quantize(const TE *src, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales, hipStream_t s) {
-    const int64_t nb = rows * (K / 32);
-    if (nb == 0) return;
-    hipLaunchKernelGGL(mx_quantize_kernel<TE>, dim3(static_cast<unsigned>((nb + 255) / 256)), dim3(256), 0, s, src,
-                       nb, codes, scales);
-}
 
 // --------------------------------------------------------------- GEMM
 
@@ -113,8 +45,7 @@ constexpr int kMxRegion = kMxTile * kMxBK;   // bytes of one operand region of a
 constexpr int kMxStage = 2 * kMxRegion;
 constexpr int kMxScaleBytes = 2 * kMxTile * 4;   // per stage: a scale word per weight row and per token row
 
-// byte offset of 16-byte chunk c of row r in a region
-__device__ __forceinline__ int mswz(int r, int c) { return r * kMxBK + ((c ^ ((r >> 1) & 7)) << 4); }
+static_assert(kMxBK == 128, "mswz assumes 128-byte rows");
 
 struct MXArgs {
     GGArgs g;              // A: weight codes [E][nb_rows][K]; tokens: g.A (codes, rows of the

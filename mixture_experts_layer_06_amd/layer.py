@@ -166,21 +166,28 @@ def backward(inp: dict, fwd: dict, grad_out, k: int, score: str, act: str,
                 grad_logits_sel=r["grad_logits_sel"])
 
 
-def quantize_experts_mx(inp: dict) -> dict:
+def quantize_experts_mx(inp: dict, for_backward: bool = False) -> dict:
     """MXFP8 codes and scales of the expert weights, each along its reduction
-    axis (done once, before inference)."""
+    axis (once per weight update): w1 and w2 along h and F for the forward;
+    with ``for_backward`` also along 2F and h, stored transposed (w1t
+    [E, h, 2F], w2t [E, F, h]) for the input gradients."""
     w1q, w1s = B.moe_mx_quantize(inp["w1"])
     w2q, w2s = B.moe_mx_quantize(inp["w2"])
-    return dict(w1_codes=w1q, w1_scales=w1s, w2_codes=w2q, w2_scales=w2s)
+    out = dict(w1_codes=w1q, w1_scales=w1s, w2_codes=w2q, w2_scales=w2s)
+    if for_backward:
+        out["w1t_codes"], out["w1t_scales"] = B.moe_mx_quantize_t(inp["w1"])
+        out["w2t_codes"], out["w2t_scales"] = B.moe_mx_quantize_t(inp["w2"])
+    return out
 
 
 def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None = None):
-    """Inference forward with the expert GEMMs in MXFP8 ("Scalable Training of
+    """Forward with the expert GEMMs in MXFP8 ("Scalable Training of
     Mixture-of-Experts Models with Megatron Core", section 5.3.3): the router
     as in ``forward`` (fp32 logits), the token rows quantised along h and
     gathered by the first GEMM, the activation quantised along F in the first
     GEMM's epilogue (from fp32), the weighted combine in fp32. SwiGLU experts
-    without bias."""
+    without bias. The result keeps the token codes (x_codes, x_scales) that
+    ``backward_mxfp8`` recomputes the first projection from."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
     r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias"))
@@ -190,11 +197,34 @@ def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None =
         xq, xs, p["offsets"], wq["w1_codes"], wq["w1_scales"], wq["w2_codes"], wq["w2_scales"],
         gather_rows=p["sorted_token"]))
     out = B.moe_unpermute(f["y"], p["row_of"], r["topk_w"])
-    res = dict(out=out)
+    res = dict(out=out, x_codes=xq, x_scales=xs)
     res.update(r)
     res.update(p)
     res.update(f)
     return res
+
+
+def backward_mxfp8(inp: dict, fwd: dict, wq: dict, grad_out, k: int, score: str, timers: dict | None = None):
+    """Gradients of sum(grad_out * out) for a ``forward_mxfp8`` run, the
+    expert GEMMs in MXFP8 (``wq`` from quantize_experts_mx(...,
+    for_backward=True); the first projection recomputed from the forward's
+    codes), the combine, dispatch and router backward as in ``backward``
+    (the router keeps fp32, section 5.1). With ``timers``, the expert
+    backward call is bracketed by HIP events (key "grouped_ffn_bwd")."""
+    E = inp["w_gate"].shape[0]
+    _, grad_w = B.moe_unpermute_bwd(grad_out, fwd["y"], fwd["row_of"], fwd["topk_w"])
+    row_w = B.moe_permute_weights(fwd["topk_w"], fwd["row_of"])
+    g = _timed(timers, "grouped_ffn_bwd", lambda: B.moe_grouped_ffn_bwd_mx(
+        grad_out, row_w, inp["x"], fwd["x_codes"], fwd["x_scales"], fwd["sorted_token"], fwd["offsets"],
+        wq["w1_codes"], wq["w1_scales"], wq["w1t_codes"], wq["w1t_scales"], wq["w2t_codes"], wq["w2t_scales"]))
+    r = B.moe_route_bwd(inp["x"], E, fwd["topk_idx"], fwd["topk_w"], grad_w, fwd["offsets"],
+                        fwd["sorted_token"], score=score, logits=fwd.get("logits"),
+                        want_b_grad=inp.get("b_gate") is not None)
+    grad_x = B.moe_permute_bwd(g["grad_x_perm"], fwd["row_of"], r["grad_logits_sel"], fwd["topk_idx"],
+                               inp["w_gate"])
+    return dict(grad_x=grad_x, grad_topk_w=grad_w, grad_x_perm=g["grad_x_perm"], grad_w1=g["grad_w1"],
+                grad_w2=g["grad_w2"], grad_w_gate=r["grad_w_gate"], grad_b_gate=r["grad_b_gate"],
+                grad_logits_sel=r["grad_logits_sel"])
 
 
 class MoELayerFn(torch.autograd.Function):

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_status_strings(lib):
     lib.moe_abi_version.restype = ctypes.c_int
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     lib.moe_status_string.restype = ctypes.c_char_p
     assert lib.moe_status_string(0) == b"ok"
     assert b"workspace" in lib.moe_status_string(3)
@@ -182,6 +182,20 @@ def _validation_cases():
     rc = L.moe_grouped_ffn_mx(dummy, dummy, None, 0, 64, 256, 256, 4, dummy, 1, dummy, dummy, dummy, dummy, dummy,
                               dummy, dummy, dummy, vp(4098), 1 << 20, None)
     assert rc == 1
+    # MXFP8 backward: R not a multiple of 32; F not a multiple of 128; GELU;
+    # no workspace; a workspace one byte short; a null token map
+    assert L.moe_mx_quantize_t(dummy, 1, 4, 48, 64, dummy, dummy, None) == 2
+    ws = L.moe_grouped_ffn_bwd_mx_workspace_size(64, 256, 256, 4)
+    # grad_out, row_w, x, x_codes, x_scales, sorted_token, T, P, h, F, E,
+    # offsets, act, w1 codes/scales, w1t, w2t, grad_x_perm, grad_w1, grad_w2
+    args = [dummy, dummy, dummy, dummy, dummy, dummy, 32, 64, 256, 256, 4, dummy, 1, dummy, dummy, dummy, dummy,
+            dummy, dummy, dummy, dummy, dummy]
+    with_ = lambda i, v: args[:i] + [v] + args[i + 1:]
+    assert L.moe_grouped_ffn_bwd_mx(*with_(9, 192), dummy, ws, None) == 2
+    assert L.moe_grouped_ffn_bwd_mx(*with_(12, 0), dummy, ws, None) == 2
+    assert L.moe_grouped_ffn_bwd_mx(*args, None, 0, None) == 3
+    assert L.moe_grouped_ffn_bwd_mx(*args, dummy, ws - 1, None) == 3
+    assert L.moe_grouped_ffn_bwd_mx(*with_(5, None), dummy, ws, None) == 1
     # routing variants: negative capacity, capacity above T, too small a workspace
     assert L.moe_capacity_drop(dummy, dummy, dummy, None, 1, 16, 64, 8, 2, -1, dummy, dummy, dummy, None, None) == 1
     assert L.moe_expert_choice(dummy, 16, 8, 17, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None) == 2
@@ -254,3 +268,19 @@ def test_binding_fails_loudly_without_library(tmp_path):
             binding.load(str(tmp_path / "absent.so"))
     finally:
         binding._lib = saved
+
+
+def test_mx_bwd_workspace_size(lib):
+    """Sub-buffers at 256-byte boundaries: padded offsets, the recomputed
+    pre-activations and activation (fp32), dY codes along h, dY and the
+    activation along the tokens (P + 127 E columns rounded up to 128), dact
+    and dgu in fp32, dgu codes along 2F and along the tokens, x along the
+    tokens (each code buffer followed by its scales, 1/32 of it)."""
+    P, h, F, E = 300, 256, 128, 4
+    Pc = ((P + 127 * E) + 127) // 128 * 128
+    r = lambda n: (n + 255) // 256 * 256
+    want = (r((E + 1) * 4) + r(P * 2 * F * 4) + r(P * F * 4) + r(P * h) + r(P * h // 32) + r(h * Pc) + r(h * Pc // 32) + r(F * Pc) + r(F * Pc // 32)
+            + r(P * F * 4) + r(P * 2 * F * 4) + r(P * 2 * F) + r(P * 2 * F // 32) + r(2 * F * Pc)
+            + r(2 * F * Pc // 32) + r(h * Pc) + r(h * Pc // 32))
+    assert lib.moe_grouped_ffn_bwd_mx_workspace_size(P, h, F, E) == want
+    assert lib.moe_grouped_ffn_bwd_mx_workspace_size(-1, h, F, E) == 0

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from mixture_experts_layer_06_amd import workloads as wl
-from parity import TOL, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
+from parity import TOL, mfma_gamma, oracle_inputs, rel_err, rel_err_tensor, to_device, to_np32
 
 pytestmark = pytest.mark.gpu
 
@@ -73,18 +73,6 @@ def test_quantize_weights_bit_exact(moe_lib):
     assert np.array_equal(scales[rows].cpu().numpy(), rs)
 
 
-def _mfma_gamma(K):
-    """Relative error bound (times sum |products|) of an fp32 dot product of
-    K exact products summed by the scaled fp8 MFMA. How one instruction adds
-    its 64 products is not specified (order, internal width, rounding or
-    truncation), so the bound is the classical one for any order: every
-    product added with its own error of at most 2u (u = 2^-24; truncation as
-    well as rounding), plus the K/64 accumulations into C and a margin of 8.
-    A tighter model, (K/64 + 8) roundings per element, was measured to be
-    exceeded by up to 3.75 times on the device."""
-    return (K + K / 64 + 8) * 2.0 ** -23
-
-
 def _check_act_codes(got_codes, got_scales, ref, o, perm, E, F):
     """Codes and scales of the activation against the oracle's, with every
     difference explained by the fp32 error bound (see the module docstring).
@@ -95,7 +83,7 @@ def _check_act_codes(got_codes, got_scales, ref, o, perm, E, F):
     multiplies. Returns (differing blocks, differing codes, blocks, codes)."""
     h = o["x"].shape[1]
     xq = oracle.mx_roundtrip(o["x"].astype(np.float64))
-    gam = _mfma_gamma(h)
+    gam = mfma_gamma(h)
     bound = np.zeros_like(ref["act"])
     for e in range(E):
         r0, r1 = int(perm["offsets"][e]), int(perm["offsets"][e + 1])

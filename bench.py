@@ -435,13 +435,19 @@ def main():
             sys.exit("--expert-choice runs the forward only; pick a forward workload")
         ec_cap = cfg.T * cfg.k // cfg.E
     if args.mxfp8:
-        if train or cfg.act != "swiglu" or cfg.n_shared or cfg.dtype != "bf16":
-            sys.exit("--mxfp8 runs the forward of bf16 SwiGLU layers without a shared expert")
-        wq = layer.quantize_experts_mx(inp)
+        if cfg.act != "swiglu" or cfg.n_shared or cfg.dtype != "bf16" or inp.get("b1") is not None:
+            sys.exit("--mxfp8 runs bf16 SwiGLU layers without expert biases or a shared expert")
+        if losses or meff or cap is not None or args.expert_choice:
+            sys.exit("--mxfp8 combines with no other variant flag")
+        # weights quantised once per weight update, outside the timed steps
+        wq = layer.quantize_experts_mx(inp, for_backward=train)
 
     def step(timers=None):
         if args.mxfp8:
-            return layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers)
+            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers)
+            if train:
+                layer.backward_mxfp8(inp, f, wq, inp["grad_out"], cfg.k, cfg.score, timers=timers)
+            return f
         if args.expert_choice:
             return layer.forward_expert_choice(inp, ec_cap, cfg.act, timers=timers)
         f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers,
@@ -526,6 +532,9 @@ def main():
     if args.mxfp8:
         kernels["grouped_ffn"] = ("grouped_gemm_mx SwiGLU launch with the activation quantised in its "
                                   "epilogue + grouped_gemm_mx plain launch (one moe_grouped_ffn_mx call)")
+        kernels["grouped_ffn_bwd"] = ("moe_grouped_ffn_bwd_mx call (first projection recomputed, five "
+                                      "mx_gemm_nt launches, quantisation and SwiGLU-backward passes); "
+                                      "algorithmic backward FLOPs only, the recomputation not credited")
     out["roofline"] = {
         "kernel": kernels[dom], "bound": "mfma",
         "achieved": call_flops[dom] / live[dom] / 1e12, "peak": peak, "unit": "TFLOP/s",

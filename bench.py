@@ -84,6 +84,9 @@ def parse():
                         "(1e-3) to a training step, and time their kernels as stages")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB elementwise copy (counter calibration)")
+    p.add_argument("--hipblaslt-reference", action="store_true",
+                   help="time only torch.matmul (hipBLASLt) on the dense shapes of the Mixtral-shaped "
+                        "layer's two projections, as a reference for the grouped GEMM")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the sub-records of the other workloads")
     p.add_argument("--config-steps", type=int, default=5, help="timed steps per sub-record")
@@ -264,6 +267,36 @@ def copy_calibration():
                                            "launches": 3}}), flush=True)
 
 
+def hipblaslt_reference(torch, reps=20):
+    """torch.matmul in bf16 (hipBLASLt) on the dense equivalents of the
+    Mixtral-shaped layer's two projections over all 8192 routed rows:
+    [8192, 4096] x [4096, 28672] and [8192, 14336] x [14336, 4096], best and
+    mean of `reps` HIP-event timings; the GPU clock sampled over a 3 s loop
+    of the first product."""
+    out = {}
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    for name, (M, K, N) in (("first projection", (8192, 4096, 28672)), ("second projection", (8192, 14336, 4096))):
+        a = torch.randn(M, K, device="cuda:0", generator=g).to(torch.bfloat16)
+        b = torch.randn(K, N, device="cuda:0", generator=g).to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        fl = 2.0 * M * K * N
+        out[name] = {"shape_mkn": [M, K, N], "tflops_best": fl / min(ts) / 1e12,
+                     "tflops_mean": fl / float(np.mean(ts)) / 1e12, "ms_mean": float(np.mean(ts)) * 1e3}
+        if name == "first projection":
+            out["gpu_clock"] = sample_clock(torch, lambda: torch.matmul(a, b), 3.0)
+        del a, b
+    return out
+
+
 def stage_bytes(cfg, P, es):
     """Algorithmic HBM bytes of the memory-bound stages (index traffic included).
     Inference permutes indices only (the first GEMM gathers rows); training
@@ -406,6 +439,9 @@ def main():
         copy_calibration()
         return
     import torch
+    if args.hipblaslt_reference:
+        print(json.dumps({"hipblaslt_reference": hipblaslt_reference(torch)}), flush=True)
+        return
     from mixture_experts_layer_06_amd import binding as B
     from mixture_experts_layer_06_amd import layer
     from mixture_experts_layer_06_amd import workloads as wl

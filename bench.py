@@ -84,6 +84,8 @@ def parse():
                         "(1e-3) to a training step, and time their kernels as stages")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB elementwise copy (counter calibration)")
+    p.add_argument("--graph-steps", type=int, default=20,
+                   help="also time this many replays of one step captured in a HIP graph (0: none)")
     p.add_argument("--hipblaslt-reference", action="store_true",
                    help="time only torch.matmul (hipBLASLt) on the dense shapes of the Mixtral-shaped "
                         "layer's two projections, as a reference for the grouped GEMM")
@@ -502,6 +504,28 @@ def main():
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     clock = sample_clock(torch, step, args.clock_seconds) if args.clock_seconds > 0 else None
+    graph_rec = None
+    if args.graph_steps > 0 and cap is None and not args.expert_choice:
+        # the same step captured once in a HIP graph and replayed: the C-ABI
+        # calls allocate nothing themselves and record no memset
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.graph_steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        dtg = (time.perf_counter() - tg) / args.graph_steps
+        graph_rec = {"ms_per_step": dtg * 1e3, "value": flops / dtg / 1e12, "steps": args.graph_steps,
+                     "note": "one captured step replayed; the headline value is the eager steps'"}
+        del graph
     if args.expert_choice:
         counts = np.full(cfg.E, ec_cap)
     else:
@@ -547,6 +571,7 @@ def main():
                                             for n in ("x_perm", "gu", "act", "y", "row_w", "logits")
                                             if res.get(n) is not None)) if train else None,
         "gpu_clock": clock,
+        "hip_graph": graph_rec,
     }
 
     # roofline of the dominant call, from the events inside the timed steps

@@ -41,6 +41,8 @@
 //  - k-segment mode (weight gradients): A [M][Pc] and B [N][Pc] are shared;
 //    expert g reduces over its columns [poffs[g], poffs[g+1]); C is expert
 //    g's [M][N], all zeros for an expert without tokens.
+#include <type_traits>
+
 #include "mx_common.hpp"
 
 namespace moe {
@@ -325,6 +327,119 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_kernel(const TE *__restr
     scales[ce / 32] = static_cast<uint8_t>(ex + 127);
 }
 
+// The same quantisation by tiles of 128 rows x 64 columns: the block reads
+// the tile's (gathered) rows with 16-byte loads along the columns into LDS
+// (bf16 sources as bf16, with the tile's row weights beside them; fp32
+// sources weighted as fp32), then wave w quantises the tile's 32-row block w
+// with one lane per column, so that each column's codes of the tile (128
+// bytes) and its four scale bytes are written by one block. Consecutive
+// blocks take consecutive column groups of one row tile, so that the blocks
+// running together read whole source rows. Needs N % 64 == 0, a 16-byte
+// aligned source with 16-byte aligned rows, and tiles that do not straddle
+// segments: token segments padded to 128 rows (poffs), or uniform segments
+// (tile t of segment s covers its rows 128 t.., the 32-row blocks past
+// seg_rows are skipped).
+constexpr int kQtRows = 128, kQtCols = 64;
+template <typename TE>
+__global__ __launch_bounds__(256) void mx_quantize_cols_tile_kernel(const TE *__restrict__ src, int64_t src_ld,
+                                                                    const int32_t *__restrict__ gather,
+                                                                    const float *__restrict__ row_w,
+                                                                    const int32_t *__restrict__ offs,
+                                                                    const int32_t *__restrict__ poffs, int nseg,
+                                                                    int seg_rows, int N, int64_t ld,
+                                                                    uint8_t *__restrict__ codes,
+                                                                    uint8_t *__restrict__ scales) {
+    constexpr bool kHalf = sizeof(TE) == 2;
+    constexpr int kVec = 16 / static_cast<int>(sizeof(TE));   // elements per 16-byte load
+    constexpr int kLpr = kQtCols / kVec;                      // lanes per tile row
+    constexpr int kRpp = 256 / kLpr;                          // rows per pass
+    constexpr int kPasses = kQtRows / kRpp;
+    constexpr int kLd = kQtCols + kVec;                       // LDS row stride (elements), 16 bytes of padding
+    typedef typename std::conditional<kHalf, bf16_t, float>::type TL;
+    __shared__ __attribute__((aligned(16))) TL T[kQtRows * kLd];
+    __shared__ float s_w[kQtRows];
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * kQtCols, tb = blockIdx.y;
+    int local, nrows, r0, nblk;
+    int64_t cbase;
+    if (offs) {
+        const int p = kQtRows * tb;
+        if (p >= poffs[nseg]) return;
+        int lo = 0, hi = nseg - 1;   // largest s with poffs[s] <= p
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (poffs[mid] <= p) lo = mid;
+            else hi = mid - 1;
+        }
+        local = p - poffs[lo];
+        r0 = offs[lo];
+        nrows = offs[lo + 1] - r0;
+        cbase = p;
+        nblk = 4;
+    } else {
+        const int tps = (seg_rows + kQtRows - 1) / kQtRows;
+        const int sg = tb / tps;
+        local = kQtRows * (tb - sg * tps);
+        r0 = sg * seg_rows;
+        nrows = seg_rows;
+        cbase = static_cast<int64_t>(sg) * N * ld + local;   // segment s: [N][ld] at s N ld
+        nblk = min(4, (seg_rows - local) / 32);
+    }
+    const int c = tid % kLpr, rr0 = tid / kLpr;
+    u32x4 q[kPasses];
+    float wrow[kPasses];
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+        const int li = local + rr0 + kRpp * i;
+        q[i] = u32x4{0u, 0u, 0u, 0u};
+        wrow[i] = 1.0f;
+        if (li < nrows) {
+            const int64_t r = gather ? gather[r0 + li] : r0 + li;
+            q[i] = *reinterpret_cast<const u32x4 *>(src + r * src_ld + n0 + kVec * c);
+            if (row_w) wrow[i] = row_w[r0 + li];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+        TL *dst = T + (rr0 + kRpp * i) * kLd + kVec * c;
+        if constexpr (kHalf) {
+            *reinterpret_cast<u32x4 *>(dst) = q[i];
+            if (c == 0) s_w[rr0 + kRpp * i] = wrow[i];
+        } else {
+            *reinterpret_cast<float4 *>(dst) =
+                make_float4(__uint_as_float(q[i][0]) * wrow[i], __uint_as_float(q[i][1]) * wrow[i],
+                            __uint_as_float(q[i][2]) * wrow[i], __uint_as_float(q[i][3]) * wrow[i]);
+        }
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63;
+    if (w >= nblk) return;
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        if constexpr (kHalf)
+            v[i] = bf16_to_f32(T[(32 * w + i) * kLd + lane]) * s_w[32 * w + i];
+        else
+            v[i] = T[(32 * w + i) * kLd + lane];
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const int ex = mx_block_exponent(amax);
+    u32x4 out[2];
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) word |= e4m3_code(ldexpf(v[4 * wd + k], -ex)) << (8 * k);
+        out[wd >> 2][wd & 3] = word;
+    }
+    const int64_t ce = cbase + static_cast<int64_t>(n0 + lane) * ld + 32 * w;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(codes + ce);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    scales[ce / 32] = static_cast<uint8_t>(ex + 127);
+}
+
 // Rows of 32-blocks along K of a gathered, row-weighted source: row p of
 // the result is row_w[p] * src[gather[p]] (fp32), quantised by the same
 // rule as mx_quantize_kernel; one thread per block.
@@ -414,6 +529,15 @@ void launch_quantize_cols(const TE *src, int64_t src_ld, const int32_t *gather, 
                           int N, int64_t ld, uint8_t *codes, uint8_t *scales, hipStream_t s) {
     const int64_t nb = padded_rows / 32;
     if (nb == 0 || N == 0) return;
+    constexpr int kVec = 16 / static_cast<int>(sizeof(TE));
+    const int64_t tiles = offs ? padded_rows / kQtRows
+                               : static_cast<int64_t>(nseg) * ((seg_rows + kQtRows - 1) / kQtRows);
+    if (N % kQtCols == 0 && aligned16(src) && src_ld % kVec == 0 && tiles <= 65535) {
+        hipLaunchKernelGGL(mx_quantize_cols_tile_kernel<TE>,
+                           dim3(static_cast<unsigned>(N / kQtCols), static_cast<unsigned>(tiles)), dim3(256), 0, s,
+                           src, src_ld, gather, row_w, offs, poffs, nseg, seg_rows, N, ld, codes, scales);
+        return;
+    }
     hipLaunchKernelGGL(mx_quantize_cols_kernel<TE>, dim3(static_cast<unsigned>(nb), static_cast<unsigned>((N + 255) / 256)),
                        dim3(256), 0, s, src, src_ld, gather, row_w, offs, poffs, nseg, seg_rows, N, ld, codes,
                        scales);

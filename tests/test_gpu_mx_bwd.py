@@ -44,16 +44,17 @@ def _gpu_chain(cfg, dinp):
     return wq, f, g
 
 
-def test_transposed_weight_quantisation_is_bit_exact(moe_lib):
+@pytest.mark.parametrize("E,R,C", [(3, 96, 320), (2, 256, 128), (2, 160, 100)])
+def test_transposed_weight_quantisation_is_bit_exact(moe_lib, E, R, C):
     """moe_mx_quantize_t of [E, R, C] against oracle.mx_quantize of each
     matrix's transpose (blocks of 32 rows of a column), including an all-zero
-    block, a huge outlier and C not a multiple of 256."""
+    block and a huge outlier: 128-row tiles with a partial last tile (R = 96,
+    160), whole tiles, and C not a multiple of 64 (one thread per block)."""
     from mixture_experts_layer_06_amd import binding as B
     g = torch.Generator().manual_seed(3)
-    E, R, C = 3, 96, 320
     w = (torch.randn(E, R, C, generator=g) * torch.exp(torch.randn(E, 1, C, generator=g) * 3)).to(torch.bfloat16)
     w[1, 32:64, 7] = 0
-    w[2, 5, 300] = 3.0e38
+    w[E - 1, 5, C - 20] = 3.0e38
     for src in (w, w.float()):
         codes, scales = B.moe_mx_quantize_t(src.cuda())
         torch.cuda.synchronize()

@@ -594,7 +594,7 @@ def main():
         kernels["grouped_ffn"] = ("grouped_gemm_mx SwiGLU launch with the activation quantised in its "
                                   "epilogue + grouped_gemm_mx plain launch (one moe_grouped_ffn_mx call)")
         kernels["grouped_ffn_bwd"] = ("moe_grouped_ffn_bwd_mx call (first projection recomputed, five "
-                                      "mx_gemm_nt launches, quantisation and SwiGLU-backward passes); "
+                                      "MXFP8 GEMM launches: three by token segments, two by k-segments; quantisation and SwiGLU-backward passes); "
                                       "algorithmic backward FLOPs only, the recomputation not credited")
     out["roofline"] = {
         "kernel": kernels[dom], "bound": "mfma",

@@ -319,7 +319,8 @@ int moe_grouped_ffn_mx(const uint8_t *x_codes, const uint8_t *x_scales, const in
  * F % 128 == 0, E <= 256, a workspace of
  * moe_grouped_ffn_bwd_mx_workspace_size(P,h,F,E) bytes (MOE_ERR_WORKSPACE
  * otherwise), tensor, code and workspace pointers 16-byte aligned, scale
- * pointers 4-byte aligned. */
+ * pointers 4-byte aligned; T*h, P*h and 2*P*F below 2^31 and P + 127 E
+ * below 2^23 (MOE_ERR_UNSUPPORTED otherwise). */
 int moe_mx_quantize_t(const void *src, int dtype, int64_t batch, int64_t R, int64_t C,
                       uint8_t *codes, uint8_t *scales, void *stream);
 size_t moe_grouped_ffn_bwd_mx_workspace_size(int64_t P, int64_t h, int64_t F, int E);

@@ -95,13 +95,13 @@ __device__ __forceinline__ void mx_sched() {
 // scale byte. The bf16 activation is stored too when a.C is set.
 template <bool HALF>
 __device__ __forceinline__ void store_tile_mx_swiglu(const GGArgs &a, const TileInfo &ti,
-                                                     floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane) {
+                                                     floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane,
+                                                     int64_t crow0) {
     constexpr int NI = HALF ? 2 : 4, NJ = 4;
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int tok0 = HALF ? 0 : (wave >> 1) * 128;
     const int rows = min(kMxTile, ti.M - ti.m0);
-    const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
     bf16_t *Cseg = a.C ? static_cast<bf16_t *>(a.C) + crow0 * a.N_out : nullptr;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -156,24 +156,40 @@ __device__ __forceinline__ void store_tile_mx_swiglu(const GGArgs &a, const Tile
     }
 }
 
-// Epilogue of a plain tile (the second projection): the bf16 outputs.
+// Epilogue of a plain tile: the outputs in bf16 (the second projection), or
+// in fp32 (kModeF32Out), at rows crow0 + m of C [.][N_out]. In fp32 the four
+// stores that fill a row's 128-byte line (columns 8 gq + 4 lhi of one
+// 32-column subtile) are issued back to back, so that L2 holds no partly
+// written lines that it might write back twice.
 template <int MODE, bool HALF>
 __device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileInfo &ti,
-                                              floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane) {
+                                                    floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane,
+                                                    int64_t crow0) {
     constexpr int NI = HALF ? 2 : 4, NJ = 4;
     const int l32 = lane & 31, lhi = lane >> 5;
     const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int tok0 = HALF ? 0 : (wave >> 1) * 128;
     const int rows = min(kMxTile, ti.M - ti.m0);
-    bf16_t *Cseg = static_cast<bf16_t *>(a.C) + (static_cast<int64_t>(ti.row0) + ti.m0) * a.N_out;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int m = tok0 + j * 32 + l32;
         if (m >= rows) continue;
+        const int64_t e0 = (crow0 + m) * a.N_out;
+        if constexpr (MODE == kModeF32Out) {
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int nl = 8 * gq + 4 * lhi;
-            {
+            for (int i = 0; i < NI; ++i) {
+                const int n0 = ti.n_tile * kMxTile + wrow0 + i * 32;
+                if (n0 >= a.N_out) continue;   // N_out % 32 == 0: whole subtiles
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    *reinterpret_cast<float4 *>(static_cast<float *>(a.C) + e0 + n0 + 8 * gq + 4 * lhi) =
+                        make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                                    acc[i][j][4 * gq + 3]);
+            }
+        } else {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int nl = 8 * gq + 4 * lhi;
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int n = ti.n_tile * kMxTile + wrow0 + i * 32 + nl;
@@ -181,7 +197,7 @@ __device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileI
                     uint2 o;
                     o.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
                     o.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-                    *reinterpret_cast<uint2 *>(Cseg + static_cast<int64_t>(m) * a.N_out + n) = o;
+                    *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(a.C) + e0 + n) = o;
                 }
             }
         }
@@ -203,9 +219,12 @@ __device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileI
 // token rows are addressed as one per-lane offset plus a per-row-group
 // scalar offset, through buffer resources bounded to the tile's valid rows
 // (rows past them read as zeros and are never stored).
+// k-steps k0 + t for t < nreal, then (t >= nreal, when nks > nreal) the
+// k-step kzero, which holds zero codes and scales: a product of zeros adds
+// exactly nothing, so a tile may run an even number of steps.
 template <int MODE, bool ODD, bool HALF, bool GATHER>
 __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti, uint8_t *LB0, uint8_t *LB1, int k0,
-                                             int nks, float *part) {
+                                             int nks, float *part, int64_t crow0, int nreal, int kzero) {
     const GGArgs &a = x.g;
     constexpr int NI = HALF ? 2 : 4;
     constexpr int NJ = 4;
@@ -284,21 +303,22 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
         return f;
     };
     auto load_step = [&](int kt) {
+        const int ka = kt < nreal ? k0 + kt : kzero;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int soff = (MODE == kModeSwiGLU ? (j >> 1) : j) * 32 * K + kt * kMxBK;
+            const int soff = (MODE == kModeSwiGLU ? (j >> 1) : j) * 32 * K + ka * kMxBK;
             RW[j] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (j & 1)) ? rwu : rwg, wlane,
-                                                          soff + k0 * kMxBK, 0);
+                                                          soff, 0);
         }
 #pragma unroll
         for (int j = 0; j < XJ; ++j) {
             if constexpr (GATHER)
-                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], (k0 + kt) * kMxBK, 0);
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], ka * kMxBK, 0);
             else
-                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + (k0 + kt) * kMxBK, 0);
+                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + ka * kMxBK, 0);
         }
-        RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, (k0 + kt) * 4, 0);
-        RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, (k0 + kt) * 4, 0);
+        RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, ka * 4, 0);
+        RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, ka * 4, 0);
     };
     auto read_scales = [&](const uint8_t *LB, uint32_t (&SA)[NI], uint32_t (&SB)[NJ]) {
         const uint32_t *LS = reinterpret_cast<const uint32_t *>(LB + kMxStage);
@@ -336,6 +356,58 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    // Staging item q of a k-step: q < 8 the weight chunk RW[q], then the
+    // token chunks RX[q - 8], then the two scale words.
+    constexpr int NIT = NWR + 2;
+    auto write_item = [&](uint8_t *LB, auto q_tag) {
+        constexpr int q = decltype(q_tag)::value;
+        if constexpr (q < 8) *reinterpret_cast<u32x4 *>(LB + so + q * 32 * kMxBK) = RW[q];
+        else if constexpr (q < NWR) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + (q - 8) * 32 * kMxBK) = RX[q - 8];
+        else reinterpret_cast<uint32_t *>(LB + kMxStage)[(q - NWR) * kMxTile + tid] = RS[q - NWR];
+    };
+    auto load_item = [&](int kt, auto q_tag) {
+        constexpr int q = decltype(q_tag)::value;
+        const int ka = kt < nreal ? k0 + kt : kzero;
+        if constexpr (q < 8) {
+            const int soff = (MODE == kModeSwiGLU ? (q >> 1) : q) * 32 * K + ka * kMxBK;
+            RW[q] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (q & 1)) ? rwu : rwg, wlane, soff, 0);
+        } else if constexpr (q < NWR) {
+            if constexpr (GATHER)
+                RX[q - 8] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[q - 8], ka * kMxBK, 0);
+            else
+                RX[q - 8] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], (q - 8) * 32 * K + ka * kMxBK, 0);
+        } else if constexpr (q == NWR) {
+            RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, ka * 4, 0);
+        } else {
+            RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, ka * 4, 0);
+        }
+    };
+    // Half 0 with the staging pinned: MFMA slot q (weight subtile i = q / NJ,
+    // token subtile j) is followed by its fragment reads (the next weight
+    // fragment at j = 0, the next k-sub's token fragments at j = 1 ..), then
+    // the LDS write of item q of k-step t+1 and the load of item q of k-step
+    // t+2 (items spread evenly over the slots). Items keep one order in
+    // every step, so each write waits for the load issued one k-step before
+    // it and no earlier one.
+    auto half0 = [&](const uint8_t *LBc, uint8_t *NXT, int kk, const uint32_t (&SA)[NI], const uint32_t (&SB)[NJ]) {
+        constexpr_for<NMF>([&](auto q_tag) {
+            constexpr int q = decltype(q_tag)::value;
+            constexpr int i = q / NJ, j = q % NJ;
+            v8i &fa = (i & 1) ? fy : fx;
+            v8i &fo = (i & 1) ? fx : fy;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb0[j], acc[i][j], 0, 0, 0, SA[i], 0,
+                                                                        SB[j]);
+            if constexpr (j == 0) fo = i + 1 < NI ? frag(LBc, wrow0 + (i + 1) * 32 + l32, 0) : frag(LBc, wrow0 + l32, 1);
+            if constexpr (j >= 1 && j <= NBR) fb1[i * NBR + j - 1] = frag(LBc + kMxRegion, tok0 + (i * NBR + j - 1) * 32 + l32, 1);
+            constexpr int lo = q * NIT / NMF, hi = (q + 1) * NIT / NMF;
+            constexpr_for<hi - lo>([&](auto r_tag) {
+                constexpr int it = lo + decltype(r_tag)::value;
+                write_item(NXT, std::integral_constant<int, it>{});
+                load_item(kk, std::integral_constant<int, it>{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
     auto step = [&](const uint8_t *CUR, uint8_t *NXT, int t, const uint32_t (&SAc)[NI], const uint32_t (&SBc)[NJ],
                     uint32_t (&SAn)[NI], uint32_t (&SBn)[NJ]) {
         const int kk = t + 2 < nk ? t + 2 : nk - 1;
@@ -343,12 +415,7 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
         // second half of the previous step: all of them are past it before
         // anyone overwrites it
         MOE_LDS_BARRIER();
-        half(I0{}, I1{}, CUR, CUR, fb0, fb1, SAc, SBc);
-        // k-step t+1 (data and scale words) to the other stage, k-step t+2 in
-        write_step(NXT);
-        load_step(kk);
-        mx_sched<NMF, NRD, NWR + 2, NWR + 2>();
-        __builtin_amdgcn_sched_barrier(0);
+        half0(CUR, NXT, kk, SAc, SBc);
         MOE_LDS_BARRIER();
         read_scales(NXT, SAn, SBn);
         half(I1{}, I0{}, CUR, NXT, fb1, fb0, SAc, SBc);
@@ -392,8 +459,8 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
                         make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         return;
     }
-    if constexpr (MODE == kModePlain) store_tile_mx_plain<MODE, HALF>(a, ti, acc, wave, lane);
-    else store_tile_mx_swiglu<HALF>(a, ti, acc, wave, lane);
+    if constexpr (MODE == kModeSwiGLU) store_tile_mx_swiglu<HALF>(a, ti, acc, wave, lane, crow0);
+    else store_tile_mx_plain<MODE, HALF>(a, ti, acc, wave, lane, crow0);
 }
 
 // Split workspace (second projection only): an int header of 64 KB ([0..2]:
@@ -463,8 +530,47 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
             d[3] = ti.M;
             d[4] = ti.row0;
         }
-        if (ti.M - ti.m0 > kMxTile / 2) gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LB0, LB1, k0, nks, part);
-        else gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LB0, LB1, k0, nks, part);
+        const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
+        if (ti.M - ti.m0 > kMxTile / 2)
+            gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LB0, LB1, k0, nks, part, crow0, nks, 0);
+        else
+            gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LB0, LB1, k0, nks, part, crow0, nks, 0);
+    }
+}
+
+// Weight gradients by k-segments: A [M][K] and B [N_out][K] are shared by all
+// experts (K: the row stride, the padded token count); expert e reduces over
+// its k-steps [poffs[e], poffs[e+1]) / 128 into C[e] = A B^T, [M][N_out] in
+// fp32 (zeros for an expert without tokens). Tile w: expert w / (mt nt),
+// then row tile, then column tile; the tile body is the rows mode's, with
+// the expert's k-range and its output rows e M + m. An odd number of
+// k-steps is completed by one step on the zero k-step kzero (the last 128
+// columns of A and B), so the kernel holds the even tile body only; half
+// tiles (128 rows of A) only when M % 256 != 0 (HALF_TAIL).
+template <bool HALF_TAIL>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_mx_kseg(MXArgs x, const int32_t *poffs, int M, int kzero) {
+    __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage + kMxScaleBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage + kMxScaleBytes];
+    const int m_tiles = (M + kMxTile - 1) / kMxTile;
+    const int per = m_tiles * x.g.n_tiles;
+    const int total = x.g.E * per;
+    for (int w = xcd_block_index(blockIdx.x, x.g.grid); w < total; w += x.g.grid) {
+        const int e = w / per, r = w - e * per;
+        const int mt = r / x.g.n_tiles;
+        TileInfo ti;
+        ti.seg = 0;
+        ti.m0 = mt * kMxTile;
+        ti.n_tile = r - mt * x.g.n_tiles;
+        ti.M = M;
+        ti.row0 = 0;
+        ti.shared = false;
+        const int k0 = poffs[e] / kMxBK, nks = (poffs[e + 1] - poffs[e]) / kMxBK;
+        const int64_t crow0 = static_cast<int64_t>(e) * M + ti.m0;
+        const int nrun = nks + (nks & 1);
+        if (HALF_TAIL && M - ti.m0 <= kMxTile / 2)
+            gemm_tile_mx<kModeF32Out, false, true, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
+        else
+            gemm_tile_mx<kModeF32Out, false, false, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
     }
 }
 
@@ -495,7 +601,7 @@ __device__ __forceinline__ void mx_reduce_tile(const GGArgs &a, const TileInfo &
                     acc[i][j][4 * q + 3] += v.w;
                 }
     }
-    store_tile_mx_plain<kModePlain, HALF>(a, ti, acc, tid >> 6, tid & 63);
+    store_tile_mx_plain<kModePlain, HALF>(a, ti, acc, tid >> 6, tid & 63, static_cast<int64_t>(ti.row0) + ti.m0);
 }
 
 // Sum of every split tile's pieces, in piece order, into piece 0 (one
@@ -571,6 +677,52 @@ int launch_mx(MXArgs x, int64_t P, hipStream_t s, const char *what) {
 }
 
 }  // namespace
+
+int mx_gemm_rows(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t *gather, int a_rows,
+                 const int32_t *offsets, int E, int64_t P, const uint8_t *b_codes, const uint8_t *b_scales, int N_out,
+                 int K, void *C, bool f32_out, hipStream_t s, const char *what) {
+    MXArgs g{};
+    g.g.A = a_codes;
+    g.g.gather = gather;
+    g.g.a_rows = gather ? a_rows : 0;
+    g.g.B = b_codes;
+    g.g.C = C;
+    g.g.offsets = offsets;
+    g.g.E = E;
+    g.g.N_out = N_out;
+    g.g.K = K;
+    g.ws = b_scales;
+    g.xs = a_scales;
+    return f32_out ? launch_mx<kModeF32Out>(g, P, s, what) : launch_mx<kModePlain>(g, P, s, what);
+}
+
+int mx_gemm_kseg(const uint8_t *a_codes, const uint8_t *a_scales, int M, const uint8_t *b_codes,
+                 const uint8_t *b_scales, int N, int64_t ld, const int32_t *poffs, int E, float *C, hipStream_t s,
+                 const char *what) {
+    MXArgs g{};
+    g.g.A = a_codes;
+    g.g.B = b_codes;
+    g.g.C = C;
+    g.g.E = E;
+    g.g.N_out = N;
+    g.g.K = static_cast<int>(ld);
+    g.ws = b_scales;
+    g.xs = a_scales;
+    g.g.n_tiles = (N + kMxTile - 1) / kMxTile;
+    const int64_t tiles = static_cast<int64_t>(E) * ((M + kMxTile - 1) / kMxTile) * g.g.n_tiles;
+    int64_t grid = num_cus();
+    if (grid > tiles) grid = tiles;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid < 1) grid = 1;
+    g.g.grid = static_cast<int>(grid);
+    const int kzero = static_cast<int>(ld / kMxBK) - 1;
+    if (M % kMxTile)
+        hipLaunchKernelGGL(grouped_gemm_mx_kseg<true>, dim3(g.g.grid), dim3(256), 0, s, g, poffs, M, kzero);
+    else
+        hipLaunchKernelGGL(grouped_gemm_mx_kseg<false>, dim3(g.g.grid), dim3(256), 0, s, g, poffs, M, kzero);
+    return check_launch(what);
+}
+
 }  // namespace moe
 
 using namespace moe;

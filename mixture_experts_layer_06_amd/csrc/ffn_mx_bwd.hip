@@ -24,214 +24,18 @@
 // (one k-step), so a k-step never mixes two experts and the padding adds
 // nothing; the blocks of 32 start at the segment's first token.
 //
-// mx_gemm_nt: C[m][n] = sum_k A[m][k] B[n][k] on E4M3 codes with one E8M0
-// scale per 32 values of k. Tiles of 128 x 128 (m x n); four waves of 64 x
-// 64 (2 x 2 v_mfma_scale_f32_32x32x64_f8f6f4 per k-sub of 64); k-steps of
-// 128 bytes staged global -> VGPR -> LDS in two stages, one barrier per
-// k-step, the next k-step loaded while the current one is multiplied. The
-// n side is the instruction's A operand, so a lane's four consecutive
-// accumulators are four consecutive n of one m (one 16-byte store). Operand
-// layout of the instruction and the LDS swizzle as in the forward kernel:
-// lane half g supplies chunks 4s + g and 4s + 2 + g of k-sub s and the scale
-// of block 2s + g (its row's scale word shifted right by 8 g, opsel 2s).
-//  - rows mode (recomputation, input gradients): A is the token rows [P][K]
-//    cut into the experts' segments (offsets), or with a_gather the rows
-//    a_gather[r] of an unpermuted [T][K]; B is expert g's matrix [N][K];
-//    C [P][N].
-//  - k-segment mode (weight gradients): A [M][Pc] and B [N][Pc] are shared;
-//    expert g reduces over its columns [poffs[g], poffs[g+1]); C is expert
-//    g's [M][N], all zeros for an expert without tokens.
+// The five products run on the forward's MXFP8 grouped GEMM (mx_gemm_rows:
+// 256 x 256 tiles of v_mfma_scale_f32_32x32x64_f8f6f4, one persistent block
+// per compute unit, k-step t + 1 written to LDS while k-step t is multiplied
+// and t + 2 is loaded): the recomputation and the input gradients by token
+// segments, the weight gradients by each expert's k-range of the transposed
+// operands (mx_gemm_kseg), all with fp32 accumulation.
 #include <type_traits>
 
 #include "mx_common.hpp"
 
 namespace moe {
 namespace {
-
-constexpr int kNtT = 128;                     // tile rows, m and n
-constexpr int kNtK = 128;                     // bytes (fp8 values) of a row per k-step
-constexpr int kNtRegion = kNtT * kNtK;        // one operand tile of a stage
-constexpr int kNtStage = 2 * kNtRegion + 2 * kNtT * 4;   // + a scale word per row of each side
-
-struct MxNtArgs {
-    const uint8_t *A, *As;   // m side: codes [.][lda], scales [.][lda/32]
-    const uint8_t *B, *Bs;   // n side
-    void *C;
-    const int32_t *offs;     // rows mode: segment offsets [E+1]; k-segment mode: padded offsets [E+1]
-    const int32_t *a_gather; // rows mode: A row of segment row r is a_gather[r] (or null: r)
-    int E, M, N, K;          // M: k-segment mode only; K: rows mode only
-    int64_t lda, ldb;        // row strides of the codes (bytes)
-    int64_t b_stride;        // rows mode: bytes between the experts' B matrices
-    int n_tiles, m_tiles;
-};
-
-__device__ __forceinline__ v8i nt_frag(const uint8_t *R, int row, int sub, int lhi) {
-    const u32x4 lo = *reinterpret_cast<const u32x4 *>(R + mswz(row, 4 * sub + lhi));
-    const u32x4 hi = *reinterpret_cast<const u32x4 *>(R + mswz(row, 4 * sub + 2 + lhi));
-    v8i f;
-    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-    return f;
-}
-
-// The four scaled MFMAs of k-sub S of the stage at LB.
-template <int S>
-__device__ __forceinline__ void nt_ksub(floatx16 (&acc)[2][2], const uint8_t *LB, int rn, int rm, int lhi,
-                                        const uint32_t (&SA)[2], const uint32_t (&SB)[2]) {
-    v8i fa[2], fb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) fa[i] = nt_frag(LB, rn + 32 * i, S, lhi);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = nt_frag(LB + kNtRegion, rm + 32 * j, S, lhi);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 2 * S, SA[i],
-                                                                        2 * S, SB[j]);
-}
-
-template <bool KSEG, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void mx_gemm_nt(MxNtArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t LS[2][kNtStage];
-    __shared__ int s_cum[kMaxSeg];
-    __shared__ int s_tmp[256];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, lhi = lane >> 5;
-    const int wn = wave & 1, wm = wave >> 1;
-    int g, mrows, n0, k0, nk;
-    int64_t m0;   // first A row of the tile
-    const uint8_t *Bg = a.B, *Bsg = a.Bs;
-    if constexpr (KSEG) {
-        const int per = a.m_tiles * a.n_tiles;
-        g = static_cast<int>(blockIdx.x) / per;
-        const int r = static_cast<int>(blockIdx.x) - g * per;
-        const int mt = r / a.n_tiles, nt = r - mt * a.n_tiles;
-        m0 = static_cast<int64_t>(mt) * kNtT;
-        mrows = min(kNtT, a.M - mt * kNtT);
-        n0 = nt * kNtT;
-        const int p0 = a.offs[g], p1 = a.offs[g + 1];
-        k0 = p0 / kNtK;
-        nk = (p1 - p0) / kNtK;
-    } else {
-        GGArgs gg{};
-        gg.offsets = a.offs;
-        gg.E = a.E;
-        gg.n_tiles = a.n_tiles;
-        const int total = build_tile_prefix(gg, kNtT, s_cum, s_tmp);
-        if (static_cast<int>(blockIdx.x) >= total) return;   // the whole block
-        const TileInfo ti = decode_tile(gg, s_cum, blockIdx.x, kNtT);
-        g = ti.seg;
-        m0 = static_cast<int64_t>(ti.row0) + ti.m0;
-        mrows = min(kNtT, ti.M - ti.m0);
-        n0 = ti.n_tile * kNtT;
-        k0 = 0;
-        nk = a.K / kNtK;
-        Bg = a.B + static_cast<int64_t>(g) * a.b_stride;
-        Bsg = a.Bs + static_cast<int64_t>(g) * (a.b_stride / 32);
-    }
-    g = __builtin_amdgcn_readfirstlane(g);
-    nk = __builtin_amdgcn_readfirstlane(nk);
-    k0 = __builtin_amdgcn_readfirstlane(k0);
-
-    // rows this thread stages: chunk c of rows rb + 32 j (clamped to valid
-    // rows; rows past them are computed and never stored), and one scale
-    // word: the n-side row tid (tid < 128) or the m-side row tid - 128
-    const int c = tid & 7, rb = tid >> 3;
-    const uint8_t *pa[4], *pb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int ra = min(rb + 32 * j, mrows - 1), rbn = min(n0 + rb + 32 * j, a.N - 1);
-        const int64_t arow = KSEG || a.a_gather == nullptr ? m0 + ra : a.a_gather[m0 + ra];
-        pa[j] = a.A + arow * a.lda + 16 * c;
-        pb[j] = Bg + static_cast<int64_t>(rbn) * a.ldb + 16 * c;
-    }
-    int64_t srow;   // the row whose scale word this thread stages
-    if (tid < kNtT) {
-        srow = min(n0 + tid, a.N - 1);
-    } else {
-        const int64_t r = m0 + min(tid - kNtT, mrows - 1);
-        srow = KSEG || a.a_gather == nullptr ? r : a.a_gather[r];
-    }
-    const uint32_t *ps = tid < kNtT ? reinterpret_cast<const uint32_t *>(Bsg + srow * (a.ldb / 32))
-                                    : reinterpret_cast<const uint32_t *>(a.As + srow * (a.lda / 32));
-    u32x4 RA[4], RB[4];
-    uint32_t RS = 0;
-    auto load = [&](int t) {
-        const int64_t off = static_cast<int64_t>(k0 + t) * kNtK;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            RA[j] = *reinterpret_cast<const u32x4 *>(pa[j] + off);
-            RB[j] = *reinterpret_cast<const u32x4 *>(pb[j] + off);
-        }
-        RS = ps[k0 + t];
-    };
-    auto store = [&](uint8_t *S) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<u32x4 *>(S + mswz(rb + 32 * j, c)) = RB[j];
-            *reinterpret_cast<u32x4 *>(S + kNtRegion + mswz(rb + 32 * j, c)) = RA[j];
-        }
-        reinterpret_cast<uint32_t *>(S + 2 * kNtRegion)[tid] = RS;
-    };
-
-    floatx16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-    const int rn = 64 * wn + l32, rm = 64 * wm + l32;
-    if (nk > 0) {
-        load(0);
-        store(LS[0]);
-        __syncthreads();
-        for (int t = 0; t < nk; ++t) {
-            const uint8_t *cur = LS[t & 1];
-            if (t + 1 < nk) load(t + 1);
-            const uint32_t *W = reinterpret_cast<const uint32_t *>(cur + 2 * kNtRegion);
-            uint32_t SA[2], SB[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) SA[i] = W[rn + 32 * i] >> (8 * lhi);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) SB[j] = W[kNtT + rm + 32 * j] >> (8 * lhi);
-            nt_ksub<0>(acc, cur, rn, rm, lhi, SA, SB);
-            nt_ksub<1>(acc, cur, rn, rm, lhi, SA, SB);
-            // the other stage was last read in step t - 1, before the
-            // barrier that ended it
-            if (t + 1 < nk) store(LS[(t + 1) & 1]);
-            __syncthreads();
-        }
-    }
-
-    // accumulator q of MFMA (i, j): n = n0 + 64 wn + 32 i + 8 (q/4) + 4 lhi +
-    // q%4, m = 64 wm + 32 j + l32 within the tile
-    const int64_t crow = KSEG ? static_cast<int64_t>(g) * a.M + m0 : m0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int ml = 64 * wm + 32 * j + l32;
-        if (ml >= mrows) continue;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int n = n0 + 64 * wn + 32 * i + 8 * gq + 4 * lhi;
-                if (n >= a.N) continue;
-                const int64_t e = (crow + ml) * a.N + n;
-                if constexpr (OUT_BF16) {
-                    uint2 o;
-                    o.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
-                    o.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-                    *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(a.C) + e) = o;
-                } else {
-                    *reinterpret_cast<float4 *>(static_cast<float *>(a.C) + e) =
-                        make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                                    acc[i][j][4 * gq + 3]);
-                }
-            }
-    }
-}
 
 // poffs[e] = sum over e' < e of count_e' rounded up to 128 (one block of
 // 256 threads, E <= 256).
@@ -259,8 +63,10 @@ __global__ __launch_bounds__(256) void mx_pad_offsets_kernel(const int32_t *__re
 // uniform segments of seg_rows rows (offs null; segment s is the matrix
 // [N][ld] at s * N * ld codes, its block b at column 32 b of row n). Rows past
 // n_s, up to the segment's padded end, are zeros. Block index pb: padded
-// column / 32 over all segments. With row_w, segment row r's values are
-// multiplied by row_w[r] (in fp32) before quantising.
+// column / 32 over all segments. With token segments, the last 128 columns
+// of each codes row (from ld - 128) get zero codes and zero scale bytes: a
+// k-step of zeros for the weight gradients. With row_w, segment row r's
+// values are multiplied by row_w[r] (in fp32) before quantising.
 template <typename TE>
 __global__ __launch_bounds__(256) void mx_quantize_cols_kernel(const TE *__restrict__ src, int64_t src_ld,
                                                                const int32_t *__restrict__ gather,
@@ -276,18 +82,22 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_kernel(const TE *__restr
     int64_t cbase;   // codes offset of the block's first element in row n = 0
     if (offs) {
         const int p = 32 * pb;
-        if (p >= poffs[nseg]) return;
-        int lo = 0, hi = nseg - 1;   // largest s with poffs[s] <= p
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (poffs[mid] <= p) lo = mid;
-            else hi = mid - 1;
-        }
-        s = lo;
-        local = p - poffs[s];
-        r0 = offs[s];
-        nrows = offs[s + 1] - r0;
         cbase = p;
+        if (p >= poffs[nseg]) {
+            if (p < ld - 128) return;
+            s = local = r0 = nrows = 0;   // the zero k-step
+        } else {
+            int lo = 0, hi = nseg - 1;   // largest s with poffs[s] <= p
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (poffs[mid] <= p) lo = mid;
+                else hi = mid - 1;
+            }
+            s = lo;
+            local = p - poffs[s];
+            r0 = offs[s];
+            nrows = offs[s + 1] - r0;
+        }
     } else {
         const int per = seg_rows / 32;
         s = pb / per;
@@ -364,18 +174,22 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_tile_kernel(const TE *__
     int64_t cbase;
     if (offs) {
         const int p = kQtRows * tb;
-        if (p >= poffs[nseg]) return;
-        int lo = 0, hi = nseg - 1;   // largest s with poffs[s] <= p
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (poffs[mid] <= p) lo = mid;
-            else hi = mid - 1;
-        }
-        local = p - poffs[lo];
-        r0 = offs[lo];
-        nrows = offs[lo + 1] - r0;
         cbase = p;
         nblk = 4;
+        if (p >= poffs[nseg]) {
+            if (p != ld - kQtRows) return;
+            local = r0 = nrows = 0;   // the zero k-step
+        } else {
+            int lo = 0, hi = nseg - 1;   // largest s with poffs[s] <= p
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (poffs[mid] <= p) lo = mid;
+                else hi = mid - 1;
+            }
+            local = p - poffs[lo];
+            r0 = offs[lo];
+            nrows = offs[lo + 1] - r0;
+        }
     } else {
         const int tps = (seg_rows + kQtRows - 1) / kQtRows;
         const int sg = tb / tps;
@@ -545,22 +359,10 @@ void launch_quantize_cols(const TE *src, int64_t src_ld, const int32_t *gather, 
 
 inline unsigned grid_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192); }
 
-template <bool KSEG, bool OUT_BF16>
-void launch_nt(MxNtArgs a, int64_t P, hipStream_t s) {
-    a.n_tiles = (a.N + kNtT - 1) / kNtT;
-    int64_t grid;
-    if (KSEG) {
-        a.m_tiles = (a.M + kNtT - 1) / kNtT;
-        grid = static_cast<int64_t>(a.E) * a.m_tiles * a.n_tiles;
-    } else {
-        grid = (P / kNtT + a.E) * static_cast<int64_t>(a.n_tiles);   // upper bound; extra blocks exit
-    }
-    if (grid > 0) hipLaunchKernelGGL((mx_gemm_nt<KSEG, OUT_BF16>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
-}
-
 // Workspace of the backward: sub-buffers at 256-byte boundaries.
 struct MxBwdLayout {
-    int64_t Pc;   // columns of the token-blocked (transposed) operands
+    int64_t Pc;   // padded token columns of the token-blocked (transposed) operands
+    int64_t ldT;  // their row stride: Pc and a last k-step of zeros (the weight gradients' zero step)
     size_t poffs, gu, act, dy_c, dy_s, dyT_c, dyT_s, actT_c, actT_s, dact, dgu, dgu_c, dgu_s, dguT_c, dguT_s, xT_c,
         xT_s;
     size_t total;
@@ -569,6 +371,7 @@ struct MxBwdLayout {
 MxBwdLayout mx_bwd_layout(int64_t P, int64_t h, int64_t F, int E) {
     MxBwdLayout L{};
     L.Pc = ((P + 127 * static_cast<int64_t>(E)) + 127) / 128 * 128;
+    L.ldT = L.Pc + 128;
     size_t at = 0;
     auto take = [&](size_t bytes) {
         const size_t o = at;
@@ -576,7 +379,7 @@ MxBwdLayout mx_bwd_layout(int64_t P, int64_t h, int64_t F, int E) {
         return o;
     };
     const size_t Pz = static_cast<size_t>(P), hz = static_cast<size_t>(h), Fz = static_cast<size_t>(F),
-                 Pcz = static_cast<size_t>(L.Pc);
+                 Pcz = static_cast<size_t>(L.ldT);
     L.poffs = take(static_cast<size_t>(E + 1) * 4);
     L.gu = take(Pz * 2 * Fz * 4);
     L.act = take(Pz * Fz * 4);
@@ -651,8 +454,8 @@ extern "C" int moe_grouped_ffn_bwd_mx(const void *grad_out, const float *row_w, 
     MOE_CHECK_ARG(h % 128 == 0 && F % 128 == 0 && E <= 256, MOE_ERR_UNSUPPORTED,
                   "moe_grouped_ffn_bwd_mx: need h %% 128 == 0, F %% 128 == 0, E <= 256");
     const MxBwdLayout L = mx_bwd_layout(P, h, F, E);
-    MOE_CHECK_ARG(P < (int64_t(1) << 31) && T < (int64_t(1) << 31) && 2 * F * h < (int64_t(1) << 31) &&
-                      L.Pc / 32 < (int64_t(1) << 31),
+    MOE_CHECK_ARG(P < (int64_t(1) << 31) && T * h < (int64_t(1) << 31) && P * h < (int64_t(1) << 31) &&
+                      2 * P * F < (int64_t(1) << 31) && 2 * F * h < (int64_t(1) << 31) && L.ldT / 128 <= 65535,
                   MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_bwd_mx: sizes too large");
     MOE_CHECK_ARG(workspace && workspace_bytes >= L.total, MOE_ERR_WORKSPACE,
                   "moe_grouped_ffn_bwd_mx: needs moe_grouped_ffn_bwd_mx_workspace_size bytes of workspace");
@@ -677,96 +480,42 @@ extern "C" int moe_grouped_ffn_bwd_mx(const void *grad_out, const float *row_w, 
     hipLaunchKernelGGL(mx_pad_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, E, poffs);
     if (P > 0) {
         // gu = Q_h(X) Q_h(W1) in fp32 (the forward's codes), act = silu(g) u
-        MxNtArgs r1{};
-        r1.A = x_codes;
-        r1.As = x_scales;
-        r1.a_gather = sorted_token;
-        r1.B = w1_codes;
-        r1.Bs = w1_scales;
-        r1.C = gu;
-        r1.offs = offsets;
-        r1.E = E;
-        r1.N = 2 * FF;
-        r1.K = hh;
-        r1.lda = h;
-        r1.ldb = h;
-        r1.b_stride = 2 * F * h;
-        launch_nt<false, false>(r1, P, s);
+        int st = mx_gemm_rows(x_codes, x_scales, sorted_token, static_cast<int>(T), offsets, E, P, w1_codes,
+                              w1_scales, 2 * FF, hh, gu, true, s, "moe_grouped_ffn_bwd_mx recompute");
+        if (st != MOE_OK) return st;
         hipLaunchKernelGGL(mx_swiglu_act_kernel, dim3(grid_for(P * (F / 4))), dim3(256), 0, s, gu, P, FF, act);
         // dY = row_w * dL/dout along h (rows) and along the tokens; the
         // activation and the token rows along the tokens
         hipLaunchKernelGGL(mx_quantize_rows_gather_kernel<bf16_t>, dim3(static_cast<unsigned>((P * (h / 32) + 255) / 256)),
                            dim3(256), 0, s, G, sorted_token, row_w, P, hh, ws + L.dy_c, ws + L.dy_s);
-        launch_quantize_cols(G, h, sorted_token, row_w, offsets, poffs, E, 0, L.Pc, hh, L.Pc, ws + L.dyT_c,
+        launch_quantize_cols(G, h, sorted_token, row_w, offsets, poffs, E, 0, L.ldT, hh, L.ldT, ws + L.dyT_c,
                              ws + L.dyT_s, s);
-        launch_quantize_cols(static_cast<const float *>(act), F, nullptr, nullptr, offsets, poffs, E, 0, L.Pc, FF,
-                             L.Pc, ws + L.actT_c, ws + L.actT_s, s);
-        launch_quantize_cols(static_cast<const bf16_t *>(x), h, sorted_token, nullptr, offsets, poffs, E, 0, L.Pc, hh,
-                             L.Pc, ws + L.xT_c, ws + L.xT_s, s);
+        launch_quantize_cols(static_cast<const float *>(act), F, nullptr, nullptr, offsets, poffs, E, 0, L.ldT, FF,
+                             L.ldT, ws + L.actT_c, ws + L.actT_s, s);
+        launch_quantize_cols(static_cast<const bf16_t *>(x), h, sorted_token, nullptr, offsets, poffs, E, 0, L.ldT, hh,
+                             L.ldT, ws + L.xT_c, ws + L.xT_s, s);
         // dact = Q_h(dY) Q_h(W2)
-        MxNtArgs d2{};
-        d2.A = ws + L.dy_c;
-        d2.As = ws + L.dy_s;
-        d2.B = w2t_codes;
-        d2.Bs = w2t_scales;
-        d2.C = ws + L.dact;
-        d2.offs = offsets;
-        d2.E = E;
-        d2.N = FF;
-        d2.K = hh;
-        d2.lda = h;
-        d2.ldb = h;
-        d2.b_stride = F * h;
-        launch_nt<false, false>(d2, P, s);
+        st = mx_gemm_rows(ws + L.dy_c, ws + L.dy_s, nullptr, 0, offsets, E, P, w2t_codes, w2t_scales, FF, hh,
+                          ws + L.dact, true, s, "moe_grouped_ffn_bwd_mx dact");
+        if (st != MOE_OK) return st;
         // dgu, then along 2F (rows) and along the tokens
         hipLaunchKernelGGL(mx_swiglu_bwd_kernel, dim3(grid_for(P * (F / 4))), dim3(256), 0, s,
                            reinterpret_cast<const float *>(ws + L.dact), static_cast<const float *>(gu), P, FF, dgu);
         launch_quantize(static_cast<const float *>(dgu), P, 2 * F, ws + L.dgu_c, ws + L.dgu_s, s);
-        launch_quantize_cols(static_cast<const float *>(dgu), 2 * F, nullptr, nullptr, offsets, poffs, E, 0, L.Pc,
-                             2 * FF, L.Pc, ws + L.dguT_c, ws + L.dguT_s, s);
+        launch_quantize_cols(static_cast<const float *>(dgu), 2 * F, nullptr, nullptr, offsets, poffs, E, 0, L.ldT,
+                             2 * FF, L.ldT, ws + L.dguT_c, ws + L.dguT_s, s);
         // dX = Q_2F(dgu) Q_2F(W1)
-        MxNtArgs d1{};
-        d1.A = ws + L.dgu_c;
-        d1.As = ws + L.dgu_s;
-        d1.B = w1t_codes;
-        d1.Bs = w1t_scales;
-        d1.C = grad_x_perm;
-        d1.offs = offsets;
-        d1.E = E;
-        d1.N = hh;
-        d1.K = 2 * FF;
-        d1.lda = 2 * F;
-        d1.ldb = 2 * F;
-        d1.b_stride = 2 * F * h;
-        launch_nt<false, true>(d1, P, s);
+        st = mx_gemm_rows(ws + L.dgu_c, ws + L.dgu_s, nullptr, 0, offsets, E, P, w1t_codes, w1t_scales, hh,
+                          2 * FF, grad_x_perm, false, s, "moe_grouped_ffn_bwd_mx dX");
+        if (st != MOE_OK) return st;
     }
     // dW2 = Q_tok(dY)^T Q_tok(act), dW1 = Q_tok(dgu)^T Q_tok(X): every
     // expert's tiles run (zeros when it has no tokens)
-    MxNtArgs w2{};
-    w2.A = ws + L.dyT_c;
-    w2.As = ws + L.dyT_s;
-    w2.B = ws + L.actT_c;
-    w2.Bs = ws + L.actT_s;
-    w2.C = grad_w2;
-    w2.offs = poffs;
-    w2.E = E;
-    w2.M = hh;
-    w2.N = FF;
-    w2.lda = L.Pc;
-    w2.ldb = L.Pc;
-    launch_nt<true, false>(w2, P, s);
-    MxNtArgs w1{};
-    w1.A = ws + L.dguT_c;
-    w1.As = ws + L.dguT_s;
-    w1.B = ws + L.xT_c;
-    w1.Bs = ws + L.xT_s;
-    w1.C = grad_w1;
-    w1.offs = poffs;
-    w1.E = E;
-    w1.M = 2 * FF;
-    w1.N = hh;
-    w1.lda = L.Pc;
-    w1.ldb = L.Pc;
-    launch_nt<true, false>(w1, P, s);
+    const int st2 = mx_gemm_kseg(ws + L.dyT_c, ws + L.dyT_s, hh, ws + L.actT_c, ws + L.actT_s, FF, L.ldT, poffs, E,
+                                 grad_w2, s, "moe_grouped_ffn_bwd_mx dW2");
+    if (st2 != MOE_OK) return st2;
+    const int st1 = mx_gemm_kseg(ws + L.dguT_c, ws + L.dguT_s, 2 * FF, ws + L.xT_c, ws + L.xT_s, hh, L.ldT, poffs, E,
+                                 grad_w1, s, "moe_grouped_ffn_bwd_mx dW1");
+    if (st1 != MOE_OK) return st1;
     return check_launch("moe_grouped_ffn_bwd_mx");
 }

@@ -4,6 +4,8 @@
 // elements) and the LDS layout of the scaled-MFMA operand tiles.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -76,6 +78,15 @@ void launch_quantize(const TE *src, int64_t rows, int64_t K, uint8_t *codes, uin
                        nb, codes, scales);
 }
 
+// fn(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
+template <int N, int I = 0, typename Fn>
+__device__ __forceinline__ void constexpr_for(Fn &&fn) {
+    if constexpr (I < N) {
+        fn(std::integral_constant<int, I>{});
+        constexpr_for<N, I + 1>(fn);
+    }
+}
+
 // byte offset of 16-byte chunk c of row r in an operand region with
 // 128-byte rows (a k-step of 128 fp8 values): the chunk index is XOR-ed with
 // bits 1..3 of the row, which keeps both the row-chunk writes and the
@@ -83,4 +94,22 @@ void launch_quantize(const TE *src, int64_t rows, int64_t K, uint8_t *codes, uin
 __device__ __forceinline__ int mswz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 }  // namespace
+
+// The MXFP8 grouped GEMM (256 x 256 tiles of scaled MFMAs, persistent grid)
+// for the backward's products:
+// * rows mode: C [P][N_out] = A B_e^T per token segment e (offsets), A the
+//   codes [.][K] of the segment rows (row r is A row gather[r] when gather
+//   is set; a_rows rows then), B_e = b_codes + e N_out K, both with their
+//   block scales along K; C in fp32 (f32_out) or bf16.
+// * k-segment mode: C[e] [M][N] (fp32) = A_e B_e^T with A [M][ld] and
+//   B [N][ld] shared by the experts, expert e reducing over its columns
+//   [poffs[e], poffs[e+1]) (multiples of 128); the last 128 columns of A and
+//   B (and their scale bytes) must be zeros.
+int mx_gemm_rows(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t *gather, int a_rows,
+                 const int32_t *offsets, int E, int64_t P, const uint8_t *b_codes, const uint8_t *b_scales, int N_out,
+                 int K, void *C, bool f32_out, hipStream_t s, const char *what);
+int mx_gemm_kseg(const uint8_t *a_codes, const uint8_t *a_scales, int M, const uint8_t *b_codes,
+                 const uint8_t *b_scales, int N, int64_t ld, const int32_t *poffs, int E, float *C, hipStream_t s,
+                 const char *what);
+
 }  // namespace moe

@@ -174,19 +174,22 @@ def _fp32_bounds(xe, w1e, w2e, dy):
 
 
 def _ws_layout(P, h, F, E):
-    """Byte offsets of the backward's workspace buffers (moe.h documents
-    the order; every buffer starts at a 256-byte boundary)."""
+    """Byte offsets of the backward's workspace buffers, in the order the
+    kernel source lays them out (every buffer starts at a 256-byte
+    boundary); the token-blocked operands have rows of Pc padded token
+    columns and a zero k-step of 128 more."""
     Pc = ((P + 127 * E) + 127) // 128 * 128
+    ld = Pc + 128
     sizes = [("poffs", (E + 1) * 4), ("gu", P * 2 * F * 4), ("act", P * F * 4), ("dy_c", P * h),
-             ("dy_s", P * h // 32), ("dyT_c", h * Pc), ("dyT_s", h * Pc // 32), ("actT_c", F * Pc),
-             ("actT_s", F * Pc // 32), ("dact", P * F * 4), ("dgu", P * 2 * F * 4), ("dgu_c", P * 2 * F),
-             ("dgu_s", P * 2 * F // 32), ("dguT_c", 2 * F * Pc), ("dguT_s", 2 * F * Pc // 32), ("xT_c", h * Pc),
-             ("xT_s", h * Pc // 32)]
+             ("dy_s", P * h // 32), ("dyT_c", h * ld), ("dyT_s", h * ld // 32), ("actT_c", F * ld),
+             ("actT_s", F * ld // 32), ("dact", P * F * 4), ("dgu", P * 2 * F * 4), ("dgu_c", P * 2 * F),
+             ("dgu_s", P * 2 * F // 32), ("dguT_c", 2 * F * ld), ("dguT_s", 2 * F * ld // 32), ("xT_c", h * ld),
+             ("xT_s", h * ld // 32)]
     off, at = {}, 0
     for name, nbytes in sizes:
         off[name] = at
         at += (nbytes + 255) // 256 * 256
-    return Pc, off, at
+    return ld, off, at
 
 
 def _codes_explained(got_c, got_s, v, b, what):
@@ -214,9 +217,9 @@ def _stage_checks(cfg, dinp, f, wq, o, G, experts):
     from mixture_experts_layer_06_amd import binding as B
     P, h = int(f["sorted_token"].numel()), cfg.h
     F, E = cfg.F, cfg.E
-    Pc, off, total = _ws_layout(P, h, F, E)
+    ld, off, total = _ws_layout(P, h, F, E)
     assert total == B.lib().moe_grouped_ffn_bwd_mx_workspace_size(P, h, F, E)
-    ws = torch.zeros(total, dtype=torch.uint8, device="cuda")
+    ws = torch.full((total,), 0x5a, dtype=torch.uint8, device="cuda")
     row_w = B.moe_permute_weights(f["topk_w"], f["row_of"])
     B.moe_grouped_ffn_bwd_mx(dinp["grad_out"], row_w, dinp["x"], f["x_codes"], f["x_scales"], f["sorted_token"],
                              f["offsets"], wq["w1_codes"], wq["w1_scales"], wq["w1t_codes"], wq["w1t_scales"],
@@ -231,6 +234,12 @@ def _stage_checks(cfg, dinp, f, wq, o, G, experts):
     counts = np.bincount(r["topk_idx"].ravel(), minlength=E)
     poffs = np.concatenate([[0], np.cumsum((counts + 127) // 128 * 128)])
     assert np.array_equal(buf("poffs", (E + 1,), torch.int32).cpu().numpy(), poffs)
+    # the zero k-step after the padded token columns of every token-blocked
+    # operand (the workspace starts as 0x5a bytes): codes and scale bytes 0
+    for cname, sname, N in (("dyT_c", "dyT_s", h), ("actT_c", "actT_s", F), ("xT_c", "xT_s", h),
+                            ("dguT_c", "dguT_s", 2 * F)):
+        assert not buf(cname, (N, ld), torch.uint8)[:, ld - 128:].any(), cname
+        assert not buf(sname, (N, ld // 32), torch.uint8)[:, ld // 32 - 4:].any(), sname
     offs = f["offsets"].cpu().numpy()
     for e in experts:
         tok, slot = np.nonzero(r["topk_idx"] == e)
@@ -248,8 +257,8 @@ def _stage_checks(cfg, dinp, f, wq, o, G, experts):
         mp = -(-m // 128) * 128
 
         def tok_codes(cname, sname, N):
-            c = buf(cname, (N, Pc), torch.uint8)[:, p0:p0 + mp].cpu().numpy()
-            sc = buf(sname, (N, Pc // 32), torch.uint8)[:, p0 // 32:(p0 + mp) // 32].cpu().numpy()
+            c = buf(cname, (N, ld), torch.uint8)[:, p0:p0 + mp].cpu().numpy()
+            sc = buf(sname, (N, ld // 32), torch.uint8)[:, p0 // 32:(p0 + mp) // 32].cpu().numpy()
             return c, sc
 
         pad = lambda v: np.concatenate([v, np.zeros((mp - m, v.shape[1]))]).T      # [N, mp], zero columns

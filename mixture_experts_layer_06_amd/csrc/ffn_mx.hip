@@ -219,6 +219,91 @@ __device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileI
 // token rows are addressed as one per-lane offset plus a per-row-group
 // scalar offset, through buffer resources bounded to the tile's valid rows
 // (rows past them read as zeros and are never stored).
+// The staging registers of one k-step: 8 weight chunks, XJ token chunks and
+// the two scale words of this thread.
+template <int XJ>
+struct MxStage {
+    u32x4 W[8], X[XJ];
+    uint32_t S[2];
+};
+
+// A tile's operand sources: buffer resources over its weight rows, token
+// rows and scale words (bounded to its valid rows, so rows past them read as
+// zeros), this thread's offsets, and the k-step map (k-steps k0 + t for t <
+// nreal, the zero k-step kzero after them). load_item issues staging item q
+// of k-step kt: q < 8 the weight chunk q, then the token chunks, then the
+// two scale words.
+template <int MODE, bool HALF, bool GATHER>
+struct MxTileSrc {
+    static constexpr int XJ = HALF ? 4 : 8;
+    static constexpr int NIT = 8 + XJ + 2;
+    __amdgpu_buffer_rsrc_t rwg, rwu, rx, rws, rxs;
+    int K, k0, nreal, kzero, wlane, wsr, xsr;
+    int xv[GATHER ? XJ : 1];
+
+    __device__ __forceinline__ MxTileSrc(const MXArgs &x, const TileInfo &ti, int k0_, int nreal_, int kzero_) {
+        const GGArgs &a = x.g;
+        const int tid = threadIdx.x;
+        K = a.K;
+        const int KS = K / 32;
+        k0 = __builtin_amdgcn_readfirstlane(k0_);
+        nreal = __builtin_amdgcn_readfirstlane(nreal_);
+        kzero = __builtin_amdgcn_readfirstlane(kzero_);
+        const int chunk = tid & 7, rb = tid >> 3;
+        const int rows = min(kMxTile, ti.M - ti.m0);
+        const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
+        const uint8_t *wseg = static_cast<const uint8_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
+        const uint8_t *wsseg = x.ws + static_cast<int64_t>(ti.seg) * nb_rows * KS;
+        // weight rows of the tile: SwiGLU j even -> gate rows wfirst + (j/2)*32 + rb,
+        // j odd -> the up rows N_out + the same; plain: wfirst + 32 j + rb
+        const int wfirst = MODE == kModeSwiGLU ? ti.n_tile * (kMxTile / 2) : ti.n_tile * kMxTile;
+        const int wvalid = min(MODE == kModeSwiGLU ? kMxTile / 2 : kMxTile, a.N_out - wfirst);
+        const uint32_t wbytes = static_cast<uint32_t>(wvalid) * static_cast<uint32_t>(K);
+        rwg = make_rsrc(wseg + static_cast<int64_t>(wfirst) * K, wbytes);
+        rwu = make_rsrc(wseg + static_cast<int64_t>(MODE == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K, wbytes);
+        wlane = rb * K + chunk * 16;
+        const uint8_t *xbase = GATHER ? static_cast<const uint8_t *>(a.A)
+                                      : static_cast<const uint8_t *>(a.A) + (static_cast<int64_t>(ti.row0) + ti.m0) * K;
+        const uint8_t *xsbase = GATHER ? x.xs : x.xs + (static_cast<int64_t>(ti.row0) + ti.m0) * KS;
+        rx = make_rsrc(xbase, static_cast<uint32_t>(GATHER ? a.a_rows : rows) * static_cast<uint32_t>(K));
+        rws = make_rsrc(wsseg);
+        rxs = make_rsrc(xsbase, static_cast<uint32_t>(GATHER ? a.a_rows : rows) * static_cast<uint32_t>(KS));
+        if constexpr (GATHER) {
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) {
+                const int r = rb + 32 * j;
+                xv[j] = a.gather[ti.row0 + ti.m0 + (r < rows ? r : rows - 1)] * K + chunk * 16;
+            }
+        } else {
+            xv[0] = rb * K + chunk * 16;
+        }
+        // the scale words this thread stages: weight row and token row tid of the tile
+        wsr = weight_row<MODE>(ti.n_tile, tid, a.N_out) * KS;
+        xsr = (GATHER ? a.gather[ti.row0 + ti.m0 + min(tid, rows - 1)] : min(tid, rows - 1)) * KS;
+    }
+
+    template <int q>
+    __device__ __forceinline__ void load_item(int kt, MxStage<XJ> &R) const {
+        const int ka = kt < nreal ? k0 + kt : kzero;
+        if constexpr (q < 8) {
+            const int soff = (MODE == kModeSwiGLU ? (q >> 1) : q) * 32 * K + ka * kMxBK;
+            R.W[q] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (q & 1)) ? rwu : rwg, wlane, soff, 0);
+        } else if constexpr (q < 8 + XJ) {
+            if constexpr (GATHER)
+                R.X[q - 8] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[q - 8], ka * kMxBK, 0);
+            else
+                R.X[q - 8] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], (q - 8) * 32 * K + ka * kMxBK, 0);
+        } else if constexpr (q == 8 + XJ) {
+            R.S[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, ka * 4, 0);
+        } else {
+            R.S[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, ka * 4, 0);
+        }
+    }
+    __device__ __forceinline__ void load_step(int kt, MxStage<XJ> &R) const {
+        constexpr_for<NIT>([&](auto q_tag) { load_item<decltype(q_tag)::value>(kt, R); });
+    }
+};
+
 // k-steps k0 + t for t < nreal, then (t >= nreal, when nks > nreal) the
 // k-step kzero, which holds zero codes and scales: a product of zeros adds
 // exactly nothing, so a tile may run an even number of steps.
@@ -239,46 +324,11 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
     const int tok0 = HALF ? 0 : (wave >> 1) * 128;
     // k-steps [k0, k0 + nks) of the tile (all of them unless a split piece)
-    const int K = a.K, KS = K / 32;
-    k0 = __builtin_amdgcn_readfirstlane(k0);
+    const MxTileSrc<MODE, HALF, GATHER> src(x, ti, k0, nreal, kzero);
     const int nk = __builtin_amdgcn_readfirstlane(nks);
     const int chunk = tid & 7, rb = tid >> 3;
     const int so = mswz(rb, chunk);
-    const int rows = min(kMxTile, ti.M - ti.m0);
-    const int nb_rows = MODE == kModeSwiGLU ? 2 * a.N_out : a.N_out;
-
-    const uint8_t *wseg = static_cast<const uint8_t *>(a.B) + static_cast<int64_t>(ti.seg) * nb_rows * K;
-    const uint8_t *wsseg = x.ws + static_cast<int64_t>(ti.seg) * nb_rows * KS;
-    // weight rows of the tile: SwiGLU j even -> gate rows wfirst + (j/2)*32 + rb,
-    // j odd -> the up rows N_out + the same; plain: wfirst + 32 j + rb
-    const int wfirst = MODE == kModeSwiGLU ? ti.n_tile * (kMxTile / 2) : ti.n_tile * kMxTile;
-    const int wvalid = min(MODE == kModeSwiGLU ? kMxTile / 2 : kMxTile, a.N_out - wfirst);
-    const uint32_t wbytes = static_cast<uint32_t>(wvalid) * static_cast<uint32_t>(K);
-    const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wseg + static_cast<int64_t>(wfirst) * K, wbytes);
-    const __amdgpu_buffer_rsrc_t rwu =
-        make_rsrc(wseg + static_cast<int64_t>(MODE == kModeSwiGLU ? a.N_out + wfirst : wfirst) * K, wbytes);
-    const int wlane = rb * K + chunk * 16;
-    const uint8_t *xbase = GATHER ? static_cast<const uint8_t *>(a.A)
-                                  : static_cast<const uint8_t *>(a.A) + (static_cast<int64_t>(ti.row0) + ti.m0) * K;
-    const uint8_t *xsbase = GATHER ? x.xs : x.xs + (static_cast<int64_t>(ti.row0) + ti.m0) * KS;
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(xbase, static_cast<uint32_t>(GATHER ? a.a_rows : rows) * static_cast<uint32_t>(K));
-    const __amdgpu_buffer_rsrc_t rws = make_rsrc(wsseg);
-    const __amdgpu_buffer_rsrc_t rxs =
-        make_rsrc(xsbase, static_cast<uint32_t>(GATHER ? a.a_rows : rows) * static_cast<uint32_t>(KS));
-    int xv[GATHER ? XJ : 1];
-    if constexpr (GATHER) {
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int r = rb + 32 * j;
-            xv[j] = a.gather[ti.row0 + ti.m0 + (r < rows ? r : rows - 1)] * K + chunk * 16;
-        }
-    } else {
-        xv[0] = rb * K + chunk * 16;
-    }
-    // the scale words this thread stages: weight row and token row tid of the tile
-    const int wsr = weight_row<MODE>(ti.n_tile, tid, a.N_out) * KS;
-    const int xsr = (GATHER ? a.gather[ti.row0 + ti.m0 + min(tid, rows - 1)] : min(tid, rows - 1)) * KS;
+    (void)a;
 
     floatx16 acc[NI][NJ];
 #pragma unroll
@@ -287,11 +337,10 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-    u32x4 RW[8], RX[XJ];
+    MxStage<XJ> R;   // the next k-step's staging registers
     // the scale words of the lane's rows, shifted to its blocks; one set for
     // even and one for odd k-steps
     uint32_t SA0[NI], SB0[NJ], SA1[NI], SB1[NJ];
-    uint32_t RS[2];
     v8i fx, fy, fb0[NJ], fb1[NJ];
 
     auto frag = [&](const uint8_t *LB, int row, int sub) -> v8i {
@@ -302,24 +351,6 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
         f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
         return f;
     };
-    auto load_step = [&](int kt) {
-        const int ka = kt < nreal ? k0 + kt : kzero;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int soff = (MODE == kModeSwiGLU ? (j >> 1) : j) * 32 * K + ka * kMxBK;
-            RW[j] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (j & 1)) ? rwu : rwg, wlane,
-                                                          soff, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            if constexpr (GATHER)
-                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[j], ka * kMxBK, 0);
-            else
-                RX[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], j * 32 * K + ka * kMxBK, 0);
-        }
-        RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, ka * 4, 0);
-        RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, ka * 4, 0);
-    };
     auto read_scales = [&](const uint8_t *LB, uint32_t (&SA)[NI], uint32_t (&SB)[NJ]) {
         const uint32_t *LS = reinterpret_cast<const uint32_t *>(LB + kMxStage);
 #pragma unroll
@@ -329,11 +360,11 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     };
     auto write_step = [&](uint8_t *LB) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(LB + so + j * 32 * kMxBK) = RW[j];
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(LB + so + j * 32 * kMxBK) = R.W[j];
 #pragma unroll
-        for (int j = 0; j < XJ; ++j) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + j * 32 * kMxBK) = RX[j];
-        reinterpret_cast<uint32_t *>(LB + kMxStage)[tid] = RS[0];
-        reinterpret_cast<uint32_t *>(LB + kMxStage)[kMxTile + tid] = RS[1];
+        for (int j = 0; j < XJ; ++j) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + j * 32 * kMxBK) = R.X[j];
+        reinterpret_cast<uint32_t *>(LB + kMxStage)[tid] = R.S[0];
+        reinterpret_cast<uint32_t *>(LB + kMxStage)[kMxTile + tid] = R.S[1];
     };
     // One half: MFMAs of k-sub S of stage LBc (weight fragment 0 in fx,
     // token fragments in FBc), streaming in weight fragments of the same
@@ -356,31 +387,14 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // Staging item q of a k-step: q < 8 the weight chunk RW[q], then the
-    // token chunks RX[q - 8], then the two scale words.
+    // Staging item q of a k-step (R.W[q] for q < 8, then the token chunks,
+    // then the two scale words) to its place in stage LB.
     constexpr int NIT = NWR + 2;
     auto write_item = [&](uint8_t *LB, auto q_tag) {
         constexpr int q = decltype(q_tag)::value;
-        if constexpr (q < 8) *reinterpret_cast<u32x4 *>(LB + so + q * 32 * kMxBK) = RW[q];
-        else if constexpr (q < NWR) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + (q - 8) * 32 * kMxBK) = RX[q - 8];
-        else reinterpret_cast<uint32_t *>(LB + kMxStage)[(q - NWR) * kMxTile + tid] = RS[q - NWR];
-    };
-    auto load_item = [&](int kt, auto q_tag) {
-        constexpr int q = decltype(q_tag)::value;
-        const int ka = kt < nreal ? k0 + kt : kzero;
-        if constexpr (q < 8) {
-            const int soff = (MODE == kModeSwiGLU ? (q >> 1) : q) * 32 * K + ka * kMxBK;
-            RW[q] = __builtin_amdgcn_raw_buffer_load_b128((MODE == kModeSwiGLU && (q & 1)) ? rwu : rwg, wlane, soff, 0);
-        } else if constexpr (q < NWR) {
-            if constexpr (GATHER)
-                RX[q - 8] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[q - 8], ka * kMxBK, 0);
-            else
-                RX[q - 8] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv[0], (q - 8) * 32 * K + ka * kMxBK, 0);
-        } else if constexpr (q == NWR) {
-            RS[0] = __builtin_amdgcn_raw_buffer_load_b32(rws, wsr, ka * 4, 0);
-        } else {
-            RS[1] = __builtin_amdgcn_raw_buffer_load_b32(rxs, xsr, ka * 4, 0);
-        }
+        if constexpr (q < 8) *reinterpret_cast<u32x4 *>(LB + so + q * 32 * kMxBK) = R.W[q];
+        else if constexpr (q < NWR) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + (q - 8) * 32 * kMxBK) = R.X[q - 8];
+        else reinterpret_cast<uint32_t *>(LB + kMxStage)[(q - NWR) * kMxTile + tid] = R.S[q - NWR];
     };
     // Half 0 with the staging pinned: MFMA slot q (weight subtile i = q / NJ,
     // token subtile j) is followed by its fragment reads (the next weight
@@ -403,7 +417,7 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
             constexpr_for<hi - lo>([&](auto r_tag) {
                 constexpr int it = lo + decltype(r_tag)::value;
                 write_item(NXT, std::integral_constant<int, it>{});
-                load_item(kk, std::integral_constant<int, it>{});
+                src.template load_item<it>(kk, R);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -424,10 +438,10 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     };
 
     // prologue: k-step 0 into stage 0 with its scales, k-step 1 into VGPRs
-    load_step(0);
+    src.load_step(0, R);
     MOE_LDS_BARRIER();   // every wave is done reading the previous tile's stages
     write_step(LB0);
-    load_step(nk > 1 ? 1 : 0);
+    src.load_step(nk > 1 ? 1 : 0, R);
     MOE_LDS_BARRIER();
     read_scales(LB0, SA0, SB0);
     fx = frag(LB0, wrow0 + l32, 0);

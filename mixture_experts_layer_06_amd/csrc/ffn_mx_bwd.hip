@@ -22,7 +22,9 @@
 // stored transposed, [N][Pc]: each expert's segment starts at a padded
 // column poffs[e] and is completed with zero columns to a multiple of 128
 // (one k-step), so a k-step never mixes two experts and the padding adds
-// nothing; the blocks of 32 start at the segment's first token.
+// nothing; the blocks of 32 start at the segment's first token. act and dgu
+// exist only inside the passes that quantise them (fp32 in LDS): act along
+// the tokens, dgu along 2F and along the tokens.
 //
 // The five products run on the forward's MXFP8 grouped GEMM (mx_gemm_rows:
 // 256 x 256 tiles of v_mfma_scale_f32_32x32x64_f8f6f4, one persistent block
@@ -254,6 +256,173 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_tile_kernel(const TE *__
     scales[ce / 32] = static_cast<uint8_t>(ex + 127);
 }
 
+// The padded token rows of column-quantisation tile tb (positions 128 tb ..):
+// segment rows r0 + local + i for local + i < nrows; for the zero k-step at
+// columns ld - 128, no rows. False for a tile past the segments otherwise.
+__device__ __forceinline__ bool qt_tile(const int32_t *__restrict__ offs, const int32_t *__restrict__ poffs, int nseg,
+                                        int64_t ld, int tb, int &local, int &r0, int &nrows) {
+    const int p = kQtRows * tb;
+    if (p >= poffs[nseg]) {
+        if (p != ld - kQtRows) return false;
+        local = r0 = nrows = 0;
+        return true;
+    }
+    int lo = 0, hi = nseg - 1;   // largest s with poffs[s] <= p
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (poffs[mid] <= p) lo = mid;
+        else hi = mid - 1;
+    }
+    local = p - poffs[lo];
+    r0 = offs[lo];
+    nrows = offs[lo + 1] - r0;
+    return true;
+}
+
+// One 32-block of fp32 values v (amax their largest magnitude) to 32 codes
+// at codes[ce..] and its scale byte at scales[ce / 32].
+__device__ __forceinline__ void mx_store_block(const float (&v)[32], float amax, uint8_t *__restrict__ codes,
+                                               uint8_t *__restrict__ scales, int64_t ce) {
+    const int ex = mx_block_exponent(amax);
+    u32x4 out[2];
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) word |= e4m3_code(ldexpf(v[4 * wd + k], -ex)) << (8 * k);
+        out[wd >> 2][wd & 3] = word;
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(codes + ce);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    scales[ce / 32] = static_cast<uint8_t>(ex + 127);
+}
+
+// Rows 32 w .. 32 w + 31 of column c of an fp32 LDS tile (row stride tld)
+// as one block along the tokens.
+__device__ __forceinline__ void qt_col_block(const float *T, int tld, int c, int w, uint8_t *__restrict__ codes,
+                                             uint8_t *__restrict__ scales, int64_t ce) {
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = T[(32 * w + i) * tld + c];
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    mx_store_block(v, amax, codes, scales, ce);
+}
+
+// The activation act = silu(g) u of the recomputed pre-activations (g | u)
+// [P][2F] (fp32, the expression of the forward's epilogue), quantised along
+// the tokens straight away: tiles of 128 padded token rows x 64 columns of
+// F as in mx_quantize_cols_tile_kernel (codes [F][ld], zero padding rows
+// and zero k-step included), so act itself is never stored.
+__global__ __launch_bounds__(256) void mx_act_cols_kernel(const float *__restrict__ gu, int F,
+                                                          const int32_t *__restrict__ offs,
+                                                          const int32_t *__restrict__ poffs, int nseg, int64_t ld,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    constexpr int kLd = kQtCols + 4;
+    __shared__ __attribute__((aligned(16))) float T[kQtRows * kLd];
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * kQtCols, tb = blockIdx.y;
+    int local, r0, nrows;
+    if (!qt_tile(offs, poffs, nseg, ld, tb, local, r0, nrows)) return;
+    const int c = tid & 15, rr0 = tid >> 4;   // 16 lanes of 4 columns per row, 16 rows per pass
+#pragma unroll
+    for (int i = 0; i < kQtRows / 16; ++i) {
+        const int li = local + rr0 + 16 * i;
+        float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (li < nrows) {
+            const float *row = gu + static_cast<int64_t>(r0 + li) * 2 * F;
+            const float4 g = *reinterpret_cast<const float4 *>(row + n0 + 4 * c);
+            const float4 u = *reinterpret_cast<const float4 *>(row + F + n0 + 4 * c);
+            a = make_float4(g.x / (1.0f + expf(-g.x)) * u.x, g.y / (1.0f + expf(-g.y)) * u.y,
+                            g.z / (1.0f + expf(-g.z)) * u.z, g.w / (1.0f + expf(-g.w)) * u.w);
+        }
+        *reinterpret_cast<float4 *>(T + (rr0 + 16 * i) * kLd + 4 * c) = a;
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63;
+    qt_col_block(T, kLd, lane, w, codes, scales, kQtRows * static_cast<int64_t>(tb) + (n0 + lane) * ld + 32 * w);
+}
+
+// The SwiGLU backward at the recomputed (g | u), fp32 (dg = dact u s (1 + g
+// (1 - s)), du = dact g s, s = sigmoid(g), the expressions of the unfused
+// pass), quantised at once both ways: along 2F into row codes [P][2F] (for
+// the input gradient) and along the tokens into codes [2F][ld] (for the
+// first weight gradient). Tiles of 128 padded token rows x 64 columns of F:
+// the tile's 64 dg and 64 du columns in LDS, then each valid row's four
+// 32-column blocks and each column's four 32-row blocks; dgu itself is never
+// stored.
+__global__ __launch_bounds__(256) void mx_dgu_quant_kernel(const float *__restrict__ dact,
+                                                           const float *__restrict__ gu, int F,
+                                                           const int32_t *__restrict__ offs,
+                                                           const int32_t *__restrict__ poffs, int nseg, int64_t ld,
+                                                           uint8_t *__restrict__ row_codes,
+                                                           uint8_t *__restrict__ row_scales,
+                                                           uint8_t *__restrict__ tok_codes,
+                                                           uint8_t *__restrict__ tok_scales) {
+    constexpr int kLd = 2 * kQtCols + 4;
+    __shared__ __attribute__((aligned(16))) float T[kQtRows * kLd];
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * kQtCols, tb = blockIdx.y;
+    int local, r0, nrows;
+    if (!qt_tile(offs, poffs, nseg, ld, tb, local, r0, nrows)) return;
+    const int c = tid & 15, rr0 = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < kQtRows / 16; ++i) {
+        const int li = local + rr0 + 16 * i;
+        float dg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, du[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (li < nrows) {
+            const int64_t p = r0 + li;
+            const float4 d4 = *reinterpret_cast<const float4 *>(dact + p * F + n0 + 4 * c);
+            const float4 g4 = *reinterpret_cast<const float4 *>(gu + p * 2 * F + n0 + 4 * c);
+            const float4 u4 = *reinterpret_cast<const float4 *>(gu + p * 2 * F + F + n0 + 4 * c);
+            const float da[4] = {d4.x, d4.y, d4.z, d4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w},
+                        uv[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float sg = 1.0f / (1.0f + expf(-gv[q]));
+                dg[q] = da[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                du[q] = da[q] * gv[q] * sg;
+            }
+        }
+        float *trow = T + (rr0 + 16 * i) * kLd + 4 * c;
+        *reinterpret_cast<float4 *>(trow) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+        *reinterpret_cast<float4 *>(trow + kQtCols) = make_float4(du[0], du[1], du[2], du[3]);
+    }
+    __syncthreads();
+    // along 2F: row i, block b (b < 2: dg columns n0 + 32 b .., else du)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int it = tid + 256 * h2;
+        const int i = it >> 2, b = it & 3;
+        if (local + i < nrows) {
+            float v[32];
+            float amax = 0.0f;
+            const float *src = T + i * kLd + 32 * b;
+#pragma unroll
+            for (int k = 0; k < 32; k += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(src + k);
+                v[k] = f.x; v[k + 1] = f.y; v[k + 2] = f.z; v[k + 3] = f.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(v[k]));
+            const int col0 = b < 2 ? n0 + 32 * b : F + n0 + 32 * (b - 2);
+            mx_store_block(v, amax, row_codes, row_scales, static_cast<int64_t>(r0 + local + i) * 2 * F + col0);
+        }
+    }
+    // along the tokens: wave w takes the 32-row block w of the tile's columns
+    const int w = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int cc = lane + kQtCols * h2;
+        const int gcol = h2 == 0 ? n0 + lane : F + n0 + lane;
+        qt_col_block(T, kLd, cc, w, tok_codes, tok_scales,
+                     kQtRows * static_cast<int64_t>(tb) + static_cast<int64_t>(gcol) * ld + 32 * w);
+    }
+}
+
 // Rows of 32-blocks along K of a gathered, row-weighted source: row p of
 // the result is row_w[p] * src[gather[p]] (fp32), quantised by the same
 // rule as mx_quantize_kernel; one thread per block.
@@ -293,50 +462,6 @@ __global__ __launch_bounds__(256) void mx_quantize_rows_gather_kernel(const TE *
     scales[b] = static_cast<uint8_t>(ex + 127);
 }
 
-// act = silu(g) u from the recomputed fp32 pre-activations (g | u) [P][2F];
-// four columns per thread.
-__global__ __launch_bounds__(256) void mx_swiglu_act_kernel(const float *__restrict__ gu, int64_t P, int F,
-                                                            float *__restrict__ act) {
-    const int64_t nq = P * (F / 4);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nq;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t p = i / (F / 4);
-        const int f = static_cast<int>(i - p * (F / 4)) * 4;
-        const float4 g = *reinterpret_cast<const float4 *>(gu + p * 2 * F + f);
-        const float4 u = *reinterpret_cast<const float4 *>(gu + p * 2 * F + F + f);
-        *reinterpret_cast<float4 *>(act + p * F + f) =
-            make_float4(g.x / (1.0f + expf(-g.x)) * u.x, g.y / (1.0f + expf(-g.y)) * u.y,
-                        g.z / (1.0f + expf(-g.z)) * u.z, g.w / (1.0f + expf(-g.w)) * u.w);
-    }
-}
-
-// dgu = SwiGLU backward of dact at the recomputed pre-activations (g | u),
-// fp32: dg = dact u s (1 + g (1 - s)), du = dact g s, s = sigmoid(g); four
-// columns per thread.
-__global__ __launch_bounds__(256) void mx_swiglu_bwd_kernel(const float *__restrict__ dact,
-                                                            const float *__restrict__ gu, int64_t P, int F,
-                                                            float *__restrict__ dgu) {
-    const int64_t nq = P * (F / 4);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nq;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t p = i / (F / 4);
-        const int f = static_cast<int>(i - p * (F / 4)) * 4;
-        const float4 d = *reinterpret_cast<const float4 *>(dact + p * F + f);
-        const float4 g4 = *reinterpret_cast<const float4 *>(gu + p * 2 * F + f);
-        const float4 u4 = *reinterpret_cast<const float4 *>(gu + p * 2 * F + F + f);
-        const float da[4] = {d.x, d.y, d.z, d.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
-        float dg[4], du[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float sg = 1.0f / (1.0f + expf(-gv[q]));
-            dg[q] = da[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-            du[q] = da[q] * gv[q] * sg;
-        }
-        *reinterpret_cast<float4 *>(dgu + p * 2 * F + f) = make_float4(dg[0], dg[1], dg[2], dg[3]);
-        *reinterpret_cast<float4 *>(dgu + p * 2 * F + F + f) = make_float4(du[0], du[1], du[2], du[3]);
-    }
-}
-
 template <typename TE>
 void launch_quantize_cols(const TE *src, int64_t src_ld, const int32_t *gather, const float *row_w,
                           const int32_t *offs, const int32_t *poffs, int nseg, int seg_rows, int64_t padded_rows,
@@ -357,13 +482,12 @@ void launch_quantize_cols(const TE *src, int64_t src_ld, const int32_t *gather, 
                        scales);
 }
 
-inline unsigned grid_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192); }
 
 // Workspace of the backward: sub-buffers at 256-byte boundaries.
 struct MxBwdLayout {
     int64_t Pc;   // padded token columns of the token-blocked (transposed) operands
     int64_t ldT;  // their row stride: Pc and a last k-step of zeros (the weight gradients' zero step)
-    size_t poffs, gu, act, dy_c, dy_s, dyT_c, dyT_s, actT_c, actT_s, dact, dgu, dgu_c, dgu_s, dguT_c, dguT_s, xT_c,
+    size_t poffs, gu, dy_c, dy_s, dyT_c, dyT_s, actT_c, actT_s, dact, dgu_c, dgu_s, dguT_c, dguT_s, xT_c,
         xT_s;
     size_t total;
 };
@@ -382,7 +506,6 @@ MxBwdLayout mx_bwd_layout(int64_t P, int64_t h, int64_t F, int E) {
                  Pcz = static_cast<size_t>(L.ldT);
     L.poffs = take(static_cast<size_t>(E + 1) * 4);
     L.gu = take(Pz * 2 * Fz * 4);
-    L.act = take(Pz * Fz * 4);
     L.dy_c = take(Pz * hz);
     L.dy_s = take(Pz * hz / 32);
     L.dyT_c = take(hz * Pcz);
@@ -390,7 +513,6 @@ MxBwdLayout mx_bwd_layout(int64_t P, int64_t h, int64_t F, int E) {
     L.actT_c = take(Fz * Pcz);
     L.actT_s = take(Fz * Pcz / 32);
     L.dact = take(Pz * Fz * 4);
-    L.dgu = take(Pz * 2 * Fz * 4);
     L.dgu_c = take(Pz * 2 * Fz);
     L.dgu_s = take(Pz * 2 * Fz / 32);
     L.dguT_c = take(2 * Fz * Pcz);
@@ -474,36 +596,33 @@ extern "C" int moe_grouped_ffn_bwd_mx(const void *grad_out, const float *row_w, 
     const bf16_t *G = static_cast<const bf16_t *>(grad_out);
     const int hh = static_cast<int>(h), FF = static_cast<int>(F);
     float *gu = reinterpret_cast<float *>(ws + L.gu);
-    float *act = reinterpret_cast<float *>(ws + L.act);
-    float *dgu = reinterpret_cast<float *>(ws + L.dgu);
 
     hipLaunchKernelGGL(mx_pad_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, E, poffs);
     if (P > 0) {
-        // gu = Q_h(X) Q_h(W1) in fp32 (the forward's codes), act = silu(g) u
+        // gu = Q_h(X) Q_h(W1) in fp32 (the forward's codes); act = silu(g) u
+        // quantised along the tokens as it is formed
         int st = mx_gemm_rows(x_codes, x_scales, sorted_token, static_cast<int>(T), offsets, E, P, w1_codes,
                               w1_scales, 2 * FF, hh, gu, true, s, "moe_grouped_ffn_bwd_mx recompute");
         if (st != MOE_OK) return st;
-        hipLaunchKernelGGL(mx_swiglu_act_kernel, dim3(grid_for(P * (F / 4))), dim3(256), 0, s, gu, P, FF, act);
+        const dim3 qt_grid(static_cast<unsigned>(F / kQtCols), static_cast<unsigned>(L.ldT / kQtRows));
+        hipLaunchKernelGGL(mx_act_cols_kernel, qt_grid, dim3(256), 0, s, static_cast<const float *>(gu), FF, offsets,
+                           poffs, E, L.ldT, ws + L.actT_c, ws + L.actT_s);
         // dY = row_w * dL/dout along h (rows) and along the tokens; the
-        // activation and the token rows along the tokens
+        // token rows along the tokens
         hipLaunchKernelGGL(mx_quantize_rows_gather_kernel<bf16_t>, dim3(static_cast<unsigned>((P * (h / 32) + 255) / 256)),
                            dim3(256), 0, s, G, sorted_token, row_w, P, hh, ws + L.dy_c, ws + L.dy_s);
         launch_quantize_cols(G, h, sorted_token, row_w, offsets, poffs, E, 0, L.ldT, hh, L.ldT, ws + L.dyT_c,
                              ws + L.dyT_s, s);
-        launch_quantize_cols(static_cast<const float *>(act), F, nullptr, nullptr, offsets, poffs, E, 0, L.ldT, FF,
-                             L.ldT, ws + L.actT_c, ws + L.actT_s, s);
         launch_quantize_cols(static_cast<const bf16_t *>(x), h, sorted_token, nullptr, offsets, poffs, E, 0, L.ldT, hh,
                              L.ldT, ws + L.xT_c, ws + L.xT_s, s);
         // dact = Q_h(dY) Q_h(W2)
         st = mx_gemm_rows(ws + L.dy_c, ws + L.dy_s, nullptr, 0, offsets, E, P, w2t_codes, w2t_scales, FF, hh,
                           ws + L.dact, true, s, "moe_grouped_ffn_bwd_mx dact");
         if (st != MOE_OK) return st;
-        // dgu, then along 2F (rows) and along the tokens
-        hipLaunchKernelGGL(mx_swiglu_bwd_kernel, dim3(grid_for(P * (F / 4))), dim3(256), 0, s,
-                           reinterpret_cast<const float *>(ws + L.dact), static_cast<const float *>(gu), P, FF, dgu);
-        launch_quantize(static_cast<const float *>(dgu), P, 2 * F, ws + L.dgu_c, ws + L.dgu_s, s);
-        launch_quantize_cols(static_cast<const float *>(dgu), 2 * F, nullptr, nullptr, offsets, poffs, E, 0, L.ldT,
-                             2 * FF, L.ldT, ws + L.dguT_c, ws + L.dguT_s, s);
+        // dgu quantised along 2F (rows) and along the tokens as it is formed
+        hipLaunchKernelGGL(mx_dgu_quant_kernel, qt_grid, dim3(256), 0, s, reinterpret_cast<const float *>(ws + L.dact),
+                           static_cast<const float *>(gu), FF, offsets, poffs, E, L.ldT, ws + L.dgu_c, ws + L.dgu_s,
+                           ws + L.dguT_c, ws + L.dguT_s);
         // dX = Q_2F(dgu) Q_2F(W1)
         st = mx_gemm_rows(ws + L.dgu_c, ws + L.dgu_s, nullptr, 0, offsets, E, P, w1t_codes, w1t_scales, hh,
                           2 * FF, grad_x_perm, false, s, "moe_grouped_ffn_bwd_mx dX");

@@ -272,16 +272,16 @@ def test_binding_fails_loudly_without_library(tmp_path):
 
 def test_mx_bwd_workspace_size(lib):
     """Sub-buffers at 256-byte boundaries: padded offsets, the recomputed
-    pre-activations and activation (fp32), dY codes along h, dY and the
-    activation along the tokens (rows of P + 127 E columns rounded up to
-    128, then a zero k-step of 128), dact and dgu in fp32, dgu codes along
-    2F and along the tokens, x along the tokens (each code buffer followed
-    by its scales, 1/32 of it)."""
+    pre-activations (fp32), dY codes along h, dY and the activation along
+    the tokens (rows of P + 127 E columns rounded up to 128, then a zero
+    k-step of 128), dact in fp32, dgu codes along 2F and along the tokens,
+    x along the tokens (each code buffer followed by its scales, 1/32 of
+    it)."""
     P, h, F, E = 300, 256, 128, 4
     Pc = ((P + 127 * E) + 127) // 128 * 128 + 128
     r = lambda n: (n + 255) // 256 * 256
-    want = (r((E + 1) * 4) + r(P * 2 * F * 4) + r(P * F * 4) + r(P * h) + r(P * h // 32) + r(h * Pc) + r(h * Pc // 32) + r(F * Pc) + r(F * Pc // 32)
-            + r(P * F * 4) + r(P * 2 * F * 4) + r(P * 2 * F) + r(P * 2 * F // 32) + r(2 * F * Pc)
+    want = (r((E + 1) * 4) + r(P * 2 * F * 4) + r(P * h) + r(P * h // 32) + r(h * Pc) + r(h * Pc // 32) + r(F * Pc) + r(F * Pc // 32)
+            + r(P * F * 4) + r(P * 2 * F) + r(P * 2 * F // 32) + r(2 * F * Pc)
             + r(2 * F * Pc // 32) + r(h * Pc) + r(h * Pc // 32))
     assert lib.moe_grouped_ffn_bwd_mx_workspace_size(P, h, F, E) == want
     assert lib.moe_grouped_ffn_bwd_mx_workspace_size(-1, h, F, E) == 0

@@ -180,9 +180,9 @@ def _ws_layout(P, h, F, E):
     columns and a zero k-step of 128 more."""
     Pc = ((P + 127 * E) + 127) // 128 * 128
     ld = Pc + 128
-    sizes = [("poffs", (E + 1) * 4), ("gu", P * 2 * F * 4), ("act", P * F * 4), ("dy_c", P * h),
+    sizes = [("poffs", (E + 1) * 4), ("gu", P * 2 * F * 4), ("dy_c", P * h),
              ("dy_s", P * h // 32), ("dyT_c", h * ld), ("dyT_s", h * ld // 32), ("actT_c", F * ld),
-             ("actT_s", F * ld // 32), ("dact", P * F * 4), ("dgu", P * 2 * F * 4), ("dgu_c", P * 2 * F),
+             ("actT_s", F * ld // 32), ("dact", P * F * 4), ("dgu_c", P * 2 * F),
              ("dgu_s", P * 2 * F // 32), ("dguT_c", 2 * F * ld), ("dguT_s", 2 * F * ld // 32), ("xT_c", h * ld),
              ("xT_s", h * ld // 32)]
     off, at = {}, 0
@@ -210,10 +210,12 @@ def _codes_explained(got_c, got_s, v, b, what):
 def _stage_checks(cfg, dinp, f, wq, o, G, experts):
     """The backward's intermediates, read from a workspace the test hands
     to the call, for each listed expert over all of its tokens: the padded
-    segment offsets exactly; the recomputed pre-activations, the activation,
-    dact and dgu within their fp32 bounds of the oracle's; x blocked along
-    the tokens bit for bit; dY's codes along h and along the tokens equal
-    but for differences the fp32 bound explains."""
+    segment offsets exactly; the recomputed pre-activations and dact within
+    their fp32 bounds of the oracle's; x blocked along the tokens bit for
+    bit; the codes of dY (along h and along the tokens), of the activation
+    (along the tokens) and of dgu (along 2F and along the tokens), which
+    only exist quantised, equal but for differences their fp32 bounds
+    explain."""
     from mixture_experts_layer_06_amd import binding as B
     P, h = int(f["sorted_token"].numel()), cfg.h
     F, E = cfg.F, cfg.E
@@ -250,8 +252,7 @@ def _stage_checks(cfg, dinp, f, wq, o, G, experts):
         xe = np.asarray(o["x"][tok], dtype=np.float64)
         w1e, w2e = np.asarray(o["w1"][e], dtype=np.float64), np.asarray(o["w2"][e], dtype=np.float64)
         bd = _fp32_bounds(xe, w1e, w2e, dy)
-        for name, ref, bound, cols in (("gu", bd["a"], bd["b_a"], 2 * F), ("act", bd["hid"], bd["b_act"], F),
-                                       ("dact", bd["dact"], bd["b_dact"], F), ("dgu", bd["da"], bd["b_da"], 2 * F)):
+        for name, ref, bound, cols in (("gu", bd["a"], bd["b_a"], 2 * F), ("dact", bd["dact"], bd["b_dact"], F)):
             got = buf(name, (P, cols), torch.float32)[r0:r1].cpu().numpy().astype(np.float64)
             assert np.all(np.abs(got - ref) <= bound + 1e-30), "%s of expert %d beyond its fp32 bound" % (name, e)
         mp = -(-m // 128) * 128
@@ -270,8 +271,16 @@ def _stage_checks(cfg, dinp, f, wq, o, G, experts):
         n_r = _codes_explained(buf("dy_c", (P, h), torch.uint8)[r0:r1].cpu().numpy(),
                                buf("dy_s", (P, h // 32), torch.uint8)[r0:r1].cpu().numpy(), dy, bd["b_dy"],
                                "dY along h")
-        print("expert %d stages: gu, act, dact, dgu within bounds; x codes exact; dY codes differing %d (tokens), "
-              "%d (h) of %d, each explained" % (e, n_t, n_r, m * h), flush=True)
+        ac, asc = tok_codes("actT_c", "actT_s", F)
+        n_a = _codes_explained(ac, asc, pad(bd["hid"]), pad(bd["b_act"]), "act along the tokens")
+        gc, gs = tok_codes("dguT_c", "dguT_s", 2 * F)
+        n_gt = _codes_explained(gc, gs, pad(bd["da"]), pad(bd["b_da"]), "dgu along the tokens")
+        n_gr = _codes_explained(buf("dgu_c", (P, 2 * F), torch.uint8)[r0:r1].cpu().numpy(),
+                                buf("dgu_s", (P, 2 * F // 32), torch.uint8)[r0:r1].cpu().numpy(), bd["da"],
+                                bd["b_da"], "dgu along 2F")
+        print("expert %d stages: gu, dact within bounds; x codes exact; codes differing, each explained: dY %d "
+              "(tokens) %d (h) of %d, act %d of %d, dgu %d (tokens) %d (2F) of %d"
+              % (e, n_t, n_r, m * h, n_a, m * F, n_gt, n_gr, 2 * m * F), flush=True)
 
 
 def _beyond(got, ref, allow, terms):

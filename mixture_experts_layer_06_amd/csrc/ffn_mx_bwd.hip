@@ -350,10 +350,11 @@ __global__ __launch_bounds__(256) void mx_act_cols_kernel(const float *__restric
 // (1 - s)), du = dact g s, s = sigmoid(g), the expressions of the unfused
 // pass), quantised at once both ways: along 2F into row codes [P][2F] (for
 // the input gradient) and along the tokens into codes [2F][ld] (for the
-// first weight gradient). Tiles of 128 padded token rows x 64 columns of F:
-// the tile's 64 dg and 64 du columns in LDS, then each valid row's four
-// 32-column blocks and each column's four 32-row blocks; dgu itself is never
-// stored.
+// first weight gradient). Tiles of 128 padded token rows x 32 columns of F
+// (kDguCols): the tile's 32 dg and 32 du columns in LDS (35 KB, four blocks
+// per compute unit), then each valid row's two 32-column blocks and each
+// column's four 32-row blocks; dgu itself is never stored.
+constexpr int kDguCols = 32;
 __global__ __launch_bounds__(256) void mx_dgu_quant_kernel(const float *__restrict__ dact,
                                                            const float *__restrict__ gu, int F,
                                                            const int32_t *__restrict__ offs,
@@ -362,16 +363,16 @@ __global__ __launch_bounds__(256) void mx_dgu_quant_kernel(const float *__restri
                                                            uint8_t *__restrict__ row_scales,
                                                            uint8_t *__restrict__ tok_codes,
                                                            uint8_t *__restrict__ tok_scales) {
-    constexpr int kLd = 2 * kQtCols + 4;
+    constexpr int kLd = 2 * kDguCols + 4;
     __shared__ __attribute__((aligned(16))) float T[kQtRows * kLd];
     const int tid = threadIdx.x;
-    const int n0 = blockIdx.x * kQtCols, tb = blockIdx.y;
+    const int n0 = blockIdx.x * kDguCols, tb = blockIdx.y;
     int local, r0, nrows;
     if (!qt_tile(offs, poffs, nseg, ld, tb, local, r0, nrows)) return;
-    const int c = tid & 15, rr0 = tid >> 4;
+    const int c = tid & 7, rr0 = tid >> 3;   // 8 lanes of 4 columns per row, 32 rows per pass
 #pragma unroll
-    for (int i = 0; i < kQtRows / 16; ++i) {
-        const int li = local + rr0 + 16 * i;
+    for (int i = 0; i < kQtRows / 32; ++i) {
+        const int li = local + rr0 + 32 * i;
         float dg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, du[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (li < nrows) {
             const int64_t p = r0 + li;
@@ -387,20 +388,18 @@ __global__ __launch_bounds__(256) void mx_dgu_quant_kernel(const float *__restri
                 du[q] = da[q] * gv[q] * sg;
             }
         }
-        float *trow = T + (rr0 + 16 * i) * kLd + 4 * c;
+        float *trow = T + (rr0 + 32 * i) * kLd + 4 * c;
         *reinterpret_cast<float4 *>(trow) = make_float4(dg[0], dg[1], dg[2], dg[3]);
-        *reinterpret_cast<float4 *>(trow + kQtCols) = make_float4(du[0], du[1], du[2], du[3]);
+        *reinterpret_cast<float4 *>(trow + kDguCols) = make_float4(du[0], du[1], du[2], du[3]);
     }
     __syncthreads();
-    // along 2F: row i, block b (b < 2: dg columns n0 + 32 b .., else du)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int it = tid + 256 * h2;
-        const int i = it >> 2, b = it & 3;
+    // along 2F: row i, block b (0: the dg columns n0 .., 1: the du columns F + n0 ..)
+    {
+        const int i = tid >> 1, b = tid & 1;
         if (local + i < nrows) {
             float v[32];
             float amax = 0.0f;
-            const float *src = T + i * kLd + 32 * b;
+            const float *src = T + i * kLd + kDguCols * b;
 #pragma unroll
             for (int k = 0; k < 32; k += 4) {
                 const float4 f = *reinterpret_cast<const float4 *>(src + k);
@@ -408,19 +407,15 @@ __global__ __launch_bounds__(256) void mx_dgu_quant_kernel(const float *__restri
             }
 #pragma unroll
             for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(v[k]));
-            const int col0 = b < 2 ? n0 + 32 * b : F + n0 + 32 * (b - 2);
-            mx_store_block(v, amax, row_codes, row_scales, static_cast<int64_t>(r0 + local + i) * 2 * F + col0);
+            mx_store_block(v, amax, row_codes, row_scales,
+                           static_cast<int64_t>(r0 + local + i) * 2 * F + (b ? F + n0 : n0));
         }
     }
-    // along the tokens: wave w takes the 32-row block w of the tile's columns
+    // along the tokens: wave w takes the 32-row block w of the tile's 64 columns
     const int w = tid >> 6, lane = tid & 63;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int cc = lane + kQtCols * h2;
-        const int gcol = h2 == 0 ? n0 + lane : F + n0 + lane;
-        qt_col_block(T, kLd, cc, w, tok_codes, tok_scales,
-                     kQtRows * static_cast<int64_t>(tb) + static_cast<int64_t>(gcol) * ld + 32 * w);
-    }
+    const int gcol = lane < kDguCols ? n0 + lane : F + n0 + lane - kDguCols;
+    qt_col_block(T, kLd, lane, w, tok_codes, tok_scales,
+                 kQtRows * static_cast<int64_t>(tb) + static_cast<int64_t>(gcol) * ld + 32 * w);
 }
 
 // Rows of 32-blocks along K of a gathered, row-weighted source: row p of
@@ -620,7 +615,8 @@ extern "C" int moe_grouped_ffn_bwd_mx(const void *grad_out, const float *row_w, 
                           ws + L.dact, true, s, "moe_grouped_ffn_bwd_mx dact");
         if (st != MOE_OK) return st;
         // dgu quantised along 2F (rows) and along the tokens as it is formed
-        hipLaunchKernelGGL(mx_dgu_quant_kernel, qt_grid, dim3(256), 0, s, reinterpret_cast<const float *>(ws + L.dact),
+        hipLaunchKernelGGL(mx_dgu_quant_kernel, dim3(static_cast<unsigned>(F / kDguCols), qt_grid.y), dim3(256), 0, s,
+                           reinterpret_cast<const float *>(ws + L.dact),
                            static_cast<const float *>(gu), FF, offsets, poffs, E, L.ldT, ws + L.dgu_c, ws + L.dgu_s,
                            ws + L.dguT_c, ws + L.dguT_s);
         // dX = Q_2F(dgu) Q_2F(W1)

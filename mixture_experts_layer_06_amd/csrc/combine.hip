@@ -16,6 +16,8 @@
 // accesses, fp32 accumulation in a fixed order (j ascending), one rounding to
 // the output type. Reductions use a fixed shuffle tree, so results are
 // deterministic.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -87,7 +89,7 @@ __device__ __forceinline__ void store8_nt(float *p, const float *v) {
 // One thread per 8-element piece of an output row (a flat grid over
 // T x h/8 pieces): the k source pieces are all loaded before the fixed-order
 // weighted sum, so each thread keeps k loads in flight.
-template <typename TE>
+template <typename TE, int KM, bool WT>
 __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y, int h, int k,
                                                         const int32_t *__restrict__ row_of,
                                                         const float *__restrict__ topk_w,
@@ -96,33 +98,35 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= npieces) return;
     const int nv = h >> 3;
-    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    int t = static_cast<int>(idx / nv);
+    const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     const int64_t P = npieces / nv * k;   // rows of y
     const int64_t base = static_cast<int64_t>(t) * k;
     // indices without branches (slots past k re-read slot k - 1), then every
     // row piece loaded raw before any is used: one round trip per phase
-    int rows[8];
-    float w[8];
-    bool ok[8];
+    int rows[KM];
+    float w[KM];
+    bool ok[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KM; ++j) {
         rows[j] = row_of[base + (j < k ? j : k - 1)];
         w[j] = topk_w ? topk_w[base + (j < k ? j : k - 1)] : 1.0f;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KM; ++j) {
         ok[j] = j < k && rows[j] >= 0 && rows[j] < P;
         rows[j] = ok[j] ? rows[j] : 0;
     }
-    Raw8<TE> yr[8];
+    Raw8<TE> yr[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < k) raw8_load_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yr[j]);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < k) {
             float yv[8];
             raw8_f32(yr[j], yv);
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(1024) void unpermute_bwd_kernel(
 
 // One thread per 8-element piece (flat grid over T x h/8): the k pieces of
 // grad_x_perm and the router term's gate pieces are loaded before use.
-template <typename TE>
+template <typename TE, int KM, bool WT>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(
     const TE *__restrict__ gxp, int h, int k, const int32_t *__restrict__ row_of,
     const float *__restrict__ gl, const int32_t *__restrict__ topk_idx,
@@ -215,7 +219,9 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= npieces) return;
     const int nv = h >> 3;
-    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    int t = static_cast<int>(idx / nv);
+    const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     const int64_t P = npieces / nv * k;   // rows of grad_x_perm
     const int64_t base = static_cast<int64_t>(t) * k;
     // every load of a phase is issued before any of its values is used (k is
@@ -223,45 +229,45 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     // clamped to a valid address and their terms dropped by a select), so
     // the phases cost one memory round trip each
     // index loads without branches: slots past k re-read slot k - 1
-    int rows[8], ex[8];
-    float dl[8];
+    int rows[KM], ex[KM];
+    float dl[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rows[j] = row_of[base + (j < k ? j : k - 1)];
+    for (int j = 0; j < KM; ++j) rows[j] = row_of[base + (j < k ? j : k - 1)];
     if (gl) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < KM; ++j) {
             ex[j] = topk_idx[base + (j < k ? j : k - 1)];
             dl[j] = gl[base + (j < k ? j : k - 1)];
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < KM; ++j) {
             ex[j] = -1;
             dl[j] = 0.0f;
         }
     }
-    bool rok[8], eok[8];
+    bool rok[KM], eok[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KM; ++j) {
         rok[j] = j < k && rows[j] >= 0 && rows[j] < P;
         eok[j] = j < k && ex[j] >= 0 && ex[j] < E;
         rows[j] = rok[j] ? rows[j] : 0;
         ex[j] = eok[j] ? ex[j] : 0;
     }
-    Raw8<TE> d[8], wr[8];
+    Raw8<TE> d[KM], wr[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < k) raw8_load_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
     if (gl) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < KM; ++j)
             if (j < k) raw8_load(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wr[j]);
     }
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < k) {
             float dv[8];
             raw8_f32(d[j], dv);
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
         }
     if (gl) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < KM; ++j)
             if (j < k) {
                 float wv[8];
                 raw8_f32(wr[j], wv);
@@ -283,25 +289,43 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
 
 // Unweighted combine backward: grad_y[row_of[t,j]] = grad_out[t] for every
 // j, one 8-element piece of grad_out per thread (loaded once, stored k times).
-template <typename TE>
+template <typename TE, int KM, bool WT>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const TE *__restrict__ gout, int h, int k,
                                                            const int32_t *__restrict__ row_of, TE *__restrict__ gy,
                                                            int64_t npieces) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= npieces) return;
     const int nv = h >> 3;
-    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    int t = static_cast<int>(idx / nv);
+    const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     const int64_t P = npieces / nv * k;
     // the piece and all k row indices in flight together (slots past k
     // re-read slot k - 1 and store nothing)
-    int rows[8];
+    int rows[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
+    for (int j = 0; j < KM; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
     float g[8];
     load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < k && rows[j] >= 0 && rows[j] < P) store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, g);
+}
+
+// f(KM, WT) with KM the top-k slots a thread walks (k rounded up to 1, 2, 4
+// or 8; slots past k re-read slot k - 1 and add nothing) and WT whether each
+// wave's 64 pieces belong to one token (h / 8 a multiple of 64), so that the
+// token's indices and weights are wave-uniform and read by scalar loads.
+template <typename Fn>
+void with_slots(int k, int64_t h, Fn &&f) {
+    auto go = [&](auto km) {
+        if ((h / 8) % 64 == 0) f(km, std::true_type{});
+        else f(km, std::false_type{});
+    };
+    if (k <= 1) go(std::integral_constant<int, 1>{});
+    else if (k <= 2) go(std::integral_constant<int, 2>{});
+    else if (k <= 4) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, 8>{});
 }
 
 int check_common(const char *fn, int dtype, int64_t T, int64_t h, int k) {
@@ -332,14 +356,18 @@ extern "C" int moe_unpermute(const void *y, int dtype, int64_t T, int64_t h, int
     hipStream_t s = as_stream(stream);
     const int64_t npieces = T * (h / 8);
     const dim3 grid(static_cast<unsigned>((npieces + 255) / 256)), block(256);
-    if (dtype == MOE_DTYPE_BF16)
-        hipLaunchKernelGGL(unpermute_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t *>(y),
-                           static_cast<int>(h), k, row_of, topk_w,
-                           static_cast<const bf16_t *>(y_sh), static_cast<bf16_t *>(out), npieces);
-    else
-        hipLaunchKernelGGL(unpermute_kernel<float>, grid, block, 0, s, static_cast<const float *>(y),
-                           static_cast<int>(h), k, row_of, topk_w, static_cast<const float *>(y_sh),
-                           static_cast<float *>(out), npieces);
+    with_slots(k, h, [&](auto km, auto wt) {
+        constexpr int KM = decltype(km)::value;
+        constexpr bool WT = decltype(wt)::value;
+        if (dtype == MOE_DTYPE_BF16)
+            hipLaunchKernelGGL((unpermute_kernel<bf16_t, KM, WT>), grid, block, 0, s, static_cast<const bf16_t *>(y),
+                               static_cast<int>(h), k, row_of, topk_w, static_cast<const bf16_t *>(y_sh),
+                               static_cast<bf16_t *>(out), npieces);
+        else
+            hipLaunchKernelGGL((unpermute_kernel<float, KM, WT>), grid, block, 0, s, static_cast<const float *>(y),
+                               static_cast<int>(h), k, row_of, topk_w, static_cast<const float *>(y_sh),
+                               static_cast<float *>(out), npieces);
+    });
     return check_launch("moe_unpermute");
 }
 
@@ -358,12 +386,18 @@ extern "C" int moe_unpermute_bwd(const void *grad_out, const void *y, int dtype,
         hipStream_t s = as_stream(stream);
         const int64_t npieces = T * (h / 8);
         const dim3 grid(static_cast<unsigned>((npieces + 255) / 256)), block(256);
-        if (dtype == MOE_DTYPE_BF16)
-            hipLaunchKernelGGL(scatter_rows_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t *>(grad_out),
-                               static_cast<int>(h), k, row_of, static_cast<bf16_t *>(grad_y), npieces);
-        else
-            hipLaunchKernelGGL(scatter_rows_kernel<float>, grid, block, 0, s, static_cast<const float *>(grad_out),
-                               static_cast<int>(h), k, row_of, static_cast<float *>(grad_y), npieces);
+        with_slots(k, h, [&](auto km, auto wt) {
+            constexpr int KM = decltype(km)::value;
+            constexpr bool WT = decltype(wt)::value;
+            if (dtype == MOE_DTYPE_BF16)
+                hipLaunchKernelGGL((scatter_rows_kernel<bf16_t, KM, WT>), grid, block, 0, s,
+                                   static_cast<const bf16_t *>(grad_out), static_cast<int>(h), k, row_of,
+                                   static_cast<bf16_t *>(grad_y), npieces);
+            else
+                hipLaunchKernelGGL((scatter_rows_kernel<float, KM, WT>), grid, block, 0, s,
+                                   static_cast<const float *>(grad_out), static_cast<int>(h), k, row_of,
+                                   static_cast<float *>(grad_y), npieces);
+        });
         return check_launch("moe_unpermute_bwd");
     }
     MOE_CHECK_ARG(aligned16(grad_out) && aligned16(y) && aligned16(grad_y), MOE_ERR_INVALID_ARG,
@@ -403,15 +437,19 @@ extern "C" int moe_permute_bwd(const void *grad_x_perm, int dtype, int64_t T, in
     hipStream_t s = as_stream(stream);
     const int64_t npieces = T * (h / 8);
     const dim3 grid(static_cast<unsigned>((npieces + 255) / 256)), block(256);
-    if (dtype == MOE_DTYPE_BF16)
-        hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, grid, block, 0, s,
-                           static_cast<const bf16_t *>(grad_x_perm), static_cast<int>(h), k, row_of,
-                           grad_logits_sel, topk_idx, static_cast<const bf16_t *>(w_gate), E,
-                           static_cast<bf16_t *>(grad_x), npieces);
-    else
-        hipLaunchKernelGGL(permute_bwd_kernel<float>, grid, block, 0, s,
-                           static_cast<const float *>(grad_x_perm), static_cast<int>(h), k, row_of,
-                           grad_logits_sel, topk_idx, static_cast<const float *>(w_gate), E,
-                           static_cast<float *>(grad_x), npieces);
+    with_slots(k, h, [&](auto km, auto wt) {
+        constexpr int KM = decltype(km)::value;
+        constexpr bool WT = decltype(wt)::value;
+        if (dtype == MOE_DTYPE_BF16)
+            hipLaunchKernelGGL((permute_bwd_kernel<bf16_t, KM, WT>), grid, block, 0, s,
+                               static_cast<const bf16_t *>(grad_x_perm), static_cast<int>(h), k, row_of,
+                               grad_logits_sel, topk_idx, static_cast<const bf16_t *>(w_gate), E,
+                               static_cast<bf16_t *>(grad_x), npieces);
+        else
+            hipLaunchKernelGGL((permute_bwd_kernel<float, KM, WT>), grid, block, 0, s,
+                               static_cast<const float *>(grad_x_perm), static_cast<int>(h), k, row_of,
+                               grad_logits_sel, topk_idx, static_cast<const float *>(w_gate), E,
+                               static_cast<float *>(grad_x), npieces);
+    });
     return check_launch("moe_permute_bwd");
 }

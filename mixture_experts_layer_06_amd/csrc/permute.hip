@@ -16,6 +16,7 @@
 //   4. copy: each token row is read once from HBM and written to its k
 //      permuted rows with 16-byte accesses.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ t
 // One thread per 16-byte piece of a token row (a flat grid over T x pieces):
 // the piece is read once and stored to the token's k rows of x_perm (rows
 // outside [0, T k) are skipped).
-template <typename TE>
+template <typename TE, int KM, bool WT>
 __global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x, int h, int k,
                                                         const int32_t *__restrict__ row_of,
                                                         TE *__restrict__ x_perm, int64_t npieces) {
@@ -121,19 +122,22 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= npieces) return;
     const int nv = h / kVec;
-    const int t = static_cast<int>(idx / nv), v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
-    // the piece and all k row indices in flight together (slots past k
-    // re-read slot k - 1 and store nothing)
-    int rows[8];
+    int t = static_cast<int>(idx / nv);
+    const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
+    if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
+    // the piece and the row indices of the KM top-k slots in flight together
+    // (KM = k rounded up to 1, 2, 4 or 8; slots past k re-read slot k - 1
+    // and store nothing)
+    int rows[KM];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
+    for (int j = 0; j < KM; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
     const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * h) + v);
     // the piece is waited for here, once: a wait inside the conditional
     // stores below would, with the in-order memory counter, also wait for
     // the stores issued before it
     __asm__ volatile("" ::"v"(d));
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < k && rows[j] >= 0 && static_cast<int64_t>(rows[j]) < npieces / nv * k)
             __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(rows[j]) * h) + v);
 }
@@ -203,14 +207,25 @@ int permute_launch(const void *x, int dtype, int64_t T, int64_t h, int E, int k,
         hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(256), 0, s, topk_idx, static_cast<int>(T), E,
                            k, blockbase, P, row_of, sorted_token);
     if (x_perm && T > 0) {
-        if (dtype == MOE_DTYPE_BF16)
-            hipLaunchKernelGGL(copy_rows_kernel<bf16_t>, dim3(static_cast<unsigned>((T * (h / 8) + 255) / 256)),
-                               dim3(256), 0, s, static_cast<const bf16_t *>(x), static_cast<int>(h), k, row_of,
-                               static_cast<bf16_t *>(x_perm), T * (h / 8));
-        else
-            hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(static_cast<unsigned>((T * (h / 4) + 255) / 256)),
-                               dim3(256), 0, s, static_cast<const float *>(x), static_cast<int>(h), k, row_of,
-                               static_cast<float *>(x_perm), T * (h / 4));
+        const int64_t nv = dtype == MOE_DTYPE_BF16 ? h / 8 : h / 4;   // 16-byte pieces per row
+        auto go = [&](auto km) {
+            constexpr int KM = decltype(km)::value;
+            const dim3 grid(static_cast<unsigned>((T * nv + 255) / 256));
+            const bool wt = nv % 64 == 0;   // each wave's pieces in one token
+            if (dtype == MOE_DTYPE_BF16) {
+                auto kfn = wt ? copy_rows_kernel<bf16_t, KM, true> : copy_rows_kernel<bf16_t, KM, false>;
+                hipLaunchKernelGGL(kfn, grid, dim3(256), 0, s, static_cast<const bf16_t *>(x), static_cast<int>(h), k,
+                                   row_of, static_cast<bf16_t *>(x_perm), T * nv);
+            } else {
+                auto kfn = wt ? copy_rows_kernel<float, KM, true> : copy_rows_kernel<float, KM, false>;
+                hipLaunchKernelGGL(kfn, grid, dim3(256), 0, s, static_cast<const float *>(x), static_cast<int>(h), k,
+                                   row_of, static_cast<float *>(x_perm), T * nv);
+            }
+        };
+        if (k <= 1) go(std::integral_constant<int, 1>{});
+        else if (k <= 2) go(std::integral_constant<int, 2>{});
+        else if (k <= 4) go(std::integral_constant<int, 4>{});
+        else go(std::integral_constant<int, 8>{});
     }
     return check_launch(name);
 }

@@ -1,0 +1,96 @@
+"""The row kernels of the dispatch and the combine, forward and backward,
+through the C-ABI on seeded inputs, over the top-k slot counts the kernels
+are built for (k rounded up to 1, 2, 4 or 8: k = 1, 3, 6, 8) and both
+token layouts: h a multiple of 512, where each wave's pieces belong to one
+token and its indices are read by scalar loads, and h = 192, where a wave
+spans several tokens. References: the oracle's permutation, combine and
+router gradient; gathers and scatters are exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import TOL, rel_err, rel_err_tensor, to_np32
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(192, 3), (512, 1), (512, 3), (1024, 6), (512, 8), (64, 2)]
+
+
+def _routing(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    return idx, w, oracle.permutation(idx, E)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("h,k", SHAPES)
+def test_dispatch_copy_and_combine(moe_lib, h, k, dtype):
+    """x_perm rows are exactly the tokens' rows in the oracle's order; the
+    combine of seeded expert rows (plus a shared row) matches the oracle."""
+    from mixture_experts_layer_06_amd import binding as B
+    T, E = 131, 12
+    print("case rows", h, k, dtype, flush=True)
+    idx, w, perm = _routing(T, E, k, seed=h + k)
+    g = torch.Generator().manual_seed(h * 10 + k)
+    x = torch.randn(T, h, generator=g).to(dtype)
+    p = B.moe_permute(x.cuda(), torch.as_tensor(idx).cuda(), E)
+    torch.cuda.synchronize()
+    assert np.array_equal(p["sorted_token"].cpu().numpy(), perm["sorted_token"])
+    assert np.array_equal(p["row_of"].cpu().numpy(), perm["row_of"])
+    assert torch.equal(p["x_perm"].cpu(), x[torch.as_tensor(perm["sorted_token"]).long()])
+    y = torch.randn(T * k, h, generator=g).to(dtype)
+    y_sh = torch.randn(T, h, generator=g).to(dtype)
+    out = B.moe_unpermute(y.cuda(), p["row_of"], torch.as_tensor(w).cuda(), y_sh=y_sh.cuda())
+    ref = oracle.combine(to_np32(y), perm["row_of"], w, to_np32(y_sh))
+    tol = TOL["bf16" if dtype == torch.bfloat16 else "f32"]
+    assert rel_err(to_np32(out), ref) <= tol
+
+
+@pytest.mark.parametrize("h,k", SHAPES)
+def test_combine_backward_and_dispatch_backward(moe_lib, h, k):
+    """Weighted combine backward: grad_y[row_of[t, j]] = w[t, j] grad_out[t]
+    and grad_w[t, j] = <grad_out[t], y[row_of[t, j]]>; unweighted: grad_y
+    rows are exact copies; dispatch backward: grad_x[t] = sum_j
+    grad_x_perm[row_of[t, j]] plus the router term of the oracle's
+    router_grads for the selected logits' gradients."""
+    from mixture_experts_layer_06_amd import binding as B
+    T, E = 131, 12
+    print("case rows bwd", h, k, flush=True)
+    idx, w, perm = _routing(T, E, k, seed=7 * h + k)
+    row_of = perm["row_of"].astype(np.int32)
+    g = torch.Generator().manual_seed(h + 100 * k)
+    gout = torch.randn(T, h, generator=g).to(torch.bfloat16)
+    y = torch.randn(T * k, h, generator=g).to(torch.bfloat16)
+    rw = torch.as_tensor(row_of).cuda()
+    gy, gw = B.moe_unpermute_bwd(gout.cuda(), y.cuda(), rw, torch.as_tensor(w).cuda())
+    go64, y64 = to_np32(gout).astype(np.float64), to_np32(y).astype(np.float64)
+    gy_ref = np.zeros((T * k, h))
+    gw_ref = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            gy_ref[row_of[t, j]] = w[t, j] * go64[t]
+            gw_ref[t, j] = go64[t] @ y64[row_of[t, j]]
+    assert rel_err(to_np32(gy), gy_ref) <= TOL["bf16"]
+    # fp32 sums of exact bf16 products: within a few units of fp32 rounding
+    # of the largest weight gradient
+    assert rel_err_tensor(gw.cpu().numpy(), gw_ref) <= 1e-5
+    gy_plain, gw_none = B.moe_unpermute_bwd(gout.cuda(), None, rw, None)
+    assert gw_none is None
+    assert torch.equal(gy_plain.cpu(), gout[torch.as_tensor(perm["sorted_token"]).long()])
+    gxp = torch.randn(T * k, h, generator=g).to(torch.bfloat16)
+    gl = torch.randn(T, k, generator=g)
+    wg = (torch.randn(E, h, generator=g) / 8).to(torch.bfloat16)
+    gx = B.moe_permute_bwd(gxp.cuda(), rw, gl.cuda(), torch.as_tensor(idx).cuda(), wg.cuda())
+    D = np.zeros((T, E))
+    for t in range(T):
+        D[t, idx[t]] = gl[t].numpy()
+    gx_ref = oracle.router_grads(np.zeros((T, h)), to_np32(wg), D)["dx"]
+    gxp64 = to_np32(gxp).astype(np.float64)
+    for j in range(k):
+        gx_ref = gx_ref + gxp64[row_of[:, j]]
+    assert rel_err(to_np32(gx), gx_ref) <= TOL["bf16"]
+    gx_plain = B.moe_permute_bwd(gxp.cuda(), rw)
+    ref_plain = sum(gxp64[row_of[:, j]] for j in range(k))
+    assert rel_err(to_np32(gx_plain), ref_plain) <= TOL["bf16"]

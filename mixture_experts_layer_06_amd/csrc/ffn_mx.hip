@@ -29,6 +29,9 @@
 //   quantises the fp32 activation along F (and optionally also stores it in
 //   bf16), then the second projection on those codes (bf16 expert outputs).
 //   Tokens enter quantised along h, optionally gathered.
+// * mx_gemm_rows / mx_gemm_kseg (for the backward in ffn_mx_bwd.hip): the
+//   same tile body by token segments with an fp32 or bf16 epilogue, and by
+//   per-expert k-ranges of shared operands (weight gradients, fp32).
 #include <type_traits>
 
 #include "mx_common.hpp"
@@ -204,21 +207,6 @@ __device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileI
     }
 }
 
-// One tile over all k-steps. Each k-step t runs two halves (k-subs s = 0,
-// 1) of NI x NJ scaled MFMAs, weight-subtile-major. Fragments stream one
-// weight subtile ahead: during the MFMAs of weight subtile i the next weight
-// fragment is read, and one (half tile: two) of the token fragments of the
-// next k-sub, so a half ends with the next k-sub's token fragments and its
-// first weight fragment in registers (80 fragment VGPRs instead of 128 for
-// two full sets). Half 0 also writes k-step t+1 (held in VGPRs) to the
-// other stage and loads k-step t+2 and the scales of k-step t+1; then this
-// wave's LDS traffic is waited for and the block synchronises; half 1 reads
-// the next k-sub from the other stage. Half 1 still reads the current
-// stage (its weight fragments), so each k-step starts with a second block
-// synchronisation before that stage is written again. Weight rows and (without gathering)
-// token rows are addressed as one per-lane offset plus a per-row-group
-// scalar offset, through buffer resources bounded to the tile's valid rows
-// (rows past them read as zeros and are never stored).
 // The staging registers of one k-step: 8 weight chunks, XJ token chunks and
 // the two scale words of this thread.
 template <int XJ>
@@ -304,6 +292,22 @@ struct MxTileSrc {
     }
 };
 
+// One tile over all k-steps. Each k-step t runs two halves (k-subs s = 0,
+// 1) of NI x NJ scaled MFMAs, weight-subtile-major. Fragments stream one
+// weight subtile ahead: during the MFMAs of weight subtile i the next weight
+// fragment is read, and one (half tile: two) of the token fragments of the
+// next k-sub, so a half ends with the next k-sub's token fragments and its
+// first weight fragment in registers (80 fragment VGPRs instead of 128 for
+// two full sets). Half 0 also writes k-step t+1 (held in VGPRs) to the
+// other stage and loads k-step t+2 and the scales of k-step t+1, one
+// staging item after each MFMA slot in a fixed order; then this wave's LDS
+// traffic is waited for and the block synchronises; half 1 reads the next
+// k-sub from the other stage. Half 1 still reads the current stage (its
+// weight fragments), so each k-step starts with a second block
+// synchronisation before that stage is written again. Weight rows and
+// (without gathering) token rows are addressed as one per-lane offset plus
+// a per-row-group scalar offset, through buffer resources bounded to the
+// tile's valid rows (rows past them read as zeros and are never stored).
 // k-steps k0 + t for t < nreal, then (t >= nreal, when nks > nreal) the
 // k-step kzero, which holds zero codes and scales: a product of zeros adds
 // exactly nothing, so a tile may run an even number of steps.

@@ -137,11 +137,9 @@ __device__ __forceinline__ void store_tile_mx_swiglu(const GGArgs &a, const Tile
             const int ex = mx_block_exponent(amax);
             uint32_t c[4];
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                c[gq] = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) c[gq] |= e4m3_code(ldexpf(hv[4 * gq + q], -ex)) << (8 * q);
-            }
+            for (int gq = 0; gq < 4; ++gq)
+                c[gq] = e4m3_word(ldexpf(hv[4 * gq], -ex), ldexpf(hv[4 * gq + 1], -ex), ldexpf(hv[4 * gq + 2], -ex),
+                                  ldexpf(hv[4 * gq + 3], -ex));
             // half 0 keeps columns 0..15 (its gq 0, 1 and the partner's), half 1
             // columns 16..31 (gq 2, 3)
             const uint32_t r0 = __shfl_xor(lhi ? c[0] : c[2], 32);

@@ -127,9 +127,8 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_kernel(const TE *__restr
     u32x4 out[2];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) word |= e4m3_code(ldexpf(v[4 * w + q], -ex)) << (8 * q);
+        const uint32_t word = e4m3_word(ldexpf(v[4 * w], -ex), ldexpf(v[4 * w + 1], -ex),
+                                        ldexpf(v[4 * w + 2], -ex), ldexpf(v[4 * w + 3], -ex));
         out[w >> 2][w & 3] = word;
     }
     const int64_t ce = cbase + static_cast<int64_t>(n) * ld;
@@ -244,9 +243,8 @@ __global__ __launch_bounds__(256) void mx_quantize_cols_tile_kernel(const TE *__
     u32x4 out[2];
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) word |= e4m3_code(ldexpf(v[4 * wd + k], -ex)) << (8 * k);
+        const uint32_t word = e4m3_word(ldexpf(v[4 * wd], -ex), ldexpf(v[4 * wd + 1], -ex),
+                                        ldexpf(v[4 * wd + 2], -ex), ldexpf(v[4 * wd + 3], -ex));
         out[wd >> 2][wd & 3] = word;
     }
     const int64_t ce = cbase + static_cast<int64_t>(n0 + lane) * ld + 32 * w;
@@ -287,9 +285,8 @@ __device__ __forceinline__ void mx_store_block(const float (&v)[32], float amax,
     u32x4 out[2];
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) word |= e4m3_code(ldexpf(v[4 * wd + k], -ex)) << (8 * k);
+        const uint32_t word = e4m3_word(ldexpf(v[4 * wd], -ex), ldexpf(v[4 * wd + 1], -ex),
+                                        ldexpf(v[4 * wd + 2], -ex), ldexpf(v[4 * wd + 3], -ex));
         out[wd >> 2][wd & 3] = word;
     }
     u32x4 *dst = reinterpret_cast<u32x4 *>(codes + ce);
@@ -446,9 +443,8 @@ __global__ __launch_bounds__(256) void mx_quantize_rows_gather_kernel(const TE *
     u32x4 out[2];
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) word |= e4m3_code(ldexpf(v[4 * wd + q], -ex)) << (8 * q);
+        const uint32_t word = e4m3_word(ldexpf(v[4 * wd], -ex), ldexpf(v[4 * wd + 1], -ex),
+                                        ldexpf(v[4 * wd + 2], -ex), ldexpf(v[4 * wd + 3], -ex));
         out[wd >> 2][wd & 3] = word;
     }
     u32x4 *dst = reinterpret_cast<u32x4 *>(codes + b * 32);

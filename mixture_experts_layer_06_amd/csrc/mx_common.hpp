@@ -14,23 +14,19 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// E4M3 code of |y| < 2^9 given as fp32 (exact scaled value), sign apart.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const uint32_t s = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (a >= 448.0f) return s | 0x7eu;                       // saturate (all of [448, 512) rounds to 448)
-    if (a < 0.015625f) return s | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // subnormals; 8 = 2^-6
-    const uint32_t b = __float_as_uint(a);
-    int e = static_cast<int>(b >> 23) - 127;                 // -6 .. 8
-    const uint32_t mant = b & 0x7fffffu;
-    uint32_t m = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, nearest-even
-    if (m == 8) {
-        m = 0;
-        ++e;
-    }
-    uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | m;
-    if (code > 0x7eu) code = 0x7eu;
-    return s | code;
+// E4M3 codes of four values y (fp32, the exact scaled values, |y| < 2^9),
+// packed little-endian into a word: the hardware's round-to-nearest-even
+// conversion (v_cvt_pk_fp8_f32, two values per instruction), with each
+// value clamped to +-448 first, so that (464, 512) saturates to 448 like
+// the rest of [448, 512) (alone, the conversion rounds it to 480, which
+// E4M3 has no code for, and returns the NaN code). Checked on the device
+// against a bitwise reference rounding for every fp32 in [0, 512) and its
+// negative: equal everywhere (subnormals and signed zeros included).
+// Finite inputs only.
+__device__ __forceinline__ float e4m3_clamp(float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); }
+__device__ __forceinline__ uint32_t e4m3_word(float y0, float y1, float y2, float y3) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(y0), e4m3_clamp(y1), 0, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(y2), e4m3_clamp(y3), lo, true));
 }
 
 // Shared exponent of a block whose largest magnitude is amax (>= 0):
@@ -59,9 +55,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const TE *__restrict__
     u32x4 out[2];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) word |= e4m3_code(ldexpf(v[4 * w + q], -ex)) << (8 * q);
+        const uint32_t word = e4m3_word(ldexpf(v[4 * w], -ex), ldexpf(v[4 * w + 1], -ex),
+                                        ldexpf(v[4 * w + 2], -ex), ldexpf(v[4 * w + 3], -ex));
         out[w >> 2][w & 3] = word;
     }
     u32x4 *dst = reinterpret_cast<u32x4 *>(codes + b * 32);

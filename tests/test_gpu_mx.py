@@ -60,6 +60,34 @@ def test_quantize_bit_exact(moe_lib, dtype):
     assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], rc[bad][:5])
 
 
+@pytest.mark.parametrize("lo", [256.0, 1.0, 2.0 ** -7, 2.0 ** -10])
+def test_quantize_whole_binade(moe_lib, lo):
+    """Every fp32 value of the binade [lo, 2 lo), both signs, quantised with
+    the block scale fixed at 2^0 (each block of 32 holds 31 sweep values and
+    the anchor 300): the elements are then the values themselves, so this
+    covers every input of the E4M3 rounding in that binade. The binades: the
+    top one (saturation of (448, 512) included), one of the normal range,
+    the top subnormal one (rounding up into the smallest normal 2^-6) and
+    the one rounding to the smallest subnormal 2^-9 or to zero."""
+    first = np.float32(lo).view(np.uint32)
+    sweep = (first + np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
+    n = sweep.size // 31 * 31
+    tail = sweep[n:]
+    blocks = np.concatenate([sweep[:n].reshape(-1, 31), np.pad(tail, (0, 31 - tail.size))[None]])
+    blocks = np.pad(blocks, ((0, -blocks.shape[0] % 8), (0, 0)))
+    v = np.concatenate([blocks, np.full((blocks.shape[0], 1), np.float32(300.0))], axis=1)
+    v[1::2] *= -1
+    v = v.reshape(-1, 256)                          # rows of 8 blocks
+    print("case binade", lo, v.shape, flush=True)
+    codes, scales = moe_lib.moe_mx_quantize(torch.as_tensor(v).cuda())
+    rc, rs = oracle.mx_quantize(v.astype(np.float64))
+    assert (rs == 127).all()
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    got = codes.cpu().numpy()
+    bad = np.nonzero(got != rc)
+    assert bad[0].size == 0, (v[bad][:5], got[bad][:5], rc[bad][:5])
+
+
 def test_quantize_weights_bit_exact(moe_lib):
     """The Mixtral-shaped layer's first expert matrix (14336 x 2 rows of
     4096), quantised along h."""

@@ -47,6 +47,7 @@ constexpr int kMxTile = 256;
 constexpr int kMxRegion = kMxTile * kMxBK;   // bytes of one operand region of a stage
 constexpr int kMxStage = 2 * kMxRegion;
 constexpr int kMxScaleBytes = 2 * kMxTile * 4;   // per stage: a scale word per weight row and per token row
+constexpr int kModeF32T = 4;   // fp32 out, stored transposed (the k-segment products)
 
 static_assert(kMxBK == 128, "mswz assumes 128-byte rows");
 
@@ -202,6 +203,39 @@ __device__ __forceinline__ void store_tile_mx_plain(const GGArgs &a, const TileI
                 }
             }
         }
+    }
+}
+
+// Epilogue of a k-segment tile, stored transposed in fp32: the weight-slot
+// row is the row of C (rows crow0 + n_tile * 256 + ...) and the token-slot
+// row its column (pitch ti.M). A lane's accumulators run down one column, so
+// each dword store writes two whole 128-byte lines (32 consecutive columns of
+// rows r and r + 4), and the four stores of a row's 512 bytes follow each
+// other. (Stored untransposed, each 16-byte store touched 32 rows.) The
+// stores are non-temporal: nothing reads the gradients back in this pass.
+template <bool HALF>
+__device__ __forceinline__ void store_tile_mx_t(const GGArgs &a, const TileInfo &ti,
+                                                floatx16 (&acc)[HALF ? 2 : 4][4], int wave, int lane,
+                                                int64_t crow0) {
+    constexpr int NI = HALF ? 2 : 4, NJ = 4;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int wrow0 = HALF ? wave * 64 : (wave & 1) * 128;
+    const int tok0 = HALF ? 0 : (wave >> 1) * 128;
+    const int cols = min(kMxTile, ti.M - ti.m0);
+    float *C = static_cast<float *>(a.C);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r0 = ti.n_tile * kMxTile + wrow0 + i * 32;
+        if (r0 >= a.N_out) continue;   // N_out % 32 == 0: whole subtiles
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float *dst = C + (crow0 + r0 + 8 * gq + 4 * lhi + q) * ti.M + ti.m0 + tok0 + l32;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    if (tok0 + j * 32 + l32 < cols) __builtin_nontemporal_store(acc[i][j][4 * gq + q], dst + j * 32);
+            }
     }
 }
 
@@ -476,6 +510,7 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
         return;
     }
     if constexpr (MODE == kModeSwiGLU) store_tile_mx_swiglu<HALF>(a, ti, acc, wave, lane, crow0);
+    else if constexpr (MODE == kModeF32T) store_tile_mx_t<HALF>(a, ti, acc, wave, lane, crow0);
     else store_tile_mx_plain<MODE, HALF>(a, ti, acc, wave, lane, crow0);
 }
 
@@ -554,39 +589,65 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
     }
 }
 
-// Weight gradients by k-segments: A [M][K] and B [N_out][K] are shared by all
-// experts (K: the row stride, the padded token count); expert e reduces over
-// its k-steps [poffs[e], poffs[e+1]) / 128 into C[e] = A B^T, [M][N_out] in
-// fp32 (zeros for an expert without tokens). Tile w: expert w / (mt nt),
-// then row tile, then column tile; the tile body is the rows mode's, with
-// the expert's k-range and its output rows e M + m. An odd number of
-// k-steps is completed by one step on the zero k-step kzero (the last 128
-// columns of A and B), so the kernel holds the even tile body only; half
-// tiles (128 rows of A) only when M % 256 != 0 (HALF_TAIL).
+// Weight gradients by k-segments: the token-slot operand A [M][K] and the
+// weight-slot operand B [N_out][K] are shared by all experts (K: the row
+// stride, the padded token count); expert e reduces over its k-steps
+// [poffs[e], poffs[e+1]) / 128 into C[e] = B A^T, [N_out][M] in fp32 (zeros
+// for an expert without tokens), stored by the transposed epilogue. Tile
+// order: the experts by decreasing k-range, then groups of 4 weight-slot
+// tiles (rows of C), then the token-slot tile (columns of C), then the
+// weight-slot tile within the group; the tile body is the rows mode's, with
+// the expert's k-range. An odd number of k-steps is completed by one step on
+// the zero k-step kzero (the last 128 columns of A and B), so the kernel
+// holds the even tile body only; half tiles (128 rows of A) only when
+// M % 256 != 0 (HALF_TAIL).
 template <bool HALF_TAIL>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_mx_kseg(MXArgs x, const int32_t *poffs, int M, int kzero) {
     __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage + kMxScaleBytes];
     __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage + kMxScaleBytes];
+    __shared__ int s_order[256], s_len[256];
+    const int tid = threadIdx.x;
+    // experts by decreasing k-range (ties: lower index first)
+    s_len[tid] = tid < x.g.E ? poffs[tid + 1] - poffs[tid] : -1;
+    __syncthreads();
+    if (tid < x.g.E) {
+        const int m = s_len[tid];
+        int rank = 0;
+        for (int e = 0; e < x.g.E; ++e) rank += (s_len[e] > m) || (s_len[e] == m && e < tid);
+        s_order[rank] = tid;
+    }
+    __syncthreads();
     const int m_tiles = (M + kMxTile - 1) / kMxTile;
     const int per = m_tiles * x.g.n_tiles;
     const int total = x.g.E * per;
-    for (int w = xcd_block_index(blockIdx.x, x.g.grid); w < total; w += x.g.grid) {
-        const int e = w / per, r = w - e * per;
-        const int mt = r / x.g.n_tiles;
+    const int G = x.g.grid, slot = xcd_block_index(blockIdx.x, G);
+    for (int w0 = 0; w0 < total; w0 += G) {
+        // every other round of tiles in reverse block order, so that a block
+        // that took a heavy expert's tile takes a light one next
+        const int w = ((w0 / G) & 1) ? w0 + G - 1 - slot : w0 + slot;
+        if (w >= total) continue;
+        // groups of 4 weight-slot tiles by every token-slot tile, column by
+        // column: the 32 tiles an XCD runs at a time (consecutive w) form a
+        // 4 x 8 block and share 12 operand panels per k-step
+        const int eo = w / per, r = w - eo * per;
+        const int e = s_order[eo];
+        const int g = r / (4 * m_tiles), rg = r - g * (4 * m_tiles);
+        const int gn = min(x.g.n_tiles - 4 * g, 4);
+        const int mt = rg / gn;
         TileInfo ti;
         ti.seg = 0;
         ti.m0 = mt * kMxTile;
-        ti.n_tile = r - mt * x.g.n_tiles;
+        ti.n_tile = 4 * g + (rg - mt * gn);
         ti.M = M;
         ti.row0 = 0;
         ti.shared = false;
         const int k0 = poffs[e] / kMxBK, nks = (poffs[e + 1] - poffs[e]) / kMxBK;
-        const int64_t crow0 = static_cast<int64_t>(e) * M + ti.m0;
+        const int64_t crow0 = static_cast<int64_t>(e) * x.g.N_out;
         const int nrun = nks + (nks & 1);
         if (HALF_TAIL && M - ti.m0 <= kMxTile / 2)
-            gemm_tile_mx<kModeF32Out, false, true, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
+            gemm_tile_mx<kModeF32T, false, true, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
         else
-            gemm_tile_mx<kModeF32Out, false, false, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
+            gemm_tile_mx<kModeF32T, false, false, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
     }
 }
 
@@ -715,27 +776,30 @@ int mx_gemm_rows(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t 
 int mx_gemm_kseg(const uint8_t *a_codes, const uint8_t *a_scales, int M, const uint8_t *b_codes,
                  const uint8_t *b_scales, int N, int64_t ld, const int32_t *poffs, int E, float *C, hipStream_t s,
                  const char *what) {
+    // A in the kernel's weight slot and B in its token slot, so that a lane's
+    // accumulators run along a row of C (the transposed epilogue): the
+    // kernel's tiles are 256 rows of A (n_tile) by 256 rows of B (m0)
     MXArgs g{};
-    g.g.A = a_codes;
-    g.g.B = b_codes;
+    g.g.A = b_codes;
+    g.g.B = a_codes;
     g.g.C = C;
     g.g.E = E;
-    g.g.N_out = N;
+    g.g.N_out = M;
     g.g.K = static_cast<int>(ld);
-    g.ws = b_scales;
-    g.xs = a_scales;
-    g.g.n_tiles = (N + kMxTile - 1) / kMxTile;
-    const int64_t tiles = static_cast<int64_t>(E) * ((M + kMxTile - 1) / kMxTile) * g.g.n_tiles;
+    g.ws = a_scales;
+    g.xs = b_scales;
+    g.g.n_tiles = (M + kMxTile - 1) / kMxTile;
+    const int64_t tiles = static_cast<int64_t>(E) * ((N + kMxTile - 1) / kMxTile) * g.g.n_tiles;
     int64_t grid = num_cus();
     if (grid > tiles) grid = tiles;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
     g.g.grid = static_cast<int>(grid);
     const int kzero = static_cast<int>(ld / kMxBK) - 1;
-    if (M % kMxTile)
-        hipLaunchKernelGGL(grouped_gemm_mx_kseg<true>, dim3(g.g.grid), dim3(256), 0, s, g, poffs, M, kzero);
+    if (N % kMxTile)
+        hipLaunchKernelGGL(grouped_gemm_mx_kseg<true>, dim3(g.g.grid), dim3(256), 0, s, g, poffs, N, kzero);
     else
-        hipLaunchKernelGGL(grouped_gemm_mx_kseg<false>, dim3(g.g.grid), dim3(256), 0, s, g, poffs, M, kzero);
+        hipLaunchKernelGGL(grouped_gemm_mx_kseg<false>, dim3(g.g.grid), dim3(256), 0, s, g, poffs, N, kzero);
     return check_launch(what);
 }
 

@@ -99,7 +99,7 @@ __device__ __forceinline__ int mswz(int r, int c) { return r * 128 + ((c ^ ((r >
 // * k-segment mode: C[e] [M][N] (fp32) = A_e B_e^T with A [M][ld] and
 //   B [N][ld] shared by the experts, expert e reducing over its columns
 //   [poffs[e], poffs[e+1]) (multiples of 128); the last 128 columns of A and
-//   B (and their scale bytes) must be zeros.
+//   B (and their scale bytes) must be zeros; M % 32 == 0.
 int mx_gemm_rows(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t *gather, int a_rows,
                  const int32_t *offsets, int E, int64_t P, const uint8_t *b_codes, const uint8_t *b_scales, int N_out,
                  int K, void *C, bool f32_out, hipStream_t s, const char *what);

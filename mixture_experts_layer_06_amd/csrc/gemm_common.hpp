@@ -95,50 +95,6 @@ __device__ __forceinline__ int build_tile_prefix(const GGArgs &a, int BM, int *s
     return s_tmp[255];
 }
 
-// Balanced m-tiling of a segment of M rows for tiles of at most 256 rows:
-// nmt = ceil(M/256) tiles of R = ceil(M/nmt) rounded up to 32 rows (the last
-// one shorter). (nmt-1)*R < M always holds because R <= 256.
-__device__ __forceinline__ int bal_ntiles(int M) { return M > 0 ? (M + 255) >> 8 : 0; }
-__device__ __forceinline__ int bal_rows(int M, int nmt) {
-    const int r = (M + nmt - 1) / nmt;
-    return (r + 31) & ~31;
-}
-
-// Same prefix as build_tile_prefix, with the balanced m-tiling. Any block
-// size >= 256: threads 256.. only take part in the barriers.
-__device__ __forceinline__ int build_tile_prefix_bal(const GGArgs &a, int *s_cum, int *s_tmp) {
-    const int S = a.E + (a.M_sh > 0 ? 1 : 0);
-    const int t = threadIdx.x;
-    const bool on = t < 256;
-    int v[2] = {0, 0};
-    if (on) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int s = 2 * t + i;
-            int m = 0;
-            if (s < a.E) m = a.offsets[s + 1] - a.offsets[s];
-            else if (s < S) m = a.M_sh;
-            if (m < 0) m = 0;
-            v[i] = s < S ? bal_ntiles(m) * a.n_tiles : 0;
-        }
-        s_tmp[t] = v[0] + v[1];
-    }
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-        const int add = (on && t >= d) ? s_tmp[t - d] : 0;
-        __syncthreads();
-        if (on) s_tmp[t] += add;
-        __syncthreads();
-    }
-    if (on) {
-        const int excl = s_tmp[t] - v[0] - v[1];
-        if (2 * t < kMaxSeg) s_cum[2 * t] = excl;
-        if (2 * t + 1 < kMaxSeg) s_cum[2 * t + 1] = excl + v[0];
-    }
-    __syncthreads();
-    return s_tmp[255];
-}
-
 // Segment containing tile L: the largest s with s_cum[s] <= L.
 __device__ __forceinline__ int find_segment(const int *s_cum, int S, int L) {
     int lo = 0, hi = S - 1;
@@ -180,33 +136,6 @@ __device__ __forceinline__ TileInfo decode_tile(const GGArgs &a, const int *s_cu
     // m fastest: consecutive tiles reuse the same weight panel
     ti.m0 = (local % mt) * BM;
     ti.n_tile = local / mt;
-    return ti;
-}
-
-struct BalTile {
-    int seg, n_tile, M, row0, row_lo, rows;   // rows [row_lo, row_lo + rows) of the segment
-    bool shared;
-};
-
-__device__ __forceinline__ BalTile decode_tile_bal(const GGArgs &a, const int *s_cum, int L) {
-    const int S = a.E + (a.M_sh > 0 ? 1 : 0);
-    BalTile ti;
-    ti.seg = find_segment(s_cum, S, L);
-    ti.shared = ti.seg >= a.E;
-    if (ti.shared) {
-        ti.M = a.M_sh;
-        ti.row0 = 0;
-    } else {
-        ti.row0 = a.offsets[ti.seg];
-        ti.M = a.offsets[ti.seg + 1] - ti.row0;
-    }
-    const int nmt = bal_ntiles(ti.M);
-    const int R = bal_rows(ti.M, nmt);
-    const int local = L - s_cum[ti.seg];
-    const int mi = local % nmt;   // m fastest: consecutive tiles share a weight panel
-    ti.n_tile = local / nmt;
-    ti.row_lo = mi * R;
-    ti.rows = min(R, ti.M - ti.row_lo);
     return ti;
 }
 

@@ -344,8 +344,8 @@ struct MxTileSrc {
 // k-step kzero, which holds zero codes and scales: a product of zeros adds
 // exactly nothing, so a tile may run an even number of steps.
 template <int MODE, bool ODD, bool HALF, bool GATHER>
-__device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti, uint8_t *LB0, uint8_t *LB1, int k0,
-                                             int nks, float *part, int64_t crow0, int nreal, int kzero) {
+__device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti, uint8_t *LDSM, int k0, int nks,
+                                             float *part, int64_t crow0, int nreal, int kzero) {
     const GGArgs &a = x.g;
     constexpr int NI = HALF ? 2 : 4;
     constexpr int NJ = 4;
@@ -365,6 +365,12 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     const int chunk = tid & 7, rb = tid >> 3;
     const int so = mswz(rb, chunk);
     (void)a;
+    // LDS: the two stages' scale blocks first, then their operand data, so
+    // that every scale word sits at a 16-bit immediate offset from one
+    // per-lane base (behind a stage's 64 KB of data each word needed an
+    // address register of its own, which the loop spilled and reloaded)
+    uint8_t *const SC0 = LDSM, *const SC1 = LDSM + kMxScaleBytes;
+    uint8_t *const LB0 = LDSM + 2 * kMxScaleBytes, *const LB1 = LB0 + kMxStage;
 
     floatx16 acc[NI][NJ];
 #pragma unroll
@@ -387,20 +393,20 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
         f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
         return f;
     };
-    auto read_scales = [&](const uint8_t *LB, uint32_t (&SA)[NI], uint32_t (&SB)[NJ]) {
-        const uint32_t *LS = reinterpret_cast<const uint32_t *>(LB + kMxStage);
+    auto read_scales = [&](const uint8_t *SC, uint32_t (&SA)[NI], uint32_t (&SB)[NJ]) {
+        const uint32_t *LS = reinterpret_cast<const uint32_t *>(SC);
 #pragma unroll
         for (int i = 0; i < NI; ++i) SA[i] = LS[wrow0 + i * 32 + l32] >> (8 * lhi);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) SB[j] = LS[kMxTile + tok0 + j * 32 + l32] >> (8 * lhi);
     };
-    auto write_step = [&](uint8_t *LB) {
+    auto write_step = [&](uint8_t *LB, uint8_t *SC) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(LB + so + j * 32 * kMxBK) = R.W[j];
 #pragma unroll
         for (int j = 0; j < XJ; ++j) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + j * 32 * kMxBK) = R.X[j];
-        reinterpret_cast<uint32_t *>(LB + kMxStage)[tid] = R.S[0];
-        reinterpret_cast<uint32_t *>(LB + kMxStage)[kMxTile + tid] = R.S[1];
+        reinterpret_cast<uint32_t *>(SC)[tid] = R.S[0];
+        reinterpret_cast<uint32_t *>(SC)[kMxTile + tid] = R.S[1];
     };
     // One half: MFMAs of k-sub S of stage LBc (weight fragment 0 in fx,
     // token fragments in FBc), streaming in weight fragments of the same
@@ -426,11 +432,11 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     // Staging item q of a k-step (R.W[q] for q < 8, then the token chunks,
     // then the two scale words) to its place in stage LB.
     constexpr int NIT = NWR + 2;
-    auto write_item = [&](uint8_t *LB, auto q_tag) {
+    auto write_item = [&](uint8_t *LB, uint8_t *SC, auto q_tag) {
         constexpr int q = decltype(q_tag)::value;
         if constexpr (q < 8) *reinterpret_cast<u32x4 *>(LB + so + q * 32 * kMxBK) = R.W[q];
         else if constexpr (q < NWR) *reinterpret_cast<u32x4 *>(LB + kMxRegion + so + (q - 8) * 32 * kMxBK) = R.X[q - 8];
-        else reinterpret_cast<uint32_t *>(LB + kMxStage)[(q - NWR) * kMxTile + tid] = R.S[q - NWR];
+        else reinterpret_cast<uint32_t *>(SC)[(q - NWR) * kMxTile + tid] = R.S[q - NWR];
     };
     // Half 0 with the staging pinned: MFMA slot q (weight subtile i = q / NJ,
     // token subtile j) is followed by its fragment reads (the next weight
@@ -439,7 +445,8 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     // t+2 (items spread evenly over the slots). Items keep one order in
     // every step, so each write waits for the load issued one k-step before
     // it and no earlier one.
-    auto half0 = [&](const uint8_t *LBc, uint8_t *NXT, int kk, const uint32_t (&SA)[NI], const uint32_t (&SB)[NJ]) {
+    auto half0 = [&](const uint8_t *LBc, uint8_t *NXT, uint8_t *SNXT, int kk, const uint32_t (&SA)[NI],
+                     const uint32_t (&SB)[NJ]) {
         constexpr_for<NMF>([&](auto q_tag) {
             constexpr int q = decltype(q_tag)::value;
             constexpr int i = q / NJ, j = q % NJ;
@@ -452,22 +459,22 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
             constexpr int lo = q * NIT / NMF, hi = (q + 1) * NIT / NMF;
             constexpr_for<hi - lo>([&](auto r_tag) {
                 constexpr int it = lo + decltype(r_tag)::value;
-                write_item(NXT, std::integral_constant<int, it>{});
+                write_item(NXT, SNXT, std::integral_constant<int, it>{});
                 src.template load_item<it>(kk, R);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    auto step = [&](const uint8_t *CUR, uint8_t *NXT, int t, const uint32_t (&SAc)[NI], const uint32_t (&SBc)[NJ],
-                    uint32_t (&SAn)[NI], uint32_t (&SBn)[NJ]) {
+    auto step = [&](const uint8_t *CUR, uint8_t *NXT, uint8_t *SNXT, int t, const uint32_t (&SAc)[NI],
+                    const uint32_t (&SBc)[NJ], uint32_t (&SAn)[NI], uint32_t (&SBn)[NJ]) {
         const int kk = t + 2 < nk ? t + 2 : nk - 1;
         // NXT held k-step t-1, whose second k-sub every wave read during the
         // second half of the previous step: all of them are past it before
         // anyone overwrites it
         MOE_LDS_BARRIER();
-        half0(CUR, NXT, kk, SAc, SBc);
+        half0(CUR, NXT, SNXT, kk, SAc, SBc);
         MOE_LDS_BARRIER();
-        read_scales(NXT, SAn, SBn);
+        read_scales(SNXT, SAn, SBn);
         half(I1{}, I0{}, CUR, NXT, fb1, fb0, SAc, SBc);
         mx_sched<NMF, NRD + NI + NJ, 0, 0>();
         __builtin_amdgcn_sched_barrier(0);
@@ -476,23 +483,23 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     // prologue: k-step 0 into stage 0 with its scales, k-step 1 into VGPRs
     src.load_step(0, R);
     MOE_LDS_BARRIER();   // every wave is done reading the previous tile's stages
-    write_step(LB0);
+    write_step(LB0, SC0);
     src.load_step(nk > 1 ? 1 : 0, R);
     MOE_LDS_BARRIER();
-    read_scales(LB0, SA0, SB0);
+    read_scales(SC0, SA0, SB0);
     fx = frag(LB0, wrow0 + l32, 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb0[j] = frag(LB0 + kMxRegion, tok0 + j * 32 + l32, 0);
     if (ODD) {
         for (int t = 0; t + 1 < nk; t += 2) {
-            step(LB0, LB1, t, SA0, SB0, SA1, SB1);
-            step(LB1, LB0, t + 1, SA1, SB1, SA0, SB0);
+            step(LB0, LB1, SC1, t, SA0, SB0, SA1, SB1);
+            step(LB1, LB0, SC0, t + 1, SA1, SB1, SA0, SB0);
         }
-        step(LB0, LB1, nk - 1, SA0, SB0, SA1, SB1);
+        step(LB0, LB1, SC1, nk - 1, SA0, SB0, SA1, SB1);
     } else {
         for (int t = 0; t < nk; t += 2) {
-            step(LB0, LB1, t, SA0, SB0, SA1, SB1);
-            step(LB1, LB0, t + 1, SA1, SB1, SA0, SB0);
+            step(LB0, LB1, SC1, t, SA0, SB0, SA1, SB1);
+            step(LB1, LB0, SC0, t + 1, SA1, SB1, SA0, SB0);
         }
     }
     if (part) {
@@ -548,8 +555,7 @@ __device__ __forceinline__ MxSplitPlan mx_split_plan(const GGArgs &a, int total,
 
 template <int MODE, bool ODD, bool GATHER>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
-    __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage + kMxScaleBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage + kMxScaleBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t LDSM[2 * (kMxScaleBytes + kMxStage)];
     __shared__ int s_cum[kMaxSeg];
     __shared__ int s_tmp[256];
     const int total = __builtin_amdgcn_readfirstlane(build_tile_prefix(x.g, kMxTile, s_cum, s_tmp));
@@ -583,9 +589,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
         }
         const int64_t crow0 = static_cast<int64_t>(ti.row0) + ti.m0;
         if (ti.M - ti.m0 > kMxTile / 2)
-            gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LB0, LB1, k0, nks, part, crow0, nks, 0);
+            gemm_tile_mx<MODE, ODD, false, GATHER>(x, ti, LDSM, k0, nks, part, crow0, nks, 0);
         else
-            gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LB0, LB1, k0, nks, part, crow0, nks, 0);
+            gemm_tile_mx<MODE, ODD, true, GATHER>(x, ti, LDSM, k0, nks, part, crow0, nks, 0);
     }
 }
 
@@ -603,8 +609,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_mx(MXArgs x) {
 // M % 256 != 0 (HALF_TAIL).
 template <bool HALF_TAIL>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_mx_kseg(MXArgs x, const int32_t *poffs, int M, int kzero) {
-    __shared__ __attribute__((aligned(16))) uint8_t LB0[kMxStage + kMxScaleBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t LB1[kMxStage + kMxScaleBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t LDSM[2 * (kMxScaleBytes + kMxStage)];
     __shared__ int s_order[256], s_len[256];
     const int tid = threadIdx.x;
     // experts by decreasing k-range (ties: lower index first)
@@ -645,9 +650,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_mx_kseg(MXArgs x, const i
         const int64_t crow0 = static_cast<int64_t>(e) * x.g.N_out;
         const int nrun = nks + (nks & 1);
         if (HALF_TAIL && M - ti.m0 <= kMxTile / 2)
-            gemm_tile_mx<kModeF32T, false, true, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
+            gemm_tile_mx<kModeF32T, false, true, false>(x, ti, LDSM, k0, nrun, nullptr, crow0, nks, kzero);
         else
-            gemm_tile_mx<kModeF32T, false, false, false>(x, ti, LB0, LB1, k0, nrun, nullptr, crow0, nks, kzero);
+            gemm_tile_mx<kModeF32T, false, false, false>(x, ti, LDSM, k0, nrun, nullptr, crow0, nks, kzero);
     }
 }
 

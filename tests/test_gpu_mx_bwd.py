@@ -380,3 +380,30 @@ def test_mxfp8_training_step_full_size_sampled(moe_lib):
     torch.cuda.synchronize()
     for key in ("grad_x", "grad_w1", "grad_w2", "grad_w_gate"):
         assert torch.equal(g[key], g2[key]), key
+
+
+def test_mxfp8_training_step_imbalanced_full_size(moe_lib):
+    """The full imbalanced Qwen3-shaped step (T=8192, h=4096, F=1536,
+    E=128, top-8, Zipf-skewed gate bias, empty experts): the heaviest expert
+    (about 6,300 rows, 50 k-steps in each weight-gradient tile) and the
+    lightest expert with tokens (one k-step) over all of their tokens. The
+    weight-gradient launches run their tiles heaviest expert first, every
+    other round reversed, over many rounds of the persistent grid."""
+    cfg = wl.CONFIGS[5]
+    print("case mx backward imbalanced full size", flush=True)
+    dinp = wl.make_inputs(cfg, device="cuda", with_grad_out=True)
+    wq, f, g = _gpu_chain(cfg, dinp)
+    counts = f["counts"].cpu().numpy()
+    live = np.nonzero(counts > 0)[0]
+    experts = [int(live[np.argmax(counts[live])]), int(live[np.argmin(counts[live])])]
+    assert counts[experts[0]] > 48 * 128 and counts[experts[1]] <= 128
+    o = {"x": to_np32(dinp["x"]), "w_gate": to_np32(dinp["w_gate"]), "b_gate": to_np32(dinp["b_gate"]),
+         "w1": _LazyExperts(dinp["w1"]), "w2": _LazyExperts(dinp["w2"])}
+    G = to_np32(dinp["grad_out"]).astype(np.float64)
+    errs = {}
+    _expert_errs(cfg, o, G, f, g, experts, errs)
+    print({k: round(v, 5) for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
+    # an expert without tokens gets zero weight gradients
+    dead = int(np.nonzero(counts == 0)[0][0])
+    assert not g["grad_w1"][dead].any() and not g["grad_w2"][dead].any()

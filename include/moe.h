@@ -39,7 +39,7 @@
  *   (counts, offsets, weight and bias gradients) are still written (zeros).
  *
  * Supported sizes (MOE_ERR_UNSUPPORTED otherwise): h % 64 == 0, F % 64 == 0,
- * 1 <= k <= E <= 256, k <= 8, T*k < 2^31.
+ * 1 <= k <= E <= 256, T*k < 2^31.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -42,15 +42,18 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(int T, int k, int E, 
     if (!sigmoid) {
         for (int j = 0; j < k; ++j) dl[base + j] = w[base + j] * (gw[base + j] - c);
     } else {
-        float s[8], S = 0.0f;
-        for (int j = 0; j < k && j < 8; ++j) {
+        // the selected sigmoids: their sum, then each again (the same value)
+        auto sig_of = [&](int j) {
             int e = topk_idx[base + j];
             e = (e >= 0 && e < E) ? e : 0;
-            const float l = logits[static_cast<int64_t>(t) * E + e];
-            s[j] = 1.0f / (1.0f + expf(-l));
-            S += s[j];
+            return 1.0f / (1.0f + expf(-logits[static_cast<int64_t>(t) * E + e]));
+        };
+        float S = 0.0f;
+        for (int j = 0; j < k; ++j) S += sig_of(j);
+        for (int j = 0; j < k; ++j) {
+            const float sj = sig_of(j);
+            dl[base + j] = sj * (1.0f - sj) / S * (gw[base + j] - c);
         }
-        for (int j = 0; j < k && j < 8; ++j) dl[base + j] = s[j] * (1.0f - s[j]) / S * (gw[base + j] - c);
     }
 }
 
@@ -212,8 +215,8 @@ extern "C" int moe_route_bwd(const void *x, int dtype, int64_t T, int64_t h, int
     MOE_CHECK_ARG(score == MOE_SCORE_SOFTMAX || logits, MOE_ERR_INVALID_ARG,
                   "moe_route_bwd: sigmoid scoring needs the logits");
     MOE_CHECK_ARG(T >= 0 && h > 0 && E > 0 && k > 0, MOE_ERR_INVALID_ARG, "moe_route_bwd: bad sizes");
-    MOE_CHECK_ARG(k <= E && E <= 256 && k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED,
-                  "moe_route_bwd: need k <= E <= 256, k <= 8, h %% 64 == 0");
+    MOE_CHECK_ARG(k <= E && E <= 256 && h % 64 == 0, MOE_ERR_UNSUPPORTED,
+                  "moe_route_bwd: need k <= E <= 256, h %% 64 == 0");
     MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
                   "moe_route_bwd: T*k must be < 2^31");
     const size_t need = moe_route_bwd_workspace_size(T, h, E, k);

@@ -102,32 +102,35 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
     const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
     if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     const int64_t P = npieces / nv * k;   // rows of y
-    const int64_t base = static_cast<int64_t>(t) * k;
-    // indices without branches (slots past k re-read slot k - 1), then every
-    // row piece loaded raw before any is used: one round trip per phase
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    // the slots in chunks of KM (one chunk unless k > 8): indices without
+    // branches (slots past the chunk re-read its last slot), then every row
+    // piece loaded raw before any is used: one round trip per phase
+    for (int j0 = 0; j0 < k; j0 += KM) {
+    const int kc = min(KM, k - j0);
+    const int64_t base = static_cast<int64_t>(t) * k + j0;
     int rows[KM];
     float w[KM];
     bool ok[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-        rows[j] = row_of[base + (j < k ? j : k - 1)];
-        w[j] = topk_w ? topk_w[base + (j < k ? j : k - 1)] : 1.0f;
+        rows[j] = row_of[base + (j < kc ? j : kc - 1)];
+        w[j] = topk_w ? topk_w[base + (j < kc ? j : kc - 1)] : 1.0f;
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-        ok[j] = j < k && rows[j] >= 0 && rows[j] < P;
+        ok[j] = j < kc && rows[j] >= 0 && rows[j] < P;
         rows[j] = ok[j] ? rows[j] : 0;
     }
     Raw8<TE> yr[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-        if (j < k) raw8_load_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yr[j]);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        if (j < kc) raw8_load_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yr[j]);
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-        if (j < k) {
+        if (j < kc) {
             float yv[8];
             raw8_f32(yr[j], yv);
             // a dropped pair (row -1) loaded row 0 only to keep the loads
@@ -138,6 +141,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[i], acc[i]);
         }
+    }
     if (y_sh) {
         float sv[8];
         load8_nt(y_sh + static_cast<int64_t>(t) * h + 8 * v, sv);
@@ -159,28 +163,32 @@ __global__ __launch_bounds__(1024) void unpermute_bwd_kernel(
     float *__restrict__ gw) {
     __shared__ float red[8][16];
     const int t = blockIdx.x;
+    const int nv = h / 8;
+    // the slots in chunks of 8 (one chunk unless k > 8)
+    for (int j0 = 0; j0 < k; j0 += 8) {
+    const int kc = min(8, k - j0);
+    const int64_t base = static_cast<int64_t>(t) * k + j0;
     int rows[8];
     float w[8], dot[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        rows[j] = j < k ? row_of[static_cast<int64_t>(t) * k + j] : -1;
+        rows[j] = j < kc ? row_of[base + j] : -1;
         if (rows[j] >= static_cast<int64_t>(gridDim.x) * k) rows[j] = -1;   // rows of y: T k
-        w[j] = j < k ? topk_w[static_cast<int64_t>(t) * k + j] : 0.0f;
+        w[j] = j < kc ? topk_w[base + j] : 0.0f;
         dot[j] = 0.0f;
     }
-    const int nv = h / 8;
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
         // every piece loaded raw before any is used (one round trip)
         Raw8<TE> gr, yr[8];
         raw8_load_nt(gout + static_cast<int64_t>(t) * h + 8 * v, gr);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (j < k) raw8_load_nt(y + static_cast<int64_t>(rows[j] >= 0 ? rows[j] : 0) * h + 8 * v, yr[j]);
+            if (j < kc) raw8_load_nt(y + static_cast<int64_t>(rows[j] >= 0 ? rows[j] : 0) * h + 8 * v, yr[j]);
         float g[8];
         raw8_f32(gr, g);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (j < k && rows[j] >= 0) {
+            if (j < kc && rows[j] >= 0) {
                 float yv[8], d[8];
                 raw8_f32(yr[j], yv);
 #pragma unroll
@@ -201,11 +209,13 @@ __global__ __launch_bounds__(1024) void unpermute_bwd_kernel(
         if (lane == 0) red[j][wave] = sdot;
     }
     __syncthreads();
-    if (threadIdx.x < k) {
+    if (threadIdx.x < kc) {
         const int j = threadIdx.x;
         float sdot = red[j][0];
         for (int wv = 1; wv < nw; ++wv) sdot += red[j][wv];
-        gw[static_cast<int64_t>(t) * k + j] = sdot;
+        gw[base + j] = sdot;
+    }
+    __syncthreads();   // red is rewritten by the next chunk
     }
 }
 
@@ -223,21 +233,27 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
     if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     const int64_t P = npieces / nv * k;   // rows of grad_x_perm
-    const int64_t base = static_cast<int64_t>(t) * k;
-    // every load of a phase is issued before any of its values is used (k is
-    // uniform, so `j < k` is a scalar branch; out-of-range indices are
-    // clamped to a valid address and their terms dropped by a select), so
-    // the phases cost one memory round trip each
-    // index loads without branches: slots past k re-read slot k - 1
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    // the slots in chunks of KM (one chunk unless k > 8); every load of a
+    // phase is issued before any of its values is used (k is uniform, so
+    // `j < kc` is a scalar branch; out-of-range indices are clamped to a
+    // valid address and their terms dropped by a select), so the phases cost
+    // one memory round trip each
+    for (int j0 = 0; j0 < k; j0 += KM) {
+    const int kc = min(KM, k - j0);
+    const int64_t base = static_cast<int64_t>(t) * k + j0;
+    // index loads without branches: slots past the chunk re-read its last slot
     int rows[KM], ex[KM];
     float dl[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) rows[j] = row_of[base + (j < k ? j : k - 1)];
+    for (int j = 0; j < KM; ++j) rows[j] = row_of[base + (j < kc ? j : kc - 1)];
     if (gl) {
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
-            ex[j] = topk_idx[base + (j < k ? j : k - 1)];
-            dl[j] = gl[base + (j < k ? j : k - 1)];
+            ex[j] = topk_idx[base + (j < kc ? j : kc - 1)];
+            dl[j] = gl[base + (j < kc ? j : kc - 1)];
         }
     } else {
 #pragma unroll
@@ -249,26 +265,23 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     bool rok[KM], eok[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-        rok[j] = j < k && rows[j] >= 0 && rows[j] < P;
-        eok[j] = j < k && ex[j] >= 0 && ex[j] < E;
+        rok[j] = j < kc && rows[j] >= 0 && rows[j] < P;
+        eok[j] = j < kc && ex[j] >= 0 && ex[j] < E;
         rows[j] = rok[j] ? rows[j] : 0;
         ex[j] = eok[j] ? ex[j] : 0;
     }
     Raw8<TE> d[KM], wr[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-        if (j < k) raw8_load_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
+        if (j < kc) raw8_load_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
     if (gl) {
 #pragma unroll
         for (int j = 0; j < KM; ++j)
-            if (j < k) raw8_load(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wr[j]);
+            if (j < kc) raw8_load(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wr[j]);
     }
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-        if (j < k) {
+        if (j < kc) {
             float dv[8];
             raw8_f32(d[j], dv);
 #pragma unroll
@@ -277,12 +290,13 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     if (gl) {
 #pragma unroll
         for (int j = 0; j < KM; ++j)
-            if (j < k) {
+            if (j < kc) {
                 float wv[8];
                 raw8_f32(wr[j], wv);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], eok[j] ? wv[i] : 0.0f, acc[i]);
             }
+    }
     }
     store8_nt(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
 }
@@ -300,20 +314,26 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const TE *__restrict_
     const int v = static_cast<int>(idx - static_cast<int64_t>(t) * nv);
     if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     const int64_t P = npieces / nv * k;
-    // the piece and all k row indices in flight together (slots past k
-    // re-read slot k - 1 and store nothing)
-    int rows[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
+    // the piece and a chunk's KM row indices in flight together (slots past
+    // the chunk re-read its last slot and store nothing; one chunk unless
+    // k > 8)
     float g[8];
-    load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+    for (int j0 = 0; j0 < k; j0 += KM) {
+        const int kc = min(KM, k - j0);
+        const int64_t base = static_cast<int64_t>(t) * k + j0;
+        int rows[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-        if (j < k && rows[j] >= 0 && rows[j] < P) store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, g);
+        for (int j = 0; j < KM; ++j) rows[j] = row_of[base + (j < kc ? j : kc - 1)];
+        if (j0 == 0) load8_nt(gout + static_cast<int64_t>(t) * h + 8 * v, g);
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            if (j < kc && rows[j] >= 0 && rows[j] < P) store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, g);
+    }
 }
 
-// f(KM, WT) with KM the top-k slots a thread walks (k rounded up to 1, 2, 4
-// or 8; slots past k re-read slot k - 1 and add nothing) and WT whether each
+// f(KM, WT) with KM the top-k slots a thread walks at a time (k rounded up
+// to 1, 2, 4 or 8, and 8 at a time for k > 8; slots past k re-read slot
+// k - 1 and add nothing) and WT whether each
 // wave's 64 pieces belong to one token (h / 8 a multiple of 64), so that the
 // token's indices and weights are wave-uniform and read by scalar loads.
 template <typename Fn>
@@ -332,7 +352,7 @@ int check_common(const char *fn, int dtype, int64_t T, int64_t h, int k) {
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG,
                   "%s: bad dtype %d", fn, dtype);
     MOE_CHECK_ARG(T >= 0 && h > 0 && k > 0, MOE_ERR_INVALID_ARG, "%s: bad sizes", fn);
-    MOE_CHECK_ARG(k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: need k <= 8, h %% 64 == 0", fn);
+    MOE_CHECK_ARG(k <= 256 && h % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: need k <= 256, h %% 64 == 0", fn);
     MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && T < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
                   "%s: T*k must be < 2^31", fn);
     return MOE_OK;

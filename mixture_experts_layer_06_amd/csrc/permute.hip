@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x
     if constexpr (WT) t = __builtin_amdgcn_readfirstlane(t);   // one token per wave: scalar index loads
     // the piece and the row indices of the KM top-k slots in flight together
     // (KM = k rounded up to 1, 2, 4 or 8; slots past k re-read slot k - 1
-    // and store nothing)
+    // and store nothing; for k > 8 further chunks of 8 follow)
     int rows[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + (j < k ? j : k - 1)];
@@ -136,10 +136,17 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const TE *__restrict__ x
     // stores below would, with the in-order memory counter, also wait for
     // the stores issued before it
     __asm__ volatile("" ::"v"(d));
+    for (int j0 = 0; j0 < k; j0 += KM) {
+        const int kc = min(KM, k - j0);
+        if (j0 > 0) {
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-        if (j < k && rows[j] >= 0 && static_cast<int64_t>(rows[j]) < npieces / nv * k)
-            __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(rows[j]) * h) + v);
+            for (int j = 0; j < KM; ++j) rows[j] = row_of[static_cast<int64_t>(t) * k + j0 + (j < kc ? j : kc - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            if (j < kc && rows[j] >= 0 && static_cast<int64_t>(rows[j]) < npieces / nv * k)
+                __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(x_perm + static_cast<int64_t>(rows[j]) * h) + v);
+    }
 }
 
 // Routing weights in permuted-row order and back:
@@ -181,8 +188,8 @@ int permute_check(const void *x, int dtype, int64_t T, int64_t h, int E, int k, 
     MOE_CHECK_ARG(dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16, MOE_ERR_INVALID_ARG, "%s: bad dtype %d", name,
                   dtype);
     MOE_CHECK_ARG(T >= 0 && h > 0 && E > 0 && k > 0, MOE_ERR_INVALID_ARG, "%s: bad sizes", name);
-    MOE_CHECK_ARG(k <= E && E <= kMaxE && k <= 8 && h % 64 == 0, MOE_ERR_UNSUPPORTED,
-                  "%s: need k <= E <= 256, k <= 8, h %% 64 == 0", name);
+    MOE_CHECK_ARG(k <= E && E <= kMaxE && h % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: need k <= E <= 256, h %% 64 == 0",
+                  name);
     MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
                   "%s: T*k must be < 2^31", name);
     MOE_CHECK_ARG(x_perm == nullptr || (aligned16(x) && aligned16(x_perm)), MOE_ERR_INVALID_ARG,

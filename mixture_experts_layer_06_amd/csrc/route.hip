@@ -175,7 +175,10 @@ __device__ __forceinline__ void gate_item(const TIn *__restrict__ xrow, const TI
 
 // Work items of a block: (token tt in [0,8), expert group eg); lane group lg
 // of the block (32 per block, 8 per wave) takes items lg, lg + 32, ...
-template <typename TIn, int EPG, int U>
+// BIGK (k > 8): each round's choice is recorded in LDS instead of the
+// registers of the lane group, the weights are formed from there in the same
+// order, and the routing map is read from the groups' removed-expert bits.
+template <typename TIn, int EPG, int U, bool BIGK>
 __global__ __launch_bounds__(256) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wg, const float *__restrict__ bg,
     const float *__restrict__ sel_bias, int T, int h, int E, int k, int sigmoid,
@@ -183,6 +186,8 @@ __global__ __launch_bounds__(256) void route_kernel(
     uint8_t *__restrict__ rmap) {
     __shared__ float s_logit[kTokPerBlock][kMaxE];
     __shared__ float s_key[kTokPerBlock][kMaxE];
+    __shared__ float s_sel_l[BIGK ? kTokPerBlock : 1][BIGK ? kMaxE : 1];
+    __shared__ int s_sel_e[BIGK ? kTokPerBlock : 1][BIGK ? kMaxE : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -254,10 +259,39 @@ __global__ __launch_bounds__(256) void route_kernel(
                 if (precedes(ok, oi, bk, bi)) { bk = ok; bi = oi; }
             }
             if ((bi & 7) == q && bi < E) removed |= 1u << (bi >> 3);
+            if constexpr (BIGK) {
+                if (q == 0) {
+                    s_sel_e[g][j] = bi;
+                    s_sel_l[g][j] = s_logit[g][bi < E ? bi : 0];
+                }
+            } else {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                if (jj == j) { sel_e[jj] = bi; sel_l[jj] = s_logit[g][bi < E ? bi : 0]; }
+                for (int jj = 0; jj < 8; ++jj)
+                    if (jj == j) { sel_e[jj] = bi; sel_l[jj] = s_logit[g][bi < E ? bi : 0]; }
+            }
         }
+        if constexpr (BIGK) {
+            // lane 0 of the group wrote the lists: the weights as in
+            // route_weights, over k entries
+            if (q == 0) {
+                float wsum = 0.0f;
+                for (int j = 0; j < k; ++j) {
+                    const float l = s_sel_l[g][j];
+                    wsum += sigmoid ? 1.0f / (1.0f + expf(-l)) : expf(l - s_sel_l[g][0]);
+                }
+                const float inv = 1.0f / wsum;
+                for (int j = 0; j < k; ++j) {
+                    const float l = s_sel_l[g][j];
+                    const float wj = sigmoid ? 1.0f / (1.0f + expf(-l)) : expf(l - s_sel_l[g][0]);
+                    topk_idx[static_cast<int64_t>(t) * k + j] = s_sel_e[g][j];
+                    topk_w[static_cast<int64_t>(t) * k + j] = wj * inv;
+                }
+            }
+            if (rmap) {
+                uint8_t *row = rmap + static_cast<int64_t>(t) * E;
+                for (int m = 0; q + 8 * m < E; ++m) row[q + 8 * m] = (removed >> m) & 1u;
+            }
+        } else {
         if (q == 0) {
             float wv[8];
             route_weights(sel_l, k, sigmoid, wv);
@@ -277,6 +311,7 @@ __global__ __launch_bounds__(256) void route_kernel(
                 for (int j = 0; j < 8; ++j) on |= (j < k) && (sel_e[j] == e);
                 row[e] = on ? 1 : 0;
             }
+        }
         }
     }
 }
@@ -833,8 +868,7 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
                   "moe_route: bad sizes T=%lld h=%lld E=%d k=%d", (long long)T, (long long)h, E, k);
     MOE_CHECK_ARG(h % 64 == 0, MOE_ERR_UNSUPPORTED, "moe_route: h=%lld not a multiple of 64",
                   (long long)h);
-    MOE_CHECK_ARG(k <= E && E <= kMaxE && k <= 8, MOE_ERR_UNSUPPORTED,
-                  "moe_route: need k <= E <= 256 and k <= 8 (E=%d k=%d)", E, k);
+    MOE_CHECK_ARG(k <= E && E <= kMaxE, MOE_ERR_UNSUPPORTED, "moe_route: need k <= E <= 256 (E=%d k=%d)", E, k);
     MOE_CHECK_ARG(T * k < (int64_t(1) << 31) && h < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
                   "moe_route: T*k must be < 2^31");
     MOE_CHECK_ARG(sel_bias == nullptr || score == MOE_SCORE_SIGMOID, MOE_ERR_INVALID_ARG,
@@ -861,6 +895,29 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
     };
     const int sig = score == MOE_SCORE_SIGMOID;
     const int hh = static_cast<int>(h), TT = static_cast<int>(T);
+    if (k > 8) {
+        // more than 8 selections per token: the fixed-order kernel with its
+        // selections kept in LDS (no workload on the pages selects more than 8)
+        const dim3 grid(static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock));
+        if (dtype == MOE_DTYPE_BF16) {
+            const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
+            if (E <= 16)
+                hipLaunchKernelGGL((route_kernel<bf16_t, 1, 8, true>), grid, dim3(256), 0, s, xp, wp, b_gate, sel_bias,
+                                   TT, hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
+            else
+                hipLaunchKernelGGL((route_kernel<bf16_t, 8, 2, true>), grid, dim3(256), 0, s, xp, wp, b_gate, sel_bias,
+                                   TT, hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
+        } else {
+            const float *xp = static_cast<const float *>(x), *wp = static_cast<const float *>(w_gate);
+            if (E <= 16)
+                hipLaunchKernelGGL((route_kernel<float, 1, 4, true>), grid, dim3(256), 0, s, xp, wp, b_gate, sel_bias,
+                                   TT, hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
+            else
+                hipLaunchKernelGGL((route_kernel<float, 8, 1, true>), grid, dim3(256), 0, s, xp, wp, b_gate, sel_bias,
+                                   TT, hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
+        }
+        return count("moe_route (k > 8)");
+    }
     if (dtype == MOE_DTYPE_BF16 && logits == nullptr && E >= 32 && workspace && h <= 8192 &&
         workspace_bytes >= moe_route_workspace_size(T, E) && T * E < (int64_t(1) << 31)) {
         const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
@@ -912,18 +969,18 @@ extern "C" int moe_route(const void *x, int dtype, int64_t T, int64_t h, const v
     if (dtype == MOE_DTYPE_BF16) {
         const bf16_t *xp = static_cast<const bf16_t *>(x), *wp = static_cast<const bf16_t *>(w_gate);
         if (E <= 16)
-            hipLaunchKernelGGL((route_kernel<bf16_t, 1, 8>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
+            hipLaunchKernelGGL((route_kernel<bf16_t, 1, 8, false>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
                                hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
         else
-            hipLaunchKernelGGL((route_kernel<bf16_t, 8, 2>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
+            hipLaunchKernelGGL((route_kernel<bf16_t, 8, 2, false>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
                                hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
     } else {
         const float *xp = static_cast<const float *>(x), *wp = static_cast<const float *>(w_gate);
         if (E <= 16)
-            hipLaunchKernelGGL((route_kernel<float, 1, 4>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
+            hipLaunchKernelGGL((route_kernel<float, 1, 4, false>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
                                hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
         else
-            hipLaunchKernelGGL((route_kernel<float, 8, 1>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
+            hipLaunchKernelGGL((route_kernel<float, 8, 1, false>), grid, block, 0, s, xp, wp, b_gate, sel_bias, TT,
                                hh, E, k, sig, logits, topk_idx, topk_w, routing_map);
     }
     return count("moe_route");

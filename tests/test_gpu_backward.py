@@ -34,18 +34,22 @@ def _gpu_fwd_bwd(cfg, dinp):
     return f, g
 
 
-def _check_all(cfg, inp, f, g, ref, experts):
+def _check_all(cfg, inp, f, g, ref, experts, logit_terms=None):
     """Token-row tensors (input gradients, routing-weight gradients) are held
     to the tolerance row by row; weight-gradient tensors (sums over an
     expert's tokens) tensor by tensor, per expert. A weight-gradient row of an
     expert with one or two tokens is one or two products scaled by a single
     activation gradient, which is itself a long cancelling sum, so its
-    row-relative error measures that cancellation, not the kernel."""
+    row-relative error measures that cancellation, not the kernel. With
+    logit_terms, the selected logits' gradients (w_j (gw_j - sum_i w_i gw_i),
+    a cancelling difference) are held relative to those terms instead."""
     tol = TOL[cfg.dtype]
     assert np.array_equal(f["topk_idx"].cpu().numpy(), ref_route(inp, cfg)["topk_idx"])
+    gls = g["grad_logits_sel"].cpu().numpy()
     errs = {
         "grad_topk_w": rel_err(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"]),
-        "grad_logits_sel": rel_err(g["grad_logits_sel"].cpu().numpy(), ref["d_logits_sel"]),
+        "grad_logits_sel": (rel_err(gls, ref["d_logits_sel"]) if logit_terms is None
+                            else rel_err_terms(gls, ref["d_logits_sel"], logit_terms)),
         "grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
         "grad_w_gate": rel_err_tensor(g["grad_w_gate"].cpu().numpy(), ref["dw_gate"]),
     }
@@ -97,6 +101,35 @@ def test_backward_sigmoid_router_and_ragged_tails(moe_lib):
     ref = oracle.backward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
                           to_np32(inp["grad_out"]))
     _check_all(cfg, inp, f, g, ref, range(cfg.E))
+
+
+@pytest.mark.parametrize("E,k,score", [(24, 12, "softmax"), (16, 16, "sigmoid"), (40, 9, "softmax")])
+def test_backward_more_than_eight_selections(moe_lib, E, k, score):
+    """More than 8 selections per token: the route keeps its choices in LDS
+    and the row kernels walk a token's slots in chunks of 8 (k = 9: a
+    one-slot second chunk; k = E = 16: every expert selected). With a dozen
+    weights of about 1/k each, c_j (gw_j - sum_i w_i gw_i) cancels strongly
+    and carries the bf16 rounding of the expert outputs inside gw, so the
+    selected logits' gradients are held relative to the sum of their terms,
+    c_j (|gw_j| + sum_i w_i |gw_i|) with c_j = w_j (softmax) or w_j (1 - s_j)
+    (sigmoid), like the weight gradients."""
+    cfg = wl.small_variant(wl.CONFIGS[5], T=150, h=128, F=64, E=E, k=k).with_shape(
+        score=score, skew=False, gate_bias=score == "softmax")
+    print("case k > 8", E, k, score, flush=True)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=True)
+    f, g = _gpu_fwd_bwd(cfg, to_device(inp))
+    o = oracle_inputs(inp)
+    ref = oracle.backward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                          to_np32(inp["grad_out"]), b_gate=o["b_gate"])
+    r = ref_route(inp, cfg)
+    w = r["topk_w"].astype(np.float64)
+    scale = w   # d(logit_j) = scale_j (gw_j - sum_i w_i gw_i)
+    if score == "sigmoid":
+        sj = 1.0 / (1.0 + np.exp(-np.take_along_axis(r["logits"].astype(np.float64), r["topk_idx"], axis=1)))
+        scale = w * (1.0 - sj)
+    agw = np.abs(ref["d_topk_w"])
+    terms = scale * (agw + (w * agw).sum(axis=1, keepdims=True))
+    _check_all(cfg, inp, f, g, ref, range(cfg.E), logit_terms=terms)
 
 
 def test_backward_slice_of_imbalanced_workload(moe_lib):

@@ -166,6 +166,23 @@ def test_route_sigmoid_bias_ties_and_k_equals_e(moe_lib):
     assert rel_err(r["topk_w"].cpu().numpy(), ref["topk_w"]) <= 1e-5
 
 
+@pytest.mark.parametrize("E,k,score", [(32, 32, "sigmoid"), (64, 17, "softmax"), (12, 12, "softmax")])
+def test_route_more_than_eight_selections(moe_lib, E, k, score):
+    """k above 8 (the selections kept in LDS), against the oracle: indices,
+    routing map and counts exactly, weights to 1e-5; k = E with tied
+    selection biases, and a one-slot last chunk (k = 17)."""
+    g = torch.Generator().manual_seed(E + k)
+    x = torch.randn(70, 256, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(E, 256, generator=g) / 16).to(torch.bfloat16)
+    bias = None
+    if score == "sigmoid":
+        bias = (torch.rand(E, generator=g) * 0.2 - 0.1).float()
+        bias[3] = bias[6]
+    r, ref = _route_only(x, wg, k, score, sel_bias=bias)
+    _assert_route_equal(r, ref)
+    assert rel_err(r["topk_w"].cpu().numpy(), ref["topk_w"]) <= 1e-5
+
+
 def _route_both(x, wg, k, score="softmax", b_gate=None, sel_bias=None):
     """The MFMA-filtered route (no logits requested) and the fixed-order pass."""
     from mixture_experts_layer_06_amd import binding as B
@@ -258,7 +275,7 @@ def test_route_mfma_filter_tiny_tokens(moe_lib, score):
     assert 0 < tiny < 2.0 ** -100, tiny       # the smallest tokens' logits are tiny and non-zero
 
 
-@pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (256, 8), (64, 1)])
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (256, 8), (64, 1), (16, 16), (32, 9), (256, 24)])
 def test_layer_edge_shapes(moe_lib, E, k):
     from mixture_experts_layer_06_amd import layer
     cfg = wl.small_variant(wl.CONFIGS[3], T=77, h=128, F=64, E=E, k=k)

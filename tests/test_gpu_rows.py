@@ -1,6 +1,7 @@
 """The row kernels of the dispatch and the combine, forward and backward,
 through the C-ABI on seeded inputs, over the top-k slot counts the kernels
-are built for (k rounded up to 1, 2, 4 or 8: k = 1, 3, 6, 8) and both
+are built for (k rounded up to 1, 2, 4 or 8: k = 1, 3, 6, 8; above 8 in
+chunks of 8: k = 9, 12, 16) and both
 token layouts: h a multiple of 512, where each wave's pieces belong to one
 token and its indices are read by scalar loads, and h = 192, where a wave
 spans several tokens. References: the oracle's permutation, combine and
@@ -14,7 +15,7 @@ from parity import TOL, rel_err, rel_err_tensor, to_np32
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(192, 3), (512, 1), (512, 3), (1024, 6), (512, 8), (64, 2)]
+SHAPES = [(192, 3), (512, 1), (512, 3), (1024, 6), (512, 8), (64, 2), (512, 12), (192, 9), (1024, 16)]
 
 
 def _routing(T, E, k, seed):
@@ -30,7 +31,7 @@ def test_dispatch_copy_and_combine(moe_lib, h, k, dtype):
     """x_perm rows are exactly the tokens' rows in the oracle's order; the
     combine of seeded expert rows (plus a shared row) matches the oracle."""
     from mixture_experts_layer_06_amd import binding as B
-    T, E = 131, 12
+    T, E = 131, max(12, k + 3)
     print("case rows", h, k, dtype, flush=True)
     idx, w, perm = _routing(T, E, k, seed=h + k)
     g = torch.Generator().manual_seed(h * 10 + k)
@@ -56,7 +57,7 @@ def test_combine_backward_and_dispatch_backward(moe_lib, h, k):
     grad_x_perm[row_of[t, j]] plus the router term of the oracle's
     router_grads for the selected logits' gradients."""
     from mixture_experts_layer_06_amd import binding as B
-    T, E = 131, 12
+    T, E = 131, max(12, k + 3)
     print("case rows bwd", h, k, flush=True)
     idx, w, perm = _routing(T, E, k, seed=7 * h + k)
     row_of = perm["row_of"].astype(np.int32)

@@ -19,7 +19,8 @@ sub-record per other workload under "configs": the tiny fp32 GELU layer, the
 Qwen3-235B and DeepSeek-V3 inference layers, the imbalanced Qwen3 training
 step and the handbook training step, each timed over a few steps with its
 dominant call's MFMA fraction from HIP events and the oracle timed on a few
-of its tokens. The GPU clock is sampled while the headline step is repeated
+of its tokens; then the Mixtral-shaped forward and the imbalanced training
+step again with MXFP8 expert GEMMs (fractions of the fp8 peak). The GPU clock is sampled while the headline step is repeated
 for about three seconds after the timed steps (the driver's metrics table
 refreshes about once a second, too slowly for the timed steps alone).
 
@@ -373,18 +374,27 @@ def cpu_baseline(cfg, inp, n_tok):
 
 
 SUB_CONFIGS = (1, 3, 4, 5, 6)
+MX_SUB_CONFIGS = (2, 5)   # the same workloads with MXFP8 expert GEMMs
 
 
-def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu):
+def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu, mx=False):
     """One other workload's step: forward (plus backward for training
     workloads), timed over `steps` steps after `warmup`, with the dominant
     call's MFMA fraction from HIP events on its stream; the oracle's forward
-    on the first cpu_tokens tokens as its CPU baseline."""
+    on the first cpu_tokens tokens as its CPU baseline. With mx, the expert
+    GEMMs in MXFP8 (weights quantised once, before timing; fractions of the
+    fp8 peak)."""
     cfg = wl.CONFIGS[cid]
     inp = wl.make_inputs(cfg, device="cuda:0")
     train = cfg.backward
+    wq = layer.quantize_experts_mx(inp, for_backward=train) if mx else None
 
     def step(timers=None):
+        if mx:
+            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers)
+            if train:
+                layer.backward_mxfp8(inp, f, wq, inp["grad_out"], cfg.k, cfg.score, timers=timers)
+            return f
         f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train, timers=timers)
         if train:
             layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act, timers=timers)
@@ -405,10 +415,13 @@ def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu):
     nmat = 3 if cfg.act == "swiglu" else 2
     call_flops = {"grouped_ffn": ffn_flops(cfg), "grouped_ffn_bwd": 2.0 * cfg.P * nmat * 2.0 * cfg.h * cfg.F}
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    if mx:
+        peak = PEAK_FP8_TFLOPS
     dom = max(live, key=lambda n: live[n])
     rec = {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "tokens_per_s": cfg.T / dt,
-        "ms_per_step": dt * 1e3, "steps": steps, "warmup": warmup, "dtype": cfg.dtype,
+        "ms_per_step": dt * 1e3, "steps": steps, "warmup": warmup,
+        "dtype": "mxfp8 (e4m3, e8m0 1x32)" if mx else cfg.dtype,
         "step": "forward + backward" if train else "forward",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.h, "experts": cfg.E,
                    "topk": cfg.k, "expert_ffn": cfg.F, "score": cfg.score, "act": cfg.act,
@@ -420,12 +433,14 @@ def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu):
                           "timing": "HIP events around the call on its stream, mean over the timed steps"},
         "calls_ms": {n: v * 1e3 for n, v in live.items()},
     }
+    if mx and train:
+        rec["dominant_call"]["flops_note"] = "algorithmic backward FLOPs only, the recomputation not credited"
     if with_cpu:
         try:
             rec["cpu_baseline"] = cpu_baseline(cfg, inp, min(cpu_tokens, cfg.T))
         except Exception as exc:
             rec["cpu_baseline"] = {"error": repr(exc)}
-    del inp
+    del inp, wq
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec
@@ -751,6 +766,10 @@ def main():
             print("sub-record %s" % wl.CONFIGS[cid].name, file=sys.stderr, flush=True)
             out["configs"][wl.CONFIGS[cid].name] = sub_record(
                 torch, layer, wl, cid, args.config_steps, 2, args.config_cpu_tokens, not args.no_cpu_baseline)
+        for cid in MX_SUB_CONFIGS:
+            name = wl.CONFIGS[cid].name + "_mxfp8"
+            print("sub-record %s" % name, file=sys.stderr, flush=True)
+            out["configs"][name] = sub_record(torch, layer, wl, cid, args.config_steps, 2, 0, False, mx=True)
     print(json.dumps(out), flush=True)
 
 

@@ -109,38 +109,38 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const TE *__restrict__ y
     // branches (slots past the chunk re-read its last slot), then every row
     // piece loaded raw before any is used: one round trip per phase
     for (int j0 = 0; j0 < k; j0 += KM) {
-    const int kc = min(KM, k - j0);
-    const int64_t base = static_cast<int64_t>(t) * k + j0;
-    int rows[KM];
-    float w[KM];
-    bool ok[KM];
+        const int kc = min(KM, k - j0);
+        const int64_t base = static_cast<int64_t>(t) * k + j0;
+        int rows[KM];
+        float w[KM];
+        bool ok[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-        rows[j] = row_of[base + (j < kc ? j : kc - 1)];
-        w[j] = topk_w ? topk_w[base + (j < kc ? j : kc - 1)] : 1.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-        ok[j] = j < kc && rows[j] >= 0 && rows[j] < P;
-        rows[j] = ok[j] ? rows[j] : 0;
-    }
-    Raw8<TE> yr[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-        if (j < kc) raw8_load_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yr[j]);
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-        if (j < kc) {
-            float yv[8];
-            raw8_f32(yr[j], yv);
-            // a dropped pair (row -1) loaded row 0 only to keep the loads
-            // uniform: its value is masked, not just its weight, so that a
-            // non-finite row 0 cannot reach this token (0 * inf = NaN)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) yv[i] = ok[j] ? yv[i] : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[i], acc[i]);
+        for (int j = 0; j < KM; ++j) {
+            rows[j] = row_of[base + (j < kc ? j : kc - 1)];
+            w[j] = topk_w ? topk_w[base + (j < kc ? j : kc - 1)] : 1.0f;
         }
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            ok[j] = j < kc && rows[j] >= 0 && rows[j] < P;
+            rows[j] = ok[j] ? rows[j] : 0;
+        }
+        Raw8<TE> yr[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            if (j < kc) raw8_load_nt(y + static_cast<int64_t>(rows[j]) * h + 8 * v, yr[j]);
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            if (j < kc) {
+                float yv[8];
+                raw8_f32(yr[j], yv);
+                // a dropped pair (row -1) loaded row 0 only to keep the loads
+                // uniform: its value is masked, not just its weight, so that a
+                // non-finite row 0 cannot reach this token (0 * inf = NaN)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) yv[i] = ok[j] ? yv[i] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], yv[i], acc[i]);
+            }
     }
     if (y_sh) {
         float sv[8];
@@ -166,56 +166,56 @@ __global__ __launch_bounds__(1024) void unpermute_bwd_kernel(
     const int nv = h / 8;
     // the slots in chunks of 8 (one chunk unless k > 8)
     for (int j0 = 0; j0 < k; j0 += 8) {
-    const int kc = min(8, k - j0);
-    const int64_t base = static_cast<int64_t>(t) * k + j0;
-    int rows[8];
-    float w[8], dot[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        rows[j] = j < kc ? row_of[base + j] : -1;
-        if (rows[j] >= static_cast<int64_t>(gridDim.x) * k) rows[j] = -1;   // rows of y: T k
-        w[j] = j < kc ? topk_w[base + j] : 0.0f;
-        dot[j] = 0.0f;
-    }
-    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        // every piece loaded raw before any is used (one round trip)
-        Raw8<TE> gr, yr[8];
-        raw8_load_nt(gout + static_cast<int64_t>(t) * h + 8 * v, gr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < kc) raw8_load_nt(y + static_cast<int64_t>(rows[j] >= 0 ? rows[j] : 0) * h + 8 * v, yr[j]);
-        float g[8];
-        raw8_f32(gr, g);
+        const int kc = min(8, k - j0);
+        const int64_t base = static_cast<int64_t>(t) * k + j0;
+        int rows[8];
+        float w[8], dot[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (j < kc && rows[j] >= 0) {
-                float yv[8], d[8];
-                raw8_f32(yr[j], yv);
+            rows[j] = j < kc ? row_of[base + j] : -1;
+            if (rows[j] >= static_cast<int64_t>(gridDim.x) * k) rows[j] = -1;   // rows of y: T k
+            w[j] = j < kc ? topk_w[base + j] : 0.0f;
+            dot[j] = 0.0f;
+        }
+        for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+            // every piece loaded raw before any is used (one round trip)
+            Raw8<TE> gr, yr[8];
+            raw8_load_nt(gout + static_cast<int64_t>(t) * h + 8 * v, gr);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    dot[j] = fmaf(g[i], yv[i], dot[j]);
-                    d[i] = w[j] * g[i];
+            for (int j = 0; j < 8; ++j)
+                if (j < kc) raw8_load_nt(y + static_cast<int64_t>(rows[j] >= 0 ? rows[j] : 0) * h + 8 * v, yr[j]);
+            float g[8];
+            raw8_f32(gr, g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < kc && rows[j] >= 0) {
+                    float yv[8], d[8];
+                    raw8_f32(yr[j], yv);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        dot[j] = fmaf(g[i], yv[i], dot[j]);
+                        d[i] = w[j] * g[i];
+                    }
+                    store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
                 }
-                store8_nt(gy + static_cast<int64_t>(rows[j]) * h + 8 * v, d);
             }
         }
-    }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float sdot = dot[j];
+        for (int j = 0; j < 8; ++j) {
+            float sdot = dot[j];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) sdot += __shfl_down(sdot, off);
-        if (lane == 0) red[j][wave] = sdot;
-    }
-    __syncthreads();
-    if (threadIdx.x < kc) {
-        const int j = threadIdx.x;
-        float sdot = red[j][0];
-        for (int wv = 1; wv < nw; ++wv) sdot += red[j][wv];
-        gw[base + j] = sdot;
-    }
-    __syncthreads();   // red is rewritten by the next chunk
+            for (int off = 32; off > 0; off >>= 1) sdot += __shfl_down(sdot, off);
+            if (lane == 0) red[j][wave] = sdot;
+        }
+        __syncthreads();
+        if (threadIdx.x < kc) {
+            const int j = threadIdx.x;
+            float sdot = red[j][0];
+            for (int wv = 1; wv < nw; ++wv) sdot += red[j][wv];
+            gw[base + j] = sdot;
+        }
+        __syncthreads();   // red is rewritten by the next chunk
     }
 }
 
@@ -242,61 +242,61 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(
     // valid address and their terms dropped by a select), so the phases cost
     // one memory round trip each
     for (int j0 = 0; j0 < k; j0 += KM) {
-    const int kc = min(KM, k - j0);
-    const int64_t base = static_cast<int64_t>(t) * k + j0;
-    // index loads without branches: slots past the chunk re-read its last slot
-    int rows[KM], ex[KM];
-    float dl[KM];
+        const int kc = min(KM, k - j0);
+        const int64_t base = static_cast<int64_t>(t) * k + j0;
+        // index loads without branches: slots past the chunk re-read its last slot
+        int rows[KM], ex[KM];
+        float dl[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) rows[j] = row_of[base + (j < kc ? j : kc - 1)];
-    if (gl) {
+        for (int j = 0; j < KM; ++j) rows[j] = row_of[base + (j < kc ? j : kc - 1)];
+        if (gl) {
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                ex[j] = topk_idx[base + (j < kc ? j : kc - 1)];
+                dl[j] = gl[base + (j < kc ? j : kc - 1)];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                ex[j] = -1;
+                dl[j] = 0.0f;
+            }
+        }
+        bool rok[KM], eok[KM];
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
-            ex[j] = topk_idx[base + (j < kc ? j : kc - 1)];
-            dl[j] = gl[base + (j < kc ? j : kc - 1)];
+            rok[j] = j < kc && rows[j] >= 0 && rows[j] < P;
+            eok[j] = j < kc && ex[j] >= 0 && ex[j] < E;
+            rows[j] = rok[j] ? rows[j] : 0;
+            ex[j] = eok[j] ? ex[j] : 0;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < KM; ++j) {
-            ex[j] = -1;
-            dl[j] = 0.0f;
-        }
-    }
-    bool rok[KM], eok[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-        rok[j] = j < kc && rows[j] >= 0 && rows[j] < P;
-        eok[j] = j < kc && ex[j] >= 0 && ex[j] < E;
-        rows[j] = rok[j] ? rows[j] : 0;
-        ex[j] = eok[j] ? ex[j] : 0;
-    }
-    Raw8<TE> d[KM], wr[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-        if (j < kc) raw8_load_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
-    if (gl) {
+        Raw8<TE> d[KM], wr[KM];
 #pragma unroll
         for (int j = 0; j < KM; ++j)
-            if (j < kc) raw8_load(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wr[j]);
-    }
+            if (j < kc) raw8_load_nt(gxp + static_cast<int64_t>(rows[j]) * h + 8 * v, d[j]);
+        if (gl) {
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-        if (j < kc) {
-            float dv[8];
-            raw8_f32(d[j], dv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += rok[j] ? dv[i] : 0.0f;
+            for (int j = 0; j < KM; ++j)
+                if (j < kc) raw8_load(wg + static_cast<int64_t>(ex[j]) * h + 8 * v, wr[j]);
         }
-    if (gl) {
 #pragma unroll
         for (int j = 0; j < KM; ++j)
             if (j < kc) {
-                float wv[8];
-                raw8_f32(wr[j], wv);
+                float dv[8];
+                raw8_f32(d[j], dv);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], eok[j] ? wv[i] : 0.0f, acc[i]);
+                for (int i = 0; i < 8; ++i) acc[i] += rok[j] ? dv[i] : 0.0f;
             }
-    }
+        if (gl) {
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+                if (j < kc) {
+                    float wv[8];
+                    raw8_f32(wr[j], wv);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], eok[j] ? wv[i] : 0.0f, acc[i]);
+                }
+        }
     }
     store8_nt(gx + static_cast<int64_t>(t) * h + 8 * v, acc);
 }

@@ -292,26 +292,26 @@ __global__ __launch_bounds__(256) void route_kernel(
                 for (int m = 0; q + 8 * m < E; ++m) row[q + 8 * m] = (removed >> m) & 1u;
             }
         } else {
-        if (q == 0) {
-            float wv[8];
-            route_weights(sel_l, k, sigmoid, wv);
+            if (q == 0) {
+                float wv[8];
+                route_weights(sel_l, k, sigmoid, wv);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < k) {
-                    topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
-                    topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
+                for (int j = 0; j < 8; ++j) {
+                    if (j < k) {
+                        topk_idx[static_cast<int64_t>(t) * k + j] = sel_e[j];
+                        topk_w[static_cast<int64_t>(t) * k + j] = wv[j];
+                    }
                 }
             }
-        }
-        if (rmap) {
-            uint8_t *row = rmap + static_cast<int64_t>(t) * E;
-            for (int e = q; e < E; e += 8) {
-                bool on = false;
+            if (rmap) {
+                uint8_t *row = rmap + static_cast<int64_t>(t) * E;
+                for (int e = q; e < E; e += 8) {
+                    bool on = false;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) on |= (j < k) && (sel_e[j] == e);
-                row[e] = on ? 1 : 0;
+                    for (int j = 0; j < 8; ++j) on |= (j < k) && (sel_e[j] == e);
+                    row[e] = on ? 1 : 0;
+                }
             }
-        }
         }
     }
 }

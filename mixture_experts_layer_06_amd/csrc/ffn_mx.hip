@@ -21,10 +21,11 @@
 //   scale of block b of row r comes from lane r + 32 b. So lane half g reads
 //   chunks 4s + g and 4s + 2 + g of k-sub s and supplies the scale of block
 //   2s + g. The four block scales of a row and k-step (one 4-byte word) are
-//   staged through LDS with the k-step's data, one word of weight rows and
-//   one of token rows per thread; a lane reads its row's word, shifted right
-//   by 8 g bits, so that k-sub s takes byte 2s (opsel 2s). Accumulators as
-//   in the bf16 kernel.
+//   staged through LDS with the k-step's data (both stages' scale blocks
+//   ahead of their operand data), one word of weight rows and one of token
+//   rows per thread; a lane reads its row's word, shifted right by 8 g bits,
+//   so that k-sub s takes byte 2s (opsel 2s). Accumulators as in the bf16
+//   kernel.
 // * moe_grouped_ffn_mx: first projection with SwiGLU, whose epilogue
 //   quantises the fp32 activation along F (and optionally also stores it in
 //   bf16), then the second projection on those codes (bf16 expert outputs).
@@ -430,7 +431,7 @@ __device__ __forceinline__ void gemm_tile_mx(const MXArgs &x, const TileInfo &ti
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     // Staging item q of a k-step (R.W[q] for q < 8, then the token chunks,
-    // then the two scale words) to its place in stage LB.
+    // then the two scale words) to its place in stage LB (scale words: SC).
     constexpr int NIT = NWR + 2;
     auto write_item = [&](uint8_t *LB, uint8_t *SC, auto q_tag) {
         constexpr int q = decltype(q_tag)::value;

@@ -101,7 +101,7 @@ const char *moe_last_error(void);
  *
  * Workspace (optional; NULL with 0 bytes is valid): device memory of
  * moe_route_workspace_size(T,E) bytes, 16-byte aligned. With it, bf16, at
- * least 32 experts and no logits output, the route first computes all logits
+ * least 32 experts, k <= 8 and no logits output, the route first computes all logits
  * with bf16 MFMA and proven error bounds, then the fixed-order logits only of
  * the experts that can still reach the top k; the outputs are identical, bit
  * for bit, to those of the fixed-order pass over all experts, for all finite

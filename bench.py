@@ -435,6 +435,15 @@ def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu, mx=Fa
     }
     if mx and train:
         rec["dominant_call"]["flops_note"] = "algorithmic backward FLOPs only, the recomputation not credited"
+    if dom == "grouped_ffn":
+        # the forward expert call's roof: the slower of its MFMA work at peak
+        # and one read of every expert weight at the nominal HBM rate
+        w_bytes = ffn_weight_bytes(cfg, 1) * 33 / 32 if mx else ffn_weight_bytes(cfg, 2 if cfg.dtype == "bf16" else 4)
+        t_mfma = call_flops[dom] / (peak * 1e12)
+        t_w = w_bytes / (PEAK_HBM_GBS * 1e9)
+        rec["dominant_call"].update({
+            "bound": "hbm (weight bytes)" if t_w > t_mfma else "mfma",
+            "roof_ms": max(t_mfma, t_w) * 1e3, "roof_frac": max(t_mfma, t_w) / live[dom]})
     if with_cpu:
         try:
             rec["cpu_baseline"] = cpu_baseline(cfg, inp, min(cpu_tokens, cfg.T))

@@ -34,7 +34,7 @@ def _gpu_fwd_bwd(cfg, dinp):
     return f, g
 
 
-def _check_all(cfg, inp, f, g, ref, experts, logit_terms=None):
+def _check_all(cfg, inp, f, g, ref, experts, logit_terms=None, w_terms=None):
     """Token-row tensors (input gradients, routing-weight gradients) are held
     to the tolerance row by row; weight-gradient tensors (sums over an
     expert's tokens) tensor by tensor, per expert. A weight-gradient row of an
@@ -42,12 +42,15 @@ def _check_all(cfg, inp, f, g, ref, experts, logit_terms=None):
     activation gradient, which is itself a long cancelling sum, so its
     row-relative error measures that cancellation, not the kernel. With
     logit_terms, the selected logits' gradients (w_j (gw_j - sum_i w_i gw_i),
-    a cancelling difference) are held relative to those terms instead."""
+    a cancelling difference) are held relative to those terms instead; with
+    w_terms, the routing-weight gradients (each one dot product <dL/dout_t,
+    y_tj> over h) relative to the sums of their products' magnitudes."""
     tol = TOL[cfg.dtype]
     assert np.array_equal(f["topk_idx"].cpu().numpy(), ref_route(inp, cfg)["topk_idx"])
     gls = g["grad_logits_sel"].cpu().numpy()
     errs = {
-        "grad_topk_w": rel_err(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"]),
+        "grad_topk_w": (rel_err(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"]) if w_terms is None
+                        else rel_err_terms(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"], w_terms)),
         "grad_logits_sel": (rel_err(gls, ref["d_logits_sel"]) if logit_terms is None
                             else rel_err_terms(gls, ref["d_logits_sel"], logit_terms)),
         "grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
@@ -130,6 +133,56 @@ def test_backward_more_than_eight_selections(moe_lib, E, k, score):
     agw = np.abs(ref["d_topk_w"])
     terms = scale * (agw + (w * agw).sum(axis=1, keepdims=True))
     _check_all(cfg, inp, f, g, ref, range(cfg.E), logit_terms=terms)
+
+
+def _logit_terms(inp, cfg, ref):
+    """c_j (|gw_j| + sum_i w_i |gw_i|) per selected logit: the terms whose
+    cancelling sum is its gradient (c_j = w_j, or w_j (1 - s_j) for sigmoid)."""
+    r = ref_route(inp, cfg)
+    w = r["topk_w"].astype(np.float64)
+    scale = w
+    if cfg.score == "sigmoid":
+        sj = 1.0 / (1.0 + np.exp(-np.take_along_axis(r["logits"].astype(np.float64), r["topk_idx"], axis=1)))
+        scale = w * (1.0 - sj)
+    agw = np.abs(ref["d_topk_w"])
+    return scale * (agw + (w * agw).sum(axis=1, keepdims=True))
+
+
+def _random_backward_cases(n=9, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        base = (5, 6, 4)[i % 3]   # skewed softmax, plain softmax, sigmoid with selection bias
+        T = int(rng.integers(1, 400))
+        h = 64 * int(rng.integers(1, 9))
+        F = 64 * int(rng.integers(1, 7))
+        E = int(rng.integers(9 if base == 5 else 1, 65))
+        k = int(rng.integers(1, min(E, 12) + 1))
+        out.append((i, base, T, h, F, E, k))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_backward_cases(), ids=lambda c: "r%d_c%d_T%d_h%d_F%d_E%d_k%d" % c)
+def test_backward_random_layers(moe_lib, case):
+    """Seeded random sizes (h and F multiples of 64, 1 <= k <= E) on the
+    training structures: the skewed softmax router with its gate bias, the
+    plain softmax one, and sigmoid scoring with a selection bias (no shared
+    expert). Every expert's weight gradients are checked. A token's
+    routing-weight gradients are dot products over h that can cancel (with
+    k = 1 its row is a single one), so they are held relative to the sums of
+    their products' magnitudes, as are the selected logits' gradients."""
+    i, base, T, h, F, E, k = case
+    print("case random backward", case, flush=True)
+    cfg = wl.small_variant(wl.CONFIGS[base], T=T, h=h, F=F, E=E, k=k).with_shape(n_shared=0)
+    inp = wl.make_inputs(cfg, device="cpu", with_grad_out=True)
+    f, g = _gpu_fwd_bwd(cfg, to_device(inp))
+    o = oracle_inputs(inp)
+    ref = oracle.backward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                          to_np32(inp["grad_out"]), b_gate=o["b_gate"], sel_bias=o["sel_bias"])
+    fwd = oracle.forward(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act,
+                         b_gate=o["b_gate"], sel_bias=o["sel_bias"])
+    w_terms = (np.abs(to_np32(inp["grad_out"]).astype(np.float64))[:, None, :] * np.abs(fwd["y_pair"])).sum(axis=2)
+    _check_all(cfg, inp, f, g, ref, range(cfg.E), logit_terms=_logit_terms(inp, cfg, ref), w_terms=w_terms)
 
 
 def test_backward_slice_of_imbalanced_workload(moe_lib):

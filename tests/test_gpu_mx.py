@@ -180,6 +180,27 @@ MX_CASES = {
 }
 
 
+def _random_mx_cases(n=6, seed=20261205):
+    """Seeded random sizes (h and F multiples of 128, 1 <= k <= E) on the
+    Mixtral, Qwen3, DeepSeek-V3 (sigmoid with a selection bias, no shared
+    expert), imbalanced and handbook structures."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        base = (2, 3, 4, 5, 6)[i % 5]
+        T = int(rng.integers(1, 600))
+        h = 128 * int(rng.integers(1, 7))
+        F = 128 * int(rng.integers(1, 5))
+        E = int(rng.integers(9 if base == 5 else 1, 65))
+        k = int(rng.integers(1, min(E, 12) + 1))
+        out["random%d_c%d_T%d_h%d_F%d_E%d_k%d" % (i, base, T, h, F, E, k)] = wl.small_variant(
+            wl.CONFIGS[base], T=T, h=h, F=F, E=E, k=k).with_shape(n_shared=0)
+    return out
+
+
+MX_CASES.update(_random_mx_cases())
+
+
 @pytest.mark.parametrize("name", list(MX_CASES))
 def test_mxfp8_layer_parity(moe_lib, name):
     """Layer output of the MXFP8 path against the oracle's MXFP8 layer;

@@ -391,7 +391,7 @@ def sub_record(torch, layer, wl, cid, steps, warmup, cpu_tokens, with_cpu, mx=Fa
 
     def step(timers=None):
         if mx:
-            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers)
+            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers, keep_for_backward=train)
             if train:
                 layer.backward_mxfp8(inp, f, wq, inp["grad_out"], cfg.k, cfg.score, timers=timers)
             return f
@@ -506,7 +506,7 @@ def main():
 
     def step(timers=None):
         if args.mxfp8:
-            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers)
+            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, timers=timers, keep_for_backward=train)
             if train:
                 layer.backward_mxfp8(inp, f, wq, inp["grad_out"], cfg.k, cfg.score, timers=timers)
             return f

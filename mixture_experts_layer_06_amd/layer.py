@@ -180,17 +180,21 @@ def quantize_experts_mx(inp: dict, for_backward: bool = False) -> dict:
     return out
 
 
-def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None = None):
+def forward_mxfp8(inp: dict, wq: dict, k: int, score: str, timers: dict | None = None,
+                  keep_for_backward: bool = False):
     """Forward with the expert GEMMs in MXFP8 ("Scalable Training of
     Mixture-of-Experts Models with Megatron Core", section 5.3.3): the router
     as in ``forward`` (fp32 logits), the token rows quantised along h and
     gathered by the first GEMM, the activation quantised along F in the first
     GEMM's epilogue (from fp32), the weighted combine in fp32. SwiGLU experts
     without bias. The result keeps the token codes (x_codes, x_scales) that
-    ``backward_mxfp8`` recomputes the first projection from."""
+    ``backward_mxfp8`` recomputes the first projection from, and, with
+    ``keep_for_backward`` and sigmoid scoring, the logits the router's
+    backward needs."""
     x = inp["x"]
     E = inp["w_gate"].shape[0]
-    r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias"))
+    r = B.moe_route(x, inp["w_gate"], k, score, b_gate=inp.get("b_gate"), sel_bias=inp.get("sel_bias"),
+                    want_logits=keep_for_backward and score == "sigmoid")
     p = B.moe_permute(x, r["topk_idx"], E, with_x_perm=False)
     xq, xs = B.moe_mx_quantize(x)
     f = _timed(timers, "grouped_ffn", lambda: B.moe_grouped_ffn_mx(

@@ -36,7 +36,7 @@ def test_graph_replay_equals_eager(moe_lib, name):
 
     def step():
         if mx:
-            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score)
+            f = layer.forward_mxfp8(inp, wq, cfg.k, cfg.score, keep_for_backward=True)
             return f, layer.backward_mxfp8(inp, f, wq, inp["grad_out"], cfg.k, cfg.score)
         f = layer.forward(inp, cfg.k, cfg.score, cfg.act, keep_for_backward=train)
         g = layer.backward(inp, f, inp["grad_out"], cfg.k, cfg.score, cfg.act) if train else {}

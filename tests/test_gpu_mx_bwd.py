@@ -38,7 +38,7 @@ class _LazyExperts:
 def _gpu_chain(cfg, dinp):
     from mixture_experts_layer_06_amd import layer
     wq = layer.quantize_experts_mx(dinp, for_backward=True)
-    f = layer.forward_mxfp8(dinp, wq, cfg.k, cfg.score)
+    f = layer.forward_mxfp8(dinp, wq, cfg.k, cfg.score, keep_for_backward=True)
     g = layer.backward_mxfp8(dinp, f, wq, dinp["grad_out"], cfg.k, cfg.score)
     torch.cuda.synchronize()
     return wq, f, g
@@ -75,6 +75,27 @@ CASES = {
 }
 
 
+def _random_cases(n=5, seed=20261206):
+    """Seeded random sizes (h and F multiples of 128, 1 <= k <= E) on the
+    Mixtral, Qwen3, DeepSeek-V3 (sigmoid with a selection bias, no shared
+    expert), imbalanced and handbook structures."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        base = (2, 3, 4, 5, 6)[i % 5]
+        T = int(rng.integers(1, 400))
+        h = 128 * int(rng.integers(1, 5))
+        F = 128 * int(rng.integers(1, 4))
+        E = int(rng.integers(9 if base == 5 else 1, 49))
+        k = int(rng.integers(1, min(E, 12) + 1))
+        out["random%d_c%d_T%d_h%d_F%d_E%d_k%d" % (i, base, T, h, F, E, k)] = wl.small_variant(
+            wl.CONFIGS[base], T=T, h=h, F=F, E=E, k=k).with_shape(n_shared=0)
+    return out
+
+
+CASES.update(_random_cases())
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_mxfp8_training_step_small(moe_lib, name):
     cfg = CASES[name]
@@ -85,9 +106,9 @@ def test_mxfp8_training_step_small(moe_lib, name):
     o = oracle_inputs(inp)
     G = to_np32(inp["grad_out"]).astype(np.float64)
     ref = oracle.backward_mxfp8(o["x"], o["w_gate"], o["w1"], o["w2"], cfg.k, cfg.score, cfg.act, G,
-                                b_gate=o["b_gate"])
+                                b_gate=o["b_gate"], sel_bias=o["sel_bias"])
     assert np.array_equal(f["topk_idx"].cpu().numpy(), oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score,
-                                                                    o["b_gate"])["topk_idx"])
+                                                                    o["b_gate"], o["sel_bias"])["topk_idx"])
     tol = TOL[cfg.dtype]
     errs = {"grad_x": rel_err(to_np32(g["grad_x"]), ref["dx"]),
             "grad_topk_w": rel_err_tensor(g["grad_topk_w"].cpu().numpy(), ref["d_topk_w"]),
@@ -98,8 +119,15 @@ def test_mxfp8_training_step_small(moe_lib, name):
         if counts[e] == 0:
             assert not gw1.any() and not gw2.any(), "empty expert %d" % e
             continue
-        errs["grad_w1[%d]" % e] = rel_err_tensor(gw1, ref["dw1"][e])
-        errs["grad_w2[%d]" % e] = rel_err_tensor(gw2, ref["dw2"][e])
+        if not name.startswith("random"):
+            errs["grad_w1[%d]" % e] = rel_err_tensor(gw1, ref["dw1"][e])
+            errs["grad_w2[%d]" % e] = rel_err_tensor(gw2, ref["dw2"][e])
+    if name.startswith("random"):
+        # every expert over all of its tokens with the code-flip allowance
+        # (an E4M3 code may differ where its operand lies within the fp32
+        # bound of a rounding boundary): the plain per-tensor bound cannot
+        # absorb one flipped code in an expert of a few tokens
+        _expert_errs(cfg, o, G, f, g, [e for e in range(cfg.E) if counts[e] > 0], errs)
     if name == "empty_experts":
         assert (counts == 0).any()
     worst = max(errs, key=errs.get)
@@ -299,7 +327,7 @@ def _expert_errs(cfg, o, G, f, g, experts, errs):
     accumulation bound). What remains must be within the tolerance of each
     row's sum of absolute terms; the share of elements such a spread touches
     and the plain per-tensor errors are printed."""
-    r = oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score, o["b_gate"])
+    r = oracle.route(o["x"], o["w_gate"], cfg.k, cfg.score, o["b_gate"], o.get("sel_bias"))
     offs = f["offsets"].cpu().numpy()
     for e in experts:
         tok, slot = np.nonzero(r["topk_idx"] == e)        # ascending tokens: the segment's order

@@ -84,6 +84,31 @@ CASES = {
 }
 
 
+def _random_cases(n=4, seed=20261207):
+    """Seeded random sizes (h and F multiples of 64, 1 <= k <= E) for each
+    expert kind with biases: GELU fp32, GELU bf16, SwiGLU fp32, SwiGLU bf16."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        T = int(rng.integers(1, 400))
+        h = 64 * int(rng.integers(1, 7))
+        F = 64 * int(rng.integers(1, 7))
+        E = int(rng.integers(9, 41))
+        k = int(rng.integers(1, min(E, 12) + 1))
+        kind = ("gelu", "gelu", "swiglu", "swiglu")[i % 4]
+        dt = ("f32", "bf16", "f32", "bf16")[i % 4]
+        if kind == "swiglu" and dt == "bf16":
+            cfg = wl.small_variant(wl.CONFIGS[5], T=T, h=h, F=F, E=E, k=k).with_shape(
+                expert_bias=True, gate_bias=False)
+        else:
+            cfg = wl.small_variant(wl.CONFIGS[1], T=T, h=h, F=F, E=E, k=k).with_shape(act=kind, dtype=dt)
+        out["random%d_%s_%s_T%d_h%d_F%d_E%d_k%d" % (i, kind, dt, T, h, F, E, k)] = (cfg, {})
+    return out
+
+
+CASES.update(_random_cases())
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_backward_expert_kinds_with_biases(moe_lib, name):
     from mixture_experts_layer_06_amd import layer
